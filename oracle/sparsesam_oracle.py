@@ -1,0 +1,388 @@
+"""Plain CPU statement of the SparseSAM encoder-block hot path (the oracle).
+
+TEST INFRASTRUCTURE ONLY: used by tests/, by ``__graft_entry__.smoke()`` and by
+the ``cpu_baseline`` leg of ``bench.py``; never by the product path.
+
+What it computes, step by step, with the passage each step follows:
+
+* importance -- a parameter-free Sobel operator gives a local gradient
+  magnitude per pixel as a proxy for information density ("Technische
+  Samenvatting: SparseSAM", Methodologie, 1. Stripe-Sort Attention, the
+  gradient-based ordering bullet; the same step in "技術概要：SparseSAM", 手法).
+  Reading: unnormalised [1,2,1] x [-1,0,1] kernels, zero border, L2 magnitude,
+  mean over each 16 x 16 patch in a fixed order (the token grid is SAM's).
+  These steps are fp32 with one rounding per operation in the order written,
+  because the sort below turns them into integers.
+* descending order -- tokens sorted by importance, highest first (same page,
+  stripe-sort bullet: a plain sort would put the foreground first). Ties go to
+  the lower token index; -0.0 equals +0.0; NaN sorts after every number.
+* stripe-sort -- the sorted list is read as a matrix of g columns, transposed
+  and flattened (same bullet). g = 4 from the 4 x 4 mosaic of the static
+  pattern bullet.
+* static pattern -- a 4 x 4 mosaic of sub-maps, each banded along its
+  diagonal, plus a small global keep-set (same page, static pattern bullet).
+  Reading: the same band of radius r (in B-token blocks of each stripe) in
+  every sub-map; the global set is the first G positions of stripe 0 and is
+  symmetric; r is the smallest radius whose kept share of the N x N map
+  reaches the requested density.
+* attention -- ordinary softmax attention restricted to the kept pairs, built
+  densely with an explicit mask in the original token order.
+* routed MLP -- the top K tokens of the importance order form the keep-set,
+  the MLP runs on them only, every other token keeps its residual value
+  unchanged ("Technische Samenvatting: SparseSAM", Methodologie,
+  2. Residual-Consistency MLP, token routing / selective computation /
+  residual propagation bullets). Reading: the undefined correction on the
+  residual set is zero; K = floor(d * n_real + 1/2), at least 1.
+* one permutation per image (global blocks) or per window (windowed blocks),
+  reused by every block of that type (the closing paragraph of that section).
+
+Block structure (not on the pages; SAM encoder conventions): pre-LN block,
+LayerNorm eps 1e-6 with biased variance, biases on qkv/proj/fc1/fc2, exact-erf
+GELU, softmax scale head_dim ** -0.5, matrices in [out, in] layout.
+
+Floating point: importance in fp32 (it decides integers, so both sides take it
+in the same precision); the block arithmetic in fp64.
+
+Parity status: every function here is pinned by tests in tests/test_oracle_*.py
+against brute force, closed forms, library special cases or hand-worked
+examples. The exact pattern semantics (which band, which global set, how r is
+chosen) are readings of the pages, which print no mask, no density table and no
+value: they are pinned only to their own written definitions (the hand-worked
+examples under tests/golden/ are derived from those definitions), so for the
+pattern rule itself parity is unpinned by the pages.
+"""
+import math
+
+import numpy as np
+from scipy.special import erf
+
+__all__ = [
+    "sobel_magnitude",
+    "patch_mean",
+    "importance",
+    "window_token_map",
+    "segment_importance",
+    "descending_order",
+    "stripe_sort",
+    "routed_count",
+    "routed_tokens",
+    "position_keep",
+    "band_radius",
+    "token_mask",
+    "masked_attention",
+    "layer_norm",
+    "gelu",
+    "routed_mlp",
+    "segments_for_image",
+    "block_forward",
+    "encoder_forward",
+]
+
+F32 = np.float32
+
+
+# ----------------------------------------------------------------------------
+# Importance (fp32, fixed operation order)
+# ----------------------------------------------------------------------------
+
+def sobel_magnitude(img: np.ndarray) -> np.ndarray:
+    """L2 Sobel gradient magnitude of a grayscale image, zero outside the image.
+
+    gx = ((P[y-1,x+1] + 2 P[y,x+1]) + P[y+1,x+1]) - ((P[y-1,x-1] + 2 P[y,x-1]) + P[y+1,x-1])
+    gy = ((P[y+1,x-1] + 2 P[y+1,x]) + P[y+1,x+1]) - ((P[y-1,x-1] + 2 P[y-1,x]) + P[y-1,x+1])
+    m  = sqrt(gx*gx + gy*gy)
+    Each operation rounds once to fp32 in exactly this order (no fused multiply-add).
+    """
+    img = np.asarray(img, dtype=F32)
+    H, W = img.shape
+    P = np.zeros((H + 2, W + 2), F32)
+    P[1:-1, 1:-1] = img
+
+    def at(dy, dx):
+        return P[1 + dy:1 + dy + H, 1 + dx:1 + dx + W]
+
+    two = F32(2.0)
+    gx = ((at(-1, 1) + two * at(0, 1)) + at(1, 1)) - ((at(-1, -1) + two * at(0, -1)) + at(1, -1))
+    gy = ((at(1, -1) + two * at(1, 0)) + at(1, 1)) - ((at(-1, -1) + two * at(-1, 0)) + at(-1, 1))
+    sq = gx * gx
+    sq = sq + gy * gy
+    return np.sqrt(sq).astype(F32)
+
+
+def patch_mean(mag: np.ndarray, patch: int) -> np.ndarray:
+    """Mean of each patch x patch tile, tokens in raster order -> fp32 [Hg * Wg].
+
+    Fixed order: each pixel row of a tile is summed left to right starting from 0,
+    the row sums are added top to bottom starting from 0, then the total is divided
+    by patch * patch (one correctly rounded fp32 division).
+    """
+    mag = np.asarray(mag, dtype=F32)
+    H, W = mag.shape
+    Hg, Wg = H // patch, W // patch
+    t = mag[:Hg * patch, :Wg * patch].reshape(Hg, patch, Wg, patch)
+    rows = np.zeros((Hg, patch, Wg), F32)
+    for c in range(patch):
+        rows = rows + t[:, :, :, c]
+    total = np.zeros((Hg, Wg), F32)
+    for r in range(patch):
+        total = total + rows[:, r, :]
+    return (total / F32(patch * patch)).astype(F32).reshape(-1)
+
+
+def importance(img: np.ndarray, patch: int = 16) -> np.ndarray:
+    """Per-token importance of one image: Sobel magnitude pooled per patch."""
+    return patch_mean(sobel_magnitude(img), patch)
+
+
+# ----------------------------------------------------------------------------
+# Segments: one global segment per image, or w x w windows
+# ----------------------------------------------------------------------------
+
+def window_token_map(grid_h: int, grid_w: int, window: int) -> np.ndarray:
+    """[n_windows, window*window] image token id of each window-local slot, -1 for pad.
+
+    The grid is padded at the bottom and right up to multiples of ``window``;
+    windows are taken in raster order and the slots of a window in raster order.
+    """
+    nwy = -(-grid_h // window)
+    nwx = -(-grid_w // window)
+    out = np.full((nwy * nwx, window * window), -1, np.int64)
+    for wy in range(nwy):
+        for wx in range(nwx):
+            for ly in range(window):
+                for lx in range(window):
+                    y, x = wy * window + ly, wx * window + lx
+                    if y < grid_h and x < grid_w:
+                        out[wy * nwx + wx, ly * window + lx] = y * grid_w + x
+    return out
+
+
+def segments_for_image(grid_h: int, grid_w: int, window: int) -> np.ndarray:
+    """Token map of the attention segments of one image: [segments, N] ids or -1."""
+    if window == 0:
+        return np.arange(grid_h * grid_w, dtype=np.int64)[None, :]
+    return window_token_map(grid_h, grid_w, window)
+
+
+def segment_importance(imp: np.ndarray, token_map: np.ndarray) -> np.ndarray:
+    """Importance of each segment slot; pad slots get -1.0 (below every magnitude)."""
+    out = np.where(token_map >= 0, imp[np.maximum(token_map, 0)], F32(-1.0))
+    return out.astype(F32)
+
+
+# ----------------------------------------------------------------------------
+# Ordering and stripe-sort
+# ----------------------------------------------------------------------------
+
+def descending_order(imp: np.ndarray) -> np.ndarray:
+    """Token ids sorted by importance, highest first, written as a rank count.
+
+    Token j precedes token i when imp[j] > imp[i], or when they are equal and j < i.
+    -0.0 and +0.0 are equal; a NaN is below every number and equal to every NaN.
+    rank[i] = number of tokens preceding i; s[rank[i]] = i.
+    """
+    v = np.asarray(imp, dtype=F32).astype(np.float64)
+    v = np.where(v == 0.0, 0.0, v)
+    nan = np.isnan(v)
+    n = v.shape[0]
+    idx = np.arange(n)
+    vi, vj = v[:, None], v[None, :]
+    ni, nj = nan[:, None], nan[None, :]
+    with np.errstate(invalid="ignore"):
+        j_higher = (~nj) & (ni | (vj > vi))
+        same = (ni & nj) | ((~ni) & (~nj) & (vj == vi))
+    precedes = j_higher | (same & (idx[None, :] < idx[:, None]))
+    rank = precedes.sum(axis=1)
+    s = np.empty(n, np.int64)
+    s[rank] = idx
+    return s
+
+
+def stripe_sort(s: np.ndarray, stripes: int):
+    """Stripe-sort of a sorted token list: (perm, inv).
+
+    The sorted list is viewed as a matrix with ``stripes`` columns (row k holds
+    ranks k*g .. k*g+g-1), transposed, and flattened. perm[p] is the token at
+    position p of the new sequence; inv[perm[p]] = p.
+    """
+    s = np.asarray(s, dtype=np.int64)
+    n = s.shape[0]
+    if n % stripes != 0:
+        raise ValueError("sequence length must be a multiple of the stripe count")
+    perm = s.reshape(n // stripes, stripes).T.reshape(-1).copy()
+    inv = np.empty(n, np.int64)
+    inv[perm] = np.arange(n)
+    return perm, inv
+
+
+def routed_count(mlp_density: float, n_real: int) -> int:
+    """K = floor(d * n_real + 1/2) in double precision, at least 1 (d given as fp32)."""
+    d = float(np.float32(mlp_density))
+    return max(1, int(math.floor(d * n_real + 0.5)))
+
+
+def routed_tokens(s: np.ndarray, token_map_row: np.ndarray, mlp_density: float) -> np.ndarray:
+    """Image token ids of the keep-set of one segment, ascending.
+
+    The keep-set is the first K entries of the importance order; pad slots sort
+    last and are never taken because K <= number of real slots.
+    """
+    n_real = int((token_map_row >= 0).sum())
+    k = routed_count(mlp_density, n_real)
+    return np.sort(token_map_row[s[:k]])
+
+
+# ----------------------------------------------------------------------------
+# Static pattern
+# ----------------------------------------------------------------------------
+
+def position_keep(n: int, stripes: int, block: int, global_tokens: int, radius: int) -> np.ndarray:
+    """Kept (query position, key position) pairs of the stripe-sorted sequence, [n, n] bool.
+
+    Position p lies in stripe a = p // S at offset u = p % S (S = n / stripes), in
+    stripe-local block j = u // block. A pair is kept when the blocks are within
+    ``radius`` of each other (the band, the same in every stripe pair), or when either
+    position is global (stripe 0, u < global_tokens).
+    """
+    S = n // stripes
+    p = np.arange(n)
+    u = p % S
+    a = p // S
+    j = u // block
+    glob = (a == 0) & (u < global_tokens)
+    band = np.abs(j[:, None] - j[None, :]) <= radius
+    return band | glob[:, None] | glob[None, :]
+
+
+def band_radius(n: int, stripes: int, block: int, global_tokens: int, attn_density: float) -> int:
+    """Smallest radius r >= 0 whose kept share of the n x n map reaches the density."""
+    d = float(np.float32(attn_density))
+    S = n // stripes
+    last = (S - 1) // block
+    for r in range(last + 1):
+        kept = int(position_keep(n, stripes, block, global_tokens, r).sum())
+        if kept / float(n * n) >= d:
+            return r
+    return last
+
+
+def token_mask(inv: np.ndarray, stripes: int, block: int, global_tokens: int, radius: int) -> np.ndarray:
+    """The pattern in original token order: M[i, k] = keep(inv[i], inv[k])."""
+    n = inv.shape[0]
+    keep = position_keep(n, stripes, block, global_tokens, radius)
+    return keep[np.ix_(inv, inv)]
+
+
+# ----------------------------------------------------------------------------
+# Block arithmetic (fp64)
+# ----------------------------------------------------------------------------
+
+def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
+                     scale: float) -> np.ndarray:
+    """softmax(q k^T * scale) v with pairs outside ``mask`` removed (score -inf).
+
+    q, k, v: [n, D]; mask: [n, n] bool (every row keeps at least one key).
+    """
+    s = (q.astype(np.float64) @ k.astype(np.float64).T) * scale
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return (e / e.sum(axis=1, keepdims=True)) @ v.astype(np.float64)
+
+
+def layer_norm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """LayerNorm over the last axis with the biased variance."""
+    x = x.astype(np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * gamma.astype(np.float64) + beta.astype(np.float64)
+
+
+def gelu(z: np.ndarray) -> np.ndarray:
+    """GELU with the exact Gaussian CDF: z * (1 + erf(z / sqrt 2)) / 2."""
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def _linear(x, w, b):
+    return x @ w.astype(np.float64).T + b.astype(np.float64)
+
+
+def routed_mlp(x: np.ndarray, routed: np.ndarray, w: dict) -> np.ndarray:
+    """Residual-Consistency MLP on rows of x [rows, C]: only routed rows change.
+
+    x2[t] = x[t] + fc2(GELU(fc1(LN2(x[t])))) for t in routed; x2[t] = x[t] otherwise.
+    """
+    out = x.astype(np.float64).copy()
+    xr = out[routed]
+    h = gelu(_linear(layer_norm(xr, w["ln2_g"], w["ln2_b"]), w["w1"], w["b1"]))
+    out[routed] = xr + _linear(h, w["w2"], w["b2"])
+    return out
+
+
+def block_forward(x: np.ndarray, imp: np.ndarray, w: dict, cfg, radius: int = None,
+                  return_parts: bool = False):
+    """One SparseSAM encoder block on x [batch, gh, gw, C] (fp32 in, fp64 out).
+
+    imp: [batch, gh*gw] fp32 importance. The pattern and keep-set come from
+    ``cfg`` (window, stripes, block, global_tokens, band_radius, attn_density,
+    mlp_density, heads, head_dim). Attention is dense with an explicit mask in the
+    original token order, per segment; window pad slots carry h = 0 as keys and
+    queries and their outputs are dropped.
+    """
+    b, gh, gw, C = x.shape
+    H, D = cfg.heads, cfg.head_dim
+    tmap = segments_for_image(gh, gw, cfg.window)
+    n = tmap.shape[1]
+    if radius is None:
+        radius = cfg.band_radius if cfg.band_radius >= 0 else band_radius(
+            n, cfg.stripes, cfg.block, cfg.global_tokens, cfg.attn_density)
+    scale = D ** -0.5
+    xf = x.reshape(b, gh * gw, C).astype(np.float64)
+    out = np.empty_like(xf)
+    parts = {"perm": [], "inv": [], "routed": [], "radius": radius}
+    for i in range(b):
+        h = layer_norm(xf[i], w["ln1_g"], w["ln1_b"])
+        attn_out = np.zeros((gh * gw, C))
+        routed_img = []
+        for seg in range(tmap.shape[0]):
+            row = tmap[seg]
+            real = row >= 0
+            simp = segment_importance(imp[i], row)
+            s = descending_order(simp)
+            perm, inv = stripe_sort(s, cfg.stripes)
+            parts["perm"].append(perm)
+            parts["inv"].append(inv)
+            routed_img.append(routed_tokens(s, row, cfg.mlp_density))
+            hs = np.zeros((n, C))
+            hs[real] = h[row[real]]
+            qkv = _linear(hs, w["w_qkv"], w["b_qkv"])
+            mask = token_mask(inv, cfg.stripes, cfg.block, cfg.global_tokens, radius)
+            o = np.empty((n, C))
+            for hd in range(H):
+                q = qkv[:, hd * D:(hd + 1) * D]
+                k = qkv[:, C + hd * D:C + (hd + 1) * D]
+                v = qkv[:, 2 * C + hd * D:2 * C + (hd + 1) * D]
+                o[:, hd * D:(hd + 1) * D] = masked_attention(q, k, v, mask, scale)
+            attn_out[row[real]] = o[real]
+        x1 = xf[i] + _linear(attn_out, w["w_proj"], w["b_proj"])
+        routed = np.sort(np.concatenate(routed_img))
+        parts["routed"].append(routed + i * gh * gw)
+        out[i] = routed_mlp(x1, routed, w)
+    out = out.reshape(b, gh, gw, C)
+    if return_parts:
+        return out, parts
+    return out
+
+
+def encoder_forward(x: np.ndarray, imp: np.ndarray, layer_weights: list, global_layers: list,
+                    cfg_global, cfg_window):
+    """A stack of blocks: global-attention blocks at ``global_layers``, windowed elsewhere.
+
+    Each block recomputes nothing of the ordering that depends on activations: the
+    permutation depends on the image only, so every block of a type sees the same one.
+    """
+    h = x.astype(np.float64)
+    for l, w in enumerate(layer_weights):
+        cfg = cfg_global if l in global_layers else cfg_window
+        h = block_forward(h, imp, w, cfg)
+    return h
