@@ -1,0 +1,306 @@
+"""Benchmark of the SparseSAM encoder-block hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: Sobel importance,
+stripe-sort permutation and keep-set, then one SparseSAM block (gathered LayerNorm,
+QKV, block-sparse attention, projection with residual scatter, routed MLP), on the
+SAM ViT-B global-attention workload (64 x 64 tokens, C 768, 12 heads x 64, MLP
+3072, batch 1, attention and MLP density 0.4). Inputs are resident in HBM before
+timing starts.
+
+Prints ONE JSON line (rank 0). Extra fields report the attention and MLP kernels'
+TFLOP/s on the computed work (the kept tiles and routed tokens only), the same at
+density 0.3, the dense comparators (this library at density 1.0 and a PyTorch eager
+bf16 dense block) and the CPU oracle timed on this host on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--profile-only]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+METRIC = "SparseSAM block tokens/s + attn/MLP TFLOP/s (% bf16 peak) at density 0.4/0.3"
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attention_flops(plan):
+    """4 * B^2 * D per kept tile per head (2 for Q K^T, 2 for P V), per segment."""
+    info = plan.info
+    return 4.0 * info["pairs_kept"] * plan.desc.head_dim * plan.desc.heads
+
+
+def mlp_flops(plan, batch):
+    return 4.0 * plan.desc.channels * plan.desc.mlp_hidden * plan.info["routed_per_image"] * batch
+
+
+def block_flops(plan, batch):
+    C = plan.desc.channels
+    tokens = plan.info["seq_len"] * plan.info["segments_per_image"] * batch
+    segs = plan.info["segments_per_image"] * batch
+    return 8.0 * C * C * tokens + attention_flops(plan) * segs + mlp_flops(plan, batch)
+
+
+class Workload:
+    """Device-resident inputs, weights, outputs and workspace of one config."""
+
+    def __init__(self, cfg, dev, seed=0):
+        import numpy as np
+        import torch
+
+        import structured_sparse_vit_amd as ss
+        from synth import block_weights, synthetic_images, token_features
+
+        self.cfg = cfg
+        self.ss = ss
+        self.plan = ss.Plan.from_config(cfg)
+        self.img = torch.from_numpy(synthetic_images(cfg, seed)).to(dev)
+        self.x0 = torch.from_numpy(token_features(cfg, seed)).to(dev)
+        self.x = self.x0.clone()
+        self.w = ss.weights_to_device(block_weights(cfg, seed), self.plan)
+        info = self.plan.info
+        b = cfg.batch
+        self.imp = torch.empty(b, cfg.grid * cfg.grid, dtype=torch.float32, device=dev)
+        self.perm = torch.empty(b * info["segments_per_image"], info["seq_len"], dtype=torch.int32, device=dev)
+        self.inv = torch.empty_like(self.perm)
+        self.routed = torch.empty(b * info["routed_per_image"], dtype=torch.int32, device=dev)
+        self.ws = torch.empty(info["block_workspace_bytes"], dtype=torch.uint8, device=dev)
+        self.mlp_ws = torch.empty(info["mlp_workspace_bytes"], dtype=torch.uint8, device=dev)
+        self.np = np
+
+    def step(self):
+        ss = self.ss
+        ss.importance(self.img, self.cfg.patch, out=self.imp)
+        ss.permute(self.plan, self.imp, out=(self.perm, self.inv, self.routed))
+        ss.block(self.plan, self.w, self.x, self.perm, self.routed, workspace=self.ws)
+
+    def attn_operands(self, seed=1):
+        """Random q, k, vt and an output buffer in the layout sparsesam_attn takes."""
+        import torch
+        p = self.plan
+        info = p.info
+        segs = self.cfg.batch * info["segments_per_image"]
+        n, H, D = info["seq_len"], p.desc.heads, p.desc.head_dim
+        n_pad = (n + 7) // 8 * 8
+        g = torch.Generator(device=self.x.device).manual_seed(seed)
+        dt = p.torch_dtype
+        q = torch.randn(segs, H, n, D, generator=g, device=self.x.device).to(dt)
+        k = torch.randn(segs, H, n, D, generator=g, device=self.x.device).to(dt)
+        vt = torch.randn(segs, H, D, n_pad, generator=g, device=self.x.device).to(dt)
+        o = torch.empty(segs, n, H * D, dtype=dt, device=self.x.device)
+        return q, k, vt, o
+
+
+def time_region(fn, iters, warmup):
+    """Average milliseconds of fn() measured with HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(iters):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def torch_dense_block_ms(cfg, dev, iters=20):
+    """PyTorch eager bf16 dense block (SDPA + F.linear) on the same shapes, in ms."""
+    import torch
+    import torch.nn.functional as F
+    from synth import block_weights, token_features
+
+    w = {k: torch.from_numpy(v).to(dev) for k, v in block_weights(cfg).items()}
+    for k in ("w_qkv", "w_proj", "w1", "w2", "b_qkv", "b_proj", "b1", "b2"):
+        w[k] = w[k].to(torch.bfloat16)
+    x = torch.from_numpy(token_features(cfg)).to(dev).view(cfg.batch, -1, cfg.channels)
+    H, D, C = cfg.heads, cfg.head_dim, cfg.channels
+
+    def run():
+        h = F.layer_norm(x, (C,), w["ln1_g"], w["ln1_b"], eps=1e-6).to(torch.bfloat16)
+        qkv = F.linear(h, w["w_qkv"], w["b_qkv"])
+        q, k, v = qkv.view(cfg.batch, -1, 3, H, D).permute(2, 0, 3, 1, 4).contiguous().unbind(0)
+        o = F.scaled_dot_product_attention(q, k, v).transpose(1, 2).reshape(cfg.batch, -1, C)
+        x1 = x + F.linear(o, w["w_proj"], w["b_proj"]).float()
+        h2 = F.layer_norm(x1, (C,), w["ln2_g"], w["ln2_b"], eps=1e-6).to(torch.bfloat16)
+        return x1 + F.linear(F.gelu(F.linear(h2, w["w1"], w["b1"])), w["w2"], w["b2"]).float()
+
+    with torch.no_grad():
+        return time_region(run, iters, 3)
+
+
+def cpu_baseline(cfg, budget_s=25.0):
+    """The oracle, as it stands, on a bounded sample of the same workload on this host."""
+    import numpy as np
+
+    import oracle
+    from synth import block_weights, synthetic_images, token_features
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    imgs = synthetic_images(cfg)
+    x = token_features(cfg)
+    w = block_weights(cfg)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        imp = np.stack([oracle.importance(im, cfg.patch) for im in imgs])
+        oracle.block_forward(x, imp, w, cfg)
+        done += 1
+        if time.perf_counter() - t0 > budget_s / 2 or done >= 3:
+            break
+    dt = (time.perf_counter() - t0) / done
+    tokens = cfg.batch * cfg.grid * cfg.grid
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d full step(s) of the same workload (importance + permutation + one block, dense "
+                      "attention with an explicit mask, fp64 numpy), %.2f s each" % (done, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--profile-only", action="store_true", help="run the steps only (for rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the data-parallel "
+              "split is by image, with no communication; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from synth import get_config
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = get_config(args.config)
+    _log("workload", cfg)
+    wl = Workload(cfg, dev)
+
+    # timed region: K full steps
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        wl.step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    _log("step %.4f ms (events), wall %.4f ms" % (ms, wall * 1e3 / args.steps))
+    if args.profile_only:
+        return
+
+    ss = wl.ss
+    plan = wl.plan
+    tokens = cfg.batch * cfg.grid * cfg.grid
+    # per-kernel: attention (dominant kernel) and routed MLP, same launch configuration as in the block
+    q, k, vt, o = wl.attn_operands()
+    segs = cfg.batch * plan.info["segments_per_image"]
+    attn_ms = time_region(lambda: ss.attn(plan, q, k, vt, out=o), 50, 5)
+    attn_tf = attention_flops(plan) * segs / (attn_ms * 1e-3) / 1e12
+    xr = wl.x.view(-1, cfg.channels)
+    mlp_ms = time_region(lambda: ss.mlp(plan, xr, wl.routed, wl.w["ln2_g"], wl.w["ln2_b"], wl.w["w1"], wl.w["b1"],
+                                        wl.w["w2"], wl.w["b2"], workspace=wl.mlp_ws), 50, 5)
+    mlp_tf = mlp_flops(plan, cfg.batch) / (mlp_ms * 1e-3) / 1e12
+    imp_ms = time_region(lambda: ss.importance(wl.img, cfg.patch, out=wl.imp), 50, 5)
+    perm_ms = time_region(lambda: ss.permute(plan, wl.imp, out=(wl.perm, wl.inv, wl.routed)), 50, 5)
+    block_ms = time_region(lambda: ss.block(plan, wl.w, wl.x, wl.perm, wl.routed, workspace=wl.ws), 50, 5)
+    _log("attn %.4f ms (%.1f TFLOP/s), mlp %.4f ms (%.1f TFLOP/s), importance %.4f ms, permute %.4f ms, block %.4f ms"
+         % (attn_ms, attn_tf, mlp_ms, mlp_tf, imp_ms, perm_ms, block_ms))
+
+    extra = {}
+    # the same workload at density 0.3
+    cfg3 = cfg.with_(attn_density=0.3, mlp_density=0.3)
+    wl3 = Workload(cfg3, dev)
+    wl3.step()
+    q3, k3, vt3, o3 = wl3.attn_operands()
+    a3 = time_region(lambda: ss.attn(wl3.plan, q3, k3, vt3, out=o3), 50, 5)
+    xr3 = wl3.x.view(-1, cfg.channels)
+    m3 = time_region(lambda: ss.mlp(wl3.plan, xr3, wl3.routed, wl3.w["ln2_g"], wl3.w["ln2_b"], wl3.w["w1"],
+                                    wl3.w["b1"], wl3.w["w2"], wl3.w["b2"], workspace=wl3.mlp_ws), 50, 5)
+    s3 = time_region(wl3.step, 30, 5)
+    extra["density_0.3"] = {
+        "step_ms": round(s3, 5), "tokens_per_s": round(tokens / (s3 * 1e-3), 1),
+        "realised_attn_density": wl3.plan.info["realised_density"],
+        "attn_ms": round(a3, 5), "attn_tflops": round(attention_flops(wl3.plan) * segs / (a3 * 1e-3) / 1e12, 2),
+        "mlp_ms": round(m3, 5), "mlp_tflops": round(mlp_flops(wl3.plan, cfg.batch) / (m3 * 1e-3) / 1e12, 2),
+    }
+    extra["density_0.3"]["attn_pct_peak"] = round(100 * extra["density_0.3"]["attn_tflops"] / PEAK_BF16_TFLOPS, 2)
+    extra["density_0.3"]["mlp_pct_peak"] = round(100 * extra["density_0.3"]["mlp_tflops"] / PEAK_BF16_TFLOPS, 2)
+    del wl3
+
+    if not args.no_dense:
+        cfgd = cfg.with_(attn_density=1.0, mlp_density=1.0)
+        wld = Workload(cfgd, dev)
+        dense_lib = time_region(wld.step, 30, 5)
+        qd, kd, vtd, od = wld.attn_operands()
+        dense_attn = time_region(lambda: ss.attn(wld.plan, qd, kd, vtd, out=od), 30, 5)
+        del wld
+        dense_torch = torch_dense_block_ms(cfg, dev)
+        best = min(dense_lib, dense_torch)
+        extra["dense"] = {"library_step_ms": round(dense_lib, 5), "library_attn_ms": round(dense_attn, 5),
+                          "torch_eager_block_ms": round(dense_torch, 5),
+                          "speedup_vs_faster_dense": round(best / ms, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg)
+        _log("cpu baseline", cpu)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "grid": cfg.grid, "channels": cfg.channels, "heads": cfg.heads,
+                   "head_dim": cfg.head_dim, "mlp_hidden": cfg.mlp_hidden, "batch": cfg.batch,
+                   "attn_density": cfg.attn_density, "mlp_density": cfg.mlp_density,
+                   "realised_attn_density": plan.info["realised_density"],
+                   "routed_tokens": plan.info["routed_per_image"] * cfg.batch},
+        "roofline": {"bound": "mfma", "kernel": "attn_mfma64_kernel", "achieved": round(attn_tf, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "launch_ms": round(attn_ms, 5),
+                     "algorithmic_flop": attention_flops(plan) * segs},
+        "cpu_baseline": cpu,
+        "attn_tflops": round(attn_tf, 2),
+        "attn_pct_peak": round(100 * attn_tf / PEAK_BF16_TFLOPS, 2),
+        "mlp_tflops": round(mlp_tf, 2),
+        "mlp_pct_peak": round(100 * mlp_tf / PEAK_BF16_TFLOPS, 2),
+        "block_tflops": round(block_flops(plan, cfg.batch) / (block_ms * 1e-3) / 1e12, 2),
+        "kernel_ms": {"importance": round(imp_ms, 5), "permute": round(perm_ms, 5), "block": round(block_ms, 5),
+                      "attention": round(attn_ms, 5), "mlp": round(mlp_ms, 5)},
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+/*
+ * sparsesam.h -- C ABI of the SparseSAM encoder-block hot path on MI355X (gfx950).
+ *
+ * The method: "SparseSAM: Structured Sparsification of Activations in Segment
+ * Anything Models" (arXiv 2605.17633). Stripe-Sort Attention orders the tokens
+ * of an image by Sobel gradient magnitude, stripe-sorts them, and runs attention
+ * over a static banded block pattern; the Residual-Consistency MLP runs the MLP
+ * only on the most important tokens and passes the others through the residual.
+ * The steps are described in "Technische Samenvatting: SparseSAM" (gist.science),
+ * section Methodologie, parts 1 (Stripe-Sort Attention) and 2 (Residual-Consistency
+ * MLP), and in the arXiv abstract.
+ *
+ * Conventions for every call below.
+ *  - Pointers are device pointers unless the comment says "host".
+ *  - The caller owns every buffer; the library never frees caller memory and the
+ *    five compute calls never allocate: scratch memory comes from the caller's
+ *    workspace, sized by sparsesam_plan_get_info().
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Compute
+ *    calls only enqueue work on it and never synchronise the host.
+ *  - Host-side validation runs before any launch; a call that returns an error has
+ *    enqueued nothing and written nothing. Launch failures return SPARSESAM_ERR_HIP.
+ *    Device faults surface at the caller's next synchronisation, as for any HIP call.
+ *  - sparsesam_last_error() returns a thread-local message for the last failure.
+ *  - Matrices are row-major. Weight matrices are [out, in] (the layout of a
+ *    torch.nn.Linear weight). Biases and LayerNorm parameters are always fp32. The
+ *    residual stream x is always fp32.
+ *  - A plan is immutable after creation and may be shared across threads and streams.
+ *    Its device copy lives on the device that was current at creation; compute calls
+ *    must run with that device current.
+ */
+#ifndef SPARSESAM_H
+#define SPARSESAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sparsesam_status {
+  SPARSESAM_OK = 0,
+  SPARSESAM_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, inconsistent shapes */
+  SPARSESAM_ERR_UNSUPPORTED = 2,      /* valid request that this build has no kernel for */
+  SPARSESAM_ERR_WORKSPACE = 3,        /* workspace smaller than the plan requires */
+  SPARSESAM_ERR_OUT_OF_MEMORY = 4,    /* host or device allocation in plan creation failed */
+  SPARSESAM_ERR_HIP = 5,              /* a HIP runtime call or launch failed */
+  SPARSESAM_ERR_NO_DEVICE = 6         /* the plan has no device copy (no GPU, or another device) */
+} sparsesam_status;
+
+typedef enum sparsesam_dtype {
+  SPARSESAM_F32 = 0,  /* fp32 weights and activations everywhere (small configs, exactness) */
+  SPARSESAM_BF16 = 1  /* bf16 weights and matrix-core operands, fp32 accumulation and residual */
+} sparsesam_dtype;
+
+typedef struct sparsesam_plan* sparsesam_plan_t;
+
+/*
+ * What one plan describes: the segments of an image (one global segment of
+ * grid_h*grid_w tokens, or window x window windows over the grid padded up to
+ * multiples of `window`), the stripe-sort and its static attention pattern, the
+ * MLP keep-set size and the block's dimensions.
+ *
+ * Pattern ("Technische Samenvatting: SparseSAM", Methodologie, 1. Stripe-Sort
+ * Attention, static-pattern bullet: a 4 x 4 mosaic of sub-maps with a banded
+ * diagonal plus a small global keep-set). Reading used here: a segment of N tokens
+ * is stripe-sorted into g = `stripes` stripes of S = N/g positions; position p is in
+ * stripe a = p / S at offset u = p % S, in stripe-local block j = u / B (B = `block`,
+ * the last block of a stripe may be shorter). The pair (p, q) is kept when
+ * |j_p - j_q| <= r, or when p or q is global (a == 0 and u < G, G = `global_tokens`).
+ * r = `band_radius`, or, when it is -1, the smallest r whose kept share of the
+ * N x N map reaches `attn_density`.
+ *
+ * Keep-set (same page, 2. Residual-Consistency MLP): per segment the K most important
+ * real tokens, K = floor(mlp_density * n_real + 0.5) computed in double, at least 1.
+ */
+typedef struct sparsesam_plan_desc {
+  int32_t grid_h, grid_w;  /* token grid of one image (64 x 64 for SAM at 1024 px) */
+  int32_t window;          /* 0: one global segment per image; w > 0: w x w windows */
+  int32_t stripes;         /* g >= 1; N must be a multiple of g */
+  int32_t block;           /* B: pattern tile in tokens, 1..S */
+  int32_t global_tokens;   /* G: 0 <= G <= S */
+  int32_t band_radius;     /* r >= 0, or -1 to derive r from attn_density */
+  float attn_density;      /* in (0, 1] */
+  float mlp_density;       /* in (0, 1] */
+  int32_t channels;        /* C = heads * head_dim */
+  int32_t heads;
+  int32_t head_dim;
+  int32_t mlp_hidden;
+  int32_t max_batch;       /* largest batch a call will pass; sizes the workspace */
+  int32_t dtype;           /* sparsesam_dtype */
+} sparsesam_plan_desc;
+
+typedef struct sparsesam_plan_info {
+  int32_t seq_len;              /* N: tokens per segment, pads included */
+  int32_t segments_per_image;   /* 1, or the number of windows */
+  int32_t band_radius;          /* r in use */
+  int32_t tiles_per_stripe;     /* ceil(S / B) */
+  int32_t tiles;                /* T = g * tiles_per_stripe (query tiles = key tiles) */
+  int32_t tiles_kept;           /* kept (query tile, key tile) pairs of one segment */
+  int64_t pairs_kept;           /* kept token pairs of one segment */
+  double realised_density;      /* pairs_kept / N^2 */
+  int32_t routed_per_image;     /* keep-set size summed over the segments of one image */
+  int32_t reserved0;
+  size_t block_workspace_bytes; /* workspace sparsesam_block needs at max_batch */
+  size_t mlp_workspace_bytes;   /* workspace sparsesam_mlp needs for max_batch images' keep-sets */
+  int32_t has_device_copy;      /* 1 when the plan can run on the current device */
+  int32_t device;               /* HIP device of the device copy, -1 when none */
+} sparsesam_plan_info;
+
+/* Plan lifecycle. sparsesam_plan_create validates the description, builds the
+ * static tile list on the host and copies it to the current device when one is
+ * present (host-only plans can be queried but not run). */
+sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc /* host */, sparsesam_plan_t* out /* host */);
+sparsesam_status sparsesam_plan_get_info(sparsesam_plan_t plan, sparsesam_plan_info* info /* host */);
+/* The kept key tiles of every query tile, in CSR form: row_ptr[T + 1] and
+ * col_idx[tiles_kept] (host buffers the caller sizes from the info). Tile t covers
+ * stripe t / tiles_per_stripe, stripe-local block t % tiles_per_stripe. */
+sparsesam_status sparsesam_plan_tile_list(sparsesam_plan_t plan, int32_t* row_ptr /* host */, int32_t* col_idx /* host */);
+void sparsesam_plan_destroy(sparsesam_plan_t plan);
+
+const char* sparsesam_status_string(sparsesam_status status);
+const char* sparsesam_last_error(void);
+
+/*
+ * (1) Token importance: per-pixel L2 magnitude of the unnormalised Sobel gradient
+ * with zero padding, averaged over each patch x patch tile ("Technische
+ * Samenvatting: SparseSAM", Methodologie, 1. Stripe-Sort Attention, the
+ * gradient-based ordering bullet: a parameter-free Sobel operator measures local
+ * information density).
+ *   img [batch, height, width] fp32 grayscale; imp [batch, (height/patch) * (width/patch)]
+ *   fp32, tokens in raster order. height and width must be multiples of patch.
+ * Every operation rounds once to fp32 in a fixed order, so the result is exactly
+ * reproducible: gx = ((P[y-1][x+1] + 2P[y][x+1]) + P[y+1][x+1]) - ((P[y-1][x-1] +
+ * 2P[y][x-1]) + P[y+1][x-1]), gy likewise with rows, m = sqrt(gx*gx + gy*gy) correctly
+ * rounded; each tile row is summed left to right, the row sums top to bottom, and
+ * the total divided by patch^2.
+ */
+sparsesam_status sparsesam_importance(const float* img, int32_t batch, int32_t height, int32_t width,
+                                      int32_t patch, float* imp, void* stream);
+
+/*
+ * (2) Stripe-sort permutation and keep-set of every segment of `batch` images
+ * (same page, stripe-sort bullet; 2. Residual-Consistency MLP, token routing).
+ *   imp    [batch, grid_h * grid_w] fp32 (window pads get importance -1).
+ *   perm   [batch * segments_per_image, N] int32: segment-local slot at each position
+ *          of the stripe-sorted sequence (slot = token index in raster order within the
+ *          global grid or within the window).
+ *   inv    [batch * segments_per_image, N] int32: inv[perm[p]] = p.
+ *   routed [batch * routed_per_image] int32: global row ids (image * grid_h * grid_w +
+ *          token) of the keep-set, ascending.
+ * Order: importance descending, ties by lower slot, -0.0 == +0.0, NaN last. The
+ * stripe-sort reads the sorted list as an (N/g) x g matrix, transposes it and
+ * flattens it: perm[p] = sorted[g * (p % S) + p / S]. All outputs are integers and
+ * exactly determined.
+ */
+sparsesam_status sparsesam_permute(sparsesam_plan_t plan, const float* imp, int32_t batch, int32_t* perm,
+                                   int32_t* inv, int32_t* routed, void* stream);
+
+/*
+ * (3) Block-sparse attention over the plan's static pattern, on already
+ * stripe-sorted tokens (same page, static-pattern bullet: the pattern is fixed, so
+ * no mask is built at run time). For each segment s and head h:
+ *   o[s, p, h, :] = sum_q softmax_q(scale * <q[s,h,p,:], k[s,h,q,:]>) v[s,h,q,:]
+ * over the kept positions q of row p only.
+ *   q, k [segments, heads, N, head_dim]       (plan dtype)
+ *   vt   [segments, heads, head_dim, N_pad]   (plan dtype; V transposed, N_pad = N
+ *                                              rounded up to a multiple of 8; columns
+ *                                              N..N_pad-1 are never read)
+ *   o    [segments, N, heads * head_dim]      (plan dtype)
+ * `scale` is usually head_dim^-0.5. bf16 plans need head_dim 64 or 80 and either
+ * B = 64 with S a multiple of 64 (global segments) or N <= 256 (windows).
+ */
+sparsesam_status sparsesam_attn(sparsesam_plan_t plan, int32_t segments, const void* q, const void* k,
+                                const void* vt, void* o, float scale, void* stream);
+
+/*
+ * (4) Residual-Consistency MLP, in place on the fp32 residual stream (same page,
+ * 2. Residual-Consistency MLP: the MLP runs on the keep-set only; every other token
+ * passes through the residual unchanged). For each row t in routed:
+ *   x[t] += fc2(GELU(fc1(LayerNorm(x[t]))))   (exact-erf GELU, LayerNorm eps 1e-6)
+ * Rows not in `routed` are never read or written.
+ *   x [rows, C] fp32; routed [routed_count] int32 distinct row ids in [0, rows);
+ *   ln_g, ln_b [C] fp32; w1 [hidden, C], w2 [C, hidden] (plan dtype); b1 [hidden],
+ *   b2 [C] fp32. routed_count must not exceed max_batch * routed_per_image;
+ *   workspace >= mlp_workspace_bytes.
+ */
+sparsesam_status sparsesam_mlp(sparsesam_plan_t plan, float* x, int64_t rows, const int32_t* routed,
+                               int32_t routed_count, const float* ln_g, const float* ln_b, const void* w1,
+                               const float* b1, const void* w2, const float* b2, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Parameters of one pre-LN ViT block. Matrices in the plan dtype, [out, in]. */
+typedef struct sparsesam_block_weights {
+  const float* ln1_g;  /* [C] */
+  const float* ln1_b;  /* [C] */
+  const void* w_qkv;   /* [3C, C]: rows 0..C-1 give q, C..2C-1 k, 2C..3C-1 v; head h uses h*D..h*D+D-1 */
+  const float* b_qkv;  /* [3C] */
+  const void* w_proj;  /* [C, C] */
+  const float* b_proj; /* [C] */
+  const float* ln2_g;  /* [C] */
+  const float* ln2_b;  /* [C] */
+  const void* w1;      /* [hidden, C] */
+  const float* b1;     /* [hidden] */
+  const void* w2;      /* [C, hidden] */
+  const float* b2;     /* [C] */
+} sparsesam_block_weights;
+
+/*
+ * (5) One SparseSAM encoder block, in place on x [batch, grid_h, grid_w, C] fp32 in
+ * raster order, with the perm and routed outputs of sparsesam_permute for the same
+ * plan and images (one permutation set serves every block of a type: same page,
+ * closing paragraph of part 2):
+ *   h  = LayerNorm1(x) gathered into stripe-sorted order (window pads: h = 0)
+ *   qkv = h W_qkv^T + b_qkv
+ *   o  = sparse attention (3) per segment and head, scale head_dim^-0.5
+ *   x  = x + o W_proj^T + b_proj          scattered back to raster order, pads dropped
+ *   x  = the routed MLP (4) on the keep-set
+ * workspace >= block_workspace_bytes; batch <= max_batch.
+ */
+sparsesam_status sparsesam_block(sparsesam_plan_t plan, const sparsesam_block_weights* weights /* host */,
+                                 float* x, int32_t batch, const int32_t* perm, const int32_t* routed,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSESAM_H */

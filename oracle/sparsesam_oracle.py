@@ -165,8 +165,8 @@ def segments_for_image(grid_h: int, grid_w: int, window: int) -> np.ndarray:
 
 
 def segment_importance(imp: np.ndarray, token_map: np.ndarray) -> np.ndarray:
-    """Importance of each segment slot; pad slots get -1.0 (below every magnitude)."""
-    out = np.where(token_map >= 0, imp[np.maximum(token_map, 0)], F32(-1.0))
+    """Importance of each segment slot (pad slots read as 0; their order is set apart)."""
+    out = np.where(token_map >= 0, imp[np.maximum(token_map, 0)], F32(0.0))
     return out.astype(F32)
 
 
@@ -174,24 +174,28 @@ def segment_importance(imp: np.ndarray, token_map: np.ndarray) -> np.ndarray:
 # Ordering and stripe-sort
 # ----------------------------------------------------------------------------
 
-def descending_order(imp: np.ndarray) -> np.ndarray:
-    """Token ids sorted by importance, highest first, written as a rank count.
+def descending_order(imp: np.ndarray, valid: np.ndarray = None) -> np.ndarray:
+    """Slot ids sorted by importance, highest first, written as a rank count.
 
-    Token j precedes token i when imp[j] > imp[i], or when they are equal and j < i.
+    Slot j precedes slot i when imp[j] > imp[i], or when they are equal and j < i.
     -0.0 and +0.0 are equal; a NaN is below every number and equal to every NaN.
-    rank[i] = number of tokens preceding i; s[rank[i]] = i.
+    Slots with valid == False (window padding) come after every valid slot, in
+    index order. rank[i] = number of slots preceding i; s[rank[i]] = i.
     """
     v = np.asarray(imp, dtype=F32).astype(np.float64)
     v = np.where(v == 0.0, 0.0, v)
     nan = np.isnan(v)
     n = v.shape[0]
+    ok = np.ones(n, bool) if valid is None else np.asarray(valid, bool)
     idx = np.arange(n)
     vi, vj = v[:, None], v[None, :]
     ni, nj = nan[:, None], nan[None, :]
+    oi, oj = ok[:, None], ok[None, :]
     with np.errstate(invalid="ignore"):
         j_higher = (~nj) & (ni | (vj > vi))
         same = (ni & nj) | ((~ni) & (~nj) & (vj == vi))
-    precedes = j_higher | (same & (idx[None, :] < idx[:, None]))
+    by_value = j_higher | (same & (idx[None, :] < idx[:, None]))
+    precedes = (oj & ~oi) | (oj & oi & by_value) | (~oj & ~oi & (idx[None, :] < idx[:, None]))
     rank = precedes.sum(axis=1)
     s = np.empty(n, np.int64)
     s[rank] = idx
@@ -225,11 +229,13 @@ def routed_tokens(s: np.ndarray, token_map_row: np.ndarray, mlp_density: float) 
     """Image token ids of the keep-set of one segment, ascending.
 
     The keep-set is the first K entries of the importance order; pad slots sort
-    last and are never taken because K <= number of real slots.
+    after every real slot and K <= number of real slots, so none is taken.
     """
     n_real = int((token_map_row >= 0).sum())
     k = routed_count(mlp_density, n_real)
-    return np.sort(token_map_row[s[:k]])
+    picked = token_map_row[s[:k]]
+    assert (picked >= 0).all()
+    return np.sort(picked)
 
 
 # ----------------------------------------------------------------------------
@@ -348,7 +354,7 @@ def block_forward(x: np.ndarray, imp: np.ndarray, w: dict, cfg, radius: int = No
             row = tmap[seg]
             real = row >= 0
             simp = segment_importance(imp[i], row)
-            s = descending_order(simp)
+            s = descending_order(simp, valid=real)
             perm, inv = stripe_sort(s, cfg.stripes)
             parts["perm"].append(perm)
             parts["inv"].append(inv)

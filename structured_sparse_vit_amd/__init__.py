@@ -1,0 +1,226 @@
+"""SparseSAM encoder-block hot path on MI355X: Python binding of libsparsesam.so.
+
+Argument marshalling only: every step of the path runs in the HIP kernels behind
+the C ABI in include/sparsesam.h. torch provides device memory and the current
+stream. If the library is not built, every call raises.
+
+    plan = Plan.from_config(cfg)              # static pattern + sizes
+    imp = importance(img)                     # [b, H, W] fp32 -> [b, tokens]
+    perm, inv, routed = permute(plan, imp)    # stripe-sort + keep-set
+    block(plan, weights, x, perm, routed)     # one encoder block, in place on x
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import SPARSESAM_BF16, SPARSESAM_F32, SparseSAMError, check
+
+__all__ = ["Plan", "importance", "permute", "attn", "mlp", "block", "SparseSAMError", "library_path", "weights_to_device"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on a GPU" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+class Plan:
+    """Static description of one block type: segments, stripe-sort pattern, keep-set size."""
+
+    def __init__(self, grid_h, grid_w, window, stripes, block, global_tokens, band_radius, attn_density,
+                 mlp_density, channels, heads, head_dim, mlp_hidden, max_batch, dtype):
+        lib = _lib.load()
+        self._lib = lib
+        self.dtype = dtype
+        self.desc = _lib.PlanDesc(grid_h, grid_w, window, stripes, block, global_tokens, band_radius,
+                                  attn_density, mlp_density, channels, heads, head_dim, mlp_hidden, max_batch,
+                                  SPARSESAM_BF16 if dtype == "bf16" else SPARSESAM_F32)
+        h = ctypes.c_void_p()
+        check(lib.sparsesam_plan_create(ctypes.byref(self.desc), ctypes.byref(h)), "sparsesam_plan_create")
+        self._h = h
+        info = _lib.PlanInfo()
+        check(lib.sparsesam_plan_get_info(self._h, ctypes.byref(info)), "sparsesam_plan_get_info")
+        self.info = {f: getattr(info, f) for f, _ in _lib.PlanInfo._fields_ if f != "reserved0"}
+        self.device = torch.device("cuda", info.device) if info.has_device_copy else None
+
+    @classmethod
+    def from_config(cls, cfg, max_batch=None):
+        return cls(cfg.grid, cfg.grid, cfg.window, cfg.stripes, cfg.block, cfg.global_tokens, cfg.band_radius,
+                   cfg.attn_density, cfg.mlp_density, cfg.channels, cfg.heads, cfg.head_dim, cfg.mlp_hidden,
+                   max_batch or cfg.batch, cfg.dtype)
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def tile_list(self):
+        import numpy as np
+        rp = np.zeros(self.info["tiles"] + 1, np.int32)
+        ci = np.zeros(max(1, self.info["tiles_kept"]), np.int32)
+        check(self._lib.sparsesam_plan_tile_list(self._h, rp.ctypes.data_as(ctypes.c_void_p),
+                                                 ci.ctypes.data_as(ctypes.c_void_p)), "sparsesam_plan_tile_list")
+        return rp, ci[:self.info["tiles_kept"]]
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.sparsesam_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def importance(img, patch=16, out=None):
+    """Sobel-magnitude token importance: img [b, H, W] fp32 -> [b, (H/patch)*(W/patch)] fp32."""
+    lib = _lib.load()
+    if img.dim() != 3:
+        raise ValueError("img must be [batch, height, width]")
+    _need(img, "img", torch.float32)
+    b, H, W = img.shape
+    if out is None:
+        out = torch.empty(b, (H // patch) * (W // patch), dtype=torch.float32, device=img.device)
+    _need(out, "out", torch.float32, (b, (H // patch) * (W // patch)), img.device)
+    check(lib.sparsesam_importance(_ptr(img), b, H, W, patch, _ptr(out), _stream(img.device)),
+          "sparsesam_importance")
+    return out
+
+
+def permute(plan, imp, out=None):
+    """Stripe-sort permutation and keep-set: returns (perm, inv, routed), int32 on the device."""
+    lib = _lib.load()
+    tokens = plan.desc.grid_h * plan.desc.grid_w
+    _need(imp, "imp", torch.float32, device=plan.device)
+    if imp.dim() != 2 or imp.shape[1] != tokens:
+        raise ValueError("imp must be [batch, %d]" % tokens)
+    b = imp.shape[0]
+    n, segs, rpi = plan.info["seq_len"], plan.info["segments_per_image"], plan.info["routed_per_image"]
+    if out is None:
+        perm = torch.empty(b * segs, n, dtype=torch.int32, device=imp.device)
+        inv = torch.empty_like(perm)
+        routed = torch.empty(b * rpi, dtype=torch.int32, device=imp.device)
+    else:
+        perm, inv, routed = out
+    _need(perm, "perm", torch.int32, (b * segs, n), imp.device)
+    _need(inv, "inv", torch.int32, (b * segs, n), imp.device)
+    _need(routed, "routed", torch.int32, (b * rpi,), imp.device)
+    check(lib.sparsesam_permute(plan.handle, _ptr(imp), b, _ptr(perm), _ptr(inv), _ptr(routed),
+                                _stream(imp.device)), "sparsesam_permute")
+    return perm, inv, routed
+
+
+def attn(plan, q, k, vt, scale=None, out=None):
+    """Block-sparse attention on stripe-sorted tokens.
+
+    q, k [segments, heads, N, D]; vt [segments, heads, D, N_pad] -> o [segments, N, heads * D].
+    """
+    lib = _lib.load()
+    dt = plan.torch_dtype
+    H, D, n = plan.desc.heads, plan.desc.head_dim, plan.info["seq_len"]
+    n_pad = (n + 7) // 8 * 8
+    segs = q.shape[0]
+    _need(q, "q", dt, (segs, H, n, D), plan.device)
+    _need(k, "k", dt, (segs, H, n, D), plan.device)
+    _need(vt, "vt", dt, (segs, H, D, n_pad), plan.device)
+    if out is None:
+        out = torch.empty(segs, n, H * D, dtype=dt, device=q.device)
+    _need(out, "out", dt, (segs, n, H * D), plan.device)
+    scale = D ** -0.5 if scale is None else float(scale)
+    check(lib.sparsesam_attn(plan.handle, segs, _ptr(q), _ptr(k), _ptr(vt), _ptr(out), scale, _stream(q.device)),
+          "sparsesam_attn")
+    return out
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is None:
+        return torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", torch.uint8, device=device)
+    return workspace
+
+
+def mlp(plan, x, routed, ln_g, ln_b, w1, b1, w2, b2, workspace=None):
+    """Residual-Consistency MLP in place on x [rows, C] fp32 for the rows in `routed`."""
+    lib = _lib.load()
+    dt = plan.torch_dtype
+    C, Hm = plan.desc.channels, plan.desc.mlp_hidden
+    x2 = x.view(-1, C)
+    _need(x, "x", torch.float32, device=plan.device)
+    _need(routed, "routed", torch.int32, device=plan.device)
+    _need(ln_g, "ln_g", torch.float32, (C,), plan.device)
+    _need(ln_b, "ln_b", torch.float32, (C,), plan.device)
+    _need(w1, "w1", dt, (Hm, C), plan.device)
+    _need(b1, "b1", torch.float32, (Hm,), plan.device)
+    _need(w2, "w2", dt, (C, Hm), plan.device)
+    _need(b2, "b2", torch.float32, (C,), plan.device)
+    ws = _workspace(plan.info["mlp_workspace_bytes"], x.device, workspace)
+    check(lib.sparsesam_mlp(plan.handle, _ptr(x), x2.shape[0], _ptr(routed), routed.numel(), _ptr(ln_g), _ptr(ln_b),
+                            _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(ws), ws.numel(), _stream(x.device)),
+          "sparsesam_mlp")
+    return x
+
+
+_WEIGHT_NAMES = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_proj", "b_proj", "ln2_g", "ln2_b", "w1", "b1", "w2", "b2")
+_MATRICES = ("w_qkv", "w_proj", "w1", "w2")
+
+
+def weights_to_device(w, plan, device=None):
+    """Host arrays (numpy or torch) -> device tensors in the plan's layout and dtypes."""
+    device = device or plan.device
+    out = {}
+    for name in _WEIGHT_NAMES:
+        t = torch.as_tensor(w[name])
+        dt = plan.torch_dtype if name in _MATRICES else torch.float32
+        out[name] = t.to(device=device, dtype=dt).contiguous()
+    return out
+
+
+def block(plan, weights, x, perm, routed, workspace=None):
+    """One SparseSAM encoder block in place on x [batch, grid_h, grid_w, C] fp32."""
+    lib = _lib.load()
+    dt = plan.torch_dtype
+    C, Hm = plan.desc.channels, plan.desc.mlp_hidden
+    gh, gw = plan.desc.grid_h, plan.desc.grid_w
+    _need(x, "x", torch.float32, device=plan.device)
+    b = x.shape[0]
+    if tuple(x.shape) != (b, gh, gw, C):
+        raise ValueError("x must be [batch, %d, %d, %d]" % (gh, gw, C))
+    shapes = {"ln1_g": (C,), "ln1_b": (C,), "w_qkv": (3 * C, C), "b_qkv": (3 * C,), "w_proj": (C, C),
+              "b_proj": (C,), "ln2_g": (C,), "ln2_b": (C,), "w1": (Hm, C), "b1": (Hm,), "w2": (C, Hm), "b2": (C,)}
+    for name in _WEIGHT_NAMES:
+        _need(weights[name], name, dt if name in _MATRICES else torch.float32, shapes[name], plan.device)
+    n, segs, rpi = plan.info["seq_len"], plan.info["segments_per_image"], plan.info["routed_per_image"]
+    _need(perm, "perm", torch.int32, (b * segs, n), plan.device)
+    _need(routed, "routed", torch.int32, (b * rpi,), plan.device)
+    ws = _workspace(plan.info["block_workspace_bytes"], x.device, workspace)
+    bw = _lib.BlockWeights(*[weights[name].data_ptr() for name in _WEIGHT_NAMES])
+    check(lib.sparsesam_block(plan.handle, ctypes.byref(bw), _ptr(x), b, _ptr(perm), _ptr(routed), _ptr(ws),
+                              ws.numel(), _stream(x.device)), "sparsesam_block")
+    return x

@@ -1,0 +1,491 @@
+// C ABI of libsparsesam: plans, validation and the five hot-path entry points.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "internal.hpp"
+
+namespace sparsesam {
+
+static thread_local std::string g_error;
+
+void set_error(const std::string& msg) { g_error = msg; }
+
+sparsesam_status hip_fail(hipError_t e, const char* where) {
+  set_error(std::string(where) + ": " + hipGetErrorString(e));
+  return SPARSESAM_ERR_HIP;
+}
+
+static sparsesam_status invalid(const std::string& msg) {
+  set_error(msg);
+  return SPARSESAM_ERR_INVALID_ARGUMENT;
+}
+
+static sparsesam_status unsupported(const std::string& msg) {
+  set_error(msg);
+  return SPARSESAM_ERR_UNSUPPORTED;
+}
+
+size_t permute_lds_bytes(const sparsesam_plan& p);
+
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+static size_t elem_size(const sparsesam_plan& p) { return p.desc.dtype == SPARSESAM_BF16 ? 2 : 4; }
+
+int mlp_splits(const sparsesam_plan& p, int rows) {
+  if (p.desc.dtype != SPARSESAM_BF16 || rows <= 0) return 1;
+  const int tiles = ((rows + 127) / 128) * ((p.desc.channels + 127) / 128);
+  const int nk = p.desc.mlp_hidden / 64;
+  static const int cand[] = {1, 2, 3, 4, 6, 8, 12, 16};
+  int best = 1;
+  for (int s : cand) {
+    if (nk % s != 0) continue;
+    best = s;
+    if (tiles * s >= 448) break;
+  }
+  return best;
+}
+
+size_t mlp_workspace(const sparsesam_plan& p, int rows, size_t* a2, size_t* hid, size_t* part, int* splits) {
+  const size_t es = elem_size(p);
+  const int s = mlp_splits(p, rows);
+  size_t off = 0;
+  *a2 = off;
+  off += align256((size_t)rows * p.desc.channels * es);
+  *hid = off;
+  off += align256((size_t)rows * p.desc.mlp_hidden * es);
+  *part = off;
+  if (s > 1) off += align256((size_t)s * rows * p.desc.channels * 4);
+  *splits = s;
+  return off;
+}
+
+BlockLayout block_layout(const sparsesam_plan& p, int batch) {
+  BlockLayout L;
+  const size_t es = elem_size(p);
+  const size_t segs = (size_t)batch * p.segs_per_img;
+  const size_t M = segs * p.n;
+  const size_t C = p.desc.channels;
+  size_t off = 0;
+  L.h = off;
+  off += align256(M * C * es);
+  L.q = off;
+  off += align256(M * C * es);
+  L.k = off;
+  off += align256(M * C * es);
+  L.vt = off;
+  off += align256(segs * p.desc.heads * p.desc.head_dim * (size_t)p.n_pad * es);
+  L.o = off;
+  off += align256(M * C * es);
+  L.total_attn = off;
+  L.total_mlp = mlp_workspace(p, batch * p.routed_per_image, &L.a2, &L.hid, &L.part, &L.splits);
+  return L;
+}
+
+static sparsesam_status check_device(const sparsesam_plan* p) {
+  if (!p) return invalid("plan is null");
+  if (!p->dev) {
+    set_error("plan has no device copy (no GPU was present when it was created)");
+    return SPARSESAM_ERR_NO_DEVICE;
+  }
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != p->device) {
+    set_error("current device " + std::to_string(dev) + " differs from the plan's device " +
+              std::to_string(p->device));
+    return SPARSESAM_ERR_NO_DEVICE;
+  }
+  return SPARSESAM_OK;
+}
+
+static sparsesam_status validate_desc(const sparsesam_plan_desc& d) {
+  if (d.grid_h <= 0 || d.grid_w <= 0) return invalid("grid_h and grid_w must be positive");
+  if (d.window < 0) return invalid("window must be >= 0");
+  const long long n = d.window > 0 ? (long long)d.window * d.window : (long long)d.grid_h * d.grid_w;
+  if (n > (1 << 20)) return invalid("segment too long");
+  if (d.stripes < 1 || n % d.stripes != 0) return invalid("stripes must be >= 1 and divide the segment length");
+  const long long S = n / d.stripes;
+  if (d.block < 1 || d.block > S) return invalid("block must be in [1, N / stripes]");
+  if (d.global_tokens < 0 || d.global_tokens > S) return invalid("global_tokens must be in [0, N / stripes]");
+  if (d.global_tokens % d.block != 0) return invalid("global_tokens must be a multiple of block");
+  if (d.band_radius < -1) return invalid("band_radius must be >= -1");
+  if (!(d.attn_density > 0.0f && d.attn_density <= 1.0f)) return invalid("attn_density must be in (0, 1]");
+  if (!(d.mlp_density > 0.0f && d.mlp_density <= 1.0f)) return invalid("mlp_density must be in (0, 1]");
+  if (d.heads < 1 || d.head_dim < 1 || d.channels != d.heads * d.head_dim)
+    return invalid("channels must equal heads * head_dim");
+  if (d.mlp_hidden < 1) return invalid("mlp_hidden must be positive");
+  if (d.max_batch < 1) return invalid("max_batch must be >= 1");
+  if (d.dtype != SPARSESAM_F32 && d.dtype != SPARSESAM_BF16) return invalid("dtype must be SPARSESAM_F32 or SPARSESAM_BF16");
+  if (d.channels > 1536) return unsupported("channels above 1536 are not supported");
+  if (d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 80 && d.head_dim != 128)
+    return unsupported("head_dim must be 32, 64, 80 or 128");
+  if (d.dtype == SPARSESAM_BF16) {
+    if (d.channels % 128 != 0 || d.mlp_hidden % 128 != 0)
+      return unsupported("bf16 plans need channels and mlp_hidden multiples of 128");
+    if (d.head_dim != 64 && d.head_dim != 80) return unsupported("bf16 plans need head_dim 64 or 80");
+  }
+  return SPARSESAM_OK;
+}
+
+static void build_tiles(sparsesam_plan& p, int radius) {
+  const int g = p.desc.stripes, B = p.desc.block, G = p.desc.global_tokens;
+  p.nbs = (p.s + B - 1) / B;
+  p.tiles = g * p.nbs;
+  p.tile_start.resize(p.tiles);
+  p.tile_len.resize(p.tiles);
+  for (int t = 0; t < p.tiles; ++t) {
+    int a = t / p.nbs, j = t % p.nbs;
+    p.tile_start[t] = a * p.s + j * B;
+    p.tile_len[t] = std::min(B, p.s - j * B);
+  }
+  auto global_tile = [&](int t) { return (t / p.nbs) == 0 && (t % p.nbs) * B < G; };
+  p.row_ptr.assign(p.tiles + 1, 0);
+  p.col_idx.clear();
+  p.pairs_kept = 0;
+  for (int t1 = 0; t1 < p.tiles; ++t1) {
+    for (int t2 = 0; t2 < p.tiles; ++t2) {
+      int j1 = t1 % p.nbs, j2 = t2 % p.nbs;
+      bool keep = std::abs(j1 - j2) <= radius || global_tile(t1) || global_tile(t2);
+      if (keep) {
+        p.col_idx.push_back(t2);
+        p.pairs_kept += (long long)p.tile_len[t1] * p.tile_len[t2];
+      }
+    }
+    p.row_ptr[t1 + 1] = (int)p.col_idx.size();
+  }
+  p.tiles_kept = (int)p.col_idx.size();
+  p.density = (double)p.pairs_kept / ((double)p.n * (double)p.n);
+  p.radius = radius;
+}
+
+}  // namespace sparsesam
+
+using namespace sparsesam;
+
+extern "C" {
+
+const char* sparsesam_status_string(sparsesam_status s) {
+  switch (s) {
+    case SPARSESAM_OK: return "ok";
+    case SPARSESAM_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SPARSESAM_ERR_UNSUPPORTED: return "unsupported";
+    case SPARSESAM_ERR_WORKSPACE: return "workspace too small";
+    case SPARSESAM_ERR_OUT_OF_MEMORY: return "out of memory";
+    case SPARSESAM_ERR_HIP: return "HIP error";
+    case SPARSESAM_ERR_NO_DEVICE: return "no device copy for the current device";
+  }
+  return "unknown status";
+}
+
+const char* sparsesam_last_error(void) { return g_error.c_str(); }
+
+sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesam_plan_t* out) {
+  if (!desc || !out) return invalid("desc and out must not be null");
+  *out = nullptr;
+  sparsesam_status st = validate_desc(*desc);
+  if (st != SPARSESAM_OK) return st;
+  sparsesam_plan* p = new (std::nothrow) sparsesam_plan();
+  if (!p) {
+    set_error("host allocation failed");
+    return SPARSESAM_ERR_OUT_OF_MEMORY;
+  }
+  p->desc = *desc;
+  const sparsesam_plan_desc& d = p->desc;
+  if (d.window > 0) {
+    p->nwy = (d.grid_h + d.window - 1) / d.window;
+    p->nwx = (d.grid_w + d.window - 1) / d.window;
+    p->segs_per_img = p->nwy * p->nwx;
+    p->n = d.window * d.window;
+  } else {
+    p->n = d.grid_h * d.grid_w;
+  }
+  p->n_pad = (p->n + 7) & ~7;
+  p->s = p->n / d.stripes;
+  int radius = d.band_radius;
+  const int last = (p->s - 1) / d.block;
+  if (radius < 0) {
+    for (radius = 0; radius <= last; ++radius) {
+      build_tiles(*p, radius);
+      if (p->density >= (double)d.attn_density) break;
+    }
+    if (radius > last) radius = last;
+  }
+  build_tiles(*p, radius);
+  // longest tile row first
+  p->order.resize(p->tiles);
+  for (int t = 0; t < p->tiles; ++t) p->order[t] = t;
+  std::stable_sort(p->order.begin(), p->order.end(), [&](int a, int b) {
+    return (p->row_ptr[a + 1] - p->row_ptr[a]) > (p->row_ptr[b + 1] - p->row_ptr[b]);
+  });
+  // keep-set size per segment
+  p->seg_k.resize(p->segs_per_img);
+  p->routed_per_image = 0;
+  for (int w = 0; w < p->segs_per_img; ++w) {
+    int n_real = p->n;
+    if (d.window > 0) {
+      int wy = w / p->nwx, wx = w % p->nwx;
+      int ry = std::min(d.window, d.grid_h - wy * d.window);
+      int rx = std::min(d.window, d.grid_w - wx * d.window);
+      n_real = ry * rx;
+    }
+    int k = (int)std::floor((double)d.mlp_density * (double)n_real + 0.5);
+    k = std::max(1, std::min(k, n_real));
+    p->seg_k[w] = k;
+    p->routed_per_image += k;
+  }
+  p->sort_pow2 = 1;
+  while (p->sort_pow2 < p->n) p->sort_pow2 <<= 1;
+  if (permute_lds_bytes(*p) > 160 * 1024) {
+    delete p;
+    return unsupported("segments of one image do not fit the permutation kernel's 160 KiB of LDS");
+  }
+  BlockLayout L = block_layout(*p, d.max_batch);
+  p->block_ws = std::max(L.total_attn, L.total_mlp);
+  size_t a2, hid, part;
+  int splits;
+  p->mlp_ws = mlp_workspace(*p, d.max_batch * p->routed_per_image, &a2, &hid, &part, &splits);
+
+  // device copy, when a device is present
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    size_t words = p->row_ptr.size() + p->col_idx.size() + 3 * (size_t)p->tiles + p->seg_k.size();
+    std::vector<int> blob;
+    blob.reserve(words);
+    auto put = [&](const std::vector<int>& v) {
+      size_t o = blob.size();
+      blob.insert(blob.end(), v.begin(), v.end());
+      return o;
+    };
+    size_t o_rp = put(p->row_ptr), o_ci = put(p->col_idx), o_ts = put(p->tile_start), o_tl = put(p->tile_len),
+           o_or = put(p->order), o_sk = put(p->seg_k);
+    void* dptr = nullptr;
+    hipError_t e = hipMalloc(&dptr, blob.size() * sizeof(int));
+    if (e != hipSuccess) {
+      delete p;
+      set_error(std::string("hipMalloc of the tile list failed: ") + hipGetErrorString(e));
+      return SPARSESAM_ERR_OUT_OF_MEMORY;
+    }
+    e = hipMemcpy(dptr, blob.data(), blob.size() * sizeof(int), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(dptr);
+      delete p;
+      return hip_fail(e, "hipMemcpy of the tile list");
+    }
+    const int* b = static_cast<const int*>(dptr);
+    p->dev = dptr;
+    p->device = dev;
+    p->d_row_ptr = b + o_rp;
+    p->d_col_idx = b + o_ci;
+    p->d_tile_start = b + o_ts;
+    p->d_tile_len = b + o_tl;
+    p->d_order = b + o_or;
+    p->d_seg_k = b + o_sk;
+  } else {
+    (void)hipGetLastError();
+  }
+  *out = p;
+  return SPARSESAM_OK;
+}
+
+sparsesam_status sparsesam_plan_get_info(sparsesam_plan_t p, sparsesam_plan_info* info) {
+  if (!p || !info) return invalid("plan and info must not be null");
+  std::memset(info, 0, sizeof(*info));
+  info->seq_len = p->n;
+  info->segments_per_image = p->segs_per_img;
+  info->band_radius = p->radius;
+  info->tiles_per_stripe = p->nbs;
+  info->tiles = p->tiles;
+  info->tiles_kept = p->tiles_kept;
+  info->pairs_kept = p->pairs_kept;
+  info->realised_density = p->density;
+  info->routed_per_image = p->routed_per_image;
+  info->block_workspace_bytes = p->block_ws;
+  info->mlp_workspace_bytes = p->mlp_ws;
+  info->has_device_copy = p->dev ? 1 : 0;
+  info->device = p->dev ? p->device : -1;
+  return SPARSESAM_OK;
+}
+
+sparsesam_status sparsesam_plan_tile_list(sparsesam_plan_t p, int32_t* row_ptr, int32_t* col_idx) {
+  if (!p || !row_ptr || !col_idx) return invalid("plan, row_ptr and col_idx must not be null");
+  std::memcpy(row_ptr, p->row_ptr.data(), p->row_ptr.size() * sizeof(int32_t));
+  std::memcpy(col_idx, p->col_idx.data(), p->col_idx.size() * sizeof(int32_t));
+  return SPARSESAM_OK;
+}
+
+void sparsesam_plan_destroy(sparsesam_plan_t p) {
+  if (!p) return;
+  if (p->dev) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != p->device) (void)hipSetDevice(p->device);
+    (void)hipFree(p->dev);
+    if (cur >= 0 && cur != p->device) (void)hipSetDevice(cur);
+  }
+  delete p;
+}
+
+sparsesam_status sparsesam_importance(const float* img, int32_t batch, int32_t height, int32_t width, int32_t patch,
+                                      float* imp, void* stream) {
+  if (batch < 0) return invalid("batch must be >= 0");
+  if (patch < 1 || patch > 32) return unsupported("patch must be in [1, 32]");
+  if (height <= 0 || width <= 0 || height % patch || width % patch)
+    return invalid("height and width must be positive multiples of patch");
+  if (batch > 65535 || height / patch > 65535 || width / patch > (1 << 30)) return invalid("grid too large");
+  if (batch == 0) return SPARSESAM_OK;
+  if (!img || !imp) return invalid("img and imp must not be null");
+  hipError_t e = launch_importance(img, batch, height, width, patch, imp, (hipStream_t)stream);
+  return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_importance launch");
+}
+
+sparsesam_status sparsesam_permute(sparsesam_plan_t p, const float* imp, int32_t batch, int32_t* perm, int32_t* inv,
+                                   int32_t* routed, void* stream) {
+  sparsesam_status st = check_device(p);
+  if (st != SPARSESAM_OK) return st;
+  if (batch < 0) return invalid("batch must be >= 0");
+  if (batch == 0) return SPARSESAM_OK;
+  if (!imp || !perm || !inv || !routed) return invalid("imp, perm, inv and routed must not be null");
+  hipError_t e = launch_permute(*p, imp, batch, perm, inv, routed, (hipStream_t)stream);
+  return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_permute launch");
+}
+
+sparsesam_status sparsesam_attn(sparsesam_plan_t p, int32_t segments, const void* q, const void* k, const void* vt,
+                                void* o, float scale, void* stream) {
+  sparsesam_status st = check_device(p);
+  if (st != SPARSESAM_OK) return st;
+  if (segments < 0) return invalid("segments must be >= 0");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return invalid("scale must be positive and finite");
+  if (segments == 0) return SPARSESAM_OK;
+  if (!q || !k || !vt || !o) return invalid("q, k, vt and o must not be null");
+  hipError_t e;
+  if (p->desc.dtype == SPARSESAM_BF16)
+    e = launch_attention<bf16_t>(*p, segments, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt, (bf16_t*)o, scale,
+                                 (hipStream_t)stream);
+  else
+    e = launch_attention<float>(*p, segments, (const float*)q, (const float*)k, (const float*)vt, (float*)o, scale,
+                                (hipStream_t)stream);
+  return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_attn launch");
+}
+
+}  // extern "C"
+
+template <typename T>
+static hipError_t run_mlp(const sparsesam_plan& p, float* x, const int32_t* routed, int rows, const float* ln_g,
+                          const float* ln_b, const void* w1, const float* b1, const void* w2, const float* b2,
+                          char* ws, hipStream_t st) {
+  size_t o_a2, o_hid, o_part;
+  int splits;
+  mlp_workspace(p, rows, &o_a2, &o_hid, &o_part, &splits);
+  T* a2 = reinterpret_cast<T*>(ws + o_a2);
+  T* hid = reinterpret_cast<T*>(ws + o_hid);
+  float* part = reinterpret_cast<float*>(ws + o_part);
+  const int C = p.desc.channels, Hm = p.desc.mlp_hidden;
+  hipError_t e = launch_gather_ln<T>(p, x, rows, nullptr, routed, ln_g, ln_b, a2, st);
+  if (e != hipSuccess) return e;
+  EpiGelu eg{b1, hid, Hm};
+  e = launch_gemm_gelu<T>(a2, (const T*)w1, rows, Hm, C, eg, st);
+  if (e != hipSuccess) return e;
+  EpiResidualScatter er{b2, x, nullptr, routed, p.segmap(), C};
+  return launch_gemm_residual<T>(hid, (const T*)w2, rows, C, Hm, er, splits, part, st);
+}
+
+extern "C" {
+
+sparsesam_status sparsesam_mlp(sparsesam_plan_t p, float* x, int64_t rows, const int32_t* routed, int32_t routed_count,
+                               const float* ln_g, const float* ln_b, const void* w1, const float* b1, const void* w2,
+                               const float* b2, void* workspace, size_t workspace_bytes, void* stream) {
+  sparsesam_status st = check_device(p);
+  if (st != SPARSESAM_OK) return st;
+  if (rows < 0 || routed_count < 0) return invalid("rows and routed_count must be >= 0");
+  if ((int64_t)routed_count > rows) return invalid("routed_count exceeds rows");
+  if ((int64_t)routed_count > (int64_t)p->desc.max_batch * p->routed_per_image)
+    return invalid("routed_count exceeds max_batch * routed_per_image");
+  if (routed_count == 0) return SPARSESAM_OK;
+  if (!x || !routed || !ln_g || !ln_b || !w1 || !b1 || !w2 || !b2) return invalid("null pointer argument");
+  size_t a2, hid, part;
+  int splits;
+  size_t need = mlp_workspace(*p, routed_count, &a2, &hid, &part, &splits);
+  if (!workspace || workspace_bytes < need) {
+    set_error("mlp workspace needs " + std::to_string(need) + " bytes");
+    return SPARSESAM_ERR_WORKSPACE;
+  }
+  hipError_t e;
+  if (p->desc.dtype == SPARSESAM_BF16)
+    e = run_mlp<bf16_t>(*p, x, routed, routed_count, ln_g, ln_b, w1, b1, w2, b2, (char*)workspace, (hipStream_t)stream);
+  else
+    e = run_mlp<float>(*p, x, routed, routed_count, ln_g, ln_b, w1, b1, w2, b2, (char*)workspace, (hipStream_t)stream);
+  return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_mlp launch");
+}
+
+}  // extern "C"
+
+template <typename T>
+static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weights& w, float* x, int batch,
+                            const int32_t* perm, const int32_t* routed, char* ws, hipStream_t st) {
+  BlockLayout L = block_layout(p, batch);
+  const int segs = batch * p.segs_per_img;
+  const int M = segs * p.n;
+  const int C = p.desc.channels;
+  T* h = reinterpret_cast<T*>(ws + L.h);
+  T* q = reinterpret_cast<T*>(ws + L.q);
+  T* k = reinterpret_cast<T*>(ws + L.k);
+  T* vt = reinterpret_cast<T*>(ws + L.vt);
+  T* o = reinterpret_cast<T*>(ws + L.o);
+  hipError_t e = launch_gather_ln<T>(p, x, M, perm, nullptr, w.ln1_g, w.ln1_b, h, st);
+  if (e != hipSuccess) return e;
+  EpiQKV eq{w.b_qkv, q, k, vt, p.n, p.n_pad, p.desc.heads, p.desc.head_dim, C};
+  e = launch_gemm_qkv<T>(h, (const T*)w.w_qkv, M, C, eq, st);
+  if (e != hipSuccess) return e;
+  e = launch_attention<T>(p, segs, q, k, vt, o, 1.0f / std::sqrt((float)p.desc.head_dim), st);
+  if (e != hipSuccess) return e;
+  EpiResidualScatter er{w.b_proj, x, perm, nullptr, p.segmap(), C};
+  e = launch_gemm_residual<T>(o, (const T*)w.w_proj, M, C, C, er, 1, nullptr, st);
+  if (e != hipSuccess) return e;
+  const int rows = batch * p.routed_per_image;
+  T* a2 = reinterpret_cast<T*>(ws + L.a2);
+  T* hid = reinterpret_cast<T*>(ws + L.hid);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  e = launch_gather_ln<T>(p, x, rows, nullptr, routed, w.ln2_g, w.ln2_b, a2, st);
+  if (e != hipSuccess) return e;
+  EpiGelu eg{w.b1, hid, p.desc.mlp_hidden};
+  e = launch_gemm_gelu<T>(a2, (const T*)w.w1, rows, p.desc.mlp_hidden, C, eg, st);
+  if (e != hipSuccess) return e;
+  EpiResidualScatter e2{w.b2, x, nullptr, routed, p.segmap(), C};
+  return launch_gemm_residual<T>(hid, (const T*)w.w2, rows, C, p.desc.mlp_hidden, e2, L.splits, part, st);
+}
+
+extern "C" {
+
+sparsesam_status sparsesam_block(sparsesam_plan_t p, const sparsesam_block_weights* w, float* x, int32_t batch,
+                                 const int32_t* perm, const int32_t* routed, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  sparsesam_status st = check_device(p);
+  if (st != SPARSESAM_OK) return st;
+  if (!w) return invalid("weights must not be null");
+  if (batch < 0 || batch > p->desc.max_batch) return invalid("batch must be in [0, max_batch]");
+  if (batch == 0) return SPARSESAM_OK;
+  if (!x || !perm || !routed) return invalid("x, perm and routed must not be null");
+  if (!w->ln1_g || !w->ln1_b || !w->w_qkv || !w->b_qkv || !w->w_proj || !w->b_proj || !w->ln2_g || !w->ln2_b ||
+      !w->w1 || !w->b1 || !w->w2 || !w->b2)
+    return invalid("a weight pointer is null");
+  BlockLayout L = block_layout(*p, batch);
+  size_t need = std::max(L.total_attn, L.total_mlp);
+  if (!workspace || workspace_bytes < need) {
+    set_error("block workspace needs " + std::to_string(need) + " bytes");
+    return SPARSESAM_ERR_WORKSPACE;
+  }
+  hipError_t e;
+  if (p->desc.dtype == SPARSESAM_BF16)
+    e = run_block<bf16_t>(*p, *w, x, batch, perm, routed, (char*)workspace, (hipStream_t)stream);
+  else
+    e = run_block<float>(*p, *w, x, batch, perm, routed, (char*)workspace, (hipStream_t)stream);
+  return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_block launch");
+}
+
+}  // extern "C"

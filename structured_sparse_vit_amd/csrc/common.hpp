@@ -1,0 +1,71 @@
+// Device-side helpers shared by the SparseSAM kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sparsesam {
+
+typedef __bf16 bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+
+constexpr int kWave = 64;
+
+// fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ bf16_t to_bf16(float f) { return (bf16_t)f; }
+__device__ __forceinline__ float to_f32(bf16_t b) { return (float)b; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float f);
+template <>
+__device__ __forceinline__ float from_f32<float>(float f) { return f; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) { return to_bf16(f); }
+
+template <typename T>
+__device__ __forceinline__ float load_f32(const T* p) { return (float)(*p); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// GELU with the exact Gaussian CDF.
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+
+// Image-token row of a segment slot. Global segments map slot -> token directly;
+// windowed segments map (window, slot) through the padded window grid. Returns -1
+// for a pad slot.
+struct SegmentMap {
+  int grid_h, grid_w, window, nwx, segs_per_img, n;
+
+  __device__ __forceinline__ int row_of(int seg, int slot) const {
+    int img = seg / segs_per_img;
+    int tok;
+    if (window == 0) {
+      tok = slot;
+    } else {
+      int w = seg - img * segs_per_img;
+      int wy = w / nwx, wx = w - wy * nwx;
+      int ly = slot / window, lx = slot - ly * window;
+      int y = wy * window + ly, x = wx * window + lx;
+      if (y >= grid_h || x >= grid_w) return -1;
+      tok = y * grid_w + x;
+    }
+    return img * grid_h * grid_w + tok;
+  }
+};
+
+}  // namespace sparsesam

@@ -1,0 +1,120 @@
+// Host-side plan and kernel launch interfaces of libsparsesam (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/sparsesam.h"
+#include "common.hpp"
+
+struct sparsesam_plan {
+  sparsesam_plan_desc desc;
+  int n = 0;              // tokens per segment (pads included)
+  int n_pad = 0;          // n rounded up to a multiple of 8 (row stride of V^T)
+  int s = 0;              // stripe length n / g
+  int nbs = 0;            // tiles per stripe
+  int tiles = 0;          // g * nbs
+  int radius = 0;
+  int segs_per_img = 1;
+  int nwx = 1, nwy = 1;
+  int tiles_kept = 0;
+  long long pairs_kept = 0;
+  double density = 0.0;
+  int routed_per_image = 0;
+  int sort_pow2 = 0;      // per-segment sort width (power of two >= n)
+  size_t block_ws = 0, mlp_ws = 0;
+
+  // host copies of the static tables
+  std::vector<int> row_ptr, col_idx;  // CSR of kept key tiles per query tile
+  std::vector<int> tile_start, tile_len;
+  std::vector<int> order;             // query tiles, longest row first
+  std::vector<int> seg_k;             // keep-set size of each segment of an image
+
+  // device copy (one allocation) on `device`
+  int device = -1;
+  void* dev = nullptr;
+  const int* d_row_ptr = nullptr;
+  const int* d_col_idx = nullptr;
+  const int* d_tile_start = nullptr;
+  const int* d_tile_len = nullptr;
+  const int* d_order = nullptr;
+  const int* d_seg_k = nullptr;
+
+  sparsesam::SegmentMap segmap() const {
+    sparsesam::SegmentMap m;
+    m.grid_h = desc.grid_h;
+    m.grid_w = desc.grid_w;
+    m.window = desc.window;
+    m.nwx = nwx;
+    m.segs_per_img = segs_per_img;
+    m.n = n;
+    return m;
+  }
+};
+
+namespace sparsesam {
+
+void set_error(const std::string& msg);
+sparsesam_status hip_fail(hipError_t e, const char* where);
+
+// Workspace carve-up of sparsesam_block / sparsesam_mlp.
+struct BlockLayout {
+  size_t h = 0, q = 0, k = 0, vt = 0, o = 0, total_attn = 0;
+  size_t a2 = 0, hid = 0, part = 0, total_mlp = 0;
+  int splits = 1;
+};
+BlockLayout block_layout(const sparsesam_plan& p, int batch);
+size_t mlp_workspace(const sparsesam_plan& p, int routed_rows, size_t* a2, size_t* hid, size_t* part, int* splits);
+int mlp_splits(const sparsesam_plan& p, int routed_rows);
+
+// ---- launches (each returns hipSuccess or the launch error) ----
+hipError_t launch_importance(const float* img, int batch, int height, int width, int patch, float* imp,
+                             hipStream_t st);
+hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
+                          hipStream_t st);
+
+// LayerNorm of gathered rows: out[r] = LN(x[src(r)]) for r < rows_out, zero rows for pads.
+// Row source: mode 0 = stripe-sorted segment rows through perm, mode 1 = explicit list.
+template <typename T>
+hipError_t launch_gather_ln(const sparsesam_plan& p, const float* x, int rows_out, const int* perm,
+                            const int* list, const float* g, const float* b, T* out, hipStream_t st);
+
+// GEMM C = A W^T with fused epilogues (bf16 matrix cores or fp32 SIMT).
+struct EpiQKV {  // q, k [seg, H, N, D]; vt [seg, H, D, N_pad]
+  const float* bias;
+  void* q;
+  void* k;
+  void* vt;
+  int n, n_pad, heads, head_dim, channels;
+};
+struct EpiResidualScatter {  // x[map(r)] += acc + bias, or partials when split
+  const float* bias;
+  float* x;
+  const int* perm;  // stripe-sorted rows -> slot (mode 0), or null
+  const int* list;  // explicit row list (mode 1), or null
+  SegmentMap map;
+  int ldx;
+};
+struct EpiGelu {  // out[r, c] = GELU(acc + bias)
+  const float* bias;
+  void* out;
+  int ld;
+};
+
+template <typename T>
+hipError_t launch_gemm_qkv(const T* a, const T* w, int m, int k, const EpiQKV& e, hipStream_t st);
+template <typename T>
+hipError_t launch_gemm_gelu(const T* a, const T* w, int m, int n, int k, const EpiGelu& e, hipStream_t st);
+// Residual GEMM: when splits > 1, partial sums go to `part` [splits, m, n] fp32 and a
+// reduction adds them in split order, then the bias, into x.
+template <typename T>
+hipError_t launch_gemm_residual(const T* a, const T* w, int m, int n, int k, const EpiResidualScatter& e,
+                                int splits, float* part, hipStream_t st);
+
+template <typename T>
+hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
+                            float scale, hipStream_t st);
+
+}  // namespace sparsesam

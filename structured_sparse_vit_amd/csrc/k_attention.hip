@@ -1,0 +1,257 @@
+// Block-sparse attention over the static stripe-sort pattern.
+//
+// "Technische Samenvatting: SparseSAM", Methodologie, 1. Stripe-Sort Attention,
+// static-pattern bullet: after the stripe-sort permutation the N x N map is a 4 x 4
+// mosaic of banded sub-maps plus a small global keep-set; the pattern is fixed, so a
+// FlashAttention-2-style kernel runs it with no mask built at run time. Here the
+// plan's tile list (CSR: kept key tiles of every query tile) is that pattern; every
+// kept tile is computed whole and nothing inside a tile is masked.
+//
+// Kernels:
+//  * attn_mfma64_kernel (bf16, head_dim 64, B = 64, stripes a multiple of 64 long):
+//    one 128-thread workgroup per (query tile, segment, head), issued longest tile row
+//    first. Each wavefront owns 32 queries. S^T = K Q^T and O^T = V^T P^T run on
+//    v_mfma_f32_32x32x16_bf16, so a lane holds one query's scores (the softmax row
+//    max needs one exchange with lane ^ 32) and one query's output column. K and the
+//    transposed V tiles are staged through LDS, the next tile prefetched into
+//    registers during the current one. Online softmax in fp32 with exp2 and the
+//    scale folded into one multiply-add per score.
+//  * attn_simt_kernel (fp32 or bf16 storage, any pattern and head_dim <= 128): one
+//    thread per query, keys read through the cache; the exact path for small
+//    configs and for windows.
+#include "internal.hpp"
+
+namespace sparsesam {
+
+// ---------------------------------------------------------------- MFMA kernel (D = 64, B = 64)
+
+constexpr int kTile = 64;
+constexpr int kLd = 64 + 8;  // LDS row stride in bf16 (16-byte pad)
+
+__global__ void __launch_bounds__(128) attn_mfma64_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
+                                                          const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
+                                                          const int* __restrict__ row_ptr,
+                                                          const int* __restrict__ col_idx,
+                                                          const int* __restrict__ tile_start,
+                                                          const int* __restrict__ order, int n, int n_pad, int heads,
+                                                          int seg_heads, float c_log2) {
+  constexpr int D = 64;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[kTile * kLd];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[D * kLd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qt = order[blockIdx.x / seg_heads];
+  const int sh = blockIdx.x - (blockIdx.x / seg_heads) * seg_heads;  // seg * heads + head
+  const int seg = sh / heads, h = sh - seg * heads;
+  const bf16_t* q_base = Q + (size_t)sh * n * D;
+  const bf16_t* k_base = Kt + (size_t)sh * n * D;
+  const bf16_t* v_base = VT + (size_t)sh * D * n_pad;
+
+  const int q0 = tile_start[qt] + wave * 32;
+  const int my_q = q0 + (lane & 31);
+  // Q^T operand: lane holds Q[my_q][16 ks + 8 (lane / 32) .. + 7]
+  bf16x8 qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(q_base + (size_t)my_q * D + ks * 16 + (lane >> 5) * 8);
+
+  f32x16 oacc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int kb = row_ptr[qt], ke = row_ptr[qt + 1];
+  // staging: K tile 64 x 64 and V^T tile 64 x 64, 4 + 4 chunks of 16 bytes per thread
+  i32x4 rk[4], rv[4];
+  auto load_regs = [&](int kt) {
+    const int k0 = tile_start[kt];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + 128 * i;  // 512 chunks: row = c / 8, chunk = c % 8
+      int row = c >> 3, ch = c & 7;
+      rk[i] = *reinterpret_cast<const i32x4*>(k_base + (size_t)(k0 + row) * D + ch * 8);
+      rv[i] = *reinterpret_cast<const i32x4*>(v_base + (size_t)row * n_pad + k0 + ch * 8);
+    }
+  };
+  auto store_lds = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + 128 * i;
+      int row = c >> 3, ch = c & 7;
+      *reinterpret_cast<i32x4*>(Ks + row * kLd + ch * 8) = rk[i];
+      // V^T: inside each 16-key group store keys as [0..3, 8..11, 4..7, 12..15] so a
+      // lane's eight k-slots of the P^T operand are contiguous
+      int grp = ch >> 1, half = ch & 1;
+      bf16_t* dst = Vs + row * kLd + grp * 16 + half * 4;
+      *reinterpret_cast<i32x2*>(dst) = i32x2{rv[i][0], rv[i][1]};
+      *reinterpret_cast<i32x2*>(dst + 8) = i32x2{rv[i][2], rv[i][3]};
+    }
+  };
+
+  if (kb < ke) load_regs(col_idx[kb]);
+  for (int t = kb; t < ke; ++t) {
+    __syncthreads();
+    store_lds();
+    __syncthreads();
+    if (t + 1 < ke) load_regs(col_idx[t + 1]);
+
+    // S^T = K Q^T: two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[mb][e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (mb * 32 + (lane & 31)) * kLd + ks * 16 + (lane >> 5) * 8);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
+      }
+    }
+    // online softmax for this lane's query (32 of the 64 scores here, the rest in lane ^ 32)
+    float mx = s[0][0];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * c_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.0f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][hh * 8 + e], c_log2, -m_new));
+          psum += p;
+          pf[mb * 2 + hh][e] = to_bf16(p);
+        }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int md = 0; md < 2; ++md)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
+    // O^T += V^T P^T over four 16-key steps
+#pragma unroll
+    for (int md = 0; md < 2; ++md)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + (md * 32 + (lane & 31)) * kLd + kk * 16 + (lane >> 5) * 8);
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[md], 0, 0, 0);
+      }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv_l = 1.0f / l_tot;
+  bf16_t* o_row = O + ((size_t)seg * n + my_q) * ((size_t)heads * D) + (size_t)h * D;
+#pragma unroll
+  for (int md = 0; md < 2; ++md)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      int d = md * 32 + g4 * 8 + (lane >> 5) * 4;
+      bf16x4 v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = to_bf16(oacc[md][g4 * 4 + e] * inv_l);
+      *reinterpret_cast<bf16x4*>(o_row + d) = v4;
+    }
+}
+
+// ---------------------------------------------------------------- SIMT kernel (any pattern)
+
+template <typename T, int D>
+__global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, const T* __restrict__ Kt,
+                                                       const T* __restrict__ VT, T* __restrict__ O,
+                                                       const int* __restrict__ row_ptr,
+                                                       const int* __restrict__ col_idx,
+                                                       const int* __restrict__ tile_start,
+                                                       const int* __restrict__ tile_len, int n, int n_pad, int heads,
+                                                       int chunks, float c_log2) {
+  const int qt = blockIdx.x / chunks, chunk = blockIdx.x - (blockIdx.x / chunks) * chunks;
+  const int h = blockIdx.y, seg = blockIdx.z;
+  const int len = tile_len[qt];
+  const size_t sh = (size_t)seg * heads + h;
+  float qv[D], acc[D];
+  const int local = chunk * 64 + threadIdx.x;
+  const bool active = local < len;
+  const int qi = tile_start[qt] + (active ? local : 0);
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qv[d] = active ? (float)Q[(sh * n + qi) * D + d] : 0.0f;
+    acc[d] = 0.0f;
+  }
+  float m_run = -INFINITY, l_run = 0.0f;
+  for (int t = row_ptr[qt]; t < row_ptr[qt + 1]; ++t) {
+    const int kt = col_idx[t];
+    const int k0 = tile_start[kt], kl = tile_len[kt];
+    for (int j = 0; j < kl; ++j) {
+      const int kj = k0 + j;
+      const T* kr = Kt + (sh * n + kj) * D;
+      float sc = 0.0f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) sc = fmaf(qv[d], (float)kr[d], sc);
+      sc *= c_log2;
+      const float m_new = fmaxf(m_run, sc);
+      const float alpha = exp2f(m_run - m_new);
+      const float p = exp2f(sc - m_new);
+      l_run = l_run * alpha + p;
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, (float)VT[(sh * D + d) * n_pad + kj], acc[d] * alpha);
+    }
+  }
+  if (!active) return;
+  T* orow = O + ((size_t)seg * n + qi) * ((size_t)heads * D) + (size_t)h * D;
+  const float inv_l = 1.0f / l_run;
+#pragma unroll
+  for (int d = 0; d < D; ++d) orow[d] = from_f32<T>(acc[d] * inv_l);
+}
+
+// ---------------------------------------------------------------- launchers
+
+bool attn_mfma64_supported(const sparsesam_plan& p) {
+  return p.desc.dtype == SPARSESAM_BF16 && p.desc.head_dim == 64 && p.desc.block == 64 && p.s % 64 == 0;
+}
+
+template <typename T, int D>
+static hipError_t run_simt(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
+                           float c_log2, hipStream_t st) {
+  const int chunks = (p.desc.block + 63) / 64;
+  dim3 grid(p.tiles * chunks, p.desc.heads, segments);
+  hipLaunchKernelGGL((attn_simt_kernel<T, D>), grid, dim3(64), 0, st, q, k, vt, o, p.d_row_ptr, p.d_col_idx,
+                     p.d_tile_start, p.d_tile_len, p.n, p.n_pad, p.desc.heads, chunks, c_log2);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
+                            float scale, hipStream_t st) {
+  if (segments <= 0) return hipSuccess;
+  const float c_log2 = scale * 1.4426950408889634f;
+  if constexpr (sizeof(T) == 2) {
+    if (attn_mfma64_supported(p)) {
+      int seg_heads = segments * p.desc.heads;
+      dim3 grid(p.tiles * seg_heads);
+      hipLaunchKernelGGL(attn_mfma64_kernel, grid, dim3(128), 0, st, q, k, vt, o, p.d_row_ptr, p.d_col_idx,
+                         p.d_tile_start, p.d_order, p.n, p.n_pad, p.desc.heads, seg_heads, c_log2);
+      return hipGetLastError();
+    }
+  }
+  switch (p.desc.head_dim) {
+    case 64: return run_simt<T, 64>(p, segments, q, k, vt, o, c_log2, st);
+    case 80: return run_simt<T, 80>(p, segments, q, k, vt, o, c_log2, st);
+    case 32: return run_simt<T, 32>(p, segments, q, k, vt, o, c_log2, st);
+    case 128: return run_simt<T, 128>(p, segments, q, k, vt, o, c_log2, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template hipError_t launch_attention<float>(const sparsesam_plan&, int, const float*, const float*, const float*,
+                                            float*, float, hipStream_t);
+template hipError_t launch_attention<bf16_t>(const sparsesam_plan&, int, const bf16_t*, const bf16_t*, const bf16_t*,
+                                             bf16_t*, float, hipStream_t);
+
+}  // namespace sparsesam

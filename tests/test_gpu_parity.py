@@ -1,0 +1,253 @@
+"""GPU parity: every C-ABI entry point against the oracle on the same seeded inputs.
+
+Integer outputs (importance bits, perm, inv, keep-set) must match bit for bit;
+floating-point outputs within max-abs 1e-2 and relative L2 5e-3.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import structured_sparse_vit_amd as ss
+from synth import round_to_bf16
+from tests.gpu_cases import check_close, config, images, oracle_block, oracle_importance
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _plan(cfg, **over):
+    return ss.Plan.from_config(cfg.with_(**over) if over else cfg)
+
+
+def _oracle_perm(cfg, imp):
+    """Oracle perm / inv / keep-set for a batch of importance maps."""
+    tm = oracle.segments_for_image(cfg.grid, cfg.grid, cfg.window)
+    perms, invs, routed = [], [], []
+    tokens = cfg.grid * cfg.grid
+    for b in range(imp.shape[0]):
+        rs = []
+        for row in tm:
+            s = oracle.descending_order(oracle.segment_importance(imp[b], row), valid=row >= 0)
+            p, i = oracle.stripe_sort(s, cfg.stripes)
+            perms.append(p)
+            invs.append(i)
+            rs.append(oracle.routed_tokens(s, row, cfg.mlp_density))
+        routed.append(np.sort(np.concatenate(rs)) + b * tokens)
+    return np.stack(perms), np.stack(invs), np.concatenate(routed)
+
+
+# ------------------------------------------------------------------ importance
+
+@pytest.mark.parametrize("key,noise", [("c1", 0.05), ("c2", 0.05), ("c3", 0.05), ("c2", 0.0)])
+def test_importance_bit_exact(key, noise):
+    _say("importance", key, noise)
+    img = images(key, 0, noise)
+    got = ss.importance(torch.from_numpy(img).to(DEV), config(key).patch).cpu().numpy()
+    want = oracle_importance(key, 0, noise)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_importance_edge_images():
+    _say("importance edges")
+    rng = np.random.default_rng(1)
+    imgs = np.stack([
+        np.zeros((64, 96), np.float32),
+        np.full((64, 96), 0.5, np.float32),
+        rng.integers(0, 256, (64, 96)).astype(np.float32),
+        (rng.normal(size=(64, 96)) * 1e-20).astype(np.float32),   # tiny values, subnormal squares
+        (rng.normal(size=(64, 96)) * 1e15).astype(np.float32),    # large values
+    ])
+    got = ss.importance(torch.from_numpy(imgs).to(DEV), 16).cpu().numpy()
+    want = np.stack([oracle.importance(im, 16) for im in imgs])
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    got8 = ss.importance(torch.from_numpy(imgs[:, :, :96]).to(DEV), 8).cpu().numpy()
+    want8 = np.stack([oracle.importance(im, 8) for im in imgs])
+    assert np.array_equal(got8.view(np.uint32), want8.view(np.uint32))
+
+
+# ------------------------------------------------------------------ permute
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "ragged"])
+def test_permute_bit_exact(key):
+    _say("permute", key)
+    cfg = config(key)
+    plan = _plan(cfg)
+    imp = oracle_importance(key)
+    perm, inv, routed = ss.permute(plan, torch.from_numpy(imp).to(DEV))
+    wp, wi, wr = _oracle_perm(cfg, imp)
+    assert np.array_equal(perm.cpu().numpy(), wp)
+    assert np.array_equal(inv.cpu().numpy(), wi)
+    assert np.array_equal(routed.cpu().numpy(), wr)
+
+
+@pytest.mark.parametrize("key", ["c2", "c3"])
+def test_permute_ties_zero_nan(key):
+    _say("permute ties", key)
+    cfg = config(key).with_(batch=3)
+    plan = _plan(cfg)
+    rng = np.random.default_rng(7)
+    t = cfg.grid * cfg.grid
+    imp = np.stack([
+        np.zeros(t, np.float32),                                        # all ties
+        rng.integers(0, 4, t).astype(np.float32) * np.float32(0.25),    # many ties
+        rng.uniform(size=t).astype(np.float32),
+    ])
+    imp[1, ::5] = -0.0
+    imp[2, ::97] = np.nan
+    imp[2, 3] = np.inf
+    perm, inv, routed = ss.permute(plan, torch.from_numpy(imp).to(DEV))
+    wp, wi, wr = _oracle_perm(cfg, imp)
+    assert np.array_equal(perm.cpu().numpy(), wp)
+    assert np.array_equal(inv.cpu().numpy(), wi)
+    assert np.array_equal(routed.cpu().numpy(), wr)
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn_case(key, seed=0, **over):
+    cfg = config(key)
+    if over:
+        cfg = cfg.with_(**over)
+    plan = _plan(cfg)
+    n, H, D = plan.info["seq_len"], cfg.heads, cfg.head_dim
+    segs = cfg.batch * plan.info["segments_per_image"]
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((segs, H, n, D), dtype=np.float32) for _ in range(3))
+    if cfg.dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    n_pad = (n + 7) // 8 * 8
+    vt = np.full((segs, H, D, n_pad), np.nan, np.float32)  # pad columns must never be read
+    vt[..., :n] = v.transpose(0, 1, 3, 2)
+    dt = plan.torch_dtype
+    dev = [torch.from_numpy(a).to(DEV, dt).contiguous() for a in (q, k, vt)]
+    o = ss.attn(plan, *dev).float().cpu().numpy()
+    keep = oracle.position_keep(n, cfg.stripes, cfg.block, cfg.global_tokens, plan.info["band_radius"])
+    want = np.empty((segs, n, H * D))
+    for s in range(segs):
+        for h in range(H):
+            want[s, :, h * D:(h + 1) * D] = oracle.masked_attention(q[s, h], k[s, h], v[s, h], keep, D ** -0.5)
+    return o, want
+
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3b1", "c5g", "c5w", "ragged"])
+def test_attention_parity(key):
+    _say("attention", key)
+    o, want = _attn_case(key)
+    check_close(o, want, what="attention " + key)
+
+
+@pytest.mark.parametrize("key", ["c2", "c3b1", "c1"])
+def test_attention_density_one_is_dense(key):
+    _say("attention dense", key)
+    o, want = _attn_case(key, seed=3, attn_density=1.0)
+    check_close(o, want, what="dense attention " + key)
+
+
+def test_attention_single_stripe_and_wide_band():
+    _say("attention stripes=1")
+    o, want = _attn_case("c2", seed=4, stripes=1, band_radius=2)
+    check_close(o, want, what="stripes=1")
+
+
+# ------------------------------------------------------------------ MLP
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3b1"])
+def test_mlp_parity_and_unrouted_rows_untouched(key):
+    _say("mlp", key)
+    x, w, imp, _, parts = oracle_block(key)
+    cfg = config(key)
+    plan = _plan(cfg)
+    rows = x.reshape(-1, cfg.channels)
+    routed = np.concatenate(parts["routed"]).astype(np.int32)
+    wd = ss.weights_to_device(w, plan)
+    xd = torch.from_numpy(rows.copy()).to(DEV)
+    rd = torch.from_numpy(routed).to(DEV)
+    ss.mlp(plan, xd, rd, wd["ln2_g"], wd["ln2_b"], wd["w1"], wd["b1"], wd["w2"], wd["b2"])
+    got = xd.cpu().numpy()
+    want = oracle.routed_mlp(rows, routed, w)
+    check_close(got, want, what="mlp " + key)
+    other = np.setdiff1d(np.arange(rows.shape[0]), routed)
+    assert np.array_equal(got[other].view(np.uint32), rows[other].view(np.uint32))
+
+
+def test_mlp_empty_keep_set_is_noop():
+    cfg = config("c1")
+    plan = _plan(cfg)
+    w = ss.weights_to_device(oracle_block("c1")[1], plan)
+    x = torch.randn(256, 64, device=DEV)
+    x0 = x.clone()
+    ss.mlp(plan, x, torch.empty(0, dtype=torch.int32, device=DEV), w["ln2_g"], w["ln2_b"], w["w1"], w["b1"],
+           w["w2"], w["b2"])
+    assert torch.equal(x, x0)
+
+
+# ------------------------------------------------------------------ whole block
+
+def _run_block(key, seed=0):
+    x, w, imp, want, parts = oracle_block(key, seed)
+    cfg = config(key)
+    plan = _plan(cfg)
+    img = torch.from_numpy(images(key, seed)).to(DEV)
+    imp_d = ss.importance(img, cfg.patch)
+    perm, inv, routed = ss.permute(plan, imp_d)
+    wd = ss.weights_to_device(w, plan)
+    xd = torch.from_numpy(x.copy()).to(DEV)
+    ss.block(plan, wd, xd, perm, routed)
+    torch.cuda.synchronize()
+    return dict(x=x, want=want, parts=parts, imp=imp, got=xd.cpu().numpy(), imp_d=imp_d.cpu().numpy(),
+                perm=perm.cpu().numpy(), inv=inv.cpu().numpy(), routed=routed.cpu().numpy(), plan=plan, wd=wd,
+                img=img)
+
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "ragged", "c4g", "c4w"])
+def test_block_parity(key):
+    _say("block", key)
+    r = _run_block(key)
+    assert np.array_equal(r["imp_d"].view(np.uint32), r["imp"].view(np.uint32))
+    assert np.array_equal(r["perm"], np.stack(r["parts"]["perm"]))
+    assert np.array_equal(r["inv"], np.stack(r["parts"]["inv"]))
+    assert np.array_equal(r["routed"], np.concatenate(r["parts"]["routed"]))
+    check_close(r["got"], r["want"], what="block " + key)
+    # the block's own contribution, a stricter view than the residual sum
+    check_close(r["got"] - r["x"], r["want"] - r["x"], max_abs=1e-2, rel_l2=2e-2, what="block delta " + key)
+
+
+def test_block_is_deterministic():
+    _say("block determinism")
+    cfg = config("c2")
+    r = _run_block("c2")
+    plan, wd = r["plan"], r["wd"]
+    perm = torch.from_numpy(r["perm"]).to(DEV)
+    routed = torch.from_numpy(r["routed"]).to(DEV)
+    outs = []
+    for _ in range(2):
+        xd = torch.from_numpy(r["x"].copy()).to(DEV)
+        ss.block(plan, wd, xd, perm, routed)
+        outs.append(xd.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), r["got"].view(np.uint32))
+
+
+def test_block_density_one_matches_dense_oracle():
+    _say("block dense c1")
+    import oracle as O
+    from synth import block_weights, token_features
+    cfg = config("c1").with_(attn_density=1.0, mlp_density=1.0)
+    plan = _plan(cfg)
+    img = images("c1")
+    imp = np.stack([O.importance(im, cfg.patch) for im in img])
+    x, w = token_features(cfg), block_weights(cfg)
+    want = O.block_forward(x, imp, w, cfg)
+    imp_d = ss.importance(torch.from_numpy(img).to(DEV), cfg.patch)
+    perm, inv, routed = ss.permute(plan, imp_d)
+    xd = torch.from_numpy(x.copy()).to(DEV)
+    ss.block(plan, ss.weights_to_device(w, plan), xd, perm, routed)
+    check_close(xd.cpu().numpy(), want, max_abs=1e-4, rel_l2=1e-5, what="dense fp32 block")

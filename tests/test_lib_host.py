@@ -1,0 +1,164 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every declared symbol,
+builds the static tile list on the host, and validates arguments before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import structured_sparse_vit_amd as ss
+from oracle import band_radius, position_keep, routed_count, window_token_map
+from structured_sparse_vit_amd import _lib
+from synth import get_config
+from synth.configs import global_variant
+from tests.conftest import ROOT
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libsparsesam.so not built")
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "sparsesam.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparsesam_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared_symbols()
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code in range(7):
+        assert lib.sparsesam_status_string(code)
+    assert lib.sparsesam_status_string(99) == b"unknown status"
+
+
+def _tile_pairs_from_oracle(n, g, B, G, r):
+    keep = position_keep(n, g, B, G, r)
+    S = n // g
+    nbs = -(-S // B)
+    pos = np.arange(n)
+    tile = (pos // S) * nbs + (pos % S) // B
+    T = g * nbs
+    kept = np.zeros((T, T), bool)
+    qi, ki = np.nonzero(keep)
+    kept[tile[qi], tile[ki]] = True
+    return kept, int(keep.sum())
+
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c4g", "c5"])
+def test_plan_matches_oracle_pattern(key):
+    cfg = global_variant(get_config("c4")) if key == "c4g" else get_config(key)
+    plan = ss.Plan.from_config(cfg)
+    info = plan.info
+    n = cfg.window ** 2 if cfg.window else cfg.grid ** 2
+    r = band_radius(n, cfg.stripes, cfg.block, cfg.global_tokens, cfg.attn_density)
+    assert info["seq_len"] == n
+    assert info["band_radius"] == r
+    kept, pairs = _tile_pairs_from_oracle(n, cfg.stripes, cfg.block, cfg.global_tokens, r)
+    rp, ci = plan.tile_list()
+    got = np.zeros_like(kept)
+    for t in range(info["tiles"]):
+        got[t, ci[rp[t]:rp[t + 1]]] = True
+    assert np.array_equal(got, kept)
+    assert info["tiles_kept"] == kept.sum()
+    assert info["pairs_kept"] == pairs
+    assert abs(info["realised_density"] - pairs / n ** 2) < 1e-15
+    # keep-set size per image
+    tm = window_token_map(cfg.grid, cfg.grid, cfg.window) if cfg.window else np.arange(n)[None]
+    want = sum(routed_count(cfg.mlp_density, int((row >= 0).sum())) for row in tm)
+    assert info["routed_per_image"] == want
+
+
+def test_plan_known_values():
+    info = ss.Plan.from_config(get_config("c2")).info
+    assert (info["band_radius"], info["tiles_kept"], info["routed_per_image"]) == (3, 1696, 1638)
+    assert abs(info["realised_density"] - 0.4140625) < 1e-12
+    info = ss.Plan.from_config(get_config("c3")).info
+    assert (info["band_radius"], info["tiles_kept"], info["pairs_kept"], info["routed_per_image"]) == (0, 88, 16528, 1634)
+    info = ss.Plan.from_config(get_config("c1")).info
+    assert (info["band_radius"], info["tiles_kept"], info["routed_per_image"]) == (1, 112, 102)
+
+
+def test_plan_density_one_is_dense():
+    cfg = get_config("c2").with_(attn_density=1.0, mlp_density=1.0)
+    info = ss.Plan.from_config(cfg).info
+    assert info["tiles_kept"] == info["tiles"] ** 2
+    assert info["realised_density"] == 1.0
+    assert info["routed_per_image"] == 4096
+
+
+def _create(**over):
+    cfg = get_config("c2")
+    d = dict(grid_h=64, grid_w=64, window=0, stripes=4, block=64, global_tokens=64, band_radius=-1,
+             attn_density=0.4, mlp_density=0.4, channels=768, heads=12, head_dim=64, mlp_hidden=3072,
+             max_batch=1, dtype="bf16")
+    d.update(over)
+    return ss.Plan(**d)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(stripes=3), 1),                # 4096 % 3 != 0
+    (dict(block=0), 1),
+    (dict(block=2000), 1),               # > S
+    (dict(global_tokens=32), 1),         # not a multiple of block
+    (dict(attn_density=0.0), 1),
+    (dict(attn_density=1.5), 1),
+    (dict(mlp_density=-0.1), 1),
+    (dict(channels=700), 1),             # != heads * head_dim
+    (dict(max_batch=0), 1),
+    (dict(band_radius=-2), 1),
+    (dict(head_dim=48, channels=576), 2),
+    (dict(channels=1600, heads=20, head_dim=80), 2),
+    (dict(window=128, grid_h=128, grid_w=128, block=64, global_tokens=64), 2),  # 16384 keys in LDS is fine ...
+])
+def test_plan_validation(over, status):
+    if over.get("window") == 128:
+        # 1 window of 16384 tokens: sort keys need 128 KiB + flags: accepted
+        _create(**over)
+        return
+    with pytest.raises(ss.SparseSAMError) as ei:
+        _create(**over)
+    assert ei.value.status == status
+
+
+def test_plan_rejects_sort_beyond_lds():
+    with pytest.raises(ss.SparseSAMError) as ei:
+        _create(grid_h=256, grid_w=256, block=64, global_tokens=64)
+    assert ei.value.status == 2
+
+
+def test_compute_calls_without_device_return_no_device():
+    lib = _lib.load()
+    plan = _create()
+    if plan.info["has_device_copy"]:
+        pytest.skip("a GPU is present")
+    p = ctypes.c_void_p(16)
+    st = lib.sparsesam_permute(plan.handle, p, 1, p, p, p, None)
+    assert st == 6
+    st = lib.sparsesam_attn(plan.handle, 1, p, p, p, p, ctypes.c_float(0.125), None)
+    assert st == 6
+    assert b"no device copy" in lib.sparsesam_last_error()
+
+
+def test_importance_argument_validation_before_launch():
+    lib = _lib.load()
+    p = ctypes.c_void_p(16)
+    assert lib.sparsesam_importance(p, 1, 100, 64, 16, p, None) == 1   # 100 % 16
+    assert lib.sparsesam_importance(p, 1, 64, 64, 64, p, None) == 2    # patch > 32
+    assert lib.sparsesam_importance(None, 1, 64, 64, 16, p, None) == 1
+    assert lib.sparsesam_importance(p, -1, 64, 64, 16, p, None) == 1
+    assert lib.sparsesam_importance(None, 0, 64, 64, 16, None, None) == 0  # empty batch is a no-op
+
+
+def test_null_plan_and_info():
+    lib = _lib.load()
+    assert lib.sparsesam_plan_create(None, None) == 1
+    assert lib.sparsesam_plan_get_info(None, None) == 1
+    lib.sparsesam_plan_destroy(None)

@@ -38,6 +38,12 @@ def test_order_negative_zero_equals_zero():
     assert list(descending_order(v)) == [3, 0, 1, 2]
 
 
+def test_order_invalid_slots_last_even_after_nan():
+    v = np.array([np.nan, 5.0, -1.0, 0.0, 2.0], np.float32)
+    valid = np.array([True, False, True, False, True])
+    assert list(descending_order(v, valid)) == [4, 2, 0, 1, 3]
+
+
 def test_order_nan_after_every_number():
     v = np.array([np.nan, -1.0, 2.0, np.nan, -np.inf, 0.5], np.float32)
     assert list(descending_order(v)) == [2, 5, 1, 4, 0, 3]
@@ -131,7 +137,7 @@ def test_window_pads_never_routed_and_sort_last():
     imp = rng.uniform(size=4096).astype(np.float32)
     tm = window_token_map(64, 64, 14)
     seg = segment_importance(imp, tm[24])  # the corner window: 8 x 8 real
-    s = descending_order(seg)
+    s = descending_order(seg, valid=tm[24] >= 0)
     n_real = int((tm[24] >= 0).sum())
     assert n_real == 64
     assert np.all(tm[24][s[:n_real]] >= 0)
