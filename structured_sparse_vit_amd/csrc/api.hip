@@ -376,7 +376,8 @@ sparsesam_status sparsesam_attn(sparsesam_plan_t p, int32_t segments, const void
 }  // extern "C"
 
 template <typename T>
-static hipError_t run_mlp(const sparsesam_plan& p, float* x, const int32_t* routed, int rows, const float* ln_g,
+static hipError_t run_mlp(const sparsesam_plan& p, float* x, int64_t x_rows, const int32_t* routed, int rows,
+                          const float* ln_g,
                           const float* ln_b, const void* w1, const float* b1, const void* w2, const float* b2,
                           char* ws, hipStream_t st) {
   size_t o_a2, o_hid, o_part;
@@ -386,12 +387,12 @@ static hipError_t run_mlp(const sparsesam_plan& p, float* x, const int32_t* rout
   T* hid = reinterpret_cast<T*>(ws + o_hid);
   float* part = reinterpret_cast<float*>(ws + o_part);
   const int C = p.desc.channels, Hm = p.desc.mlp_hidden;
-  hipError_t e = launch_gather_ln<T>(p, x, rows, nullptr, routed, ln_g, ln_b, a2, st);
+  hipError_t e = launch_gather_ln<T>(p, x, (int)x_rows, rows, nullptr, routed, ln_g, ln_b, a2, st);
   if (e != hipSuccess) return e;
   EpiGelu eg{b1, hid, Hm};
   e = launch_gemm_gelu<T>(a2, (const T*)w1, rows, Hm, C, eg, st);
   if (e != hipSuccess) return e;
-  EpiResidualScatter er{b2, x, nullptr, routed, p.segmap(), C};
+  EpiResidualScatter er{b2, x, nullptr, routed, p.segmap(), C, x_rows};
   return launch_gemm_residual<T>(hid, (const T*)w2, rows, C, Hm, er, splits, part, st);
 }
 
@@ -417,9 +418,9 @@ sparsesam_status sparsesam_mlp(sparsesam_plan_t p, float* x, int64_t rows, const
   }
   hipError_t e;
   if (p->desc.dtype == SPARSESAM_BF16)
-    e = run_mlp<bf16_t>(*p, x, routed, routed_count, ln_g, ln_b, w1, b1, w2, b2, (char*)workspace, (hipStream_t)stream);
+    e = run_mlp<bf16_t>(*p, x, rows, routed, routed_count, ln_g, ln_b, w1, b1, w2, b2, (char*)workspace, (hipStream_t)stream);
   else
-    e = run_mlp<float>(*p, x, routed, routed_count, ln_g, ln_b, w1, b1, w2, b2, (char*)workspace, (hipStream_t)stream);
+    e = run_mlp<float>(*p, x, rows, routed, routed_count, ln_g, ln_b, w1, b1, w2, b2, (char*)workspace, (hipStream_t)stream);
   return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_mlp launch");
 }
 
@@ -437,26 +438,27 @@ static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weigh
   T* k = reinterpret_cast<T*>(ws + L.k);
   T* vt = reinterpret_cast<T*>(ws + L.vt);
   T* o = reinterpret_cast<T*>(ws + L.o);
-  hipError_t e = launch_gather_ln<T>(p, x, M, perm, nullptr, w.ln1_g, w.ln1_b, h, st);
+  const long long x_rows = (long long)batch * p.desc.grid_h * p.desc.grid_w;
+  hipError_t e = launch_gather_ln<T>(p, x, (int)x_rows, M, perm, nullptr, w.ln1_g, w.ln1_b, h, st);
   if (e != hipSuccess) return e;
   EpiQKV eq{w.b_qkv, q, k, vt, p.n, p.n_pad, p.desc.heads, p.desc.head_dim, C};
   e = launch_gemm_qkv<T>(h, (const T*)w.w_qkv, M, C, eq, st);
   if (e != hipSuccess) return e;
   e = launch_attention<T>(p, segs, q, k, vt, o, 1.0f / std::sqrt((float)p.desc.head_dim), st);
   if (e != hipSuccess) return e;
-  EpiResidualScatter er{w.b_proj, x, perm, nullptr, p.segmap(), C};
+  EpiResidualScatter er{w.b_proj, x, perm, nullptr, p.segmap(), C, x_rows};
   e = launch_gemm_residual<T>(o, (const T*)w.w_proj, M, C, C, er, 1, nullptr, st);
   if (e != hipSuccess) return e;
   const int rows = batch * p.routed_per_image;
   T* a2 = reinterpret_cast<T*>(ws + L.a2);
   T* hid = reinterpret_cast<T*>(ws + L.hid);
   float* part = reinterpret_cast<float*>(ws + L.part);
-  e = launch_gather_ln<T>(p, x, rows, nullptr, routed, w.ln2_g, w.ln2_b, a2, st);
+  e = launch_gather_ln<T>(p, x, (int)x_rows, rows, nullptr, routed, w.ln2_g, w.ln2_b, a2, st);
   if (e != hipSuccess) return e;
   EpiGelu eg{w.b1, hid, p.desc.mlp_hidden};
   e = launch_gemm_gelu<T>(a2, (const T*)w.w1, rows, p.desc.mlp_hidden, C, eg, st);
   if (e != hipSuccess) return e;
-  EpiResidualScatter e2{w.b2, x, nullptr, routed, p.segmap(), C};
+  EpiResidualScatter e2{w.b2, x, nullptr, routed, p.segmap(), C, x_rows};
   return launch_gemm_residual<T>(hid, (const T*)w.w2, rows, C, p.desc.mlp_hidden, e2, L.splits, part, st);
 }
 

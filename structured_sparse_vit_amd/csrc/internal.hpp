@@ -78,7 +78,7 @@ hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, 
 // LayerNorm of gathered rows: out[r] = LN(x[src(r)]) for r < rows_out, zero rows for pads.
 // Row source: mode 0 = stripe-sorted segment rows through perm, mode 1 = explicit list.
 template <typename T>
-hipError_t launch_gather_ln(const sparsesam_plan& p, const float* x, int rows_out, const int* perm,
+hipError_t launch_gather_ln(const sparsesam_plan& p, const float* x, int x_rows, int rows_out, const int* perm,
                             const int* list, const float* g, const float* b, T* out, hipStream_t st);
 
 // GEMM C = A W^T with fused epilogues (bf16 matrix cores or fp32 SIMT).
@@ -96,6 +96,7 @@ struct EpiResidualScatter {  // x[map(r)] += acc + bias, or partials when split
   const int* list;  // explicit row list (mode 1), or null
   SegmentMap map;
   int ldx;
+  long long x_rows;  // rows of x; destination rows outside [0, x_rows) are skipped
 };
 struct EpiGelu {  // out[r, c] = GELU(acc + bias)
   const float* bias;

@@ -59,13 +59,14 @@ struct ResidualAdd {
   const int* list;
   SegmentMap map;
   int ldx;
+  long long x_rows;
   __device__ __forceinline__ int dst_row(int r) const {
     if (list) return list[r];
     return map.row_of(r / map.n, perm[r]);
   }
   __device__ __forceinline__ void operator()(int r, int c, float v) const {
     int row = dst_row(r);
-    if (row < 0) return;
+    if (row < 0 || row >= x_rows) return;
     float* px = x + (size_t)row * ldx + c;
     *px = *px + (v + bias[c]);
   }
@@ -296,7 +297,7 @@ template <typename T>
 hipError_t launch_gemm_residual(const T* a, const T* w, int m, int n, int k, const EpiResidualScatter& e, int splits,
                                 float* part, hipStream_t st) {
   if (m <= 0) return hipSuccess;
-  ResidualAdd s{e.bias, e.x, e.perm, e.list, e.map, e.ldx};
+  ResidualAdd s{e.bias, e.x, e.perm, e.list, e.map, e.ldx, e.x_rows};
   if (splits <= 1) return GemmOp<T>::template run<ResidualAdd, false>(a, w, m, n, k, 1, s, nullptr, st);
   hipError_t err = GemmOp<T>::template run<ResidualAdd, true>(a, w, m, n, k, splits, s, part, st);
   if (err != hipSuccess) return err;

@@ -12,7 +12,7 @@ namespace sparsesam {
 constexpr int kMaxPerLane = 24;  // C <= 1536
 
 template <typename T>
-__global__ void __launch_bounds__(256) gather_ln_kernel(const float* __restrict__ x, int rows_out, int C,
+__global__ void __launch_bounds__(256) gather_ln_kernel(const float* __restrict__ x, int x_rows, int rows_out, int C,
                                                         const int* __restrict__ perm, const int* __restrict__ list,
                                                         SegmentMap map, const float* __restrict__ g,
                                                         const float* __restrict__ b, T* __restrict__ out) {
@@ -27,7 +27,7 @@ __global__ void __launch_bounds__(256) gather_ln_kernel(const float* __restrict_
     src = map.row_of(seg, slot);
   }
   T* o = out + (size_t)r * C;
-  if (src < 0) {
+  if (src < 0 || src >= x_rows) {
     for (int c = lane; c < C; c += 64) o[c] = from_f32<T>(0.0f);
     return;
   }
@@ -57,19 +57,19 @@ __global__ void __launch_bounds__(256) gather_ln_kernel(const float* __restrict_
 }
 
 template <typename T>
-hipError_t launch_gather_ln(const sparsesam_plan& p, const float* x, int rows_out, const int* perm, const int* list,
-                            const float* g, const float* b, T* out, hipStream_t st) {
+hipError_t launch_gather_ln(const sparsesam_plan& p, const float* x, int x_rows, int rows_out, const int* perm,
+                            const int* list, const float* g, const float* b, T* out, hipStream_t st) {
   if (rows_out <= 0) return hipSuccess;
   const int C = p.desc.channels;
   dim3 grid((rows_out + 3) / 4);
-  hipLaunchKernelGGL(gather_ln_kernel<T>, grid, dim3(256), 0, st, x, rows_out, C, perm, list, p.segmap(), g, b,
+  hipLaunchKernelGGL(gather_ln_kernel<T>, grid, dim3(256), 0, st, x, x_rows, rows_out, C, perm, list, p.segmap(), g, b,
                      out);
   return hipGetLastError();
 }
 
-template hipError_t launch_gather_ln<float>(const sparsesam_plan&, const float*, int, const int*, const int*,
+template hipError_t launch_gather_ln<float>(const sparsesam_plan&, const float*, int, int, const int*, const int*,
                                             const float*, const float*, float*, hipStream_t);
-template hipError_t launch_gather_ln<bf16_t>(const sparsesam_plan&, const float*, int, const int*, const int*,
+template hipError_t launch_gather_ln<bf16_t>(const sparsesam_plan&, const float*, int, int, const int*, const int*,
                                              const float*, const float*, bf16_t*, hipStream_t);
 
 }  // namespace sparsesam

@@ -61,7 +61,8 @@ __global__ void __launch_bounds__(1024) stripe_permute_kernel(const float* __res
         int i = (t / j) * (2 * j) + (t % j);
         int l = i + j;
         unsigned long long a = keys[i], b = keys[l];
-        bool up = ((i & k) == 0);
+        // direction from the index inside the segment, so every segment ends ascending
+        bool up = (((i & (p2 - 1)) & k) == 0);
         if ((a > b) == up) {
           keys[i] = b;
           keys[l] = a;
@@ -82,8 +83,8 @@ __global__ void __launch_bounds__(1024) stripe_permute_kernel(const float* __res
     inv[base + slot] = p;
     if (p < seg_k[sg]) {  // rank p of the plain order is in the keep-set
       int slot_r = (int)(uint32_t)keys[sg * p2 + p];
-      int row = map.row_of(img * segs + sg, slot_r);
-      flag[row - img * tokens] = 1;
+      int row = map.row_of(img * segs + sg, slot_r) - img * tokens;
+      if (row >= 0 && row < tokens) flag[row] = 1;
     }
   }
   __syncthreads();

@@ -215,6 +215,13 @@ def test_block_parity(key):
     assert np.array_equal(r["perm"], np.stack(r["parts"]["perm"]))
     assert np.array_equal(r["inv"], np.stack(r["parts"]["inv"]))
     assert np.array_equal(r["routed"], np.concatenate(r["parts"]["routed"]))
+    C = config(key).channels
+    err = np.abs(r["got"] - r["want"]).reshape(-1, C)
+    routed = np.concatenate(r["parts"]["routed"])
+    other = np.setdiff1d(np.arange(err.shape[0]), routed)
+    _say("  block %s: max err routed rows %.3e, other rows %.3e, worst row %d, worst channel %d" % (
+        key, err[routed].max(), err[other].max() if other.size else 0.0, err.max(axis=1).argmax(),
+        err.max(axis=0).argmax()))
     check_close(r["got"], r["want"], what="block " + key)
     # the block's own contribution, a stricter view than the residual sum
     check_close(r["got"] - r["x"], r["want"] - r["x"], max_abs=1e-2, rel_l2=2e-2, what="block delta " + key)
