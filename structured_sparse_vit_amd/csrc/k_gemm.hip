@@ -23,19 +23,20 @@ struct QKVStore {
   const float* bias;
   T *q, *k, *vt;
   int n, n_pad, heads, D, C;
+  // One unconditional store through a selected base pointer and index. (A three-way
+  // if / else-if / else with a store in each arm was compiled for gfx950 into code
+  // that sent the V^T stores through the k pointer; selects avoid that shape.)
   __device__ __forceinline__ void operator()(int r, int c, float v) const {
     v += bias[c];
-    int which = c / C;
-    int cc = c - which * C;
-    int h = cc / D, d = cc - (cc / D) * D;
-    int seg = r / n, p = r - (r / n) * n;
-    size_t sh = (size_t)seg * heads + h;
-    if (which == 0)
-      q[(sh * n + p) * D + d] = from_f32<T>(v);
-    else if (which == 1)
-      k[(sh * n + p) * D + d] = from_f32<T>(v);
-    else
-      vt[(sh * D + d) * n_pad + p] = from_f32<T>(v);
+    const int which = c / C;
+    const int cc = c - which * C;
+    const int h = cc / D, d = cc - h * D;
+    const int seg = r / n, p = r - seg * n;
+    const size_t sh = (size_t)seg * heads + h;
+    const bool is_v = which >= 2;
+    const size_t idx = is_v ? (sh * D + d) * (size_t)n_pad + p : (sh * n + p) * (size_t)D + d;
+    T* base = is_v ? vt : (which == 0 ? q : k);
+    base[idx] = from_f32<T>(v);
   }
   // Column tile [c0, c0 + BN) is all V: store it transposed.
   __device__ __forceinline__ bool transposed_tile(int c0) const { return c0 >= 2 * C; }

@@ -66,10 +66,13 @@ def token_features(cfg, seed: int = 0) -> np.ndarray:
     return rng.standard_normal((cfg.batch, g, g, cfg.channels), dtype=np.float32)
 
 
-def block_weights(cfg, seed: int = 0, layer: int = 0) -> dict:
+def block_weights(cfg, seed: int = 0, layer: int = 0, gain: float = 1.0) -> dict:
     """Parameters of one pre-LN ViT block, matrices in [out, in] layout.
 
     Matrices and biases ~ N(0, 0.02); LayerNorm gamma = 1 + N(0, 0.02), beta ~ N(0, 0.02).
+    ``gain`` scales the projection matrices (w_qkv, w_proj, w1, w2): tests use gain > 1 so
+    the attention and MLP branches are large next to the residual and a mistake in either
+    stands out.
     For bf16 configs every matrix and bias is rounded to bf16 values (still stored as
     fp32 here), so that both sides read exactly the same numbers.
     """
@@ -93,6 +96,9 @@ def block_weights(cfg, seed: int = 0, layer: int = 0) -> dict:
         "w2": n(C, Hm),
         "b2": n(C),
     }
+    if gain != 1.0:
+        for k in ("w_qkv", "w_proj", "w1", "w2"):
+            w[k] = (w[k] * np.float32(gain)).astype(np.float32)
     if cfg.dtype == "bf16":
         for k in ("w_qkv", "b_qkv", "w_proj", "b_proj", "w1", "b1", "w2", "b2"):
             w[k] = round_to_bf16(w[k])

@@ -41,13 +41,19 @@ def oracle_importance(key, seed=0, noise=0.05):
 
 
 @functools.lru_cache(maxsize=None)
-def oracle_block(key, seed=0):
+def oracle_block(key, seed=0, gain=1.0):
     cfg = config(key)
     x = token_features(cfg, seed)
-    w = block_weights(cfg, seed)
+    w = block_weights(cfg, seed, gain=gain)
     imp = oracle_importance(key, seed)
     out, parts = oracle.block_forward(x, imp, w, cfg, return_parts=True)
     return x, w, imp, out, parts
+
+
+def rel_l2(got, want):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    return float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30))
 
 
 def check_close(got, want, max_abs=MAX_ABS, rel_l2=REL_L2, what=""):

@@ -12,7 +12,7 @@ import torch
 import oracle
 import structured_sparse_vit_amd as ss
 from synth import round_to_bf16
-from tests.gpu_cases import check_close, config, images, oracle_block, oracle_importance
+from tests.gpu_cases import check_close, config, images, oracle_block, oracle_importance, rel_l2
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -191,8 +191,8 @@ def test_mlp_empty_keep_set_is_noop():
 
 # ------------------------------------------------------------------ whole block
 
-def _run_block(key, seed=0):
-    x, w, imp, want, parts = oracle_block(key, seed)
+def _run_block(key, seed=0, gain=1.0):
+    x, w, imp, want, parts = oracle_block(key, seed, gain)
     cfg = config(key)
     plan = _plan(cfg)
     img = torch.from_numpy(images(key, seed)).to(DEV)
@@ -207,24 +207,46 @@ def _run_block(key, seed=0):
                 img=img)
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3", "ragged", "c4g", "c4w"])
-def test_block_parity(key):
-    _say("block", key)
-    r = _run_block(key)
+# Branch bars: the attention branch alone (x2 - x on rows outside the keep-set) and the
+# whole block delta, relative L2 against the oracle's. bf16 operands give about 2^-9
+# relative rounding per stage; fp32 runs are held far tighter.
+BRANCH_REL = {"bf16": 1.5e-2, "f32": 1e-4}
+
+
+def _check_block(key, r, gain):
+    cfg = config(key)
+    C = cfg.channels
     assert np.array_equal(r["imp_d"].view(np.uint32), r["imp"].view(np.uint32))
     assert np.array_equal(r["perm"], np.stack(r["parts"]["perm"]))
     assert np.array_equal(r["inv"], np.stack(r["parts"]["inv"]))
     assert np.array_equal(r["routed"], np.concatenate(r["parts"]["routed"]))
-    C = config(key).channels
-    err = np.abs(r["got"] - r["want"]).reshape(-1, C)
+    got, want, x = (a.reshape(-1, C) for a in (r["got"], r["want"], r["x"]))
     routed = np.concatenate(r["parts"]["routed"])
-    other = np.setdiff1d(np.arange(err.shape[0]), routed)
-    _say("  block %s: max err routed rows %.3e, other rows %.3e, worst row %d, worst channel %d" % (
-        key, err[routed].max(), err[other].max() if other.size else 0.0, err.max(axis=1).argmax(),
-        err.max(axis=0).argmax()))
-    check_close(r["got"], r["want"], what="block " + key)
-    # the block's own contribution, a stricter view than the residual sum
-    check_close(r["got"] - r["x"], r["want"] - r["x"], max_abs=1e-2, rel_l2=2e-2, what="block delta " + key)
+    other = np.setdiff1d(np.arange(got.shape[0]), routed)
+    err = np.abs(got - want)
+    attn_rel = rel_l2(got[other] - x[other], want[other] - x[other])
+    delta_rel = rel_l2(got - x, want - x)
+    _say("  block %s gain %g: max err routed %.3e other %.3e | rel-L2 attention branch %.3e, block delta %.3e" % (
+        key, gain, err[routed].max(), err[other].max() if other.size else 0.0, attn_rel, delta_rel))
+    if gain == 1.0:
+        check_close(got, want, what="block " + key)
+    bar = BRANCH_REL[cfg.dtype]
+    assert attn_rel <= bar, "block %s: attention branch rel-L2 %.3e > %.1e" % (key, attn_rel, bar)
+    assert delta_rel <= bar, "block %s: block delta rel-L2 %.3e > %.1e" % (key, delta_rel, bar)
+
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "ragged", "c4g", "c4w"])
+def test_block_parity(key):
+    _say("block", key)
+    _check_block(key, _run_block(key), 1.0)
+
+
+@pytest.mark.parametrize("key,gain", [("c1", 10.0), ("c2", 3.0), ("c3b1", 3.0), ("ragged", 3.0)])
+def test_block_parity_high_gain(key, gain):
+    """Projection weights scaled up: the attention and MLP branches dominate the residual.
+    (bf16 runs use a gain of 3 so the softmax stays far from one-hot.)"""
+    _say("block high gain", key)
+    _check_block(key, _run_block(key, gain=gain), gain)
 
 
 def test_block_is_deterministic():
