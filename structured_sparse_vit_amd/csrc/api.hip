@@ -35,31 +35,13 @@ static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 static size_t elem_size(const sparsesam_plan& p) { return p.desc.dtype == SPARSESAM_BF16 ? 2 : 4; }
 
-int mlp_splits(const sparsesam_plan& p, int rows) {
-  if (p.desc.dtype != SPARSESAM_BF16 || rows <= 0) return 1;
-  const int tiles = ((rows + 127) / 128) * ((p.desc.channels + 127) / 128);
-  const int nk = p.desc.mlp_hidden / 64;
-  static const int cand[] = {1, 2, 3, 4, 6, 8, 12, 16};
-  int best = 1;
-  for (int s : cand) {
-    if (nk % s != 0) continue;
-    best = s;
-    if (tiles * s >= 448) break;
-  }
-  return best;
-}
-
-size_t mlp_workspace(const sparsesam_plan& p, int rows, size_t* a2, size_t* hid, size_t* part, int* splits) {
+size_t mlp_workspace(const sparsesam_plan& p, int rows, size_t* a2, size_t* hid) {
   const size_t es = elem_size(p);
-  const int s = mlp_splits(p, rows);
   size_t off = 0;
   *a2 = off;
   off += align256((size_t)rows * p.desc.channels * es);
   *hid = off;
   off += align256((size_t)rows * p.desc.mlp_hidden * es);
-  *part = off;
-  if (s > 1) off += align256((size_t)s * rows * p.desc.channels * 4);
-  *splits = s;
   return off;
 }
 
@@ -81,7 +63,7 @@ BlockLayout block_layout(const sparsesam_plan& p, int batch) {
   L.o = off;
   off += align256(M * C * es);
   L.total_attn = off;
-  L.total_mlp = mlp_workspace(p, batch * p.routed_per_image, &L.a2, &L.hid, &L.part, &L.splits);
+  L.total_mlp = mlp_workspace(p, batch * p.routed_per_image, &L.a2, &L.hid);
   return L;
 }
 
@@ -245,9 +227,8 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
   }
   BlockLayout L = block_layout(*p, d.max_batch);
   p->block_ws = std::max(L.total_attn, L.total_mlp);
-  size_t a2, hid, part;
-  int splits;
-  p->mlp_ws = mlp_workspace(*p, d.max_batch * p->routed_per_image, &a2, &hid, &part, &splits);
+  size_t a2, hid;
+  p->mlp_ws = mlp_workspace(*p, d.max_batch * p->routed_per_image, &a2, &hid);
 
   // device copy, when a device is present
   int ndev = 0;
@@ -380,12 +361,10 @@ static hipError_t run_mlp(const sparsesam_plan& p, float* x, int64_t x_rows, con
                           const float* ln_g,
                           const float* ln_b, const void* w1, const float* b1, const void* w2, const float* b2,
                           char* ws, hipStream_t st) {
-  size_t o_a2, o_hid, o_part;
-  int splits;
-  mlp_workspace(p, rows, &o_a2, &o_hid, &o_part, &splits);
+  size_t o_a2, o_hid;
+  mlp_workspace(p, rows, &o_a2, &o_hid);
   T* a2 = reinterpret_cast<T*>(ws + o_a2);
   T* hid = reinterpret_cast<T*>(ws + o_hid);
-  float* part = reinterpret_cast<float*>(ws + o_part);
   const int C = p.desc.channels, Hm = p.desc.mlp_hidden;
   hipError_t e = launch_gather_ln<T>(p, x, (int)x_rows, rows, nullptr, routed, ln_g, ln_b, a2, st);
   if (e != hipSuccess) return e;
@@ -393,7 +372,7 @@ static hipError_t run_mlp(const sparsesam_plan& p, float* x, int64_t x_rows, con
   e = launch_gemm_gelu<T>(a2, (const T*)w1, rows, Hm, C, eg, st);
   if (e != hipSuccess) return e;
   EpiResidualScatter er{b2, x, nullptr, routed, p.segmap(), C, x_rows};
-  return launch_gemm_residual<T>(hid, (const T*)w2, rows, C, Hm, er, splits, part, st);
+  return launch_gemm_residual<T>(hid, (const T*)w2, rows, C, Hm, er, st);
 }
 
 extern "C" {
@@ -409,9 +388,8 @@ sparsesam_status sparsesam_mlp(sparsesam_plan_t p, float* x, int64_t rows, const
     return invalid("routed_count exceeds max_batch * routed_per_image");
   if (routed_count == 0) return SPARSESAM_OK;
   if (!x || !routed || !ln_g || !ln_b || !w1 || !b1 || !w2 || !b2) return invalid("null pointer argument");
-  size_t a2, hid, part;
-  int splits;
-  size_t need = mlp_workspace(*p, routed_count, &a2, &hid, &part, &splits);
+  size_t a2, hid;
+  size_t need = mlp_workspace(*p, routed_count, &a2, &hid);
   if (!workspace || workspace_bytes < need) {
     set_error("mlp workspace needs " + std::to_string(need) + " bytes");
     return SPARSESAM_ERR_WORKSPACE;
@@ -447,19 +425,18 @@ static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weigh
   e = launch_attention<T>(p, segs, q, k, vt, o, 1.0f / std::sqrt((float)p.desc.head_dim), st);
   if (e != hipSuccess) return e;
   EpiResidualScatter er{w.b_proj, x, perm, nullptr, p.segmap(), C, x_rows};
-  e = launch_gemm_residual<T>(o, (const T*)w.w_proj, M, C, C, er, 1, nullptr, st);
+  e = launch_gemm_residual<T>(o, (const T*)w.w_proj, M, C, C, er, st);
   if (e != hipSuccess) return e;
   const int rows = batch * p.routed_per_image;
   T* a2 = reinterpret_cast<T*>(ws + L.a2);
   T* hid = reinterpret_cast<T*>(ws + L.hid);
-  float* part = reinterpret_cast<float*>(ws + L.part);
   e = launch_gather_ln<T>(p, x, (int)x_rows, rows, nullptr, routed, w.ln2_g, w.ln2_b, a2, st);
   if (e != hipSuccess) return e;
   EpiGelu eg{w.b1, hid, p.desc.mlp_hidden};
   e = launch_gemm_gelu<T>(a2, (const T*)w.w1, rows, p.desc.mlp_hidden, C, eg, st);
   if (e != hipSuccess) return e;
   EpiResidualScatter e2{w.b2, x, nullptr, routed, p.segmap(), C, x_rows};
-  return launch_gemm_residual<T>(hid, (const T*)w.w2, rows, C, p.desc.mlp_hidden, e2, L.splits, part, st);
+  return launch_gemm_residual<T>(hid, (const T*)w.w2, rows, C, p.desc.mlp_hidden, e2, st);
 }
 
 extern "C" {

@@ -62,12 +62,10 @@ sparsesam_status hip_fail(hipError_t e, const char* where);
 // Workspace carve-up of sparsesam_block / sparsesam_mlp.
 struct BlockLayout {
   size_t h = 0, q = 0, k = 0, vt = 0, o = 0, total_attn = 0;
-  size_t a2 = 0, hid = 0, part = 0, total_mlp = 0;
-  int splits = 1;
+  size_t a2 = 0, hid = 0, total_mlp = 0;
 };
 BlockLayout block_layout(const sparsesam_plan& p, int batch);
-size_t mlp_workspace(const sparsesam_plan& p, int routed_rows, size_t* a2, size_t* hid, size_t* part, int* splits);
-int mlp_splits(const sparsesam_plan& p, int routed_rows);
+size_t mlp_workspace(const sparsesam_plan& p, int routed_rows, size_t* a2, size_t* hid);
 
 // ---- launches (each returns hipSuccess or the launch error) ----
 hipError_t launch_importance(const float* img, int batch, int height, int width, int patch, float* imp,
@@ -108,11 +106,10 @@ template <typename T>
 hipError_t launch_gemm_qkv(const T* a, const T* w, int m, int k, const EpiQKV& e, hipStream_t st);
 template <typename T>
 hipError_t launch_gemm_gelu(const T* a, const T* w, int m, int n, int k, const EpiGelu& e, hipStream_t st);
-// Residual GEMM: when splits > 1, partial sums go to `part` [splits, m, n] fp32 and a
-// reduction adds them in split order, then the bias, into x.
+// Residual GEMM: x[dst(r)] += A W^T + bias, each element written once (deterministic).
 template <typename T>
 hipError_t launch_gemm_residual(const T* a, const T* w, int m, int n, int k, const EpiResidualScatter& e,
-                                int splits, float* part, hipStream_t st);
+                                hipStream_t st);
 
 template <typename T>
 hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,

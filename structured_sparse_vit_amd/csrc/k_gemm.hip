@@ -5,13 +5,18 @@
 // weights). bf16 operands run on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16,
 // fp32 accumulation); the fp32 path is a plain SIMT kernel for small exact checks.
 //
-// bf16 kernel: 128 x 128 output tile per 256-thread workgroup, K step 64. A and W
-// tiles are staged through LDS (rows padded by 16 bytes so the 16-byte fragment
-// reads of 32 consecutive rows hit distinct banks); the next K step is prefetched
-// into registers while the current one is multiplied. Each wavefront owns a 64 x 64
-// quarter as 2 x 2 MFMA blocks. Workgroups whose columns are all V columns of the QKV
-// product swap the MFMA operands so each lane holds consecutive tokens of one
-// channel, which is the layout of the transposed V the attention kernel reads.
+// bf16 kernel: BM x BN output tile (128 x 128 or 128 x 64) per 256-thread workgroup,
+// K step 64, four wavefronts in a 2 x 2 layout each owning a (BM/2) x (BN/2) block of
+// 32 x 32 MFMA tiles. A and W tiles go global -> registers -> LDS, double-buffered in
+// LDS with one barrier per K step: the next step's global loads are in flight while
+// the current step multiplies. LDS rows are padded by 16 bytes so the 16-byte fragment
+// reads of 32 consecutive rows hit distinct banks.
+//
+// Epilogue: the fp32 tile is staged in LDS, then written out as 16-byte chunks along
+// the destination's contiguous axis -- 8 channels of one token for q, k, the MLP
+// hidden activation and the residual stream, 8 tokens of one channel for the
+// transposed V the attention kernel reads -- so every store is a full vector store
+// and the index decoding (token -> segment, column -> head) runs once per chunk.
 #include "internal.hpp"
 
 namespace sparsesam {
@@ -19,14 +24,31 @@ namespace sparsesam {
 // ---------------------------------------------------------------- epilogues
 
 template <typename T>
+__device__ __forceinline__ void store8(T* dst, const float* v);
+template <>
+__device__ __forceinline__ void store8<bf16_t>(bf16_t* dst, const float* v) {
+  bf16x8 p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = to_bf16(v[i]);
+  *reinterpret_cast<bf16x8*>(dst) = p;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float* dst, const float* v) {
+  *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// q, k [seg, H, N, D] and V^T [seg, H, D, N_pad] from the columns of the QKV product.
+template <typename T>
 struct QKVStore {
   const float* bias;
   T *q, *k, *vt;
   int n, n_pad, heads, D, C;
-  // One unconditional store through a selected base pointer and index. (A three-way
-  // if / else-if / else with a store in each arm was compiled for gfx950 into code
-  // that sent the V^T stores through the k pointer; selects avoid that shape.)
-  __device__ __forceinline__ void operator()(int r, int c, float v) const {
+
+  // One store through a selected base pointer and index. (A three-way if / else-if /
+  // else with a store in each arm was compiled for gfx950 into code that sent the V^T
+  // stores through the k pointer; selects avoid that shape.)
+  __device__ __forceinline__ void elem(int r, int c, float v) const {
     v += bias[c];
     const int which = c / C;
     const int cc = c - which * C;
@@ -38,21 +60,69 @@ struct QKVStore {
     T* base = is_v ? vt : (which == 0 ? q : k);
     base[idx] = from_f32<T>(v);
   }
-  // Column tile [c0, c0 + BN) is all V: store it transposed.
-  __device__ __forceinline__ bool transposed_tile(int c0) const { return c0 >= 2 * C; }
+  // Tiles whose columns are all V columns are written along tokens.
+  __device__ __forceinline__ bool col_tile(int c0) const { return c0 >= 2 * C; }
+  // Eight channels c..c+7 of token r (c % 8 == 0 and D % 8 == 0: one head, one part).
+  __device__ __forceinline__ void row8(int r, int c, const float* v) const {
+    const int which = c / C;
+    if (which >= 2) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) elem(r, c + i, v[i]);
+      return;
+    }
+    const int cc = c - which * C;
+    const int h = cc / D, d = cc - h * D;
+    const int seg = r / n, p = r - seg * n;
+    const size_t sh = (size_t)seg * heads + h;
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = v[i] + bias[c + i];
+    T* base = which == 0 ? q : k;
+    store8<T>(base + (sh * n + p) * (size_t)D + d, w);
+  }
+  // Eight tokens r..r+7 (r % 8 == 0, count of them below M) of channel c.
+  __device__ __forceinline__ void col8(int r, int c, const float* v, int count) const {
+    const int seg = r / n, p = r - seg * n;
+    const int which = c / C;
+    if (which == 2 && count == 8 && p + 8 <= n && (p & 7) == 0) {
+      const int cc = c - 2 * C;
+      const int h = cc / D, d = cc - h * D;
+      const size_t sh = (size_t)seg * heads + h;
+      const float b = bias[c];
+      float w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = v[i] + b;
+      store8<T>(vt + (sh * D + d) * (size_t)n_pad + p, w);
+      return;
+    }
+    for (int i = 0; i < count; ++i) elem(r + i, c, v[i]);
+  }
 };
 
+// Hidden activation of the routed MLP: out[r, c] = GELU(acc + bias).
 template <typename T>
 struct GeluStore {
   const float* bias;
   T* out;
   int ld;
-  __device__ __forceinline__ void operator()(int r, int c, float v) const {
+  __device__ __forceinline__ void elem(int r, int c, float v) const {
     out[(size_t)r * ld + c] = from_f32<T>(gelu_erf(v + bias[c]));
   }
-  __device__ __forceinline__ bool transposed_tile(int) const { return false; }
+  __device__ __forceinline__ bool col_tile(int) const { return false; }
+  __device__ __forceinline__ void row8(int r, int c, const float* v) const {
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = gelu_erf(v[i] + bias[c + i]);
+    store8<T>(out + (size_t)r * ld + c, w);
+  }
+  __device__ __forceinline__ void col8(int r, int c, const float* v, int count) const {
+    for (int i = 0; i < count; ++i) elem(r + i, c, v[i]);
+  }
 };
 
+// Residual update of the fp32 stream: x[dst(r), c] += acc + bias, where dst maps a
+// stripe-sorted row back to its token (through perm and the segment map; pads have
+// no destination) or takes it from an explicit row list (the keep-set).
 struct ResidualAdd {
   const float* bias;
   float* x;
@@ -65,146 +135,202 @@ struct ResidualAdd {
     if (list) return list[r];
     return map.row_of(r / map.n, perm[r]);
   }
-  __device__ __forceinline__ void operator()(int r, int c, float v) const {
-    int row = dst_row(r);
+  __device__ __forceinline__ void elem(int r, int c, float v) const {
+    const int row = dst_row(r);
     if (row < 0 || row >= x_rows) return;
     float* px = x + (size_t)row * ldx + c;
     *px = *px + (v + bias[c]);
   }
-  __device__ __forceinline__ bool transposed_tile(int) const { return false; }
-};
-
-// Partial sums of a split-K product: part[z][r][c].
-struct PartialStore {
-  float* part;
-  int m, n;
-  int z;
-  __device__ __forceinline__ void operator()(int r, int c, float v) const {
-    part[((size_t)z * m + r) * n + c] = v;
+  __device__ __forceinline__ bool col_tile(int) const { return false; }
+  __device__ __forceinline__ void row8(int r, int c, const float* v) const {
+    const int row = dst_row(r);
+    if (row < 0 || row >= x_rows) return;
+    f32x4* px = reinterpret_cast<f32x4*>(x + (size_t)row * ldx + c);
+    f32x4 a = px[0], b = px[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = a[i] + (v[i] + bias[c + i]);
+      b[i] = b[i] + (v[4 + i] + bias[c + 4 + i]);
+    }
+    px[0] = a;
+    px[1] = b;
   }
-  __device__ __forceinline__ bool transposed_tile(int) const { return false; }
+  __device__ __forceinline__ void col8(int r, int c, const float* v, int count) const {
+    for (int i = 0; i < count; ++i) elem(r + i, c, v[i]);
+  }
 };
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM
 
-constexpr int BM = 128, BN = 128, BK = 64, LDS_LD = BK + 8;
+constexpr int BK = 64, LDS_LD = BK + 8;
 
-template <class Epi, bool kPartial>
-__global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
-                                                        int M, int N, int K, int k_split, Epi epi, float* part) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDS_LD];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[BN * LDS_LD];
+template <int BM, int BN>
+struct Tile {
+  static constexpr int WM = BM / 2, WN = BN / 2;  // wave block (2 x 2 waves)
+  static constexpr int MI = WM / 32, NI = WN / 32;
+  static constexpr int A_CHUNKS = BM * 8 / 256;  // 16-byte chunks per thread per K step
+  static constexpr int B_CHUNKS = BN * 8 / 256;
+  static constexpr int STAGE = (BM + BN) * LDS_LD;  // bf16 elements per stage
+  static constexpr int CT_LD = BN + 4;               // fp32 epilogue tile row stride
+  static constexpr int CTT_LD = BM + 4;              // ... of the transposed tile (V^T tiles)
+  static constexpr int STAGE_BYTES = 2 * STAGE * 2;
+  static constexpr int CT_BYTES = (BM * CT_LD > BN * CTT_LD ? BM * CT_LD : BN * CTT_LD) * 4;
+  static constexpr int LDS_BYTES = STAGE_BYTES > CT_BYTES ? STAGE_BYTES : CT_BYTES;
+};
+
+// The main loop and epilogue of one tile. TR: the tile's columns are written along
+// tokens (V^T), so the MFMA operands are swapped and the block accumulates C^T.
+template <int BM, int BN, bool TR, class Epi>
+__device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, int M,
+                                               int N, int K, const Epi& epi, char* smem) {
+  using TL = Tile<BM, BN>;
+  constexpr bool tr = TR;
+  bf16_t* stage = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const int kz = blockIdx.z;
-  const int kb = kz * k_split, ke = min(K, kb + k_split);
   const int wm = wave >> 1, wn = wave & 1;
 
-  f32x16 acc[2][2];
+  f32x16 acc[TL::MI][TL::NI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TL::NI; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // global -> register staging: 4 x 16 bytes of A and of W per thread
-  i32x4 ra[4], rb[4];
-  auto load_tile = [&](int k0) {
+  i32x4 ra[TL::A_CHUNKS], rb[TL::B_CHUNKS];
+  auto load_global = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + 256 * i;
-      int row = c >> 3, col = (c & 7) * 8;
-      int gm = m0 + row, gn = n0 + row;
+    for (int i = 0; i < TL::A_CHUNKS; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
+      const int gm = m0 + row;
       ra[i] = (gm < M) ? *reinterpret_cast<const i32x4*>(A + (size_t)gm * K + k0 + col) : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < TL::B_CHUNKS; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
+      const int gn = n0 + row;
       rb[i] = (gn < N) ? *reinterpret_cast<const i32x4*>(W + (size_t)gn * K + k0 + col) : i32x4{0, 0, 0, 0};
     }
   };
-  auto store_tile = [&]() {
+  auto store_lds = [&](int s) {
+    bf16_t* As = stage + s * TL::STAGE;
+    bf16_t* Bs = As + BM * LDS_LD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + 256 * i;
-      int row = c >> 3, col = (c & 7) * 8;
+    for (int i = 0; i < TL::A_CHUNKS; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
       *reinterpret_cast<i32x4*>(As + row * LDS_LD + col) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < TL::B_CHUNKS; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
       *reinterpret_cast<i32x4*>(Bs + row * LDS_LD + col) = rb[i];
     }
   };
 
-  const bool tr = epi.transposed_tile(n0);
-  if (kb < ke) load_tile(kb);
-  for (int k0 = kb; k0 < ke; k0 += BK) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (k0 + BK < ke) load_tile(k0 + BK);
+  const int nk = K / BK;
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_global((kt + 1) * BK);
+    const bf16_t* As = stage + cur * TL::STAGE;
+    const bf16_t* Bs = As + BM * LDS_LD;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[TL::MI], bfr[TL::NI];
+      const int col = ks * 16 + (lane >> 5) * 8;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int ar = wm * 64 + i * 32 + (lane & 31);
-        int br = wn * 64 + i * 32 + (lane & 31);
-        int col = ks * 16 + (lane >> 5) * 8;
-        af[i] = *reinterpret_cast<const bf16x8*>(As + ar * LDS_LD + col);
-        bfr[i] = *reinterpret_cast<const bf16x8*>(Bs + br * LDS_LD + col);
-      }
-      if (!tr) {
+      for (int i = 0; i < TL::MI; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(As + (wm * TL::WM + i * 32 + (lane & 31)) * LDS_LD + col);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < TL::NI; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * TL::WN + j * 32 + (lane & 31)) * LDS_LD + col);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      } else {
+      for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-      }
+        for (int j = 0; j < TL::NI; ++j) {
+          if constexpr (!TR)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        }
     }
+    if (kt + 1 < nk) store_lds(cur ^ 1);
+    __syncthreads();
   }
 
-  // epilogue: lane holds column (lane & 31) of four row quads of each 32 x 32 block
+  // Stage the fp32 tile in LDS. A lane holds one column of four row quads per 32 x 32
+  // block; on transposed tiles the block holds C^T, and the tile is staged as C^T
+  // ([BN][BM + 4]) so both the stores here and the chunk reads below run along rows.
+  float* ct = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TL::NI; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        int inner = (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        int outer = lane & 31;
-        int m, n;
-        if (!tr) {
-          m = m0 + wm * 64 + i * 32 + inner;
-          n = n0 + wn * 64 + j * 32 + outer;
-        } else {
-          n = n0 + wn * 64 + j * 32 + inner;
-          m = m0 + wm * 64 + i * 32 + outer;
-        }
-        if (m < M && n < N) {
-          if (kPartial) {
-            part[((size_t)kz * M + m) * N + n] = acc[i][j][e];
-          } else {
-            epi(m, n, acc[i][j][e]);
-          }
-        }
+        const int inner = (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        const int outer = lane & 31;
+        if constexpr (!TR)
+          ct[(wm * TL::WM + i * 32 + inner) * TL::CT_LD + wn * TL::WN + j * 32 + outer] = acc[i][j][e];
+        else
+          ct[(wn * TL::WN + j * 32 + inner) * TL::CTT_LD + wm * TL::WM + i * 32 + outer] = acc[i][j][e];
       }
+  __syncthreads();
+  if constexpr (!TR) {
+    for (int idx = tid; idx < BM * (BN / 8); idx += 256) {
+      const int ml = idx / (BN / 8), nl = (idx - ml * (BN / 8)) * 8;
+      const int m = m0 + ml, n = n0 + nl;
+      if (m >= M || n >= N) continue;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(ct + ml * TL::CT_LD + nl);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(ct + ml * TL::CT_LD + nl + 4);
+      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      if (n + 8 <= N) {
+        epi.row8(m, n, v);
+      } else {
+        for (int i = 0; i < N - n; ++i) epi.elem(m, n + i, v[i]);
+      }
+    }
+  } else {
+    for (int idx = tid; idx < BN * (BM / 8); idx += 256) {
+      const int nl = idx / (BM / 8), ml = (idx - nl * (BM / 8)) * 8;
+      const int m = m0 + ml, n = n0 + nl;
+      if (m >= M || n >= N) continue;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(ct + nl * TL::CTT_LD + ml);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(ct + nl * TL::CTT_LD + ml + 4);
+      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      epi.col8(m, n, v, min(8, M - m));
+    }
+  }
+}
+
+template <int BM, int BN, class Epi>
+__global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
+                                                        int M, int N, int K, Epi epi) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  if (epi.col_tile(blockIdx.x * BN))
+    gemm_bf16_tile<BM, BN, true>(A, W, M, N, K, epi, smem);
+  else
+    gemm_bf16_tile<BM, BN, false>(A, W, M, N, K, epi, smem);
 }
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
 
 constexpr int FT = 64, FK = 16;
 
-template <class Epi, bool kPartial>
+template <class Epi>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
-                                                       int M, int N, int K, int k_split, Epi epi, float* part) {
+                                                       int M, int N, int K, Epi epi) {
   __shared__ float As[FK][FT + 1];
   __shared__ float Bs[FK][FT + 1];
   const int tid = threadIdx.x;
   const int n0 = blockIdx.x * FT, m0 = blockIdx.y * FT;
-  const int kz = blockIdx.z;
-  const int kb = kz * k_split, ke = min(K, kb + k_split);
+  const int ke = K;
   const int tr = tid / 16, tc = tid % 16;
   float acc[4][4] = {};
-  for (int k0 = kb; k0 < ke; k0 += FK) {
+  for (int k0 = 0; k0 < ke; k0 += FK) {
     for (int i = tid; i < FT * FK; i += 256) {
       int row = i / FK, kk = i % FK;
       int gm = m0 + row, gn = n0 + row, gk = k0 + kk;
@@ -232,80 +358,58 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       int m = m0 + tr + 16 * i, n = n0 + tc + 16 * j;
-      if (m < M && n < N) {
-        if (kPartial)
-          part[((size_t)kz * M + m) * N + n] = acc[i][j];
-        else
-          epi(m, n, acc[i][j]);
-      }
+      if (m < M && n < N) epi.elem(m, n, acc[i][j]);
     }
-}
-
-// ---------------------------------------------------------------- split-K reduction
-
-__global__ void __launch_bounds__(256) splitk_residual_kernel(const float* __restrict__ part, int splits, int M, int N,
-                                                              ResidualAdd epi) {
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (size_t)M * N) return;
-  int r = (int)(i / N), c = (int)(i - (size_t)r * N);
-  float s = part[i];
-  for (int z = 1; z < splits; ++z) s += part[(size_t)z * M * N + i];
-  epi(r, c, s);
 }
 
 // ---------------------------------------------------------------- launchers
 
-template <typename T>
-struct GemmOp;
-template <>
-struct GemmOp<bf16_t> {
-  template <class Epi, bool P>
-  static hipError_t run(const bf16_t* a, const bf16_t* w, int m, int n, int k, int splits, const Epi& e, float* part,
-                        hipStream_t st) {
-    int ksplit = ((k / splits + BK - 1) / BK) * BK;
-    dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM, splits);
-    hipLaunchKernelGGL((gemm_bf16_kernel<Epi, P>), grid, dim3(256), 0, st, a, w, m, n, k, ksplit, e, part);
-    return hipGetLastError();
-  }
-};
-template <>
-struct GemmOp<float> {
-  template <class Epi, bool P>
-  static hipError_t run(const float* a, const float* w, int m, int n, int k, int splits, const Epi& e, float* part,
-                        hipStream_t st) {
-    int ksplit = ((k / splits + FK - 1) / FK) * FK;
-    dim3 grid((n + FT - 1) / FT, (m + FT - 1) / FT, splits);
-    hipLaunchKernelGGL((gemm_f32_kernel<Epi, P>), grid, dim3(256), 0, st, a, w, m, n, k, ksplit, e, part);
-    return hipGetLastError();
-  }
-};
+template <int BM, int BN, class Epi>
+static hipError_t run_bf16(const bf16_t* a, const bf16_t* w, int m, int n, int k, const Epi& e, hipStream_t st) {
+  using TL = Tile<BM, BN>;
+  auto kern = gemm_bf16_kernel<BM, BN, Epi>;
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::LDS_BYTES);
+  if (err != hipSuccess) return err;
+  dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
+  hipLaunchKernelGGL(kern, grid, dim3(256), TL::LDS_BYTES, st, a, w, m, n, k, e);
+  return hipGetLastError();
+}
+
+// 128 x 128 tiles when they already give two workgroups per CU, else 128 x 64.
+template <class Epi>
+static hipError_t run(const bf16_t* a, const bf16_t* w, int m, int n, int k, const Epi& e, hipStream_t st) {
+  const long tiles = (long)((m + 127) / 128) * ((n + 127) / 128);
+  if (tiles >= 512) return run_bf16<128, 128>(a, w, m, n, k, e, st);
+  return run_bf16<128, 64>(a, w, m, n, k, e, st);
+}
+
+template <class Epi>
+static hipError_t run(const float* a, const float* w, int m, int n, int k, const Epi& e, hipStream_t st) {
+  dim3 grid((n + FT - 1) / FT, (m + FT - 1) / FT);
+  hipLaunchKernelGGL(gemm_f32_kernel<Epi>, grid, dim3(256), 0, st, a, w, m, n, k, e);
+  return hipGetLastError();
+}
 
 template <typename T>
 hipError_t launch_gemm_qkv(const T* a, const T* w, int m, int k, const EpiQKV& e, hipStream_t st) {
   if (m <= 0) return hipSuccess;
   QKVStore<T> s{e.bias, (T*)e.q, (T*)e.k, (T*)e.vt, e.n, e.n_pad, e.heads, e.head_dim, e.channels};
-  return GemmOp<T>::template run<QKVStore<T>, false>(a, w, m, 3 * e.channels, k, 1, s, nullptr, st);
+  return run(a, w, m, 3 * e.channels, k, s, st);
 }
 
 template <typename T>
 hipError_t launch_gemm_gelu(const T* a, const T* w, int m, int n, int k, const EpiGelu& e, hipStream_t st) {
   if (m <= 0) return hipSuccess;
   GeluStore<T> s{e.bias, (T*)e.out, e.ld};
-  return GemmOp<T>::template run<GeluStore<T>, false>(a, w, m, n, k, 1, s, nullptr, st);
+  return run(a, w, m, n, k, s, st);
 }
 
 template <typename T>
-hipError_t launch_gemm_residual(const T* a, const T* w, int m, int n, int k, const EpiResidualScatter& e, int splits,
-                                float* part, hipStream_t st) {
+hipError_t launch_gemm_residual(const T* a, const T* w, int m, int n, int k, const EpiResidualScatter& e,
+                                hipStream_t st) {
   if (m <= 0) return hipSuccess;
   ResidualAdd s{e.bias, e.x, e.perm, e.list, e.map, e.ldx, e.x_rows};
-  if (splits <= 1) return GemmOp<T>::template run<ResidualAdd, false>(a, w, m, n, k, 1, s, nullptr, st);
-  hipError_t err = GemmOp<T>::template run<ResidualAdd, true>(a, w, m, n, k, splits, s, part, st);
-  if (err != hipSuccess) return err;
-  size_t total = (size_t)m * n;
-  hipLaunchKernelGGL(splitk_residual_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, part, splits, m,
-                     n, s);
-  return hipGetLastError();
+  return run(a, w, m, n, k, s, st);
 }
 
 template hipError_t launch_gemm_qkv<bf16_t>(const bf16_t*, const bf16_t*, int, int, const EpiQKV&, hipStream_t);
@@ -313,8 +417,8 @@ template hipError_t launch_gemm_qkv<float>(const float*, const float*, int, int,
 template hipError_t launch_gemm_gelu<bf16_t>(const bf16_t*, const bf16_t*, int, int, int, const EpiGelu&, hipStream_t);
 template hipError_t launch_gemm_gelu<float>(const float*, const float*, int, int, int, const EpiGelu&, hipStream_t);
 template hipError_t launch_gemm_residual<bf16_t>(const bf16_t*, const bf16_t*, int, int, int,
-                                                 const EpiResidualScatter&, int, float*, hipStream_t);
+                                                 const EpiResidualScatter&, hipStream_t);
 template hipError_t launch_gemm_residual<float>(const float*, const float*, int, int, int, const EpiResidualScatter&,
-                                                int, float*, hipStream_t);
+                                                hipStream_t);
 
 }  // namespace sparsesam

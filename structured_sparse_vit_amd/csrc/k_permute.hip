@@ -54,23 +54,31 @@ __global__ void __launch_bounds__(1024) stripe_permute_kernel(const float* __res
   for (int t = tid; t < tokens; t += nth) flag[t] = 0;
   __syncthreads();
 
-  // Bitonic sort of each p2-long run, ascending by key.
-  for (int k = 2; k <= p2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = tid; t < (total >> 1); t += nth) {
-        int i = (t / j) * (2 * j) + (t % j);
-        int l = i + j;
-        unsigned long long a = keys[i], b = keys[l];
+  // Bitonic sort of each p2-long run, ascending by key. Pair t of a stage with stride j
+  // compares keys i = (t / j) * 2j + t % j and i + j. For j <= 32 the 64 pairs of one
+  // wavefront lie inside one 128-key block that no other wavefront touches, so those
+  // stages need only a wavefront fence; a workgroup barrier precedes every stage with a
+  // larger stride (its pairs cross wavefronts) and the first stride-32 stage after one.
+  const int half = total >> 1;
+  for (int k = 2, lk = 1; k <= p2; k <<= 1, ++lk) {
+    for (int j = k >> 1, lj = lk - 1; j > 0; j >>= 1, --lj) {
+      if (j >= 32) __syncthreads();
+      for (int t = tid; t < half; t += nth) {
+        const int i = ((t >> lj) << (lj + 1)) | (t & (j - 1));
+        const int l = i + j;
+        const unsigned long long a = keys[i], b = keys[l];
         // direction from the index inside the segment, so every segment ends ascending
-        bool up = (((i & (p2 - 1)) & k) == 0);
+        const bool up = (((i & (p2 - 1)) & k) == 0);
         if ((a > b) == up) {
           keys[i] = b;
           keys[l] = a;
         }
       }
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     }
   }
+  __syncthreads();
 
   // Stripe transpose, inverse, and keep-set flags.
   const int S = n / stripes;
