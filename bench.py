@@ -75,6 +75,7 @@ class Workload:
         self.routed = torch.empty(b * info["routed_per_image"], dtype=torch.int32, device=dev)
         self.ws = torch.empty(info["block_workspace_bytes"], dtype=torch.uint8, device=dev)
         self.mlp_ws = torch.empty(info["mlp_workspace_bytes"], dtype=torch.uint8, device=dev)
+        self.attn_ws = torch.empty(max(1, info["attn_workspace_bytes"]), dtype=torch.uint8, device=dev)
         self.np = np
 
     def step(self):
@@ -216,7 +217,7 @@ def main():
     # per-kernel: attention (dominant kernel) and routed MLP, same launch configuration as in the block
     q, k, vt, o = wl.attn_operands()
     segs = cfg.batch * plan.info["segments_per_image"]
-    attn_ms = time_region(lambda: ss.attn(plan, q, k, vt, out=o), 50, 5)
+    attn_ms = time_region(lambda: ss.attn(plan, q, k, vt, out=o, workspace=wl.attn_ws), 50, 5)
     attn_tf = attention_flops(plan) * segs / (attn_ms * 1e-3) / 1e12
     xr = wl.x.view(-1, cfg.channels)
     mlp_ms = time_region(lambda: ss.mlp(plan, xr, wl.routed, wl.w["ln2_g"], wl.w["ln2_b"], wl.w["w1"], wl.w["b1"],
@@ -234,7 +235,7 @@ def main():
     wl3 = Workload(cfg3, dev)
     wl3.step()
     q3, k3, vt3, o3 = wl3.attn_operands()
-    a3 = time_region(lambda: ss.attn(wl3.plan, q3, k3, vt3, out=o3), 50, 5)
+    a3 = time_region(lambda: ss.attn(wl3.plan, q3, k3, vt3, out=o3, workspace=wl3.attn_ws), 50, 5)
     xr3 = wl3.x.view(-1, cfg.channels)
     m3 = time_region(lambda: ss.mlp(wl3.plan, xr3, wl3.routed, wl3.w["ln2_g"], wl3.w["ln2_b"], wl3.w["w1"],
                                     wl3.w["b1"], wl3.w["w2"], wl3.w["b2"], workspace=wl3.mlp_ws), 50, 5)
@@ -254,7 +255,7 @@ def main():
         wld = Workload(cfgd, dev)
         dense_lib = time_region(wld.step, 30, 5)
         qd, kd, vtd, od = wld.attn_operands()
-        dense_attn = time_region(lambda: ss.attn(wld.plan, qd, kd, vtd, out=od), 30, 5)
+        dense_attn = time_region(lambda: ss.attn(wld.plan, qd, kd, vtd, out=od, workspace=wld.attn_ws), 30, 5)
         del wld
         dense_torch = torch_dense_block_ms(cfg, dev)
         best = min(dense_lib, dense_torch)

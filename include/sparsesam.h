@@ -104,6 +104,8 @@ typedef struct sparsesam_plan_info {
   int32_t reserved0;
   size_t block_workspace_bytes; /* workspace sparsesam_block needs at max_batch */
   size_t mlp_workspace_bytes;   /* workspace sparsesam_mlp needs for max_batch images' keep-sets */
+  size_t attn_workspace_bytes;  /* workspace sparsesam_attn needs for max_batch images' segments
+                                   (0 when the plan's attention needs none) */
   int32_t has_device_copy;      /* 1 when the plan can run on the current device */
   int32_t device;               /* HIP device of the device copy, -1 when none */
 } sparsesam_plan_info;
@@ -142,14 +144,15 @@ sparsesam_status sparsesam_importance(const float* img, int32_t batch, int32_t h
 /*
  * (2) Stripe-sort permutation and keep-set of every segment of `batch` images
  * (same page, stripe-sort bullet; 2. Residual-Consistency MLP, token routing).
- *   imp    [batch, grid_h * grid_w] fp32 (window pads get importance -1).
+ *   imp    [batch, grid_h * grid_w] fp32.
  *   perm   [batch * segments_per_image, N] int32: segment-local slot at each position
  *          of the stripe-sorted sequence (slot = token index in raster order within the
  *          global grid or within the window).
  *   inv    [batch * segments_per_image, N] int32: inv[perm[p]] = p.
  *   routed [batch * routed_per_image] int32: global row ids (image * grid_h * grid_w +
  *          token) of the keep-set, ascending.
- * Order: importance descending, ties by lower slot, -0.0 == +0.0, NaN last. The
+ * Order: importance descending, ties by lower slot, -0.0 == +0.0, NaN after every
+ * number, window pad slots after every real slot (so no pad enters the keep-set). The
  * stripe-sort reads the sorted list as an (N/g) x g matrix, transposes it and
  * flattens it: perm[p] = sorted[g * (p % S) + p / S]. All outputs are integers and
  * exactly determined.
@@ -168,11 +171,15 @@ sparsesam_status sparsesam_permute(sparsesam_plan_t plan, const float* imp, int3
  *                                              rounded up to a multiple of 8; columns
  *                                              N..N_pad-1 are never read)
  *   o    [segments, N, heads * head_dim]      (plan dtype)
- * `scale` is usually head_dim^-0.5. bf16 plans need head_dim 64 or 80 and either
- * B = 64 with S a multiple of 64 (global segments) or N <= 256 (windows).
+ * `scale` must be positive; usually head_dim^-0.5. Rows with long key lists may be split
+ * into pieces whose partial results go through `workspace` (fp32 partial sums, running
+ * max and running sum); it must hold attn_workspace_bytes scaled to `segments`
+ * (attn_workspace_bytes / (max_batch * segments_per_image) bytes per segment) and may
+ * be NULL when that is 0.
  */
 sparsesam_status sparsesam_attn(sparsesam_plan_t plan, int32_t segments, const void* q, const void* k,
-                                const void* vt, void* o, float scale, void* stream);
+                                const void* vt, void* o, float scale, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /*
  * (4) Residual-Consistency MLP, in place on the fp32 residual stream (same page,

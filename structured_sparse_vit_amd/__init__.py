@@ -137,7 +137,7 @@ def permute(plan, imp, out=None):
     return perm, inv, routed
 
 
-def attn(plan, q, k, vt, scale=None, out=None):
+def attn(plan, q, k, vt, scale=None, out=None, workspace=None):
     """Block-sparse attention on stripe-sorted tokens.
 
     q, k [segments, heads, N, D]; vt [segments, heads, D, N_pad] -> o [segments, N, heads * D].
@@ -154,8 +154,10 @@ def attn(plan, q, k, vt, scale=None, out=None):
         out = torch.empty(segs, n, H * D, dtype=dt, device=q.device)
     _need(out, "out", dt, (segs, n, H * D), plan.device)
     scale = D ** -0.5 if scale is None else float(scale)
-    check(lib.sparsesam_attn(plan.handle, segs, _ptr(q), _ptr(k), _ptr(vt), _ptr(out), scale, _stream(q.device)),
-          "sparsesam_attn")
+    per_seg = plan.info["attn_workspace_bytes"] // max(1, plan.desc.max_batch * plan.info["segments_per_image"])
+    ws = _workspace(per_seg * segs, q.device, workspace)
+    check(lib.sparsesam_attn(plan.handle, segs, _ptr(q), _ptr(k), _ptr(vt), _ptr(out), scale, _ptr(ws), ws.numel(),
+                             _stream(q.device)), "sparsesam_attn")
     return out
 
 

@@ -51,6 +51,7 @@ class PlanInfo(ctypes.Structure):
         ("pairs_kept", ctypes.c_int64), ("realised_density", ctypes.c_double),
         ("routed_per_image", ctypes.c_int32), ("reserved0", ctypes.c_int32),
         ("block_workspace_bytes", ctypes.c_size_t), ("mlp_workspace_bytes", ctypes.c_size_t),
+        ("attn_workspace_bytes", ctypes.c_size_t),
         ("has_device_copy", ctypes.c_int32), ("device", ctypes.c_int32),
     ]
 
@@ -83,7 +84,7 @@ def load():
         "sparsesam_last_error": ([], ctypes.c_char_p),
         "sparsesam_importance": ([P, I32, I32, I32, I32, P, P], I32),
         "sparsesam_permute": ([P, P, I32, P, P, P, P], I32),
-        "sparsesam_attn": ([P, I32, P, P, P, P, F32, P], I32),
+        "sparsesam_attn": ([P, I32, P, P, P, P, F32, P, SZ, P], I32),
         "sparsesam_mlp": ([P, P, I64, P, I32, P, P, P, P, P, P, P, SZ, P], I32),
         "sparsesam_block": ([P, ctypes.POINTER(BlockWeights), P, I32, P, P, P, SZ, P], I32),
     }

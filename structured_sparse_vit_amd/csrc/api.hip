@@ -62,6 +62,8 @@ BlockLayout block_layout(const sparsesam_plan& p, int batch) {
   off += align256(segs * p.desc.heads * p.desc.head_dim * (size_t)p.n_pad * es);
   L.o = off;
   off += align256(M * C * es);
+  L.part = off;
+  off += align256(attn_partial_bytes(p, (int)segs));
   L.total_attn = off;
   L.total_mlp = mlp_workspace(p, batch * p.routed_per_image, &L.a2, &L.hid);
   return L;
@@ -203,6 +205,30 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
   std::stable_sort(p->order.begin(), p->order.end(), [&](int a, int b) {
     return (p->row_ptr[a + 1] - p->row_ptr[a]) > (p->row_ptr[b + 1] - p->row_ptr[b]);
   });
+  // matrix-core attention work list: rows of more than kChunk key tiles are split
+  {
+    const int kChunk = 32;
+    struct Item { int qt, kb, ke, slot; };
+    std::vector<Item> v;
+    p->splits.clear();
+    p->n_slots = 0;
+    for (int qt = 0; qt < p->tiles; ++qt) {
+      const int rb = p->row_ptr[qt], len = p->row_ptr[qt + 1] - rb;
+      const int nch = (len + kChunk - 1) / kChunk;
+      if (nch <= 1) {
+        v.push_back({qt, rb, rb + len, -1});
+        continue;
+      }
+      p->splits.insert(p->splits.end(), {qt, p->n_slots, nch});
+      for (int c = 0; c < nch; ++c)
+        v.push_back({qt, rb + (int)((long long)c * len / nch), rb + (int)((long long)(c + 1) * len / nch), p->n_slots++});
+    }
+    std::stable_sort(v.begin(), v.end(), [](const Item& a, const Item& b) { return a.ke - a.kb > b.ke - b.kb; });
+    p->items.clear();
+    for (const Item& it : v) p->items.insert(p->items.end(), {it.qt, it.kb, it.ke, it.slot});
+    p->n_items = (int)v.size();
+    p->n_split_rows = (int)p->splits.size() / 3;
+  }
   // keep-set size per segment
   p->seg_k.resize(p->segs_per_img);
   p->routed_per_image = 0;
@@ -235,16 +261,16 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
   if (hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    size_t words = p->row_ptr.size() + p->col_idx.size() + 3 * (size_t)p->tiles + p->seg_k.size();
     std::vector<int> blob;
-    blob.reserve(words);
     auto put = [&](const std::vector<int>& v) {
+      while (blob.size() % 4) blob.push_back(0);  // 16-byte alignment for int4 reads
       size_t o = blob.size();
       blob.insert(blob.end(), v.begin(), v.end());
       return o;
     };
     size_t o_rp = put(p->row_ptr), o_ci = put(p->col_idx), o_ts = put(p->tile_start), o_tl = put(p->tile_len),
-           o_or = put(p->order), o_sk = put(p->seg_k);
+           o_or = put(p->order), o_sk = put(p->seg_k), o_it = put(p->items), o_sp = put(p->splits);
+    blob.push_back(0);
     void* dptr = nullptr;
     hipError_t e = hipMalloc(&dptr, blob.size() * sizeof(int));
     if (e != hipSuccess) {
@@ -267,6 +293,8 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     p->d_tile_len = b + o_tl;
     p->d_order = b + o_or;
     p->d_seg_k = b + o_sk;
+    p->d_items = b + o_it;
+    p->d_splits = b + o_sp;
   } else {
     (void)hipGetLastError();
   }
@@ -288,6 +316,7 @@ sparsesam_status sparsesam_plan_get_info(sparsesam_plan_t p, sparsesam_plan_info
   info->routed_per_image = p->routed_per_image;
   info->block_workspace_bytes = p->block_ws;
   info->mlp_workspace_bytes = p->mlp_ws;
+  info->attn_workspace_bytes = attn_partial_bytes(*p, p->desc.max_batch * p->segs_per_img);
   info->has_device_copy = p->dev ? 1 : 0;
   info->device = p->dev ? p->device : -1;
   return SPARSESAM_OK;
@@ -337,20 +366,26 @@ sparsesam_status sparsesam_permute(sparsesam_plan_t p, const float* imp, int32_t
 }
 
 sparsesam_status sparsesam_attn(sparsesam_plan_t p, int32_t segments, const void* q, const void* k, const void* vt,
-                                void* o, float scale, void* stream) {
+                                void* o, float scale, void* workspace, size_t workspace_bytes, void* stream) {
   sparsesam_status st = check_device(p);
   if (st != SPARSESAM_OK) return st;
   if (segments < 0) return invalid("segments must be >= 0");
   if (!(scale > 0.0f) || !std::isfinite(scale)) return invalid("scale must be positive and finite");
   if (segments == 0) return SPARSESAM_OK;
   if (!q || !k || !vt || !o) return invalid("q, k, vt and o must not be null");
+  const size_t need = attn_partial_bytes(*p, segments);
+  if (need > 0 && (!workspace || workspace_bytes < need)) {
+    set_error("attention workspace needs " + std::to_string(need) + " bytes for " + std::to_string(segments) +
+              " segments");
+    return SPARSESAM_ERR_WORKSPACE;
+  }
   hipError_t e;
   if (p->desc.dtype == SPARSESAM_BF16)
     e = launch_attention<bf16_t>(*p, segments, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt, (bf16_t*)o, scale,
-                                 (hipStream_t)stream);
+                                 workspace, (hipStream_t)stream);
   else
     e = launch_attention<float>(*p, segments, (const float*)q, (const float*)k, (const float*)vt, (float*)o, scale,
-                                (hipStream_t)stream);
+                                workspace, (hipStream_t)stream);
   return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_attn launch");
 }
 
@@ -422,7 +457,7 @@ static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weigh
   EpiQKV eq{w.b_qkv, q, k, vt, p.n, p.n_pad, p.desc.heads, p.desc.head_dim, C};
   e = launch_gemm_qkv<T>(h, (const T*)w.w_qkv, M, C, eq, st);
   if (e != hipSuccess) return e;
-  e = launch_attention<T>(p, segs, q, k, vt, o, 1.0f / std::sqrt((float)p.desc.head_dim), st);
+  e = launch_attention<T>(p, segs, q, k, vt, o, 1.0f / std::sqrt((float)p.desc.head_dim), ws + L.part, st);
   if (e != hipSuccess) return e;
   EpiResidualScatter er{w.b_proj, x, perm, nullptr, p.segmap(), C, x_rows};
   e = launch_gemm_residual<T>(o, (const T*)w.w_proj, M, C, C, er, st);

@@ -31,6 +31,11 @@ struct sparsesam_plan {
   std::vector<int> tile_start, tile_len;
   std::vector<int> order;             // query tiles, longest row first
   std::vector<int> seg_k;             // keep-set size of each segment of an image
+  // matrix-core attention work list: (query tile, first, end kept-key index, partial
+  // slot or -1), longest first; rows longer than the chunk limit are split into items
+  // that write partials, merged per (query tile, first slot, chunks) in `splits`
+  std::vector<int> items, splits;
+  int n_items = 0, n_split_rows = 0, n_slots = 0;
 
   // device copy (one allocation) on `device`
   int device = -1;
@@ -41,6 +46,8 @@ struct sparsesam_plan {
   const int* d_tile_len = nullptr;
   const int* d_order = nullptr;
   const int* d_seg_k = nullptr;
+  const int* d_items = nullptr;
+  const int* d_splits = nullptr;
 
   sparsesam::SegmentMap segmap() const {
     sparsesam::SegmentMap m;
@@ -61,7 +68,7 @@ sparsesam_status hip_fail(hipError_t e, const char* where);
 
 // Workspace carve-up of sparsesam_block / sparsesam_mlp.
 struct BlockLayout {
-  size_t h = 0, q = 0, k = 0, vt = 0, o = 0, total_attn = 0;
+  size_t h = 0, q = 0, k = 0, vt = 0, o = 0, part = 0, total_attn = 0;
   size_t a2 = 0, hid = 0, total_mlp = 0;
 };
 BlockLayout block_layout(const sparsesam_plan& p, int batch);
@@ -113,6 +120,8 @@ hipError_t launch_gemm_residual(const T* a, const T* w, int m, int n, int k, con
 
 template <typename T>
 hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
-                            float scale, hipStream_t st);
+                            float scale, void* partial, hipStream_t st);
+bool attn_mfma64_supported(const sparsesam_plan& p);
+size_t attn_partial_bytes(const sparsesam_plan& p, int segments);
 
 }  // namespace sparsesam

@@ -9,13 +9,17 @@
 //
 // Kernels:
 //  * attn_mfma64_kernel (bf16, head_dim 64, B = 64, stripes a multiple of 64 long):
-//    one 128-thread workgroup per (query tile, segment, head), issued longest tile row
-//    first. Each wavefront owns 32 queries. S^T = K Q^T and O^T = V^T P^T run on
-//    v_mfma_f32_32x32x16_bf16, so a lane holds one query's scores (the softmax row
-//    max needs one exchange with lane ^ 32) and one query's output column. K and the
-//    transposed V tiles are staged through LDS, the next tile prefetched into
-//    registers during the current one. Online softmax in fp32 with exp2 and the
-//    scale folded into one multiply-add per score.
+//    one 256-thread workgroup per (work item, segment, head), issued longest first; a
+//    work item is a query tile against at most 32 of its kept key tiles (longer rows,
+//    the global one, are split and merged by attn_combine_kernel). Wavefronts 0 and 1
+//    own query halves 0..31 and 32..63 on the even key tiles of the item, wavefronts 2
+//    and 3 the same queries on the odd ones; the two halves merge through LDS at the
+//    end. S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so a lane
+//    holds one query's scores (the softmax row max needs one exchange with lane ^ 32)
+//    and one query's output column. K and transposed V tiles are double-buffered in
+//    LDS with one barrier per step, the next tile's global loads in flight during the
+//    current one. Online softmax in fp32 with exp2, the scale folded into one
+//    multiply-add per score, and the output rescale skipped when no row max moved.
 //  * attn_simt_kernel (fp32 or bf16 storage, any pattern and head_dim <= 128): one
 //    thread per query, keys read through the cache; the exact path for small
 //    configs and for windows.
@@ -26,28 +30,39 @@ namespace sparsesam {
 // ---------------------------------------------------------------- MFMA kernel (D = 64, B = 64)
 
 constexpr int kTile = 64;
-constexpr int kLd = 64 + 8;  // LDS row stride in bf16 (16-byte pad)
+constexpr int kLd = 64 + 8;                    // LDS row stride in bf16 (16-byte pad)
+constexpr int kPairElems = 2 * kTile * kLd;    // one K tile + one V^T tile
+constexpr int kAttnLds = 2 * 2 * kPairElems * 2;  // [stage][key parity][K | V^T], bytes
+constexpr int kPartLd = 68;                    // partial record: O[64], m, l, pad (floats)
 
-__global__ void __launch_bounds__(128) attn_mfma64_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
+// One work item: query tile qt against the kept key tiles col_idx[kb..ke). Rows whose
+// list is longer than the plan's chunk limit are split over several items; those
+// write an unnormalised partial (O, running max, running sum) to `partial` at `slot`
+// and a combine pass merges them.
+__global__ void __launch_bounds__(256) attn_mfma64_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                                           const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
-                                                          const int* __restrict__ row_ptr,
+                                                          const int4* __restrict__ items,
                                                           const int* __restrict__ col_idx,
-                                                          const int* __restrict__ tile_start,
-                                                          const int* __restrict__ order, int n, int n_pad, int heads,
-                                                          int seg_heads, float c_log2) {
+                                                          const int* __restrict__ tile_start, int n, int n_pad,
+                                                          int heads, int seg_heads, float c_log2,
+                                                          float* __restrict__ partial) {
   constexpr int D = 64;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kTile * kLd];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[D * kLd];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qt = order[blockIdx.x / seg_heads];
+  const int qh = wave & 1;   // query half of the tile
+  const int kp = wave >> 1;  // key-tile parity this wavefront pair walks
+  const int ptid = tid & 127;
+  const int4 it = items[blockIdx.x / seg_heads];
   const int sh = blockIdx.x - (blockIdx.x / seg_heads) * seg_heads;  // seg * heads + head
+  const int qt = it.x, kb = it.y, ke = it.z, slot = it.w;
   const int seg = sh / heads, h = sh - seg * heads;
   const bf16_t* q_base = Q + (size_t)sh * n * D;
   const bf16_t* k_base = Kt + (size_t)sh * n * D;
   const bf16_t* v_base = VT + (size_t)sh * D * n_pad;
 
-  const int q0 = tile_start[qt] + wave * 32;
-  const int my_q = q0 + (lane & 31);
+  const int q_local = qh * 32 + (lane & 31);
+  const int my_q = tile_start[qt] + q_local;
   // Q^T operand: lane holds Q[my_q][16 ks + 8 (lane / 32) .. + 7]
   bf16x8 qf[4];
 #pragma unroll
@@ -61,103 +76,187 @@ __global__ void __launch_bounds__(128) attn_mfma64_kernel(const bf16_t* __restri
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int kb = row_ptr[qt], ke = row_ptr[qt + 1];
-  // staging: K tile 64 x 64 and V^T tile 64 x 64, 4 + 4 chunks of 16 bytes per thread
+  // staging of this pair's K tile and V^T tile: 4 + 4 chunks of 16 bytes per thread
   i32x4 rk[4], rv[4];
   auto load_regs = [&](int kt) {
     const int k0 = tile_start[kt];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int c = tid + 128 * i;  // 512 chunks: row = c / 8, chunk = c % 8
-      int row = c >> 3, ch = c & 7;
+      const int c = ptid + 128 * i;  // 512 chunks: row = c / 8, chunk = c % 8
+      const int row = c >> 3, ch = c & 7;
       rk[i] = *reinterpret_cast<const i32x4*>(k_base + (size_t)(k0 + row) * D + ch * 8);
       rv[i] = *reinterpret_cast<const i32x4*>(v_base + (size_t)row * n_pad + k0 + ch * 8);
     }
   };
-  auto store_lds = [&]() {
+  auto store_lds = [&](int stage) {
+    bf16_t* Ks = lds + (stage * 2 + kp) * kPairElems;
+    bf16_t* Vs = Ks + kTile * kLd;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int c = tid + 128 * i;
-      int row = c >> 3, ch = c & 7;
+      const int c = ptid + 128 * i;
+      const int row = c >> 3, ch = c & 7;
       *reinterpret_cast<i32x4*>(Ks + row * kLd + ch * 8) = rk[i];
-      // V^T: inside each 16-key group store keys as [0..3, 8..11, 4..7, 12..15] so a
+      // V^T: inside each 16-key group keys are stored as [0..3, 8..11, 4..7, 12..15] so a
       // lane's eight k-slots of the P^T operand are contiguous
-      int grp = ch >> 1, half = ch & 1;
+      const int grp = ch >> 1, half = ch & 1;
       bf16_t* dst = Vs + row * kLd + grp * 16 + half * 4;
       *reinterpret_cast<i32x2*>(dst) = i32x2{rv[i][0], rv[i][1]};
       *reinterpret_cast<i32x2*>(dst + 8) = i32x2{rv[i][2], rv[i][3]};
     }
   };
 
-  if (kb < ke) load_regs(col_idx[kb]);
-  for (int t = kb; t < ke; ++t) {
-    __syncthreads();
-    store_lds();
-    __syncthreads();
-    if (t + 1 < ke) load_regs(col_idx[t + 1]);
-
-    // S^T = K Q^T: two 32-key blocks
-    f32x16 s[2];
+  const int total = ke - kb;
+  const int niter = (total + 1) >> 1;
+  if (kp < total) {
+    load_regs(col_idx[kb + kp]);
+    store_lds(0);
+  }
+  __syncthreads();
+  for (int i = 0; i < niter; ++i) {
+    const int cur = i & 1;
+    const bool has_cur = 2 * i + kp < total;
+    const bool has_next = 2 * (i + 1) + kp < total;
+    if (has_next) load_regs(col_idx[kb + 2 * (i + 1) + kp]);
+    if (has_cur) {
+      const bf16_t* Ks = lds + (cur * 2 + kp) * kPairElems;
+      const bf16_t* Vs = Ks + kTile * kLd;
+      // S^T = K Q^T: two 32-key blocks
+      f32x16 s[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[mb][e] = 0.0f;
+        for (int e = 0; e < 16; ++e) s[mb][e] = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (mb * 32 + (lane & 31)) * kLd + ks * 16 + (lane >> 5) * 8);
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
-      }
-    }
-    // online softmax for this lane's query (32 of the 64 scores here, the rest in lane ^ 32)
-    float mx = s[0][0];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * c_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.0f;
-    bf16x8 pf[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][hh * 8 + e], c_log2, -m_new));
-          psum += p;
-          pf[mb * 2 + hh][e] = to_bf16(p);
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 kf =
+              *reinterpret_cast<const bf16x8*>(Ks + (mb * 32 + (lane & 31)) * kLd + ks * 16 + (lane >> 5) * 8);
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
         }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int md = 0; md < 2; ++md)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
-    // O^T += V^T P^T over four 16-key steps
-#pragma unroll
-    for (int md = 0; md < 2; ++md)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + (md * 32 + (lane & 31)) * kLd + kk * 16 + (lane >> 5) * 8);
-        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[md], 0, 0, 0);
       }
+      // online softmax for this lane's query (32 of the tile's 64 scores; the rest in lane ^ 32)
+      float mx = s[0][0];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx * c_log2);
+      // rescale only when some row's running max moved (wave-uniform branch)
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int md = 0; md < 2; ++md)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
+        m_run = m_new;
+      }
+      float psum = 0.0f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][hh * 8 + e], c_log2, -m_run));
+            psum += p;
+            pf[mb * 2 + hh][e] = to_bf16(p);
+          }
+      l_run += psum;
+      // O^T += V^T P^T over four 16-key steps
+#pragma unroll
+      for (int md = 0; md < 2; ++md)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 vf =
+              *reinterpret_cast<const bf16x8*>(Vs + (md * 32 + (lane & 31)) * kLd + kk * 16 + (lane >> 5) * 8);
+          oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[md], 0, 0, 0);
+        }
+    }
+    if (has_next) store_lds(cur ^ 1);
+    __syncthreads();
   }
 
+  // merge the odd-parity pair into the even one through LDS (same lane -> same queries)
+  float* xch = reinterpret_cast<float*>(smem) + (size_t)qh * 64 * 34;
+  if (kp == 1) {
+    float* r = xch + lane * 34;
+    r[0] = m_run;
+    r[1] = l_run;
+#pragma unroll
+    for (int md = 0; md < 2; ++md)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) r[2 + md * 16 + e] = oacc[md][e];
+  }
+  __syncthreads();
+  if (kp == 1) return;
+  {
+    const float* r = xch + lane * 34;
+    const float m1 = r[0], l1 = r[1];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int md = 0; md < 2; ++md)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[md][e] = oacc[md][e] * a0 + r[2 + md * 16 + e] * a1;
+    m_run = mm;
+  }
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv_l = 1.0f / l_tot;
-  bf16_t* o_row = O + ((size_t)seg * n + my_q) * ((size_t)heads * D) + (size_t)h * D;
+  if (slot < 0) {
+    const float inv_l = 1.0f / l_tot;
+    bf16_t* o_row = O + ((size_t)seg * n + my_q) * ((size_t)heads * D) + (size_t)h * D;
 #pragma unroll
-  for (int md = 0; md < 2; ++md)
+    for (int md = 0; md < 2; ++md)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      int d = md * 32 + g4 * 8 + (lane >> 5) * 4;
-      bf16x4 v4;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = md * 32 + g4 * 8 + (lane >> 5) * 4;
+        bf16x4 v4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = to_bf16(oacc[md][g4 * 4 + e] * inv_l);
-      *reinterpret_cast<bf16x4*>(o_row + d) = v4;
+        for (int e = 0; e < 4; ++e) v4[e] = to_bf16(oacc[md][g4 * 4 + e] * inv_l);
+        *reinterpret_cast<bf16x4*>(o_row + d) = v4;
+      }
+  } else {
+    float* rec = partial + (((size_t)slot * seg_heads + sh) * kTile + q_local) * kPartLd;
+#pragma unroll
+    for (int md = 0; md < 2; ++md)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = md * 32 + g4 * 8 + (lane >> 5) * 4;
+        *reinterpret_cast<f32x4*>(rec + d) =
+            f32x4{oacc[md][g4 * 4], oacc[md][g4 * 4 + 1], oacc[md][g4 * 4 + 2], oacc[md][g4 * 4 + 3]};
+      }
+    if (lane < 32) {
+      rec[64] = m_run;
+      rec[65] = l_tot;
     }
+  }
+}
+
+// Merge the partials of split rows: O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+__global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restrict__ partial,
+                                                           const int* __restrict__ splits,
+                                                           const int* __restrict__ tile_start, bf16_t* __restrict__ O,
+                                                           int n, int heads, int seg_heads) {
+  constexpr int D = 64;
+  const int r = blockIdx.x / seg_heads, sh = blockIdx.x - (blockIdx.x / seg_heads) * seg_heads;
+  const int qt = splits[3 * r], slot0 = splits[3 * r + 1], nch = splits[3 * r + 2];
+  const int seg = sh / heads, h = sh - seg * heads;
+  for (int idx = threadIdx.x; idx < kTile * D; idx += blockDim.x) {
+    const int q = idx / D, d = idx - q * D;
+    float mm = -INFINITY;
+    for (int c = 0; c < nch; ++c)
+      mm = fmaxf(mm, partial[(((size_t)(slot0 + c) * seg_heads + sh) * kTile + q) * kPartLd + 64]);
+    float num = 0.0f, den = 0.0f;
+    for (int c = 0; c < nch; ++c) {
+      const float* rec = partial + (((size_t)(slot0 + c) * seg_heads + sh) * kTile + q) * kPartLd;
+      const float a = __builtin_amdgcn_exp2f(rec[64] - mm);
+      num += a * rec[d];
+      den += a * rec[65];
+    }
+    O[((size_t)seg * n + tile_start[qt] + q) * ((size_t)heads * D) + (size_t)h * D + d] = to_bf16(num / den);
+  }
 }
 
 // ---------------------------------------------------------------- SIMT kernel (any pattern)
@@ -216,6 +315,11 @@ bool attn_mfma64_supported(const sparsesam_plan& p) {
   return p.desc.dtype == SPARSESAM_BF16 && p.desc.head_dim == 64 && p.desc.block == 64 && p.s % 64 == 0;
 }
 
+size_t attn_partial_bytes(const sparsesam_plan& p, int segments) {
+  if (!attn_mfma64_supported(p)) return 0;
+  return (size_t)p.n_slots * segments * p.desc.heads * kTile * kPartLd * sizeof(float);
+}
+
 template <typename T, int D>
 static hipError_t run_simt(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
                            float c_log2, hipStream_t st) {
@@ -228,15 +332,24 @@ static hipError_t run_simt(const sparsesam_plan& p, int segments, const T* q, co
 
 template <typename T>
 hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
-                            float scale, hipStream_t st) {
+                            float scale, void* partial, hipStream_t st) {
   if (segments <= 0) return hipSuccess;
   const float c_log2 = scale * 1.4426950408889634f;
   if constexpr (sizeof(T) == 2) {
     if (attn_mfma64_supported(p)) {
-      int seg_heads = segments * p.desc.heads;
-      dim3 grid(p.tiles * seg_heads);
-      hipLaunchKernelGGL(attn_mfma64_kernel, grid, dim3(128), 0, st, q, k, vt, o, p.d_row_ptr, p.d_col_idx,
-                         p.d_tile_start, p.d_order, p.n, p.n_pad, p.desc.heads, seg_heads, c_log2);
+      const int seg_heads = segments * p.desc.heads;
+      hipError_t e = hipFuncSetAttribute((const void*)attn_mfma64_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         kAttnLds);
+      if (e != hipSuccess) return e;
+      dim3 grid((unsigned)(p.n_items * seg_heads));
+      hipLaunchKernelGGL(attn_mfma64_kernel, grid, dim3(256), kAttnLds, st, q, k, vt, o,
+                         reinterpret_cast<const int4*>(p.d_items), p.d_col_idx, p.d_tile_start, p.n, p.n_pad,
+                         p.desc.heads, seg_heads, c_log2, static_cast<float*>(partial));
+      e = hipGetLastError();
+      if (e != hipSuccess || p.n_split_rows == 0) return e;
+      hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(p.n_split_rows * seg_heads)), dim3(256), 0, st,
+                         static_cast<const float*>(partial), p.d_splits, p.d_tile_start, o, p.n, p.desc.heads,
+                         seg_heads);
       return hipGetLastError();
     }
   }
@@ -250,8 +363,8 @@ hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, c
 }
 
 template hipError_t launch_attention<float>(const sparsesam_plan&, int, const float*, const float*, const float*,
-                                            float*, float, hipStream_t);
+                                            float*, float, void*, hipStream_t);
 template hipError_t launch_attention<bf16_t>(const sparsesam_plan&, int, const bf16_t*, const bf16_t*, const bf16_t*,
-                                             bf16_t*, float, hipStream_t);
+                                             bf16_t*, float, void*, hipStream_t);
 
 }  // namespace sparsesam

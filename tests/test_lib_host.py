@@ -142,7 +142,7 @@ def test_compute_calls_without_device_return_no_device():
     p = ctypes.c_void_p(16)
     st = lib.sparsesam_permute(plan.handle, p, 1, p, p, p, None)
     assert st == 6
-    st = lib.sparsesam_attn(plan.handle, 1, p, p, p, p, ctypes.c_float(0.125), None)
+    st = lib.sparsesam_attn(plan.handle, 1, p, p, p, p, ctypes.c_float(0.125), p, 1 << 20, None)
     assert st == 6
     assert b"no device copy" in lib.sparsesam_last_error()
 
