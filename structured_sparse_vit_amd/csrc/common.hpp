@@ -42,6 +42,19 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each with its
+// own L2. xcd_remap turns the hardware workgroup id into a logical work index such that
+// every XCD receives one contiguous range [x * per, (x + 1) * per) of the logical order
+// (per = ceil(total / 8)). Grids are launched with 8 * per workgroups; ids that land
+// past `total` return -1 and the workgroup exits.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int hw_id, int total) {
+  const int per = (total + kXcds - 1) / kXcds;
+  const int logical = (hw_id % kXcds) * per + hw_id / kXcds;
+  return logical < total ? logical : -1;
+}
+__host__ __device__ inline int xcd_grid(int total) { return kXcds * ((total + kXcds - 1) / kXcds); }
+
 // GELU with the exact Gaussian CDF.
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 

@@ -44,17 +44,21 @@ __global__ void __launch_bounds__(256) attn_mfma64_kernel(const bf16_t* __restri
                                                           const int4* __restrict__ items,
                                                           const int* __restrict__ col_idx,
                                                           const int* __restrict__ tile_start, int n, int n_pad,
-                                                          int heads, int seg_heads, float c_log2,
+                                                          int heads, int seg_heads, int n_items, float c_log2,
                                                           float* __restrict__ partial) {
   constexpr int D = 64;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
+  // logical order: (segment, head)-major, items longest first within a head; each XCD
+  // takes a contiguous range, so its L2 holds the K/V of about heads / 8 heads
+  const int work = xcd_remap(blockIdx.x, n_items * seg_heads);
+  if (work < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qh = wave & 1;   // query half of the tile
   const int kp = wave >> 1;  // key-tile parity this wavefront pair walks
   const int ptid = tid & 127;
-  const int4 it = items[blockIdx.x / seg_heads];
-  const int sh = blockIdx.x - (blockIdx.x / seg_heads) * seg_heads;  // seg * heads + head
+  const int sh = work / n_items;  // seg * heads + head
+  const int4 it = items[work - sh * n_items];
   const int qt = it.x, kb = it.y, ke = it.z, slot = it.w;
   const int seg = sh / heads, h = sh - seg * heads;
   const bf16_t* q_base = Q + (size_t)sh * n * D;
@@ -235,28 +239,29 @@ __global__ void __launch_bounds__(256) attn_mfma64_kernel(const bf16_t* __restri
 }
 
 // Merge the partials of split rows: O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+// One wavefront per (split row, segment-head, query); lane d is channel d.
 __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restrict__ partial,
                                                            const int* __restrict__ splits,
                                                            const int* __restrict__ tile_start, bf16_t* __restrict__ O,
-                                                           int n, int heads, int seg_heads) {
+                                                           int n, int heads, int seg_heads, int total) {
   constexpr int D = 64;
-  const int r = blockIdx.x / seg_heads, sh = blockIdx.x - (blockIdx.x / seg_heads) * seg_heads;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6), d = threadIdx.x & 63;
+  if (w >= total) return;
+  const int q = w % kTile, rs = w / kTile;
+  const int sh = rs % seg_heads, r = rs / seg_heads;
   const int qt = splits[3 * r], slot0 = splits[3 * r + 1], nch = splits[3 * r + 2];
   const int seg = sh / heads, h = sh - seg * heads;
-  for (int idx = threadIdx.x; idx < kTile * D; idx += blockDim.x) {
-    const int q = idx / D, d = idx - q * D;
-    float mm = -INFINITY;
-    for (int c = 0; c < nch; ++c)
-      mm = fmaxf(mm, partial[(((size_t)(slot0 + c) * seg_heads + sh) * kTile + q) * kPartLd + 64]);
-    float num = 0.0f, den = 0.0f;
-    for (int c = 0; c < nch; ++c) {
-      const float* rec = partial + (((size_t)(slot0 + c) * seg_heads + sh) * kTile + q) * kPartLd;
-      const float a = __builtin_amdgcn_exp2f(rec[64] - mm);
-      num += a * rec[d];
-      den += a * rec[65];
-    }
-    O[((size_t)seg * n + tile_start[qt] + q) * ((size_t)heads * D) + (size_t)h * D + d] = to_bf16(num / den);
+  float mm = -INFINITY;
+  for (int c = 0; c < nch; ++c)
+    mm = fmaxf(mm, partial[(((size_t)(slot0 + c) * seg_heads + sh) * kTile + q) * kPartLd + 64]);
+  float num = 0.0f, den = 0.0f;
+  for (int c = 0; c < nch; ++c) {
+    const float* rec = partial + (((size_t)(slot0 + c) * seg_heads + sh) * kTile + q) * kPartLd;
+    const float a = __builtin_amdgcn_exp2f(rec[64] - mm);
+    num += a * rec[d];
+    den += a * rec[65];
   }
+  O[((size_t)seg * n + tile_start[qt] + q) * ((size_t)heads * D) + (size_t)h * D + d] = to_bf16(num / den);
 }
 
 // ---------------------------------------------------------------- SIMT kernel (any pattern)
@@ -341,15 +346,16 @@ hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, c
       hipError_t e = hipFuncSetAttribute((const void*)attn_mfma64_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          kAttnLds);
       if (e != hipSuccess) return e;
-      dim3 grid((unsigned)(p.n_items * seg_heads));
+      dim3 grid((unsigned)xcd_grid(p.n_items * seg_heads));
       hipLaunchKernelGGL(attn_mfma64_kernel, grid, dim3(256), kAttnLds, st, q, k, vt, o,
                          reinterpret_cast<const int4*>(p.d_items), p.d_col_idx, p.d_tile_start, p.n, p.n_pad,
-                         p.desc.heads, seg_heads, c_log2, static_cast<float*>(partial));
+                         p.desc.heads, seg_heads, p.n_items, c_log2, static_cast<float*>(partial));
       e = hipGetLastError();
       if (e != hipSuccess || p.n_split_rows == 0) return e;
-      hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(p.n_split_rows * seg_heads)), dim3(256), 0, st,
+      const int waves = p.n_split_rows * seg_heads * kTile;
+      hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
                          static_cast<const float*>(partial), p.d_splits, p.d_tile_start, o, p.n, p.desc.heads,
-                         seg_heads);
+                         seg_heads, waves);
       return hipGetLastError();
     }
   }

@@ -182,12 +182,11 @@ struct Tile {
 // tokens (V^T), so the MFMA operands are swapped and the block accumulates C^T.
 template <int BM, int BN, bool TR, class Epi>
 __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, int M,
-                                               int N, int K, const Epi& epi, char* smem) {
+                                               int N, int K, const Epi& epi, char* smem, int m0, int n0) {
   using TL = Tile<BM, BN>;
   constexpr bool tr = TR;
   bf16_t* stage = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
   const int wm = wave >> 1, wn = wave & 1;
 
   f32x16 acc[TL::MI][TL::NI];
@@ -310,10 +309,16 @@ template <int BM, int BN, class Epi>
 __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
                                                         int M, int N, int K, Epi epi) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  if (epi.col_tile(blockIdx.x * BN))
-    gemm_bf16_tile<BM, BN, true>(A, W, M, N, K, epi, smem);
+  // tiles in row-major order over the (M / BM) x (N / BN) grid, one contiguous run of
+  // whole tile rows per XCD so its L2 keeps those A rows and the W tiles they meet
+  const int nt = (N + BN - 1) / BN, mt = (M + BM - 1) / BM;
+  const int t = xcd_remap(blockIdx.x, mt * nt);
+  if (t < 0) return;
+  const int m0 = (t / nt) * BM, n0 = (t - (t / nt) * nt) * BN;
+  if (epi.col_tile(n0))
+    gemm_bf16_tile<BM, BN, true>(A, W, M, N, K, epi, smem, m0, n0);
   else
-    gemm_bf16_tile<BM, BN, false>(A, W, M, N, K, epi, smem);
+    gemm_bf16_tile<BM, BN, false>(A, W, M, N, K, epi, smem, m0, n0);
 }
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
@@ -370,8 +375,8 @@ static hipError_t run_bf16(const bf16_t* a, const bf16_t* w, int m, int n, int k
   auto kern = gemm_bf16_kernel<BM, BN, Epi>;
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::LDS_BYTES);
   if (err != hipSuccess) return err;
-  dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
-  hipLaunchKernelGGL(kern, grid, dim3(256), TL::LDS_BYTES, st, a, w, m, n, k, e);
+  const int tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(256), TL::LDS_BYTES, st, a, w, m, n, k, e);
   return hipGetLastError();
 }
 
