@@ -295,6 +295,8 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     p->d_seg_k = b + o_sk;
     p->d_items = b + o_it;
     p->d_splits = b + o_sp;
+    p->attn_resident_wgs = attn_mfma64_supported(*p) ? attn_mfma64_resident_wgs(dev) : 0;
+    (void)hipGetLastError();
   } else {
     (void)hipGetLastError();
   }

@@ -6,7 +6,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/sparsesam.h"
+#include "sparsesam.h"
 #include "common.hpp"
 
 struct sparsesam_plan {
@@ -36,6 +36,7 @@ struct sparsesam_plan {
   // that write partials, merged per (query tile, first slot, chunks) in `splits`
   std::vector<int> items, splits;
   int n_items = 0, n_split_rows = 0, n_slots = 0;
+  int attn_resident_wgs = 0;          // workgroups of the attention kernel resident at once
 
   // device copy (one allocation) on `device`
   int device = -1;
@@ -122,6 +123,7 @@ template <typename T>
 hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
                             float scale, void* partial, hipStream_t st);
 bool attn_mfma64_supported(const sparsesam_plan& p);
+int attn_mfma64_resident_wgs(int device);
 size_t attn_partial_bytes(const sparsesam_plan& p, int segments);
 
 }  // namespace sparsesam

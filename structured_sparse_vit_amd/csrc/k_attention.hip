@@ -23,6 +23,8 @@
 //  * attn_simt_kernel (fp32 or bf16 storage, any pattern and head_dim <= 128): one
 //    thread per query, keys read through the cache; the exact path for small
 //    configs and for windows.
+#include <algorithm>
+
 #include "internal.hpp"
 
 namespace sparsesam {
@@ -39,26 +41,21 @@ constexpr int kPartLd = 68;                    // partial record: O[64], m, l, p
 // list is longer than the plan's chunk limit are split over several items; those
 // write an unnormalised partial (O, running max, running sum) to `partial` at `slot`
 // and a combine pass merges them.
-__global__ void __launch_bounds__(256) attn_mfma64_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
-                                                          const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
-                                                          const int4* __restrict__ items,
-                                                          const int* __restrict__ col_idx,
-                                                          const int* __restrict__ tile_start, int n, int n_pad,
-                                                          int heads, int seg_heads, int n_items, float c_log2,
-                                                          float* __restrict__ partial) {
+// One unit of work: work item `item` (query tile qt against kept key tiles
+// col_idx[kb..ke), partial slot or -1) for segment-head sh.
+__device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
+                                                 const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
+                                                 const int4* __restrict__ items, const int* __restrict__ col_idx,
+                                                 const int* __restrict__ tile_start, int n, int n_pad, int heads,
+                                                 int seg_heads, float c_log2, float* __restrict__ partial, int item,
+                                                 int sh, char* smem) {
   constexpr int D = 64;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
-  // logical order: (segment, head)-major, items longest first within a head; each XCD
-  // takes a contiguous range, so its L2 holds the K/V of about heads / 8 heads
-  const int work = xcd_remap(blockIdx.x, n_items * seg_heads);
-  if (work < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qh = wave & 1;   // query half of the tile
   const int kp = wave >> 1;  // key-tile parity this wavefront pair walks
   const int ptid = tid & 127;
-  const int sh = work / n_items;  // seg * heads + head
-  const int4 it = items[work - sh * n_items];
+  const int4 it = items[item];
   const int qt = it.x, kb = it.y, ke = it.z, slot = it.w;
   const int seg = sh / heads, h = sh - seg * heads;
   const bf16_t* q_base = Q + (size_t)sh * n * D;
@@ -124,6 +121,21 @@ __global__ void __launch_bounds__(256) attn_mfma64_kernel(const bf16_t* __restri
     if (has_cur) {
       const bf16_t* Ks = lds + (cur * 2 + kp) * kPairElems;
       const bf16_t* Vs = Ks + kTile * kLd;
+      // all K and V^T fragments of the tile are requested up front, so LDS latency is
+      // paid once per tile and the V reads land while the softmax runs
+      bf16x8 kf[2][4], vf[2][4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          kf[mb][ks] =
+              *reinterpret_cast<const bf16x8*>(Ks + (mb * 32 + (lane & 31)) * kLd + ks * 16 + (lane >> 5) * 8);
+#pragma unroll
+      for (int md = 0; md < 2; ++md)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          vf[md][kk] =
+              *reinterpret_cast<const bf16x8*>(Vs + (md * 32 + (lane & 31)) * kLd + kk * 16 + (lane >> 5) * 8);
       // S^T = K Q^T: two 32-key blocks
       f32x16 s[2];
 #pragma unroll
@@ -131,11 +143,7 @@ __global__ void __launch_bounds__(256) attn_mfma64_kernel(const bf16_t* __restri
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[mb][e] = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(Ks + (mb * 32 + (lane & 31)) * kLd + ks * 16 + (lane >> 5) * 8);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
-        }
+        for (int ks = 0; ks < 4; ++ks) s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mb][ks], qf[ks], s[mb], 0, 0, 0);
       }
       // online softmax for this lane's query (32 of the tile's 64 scores; the rest in lane ^ 32)
       float mx = s[0][0];
@@ -172,11 +180,7 @@ __global__ void __launch_bounds__(256) attn_mfma64_kernel(const bf16_t* __restri
 #pragma unroll
       for (int md = 0; md < 2; ++md)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(Vs + (md * 32 + (lane & 31)) * kLd + kk * 16 + (lane >> 5) * 8);
-          oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[md], 0, 0, 0);
-        }
+        for (int kk = 0; kk < 4; ++kk) oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[md][kk], pf[kk], oacc[md], 0, 0, 0);
     }
     if (has_next) store_lds(cur ^ 1);
     __syncthreads();
@@ -194,7 +198,7 @@ __global__ void __launch_bounds__(256) attn_mfma64_kernel(const bf16_t* __restri
       for (int e = 0; e < 16; ++e) r[2 + md * 16 + e] = oacc[md][e];
   }
   __syncthreads();
-  if (kp == 1) return;
+  if (kp == 1) return;  // the odd pair's part of this unit is done
   {
     const float* r = xch + lane * 34;
     const float m1 = r[0], l1 = r[1];
@@ -235,6 +239,31 @@ __global__ void __launch_bounds__(256) attn_mfma64_kernel(const bf16_t* __restri
       rec[64] = m_run;
       rec[65] = l_tot;
     }
+  }
+}
+
+// Persistent launch: `nwg` workgroups (as many as stay resident) walk the units in
+// snake order -- unit u = r * nwg + (r even ? w : nwg - 1 - w) for rounds r = 0, 1, ... --
+// where units are (item, segment-head) pairs, items longest first. Long units land on
+// every workgroup in the first round and the shortest ones fill in after the shortest
+// first-round units, which evens out the work per workgroup without any atomics.
+__global__ void __launch_bounds__(256) attn_mfma64_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
+                                                          const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
+                                                          const int4* __restrict__ items,
+                                                          const int* __restrict__ col_idx,
+                                                          const int* __restrict__ tile_start, int n, int n_pad,
+                                                          int heads, int seg_heads, int n_items, float c_log2,
+                                                          float* __restrict__ partial) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nwg = gridDim.x, w = blockIdx.x;
+  const int total = n_items * seg_heads;
+  for (int r = 0;; ++r) {
+    const int u = r * nwg + ((r & 1) ? nwg - 1 - w : w);
+    if (u >= total) break;
+    if (r > 0) __syncthreads();  // the previous unit's merge has read its LDS exchange
+    const int item = u / seg_heads;
+    attn_mfma64_unit(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
+                     u - item * seg_heads, smem);
   }
 }
 
@@ -316,6 +345,18 @@ __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, 
 
 // ---------------------------------------------------------------- launchers
 
+int attn_mfma64_resident_wgs(int device) {
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return 0;
+  if (hipFuncSetAttribute((const void*)attn_mfma64_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds) !=
+      hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_mfma64_kernel, 256, kAttnLds) !=
+      hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
 bool attn_mfma64_supported(const sparsesam_plan& p) {
   return p.desc.dtype == SPARSESAM_BF16 && p.desc.head_dim == 64 && p.desc.block == 64 && p.s % 64 == 0;
 }
@@ -346,7 +387,8 @@ hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, c
       hipError_t e = hipFuncSetAttribute((const void*)attn_mfma64_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          kAttnLds);
       if (e != hipSuccess) return e;
-      dim3 grid((unsigned)xcd_grid(p.n_items * seg_heads));
+      const int units = p.n_items * seg_heads;
+      dim3 grid((unsigned)std::min(units, std::max(1, p.attn_resident_wgs)));
       hipLaunchKernelGGL(attn_mfma64_kernel, grid, dim3(256), kAttnLds, st, q, k, vt, o,
                          reinterpret_cast<const int4*>(p.d_items), p.d_col_idx, p.d_tile_start, p.n, p.n_pad,
                          p.desc.heads, seg_heads, p.n_items, c_log2, static_cast<float*>(partial));
