@@ -198,18 +198,20 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   i32x4 ra[TL::A_CHUNKS], rb[TL::B_CHUNKS];
+  // Rows past M (and N) are clamped to the last row instead of predicated: the loads
+  // stay branch-free and the extra rows only feed accumulators that are never stored.
   auto load_global = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < TL::A_CHUNKS; ++i) {
       const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      const int gm = m0 + row;
-      ra[i] = (gm < M) ? *reinterpret_cast<const i32x4*>(A + (size_t)gm * K + k0 + col) : i32x4{0, 0, 0, 0};
+      const int gm = min(m0 + row, M - 1);
+      ra[i] = *reinterpret_cast<const i32x4*>(A + (size_t)gm * K + k0 + col);
     }
 #pragma unroll
     for (int i = 0; i < TL::B_CHUNKS; ++i) {
       const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      const int gn = n0 + row;
-      rb[i] = (gn < N) ? *reinterpret_cast<const i32x4*>(W + (size_t)gn * K + k0 + col) : i32x4{0, 0, 0, 0};
+      const int gn = min(n0 + row, N - 1);
+      rb[i] = *reinterpret_cast<const i32x4*>(W + (size_t)gn * K + k0 + col);
     }
   };
   auto store_lds = [&](int s) {
@@ -236,24 +238,29 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
     if (kt + 1 < nk) load_global((kt + 1) * BK);
     const bf16_t* As = stage + cur * TL::STAGE;
     const bf16_t* Bs = As + BM * LDS_LD;
+    // every fragment of the K step is requested before the first MFMA, so the LDS
+    // latency is paid once per step
+    bf16x8 af[BK / 16][TL::MI], bfr[BK / 16][TL::NI];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[TL::MI], bfr[TL::NI];
       const int col = ks * 16 + (lane >> 5) * 8;
 #pragma unroll
       for (int i = 0; i < TL::MI; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + (wm * TL::WM + i * 32 + (lane & 31)) * LDS_LD + col);
+        af[ks][i] = *reinterpret_cast<const bf16x8*>(As + (wm * TL::WM + i * 32 + (lane & 31)) * LDS_LD + col);
 #pragma unroll
       for (int j = 0; j < TL::NI; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * TL::WN + j * 32 + (lane & 31)) * LDS_LD + col);
+        bfr[ks][j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * TL::WN + j * 32 + (lane & 31)) * LDS_LD + col);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
 #pragma unroll
       for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
         for (int j = 0; j < TL::NI; ++j) {
           if constexpr (!TR)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks][j], af[ks][i], acc[i][j], 0, 0, 0);
         }
     }
     if (kt + 1 < nk) store_lds(cur ^ 1);
