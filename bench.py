@@ -33,6 +33,39 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+ATTN_SOURCE = os.path.join(ROOT, "structured_sparse_vit_amd", "csrc", "k_attention.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_mfma64_c2_traffic.txt")
+
+
+def _source_hash(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or None.
+
+    The summary records FETCH_SIZE and WRITE_SIZE of the attention dispatch and of a
+    plain copy of known size (the scale factor), and the hash of the kernel source
+    they were taken with; a different source hash means the numbers are stale.
+    """
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_PROFILE) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    try:
+        if vals.get("source_sha256_16") != _source_hash(ATTN_SOURCE):
+            return None
+        return float(vals["scaled_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def attention_flops(plan):
     """4 * B^2 * D per kept tile per head (2 for Q K^T, 2 for P V), per segment."""
     info = plan.info
@@ -178,6 +211,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="run the steps only (for rocprofv3)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 256 MiB device copy 5 times (scale factor for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the data-parallel "
@@ -190,6 +225,14 @@ def main():
     from synth import get_config
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        _log("copied 256 MiB x 5")
+        return
     cfg = get_config(args.config)
     _log("workload", cfg)
     wl = Workload(cfg, dev)
@@ -288,7 +331,7 @@ def main():
                    "routed_tokens": plan.info["routed_per_image"] * cfg.batch},
         "roofline": {"bound": "mfma", "kernel": "attn_mfma64_kernel", "achieved": round(attn_tf, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "launch_ms": round(attn_ms, 5),
+                     "traffic": measured_traffic(), "launch_ms": round(attn_ms, 5),
                      "algorithmic_flop": attention_flops(plan) * segs},
         "cpu_baseline": cpu,
         "attn_tflops": round(attn_tf, 2),
