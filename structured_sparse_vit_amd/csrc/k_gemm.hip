@@ -162,21 +162,43 @@ struct ResidualAdd {
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM
 
-constexpr int BK = 64, LDS_LD = BK + 8;
+constexpr int BK = 64;     // K step: one 128-byte row of bf16 per tile row
+constexpr int kStages = 3; // LDS pipeline depth: two K steps in flight while one is multiplied
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding" (other
+// counters unconstrained), in the gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in bits [15:14].
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 template <int BM, int BN>
 struct Tile {
   static constexpr int WM = BM / 2, WN = BN / 2;  // wave block (2 x 2 waves)
   static constexpr int MI = WM / 32, NI = WN / 32;
-  static constexpr int A_CHUNKS = BM * 8 / 256;  // 16-byte chunks per thread per K step
-  static constexpr int B_CHUNKS = BN * 8 / 256;
-  static constexpr int STAGE = (BM + BN) * LDS_LD;  // bf16 elements per stage
-  static constexpr int CT_LD = BN + 4;               // fp32 epilogue tile row stride
-  static constexpr int CTT_LD = BM + 4;              // ... of the transposed tile (V^T tiles)
-  static constexpr int STAGE_BYTES = 2 * STAGE * 2;
+  static constexpr int GROUPS = (BM + BN) / 8;     // 1 KiB groups (8 rows x 128 B) per stage
+  static constexpr int LOADS = GROUPS / 4;         // direct-to-LDS loads per wave per stage
+  static constexpr int STAGE_BYTES = (BM + BN) * 128;
+  static constexpr int CT_LD = BN + 4;             // fp32 epilogue tile row stride
+  static constexpr int CTT_LD = BM + 4;            // ... of the transposed tile (V^T tiles)
   static constexpr int CT_BYTES = (BM * CT_LD > BN * CTT_LD ? BM * CT_LD : BN * CTT_LD) * 4;
-  static constexpr int LDS_BYTES = STAGE_BYTES > CT_BYTES ? STAGE_BYTES : CT_BYTES;
+  static constexpr int PIPE_BYTES = kStages * STAGE_BYTES;
+  static constexpr int LDS_BYTES = PIPE_BYTES > CT_BYTES ? PIPE_BYTES : CT_BYTES;
 };
+
+// Tiles live in LDS unpadded, 128 bytes per row, with the 16-byte chunk c of row r
+// stored at chunk c ^ (r & 7): the 16-byte fragment reads of 32 consecutive rows then
+// spread over all eight chunk positions (no bank conflicts), and each wavefront's
+// direct-to-LDS load -- 64 lanes x 16 bytes into one contiguous 1 KiB block, lane L
+// at byte 16 L -- fills 8 whole rows by giving lane L the chunk that belongs there.
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+// wait until at most n of this wavefront's tile loads are in flight, then meet the
+// other wavefronts; the empty asm keeps the compiler from moving LDS reads above it
+template <int N>
+__device__ __forceinline__ void stage_ready() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // The main loop and epilogue of one tile. TR: the tile's columns are written along
 // tokens (V^T), so the MFMA operands are swapped and the block accumulates C^T.
@@ -184,8 +206,6 @@ template <int BM, int BN, bool TR, class Epi>
 __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, int M,
                                                int N, int K, const Epi& epi, char* smem, int m0, int n0) {
   using TL = Tile<BM, BN>;
-  constexpr bool tr = TR;
-  bf16_t* stage = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -197,59 +217,57 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  i32x4 ra[TL::A_CHUNKS], rb[TL::B_CHUNKS];
-  // Rows past M (and N) are clamped to the last row instead of predicated: the loads
-  // stay branch-free and the extra rows only feed accumulators that are never stored.
-  auto load_global = [&](int k0) {
+  // Global source of this lane for each of its groups. Group g < BM/8 holds A rows
+  // 8g..8g+7, the rest W rows; lane L fills row 8g + L/8, chunk L%8, which is the
+  // logical chunk (L%8) ^ (L/8). Rows past M or N are clamped to the last row: the
+  // loads stay unconditional and those rows only reach accumulators never stored.
+  const bf16_t* src[TL::LOADS];
 #pragma unroll
-    for (int i = 0; i < TL::A_CHUNKS; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      const int gm = min(m0 + row, M - 1);
-      ra[i] = *reinterpret_cast<const i32x4*>(A + (size_t)gm * K + k0 + col);
+  for (int i = 0; i < TL::LOADS; ++i) {
+    const int g = wave + 4 * i;
+    const int r = lane >> 3, lc = (lane & 7) ^ r;
+    if (g < BM / 8) {
+      const int gm = min(m0 + g * 8 + r, M - 1);
+      src[i] = A + (size_t)gm * K + lc * 8;
+    } else {
+      const int gn = min(n0 + (g - BM / 8) * 8 + r, N - 1);
+      src[i] = W + (size_t)gn * K + lc * 8;
     }
+  }
+  auto issue = [&](int kt) {
+    char* base = smem + (kt % kStages) * TL::STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < TL::B_CHUNKS; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      const int gn = min(n0 + row, N - 1);
-      rb[i] = *reinterpret_cast<const i32x4*>(W + (size_t)gn * K + k0 + col);
-    }
-  };
-  auto store_lds = [&](int s) {
-    bf16_t* As = stage + s * TL::STAGE;
-    bf16_t* Bs = As + BM * LDS_LD;
-#pragma unroll
-    for (int i = 0; i < TL::A_CHUNKS; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<i32x4*>(As + row * LDS_LD + col) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < TL::B_CHUNKS; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<i32x4*>(Bs + row * LDS_LD + col) = rb[i];
+    for (int i = 0; i < TL::LOADS; ++i) {
+      const int g = wave + 4 * i;
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kt * BK),
+                                       (__attribute__((address_space(3))) void*)(base + g * 1024), 16, 0, 0);
     }
   };
 
   const int nk = K / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nk) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_global((kt + 1) * BK);
-    const bf16_t* As = stage + cur * TL::STAGE;
-    const bf16_t* Bs = As + BM * LDS_LD;
-    // every fragment of the K step is requested before the first MFMA, so the LDS
-    // latency is paid once per step
+    // stage kt must be complete; the later stages already issued may stay in flight
+    if (kt + 1 < nk)
+      stage_ready<TL::LOADS>();
+    else
+      stage_ready<0>();
+    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);  // into the buffer read last step
+    const char* As = smem + (kt % kStages) * TL::STAGE_BYTES;
+    const char* Bs = As + BM * 128;
+    // every fragment of the K step is requested before the first MFMA
     bf16x8 af[BK / 16][TL::MI], bfr[BK / 16][TL::NI];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int col = ks * 16 + (lane >> 5) * 8;
+      const int c = ks * 2 + (lane >> 5);
 #pragma unroll
       for (int i = 0; i < TL::MI; ++i)
-        af[ks][i] = *reinterpret_cast<const bf16x8*>(As + (wm * TL::WM + i * 32 + (lane & 31)) * LDS_LD + col);
+        af[ks][i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * TL::WM + i * 32 + (lane & 31), c));
 #pragma unroll
       for (int j = 0; j < TL::NI; ++j)
-        bfr[ks][j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * TL::WN + j * 32 + (lane & 31)) * LDS_LD + col);
+        bfr[ks][j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * TL::WN + j * 32 + (lane & 31), c));
     }
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
@@ -263,9 +281,10 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks][j], af[ks][i], acc[i][j], 0, 0, 0);
         }
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
-    __syncthreads();
   }
+  // every wavefront is done reading the pipeline buffers before they become the
+  // epilogue tile
+  __syncthreads();
 
   // Stage the fp32 tile in LDS. A lane holds one column of four row quads per 32 x 32
   // block; on transposed tiles the block holds C^T, and the tile is staged as C^T
