@@ -162,15 +162,15 @@ struct ResidualAdd {
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM
 
-constexpr int BK = 64;     // K step: one 128-byte row of bf16 per tile row
-constexpr int kStages = 3; // LDS pipeline depth: two K steps in flight while one is multiplied
+constexpr int BK = 64;  // K step: one 128-byte row of bf16 per tile row
 
 // s_waitcnt immediate for "at most n vector-memory operations outstanding" (other
 // counters unconstrained), in the gfx9 encoding: vmcnt[3:0], expcnt[6:4],
 // lgkmcnt[11:8], vmcnt[5:4] in bits [15:14].
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-template <int BM, int BN>
+// ST: LDS pipeline depth (ST - 1 K steps in flight while one is multiplied).
+template <int BM, int BN, int ST>
 struct Tile {
   static constexpr int WM = BM / 2, WN = BN / 2;  // wave block (2 x 2 waves)
   static constexpr int MI = WM / 32, NI = WN / 32;
@@ -180,16 +180,18 @@ struct Tile {
   static constexpr int CT_LD = BN + 4;             // fp32 epilogue tile row stride
   static constexpr int CTT_LD = BM + 4;            // ... of the transposed tile (V^T tiles)
   static constexpr int CT_BYTES = (BM * CT_LD > BN * CTT_LD ? BM * CT_LD : BN * CTT_LD) * 4;
-  static constexpr int PIPE_BYTES = kStages * STAGE_BYTES;
+  static constexpr int PIPE_BYTES = ST * STAGE_BYTES;
   static constexpr int LDS_BYTES = PIPE_BYTES > CT_BYTES ? PIPE_BYTES : CT_BYTES;
 };
 
 // Tiles live in LDS unpadded, 128 bytes per row, with the 16-byte chunk c of row r
-// stored at chunk c ^ (r & 7): the 16-byte fragment reads of 32 consecutive rows then
-// spread over all eight chunk positions (no bank conflicts), and each wavefront's
-// direct-to-LDS load -- 64 lanes x 16 bytes into one contiguous 1 KiB block, lane L
-// at byte 16 L -- fills 8 whole rows by giving lane L the chunk that belongs there.
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// stored at chunk c ^ ((r >> 1) & 7). gfx950 serves a 16-byte read for 16 lanes at a
+// time from 16 groups of banks (group = address / 16 mod 16); 16 consecutive rows of one
+// logical chunk then land in 16 distinct groups (no bank conflicts). Each wavefront's
+// direct-to-LDS load -- 64 lanes x 16 bytes into one contiguous 1 KiB block, lane L at
+// byte 16 L -- fills 8 whole rows by giving lane L the chunk that belongs there.
+__device__ __forceinline__ int swz_key(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ swz_key(r)) << 4); }
 
 // wait until at most n of this wavefront's tile loads are in flight, then meet the
 // other wavefronts; the empty asm keeps the compiler from moving LDS reads above it
@@ -202,10 +204,11 @@ __device__ __forceinline__ void stage_ready() {
 
 // The main loop and epilogue of one tile. TR: the tile's columns are written along
 // tokens (V^T), so the MFMA operands are swapped and the block accumulates C^T.
-template <int BM, int BN, bool TR, class Epi>
+template <int BM, int BN, int ST, bool TR, class Epi>
 __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, int M,
                                                int N, int K, const Epi& epi, char* smem, int m0, int n0) {
-  using TL = Tile<BM, BN>;
+  using TL = Tile<BM, BN, ST>;
+  constexpr int kStages = ST;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -218,14 +221,15 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   // Global source of this lane for each of its groups. Group g < BM/8 holds A rows
-  // 8g..8g+7, the rest W rows; lane L fills row 8g + L/8, chunk L%8, which is the
-  // logical chunk (L%8) ^ (L/8). Rows past M or N are clamped to the last row: the
-  // loads stay unconditional and those rows only reach accumulators never stored.
+  // 8g..8g+7, the rest W rows; lane L fills row 8g + L/8 at chunk position L%8, which
+  // holds logical chunk (L%8) ^ swz_key(8g + L/8). Rows past M or N are clamped to the
+  // last row: the loads stay unconditional and those rows only reach accumulators that
+  // are never stored.
   const bf16_t* src[TL::LOADS];
 #pragma unroll
   for (int i = 0; i < TL::LOADS; ++i) {
     const int g = wave + 4 * i;
-    const int r = lane >> 3, lc = (lane & 7) ^ r;
+    const int r = lane >> 3, lc = (lane & 7) ^ swz_key(8 * g + r);
     if (g < BM / 8) {
       const int gm = min(m0 + g * 8 + r, M - 1);
       src[i] = A + (size_t)gm * K + lc * 8;
@@ -249,11 +253,16 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
   for (int s = 0; s < kStages - 1; ++s)
     if (s < nk) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
-    // stage kt must be complete; the later stages already issued may stay in flight
-    if (kt + 1 < nk)
+    // stage kt must be complete; the later stages already issued (at most
+    // kStages - 2 of them) may stay in flight
+    static_assert(kStages >= 2 && kStages <= 4, "pipeline depth");
+    const int later = min(kStages - 2, nk - 1 - kt);
+    if (later <= 0)
+      stage_ready<0>();
+    else if (later == 1)
       stage_ready<TL::LOADS>();
     else
-      stage_ready<0>();
+      stage_ready<2 * TL::LOADS>();
     if (kt + kStages - 1 < nk) issue(kt + kStages - 1);  // into the buffer read last step
     const char* As = smem + (kt % kStages) * TL::STAGE_BYTES;
     const char* Bs = As + BM * 128;
@@ -331,20 +340,28 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
   }
 }
 
-template <int BM, int BN, class Epi>
+// XCD rectangles: the (mt x nt) tile grid is cut into xa bands of tile rows times xb
+// bands of tile columns (xa * xb = 8), one rectangle per XCD, so each XCD's L2 holds
+// the A rows and W rows of its own rectangle. Workgroup hw runs on XCD hw % 8 and takes
+// the (hw / 8)-th tile of that rectangle, tile rows fastest.
+struct XcdRect {
+  int xa, xb, mb, nb;  // bands, and tiles per band (ceil)
+};
+
+template <int BM, int BN, int ST, class Epi>
 __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
-                                                        int M, int N, int K, Epi epi) {
+                                                        int M, int N, int K, Epi epi, XcdRect xr) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // tiles in row-major order over the (M / BM) x (N / BN) grid, one contiguous run of
-  // whole tile rows per XCD so its L2 keeps those A rows and the W tiles they meet
   const int nt = (N + BN - 1) / BN, mt = (M + BM - 1) / BM;
-  const int t = xcd_remap(blockIdx.x, mt * nt);
-  if (t < 0) return;
-  const int m0 = (t / nt) * BM, n0 = (t - (t / nt) * nt) * BN;
+  const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int ra = x / xr.xb, rb = x - (x / xr.xb) * xr.xb;
+  const int mi = ra * xr.mb + j % xr.mb, ni = rb * xr.nb + j / xr.mb;
+  if (j >= xr.mb * xr.nb || mi >= mt || ni >= nt) return;
+  const int m0 = mi * BM, n0 = ni * BN;
   if (epi.col_tile(n0))
-    gemm_bf16_tile<BM, BN, true>(A, W, M, N, K, epi, smem, m0, n0);
+    gemm_bf16_tile<BM, BN, ST, true>(A, W, M, N, K, epi, smem, m0, n0);
   else
-    gemm_bf16_tile<BM, BN, false>(A, W, M, N, K, epi, smem, m0, n0);
+    gemm_bf16_tile<BM, BN, ST, false>(A, W, M, N, K, epi, smem, m0, n0);
 }
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
@@ -395,23 +412,39 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
 
 // ---------------------------------------------------------------- launchers
 
-template <int BM, int BN, class Epi>
+template <int BM, int BN, int ST, class Epi>
 static hipError_t run_bf16(const bf16_t* a, const bf16_t* w, int m, int n, int k, const Epi& e, hipStream_t st) {
-  using TL = Tile<BM, BN>;
-  auto kern = gemm_bf16_kernel<BM, BN, Epi>;
+  using TL = Tile<BM, BN, ST>;
+  auto kern = gemm_bf16_kernel<BM, BN, ST, Epi>;
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::LDS_BYTES);
   if (err != hipSuccess) return err;
-  const int tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
-  hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(256), TL::LDS_BYTES, st, a, w, m, n, k, e);
+  // pick the XCD split with the fewest tiles on the busiest XCD, then the smallest
+  // per-XCD working set (A rows + W rows of a rectangle)
+  const int mt = (m + BM - 1) / BM, nt = (n + BN - 1) / BN;
+  XcdRect best{8, 1, (mt + 7) / 8, nt};
+  long best_load = -1, best_ws = 0;
+  for (int xa = 1; xa <= 8; xa *= 2) {
+    const int xb = 8 / xa;
+    const int mb = (mt + xa - 1) / xa, nb = (nt + xb - 1) / xb;
+    const long load = (long)mb * nb;
+    const long ws = (long)mb * BM + (long)nb * BN;
+    if (best_load < 0 || load < best_load || (load == best_load && ws < best_ws)) {
+      best = XcdRect{xa, xb, mb, nb};
+      best_load = load;
+      best_ws = ws;
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)(kXcds * best_load)), dim3(256), TL::LDS_BYTES, st, a, w, m, n, k, e,
+                     best);
   return hipGetLastError();
 }
 
-// 128 x 128 tiles when they already give two workgroups per CU, else 128 x 64.
+// 128 x 64 tiles (48 KiB of LDS at two stages: three workgroups per CU); long K
+// (the fc2 product) keeps two steps in flight.
 template <class Epi>
 static hipError_t run(const bf16_t* a, const bf16_t* w, int m, int n, int k, const Epi& e, hipStream_t st) {
-  const long tiles = (long)((m + 127) / 128) * ((n + 127) / 128);
-  if (tiles >= 512) return run_bf16<128, 128>(a, w, m, n, k, e, st);
-  return run_bf16<128, 64>(a, w, m, n, k, e, st);
+  if (k >= 2048) return run_bf16<128, 64, 3>(a, w, m, n, k, e, st);
+  return run_bf16<128, 64, 2>(a, w, m, n, k, e, st);
 }
 
 template <class Epi>
