@@ -245,11 +245,9 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     p->seg_k[w] = k;
     p->routed_per_image += k;
   }
-  p->sort_pow2 = 1;
-  while (p->sort_pow2 < p->n) p->sort_pow2 <<= 1;
   if (permute_lds_bytes(*p) > 160 * 1024) {
     delete p;
-    return unsupported("segments of one image do not fit the permutation kernel's 160 KiB of LDS");
+    return unsupported("a segment's keys or an image's token flags do not fit the permutation kernels' 160 KiB of LDS");
   }
   BlockLayout L = block_layout(*p, d.max_batch);
   p->block_ws = std::max(L.total_attn, L.total_mlp);

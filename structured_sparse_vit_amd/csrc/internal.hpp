@@ -23,7 +23,6 @@ struct sparsesam_plan {
   long long pairs_kept = 0;
   double density = 0.0;
   int routed_per_image = 0;
-  int sort_pow2 = 0;      // per-segment sort width (power of two >= n)
   size_t block_ws = 0, mlp_ws = 0;
 
   // host copies of the static tables

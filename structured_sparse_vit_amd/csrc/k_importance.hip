@@ -51,8 +51,58 @@ __global__ void __launch_bounds__(1024) sobel_pool_kernel(const float* __restric
   }
 }
 
+// Strip kernel for patch 16: one 256-thread workgroup per 16 tokens of one token row
+// (a 16 x 256-pixel strip). The strip and its one-pixel halo (18 x 258 floats) are
+// staged in LDS with coalesced loads; thread (token tl, pixel row r) computes the 16
+// magnitudes of its patch row and sums them left to right, then the 16 row sums of a
+// token are added top to bottom -- the same operations in the same order as above.
+constexpr int kStripW = 256, kHaloW = kStripW + 2;
+
+__global__ void __launch_bounds__(256) sobel_pool_strip_kernel(const float* __restrict__ img, int height, int width,
+                                                               float* __restrict__ imp) {
+#pragma clang fp contract(off)
+  __shared__ float tile[18][kHaloW];
+  __shared__ float rowsum[16][17];
+  const int x0 = blockIdx.x * kStripW, ty = blockIdx.y, b = blockIdx.z;
+  const int y0 = ty * 16;
+  const float* P = img + (size_t)b * height * width;
+  for (int i = threadIdx.x; i < 18 * kHaloW; i += 256) {
+    const int yy = y0 - 1 + i / kHaloW, xx = x0 - 1 + i % kHaloW;
+    tile[i / kHaloW][i % kHaloW] =
+        (yy >= 0 && yy < height && xx >= 0 && xx < width) ? P[(size_t)yy * width + xx] : 0.0f;
+  }
+  __syncthreads();
+  const int tl = threadIdx.x >> 4, r = threadIdx.x & 15;
+  const float two = 2.0f;
+  float acc = 0.0f;
+  for (int c = 0; c < 16; ++c) {
+    const int y = r + 1, x = tl * 16 + c + 1;  // tile coordinates of the pixel
+    float gx = ((tile[y - 1][x + 1] + two * tile[y][x + 1]) + tile[y + 1][x + 1]) -
+               ((tile[y - 1][x - 1] + two * tile[y][x - 1]) + tile[y + 1][x - 1]);
+    float gy = ((tile[y + 1][x - 1] + two * tile[y + 1][x]) + tile[y + 1][x + 1]) -
+               ((tile[y - 1][x - 1] + two * tile[y - 1][x]) + tile[y - 1][x + 1]);
+    float sq = gx * gx;
+    float sq2 = gy * gy;
+    sq = sq + sq2;
+    acc = acc + __builtin_sqrtf(sq);
+  }
+  rowsum[tl][r] = acc;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float tot = 0.0f;
+    for (int i = 0; i < 16; ++i) tot = tot + rowsum[threadIdx.x][i];
+    const int gw = width / 16;
+    imp[(size_t)b * (height / 16) * gw + ty * gw + blockIdx.x * 16 + threadIdx.x] = tot / 256.0f;
+  }
+}
+
 hipError_t launch_importance(const float* img, int batch, int height, int width, int patch, float* imp,
                              hipStream_t st) {
+  if (patch == 16 && width % kStripW == 0) {
+    dim3 grid(width / kStripW, height / 16, batch);
+    hipLaunchKernelGGL(sobel_pool_strip_kernel, grid, dim3(256), 0, st, img, height, width, imp);
+    return hipGetLastError();
+  }
   dim3 grid(width / patch, height / patch, batch);
   hipLaunchKernelGGL(sobel_pool_kernel, grid, dim3(patch * patch), 0, st, img, height, width, patch, imp);
   return hipGetLastError();

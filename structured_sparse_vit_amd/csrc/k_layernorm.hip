@@ -56,12 +56,86 @@ __global__ void __launch_bounds__(256) gather_ln_kernel(const float* __restrict_
   }
 }
 
+// Vector form for bf16 output and C a multiple of 256: each lane holds NV float4 chunks
+// (16-byte loads) and writes four bf16 per chunk (8-byte stores).
+template <int NV>
+__global__ void __launch_bounds__(256) gather_ln_vec_kernel(const float* __restrict__ x, int x_rows, int rows_out,
+                                                            const int* __restrict__ perm,
+                                                            const int* __restrict__ list, SegmentMap map,
+                                                            const float* __restrict__ g, const float* __restrict__ b,
+                                                            bf16_t* __restrict__ out) {
+  constexpr int C = NV * 256;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows_out) return;
+  int src;
+  if (list) {
+    src = list[r];
+  } else {
+    const int seg = r / map.n, slot = perm[r];
+    src = map.row_of(seg, slot);
+  }
+  bf16_t* o = out + (size_t)r * C;
+  if (src < 0 || src >= x_rows) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) *reinterpret_cast<bf16x4*>(o + 4 * (lane + 64 * i)) = bf16x4{};
+    return;
+  }
+  const f32x4* xr = reinterpret_cast<const f32x4*>(x + (size_t)src * C);
+  f32x4 v[NV];
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i] = xr[lane + 64 * i];
+    s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+  }
+  const float mean = wave_sum(s) * (1.0f / C);
+  float q = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d = v[i][e] - mean;
+      q += d * d;
+    }
+  const float rstd = rsqrtf(wave_sum(q) * (1.0f / C) + 1e-6f);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = 4 * (lane + 64 * i);
+    const f32x4 gg = *reinterpret_cast<const f32x4*>(g + c);
+    const f32x4 bb = *reinterpret_cast<const f32x4*>(b + c);
+    bf16x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = to_bf16((v[i][e] - mean) * rstd * gg[e] + bb[e]);
+    *reinterpret_cast<bf16x4*>(o + c) = w;
+  }
+}
+
 template <typename T>
 hipError_t launch_gather_ln(const sparsesam_plan& p, const float* x, int x_rows, int rows_out, const int* perm,
                             const int* list, const float* g, const float* b, T* out, hipStream_t st) {
   if (rows_out <= 0) return hipSuccess;
   const int C = p.desc.channels;
   dim3 grid((rows_out + 3) / 4);
+  if constexpr (sizeof(T) == 2) {
+    auto* o = reinterpret_cast<bf16_t*>(out);
+    switch (C) {
+      case 768:
+        hipLaunchKernelGGL(gather_ln_vec_kernel<3>, grid, dim3(256), 0, st, x, x_rows, rows_out, perm, list,
+                           p.segmap(), g, b, o);
+        return hipGetLastError();
+      case 1024:
+        hipLaunchKernelGGL(gather_ln_vec_kernel<4>, grid, dim3(256), 0, st, x, x_rows, rows_out, perm, list,
+                           p.segmap(), g, b, o);
+        return hipGetLastError();
+      case 1280:
+        hipLaunchKernelGGL(gather_ln_vec_kernel<5>, grid, dim3(256), 0, st, x, x_rows, rows_out, perm, list,
+                           p.segmap(), g, b, o);
+        return hipGetLastError();
+      default:
+        break;
+    }
+  }
   hipLaunchKernelGGL(gather_ln_kernel<T>, grid, dim3(256), 0, st, x, x_rows, rows_out, C, perm, list, p.segmap(), g, b,
                      out);
   return hipGetLastError();

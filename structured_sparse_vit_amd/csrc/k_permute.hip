@@ -6,98 +6,99 @@
 // the whole sequence. Part 2 (Residual-Consistency MLP), token routing bullet: the
 // keep-set follows the same deterministic order.
 //
-// One workgroup (1024 threads) per image does everything in LDS:
-//  1. builds one 64-bit key per segment slot: the high word orders importance
-//     descending (-0.0 == +0.0, NaN after every number, pad slots after NaN), the low
-//     word is the slot, so the order is total and the result unique;
-//  2. bitonic-sorts every segment's keys in place (segments are padded to a power of
-//     two with keys that sort last);
-//  3. writes perm[p] = sorted[g * (p % S) + p / S] and inv[perm[p]] = p;
-//  4. flags the first K slots of each segment's order in an image-wide token map and
-//     compacts the flags in raster order, which gives the keep-set ascending.
+// The order is total: importance descending (-0.0 == +0.0, NaN after every number,
+// pad slots after every real slot), then slot ascending. A slot's rank is therefore
+// the number of slots that precede it, and its stripe-sorted position follows from
+// the rank alone: rank rho sits at stripe rho % g, offset rho / g, i.e. position
+// (rho % g) * S + rho / g. No sorted list is ever materialised.
+//
+//  * rank_kernel: one workgroup per (segment, 64-slot chunk). Each wavefront counts,
+//    for the chunk's 64 slots (one per lane), the preceding slots inside its share of
+//    the segment's keys (held in LDS as 32-bit order keys); the shares are summed in
+//    LDS and the 64 lanes of wavefront 0 write perm and inv. All 1024 threads of a
+//    workgroup keep the GPU busy even for a single image (4096 slots -> 64 workgroups).
+//  * keepset_kernel: one workgroup per image reads each real token's rank back from
+//    inv, flags the K first of its segment, and compacts the flags in raster order
+//    (block-wide scan), which gives the keep-set ascending.
+#include <algorithm>
+
 #include "internal.hpp"
 
 namespace sparsesam {
 
+// 32-bit key that orders descending importance ascending: larger value -> smaller key.
 __device__ __forceinline__ uint32_t desc_key(float f) {
   uint32_t u = __float_as_uint(f);
-  if (f != f) return 0xFFFFFFFEu;          // NaN: after every number
-  if ((u & 0x7FFFFFFFu) == 0u) u = 0u;     // -0.0 -> +0.0
-  uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ~asc;                              // larger value -> smaller key
+  if (f != f) return 0xFFFFFFFEu;       // NaN: after every number
+  if ((u & 0x7FFFFFFFu) == 0u) u = 0u;  // -0.0 -> +0.0
+  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~asc;
+}
+constexpr uint32_t kPadKey = 0xFFFFFFFFu;  // pad slots: after every real slot
+
+constexpr int kRankWaves = 16;
+
+__global__ void __launch_bounds__(64 * kRankWaves) rank_kernel(const float* __restrict__ imp, SegmentMap map,
+                                                               int n, int stripes, int chunks,
+                                                               int* __restrict__ perm, int* __restrict__ inv) {
+  extern __shared__ uint32_t key_lds[];  // n keys of the segment
+  __shared__ int part[kRankWaves][64];
+  const int seg = blockIdx.x / chunks, chunk = blockIdx.x - (blockIdx.x / chunks) * chunks;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tokens = map.grid_h * map.grid_w;
+  const int img = seg / map.segs_per_img;
+  const float* im = imp + (size_t)img * tokens;
+  for (int s = tid; s < n; s += blockDim.x) {
+    const int row = map.row_of(seg, s);
+    key_lds[s] = row >= 0 ? desc_key(im[row - img * tokens]) : kPadKey;
+  }
+  __syncthreads();
+  const int slot = chunk * 64 + lane;
+  const bool valid = slot < n;
+  const uint32_t mine = valid ? key_lds[slot] : 0u;
+  // this wavefront's share of the keys
+  const int per = (n + kRankWaves - 1) / kRankWaves;
+  const int j0 = wave * per, j1 = min(n, j0 + per);
+  int cnt = 0;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t kj = key_lds[j];  // same address in every lane: a broadcast read
+    cnt += (kj < mine) | ((kj == mine) & (j < slot));
+  }
+  part[wave][lane] = cnt;
+  __syncthreads();
+  if (wave == 0 && valid) {
+    int rank = 0;
+#pragma unroll
+    for (int w = 0; w < kRankWaves; ++w) rank += part[w][lane];
+    const int S = n / stripes;
+    const int p = (rank % stripes) * S + rank / stripes;
+    const size_t base = (size_t)seg * n;
+    perm[base + p] = slot;
+    inv[base + slot] = p;
+  }
 }
 
-__global__ void __launch_bounds__(1024) stripe_permute_kernel(const float* __restrict__ imp, SegmentMap map,
-                                                              int segs, int n, int p2, int stripes,
-                                                              const int* __restrict__ seg_k, int routed_per_image,
-                                                              int* __restrict__ perm, int* __restrict__ inv,
-                                                              int* __restrict__ routed) {
-  extern __shared__ unsigned long long smem_keys[];
+__global__ void __launch_bounds__(1024) keepset_kernel(const int* __restrict__ inv, SegmentMap map, int segs, int n,
+                                                       int stripes, const int* __restrict__ seg_k,
+                                                       int routed_per_image, int* __restrict__ routed) {
+  extern __shared__ unsigned char flag[];
   __shared__ int wave_tot[16];
   const int img = blockIdx.x;
   const int tid = threadIdx.x, nth = blockDim.x;
   const int tokens = map.grid_h * map.grid_w;
-  const int total = segs * p2;
-  unsigned long long* keys = smem_keys;
-  unsigned char* flag = reinterpret_cast<unsigned char*>(smem_keys + total);
-  const float* im = imp + (size_t)img * tokens;
-
-  for (int i = tid; i < total; i += nth) {
-    int sg = i / p2, slot = i - sg * p2;
-    uint32_t hi = 0xFFFFFFFFu;
-    if (slot < n) {
-      int row = map.row_of(img * segs + sg, slot);
-      if (row >= 0) hi = desc_key(im[row - img * tokens]);
-    }
-    keys[i] = ((unsigned long long)hi << 32) | (uint32_t)slot;
-  }
+  const int S = n / stripes;
   for (int t = tid; t < tokens; t += nth) flag[t] = 0;
   __syncthreads();
-
-  // Bitonic sort of each p2-long run, ascending by key. Pair t of a stage with stride j
-  // compares keys i = (t / j) * 2j + t % j and i + j. For j <= 32 the 64 pairs of one
-  // wavefront lie inside one 128-key block that no other wavefront touches, so those
-  // stages need only a wavefront fence; a workgroup barrier precedes every stage with a
-  // larger stride (its pairs cross wavefronts) and the first stride-32 stage after one.
-  const int half = total >> 1;
-  for (int k = 2, lk = 1; k <= p2; k <<= 1, ++lk) {
-    for (int j = k >> 1, lj = lk - 1; j > 0; j >>= 1, --lj) {
-      if (j >= 32) __syncthreads();
-      for (int t = tid; t < half; t += nth) {
-        const int i = ((t >> lj) << (lj + 1)) | (t & (j - 1));
-        const int l = i + j;
-        const unsigned long long a = keys[i], b = keys[l];
-        // direction from the index inside the segment, so every segment ends ascending
-        const bool up = (((i & (p2 - 1)) & k) == 0);
-        if ((a > b) == up) {
-          keys[i] = b;
-          keys[l] = a;
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
-  __syncthreads();
-
-  // Stripe transpose, inverse, and keep-set flags.
-  const int S = n / stripes;
   for (int i = tid; i < segs * n; i += nth) {
-    int sg = i / n, p = i - sg * n;
-    int rank = stripes * (p % S) + p / S;
-    int slot = (int)(uint32_t)keys[sg * p2 + rank];
-    size_t base = ((size_t)img * segs + sg) * n;
-    perm[base + p] = slot;
-    inv[base + slot] = p;
-    if (p < seg_k[sg]) {  // rank p of the plain order is in the keep-set
-      int slot_r = (int)(uint32_t)keys[sg * p2 + p];
-      int row = map.row_of(img * segs + sg, slot_r) - img * tokens;
-      if (row >= 0 && row < tokens) flag[row] = 1;
-    }
+    const int sg = i / n, s = i - sg * n;
+    const int row = map.row_of(img * segs + sg, s) - img * tokens;
+    if (row < 0 || row >= tokens) continue;  // pad slot
+    const int p = inv[((size_t)img * segs + sg) * n + s];
+    const int rank = stripes * (p % S) + p / S;
+    if (rank < seg_k[sg]) flag[row] = 1;
   }
   __syncthreads();
-
-  // Compact the flags in raster order (block-wide exclusive scan).
+  // compact the flags in raster order (block-wide exclusive scan)
   const int per = (tokens + nth - 1) / nth;
   const int t0 = tid * per;
   int cnt = 0;
@@ -106,7 +107,7 @@ __global__ void __launch_bounds__(1024) stripe_permute_kernel(const float* __res
   int incl = cnt;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int v = __shfl_up(incl, o, 64);
+    const int v = __shfl_up(incl, o, 64);
     if (lane >= o) incl += v;
   }
   if (lane == 63) wave_tot[wv] = incl;
@@ -124,18 +125,27 @@ __global__ void __launch_bounds__(1024) stripe_permute_kernel(const float* __res
 }
 
 size_t permute_lds_bytes(const sparsesam_plan& p) {
-  size_t tokens = (size_t)p.desc.grid_h * p.desc.grid_w;
-  return (size_t)p.segs_per_img * p.sort_pow2 * 8 + ((tokens + 15) & ~size_t(15));
+  const size_t tokens = (size_t)p.desc.grid_h * p.desc.grid_w;
+  return std::max((size_t)p.n * 4, tokens);
 }
 
 hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
                           hipStream_t st) {
-  size_t lds = permute_lds_bytes(p);
-  hipError_t e = hipFuncSetAttribute((const void*)stripe_permute_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const int chunks = (p.n + 63) / 64;
+  const int segs = batch * p.segs_per_img;
+  const size_t key_bytes = (size_t)p.n * 4;
+  hipError_t e = hipFuncSetAttribute((const void*)rank_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)key_bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(stripe_permute_kernel, dim3(batch), dim3(1024), lds, st, imp, p.segmap(), p.segs_per_img,
-                     p.n, p.sort_pow2, p.desc.stripes, p.d_seg_k, p.routed_per_image, perm, inv, routed);
+  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)(segs * chunks)), dim3(64 * kRankWaves), key_bytes, st, imp,
+                     p.segmap(), p.n, p.desc.stripes, chunks, perm, inv);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t flag_bytes = (size_t)p.desc.grid_h * p.desc.grid_w;
+  e = hipFuncSetAttribute((const void*)keepset_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)flag_bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(keepset_kernel, dim3(batch), dim3(1024), flag_bytes, st, inv, p.segmap(), p.segs_per_img, p.n,
+                     p.desc.stripes, p.d_seg_k, p.routed_per_image, routed);
   return hipGetLastError();
 }
 
