@@ -66,6 +66,7 @@ __global__ void __launch_bounds__(256) sobel_pool_strip_kernel(const float* __re
   const int x0 = blockIdx.x * kStripW, ty = blockIdx.y, b = blockIdx.z;
   const int y0 = ty * 16;
   const float* P = img + (size_t)b * height * width;
+#pragma unroll
   for (int i = threadIdx.x; i < 18 * kHaloW; i += 256) {
     const int yy = y0 - 1 + i / kHaloW, xx = x0 - 1 + i % kHaloW;
     tile[i / kHaloW][i % kHaloW] =

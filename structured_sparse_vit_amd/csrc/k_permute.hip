@@ -41,28 +41,43 @@ constexpr int kRankWaves = 16;
 __global__ void __launch_bounds__(64 * kRankWaves) rank_kernel(const float* __restrict__ imp, SegmentMap map,
                                                                int n, int stripes, int chunks,
                                                                int* __restrict__ perm, int* __restrict__ inv) {
-  extern __shared__ uint32_t key_lds[];  // n keys of the segment
+  extern __shared__ uint32_t key_lds[];  // keys of the segment, padded to a multiple of 16
   __shared__ int part[kRankWaves][64];
   const int seg = blockIdx.x / chunks, chunk = blockIdx.x - (blockIdx.x / chunks) * chunks;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tokens = map.grid_h * map.grid_w;
   const int img = seg / map.segs_per_img;
   const float* im = imp + (size_t)img * tokens;
-  for (int s = tid; s < n; s += blockDim.x) {
-    const int row = map.row_of(seg, s);
+  const int n16 = (n + 15) & ~15;
+  // keys past n are pad keys with index >= n: they never precede a real slot
+#pragma unroll 4
+  for (int s = tid; s < n16; s += blockDim.x) {
+    const int row = s < n ? map.row_of(seg, s) : -1;
     key_lds[s] = row >= 0 ? desc_key(im[row - img * tokens]) : kPadKey;
   }
   __syncthreads();
   const int slot = chunk * 64 + lane;
   const bool valid = slot < n;
   const uint32_t mine = valid ? key_lds[slot] : 0u;
-  // this wavefront's share of the keys
-  const int per = (n + kRankWaves - 1) / kRankWaves;
-  const int j0 = wave * per, j1 = min(n, j0 + per);
+  // this wavefront's share of the keys, 16 at a time (four 16-byte broadcast reads in
+  // flight per step)
+  const int per = ((n16 / 16 + kRankWaves - 1) / kRankWaves) * 16;
+  const int j0 = wave * per, j1 = min(n16, j0 + per);
   int cnt = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t kj = key_lds[j];  // same address in every lane: a broadcast read
-    cnt += (kj < mine) | ((kj == mine) & (j < slot));
+  const uint4* k4 = reinterpret_cast<const uint4*>(key_lds);
+  for (int j = j0; j < j1; j += 16) {
+    uint4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = k4[j / 4 + u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t kk[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jj = j + 4 * u + e;
+        cnt += (kk[e] < mine) | ((kk[e] == mine) & (jj < slot));
+      }
+    }
   }
   part[wave][lane] = cnt;
   __syncthreads();
@@ -89,6 +104,7 @@ __global__ void __launch_bounds__(1024) keepset_kernel(const int* __restrict__ i
   const int S = n / stripes;
   for (int t = tid; t < tokens; t += nth) flag[t] = 0;
   __syncthreads();
+#pragma unroll 4
   for (int i = tid; i < segs * n; i += nth) {
     const int sg = i / n, s = i - sg * n;
     const int row = map.row_of(img * segs + sg, s) - img * tokens;
@@ -126,14 +142,14 @@ __global__ void __launch_bounds__(1024) keepset_kernel(const int* __restrict__ i
 
 size_t permute_lds_bytes(const sparsesam_plan& p) {
   const size_t tokens = (size_t)p.desc.grid_h * p.desc.grid_w;
-  return std::max((size_t)p.n * 4, tokens);
+  return std::max((size_t)((p.n + 15) & ~15) * 4, tokens);
 }
 
 hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
                           hipStream_t st) {
   const int chunks = (p.n + 63) / 64;
   const int segs = batch * p.segs_per_img;
-  const size_t key_bytes = (size_t)p.n * 4;
+  const size_t key_bytes = (size_t)((p.n + 15) & ~15) * 4;
   hipError_t e = hipFuncSetAttribute((const void*)rank_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)key_bytes);
   if (e != hipSuccess) return e;
