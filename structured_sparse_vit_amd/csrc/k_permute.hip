@@ -12,11 +12,11 @@
 // the rank alone: rank rho sits at stripe rho % g, offset rho / g, i.e. position
 // (rho % g) * S + rho / g. No sorted list is ever materialised.
 //
-//  * rank_kernel: one workgroup per (segment, 64-slot chunk). Each wavefront counts,
-//    for the chunk's 64 slots (one per lane), the preceding slots inside its share of
-//    the segment's keys (held in LDS as 32-bit order keys); the shares are summed in
-//    LDS and the 64 lanes of wavefront 0 write perm and inv. All 1024 threads of a
-//    workgroup keep the GPU busy even for a single image (4096 slots -> 64 workgroups).
+//  * rank_kernel: one workgroup per (segment, chunk of slots). Its lanes count, for
+//    the chunk's slots, the preceding slots within shares of the segment's keys (held
+//    in LDS as 32-bit order keys); the shares are summed in LDS and one lane per slot
+//    writes perm and inv. The split is chosen so a single image's 4096 slots still
+//    spread over 256 workgroups.
 //  * keepset_kernel: one workgroup per image reads each real token's rank back from
 //    inv, flags the K first of its segment, and compacts the flags in raster order
 //    (block-wide scan), which gives the keep-set ascending.
@@ -36,60 +36,65 @@ __device__ __forceinline__ uint32_t desc_key(float f) {
 }
 constexpr uint32_t kPadKey = 0xFFFFFFFFu;  // pad slots: after every real slot
 
-constexpr int kRankWaves = 16;
+// rank_kernel layout: a workgroup of kw wavefronts ranks tpw slots of one segment
+// (tpw = 16 or 64). Lane l of a wavefront serves slot l % tpw and key residue class
+// l / tpw (mod 64 / tpw); wavefront w takes the w-th share of the keys. For N = 4096
+// that is 256 workgroups of 16 wavefronts, every lane comparing 64 keys.
+constexpr int kMaxRankWaves = 16;
 
-__global__ void __launch_bounds__(64 * kRankWaves) rank_kernel(const float* __restrict__ imp, SegmentMap map,
-                                                               int n, int stripes, int chunks,
-                                                               int* __restrict__ perm, int* __restrict__ inv) {
-  extern __shared__ uint32_t key_lds[];  // keys of the segment, padded to a multiple of 16
-  __shared__ int part[kRankWaves][64];
+__global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* __restrict__ imp, SegmentMap map,
+                                                                  int n, int stripes, int chunks, int tpw,
+                                                                  int* __restrict__ perm, int* __restrict__ inv) {
+  extern __shared__ uint32_t key_lds[];  // keys of the segment, padded to a multiple of 64
+  __shared__ int part[kMaxRankWaves * 64];
   const int seg = blockIdx.x / chunks, chunk = blockIdx.x - (blockIdx.x / chunks) * chunks;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kw = blockDim.x >> 6;
   const int tokens = map.grid_h * map.grid_w;
   const int img = seg / map.segs_per_img;
   const float* im = imp + (size_t)img * tokens;
-  const int n16 = (n + 15) & ~15;
+  const int n64 = (n + 63) & ~63;
   // keys past n are pad keys with index >= n: they never precede a real slot
 #pragma unroll 4
-  for (int s = tid; s < n16; s += blockDim.x) {
+  for (int s = tid; s < n64; s += blockDim.x) {
     const int row = s < n ? map.row_of(seg, s) : -1;
     key_lds[s] = row >= 0 ? desc_key(im[row - img * tokens]) : kPadKey;
   }
   __syncthreads();
-  const int slot = chunk * 64 + lane;
+  const int subs = 64 / tpw;                 // lanes per slot
+  const int slot = chunk * tpw + (lane % tpw);
+  const int sub = lane / tpw;
   const bool valid = slot < n;
   const uint32_t mine = valid ? key_lds[slot] : 0u;
-  // this wavefront's share of the keys, 16 at a time (four 16-byte broadcast reads in
-  // flight per step)
-  const int per = ((n16 / 16 + kRankWaves - 1) / kRankWaves) * 16;
-  const int j0 = wave * per, j1 = min(n16, j0 + per);
+  // this wavefront's share of the keys: [j0, j1), a multiple of 64 long
+  const int per = ((n64 / 64 + kw - 1) / kw) * 64;
+  const int j0 = wave * per, j1 = min(n64, j0 + per);
   int cnt = 0;
-  const uint4* k4 = reinterpret_cast<const uint4*>(key_lds);
-  for (int j = j0; j < j1; j += 16) {
-    uint4 q[4];
+  for (int jb = j0; jb < j1; jb += 4 * subs) {
+    // four keys per lane per step: jb + sub + subs * u, u = 0..3
+    uint32_t kk[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) q[u] = k4[j / 4 + u];
+    for (int u = 0; u < 4; ++u) kk[u] = key_lds[jb + sub + subs * u];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t kk[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jj = j + 4 * u + e;
-        cnt += (kk[e] < mine) | ((kk[e] == mine) & (jj < slot));
-      }
+      const int jj = jb + sub + subs * u;
+      cnt += (kk[u] < mine) | ((kk[u] == mine) & (jj < slot));
     }
   }
-  part[wave][lane] = cnt;
+  part[wave * 64 + lane] = cnt;
   __syncthreads();
-  if (wave == 0 && valid) {
-    int rank = 0;
-#pragma unroll
-    for (int w = 0; w < kRankWaves; ++w) rank += part[w][lane];
-    const int S = n / stripes;
-    const int p = (rank % stripes) * S + rank / stripes;
-    const size_t base = (size_t)seg * n;
-    perm[base + p] = slot;
-    inv[base + slot] = p;
+  if (tid < tpw) {
+    const int sl = chunk * tpw + tid;
+    if (sl < n) {
+      int rank = 0;
+      for (int w = 0; w < kw; ++w)
+        for (int u = 0; u < subs; ++u) rank += part[w * 64 + u * tpw + tid];
+      const int S = n / stripes;
+      const int p = (rank % stripes) * S + rank / stripes;
+      const size_t base = (size_t)seg * n;
+      perm[base + p] = sl;
+      inv[base + sl] = p;
+    }
   }
 }
 
@@ -142,19 +147,23 @@ __global__ void __launch_bounds__(1024) keepset_kernel(const int* __restrict__ i
 
 size_t permute_lds_bytes(const sparsesam_plan& p) {
   const size_t tokens = (size_t)p.desc.grid_h * p.desc.grid_w;
-  return std::max((size_t)((p.n + 15) & ~15) * 4, tokens);
+  return std::max((size_t)((p.n + 63) & ~63) * 4, tokens);
 }
 
 hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
                           hipStream_t st) {
-  const int chunks = (p.n + 63) / 64;
+  // long segments: 16 slots per workgroup and up to 16 wavefronts splitting the keys;
+  // short ones (windows): 64 slots per workgroup, one wavefront per 256 keys
+  const int tpw = p.n >= 1024 ? 16 : 64;
+  const int kw = std::max(1, std::min(kMaxRankWaves, (p.n + 255) / 256));
+  const int chunks = (p.n + tpw - 1) / tpw;
   const int segs = batch * p.segs_per_img;
-  const size_t key_bytes = (size_t)((p.n + 15) & ~15) * 4;
+  const size_t key_bytes = (size_t)((p.n + 63) & ~63) * 4;
   hipError_t e = hipFuncSetAttribute((const void*)rank_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)key_bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)(segs * chunks)), dim3(64 * kRankWaves), key_bytes, st, imp,
-                     p.segmap(), p.n, p.desc.stripes, chunks, perm, inv);
+  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)(segs * chunks)), dim3(64 * kw), key_bytes, st, imp, p.segmap(),
+                     p.n, p.desc.stripes, chunks, tpw, perm, inv);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t flag_bytes = (size_t)p.desc.grid_h * p.desc.grid_w;
