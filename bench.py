@@ -202,6 +202,89 @@ def cpu_baseline(cfg, budget_s=25.0):
                       "attention with an explicit mask, fp64 numpy), %.2f s each" % (done, dt)}
 
 
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -T --output-format csv -d gpurun_out/trace_c2 -o c2 -- "
+             "python3 bench.py --profile-only --steps 20 --warmup 5",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_c2 -o f -- "
+             "python3 bench.py --profile-only --steps 5 --warmup 2",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_c2 -o w -- "
+             "python3 bench.py --profile-only --steps 5 --warmup 2",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_copy -o f -- "
+                  "python3 bench.py --copy-calibration",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_copy -o w -- "
+                  "python3 bench.py --copy-calibration",
+}
+ATTN_KERNELS = ("attn_mfma64_kernel", "attn_combine_kernel")
+COPY_BYTES = 256 << 20
+
+
+def _csv_rows(folder, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit("no %s under %s" % (suffix, folder))
+    return rows
+
+
+def _counter_kib(folder, counter, match):
+    """Average of `counter` (KiB per dispatch) over the dispatches whose kernel name contains match."""
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(folder, "counter_collection.csv")
+            if r["Counter_Name"] == counter and match in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit("no %s dispatches of %s in %s" % (counter, match, folder))
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_profiles(src):
+    """Turn the rocprofv3 output of PROFILE_COMMANDS (under src) into the text summaries in profiles/."""
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    # kernel trace: per-kernel launch statistics of the timed step
+    stats = _csv_rows(os.path.join(src, "trace_c2"), "kernel_stats.csv")
+    lines = ["# Kernel-trace statistics of the c2 step (SAM ViT-B global block, 64 x 64 tokens, C 768,",
+             "# 12 heads x 64, MLP 3072, density 0.4, batch 1): Sobel importance, permutation,",
+             "# keep-set and one SparseSAM block per step; 20 timed + 5 warmup steps (plus bench setup).",
+             "# command (from the repository root):",
+             "#   " + PROFILE_COMMANDS["trace"],
+             "# Durations in microseconds.",
+             "%-88s %6s %10s %10s %10s %7s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "pct")]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append("%-88s %6d %10.2f %10.2f %10.2f %7.2f" % (
+            r["Name"][:88], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    with open(os.path.join(out_dir, "c2_step_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    # HBM traffic of the attention launch, scaled by a plain copy of known size
+    cf, _ = _counter_kib(os.path.join(src, "pmc_fetch_copy"), "FETCH_SIZE", "copyBuffer")
+    cw, _ = _counter_kib(os.path.join(src, "pmc_write_copy"), "WRITE_SIZE", "copyBuffer")
+    f_scale, w_scale = (COPY_BYTES / 1024) / cf, (COPY_BYTES / 1024) / cw
+    lines = ["# HBM traffic of one sparsesam_attn launch on the c2 workload (attention kernel plus",
+             "# the combine of split rows), from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch,",
+             "# separate passes), each scaled by the same counter on a plain 256 MiB device copy.",
+             "# commands (from the repository root):"]
+    lines += ["#   " + PROFILE_COMMANDS[k] for k in ("fetch", "write", "copy_fetch", "copy_write")]
+    lines += ["copy_fetch_kib = %.1f" % cf, "copy_write_kib = %.1f" % cw,
+              "fetch_scale = %.5f" % f_scale, "write_scale = %.5f" % w_scale]
+    total = 0.0
+    for kname in ATTN_KERNELS:
+        fk, nf = _counter_kib(os.path.join(src, "pmc_fetch_c2"), "FETCH_SIZE", kname)
+        wk, nw = _counter_kib(os.path.join(src, "pmc_write_c2"), "WRITE_SIZE", kname)
+        b = (fk * f_scale + wk * w_scale) * 1024
+        total += b
+        lines += ["%s_fetch_kib = %.1f  # average of %d dispatches" % (kname, fk, nf),
+                  "%s_write_kib = %.1f  # average of %d dispatches" % (kname, wk, nw),
+                  "%s_scaled_bytes = %.0f" % (kname, b)]
+    lines += ["scaled_bytes_per_launch = %.0f" % total,
+              "source_sha256_16 = %s" % _source_hash(ATTN_SOURCE)]
+    with open(TRAFFIC_PROFILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote", os.path.join(out_dir, "c2_step_kernel_trace.txt"), "and", TRAFFIC_PROFILE)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,7 +296,12 @@ def main():
     ap.add_argument("--profile-only", action="store_true", help="run the steps only (for rocprofv3)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy 5 times (scale factor for HBM byte counters)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ summaries from the rocprofv3 output of the profiling commands in DIR")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the data-parallel "
               "split is by image, with no communication; see the design notes). Run with --gpus 1.",
@@ -329,7 +417,7 @@ def main():
                    "attn_density": cfg.attn_density, "mlp_density": cfg.mlp_density,
                    "realised_attn_density": plan.info["realised_density"],
                    "routed_tokens": plan.info["routed_per_image"] * cfg.batch},
-        "roofline": {"bound": "mfma", "kernel": "attn_mfma64_kernel", "achieved": round(attn_tf, 2),
+        "roofline": {"bound": "mfma", "kernel": "sparsesam_attn (attn_mfma64_kernel + attn_combine_kernel)", "achieved": round(attn_tf, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(), "launch_ms": round(attn_ms, 5),
                      "algorithmic_flop": attention_flops(plan) * segs},
