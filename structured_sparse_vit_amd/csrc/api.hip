@@ -207,7 +207,7 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
   });
   // matrix-core attention work list: rows of more than kChunk key tiles are split
   {
-    const int kChunk = 32;
+    const int kChunk = kAttnItemTiles;
     struct Item { int qt, kb, ke, slot; };
     std::vector<Item> v;
     p->splits.clear();

@@ -16,6 +16,11 @@ typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 
 constexpr int kWave = 64;
 
+// s_waitcnt immediate for "at most n vector-memory operations outstanding" (other
+// counters unconstrained), in the gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in bits [15:14].
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 // fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
 __device__ __forceinline__ bf16_t to_bf16(float f) { return (bf16_t)f; }
 __device__ __forceinline__ float to_f32(bf16_t b) { return (float)b; }

@@ -9,6 +9,9 @@
 #include "sparsesam.h"
 #include "common.hpp"
 
+// Longest key-tile list of one matrix-core attention work item; longer rows are split.
+constexpr int kAttnItemTiles = 32;
+
 struct sparsesam_plan {
   sparsesam_plan_desc desc;
   int n = 0;              // tokens per segment (pads included)

@@ -37,12 +37,13 @@ constexpr int kPairElems = 2 * kTile * kLd;    // one K tile + one V^T tile
 constexpr int kAttnLds = 2 * 2 * kPairElems * 2;  // [stage][key parity][K | V^T], bytes
 constexpr int kPartLd = 68;                    // partial record: O[64], m, l, pad (floats)
 
-// One work item: query tile qt against the kept key tiles col_idx[kb..ke). Rows whose
-// list is longer than the plan's chunk limit are split over several items; those
+// One work item: query tile qt against the kept key tiles col_idx[kb..ke), at most
+// kAttnItemTiles (<= 64) of them. Rows whose list is longer are split over several items; those
 // write an unnormalised partial (O, running max, running sum) to `partial` at `slot`
 // and a combine pass merges them.
 // One unit of work: work item `item` (query tile qt against kept key tiles
 // col_idx[kb..ke), partial slot or -1) for segment-head sh.
+static_assert(kAttnItemTiles <= 64, "one key tile per lane");
 __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                                  const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
                                                  const int4* __restrict__ items, const int* __restrict__ col_idx,
@@ -69,6 +70,14 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     qf[ks] = *reinterpret_cast<const bf16x8*>(q_base + (size_t)my_q * D + ks * 16 + (lane >> 5) * 8);
+  // first token of the item's j-th key tile, held by lane j and read with readlane, so
+  // the loop never waits on a dependent index load
+  const int total = ke - kb;
+  const int koff = lane < total ? tile_start[col_idx[kb + lane]] : 0;
+  // Wait for Q and the offsets here, on every path: otherwise the compiler, unable to
+  // prove the loads done at the loop head, waits for them inside the loop -- and with
+  // them for the next tile's loads issued after them, which undoes the prefetch.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   f32x16 oacc[2];
 #pragma unroll
@@ -79,8 +88,8 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
 
   // staging of this pair's K tile and V^T tile: 4 + 4 chunks of 16 bytes per thread
   i32x4 rk[4], rv[4];
-  auto load_regs = [&](int kt) {
-    const int k0 = tile_start[kt];
+  auto load_regs = [&](int j) {
+    const int k0 = __builtin_amdgcn_readlane(koff, j);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = ptid + 128 * i;  // 512 chunks: row = c / 8, chunk = c % 8
@@ -106,10 +115,9 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
     }
   };
 
-  const int total = ke - kb;
   const int niter = (total + 1) >> 1;
   if (kp < total) {
-    load_regs(col_idx[kb + kp]);
+    load_regs(kp);
     store_lds(0);
   }
   __syncthreads();
@@ -117,7 +125,7 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
     const int cur = i & 1;
     const bool has_cur = 2 * i + kp < total;
     const bool has_next = 2 * (i + 1) + kp < total;
-    if (has_next) load_regs(col_idx[kb + 2 * (i + 1) + kp]);
+    if (has_next) load_regs(2 * (i + 1) + kp);
     if (has_cur) {
       const bf16_t* Ks = lds + (cur * 2 + kp) * kPairElems;
       const bf16_t* Vs = Ks + kTile * kLd;

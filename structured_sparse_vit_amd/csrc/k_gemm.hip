@@ -164,11 +164,6 @@ struct ResidualAdd {
 
 constexpr int BK = 64;  // K step: one 128-byte row of bf16 per tile row
 
-// s_waitcnt immediate for "at most n vector-memory operations outstanding" (other
-// counters unconstrained), in the gfx9 encoding: vmcnt[3:0], expcnt[6:4],
-// lgkmcnt[11:8], vmcnt[5:4] in bits [15:14].
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
 // ST: LDS pipeline depth (ST - 1 K steps in flight while one is multiplied).
 template <int BM, int BN, int ST>
 struct Tile {
