@@ -60,6 +60,15 @@ __device__ __forceinline__ int xcd_remap(int hw_id, int total) {
 }
 __host__ __device__ inline int xcd_grid(int total) { return kXcds * ((total + kXcds - 1) / kXcds); }
 
+// Swizzled LDS tiles: 128-byte rows (64 bf16), the 16-byte chunk c of row r stored at
+// chunk position c ^ ((r >> 1) & 7). gfx950 serves a 16-byte read for 16 lanes at a
+// time from 16 groups of banks (group = address / 16 mod 16); 16 consecutive rows of one
+// logical chunk then land in 16 distinct groups (no bank conflicts). A wavefront's
+// direct-to-LDS load -- 64 lanes x 16 bytes into one contiguous 1 KiB block, lane L at
+// byte 16 L -- fills 8 whole rows when lane L fetches the chunk that belongs there.
+__device__ __forceinline__ int swz_key(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ swz_key(r)) << 4); }
+
 // GELU with the exact Gaussian CDF.
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 

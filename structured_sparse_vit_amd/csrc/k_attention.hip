@@ -32,17 +32,32 @@ namespace sparsesam {
 // ---------------------------------------------------------------- MFMA kernel (D = 64, B = 64)
 
 constexpr int kTile = 64;
-constexpr int kLd = 64 + 8;                    // LDS row stride in bf16 (16-byte pad)
-constexpr int kPairElems = 2 * kTile * kLd;    // one K tile + one V^T tile
-constexpr int kAttnLds = 2 * 2 * kPairElems * 2;  // [stage][key parity][K | V^T], bytes
-constexpr int kPartLd = 68;                    // partial record: O[64], m, l, pad (floats)
+constexpr int kTileBytes = kTile * 128;          // one swizzled 64 x 64 bf16 tile
+constexpr int kParityBytes = 4 * kTileBytes;     // K ring (2 slots) + V^T ring (2 slots)
+constexpr int kAttnLds = 2 * kParityBytes;       // two key parities: 64 KiB
+constexpr int kPartLd = 68;                      // partial record: O[64], m, l, pad (floats)
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// max over lanes l and l ^ 32 (one permlane swap, no LDS round trip)
+__device__ __forceinline__ float max_xor32(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
 
 // One work item: query tile qt against the kept key tiles col_idx[kb..ke), at most
-// kAttnItemTiles (<= 64) of them. Rows whose list is longer are split over several items; those
-// write an unnormalised partial (O, running max, running sum) to `partial` at `slot`
-// and a combine pass merges them.
-// One unit of work: work item `item` (query tile qt against kept key tiles
-// col_idx[kb..ke), partial slot or -1) for segment-head sh.
+// kAttnItemTiles (<= 64) of them. Rows whose list is longer are split over several
+// items; those write an unnormalised partial (O, running max, running sum) to
+// `partial` at `slot` and a combine pass merges them. One unit of work is one item for
+// one segment-head sh.
+//
+// Pipeline of a wavefront (query half qh, key parity kp; its j-th tile is item tile
+// 2 j + kp): K tiles run one step ahead of V^T tiles. In step j the wavefront issues
+// the direct-to-LDS loads of K_{j+2} and V_{j+1}, starts S_{j+1} = K_{j+1} Q^T on the
+// matrix cores, and meanwhile runs the softmax of S_j and O^T += V_j^T P_j^T. Each ring
+// (K, V^T) has two slots per parity; one barrier per step both publishes the loads of
+// the previous step and retires the slots they overwrite.
 static_assert(kAttnItemTiles <= 64, "one key tile per lane");
 __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                                  const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
@@ -51,17 +66,16 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
                                                  int seg_heads, float c_log2, float* __restrict__ partial, int item,
                                                  int sh, char* smem) {
   constexpr int D = 64;
-  bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qh = wave & 1;   // query half of the tile
   const int kp = wave >> 1;  // key-tile parity this wavefront pair walks
-  const int ptid = tid & 127;
   const int4 it = items[item];
   const int qt = it.x, kb = it.y, ke = it.z, slot = it.w;
   const int seg = sh / heads, h = sh - seg * heads;
   const bf16_t* q_base = Q + (size_t)sh * n * D;
   const bf16_t* k_base = Kt + (size_t)sh * n * D;
   const bf16_t* v_base = VT + (size_t)sh * D * n_pad;
+  char* ring = smem + kp * kParityBytes;
 
   const int q_local = qh * 32 + (lane & 31);
   const int my_q = tile_start[qt] + q_local;
@@ -70,14 +84,66 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     qf[ks] = *reinterpret_cast<const bf16x8*>(q_base + (size_t)my_q * D + ks * 16 + (lane >> 5) * 8);
-  // first token of the item's j-th key tile, held by lane j and read with readlane, so
+  // first token of the item's i-th key tile, held by lane i and read with readlane, so
   // the loop never waits on a dependent index load
   const int total = ke - kb;
   const int koff = lane < total ? tile_start[col_idx[kb + lane]] : 0;
   // Wait for Q and the offsets here, on every path: otherwise the compiler, unable to
-  // prove the loads done at the loop head, waits for them inside the loop -- and with
-  // them for the next tile's loads issued after them, which undoes the prefetch.
+  // prove the loads done at the loop head, may wait for them inside the loop -- and
+  // with them for the tile loads issued after them.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  // Direct-to-LDS tile loads: the pair's two wavefronts fill the 8 row groups of a tile
+  // (wavefront qh takes groups qh, qh + 2, qh + 4, qh + 6); lane L fetches the chunk
+  // that the swizzle places at byte 16 L of its group.
+  int k_src[4], v_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = qh + 2 * i;
+    const int row = 8 * g + (lane >> 3), c = (lane & 7) ^ swz_key(8 * g + (lane >> 3));
+    k_src[i] = row * D + c * 8;
+    v_src[i] = row * n_pad + c * 8;
+  }
+  auto issue_k = [&](int j, int s) {  // K tile of step j into K slot s
+    const int k0 = __builtin_amdgcn_readlane(koff, 2 * j + kp);
+    const bf16_t* src = k_base + (size_t)k0 * D;
+    char* dst = ring + s * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src + k_src[i]),
+                                       (__attribute__((address_space(3))) void*)(dst + (qh + 2 * i) * 1024), 16, 0,
+                                       0);
+  };
+  auto issue_v = [&](int j, int s) {  // V^T tile of step j into V slot s
+    const int k0 = __builtin_amdgcn_readlane(koff, 2 * j + kp);
+    const bf16_t* src = v_base + k0;
+    char* dst = ring + (2 + s) * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src + v_src[i]),
+                                       (__attribute__((address_space(3))) void*)(dst + (qh + 2 * i) * 1024), 16, 0,
+                                       0);
+  };
+  // S^T = K Q^T for the K tile in slot s: two 32-key blocks
+  auto scores = [&](int s, f32x16 (&sc)[2]) {
+    const char* Ks = ring + s * kTileBytes;
+    bf16x8 kf[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kf[mb][ks] = *reinterpret_cast<const bf16x8*>(Ks + swz(mb * 32 + (lane & 31), ks * 2 + (lane >> 5)));
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[mb][e] = 0.0f;
+    // the two accumulation chains alternate, so each MFMA depends on the one two back
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mb][ks], qf[ks], sc[mb], 0, 0, 0);
+  };
 
   f32x16 oacc[2];
 #pragma unroll
@@ -86,113 +152,101 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // staging of this pair's K tile and V^T tile: 4 + 4 chunks of 16 bytes per thread
-  i32x4 rk[4], rv[4];
-  auto load_regs = [&](int j) {
-    const int k0 = __builtin_amdgcn_readlane(koff, j);
+  // online softmax of S_j (this lane's query: 32 of the tile's 64 scores, the rest in
+  // lane ^ 32), then O^T += V^T P^T with V^T from slot s
+  auto softmax_pv = [&](const f32x16 (&sc)[2], int s) {
+    float mx = sc[0][0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = ptid + 128 * i;  // 512 chunks: row = c / 8, chunk = c % 8
-      const int row = c >> 3, ch = c & 7;
-      rk[i] = *reinterpret_cast<const i32x4*>(k_base + (size_t)(k0 + row) * D + ch * 8);
-      rv[i] = *reinterpret_cast<const i32x4*>(v_base + (size_t)row * n_pad + k0 + ch * 8);
-    }
-  };
-  auto store_lds = [&](int stage) {
-    bf16_t* Ks = lds + (stage * 2 + kp) * kPairElems;
-    bf16_t* Vs = Ks + kTile * kLd;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = ptid + 128 * i;
-      const int row = c >> 3, ch = c & 7;
-      *reinterpret_cast<i32x4*>(Ks + row * kLd + ch * 8) = rk[i];
-      // V^T: inside each 16-key group keys are stored as [0..3, 8..11, 4..7, 12..15] so a
-      // lane's eight k-slots of the P^T operand are contiguous
-      const int grp = ch >> 1, half = ch & 1;
-      bf16_t* dst = Vs + row * kLd + grp * 16 + half * 4;
-      *reinterpret_cast<i32x2*>(dst) = i32x2{rv[i][0], rv[i][1]};
-      *reinterpret_cast<i32x2*>(dst + 8) = i32x2{rv[i][2], rv[i][3]};
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[mb][e]);
+    mx = max_xor32(mx);
+    const float m_new = fmaxf(m_run, mx * c_log2);
+    // rescale only when some row's running max moved (wave-uniform branch)
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < 2; ++md)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
+      m_run = m_new;
     }
+    // P^T operand of key group kk (keys 16 kk .. + 15): the accumulator gives lane half
+    // hf keys 4 hf + 0..3 and 8 + 4 hf + 0..3 of the group; the MFMA wants keys
+    // 8 hf + 0..7 (the V^T tile is in natural key order). Swapping the middle pairs of
+    // bf16 pairs between lane halves puts them there.
+    float psum = 0.0f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + e], c_log2, -m_run));
+        psum += p;
+        v[e] = to_bf16(p);
+      }
+      u32x4 r = __builtin_bit_cast(u32x4, v);
+      const auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+      r = u32x4{s02[0], s13[0], s02[1], s13[1]};
+      pf[kk] = __builtin_bit_cast(bf16x8, r);
+    }
+    l_run += psum;
+    const char* Vs = ring + (2 + s) * kTileBytes;
+    bf16x8 vf[2][4];
+#pragma unroll
+    for (int md = 0; md < 2; ++md)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        vf[md][kk] = *reinterpret_cast<const bf16x8*>(Vs + swz(md * 32 + (lane & 31), kk * 2 + (lane >> 5)));
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int md = 0; md < 2; ++md)
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[md][kk], pf[kk], oacc[md], 0, 0, 0);
   };
 
-  const int niter = (total + 1) >> 1;
-  if (kp < total) {
-    load_regs(kp);
-    store_lds(0);
+  const int nj = (total - kp + 1) >> 1;   // tiles of this parity
+  const int niter = (total + 1) >> 1;     // steps (the same for both parities)
+  f32x16 s0[2], s1[2];
+  if (nj > 0) issue_k(0, 0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (nj > 1) issue_k(1, 1);
+  if (nj > 0) {
+    issue_v(0, 0);
+    scores(0, s0);
   }
-  __syncthreads();
-  for (int i = 0; i < niter; ++i) {
-    const int cur = i & 1;
-    const bool has_cur = 2 * i + kp < total;
-    const bool has_next = 2 * (i + 1) + kp < total;
-    if (has_next) load_regs(2 * (i + 1) + kp);
-    if (has_cur) {
-      const bf16_t* Ks = lds + (cur * 2 + kp) * kPairElems;
-      const bf16_t* Vs = Ks + kTile * kLd;
-      // all K and V^T fragments of the tile are requested up front, so LDS latency is
-      // paid once per tile and the V reads land while the softmax runs
-      bf16x8 kf[2][4], vf[2][4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kf[mb][ks] =
-              *reinterpret_cast<const bf16x8*>(Ks + (mb * 32 + (lane & 31)) * kLd + ks * 16 + (lane >> 5) * 8);
-#pragma unroll
-      for (int md = 0; md < 2; ++md)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          vf[md][kk] =
-              *reinterpret_cast<const bf16x8*>(Vs + (md * 32 + (lane & 31)) * kLd + kk * 16 + (lane >> 5) * 8);
-      // S^T = K Q^T: two 32-key blocks
-      f32x16 s[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[mb][e] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mb][ks], qf[ks], s[mb], 0, 0, 0);
-      }
-      // online softmax for this lane's query (32 of the tile's 64 scores; the rest in lane ^ 32)
-      float mx = s[0][0];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * c_log2);
-      // rescale only when some row's running max moved (wave-uniform branch)
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int md = 0; md < 2; ++md)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
-        m_run = m_new;
-      }
-      float psum = 0.0f;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][hh * 8 + e], c_log2, -m_run));
-            psum += p;
-            pf[mb * 2 + hh][e] = to_bf16(p);
-          }
-      l_run += psum;
-      // O^T += V^T P^T over four 16-key steps
-#pragma unroll
-      for (int md = 0; md < 2; ++md)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[md][kk], pf[kk], oacc[md], 0, 0, 0);
+  // step j < nj: S_j is in (j even ? s0 : s1); V_j and K_{j+1} were issued in step
+  // j - 1. S_{j+1} and the softmax of S_j share one block so their MFMA and VALU work
+  // can interleave.
+  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j + 2 < nj) issue_k(j + 2, j & 1);
+    if (j + 1 < nj) {
+      issue_v(j + 1, (j + 1) & 1);
+      scores((j + 1) & 1, nxt);
+      softmax_pv(cur, j & 1);
+    } else {
+      softmax_pv(cur, j & 1);
     }
-    if (has_next) store_lds(cur ^ 1);
-    __syncthreads();
+  };
+  for (int j = 0; j < nj; j += 2) {
+    step(j, s0, s1);
+    if (j + 1 < nj) step(j + 1, s1, s0);
   }
+  if (nj < niter) {  // the odd pair of an odd-length item: one step fewer, same barriers
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  // every wavefront is done with the rings before the exchange area reuses them
+  __syncthreads();
 
   // merge the odd-parity pair into the even one through LDS (same lane -> same queries)
   float* xch = reinterpret_cast<float*>(smem) + (size_t)qh * 64 * 34;

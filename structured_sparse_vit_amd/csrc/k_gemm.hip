@@ -179,14 +179,7 @@ struct Tile {
   static constexpr int LDS_BYTES = PIPE_BYTES > CT_BYTES ? PIPE_BYTES : CT_BYTES;
 };
 
-// Tiles live in LDS unpadded, 128 bytes per row, with the 16-byte chunk c of row r
-// stored at chunk c ^ ((r >> 1) & 7). gfx950 serves a 16-byte read for 16 lanes at a
-// time from 16 groups of banks (group = address / 16 mod 16); 16 consecutive rows of one
-// logical chunk then land in 16 distinct groups (no bank conflicts). Each wavefront's
-// direct-to-LDS load -- 64 lanes x 16 bytes into one contiguous 1 KiB block, lane L at
-// byte 16 L -- fills 8 whole rows by giving lane L the chunk that belongs there.
-__device__ __forceinline__ int swz_key(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ swz_key(r)) << 4); }
+// Tiles live in LDS in the swizzled 128-byte-row layout of swz() (common.hpp).
 
 // wait until at most n of this wavefront's tile loads are in flight, then meet the
 // other wavefronts; the empty asm keeps the compiler from moving LDS reads above it
