@@ -9,17 +9,19 @@
 //
 // Kernels:
 //  * attn_mfma64_kernel (bf16, head_dim 64, B = 64, stripes a multiple of 64 long):
-//    one 256-thread workgroup per (work item, segment, head), issued longest first; a
-//    work item is a query tile against at most 32 of its kept key tiles (longer rows,
-//    the global one, are split and merged by attn_combine_kernel). Wavefronts 0 and 1
-//    own query halves 0..31 and 32..63 on the even key tiles of the item, wavefronts 2
-//    and 3 the same queries on the odd ones; the two halves merge through LDS at the
-//    end. S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so a lane
-//    holds one query's scores (the softmax row max needs one exchange with lane ^ 32)
-//    and one query's output column. K and transposed V tiles are double-buffered in
-//    LDS with one barrier per step, the next tile's global loads in flight during the
-//    current one. Online softmax in fp32 with exp2, the scale folded into one
-//    multiply-add per score, and the output rescale skipped when no row max moved.
+//    persistent 256-thread workgroups walk units = (work item, segment, head), longest
+//    first; a work item is a query tile against at most 32 of its kept key tiles
+//    (longer rows, the global one, are split and merged by attn_combine_kernel).
+//    Wavefronts 0 and 1 own query halves 0..31 and 32..63 on the even key tiles of the
+//    item, wavefronts 2 and 3 the same queries on the odd ones; the two halves merge
+//    through LDS at the end. S^T = K Q^T and O^T = V^T P^T run on
+//    v_mfma_f32_32x32x16_bf16, so a lane holds one query's scores (the row max needs
+//    one permlane swap with lane ^ 32) and one query's output column. K and V^T tiles
+//    arrive by direct-to-LDS loads into swizzled two-slot rings, K one tile ahead of
+//    V^T, so each step overlaps the next tile's S MFMAs with the current softmax.
+//    Online softmax in fp32 with exp2, the scale folded into one multiply-add per
+//    score, and the output rescale skipped unless a row max passes its reference
+//    by more than 2^8.
 //  * attn_simt_kernel (fp32 or bf16 storage, any pattern and head_dim <= 128): one
 //    thread per query, keys read through the cache; the exact path for small
 //    configs and for windows.
@@ -38,6 +40,12 @@ constexpr int kAttnLds = 2 * kParityBytes;       // two key parities: 64 KiB
 constexpr int kPartLd = 68;                      // partial record: O[64], m, l, pad (floats)
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// The running max of the online softmax is the reference of exp2(); moving it costs a
+// rescale of the output accumulators. The result does not depend on the reference, so
+// it only moves when a new score exceeds it by more than this many binary orders:
+// probabilities then stay below 2^8, far inside the fp32 and bf16 range.
+constexpr float kRescaleSlack = 8.0f;
 
 // max over lanes l and l ^ 32 (one permlane swap, no LDS round trip)
 __device__ __forceinline__ float max_xor32(float v) {
@@ -162,8 +170,9 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[mb][e]);
     mx = max_xor32(mx);
     const float m_new = fmaxf(m_run, mx * c_log2);
-    // rescale only when some row's running max moved (wave-uniform branch)
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+    // rescale only when some row's max passed its reference by more than the slack
+    // (wave-uniform branch; always taken on the first tile, where m_run = -inf)
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -176,7 +185,7 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
     // hf keys 4 hf + 0..3 and 8 + 4 hf + 0..3 of the group; the MFMA wants keys
     // 8 hf + 0..7 (the V^T tile is in natural key order). Swapping the middle pairs of
     // bf16 pairs between lane halves puts them there.
-    float psum = 0.0f;
+    float psum0 = 0.0f, psum1 = 0.0f;
     bf16x8 pf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -184,7 +193,10 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + e], c_log2, -m_run));
-        psum += p;
+        if (e & 1)
+          psum1 += p;
+        else
+          psum0 += p;
         v[e] = to_bf16(p);
       }
       u32x4 r = __builtin_bit_cast(u32x4, v);
@@ -193,7 +205,7 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
       r = u32x4{s02[0], s13[0], s02[1], s13[1]};
       pf[kk] = __builtin_bit_cast(bf16x8, r);
     }
-    l_run += psum;
+    l_run += psum0 + psum1;
     const char* Vs = ring + (2 + s) * kTileBytes;
     bf16x8 vf[2][4];
 #pragma unroll
