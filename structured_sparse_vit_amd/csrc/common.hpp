@@ -69,25 +69,59 @@ __host__ __device__ inline int xcd_grid(int total) { return kXcds * ((total + kX
 __device__ __forceinline__ int swz_key(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ swz_key(r)) << 4); }
 
-// GELU with the exact Gaussian CDF.
-__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2), t = 1 / (1 + p x) for
+// x >= 0 (odd symmetry otherwise), absolute error below 1.5e-7. Branch-free, one
+// reciprocal and one exp2, against a two-branch library erff.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  const float poly =
+      fmaf(fmaf(fmaf(fmaf(1.061405429f, t, -1.453152027f), t, 1.421413741f), t, -0.284496736f), t, 0.254829592f) * t;
+  const float e = __builtin_amdgcn_exp2f(-(ax * ax) * 1.4426950408889634f);
+  return copysignf(fmaf(-poly, e, 1.0f), x);
+}
+
+// GELU with the Gaussian CDF, 0.5 z (1 + erf(z / sqrt 2)).
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752f)); }
+
+// Division by a divisor fixed on the host, by multiplication (Granlund & Montgomery,
+// "Division by invariant integers using multiplication", 1994, round-up method): for
+// 0 <= x < 2^31, x / d = (umulhi(x, mul) + x) >> shift with shift = ceil(log2 d) and
+// mul = floor(2^32 (2^shift - d) / d) + 1. Three VALU operations instead of a
+// division sequence. The default object divides by 1.
+struct FastDiv {
+  uint32_t d = 1, mul = 0, shift = 0;
+  FastDiv() = default;
+  __host__ explicit FastDiv(uint32_t divisor) : d(divisor ? divisor : 1) {
+    while ((1ull << shift) < d) ++shift;
+    mul = (uint32_t)((((1ull << 32) * ((1ull << shift) - d)) / d) + 1);
+  }
+  __device__ __forceinline__ int div(int x) const {
+    return (int)((__umulhi((uint32_t)x, mul) + (uint32_t)x) >> shift);
+  }
+};
 
 // Image-token row of a segment slot. Global segments map slot -> token directly;
 // windowed segments map (window, slot) through the padded window grid. Returns -1
-// for a pad slot.
+// for a pad slot. The divisions use host-prepared FastDiv divisors.
 struct SegmentMap {
   int grid_h, grid_w, window, nwx, segs_per_img, n;
+  FastDiv f_spi, f_nwx, f_win, f_n;  // by segs_per_img, nwx, window (or 1), n
+
+  // segment of a stripe-sorted segment row r (rows are segment-major, n per segment)
+  __device__ __forceinline__ int seg_of(int r) const { return f_n.div(r); }
 
   __device__ __forceinline__ int row_of(int seg, int slot) const {
-    int img = seg / segs_per_img;
+    const int img = f_spi.div(seg);
     int tok;
     if (window == 0) {
       tok = slot;
     } else {
-      int w = seg - img * segs_per_img;
-      int wy = w / nwx, wx = w - wy * nwx;
-      int ly = slot / window, lx = slot - ly * window;
-      int y = wy * window + ly, x = wx * window + lx;
+      const int w = seg - img * segs_per_img;
+      const int wy = f_nwx.div(w), wx = w - wy * nwx;
+      const int ly = f_win.div(slot), lx = slot - ly * window;
+      const int y = wy * window + ly, x = wx * window + lx;
       if (y >= grid_h || x >= grid_w) return -1;
       tok = y * grid_w + x;
     }

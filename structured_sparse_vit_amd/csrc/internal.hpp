@@ -60,6 +60,10 @@ struct sparsesam_plan {
     m.nwx = nwx;
     m.segs_per_img = segs_per_img;
     m.n = n;
+    m.f_spi = sparsesam::FastDiv((uint32_t)segs_per_img);
+    m.f_nwx = sparsesam::FastDiv((uint32_t)nwx);
+    m.f_win = sparsesam::FastDiv((uint32_t)(desc.window > 0 ? desc.window : 1));
+    m.f_n = sparsesam::FastDiv((uint32_t)n);
     return m;
   }
 };

@@ -39,21 +39,24 @@ __device__ __forceinline__ void store8<float>(float* dst, const float* v) {
 }
 
 // q, k [seg, H, N, D] and V^T [seg, H, D, N_pad] from the columns of the QKV product.
+// Token r of the stripe-sorted rows is slot p of segment seg; column c is channel d of
+// head h of part `which` (q, k, v). Divisions by n, C and D use FastDiv.
 template <typename T>
 struct QKVStore {
   const float* bias;
   T *q, *k, *vt;
   int n, n_pad, heads, D, C;
+  FastDiv f_n, f_C, f_D;
 
   // One store through a selected base pointer and index. (A three-way if / else-if /
   // else with a store in each arm was compiled for gfx950 into code that sent the V^T
   // stores through the k pointer; selects avoid that shape.)
   __device__ __forceinline__ void elem(int r, int c, float v) const {
     v += bias[c];
-    const int which = c / C;
+    const int which = f_C.div(c);
     const int cc = c - which * C;
-    const int h = cc / D, d = cc - h * D;
-    const int seg = r / n, p = r - seg * n;
+    const int h = f_D.div(cc), d = cc - h * D;
+    const int seg = f_n.div(r), p = r - seg * n;
     const size_t sh = (size_t)seg * heads + h;
     const bool is_v = which >= 2;
     const size_t idx = is_v ? (sh * D + d) * (size_t)n_pad + p : (sh * n + p) * (size_t)D + d;
@@ -64,15 +67,15 @@ struct QKVStore {
   __device__ __forceinline__ bool col_tile(int c0) const { return c0 >= 2 * C; }
   // Eight channels c..c+7 of token r (c % 8 == 0 and D % 8 == 0: one head, one part).
   __device__ __forceinline__ void row8(int r, int c, const float* v) const {
-    const int which = c / C;
+    const int which = f_C.div(c);
     if (which >= 2) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) elem(r, c + i, v[i]);
       return;
     }
     const int cc = c - which * C;
-    const int h = cc / D, d = cc - h * D;
-    const int seg = r / n, p = r - seg * n;
+    const int h = f_D.div(cc), d = cc - h * D;
+    const int seg = f_n.div(r), p = r - seg * n;
     const size_t sh = (size_t)seg * heads + h;
     float w[8];
 #pragma unroll
@@ -82,11 +85,11 @@ struct QKVStore {
   }
   // Eight tokens r..r+7 (r % 8 == 0, count of them below M) of channel c.
   __device__ __forceinline__ void col8(int r, int c, const float* v, int count) const {
-    const int seg = r / n, p = r - seg * n;
-    const int which = c / C;
+    const int seg = f_n.div(r), p = r - seg * n;
+    const int which = f_C.div(c);
     if (which == 2 && count == 8 && p + 8 <= n && (p & 7) == 0) {
       const int cc = c - 2 * C;
-      const int h = cc / D, d = cc - h * D;
+      const int h = f_D.div(cc), d = cc - h * D;
       const size_t sh = (size_t)seg * heads + h;
       const float b = bias[c];
       float w[8];
@@ -133,7 +136,7 @@ struct ResidualAdd {
   long long x_rows;
   __device__ __forceinline__ int dst_row(int r) const {
     if (list) return list[r];
-    return map.row_of(r / map.n, perm[r]);
+    return map.row_of(map.seg_of(r), perm[r]);
   }
   __device__ __forceinline__ void elem(int r, int c, float v) const {
     const int row = dst_row(r);
@@ -197,7 +200,8 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
                                                int N, int K, const Epi& epi, char* smem, int m0, int n0) {
   using TL = Tile<BM, BN, ST>;
   constexpr int kStages = ST;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets stay scalar
   const int wm = wave >> 1, wn = wave & 1;
 
   f32x16 acc[TL::MI][TL::NI];
@@ -208,30 +212,34 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Global source of this lane for each of its groups. Group g < BM/8 holds A rows
-  // 8g..8g+7, the rest W rows; lane L fills row 8g + L/8 at chunk position L%8, which
-  // holds logical chunk (L%8) ^ swz_key(8g + L/8). Rows past M or N are clamped to the
-  // last row: the loads stay unconditional and those rows only reach accumulators that
-  // are never stored.
-  const bf16_t* src[TL::LOADS];
+  // Global source of this lane for each of its groups, as a byte offset from the tile's
+  // first A row or W row (a scalar base that advances by one K step per step). Group
+  // g < BM/8 holds A rows 8g..8g+7, the rest W rows; lane L fills row 8g + L/8 at chunk
+  // position L%8, which holds logical chunk (L%8) ^ swz_key(8g + L/8). Rows past M or N
+  // are clamped to the last row: the loads stay unconditional and those rows only reach
+  // accumulators that are never stored.
+  uint32_t voff[TL::LOADS];
 #pragma unroll
   for (int i = 0; i < TL::LOADS; ++i) {
     const int g = wave + 4 * i;
     const int r = lane >> 3, lc = (lane & 7) ^ swz_key(8 * g + r);
     if (g < BM / 8) {
       const int gm = min(m0 + g * 8 + r, M - 1);
-      src[i] = A + (size_t)gm * K + lc * 8;
+      voff[i] = (uint32_t)(((gm - m0) * K + lc * 8) * 2);
     } else {
       const int gn = min(n0 + (g - BM / 8) * 8 + r, N - 1);
-      src[i] = W + (size_t)gn * K + lc * 8;
+      voff[i] = (uint32_t)(((gn - n0) * K + lc * 8) * 2);
     }
   }
+  const char* a_base = reinterpret_cast<const char*>(A + (size_t)m0 * K);
+  const char* w_base = reinterpret_cast<const char*>(W + (size_t)n0 * K);
   auto issue = [&](int kt) {
     char* base = smem + (kt % kStages) * TL::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < TL::LOADS; ++i) {
       const int g = wave + 4 * i;
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kt * BK),
+      const char* src = (g < BM / 8 ? a_base : w_base) + kt * (BK * 2);
+      __builtin_amdgcn_global_load_lds((const void*)(src + voff[i]),
                                        (__attribute__((address_space(3))) void*)(base + g * 1024), 16, 0, 0);
     }
   };
@@ -445,7 +453,8 @@ static hipError_t run(const float* a, const float* w, int m, int n, int k, const
 template <typename T>
 hipError_t launch_gemm_qkv(const T* a, const T* w, int m, int k, const EpiQKV& e, hipStream_t st) {
   if (m <= 0) return hipSuccess;
-  QKVStore<T> s{e.bias, (T*)e.q, (T*)e.k, (T*)e.vt, e.n, e.n_pad, e.heads, e.head_dim, e.channels};
+  QKVStore<T> s{e.bias, (T*)e.q, (T*)e.k, (T*)e.vt, e.n, e.n_pad, e.heads, e.head_dim, e.channels,
+                FastDiv((uint32_t)e.n), FastDiv((uint32_t)e.channels), FastDiv((uint32_t)e.head_dim)};
   return run(a, w, m, 3 * e.channels, k, s, st);
 }
 

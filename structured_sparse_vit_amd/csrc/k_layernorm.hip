@@ -23,7 +23,7 @@ __global__ void __launch_bounds__(256) gather_ln_kernel(const float* __restrict_
   if (list) {
     src = list[r];
   } else {
-    int seg = r / map.n, slot = perm[r];
+    int seg = map.seg_of(r), slot = perm[r];
     src = map.row_of(seg, slot);
   }
   T* o = out + (size_t)r * C;
@@ -72,7 +72,7 @@ __global__ void __launch_bounds__(256) gather_ln_vec_kernel(const float* __restr
   if (list) {
     src = list[r];
   } else {
-    const int seg = r / map.n, slot = perm[r];
+    const int seg = map.seg_of(r), slot = perm[r];
     src = map.row_of(seg, slot);
   }
   bf16_t* o = out + (size_t)r * C;
