@@ -5,18 +5,21 @@
 // weights). bf16 operands run on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16,
 // fp32 accumulation); the fp32 path is a plain SIMT kernel for small exact checks.
 //
-// bf16 kernel: BM x BN output tile (128 x 128 or 128 x 64) per 256-thread workgroup,
+// bf16 kernel: BM x BN output tile (128 x 64 or 64 x 64) per 256-thread workgroup,
 // K step 64, four wavefronts in a 2 x 2 layout each owning a (BM/2) x (BN/2) block of
-// 32 x 32 MFMA tiles. A and W tiles go global -> registers -> LDS, double-buffered in
-// LDS with one barrier per K step: the next step's global loads are in flight while
-// the current step multiplies. LDS rows are padded by 16 bytes so the 16-byte fragment
-// reads of 32 consecutive rows hit distinct banks.
+// 32 x 32 MFMA tiles. A and W tiles go straight from global memory into LDS
+// (global_load_lds_dwordx4, no register staging) through an ST-stage ring of swizzled
+// 128-byte rows, with an explicit vmcnt wait and one barrier per K step; ST - 1 steps
+// of loads stay in flight while one step multiplies. The tile grid is cut into one
+// rectangle per XCD (each XCD's L2 then holds only the A and W rows it needs).
 //
 // Epilogue: the fp32 tile is staged in LDS, then written out as 16-byte chunks along
 // the destination's contiguous axis -- 8 channels of one token for q, k, the MLP
 // hidden activation and the residual stream, 8 tokens of one channel for the
 // transposed V the attention kernel reads -- so every store is a full vector store
 // and the index decoding (token -> segment, column -> head) runs once per chunk.
+// (Storing straight from the accumulators, 4-element pieces of 32 rows per
+// instruction, measured slower: four times the memory transactions.)
 #include "internal.hpp"
 
 namespace sparsesam {
@@ -251,14 +254,16 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
   for (int kt = 0; kt < nk; ++kt) {
     // stage kt must be complete; the later stages already issued (at most
     // kStages - 2 of them) may stay in flight
-    static_assert(kStages >= 2 && kStages <= 4, "pipeline depth");
+    static_assert(kStages >= 2 && kStages <= 5, "pipeline depth");
     const int later = min(kStages - 2, nk - 1 - kt);
     if (later <= 0)
       stage_ready<0>();
     else if (later == 1)
       stage_ready<TL::LOADS>();
-    else
+    else if (later == 2)
       stage_ready<2 * TL::LOADS>();
+    else
+      stage_ready<3 * TL::LOADS>();
     if (kt + kStages - 1 < nk) issue(kt + kStages - 1);  // into the buffer read last step
     const char* As = smem + (kt % kStages) * TL::STAGE_BYTES;
     const char* Bs = As + BM * 128;
@@ -435,11 +440,15 @@ static hipError_t run_bf16(const bf16_t* a, const bf16_t* w, int m, int n, int k
   return hipGetLastError();
 }
 
-// 128 x 64 tiles (48 KiB of LDS at two stages: three workgroups per CU); long K
-// (the fc2 product) keeps two steps in flight.
+// Tile choice (measured on the ViT-B shapes): wide products (QKV, fc1) take 128 x 64
+// tiles at two stages (48 KiB of LDS, three workgroups per CU); narrow ones (N <= 1024:
+// the projection) 64 x 64 tiles, twice the workgroups; long K (fc2) 64 x 64 tiles with
+// three steps in flight (64 KiB, two workgroups per CU). Resident workgroups matter
+// more than pipeline depth at K = 768.
 template <class Epi>
 static hipError_t run(const bf16_t* a, const bf16_t* w, int m, int n, int k, const Epi& e, hipStream_t st) {
-  if (k >= 2048) return run_bf16<128, 64, 3>(a, w, m, n, k, e, st);
+  if (k >= 2048) return run_bf16<64, 64, 4>(a, w, m, n, k, e, st);
+  if (n <= 1024) return run_bf16<64, 64, 2>(a, w, m, n, k, e, st);
   return run_bf16<128, 64, 2>(a, w, m, n, k, e, st);
 }
 
