@@ -150,7 +150,9 @@ sparsesam_status sparsesam_importance(const float* img, int32_t batch, int32_t h
  *          global grid or within the window).
  *   inv    [batch * segments_per_image, N] int32: inv[perm[p]] = p.
  *   routed [batch * routed_per_image] int32: global row ids (image * grid_h * grid_w +
- *          token) of the keep-set, ascending.
+ *          token) of the keep-set. Per image, segment by segment (segment w starts at
+ *          the sum of the keep-set sizes of segments 0..w-1), each segment's K tokens in
+ *          the order below: most important first.
  * Order: importance descending, ties by lower slot, -0.0 == +0.0, NaN after every
  * number, window pad slots after every real slot (so no pad enters the keep-set). The
  * stripe-sort reads the sorted list as an (N/g) x g matrix, transposes it and

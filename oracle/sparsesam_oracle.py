@@ -66,6 +66,7 @@ __all__ = [
     "stripe_sort",
     "routed_count",
     "routed_tokens",
+    "routed_rank_order",
     "position_keep",
     "band_radius",
     "token_mask",
@@ -236,6 +237,16 @@ def routed_tokens(s: np.ndarray, token_map_row: np.ndarray, mlp_density: float) 
     picked = token_map_row[s[:k]]
     assert (picked >= 0).all()
     return np.sort(picked)
+
+
+def routed_rank_order(s: np.ndarray, token_map_row: np.ndarray, mlp_density: float) -> np.ndarray:
+    """The keep-set of one segment as image token ids in importance order (the first K
+    entries of the order itself, most important first). Same set as routed_tokens."""
+    n_real = int((token_map_row >= 0).sum())
+    k = routed_count(mlp_density, n_real)
+    picked = token_map_row[s[:k]]
+    assert (picked >= 0).all()
+    return picked
 
 
 # ----------------------------------------------------------------------------

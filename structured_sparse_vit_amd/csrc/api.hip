@@ -231,6 +231,7 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
   }
   // keep-set size per segment
   p->seg_k.resize(p->segs_per_img);
+  p->seg_off.resize(p->segs_per_img);
   p->routed_per_image = 0;
   for (int w = 0; w < p->segs_per_img; ++w) {
     int n_real = p->n;
@@ -243,6 +244,7 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     int k = (int)std::floor((double)d.mlp_density * (double)n_real + 0.5);
     k = std::max(1, std::min(k, n_real));
     p->seg_k[w] = k;
+    p->seg_off[w] = p->routed_per_image;
     p->routed_per_image += k;
   }
   if (permute_lds_bytes(*p) > 160 * 1024) {
@@ -267,7 +269,8 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
       return o;
     };
     size_t o_rp = put(p->row_ptr), o_ci = put(p->col_idx), o_ts = put(p->tile_start), o_tl = put(p->tile_len),
-           o_or = put(p->order), o_sk = put(p->seg_k), o_it = put(p->items), o_sp = put(p->splits);
+           o_or = put(p->order), o_sk = put(p->seg_k), o_so = put(p->seg_off), o_it = put(p->items),
+           o_sp = put(p->splits);
     blob.push_back(0);
     void* dptr = nullptr;
     hipError_t e = hipMalloc(&dptr, blob.size() * sizeof(int));
@@ -291,6 +294,7 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     p->d_tile_len = b + o_tl;
     p->d_order = b + o_or;
     p->d_seg_k = b + o_sk;
+    p->d_seg_off = b + o_so;
     p->d_items = b + o_it;
     p->d_splits = b + o_sp;
     p->attn_resident_wgs = attn_mfma64_supported(*p) ? attn_mfma64_resident_wgs(dev) : 0;

@@ -33,6 +33,7 @@ struct sparsesam_plan {
   std::vector<int> tile_start, tile_len;
   std::vector<int> order;             // query tiles, longest row first
   std::vector<int> seg_k;             // keep-set size of each segment of an image
+  std::vector<int> seg_off;           // exclusive prefix sum of seg_k (offset in the image's keep-set)
   // matrix-core attention work list: (query tile, first, end kept-key index, partial
   // slot or -1), longest first; rows longer than the chunk limit are split into items
   // that write partials, merged per (query tile, first slot, chunks) in `splits`
@@ -49,6 +50,7 @@ struct sparsesam_plan {
   const int* d_tile_len = nullptr;
   const int* d_order = nullptr;
   const int* d_seg_k = nullptr;
+  const int* d_seg_off = nullptr;
   const int* d_items = nullptr;
   const int* d_splits = nullptr;
 

@@ -51,43 +51,63 @@ __global__ void __launch_bounds__(1024) sobel_pool_kernel(const float* __restric
   }
 }
 
-// Strip kernel for patch 16: one 256-thread workgroup per 16 tokens of one token row
+// Strip kernel for patch 16: one 1024-thread workgroup per 16 tokens of one token row
 // (a 16 x 256-pixel strip). The strip and its one-pixel halo (18 x 258 floats) are
-// staged in LDS with coalesced loads; thread (token tl, pixel row r) computes the 16
-// magnitudes of its patch row and sums them left to right, then the 16 row sums of a
-// token are added top to bottom -- the same operations in the same order as above.
-constexpr int kStripW = 256, kHaloW = kStripW + 2;
+// staged in LDS with coalesced loads. Each thread then computes four neighbouring pixel
+// magnitudes from three 6-wide windows of the tile (16-byte LDS reads) into mag; 256
+// threads sum the patch rows left to right, and 16 threads the row sums top to bottom
+// -- the same operations in the same order as the per-token kernel above.
+constexpr int kStripW = 256, kHaloW = kStripW + 2, kTileLd = 260;  // tile rows 16-byte aligned
 
-__global__ void __launch_bounds__(256) sobel_pool_strip_kernel(const float* __restrict__ img, int height, int width,
-                                                               float* __restrict__ imp) {
+__global__ void __launch_bounds__(1024) sobel_pool_strip_kernel(const float* __restrict__ img, int height, int width,
+                                                                float* __restrict__ imp) {
 #pragma clang fp contract(off)
-  __shared__ float tile[18][kHaloW];
+  __shared__ __attribute__((aligned(16))) float tile[18][kTileLd];
+  __shared__ float mag[16][kStripW + 1];  // odd row stride: the row sums read 64 distinct banks
   __shared__ float rowsum[16][17];
   const int x0 = blockIdx.x * kStripW, ty = blockIdx.y, b = blockIdx.z;
   const int y0 = ty * 16;
   const float* P = img + (size_t)b * height * width;
-#pragma unroll
-  for (int i = threadIdx.x; i < 18 * kHaloW; i += 256) {
-    const int yy = y0 - 1 + i / kHaloW, xx = x0 - 1 + i % kHaloW;
-    tile[i / kHaloW][i % kHaloW] =
-        (yy >= 0 && yy < height && xx >= 0 && xx < width) ? P[(size_t)yy * width + xx] : 0.0f;
+  for (int i = threadIdx.x; i < 18 * kHaloW; i += 1024) {
+    const int rr = i / kHaloW, cc = i - (i / kHaloW) * kHaloW;
+    const int yy = y0 - 1 + rr, xx = x0 - 1 + cc;
+    tile[rr][cc] = (yy >= 0 && yy < height && xx >= 0 && xx < width) ? P[(size_t)yy * width + xx] : 0.0f;
   }
   __syncthreads();
-  const int tl = threadIdx.x >> 4, r = threadIdx.x & 15;
-  const float two = 2.0f;
-  float acc = 0.0f;
-  for (int c = 0; c < 16; ++c) {
-    const int y = r + 1, x = tl * 16 + c + 1;  // tile coordinates of the pixel
-    float gx = ((tile[y - 1][x + 1] + two * tile[y][x + 1]) + tile[y + 1][x + 1]) -
-               ((tile[y - 1][x - 1] + two * tile[y][x - 1]) + tile[y + 1][x - 1]);
-    float gy = ((tile[y + 1][x - 1] + two * tile[y + 1][x]) + tile[y + 1][x + 1]) -
-               ((tile[y - 1][x - 1] + two * tile[y - 1][x]) + tile[y - 1][x + 1]);
-    float sq = gx * gx;
-    float sq2 = gy * gy;
-    sq = sq + sq2;
-    acc = acc + __builtin_sqrtf(sq);
+  {
+    // pixels (r, 4q + i), i < 4: tile rows r .. r + 2, tile columns 4q + i .. 4q + i + 2
+    const int r = threadIdx.x >> 6, q = threadIdx.x & 63;
+    float w[3][6];
+#pragma unroll
+    for (int dy = 0; dy < 3; ++dy) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&tile[r + dy][4 * q]);
+      const float b0 = tile[r + dy][4 * q + 4], b1 = tile[r + dy][4 * q + 5];
+      w[dy][0] = a[0];
+      w[dy][1] = a[1];
+      w[dy][2] = a[2];
+      w[dy][3] = a[3];
+      w[dy][4] = b0;
+      w[dy][5] = b1;
+    }
+    const float two = 2.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float gx = ((w[0][i + 2] + two * w[1][i + 2]) + w[2][i + 2]) - ((w[0][i] + two * w[1][i]) + w[2][i]);
+      float gy = ((w[2][i] + two * w[2][i + 1]) + w[2][i + 2]) - ((w[0][i] + two * w[0][i + 1]) + w[0][i + 2]);
+      float sq = gx * gx;
+      float sq2 = gy * gy;
+      sq = sq + sq2;
+      mag[r][4 * q + i] = __builtin_sqrtf(sq);
+    }
   }
-  rowsum[tl][r] = acc;
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int tl = threadIdx.x >> 4, r = threadIdx.x & 15;
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc = acc + mag[r][tl * 16 + c];
+    rowsum[tl][r] = acc;
+  }
   __syncthreads();
   if (threadIdx.x < 16) {
     float tot = 0.0f;
@@ -101,7 +121,7 @@ hipError_t launch_importance(const float* img, int batch, int height, int width,
                              hipStream_t st) {
   if (patch == 16 && width % kStripW == 0) {
     dim3 grid(width / kStripW, height / 16, batch);
-    hipLaunchKernelGGL(sobel_pool_strip_kernel, grid, dim3(256), 0, st, img, height, width, imp);
+    hipLaunchKernelGGL(sobel_pool_strip_kernel, grid, dim3(1024), 0, st, img, height, width, imp);
     return hipGetLastError();
   }
   dim3 grid(width / patch, height / patch, batch);

@@ -4,22 +4,21 @@
 // stripe-sort bullet: tokens are sorted by importance, the sorted list is viewed as
 // a matrix and transposed before flattening, which spreads the important tokens over
 // the whole sequence. Part 2 (Residual-Consistency MLP), token routing bullet: the
-// keep-set follows the same deterministic order.
+// keep-set is the top of the same deterministic order.
 //
 // The order is total: importance descending (-0.0 == +0.0, NaN after every number,
 // pad slots after every real slot), then slot ascending. A slot's rank is therefore
-// the number of slots that precede it, and its stripe-sorted position follows from
-// the rank alone: rank rho sits at stripe rho % g, offset rho / g, i.e. position
-// (rho % g) * S + rho / g. No sorted list is ever materialised.
+// the number of slots that precede it, and everything follows from the rank alone:
+// rank rho sits at stripe rho % g, offset rho / g, i.e. position (rho % g) * S + rho / g,
+// and the slot is in the keep-set iff rho < K, at index rho of the segment's part of
+// the keep-set list. No sorted list is ever materialised.
 //
-//  * rank_kernel: one workgroup per (segment, chunk of slots). Its lanes count, for
-//    the chunk's slots, the preceding slots within shares of the segment's keys (held
-//    in LDS as 32-bit order keys); the shares are summed in LDS and one lane per slot
-//    writes perm and inv. The split is chosen so a single image's 4096 slots still
-//    spread over 256 workgroups.
-//  * keepset_kernel: one workgroup per image reads each real token's rank back from
-//    inv, flags the K first of its segment, and compacts the flags in raster order
-//    (block-wide scan), which gives the keep-set ascending.
+// rank_kernel: one workgroup per (segment, chunk of slots). Its lanes count, for the
+// chunk's slots, the preceding slots within shares of the segment's keys (held in LDS
+// as 32-bit order keys); lanes of one slot fold their counts with shuffles, the
+// wavefronts' shares are summed in LDS, and one lane per slot writes perm, inv and --
+// when the rank is below K -- the keep-set entry. The split is chosen so a single
+// image's 4096 slots still spread over 256 workgroups.
 #include <algorithm>
 
 #include "internal.hpp"
@@ -44,14 +43,17 @@ constexpr int kMaxRankWaves = 16;
 
 __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* __restrict__ imp, SegmentMap map,
                                                                   int n, int stripes, int chunks, int tpw,
-                                                                  int* __restrict__ perm, int* __restrict__ inv) {
+                                                                  const int* __restrict__ seg_k,
+                                                                  const int* __restrict__ seg_off,
+                                                                  int routed_per_image, int* __restrict__ perm,
+                                                                  int* __restrict__ inv, int* __restrict__ routed) {
   extern __shared__ uint32_t key_lds[];  // keys of the segment, padded to a multiple of 64
   __shared__ int part[kMaxRankWaves * 64];
   const int seg = blockIdx.x / chunks, chunk = blockIdx.x - (blockIdx.x / chunks) * chunks;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kw = blockDim.x >> 6;
   const int tokens = map.grid_h * map.grid_w;
-  const int img = seg / map.segs_per_img;
+  const int img = map.f_spi.div(seg);
   const float* im = imp + (size_t)img * tokens;
   const int n64 = (n + 63) & ~63;
   // keys past n are pad keys with index >= n: they never precede a real slot
@@ -81,74 +83,29 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
       cnt += (kk[u] < mine) | ((kk[u] == mine) & (jj < slot));
     }
   }
-  part[wave * 64 + lane] = cnt;
+  // the 64 / tpw lanes of one slot are tpw apart: fold them
+  for (int o = tpw; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
+  if (lane < tpw) part[wave * 64 + lane] = cnt;
   __syncthreads();
   if (tid < tpw) {
     const int sl = chunk * tpw + tid;
     if (sl < n) {
       int rank = 0;
-      for (int w = 0; w < kw; ++w)
-        for (int u = 0; u < subs; ++u) rank += part[w * 64 + u * tpw + tid];
+#pragma unroll 4
+      for (int w = 0; w < kw; ++w) rank += part[w * 64 + tid];
       const int S = n / stripes;
       const int p = (rank % stripes) * S + rank / stripes;
       const size_t base = (size_t)seg * n;
       perm[base + p] = sl;
       inv[base + sl] = p;
+      const int w_img = seg - img * map.segs_per_img;
+      if (rank < seg_k[w_img])  // K <= real slots, so never a pad
+        routed[(size_t)img * routed_per_image + seg_off[w_img] + rank] = map.row_of(seg, sl);
     }
   }
 }
 
-__global__ void __launch_bounds__(1024) keepset_kernel(const int* __restrict__ inv, SegmentMap map, int segs, int n,
-                                                       int stripes, const int* __restrict__ seg_k,
-                                                       int routed_per_image, int* __restrict__ routed) {
-  extern __shared__ unsigned char flag[];
-  __shared__ int wave_tot[16];
-  const int img = blockIdx.x;
-  const int tid = threadIdx.x, nth = blockDim.x;
-  const int tokens = map.grid_h * map.grid_w;
-  const int S = n / stripes;
-  for (int t = tid; t < tokens; t += nth) flag[t] = 0;
-  __syncthreads();
-#pragma unroll 4
-  for (int i = tid; i < segs * n; i += nth) {
-    const int sg = i / n, s = i - sg * n;
-    const int row = map.row_of(img * segs + sg, s) - img * tokens;
-    if (row < 0 || row >= tokens) continue;  // pad slot
-    const int p = inv[((size_t)img * segs + sg) * n + s];
-    const int rank = stripes * (p % S) + p / S;
-    if (rank < seg_k[sg]) flag[row] = 1;
-  }
-  __syncthreads();
-  // compact the flags in raster order (block-wide exclusive scan)
-  const int per = (tokens + nth - 1) / nth;
-  const int t0 = tid * per;
-  int cnt = 0;
-  for (int t = t0; t < t0 + per && t < tokens; ++t) cnt += flag[t];
-  const int lane = tid & 63, wv = tid >> 6;
-  int incl = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) wave_tot[wv] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wv; ++w) before += wave_tot[w];
-  int pos = before + incl - cnt;
-  int* out = routed + (size_t)img * routed_per_image;
-  for (int t = t0; t < t0 + per && t < tokens; ++t) {
-    if (flag[t]) {
-      if (pos < routed_per_image) out[pos] = img * tokens + t;
-      ++pos;
-    }
-  }
-}
-
-size_t permute_lds_bytes(const sparsesam_plan& p) {
-  const size_t tokens = (size_t)p.desc.grid_h * p.desc.grid_w;
-  return std::max((size_t)((p.n + 63) & ~63) * 4, tokens);
-}
+size_t permute_lds_bytes(const sparsesam_plan& p) { return (size_t)((p.n + 63) & ~63) * 4; }
 
 hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
                           hipStream_t st) {
@@ -158,19 +115,12 @@ hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, 
   const int kw = std::max(1, std::min(kMaxRankWaves, (p.n + 255) / 256));
   const int chunks = (p.n + tpw - 1) / tpw;
   const int segs = batch * p.segs_per_img;
-  const size_t key_bytes = (size_t)((p.n + 63) & ~63) * 4;
+  const size_t key_bytes = permute_lds_bytes(p);
   hipError_t e = hipFuncSetAttribute((const void*)rank_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)key_bytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(rank_kernel, dim3((unsigned)(segs * chunks)), dim3(64 * kw), key_bytes, st, imp, p.segmap(),
-                     p.n, p.desc.stripes, chunks, tpw, perm, inv);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t flag_bytes = (size_t)p.desc.grid_h * p.desc.grid_w;
-  e = hipFuncSetAttribute((const void*)keepset_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)flag_bytes);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(keepset_kernel, dim3(batch), dim3(1024), flag_bytes, st, inv, p.segmap(), p.segs_per_img, p.n,
-                     p.desc.stripes, p.d_seg_k, p.routed_per_image, routed);
+                     p.n, p.desc.stripes, chunks, tpw, p.d_seg_k, p.d_seg_off, p.routed_per_image, perm, inv, routed);
   return hipGetLastError();
 }
 

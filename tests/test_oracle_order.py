@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
 
-from oracle import (descending_order, routed_count, routed_tokens, segment_importance,
+from oracle import (descending_order, routed_count, routed_rank_order, routed_tokens, segment_importance,
                     stripe_sort, window_token_map)
 from tests.conftest import GOLDEN
 
@@ -70,6 +70,8 @@ def test_stripe_sort_hand_worked_4x4():
     tmap = np.arange(16)
     assert routed_count(g["mlp_density"], 16) == g["routed_k"]
     assert routed_tokens(s, tmap, g["mlp_density"]).tolist() == g["routed"]
+    # in rank order the keep-set is the head of the hand-worked order itself
+    assert routed_rank_order(s, tmap, g["mlp_density"]).tolist() == g["sorted"][:g["routed_k"]]
     # keep-set positions in the stripe-sorted sequence: one contiguous run per stripe
     pos = sorted(inv[g["routed"]].tolist())
     runs = [list(range(a, b)) for a, b in g["routed_positions_per_stripe"]]
@@ -146,3 +148,7 @@ def test_window_pads_never_routed_and_sort_last():
     assert np.all(np.diff(s[n_real:]) > 0)
     r = routed_tokens(s, tm[24], 0.4)
     assert len(r) == 26 and np.all(r >= 0)
+    rr = routed_rank_order(s, tm[24], 0.4)
+    assert sorted(rr.tolist()) == r.tolist()
+    assert np.all(np.diff(imp[rr]) <= 0)  # most important first
+    assert imp[rr[0]] == imp[tm[24][tm[24] >= 0]].max()
