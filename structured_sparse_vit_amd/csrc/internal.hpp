@@ -10,7 +10,7 @@
 #include "common.hpp"
 
 // Longest key-tile list of one matrix-core attention work item; longer rows are split.
-constexpr int kAttnItemTiles = 32;
+constexpr int kAttnItemTiles = 64;
 
 struct sparsesam_plan {
   sparsesam_plan_desc desc;

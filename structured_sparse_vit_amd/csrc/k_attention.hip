@@ -132,25 +132,36 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
                                        (__attribute__((address_space(3))) void*)(dst + (qh + 2 * i) * 1024), 16, 0,
                                        0);
   };
-  // S^T = K Q^T for the K tile in slot s: two 32-key blocks
-  auto scores = [&](int s, f32x16 (&sc)[2]) {
+  // fragments of the K tile in slot s (A operand of S^T = K Q^T: two 32-key blocks) and
+  // of the V^T tile in slot s (A operand of O^T = V^T P^T: two 32-channel blocks)
+  auto read_k = [&](int s, bf16x8 (&kf)[4][2]) {
     const char* Ks = ring + s * kTileBytes;
-    bf16x8 kf[2][4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        kf[mb][ks] = *reinterpret_cast<const bf16x8*>(Ks + swz(mb * 32 + (lane & 31), ks * 2 + (lane >> 5)));
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sc[mb][e] = 0.0f;
-    // the two accumulation chains alternate, so each MFMA depends on the one two back
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
-        sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mb][ks], qf[ks], sc[mb], 0, 0, 0);
+        kf[ks][mb] = *reinterpret_cast<const bf16x8*>(Ks + swz(mb * 32 + (lane & 31), ks * 2 + (lane >> 5)));
+  };
+  auto read_v = [&](int s, bf16x8 (&vf)[4][2]) {
+    const char* Vs = ring + (2 + s) * kTileBytes;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int md = 0; md < 2; ++md)
+        vf[kk][md] = *reinterpret_cast<const bf16x8*>(Vs + swz(md * 32 + (lane & 31), kk * 2 + (lane >> 5)));
+  };
+  // S^T = K Q^T; the two accumulation chains alternate, so each MFMA depends on the one
+  // two back
+  auto scores = [&](const bf16x8 (&kf)[4][2], f32x16 (&sc)[2]) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[mb][e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][mb], qf[ks], sc[mb], 0, 0, 0);
   };
 
   f32x16 oacc[2];
@@ -161,8 +172,8 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   float m_run = -INFINITY, l_run = 0.0f;
 
   // online softmax of S_j (this lane's query: 32 of the tile's 64 scores, the rest in
-  // lane ^ 32), then O^T += V^T P^T with V^T from slot s
-  auto softmax_pv = [&](const f32x16 (&sc)[2], int s) {
+  // lane ^ 32) into the P^T operand
+  auto softmax = [&](const f32x16 (&sc)[2], bf16x8 (&pf)[4]) {
     float mx = sc[0][0];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -186,7 +197,6 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
     // 8 hf + 0..7 (the V^T tile is in natural key order). Swapping the middle pairs of
     // bf16 pairs between lane halves puts them there.
     float psum0 = 0.0f, psum1 = 0.0f;
-    bf16x8 pf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 v;
@@ -206,18 +216,14 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
       pf[kk] = __builtin_bit_cast(bf16x8, r);
     }
     l_run += psum0 + psum1;
-    const char* Vs = ring + (2 + s) * kTileBytes;
-    bf16x8 vf[2][4];
-#pragma unroll
-    for (int md = 0; md < 2; ++md)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        vf[md][kk] = *reinterpret_cast<const bf16x8*>(Vs + swz(md * 32 + (lane & 31), kk * 2 + (lane >> 5)));
+  };
+  // O^T += V^T P^T over four 16-key steps
+  auto pv = [&](const bf16x8 (&vf)[4][2], const bf16x8 (&pf)[4]) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int md = 0; md < 2; ++md)
-        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[md][kk], pf[kk], oacc[md], 0, 0, 0);
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk][md], pf[kk], oacc[md], 0, 0, 0);
   };
 
   const int nj = (total - kp + 1) >> 1;   // tiles of this parity
@@ -230,22 +236,31 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   if (nj > 1) issue_k(1, 1);
   if (nj > 0) {
     issue_v(0, 0);
-    scores(0, s0);
+    bf16x8 kf[4][2];
+    read_k(0, kf);
+    scores(kf, s0);
   }
   // step j < nj: S_j is in (j even ? s0 : s1); V_j and K_{j+1} were issued in step
-  // j - 1. S_{j+1} and the softmax of S_j share one block so their MFMA and VALU work
-  // can interleave.
+  // j - 1. All fragment reads of the step are issued first; S_{j+1} and the softmax of
+  // S_j share one block so their MFMA and VALU work can interleave.
   auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (j + 2 < nj) issue_k(j + 2, j & 1);
+    bf16x8 vf[4][2], pf[4];
     if (j + 1 < nj) {
       issue_v(j + 1, (j + 1) & 1);
-      scores((j + 1) & 1, nxt);
-      softmax_pv(cur, j & 1);
+      bf16x8 kf[4][2];
+      read_k((j + 1) & 1, kf);
+      read_v(j & 1, vf);
+      scores(kf, nxt);
+      softmax(cur, pf);
+      pv(vf, pf);
     } else {
-      softmax_pv(cur, j & 1);
+      read_v(j & 1, vf);
+      softmax(cur, pf);
+      pv(vf, pf);
     }
   };
   for (int j = 0; j < nj; j += 2) {
