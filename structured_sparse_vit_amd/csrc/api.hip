@@ -1,5 +1,6 @@
 // C ABI of libsparsesam: plans, validation and the five hot-path entry points.
 #include <algorithm>
+#include <map>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -205,27 +206,57 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
   std::stable_sort(p->order.begin(), p->order.end(), [&](int a, int b) {
     return (p->row_ptr[a + 1] - p->row_ptr[a]) > (p->row_ptr[b + 1] - p->row_ptr[b]);
   });
-  // matrix-core attention work list: rows of more than kChunk key tiles are split
+  // Matrix-core attention work list. Query tiles with identical kept-key lists form
+  // groups of at most four (one item each, G members, P = 4 / G key parities; G = 3
+  // runs one parity); lists longer than kAttnItemTiles are split into single-tile items
+  // with partial slots, merged per (query tile, first slot, chunks) in `splits`. Items
+  // are ordered by steps (list length / P), longest first. Record: {kb, ke, slot, G |
+  // P << 4}, {members' query tiles, -1 padded}.
   {
     const int kChunk = kAttnItemTiles;
-    struct Item { int qt, kb, ke, slot; };
+    struct Item { int kb, ke, slot, g, pq; int qt[4]; };
     std::vector<Item> v;
     p->splits.clear();
     p->n_slots = 0;
+    std::map<std::vector<int>, std::vector<int>> by_list;
+    std::vector<std::vector<int>> lists;  // first-appearance order
     for (int qt = 0; qt < p->tiles; ++qt) {
-      const int rb = p->row_ptr[qt], len = p->row_ptr[qt + 1] - rb;
-      const int nch = (len + kChunk - 1) / kChunk;
-      if (nch <= 1) {
-        v.push_back({qt, rb, rb + len, -1});
+      std::vector<int> key(p->col_idx.begin() + p->row_ptr[qt], p->col_idx.begin() + p->row_ptr[qt + 1]);
+      auto f = by_list.find(key);
+      if (f == by_list.end()) {
+        lists.push_back(key);
+        by_list[key] = {qt};
+      } else {
+        f->second.push_back(qt);
+      }
+    }
+    for (const std::vector<int>& key : lists) {
+      const std::vector<int>& members = by_list[key];
+      const int rb = p->row_ptr[members[0]], len = (int)key.size();
+      if (len > kChunk) {
+        for (int qt : members) {
+          const int rq = p->row_ptr[qt];
+          const int nch = (len + kChunk - 1) / kChunk;
+          p->splits.insert(p->splits.end(), {qt, p->n_slots, nch});
+          for (int c = 0; c < nch; ++c)
+            v.push_back({rq + (int)((long long)c * len / nch), rq + (int)((long long)(c + 1) * len / nch),
+                         p->n_slots++, 1, 4, {qt, -1, -1, -1}});
+        }
         continue;
       }
-      p->splits.insert(p->splits.end(), {qt, p->n_slots, nch});
-      for (int c = 0; c < nch; ++c)
-        v.push_back({qt, rb + (int)((long long)c * len / nch), rb + (int)((long long)(c + 1) * len / nch), p->n_slots++});
+      for (size_t m0 = 0; m0 < members.size(); m0 += 4) {
+        const int g = (int)std::min<size_t>(4, members.size() - m0);
+        Item it{rb, rb + len, -1, g, g == 1 ? 4 : g == 2 ? 2 : 1, {-1, -1, -1, -1}};
+        for (int i = 0; i < g; ++i) it.qt[i] = members[m0 + i];
+        v.push_back(it);
+      }
     }
-    std::stable_sort(v.begin(), v.end(), [](const Item& a, const Item& b) { return a.ke - a.kb > b.ke - b.kb; });
+    auto steps = [](const Item& it) { return (it.ke - it.kb + it.pq - 1) / it.pq; };
+    std::stable_sort(v.begin(), v.end(), [&](const Item& a, const Item& b) { return steps(a) > steps(b); });
     p->items.clear();
-    for (const Item& it : v) p->items.insert(p->items.end(), {it.qt, it.kb, it.ke, it.slot});
+    for (const Item& it : v)
+      p->items.insert(p->items.end(), {it.kb, it.ke, it.slot, it.g | (it.pq << 4), it.qt[0], it.qt[1], it.qt[2],
+                                       it.qt[3]});
     p->n_items = (int)v.size();
     p->n_split_rows = (int)p->splits.size() / 3;
   }

@@ -34,9 +34,11 @@ struct sparsesam_plan {
   std::vector<int> order;             // query tiles, longest row first
   std::vector<int> seg_k;             // keep-set size of each segment of an image
   std::vector<int> seg_off;           // exclusive prefix sum of seg_k (offset in the image's keep-set)
-  // matrix-core attention work list: (query tile, first, end kept-key index, partial
-  // slot or -1), longest first; rows longer than the chunk limit are split into items
-  // that write partials, merged per (query tile, first slot, chunks) in `splits`
+  // matrix-core attention work list, two int4 per item: {first, end kept-key index,
+  // partial slot or -1, G | P << 4}, {query tiles of the G members}; members share one
+  // kept-key list. Longest first; lists longer than the chunk limit are split into
+  // single-tile items that write partials, merged per (query tile, first slot, chunks)
+  // in `splits`
   std::vector<int> items, splits;
   int n_items = 0, n_split_rows = 0, n_slots = 0;
   int attn_resident_wgs = 0;          // workgroups of the attention kernel resident at once

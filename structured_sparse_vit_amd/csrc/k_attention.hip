@@ -36,7 +36,8 @@ namespace sparsesam {
 constexpr int kTile = 64;
 constexpr int kTileBytes = kTile * 128;          // one swizzled 64 x 64 bf16 tile
 constexpr int kParityBytes = 4 * kTileBytes;     // K ring (2 slots) + V^T ring (2 slots)
-constexpr int kAttnLds = 2 * kParityBytes;       // two key parities: 64 KiB
+constexpr int kAttnWaves = 8;                    // wavefronts per workgroup: 4 x (two query halves)
+constexpr int kAttnLds = 4 * kParityBytes;       // up to four key parities: 128 KiB
 constexpr int kPartLd = 68;                      // partial record: O[64], m, l, pad (floats)
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -54,18 +55,25 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 
-// One work item: query tile qt against the kept key tiles col_idx[kb..ke), at most
-// kAttnItemTiles (<= 64) of them. Rows whose list is longer are split over several
-// items; those write an unnormalised partial (O, running max, running sum) to
-// `partial` at `slot` and a combine pass merges them. One unit of work is one item for
-// one segment-head sh.
+// One work item: a group of G <= 4 query tiles whose kept key-tile lists are identical
+// (the 4 x 4 mosaic repeats one band in every sub-map, so the same tile index in each
+// stripe has the same list), against the kept key tiles col_idx[kb..ke) of that list,
+// at most kAttnItemTiles (<= 64) of them. The eight wavefronts are G tiles x two query
+// halves x P = 4 / G key parities (G = 3: P = 1, one pair idle but loading): parity p
+// walks list entries p, p + P, ...; the parities merge through LDS at the end. Every K
+// and V^T tile is loaded into LDS once for the whole group. Longer lists (none at
+// ViT sizes) are split over G = 1 items that write an unnormalised partial (O,
+// running max, running sum) to `partial` at `slot` for a combine pass.
 //
-// Pipeline of a wavefront (query half qh, key parity kp; its j-th tile is item tile
-// 2 j + kp): K tiles run one step ahead of V^T tiles. In step j the wavefront issues
-// the direct-to-LDS loads of K_{j+2} and V_{j+1}, starts S_{j+1} = K_{j+1} Q^T on the
-// matrix cores, and meanwhile runs the softmax of S_j and O^T += V_j^T P_j^T. Each ring
-// (K, V^T) has two slots per parity; one barrier per step both publishes the loads of
-// the previous step and retires the slots they overwrite.
+// Item record (two int4): {kb, ke, slot or -1, G | P << 4}, {query tile of each member}.
+//
+// Pipeline of a wavefront (its j-th tile is list entry p + P j): K tiles run one step
+// ahead of V^T tiles. In step j the workgroup issues the direct-to-LDS loads of
+// K_{j+2} and V_{j+1} of every parity (wavefront w loads row group w of each tile), and
+// each wavefront starts S_{j+1} = K_{j+1} Q^T on the matrix cores while it runs the
+// softmax of S_j and O^T += V_j^T P_j^T. Each parity has a two-slot ring for K and for
+// V^T; one barrier per step both publishes the loads of the previous step and retires
+// the slots they overwrite.
 static_assert(kAttnItemTiles <= 64, "one key tile per lane");
 __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                                  const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
@@ -74,16 +82,21 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
                                                  int seg_heads, float c_log2, float* __restrict__ partial, int item,
                                                  int sh, char* smem) {
   constexpr int D = 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qh = wave & 1;   // query half of the tile
-  const int kp = wave >> 1;  // key-tile parity this wavefront pair walks
-  const int4 it = items[item];
-  const int qt = it.x, kb = it.y, ke = it.z, slot = it.w;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int4 it0 = items[2 * item], it1 = items[2 * item + 1];
+  const int kb = __builtin_amdgcn_readfirstlane(it0.x), ke = __builtin_amdgcn_readfirstlane(it0.y);
+  const int slot = __builtin_amdgcn_readfirstlane(it0.z), gp = __builtin_amdgcn_readfirstlane(it0.w);
+  const int G = gp & 15, P = gp >> 4;
+  const int qh = wave & 1, pr = wave >> 1;  // query half; wavefront pair 0..3
+  const int gi = pr % G, kp = pr / G;       // member of the group; key parity
+  const bool active = kp < P;               // false only for the spare pair of a G = 3 group
+  const int qt = gi == 0 ? it1.x : gi == 1 ? it1.y : gi == 2 ? it1.z : it1.w;
   const int seg = sh / heads, h = sh - seg * heads;
   const bf16_t* q_base = Q + (size_t)sh * n * D;
   const bf16_t* k_base = Kt + (size_t)sh * n * D;
   const bf16_t* v_base = VT + (size_t)sh * D * n_pad;
-  char* ring = smem + kp * kParityBytes;
+  char* ring = smem + (active ? kp : 0) * kParityBytes;
 
   const int q_local = qh * 32 + (lane & 31);
   const int my_q = tile_start[qt] + q_local;
@@ -101,36 +114,30 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   // with them for the tile loads issued after them.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // Direct-to-LDS tile loads: the pair's two wavefronts fill the 8 row groups of a tile
-  // (wavefront qh takes groups qh, qh + 2, qh + 4, qh + 6); lane L fetches the chunk
-  // that the swizzle places at byte 16 L of its group.
-  int k_src[4], v_src[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int g = qh + 2 * i;
-    const int row = 8 * g + (lane >> 3), c = (lane & 7) ^ swz_key(8 * g + (lane >> 3));
-    k_src[i] = row * D + c * 8;
-    v_src[i] = row * n_pad + c * 8;
-  }
-  auto issue_k = [&](int j, int s) {  // K tile of step j into K slot s
-    const int k0 = __builtin_amdgcn_readlane(koff, 2 * j + kp);
-    const bf16_t* src = k_base + (size_t)k0 * D;
-    char* dst = ring + s * kTileBytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src + k_src[i]),
-                                       (__attribute__((address_space(3))) void*)(dst + (qh + 2 * i) * 1024), 16, 0,
-                                       0);
+  // Direct-to-LDS tile loads: wavefront w fills row group w (rows 8 w .. 8 w + 7) of
+  // every tile; lane L fetches the chunk that the swizzle places at byte 16 L.
+  const int krow = 8 * wave + (lane >> 3), kch = (lane & 7) ^ swz_key(8 * wave + (lane >> 3));
+  const int k_src = krow * D + kch * 8, v_src = krow * n_pad + kch * 8;
+  auto issue_k = [&](int j, int s) {  // K tiles of step j (every parity) into K slot s
+    for (int p = 0; p < P; ++p) {
+      const int t = p + P * j;
+      if (t >= total) break;
+      const int k0 = __builtin_amdgcn_readlane(koff, t);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(k_base + (size_t)k0 * D + k_src),
+          (__attribute__((address_space(3))) void*)(smem + p * kParityBytes + s * kTileBytes + wave * 1024), 16, 0, 0);
+    }
   };
-  auto issue_v = [&](int j, int s) {  // V^T tile of step j into V slot s
-    const int k0 = __builtin_amdgcn_readlane(koff, 2 * j + kp);
-    const bf16_t* src = v_base + k0;
-    char* dst = ring + (2 + s) * kTileBytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src + v_src[i]),
-                                       (__attribute__((address_space(3))) void*)(dst + (qh + 2 * i) * 1024), 16, 0,
-                                       0);
+  auto issue_v = [&](int j, int s) {  // V^T tiles of step j (every parity) into V slot s
+    for (int p = 0; p < P; ++p) {
+      const int t = p + P * j;
+      if (t >= total) break;
+      const int k0 = __builtin_amdgcn_readlane(koff, t);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(v_base + k0 + v_src),
+          (__attribute__((address_space(3))) void*)(smem + p * kParityBytes + (2 + s) * kTileBytes + wave * 1024), 16,
+          0, 0);
+    }
   };
   // fragments of the K tile in slot s (A operand of S^T = K Q^T: two 32-key blocks) and
   // of the V^T tile in slot s (A operand of O^T = V^T P^T: two 32-channel blocks)
@@ -226,59 +233,57 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
         oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk][md], pf[kk], oacc[md], 0, 0, 0);
   };
 
-  const int nj = (total - kp + 1) >> 1;   // tiles of this parity
-  const int niter = (total + 1) >> 1;     // steps (the same for both parities)
+  const int nj = active ? (total - kp + P - 1) / P : 0;  // tiles of this wavefront's parity
+  const int niter = (total + P - 1) / P;                  // steps (parity 0 has the most)
   f32x16 s0[2], s1[2];
-  if (nj > 0) issue_k(0, 0);
+  issue_k(0, 0);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  if (nj > 1) issue_k(1, 1);
+  issue_k(1, 1);
+  issue_v(0, 0);
   if (nj > 0) {
-    issue_v(0, 0);
     bf16x8 kf[4][2];
     read_k(0, kf);
     scores(kf, s0);
   }
-  // step j < nj: S_j is in (j even ? s0 : s1); V_j and K_{j+1} were issued in step
-  // j - 1. All fragment reads of the step are issued first; S_{j+1} and the softmax of
-  // S_j share one block so their MFMA and VALU work can interleave.
+  // step j: S_j is in (j even ? s0 : s1); V_j and K_{j+1} were issued in step j - 1.
+  // All fragment reads of the step are issued first; S_{j+1} and the softmax of S_j
+  // share one block so their MFMA and VALU work can interleave. Every wavefront takes
+  // every step's barrier; it computes while j < nj.
   auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (j + 2 < nj) issue_k(j + 2, j & 1);
+    issue_k(j + 2, j & 1);
+    issue_v(j + 1, (j + 1) & 1);
     bf16x8 vf[4][2], pf[4];
     if (j + 1 < nj) {
-      issue_v(j + 1, (j + 1) & 1);
       bf16x8 kf[4][2];
       read_k((j + 1) & 1, kf);
       read_v(j & 1, vf);
       scores(kf, nxt);
       softmax(cur, pf);
       pv(vf, pf);
-    } else {
+    } else if (j < nj) {
       read_v(j & 1, vf);
       softmax(cur, pf);
       pv(vf, pf);
     }
   };
-  for (int j = 0; j < nj; j += 2) {
+  for (int j = 0; j < niter; j += 2) {
     step(j, s0, s1);
-    if (j + 1 < nj) step(j + 1, s1, s0);
-  }
-  if (nj < niter) {  // the odd pair of an odd-length item: one step fewer, same barriers
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    if (j + 1 < niter) step(j + 1, s1, s0);
   }
   // every wavefront is done with the rings before the exchange area reuses them
   __syncthreads();
 
-  // merge the odd-parity pair into the even one through LDS (same lane -> same queries)
-  float* xch = reinterpret_cast<float*>(smem) + (size_t)qh * 64 * 34;
-  if (kp == 1) {
-    float* r = xch + lane * 34;
+  // merge parities 1 .. P-1 into parity 0 through LDS, in parity order (same lane ->
+  // same queries); exchange record: [parity - 1][member][query half][lane][m, l, O[32]]
+  float* xch = reinterpret_cast<float*>(smem);
+  auto rec_of = [&](int p) { return xch + ((((size_t)(p - 1) * G + gi) * 2 + qh) * 64 + lane) * 34; };
+  if (active && kp > 0) {
+    float* r = rec_of(kp);
     r[0] = m_run;
     r[1] = l_run;
 #pragma unroll
@@ -287,9 +292,9 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
       for (int e = 0; e < 16; ++e) r[2 + md * 16 + e] = oacc[md][e];
   }
   __syncthreads();
-  if (kp == 1) return;  // the odd pair's part of this unit is done
-  {
-    const float* r = xch + lane * 34;
+  if (!active || kp > 0) return;  // this wavefront's part of the unit is done
+  for (int p = 1; p < P; ++p) {
+    const float* r = rec_of(p);
     const float m1 = r[0], l1 = r[1];
     const float mm = fmaxf(m_run, m1);
     const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
@@ -336,7 +341,7 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
 // where units are (item, segment-head) pairs, items longest first. Long units land on
 // every workgroup in the first round and the shortest ones fill in after the shortest
 // first-round units, which evens out the work per workgroup without any atomics.
-__global__ void __launch_bounds__(256) attn_mfma64_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
+__global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma64_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                                           const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
                                                           const int4* __restrict__ items,
                                                           const int* __restrict__ col_idx,
@@ -440,7 +445,8 @@ int attn_mfma64_resident_wgs(int device) {
   if (hipFuncSetAttribute((const void*)attn_mfma64_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds) !=
       hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_mfma64_kernel, 256, kAttnLds) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_mfma64_kernel, 64 * kAttnWaves,
+                                                   kAttnLds) !=
       hipSuccess)
     return 0;
   return cus * per_cu;
@@ -478,7 +484,7 @@ hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, c
       if (e != hipSuccess) return e;
       const int units = p.n_items * seg_heads;
       dim3 grid((unsigned)std::min(units, std::max(1, p.attn_resident_wgs)));
-      hipLaunchKernelGGL(attn_mfma64_kernel, grid, dim3(256), kAttnLds, st, q, k, vt, o,
+      hipLaunchKernelGGL(attn_mfma64_kernel, grid, dim3(64 * kAttnWaves), kAttnLds, st, q, k, vt, o,
                          reinterpret_cast<const int4*>(p.d_items), p.d_col_idx, p.d_tile_start, p.n, p.n_pad,
                          p.desc.heads, seg_heads, p.n_items, c_log2, static_cast<float*>(partial));
       e = hipGetLastError();
