@@ -260,6 +260,31 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     p->n_items = (int)v.size();
     p->n_split_rows = (int)p->splits.size() / 3;
   }
+  // short-segment attention tables (n <= 256)
+  p->pos_tile.clear();
+  p->keep32.clear();
+  p->any32.clear();
+  p->nt32 = 0;
+  if (p->n <= kShortMaxN) {
+    const int nt32 = (p->n + 31) / 32;
+    p->nt32 = nt32;
+    p->pos_tile.assign(p->n, 0);
+    for (int t = 0; t < p->tiles; ++t)
+      for (int i = 0; i < p->tile_len[t]; ++i) p->pos_tile[p->tile_start[t] + i] = t;
+    p->keep32.assign((size_t)p->tiles * nt32, 0);
+    for (int t = 0; t < p->tiles; ++t)
+      for (int c = p->row_ptr[t]; c < p->row_ptr[t + 1]; ++c) {
+        const int t2 = p->col_idx[c];
+        for (int i = 0; i < p->tile_len[t2]; ++i) {
+          const int k = p->tile_start[t2] + i;
+          p->keep32[(size_t)t * nt32 + k / 32] |= (int)(1u << (k % 32));
+        }
+      }
+    p->any32.assign(nt32, 0);
+    for (int q = 0; q < p->n; ++q)
+      for (int kt = 0; kt < nt32; ++kt)
+        if (p->keep32[(size_t)p->pos_tile[q] * nt32 + kt] != 0) p->any32[q / 32] |= 1 << kt;
+  }
   // keep-set size per segment
   p->seg_k.resize(p->segs_per_img);
   p->seg_off.resize(p->segs_per_img);
@@ -301,7 +326,7 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     };
     size_t o_rp = put(p->row_ptr), o_ci = put(p->col_idx), o_ts = put(p->tile_start), o_tl = put(p->tile_len),
            o_or = put(p->order), o_sk = put(p->seg_k), o_so = put(p->seg_off), o_it = put(p->items),
-           o_sp = put(p->splits);
+           o_sp = put(p->splits), o_pt = put(p->pos_tile), o_k32 = put(p->keep32), o_a32 = put(p->any32);
     blob.push_back(0);
     void* dptr = nullptr;
     hipError_t e = hipMalloc(&dptr, blob.size() * sizeof(int));
@@ -328,6 +353,9 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     p->d_seg_off = b + o_so;
     p->d_items = b + o_it;
     p->d_splits = b + o_sp;
+    p->d_pos_tile = b + o_pt;
+    p->d_keep32 = b + o_k32;
+    p->d_any32 = b + o_a32;
     p->attn_resident_wgs = attn_mfma64_supported(*p) ? attn_mfma64_resident_wgs(dev) : 0;
     (void)hipGetLastError();
   } else {

@@ -11,6 +11,8 @@
 
 // Longest key-tile list of one matrix-core attention work item; longer rows are split.
 constexpr int kAttnItemTiles = 64;
+// Segments up to this length (the windows) take the short-segment attention kernel.
+constexpr int kShortMaxN = 256;
 
 struct sparsesam_plan {
   sparsesam_plan_desc desc;
@@ -42,6 +44,11 @@ struct sparsesam_plan {
   std::vector<int> items, splits;
   int n_items = 0, n_split_rows = 0, n_slots = 0;
   int attn_resident_wgs = 0;          // workgroups of the attention kernel resident at once
+  // short segments (n <= 256, the windows): tile of every position; for each (query
+  // tile, 32-key block) the kept key positions of the block as a bit mask; for each
+  // 32-query block the 32-key blocks holding any kept pair
+  std::vector<int> pos_tile, keep32, any32;
+  int nt32 = 0;
 
   // device copy (one allocation) on `device`
   int device = -1;
@@ -55,6 +62,9 @@ struct sparsesam_plan {
   const int* d_seg_off = nullptr;
   const int* d_items = nullptr;
   const int* d_splits = nullptr;
+  const int* d_pos_tile = nullptr;
+  const int* d_keep32 = nullptr;
+  const int* d_any32 = nullptr;
 
   sparsesam::SegmentMap segmap() const {
     sparsesam::SegmentMap m;

@@ -387,6 +387,173 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
   O[((size_t)seg * n + tile_start[qt] + q) * ((size_t)heads * D) + (size_t)h * D + d] = to_bf16(num / den);
 }
 
+// ---------------------------------------------------------------- short segments (windows)
+
+// Segments of at most 256 tokens (the 14 x 14 windows): one 256-thread workgroup per
+// (segment, head) holds the segment's whole K and V^T in LDS (keys past n zero) and
+// each wavefront takes 32-query blocks. The pattern's blocks (16 tokens, ragged at
+// stripe ends) do not align with 32-token MFMA blocks, so each (query, 32-key block)
+// applies the plan's kept-key bit mask -- static, from the plan -- and 32 x 32 blocks
+// without any kept pair are skipped. S^T = K Q^T and O^T = V^T P^T on
+// v_mfma_f32_32x32x16_bf16 as in the long-segment kernel; head_dim 80 runs V^T as
+// three 32-row blocks with rows 80..95 zero in registers.
+template <int D>
+struct ShortLds {
+  static constexpr int KLD = D + 8;        // K row stride (bf16): 16-byte pad, conflict-free reads
+  static constexpr int MD = (D + 31) / 32;  // 32-row blocks of V^T
+  static size_t bytes(int nt32) {
+    const int nk = nt32 * 32;
+    return (size_t)nk * KLD * 2 + (size_t)D * (nk + 8) * 2;
+  }
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
+                                                         const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
+                                                         const int* __restrict__ pos_tile,
+                                                         const int* __restrict__ keep32,
+                                                         const int* __restrict__ any32, int n, int n_pad, int nt32,
+                                                         int heads, float c_log2) {
+  using L = ShortLds<D>;
+  constexpr int KS = D / 16;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nk = nt32 * 32, vld = nk + 8;  // V^T row stride (bf16)
+  bf16_t* Ks = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* Vs = Ks + (size_t)nk * L::KLD;
+  const int sh = blockIdx.x;
+  const int seg = sh / heads, h = sh - seg * heads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bf16_t* q_base = Q + (size_t)sh * n * D;
+  const bf16_t* k_base = Kt + (size_t)sh * n * D;
+  const bf16_t* v_base = VT + (size_t)sh * D * n_pad;
+
+  // K rows 0..nk-1 (zero past n), 8 channels per 16-byte chunk
+  for (int c = tid; c < nk * (D / 8); c += 256) {
+    const int r = c / (D / 8), ch = c - (c / (D / 8)) * (D / 8);
+    i32x4 v = {0, 0, 0, 0};
+    if (r < n) v = *reinterpret_cast<const i32x4*>(k_base + (size_t)r * D + ch * 8);
+    *reinterpret_cast<i32x4*>(Ks + r * L::KLD + ch * 8) = v;
+  }
+  // V^T rows 0..D-1, keys 0..nk-1 (zero at keys >= n: V^T holds nothing there)
+  for (int c = tid; c < D * (nk / 8); c += 256) {
+    const int d = c / (nk / 8), kc = (c - (c / (nk / 8)) * (nk / 8)) * 8;
+    bf16x8 v;
+    if (kc + 8 <= n) {
+      v = *reinterpret_cast<const bf16x8*>(v_base + (size_t)d * n_pad + kc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = kc + i < n ? v_base[(size_t)d * n_pad + kc + i] : (bf16_t)0.0f;
+    }
+    *reinterpret_cast<bf16x8*>(Vs + d * vld + kc) = v;
+  }
+  __syncthreads();
+
+  const int hi = lane >> 5, l32 = lane & 31;
+  for (int qt = wave; qt < nt32; qt += 4) {
+    const int qpos = qt * 32 + l32;
+    const int qrow = min(qpos, n - 1);
+    const int tq = pos_tile[qrow];
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(q_base + (size_t)qrow * D + ks * 16 + hi * 8);
+    f32x16 oacc[L::MD];
+#pragma unroll
+    for (int md = 0; md < L::MD; ++md)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[md][e] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+    const int any = any32[qt];
+    for (int kt = 0; kt < nt32; ++kt) {
+      if (!((any >> kt) & 1)) continue;  // no kept pair in this 32 x 32 block
+      const unsigned bits = (unsigned)keep32[tq * nt32 + kt];
+      // S^T block: keys kt*32 + 8 (e / 4) + 4 hi + (e % 4) of this lane's query
+      f32x16 sc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + l32) * L::KLD + ks * 16 + hi * 8);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc, 0, 0, 0);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const bool keep = (bits >> (8 * (e >> 2) + 4 * hi + (e & 3))) & 1u;
+        sc[e] = keep ? sc[e] : -INFINITY;
+        mx = fmaxf(mx, sc[e]);
+      }
+      mx = max_xor32(mx);
+      const float m_new = fmaxf(m_run, mx * c_log2);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
+        // a lane whose reference does not move keeps alpha = 1 (also when both are -inf)
+        const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        l_run *= alpha;
+#pragma unroll
+        for (int md = 0; md < L::MD; ++md)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
+        m_run = m_new;
+      }
+      float ps0 = 0.0f, ps1 = 0.0f;
+      bf16x8 pf[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = sc[kk * 8 + e];
+          const float p = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c_log2, -m_run));
+          if (e & 1)
+            ps1 += p;
+          else
+            ps0 += p;
+          v[e] = to_bf16(p);
+        }
+        u32x4 r = __builtin_bit_cast(u32x4, v);
+        const auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+        r = u32x4{s02[0], s13[0], s02[1], s13[1]};
+        pf[kk] = __builtin_bit_cast(bf16x8, r);
+      }
+      l_run += ps0 + ps1;
+      // O^T += V^T P^T: rows d = 32 md + l32 (zero past D), keys kt*32 + 16 kk + 8 hi ..
+#pragma unroll
+      for (int md = 0; md < L::MD; ++md) {
+        const int d = md * 32 + l32;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          bf16x8 vf;
+          if (md * 32 + 32 <= D || d < D)
+            vf = *reinterpret_cast<const bf16x8*>(Vs + (size_t)min(d, D - 1) * vld + kt * 32 + kk * 16 + hi * 8);
+          if (!(md * 32 + 32 <= D) && d >= D) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vf[i] = (bf16_t)0.0f;
+          }
+          oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[md], 0, 0, 0);
+        }
+      }
+    }
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (qpos < n) {
+      const float inv_l = 1.0f / l_tot;
+      bf16_t* o_row = O + ((size_t)seg * n + qpos) * ((size_t)heads * D) + (size_t)h * D;
+#pragma unroll
+      for (int md = 0; md < L::MD; ++md)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = md * 32 + g4 * 8 + hi * 4;
+          if (d < D) {
+            bf16x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = to_bf16(oacc[md][g4 * 4 + e] * inv_l);
+            *reinterpret_cast<bf16x4*>(o_row + d) = v4;
+          }
+        }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- SIMT kernel (any pattern)
 
 template <typename T, int D>
@@ -477,6 +644,29 @@ hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, c
   if (segments <= 0) return hipSuccess;
   const float c_log2 = scale * 1.4426950408889634f;
   if constexpr (sizeof(T) == 2) {
+    if (p.nt32 > 0 && (p.desc.head_dim == 64 || p.desc.head_dim == 80)) {
+      const int units = segments * p.desc.heads;
+      const auto* qb = reinterpret_cast<const bf16_t*>(q);
+      const auto* kb = reinterpret_cast<const bf16_t*>(k);
+      const auto* vb = reinterpret_cast<const bf16_t*>(vt);
+      auto* ob = reinterpret_cast<bf16_t*>(o);
+      if (p.desc.head_dim == 64) {
+        const size_t lds = ShortLds<64>::bytes(p.nt32);
+        hipError_t e = hipFuncSetAttribute((const void*)attn_short_kernel<64>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_short_kernel<64>, dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
+                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2);
+      } else {
+        const size_t lds = ShortLds<80>::bytes(p.nt32);
+        hipError_t e = hipFuncSetAttribute((const void*)attn_short_kernel<80>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_short_kernel<80>, dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
+                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2);
+      }
+      return hipGetLastError();
+    }
     if (attn_mfma64_supported(p)) {
       const int seg_heads = segments * p.desc.heads;
       hipError_t e = hipFuncSetAttribute((const void*)attn_mfma64_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
