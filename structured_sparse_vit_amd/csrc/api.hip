@@ -356,7 +356,7 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     p->d_pos_tile = b + o_pt;
     p->d_keep32 = b + o_k32;
     p->d_any32 = b + o_a32;
-    p->attn_resident_wgs = attn_mfma64_supported(*p) ? attn_mfma64_resident_wgs(dev) : 0;
+    p->attn_resident_wgs = attn_long_supported(*p) ? attn_long_resident_wgs(dev, p->desc.head_dim) : 0;
     (void)hipGetLastError();
   } else {
     (void)hipGetLastError();

@@ -142,8 +142,8 @@ hipError_t launch_gemm_residual(const T* a, const T* w, int m, int n, int k, con
 template <typename T>
 hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
                             float scale, void* partial, hipStream_t st);
-bool attn_mfma64_supported(const sparsesam_plan& p);
-int attn_mfma64_resident_wgs(int device);
+bool attn_long_supported(const sparsesam_plan& p);
+int attn_long_resident_wgs(int device, int head_dim);
 size_t attn_partial_bytes(const sparsesam_plan& p, int segments);
 
 }  // namespace sparsesam

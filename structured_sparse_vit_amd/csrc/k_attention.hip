@@ -38,7 +38,8 @@ constexpr int kTileBytes = kTile * 128;          // one swizzled 64 x 64 bf16 ti
 constexpr int kParityBytes = 4 * kTileBytes;     // K ring (2 slots) + V^T ring (2 slots)
 constexpr int kAttnWaves = 8;                    // wavefronts per workgroup: 4 x (two query halves)
 constexpr int kAttnLds = 4 * kParityBytes;       // up to four key parities: 128 KiB
-constexpr int kPartLd = 68;                      // partial record: O[64], m, l, pad (floats)
+// partial record of a split row (floats): O[D], m, l, pad
+__host__ __device__ constexpr int part_ld(int D) { return D + 4; }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -320,7 +321,7 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
         *reinterpret_cast<bf16x4*>(o_row + d) = v4;
       }
   } else {
-    float* rec = partial + (((size_t)slot * seg_heads + sh) * kTile + q_local) * kPartLd;
+    float* rec = partial + (((size_t)slot * seg_heads + sh) * kTile + q_local) * part_ld(D);
 #pragma unroll
     for (int md = 0; md < 2; ++md)
 #pragma unroll
@@ -330,8 +331,8 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
             f32x4{oacc[md][g4 * 4], oacc[md][g4 * 4 + 1], oacc[md][g4 * 4 + 2], oacc[md][g4 * 4 + 3]};
       }
     if (lane < 32) {
-      rec[64] = m_run;
-      rec[65] = l_tot;
+      rec[D] = m_run;
+      rec[D + 1] = l_tot;
     }
   }
 }
@@ -361,30 +362,283 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma64_kernel(const bf16
   }
 }
 
+// ---------------------------------------------------------------- long segments, head_dim 80
+
+// The same work items, wavefront roles and parity merge as attn_mfma64_kernel, for
+// head_dim 80 (ViT-H). A K tile is 64 rows of 160 bytes, its 10 chunks of row r
+// rotated by r / 8 so that 16 consecutive rows of one logical chunk fall in distinct
+// bank groups; a V^T tile is 80 rows of the swizzled 128-byte layout. Both arrive by
+// direct-to-LDS loads into two-slot rings per parity (160 KiB for four parities), one
+// step ahead; S^T = K Q^T takes five 16-channel steps and O^T = V^T P^T three 32-row
+// blocks, rows 80..95 zero in registers. No S-ahead pipelining here: the registers are
+// taken by the wider operands.
+constexpr int kD80 = 80;
+constexpr int kD80Tile = kTile * kD80 * 2;         // bytes of one K or V^T tile (10 KiB)
+constexpr int kD80Parity = 4 * kD80Tile;           // K ring + V^T ring, two slots each
+constexpr int kD80Lds = 4 * kD80Parity;            // four parities: 160 KiB
+__device__ __forceinline__ int k80_off(int r, int c) { return r * 160 + ((c + (r >> 3)) % 10) * 16; }
+
+__device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
+                                              const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
+                                              const int4* __restrict__ items, const int* __restrict__ col_idx,
+                                              const int* __restrict__ tile_start, int n, int n_pad, int heads,
+                                              int seg_heads, float c_log2, float* __restrict__ partial, int item,
+                                              int sh, char* smem) {
+  constexpr int D = kD80, KS = D / 16, MD = 3;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int4 it0 = items[2 * item], it1 = items[2 * item + 1];
+  const int kb = __builtin_amdgcn_readfirstlane(it0.x), ke = __builtin_amdgcn_readfirstlane(it0.y);
+  const int slot = __builtin_amdgcn_readfirstlane(it0.z), gp = __builtin_amdgcn_readfirstlane(it0.w);
+  const int G = gp & 15, P = gp >> 4;
+  const int qh = wave & 1, pr = wave >> 1;
+  const int gi = pr % G, kp = pr / G;
+  const bool active = kp < P;
+  const int qt = gi == 0 ? it1.x : gi == 1 ? it1.y : gi == 2 ? it1.z : it1.w;
+  const int seg = sh / heads, h = sh - seg * heads;
+  const bf16_t* q_base = Q + (size_t)sh * n * D;
+  const bf16_t* k_base = Kt + (size_t)sh * n * D;
+  const bf16_t* v_base = VT + (size_t)sh * D * n_pad;
+  char* ring = smem + (active ? kp : 0) * kD80Parity;
+  const int hi = lane >> 5, l32 = lane & 31;
+
+  const int q_local = qh * 32 + l32;
+  const int my_q = tile_start[qt] + q_local;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(q_base + (size_t)my_q * D + ks * 16 + hi * 8);
+  const int total = ke - kb;
+  const int koff = lane < total ? tile_start[col_idx[kb + lane]] : 0;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  // loads: 10 groups of 1 KiB per tile (K and V^T alike); wavefront w takes groups w
+  // and w + 8 (< 10). K: physical chunk 64 g + L is row (64 g + L) / 10, position
+  // (64 g + L) % 10, which holds logical chunk (position - row / 8) mod 10. V^T: row
+  // 8 g + L / 8, position L % 8 holding logical chunk (L % 8) ^ swz_key(row).
+  int k_src[2], v_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int g = wave + 8 * i;
+    const int pc = 64 * g + lane, kr = pc / 10, kpos = pc - (pc / 10) * 10;
+    const int kc = (kpos + 10 - ((kr >> 3) % 10)) % 10;
+    k_src[i] = kr * D + kc * 8;
+    const int vr = 8 * g + (lane >> 3), vc = (lane & 7) ^ swz_key(8 * g + (lane >> 3));
+    v_src[i] = vr * n_pad + vc * 8;
+  }
+  const int ngrp = wave + 8 < 10 ? 2 : 1;
+  auto issue = [&](int j, int s) {  // K and V^T tiles of step j (every parity) into slot s
+    for (int p = 0; p < P; ++p) {
+      const int t = p + P * j;
+      if (t >= total) break;
+      const int k0 = __builtin_amdgcn_readlane(koff, t);
+      char* base = smem + p * kD80Parity;
+      for (int i = 0; i < ngrp; ++i) {
+        const int g = wave + 8 * i;
+        __builtin_amdgcn_global_load_lds((const void*)(k_base + (size_t)k0 * D + k_src[i]),
+                                         (__attribute__((address_space(3))) void*)(base + s * kD80Tile + g * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(v_base + k0 + v_src[i]),
+            (__attribute__((address_space(3))) void*)(base + (2 + s) * kD80Tile + g * 1024), 16, 0, 0);
+      }
+    }
+  };
+
+  f32x16 oacc[MD];
+#pragma unroll
+  for (int i = 0; i < MD; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  auto tile_step = [&](int s) {
+    const char* Ks = ring + s * kD80Tile;
+    const char* Vs = ring + (2 + s) * kD80Tile;
+    f32x16 sc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[mb][e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + k80_off(mb * 32 + l32, ks * 2 + hi));
+        sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[mb], 0, 0, 0);
+      }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[mb][e]);
+    mx = max_xor32(mx);
+    const float m_new = fmaxf(m_run, mx * c_log2);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
+      m_run = m_new;
+    }
+    float ps0 = 0.0f, ps1 = 0.0f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + e], c_log2, -m_run));
+        if (e & 1)
+          ps1 += p;
+        else
+          ps0 += p;
+        v[e] = to_bf16(p);
+      }
+      u32x4 r = __builtin_bit_cast(u32x4, v);
+      const auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+      r = u32x4{s02[0], s13[0], s02[1], s13[1]};
+      pf[kk] = __builtin_bit_cast(bf16x8, r);
+    }
+    l_run += ps0 + ps1;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const int d = md * 32 + l32;
+        bf16x8 vf;
+        if (md < 2 || d < D) {
+          vf = *reinterpret_cast<const bf16x8*>(Vs + swz(min(d, D - 1), kk * 2 + hi));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) vf[i] = (bf16_t)0.0f;
+        }
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[md], 0, 0, 0);
+      }
+  };
+
+  const int nj = active ? (total - kp + P - 1) / P : 0;
+  const int niter = (total + P - 1) / P;
+  issue(0, 0);
+  for (int j = 0; j < niter; ++j) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(j + 1, (j + 1) & 1);  // into the slot read in step j - 1
+    if (j < nj) tile_step(j & 1);
+  }
+  __syncthreads();
+
+  float* xch = reinterpret_cast<float*>(smem);
+  constexpr int RL = 2 + 16 * MD;  // exchange record: m, l, O[48]
+  auto rec_of = [&](int p) { return xch + ((((size_t)(p - 1) * G + gi) * 2 + qh) * 64 + lane) * RL; };
+  if (active && kp > 0) {
+    float* r = rec_of(kp);
+    r[0] = m_run;
+    r[1] = l_run;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) r[2 + md * 16 + e] = oacc[md][e];
+  }
+  __syncthreads();
+  if (!active || kp > 0) return;
+  for (int p = 1; p < P; ++p) {
+    const float* r = rec_of(p);
+    const float m1 = r[0], l1 = r[1];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[md][e] = oacc[md][e] * a0 + r[2 + md * 16 + e] * a1;
+    m_run = mm;
+  }
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (slot < 0) {
+    const float inv_l = 1.0f / l_tot;
+    bf16_t* o_row = O + ((size_t)seg * n + my_q) * ((size_t)heads * D) + (size_t)h * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = md * 32 + g4 * 8 + hi * 4;
+        if (d < D) {
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = to_bf16(oacc[md][g4 * 4 + e] * inv_l);
+          *reinterpret_cast<bf16x4*>(o_row + d) = v4;
+        }
+      }
+  } else {
+    float* rec = partial + (((size_t)slot * seg_heads + sh) * kTile + q_local) * part_ld(D);
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = md * 32 + g4 * 8 + hi * 4;
+        if (d < D)
+          *reinterpret_cast<f32x4*>(rec + d) =
+              f32x4{oacc[md][g4 * 4], oacc[md][g4 * 4 + 1], oacc[md][g4 * 4 + 2], oacc[md][g4 * 4 + 3]};
+      }
+    if (lane < 32) {
+      rec[D] = m_run;
+      rec[D + 1] = l_tot;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(64 * kAttnWaves) attn_d80_kernel(const bf16_t* __restrict__ Q,
+                                                                  const bf16_t* __restrict__ Kt,
+                                                                  const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
+                                                                  const int4* __restrict__ items,
+                                                                  const int* __restrict__ col_idx,
+                                                                  const int* __restrict__ tile_start, int n, int n_pad,
+                                                                  int heads, int seg_heads, int n_items, float c_log2,
+                                                                  float* __restrict__ partial) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nwg = gridDim.x, w = blockIdx.x;
+  const int total = n_items * seg_heads;
+  for (int r = 0;; ++r) {
+    const int u = r * nwg + ((r & 1) ? nwg - 1 - w : w);
+    if (u >= total) break;
+    if (r > 0) __syncthreads();
+    const int item = u / seg_heads;
+    attn_d80_unit(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
+                  u - item * seg_heads, smem);
+  }
+}
+
 // Merge the partials of split rows: O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
-// One wavefront per (split row, segment-head, query); lane d is channel d.
+// One wavefront per (split row, segment-head, query); lane d is channel d (and d + 64).
+template <int D>
 __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restrict__ partial,
                                                            const int* __restrict__ splits,
                                                            const int* __restrict__ tile_start, bf16_t* __restrict__ O,
                                                            int n, int heads, int seg_heads, int total) {
-  constexpr int D = 64;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6), d = threadIdx.x & 63;
+  constexpr int LD = part_ld(D);
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (w >= total) return;
   const int q = w % kTile, rs = w / kTile;
   const int sh = rs % seg_heads, r = rs / seg_heads;
   const int qt = splits[3 * r], slot0 = splits[3 * r + 1], nch = splits[3 * r + 2];
   const int seg = sh / heads, h = sh - seg * heads;
   float mm = -INFINITY;
-  for (int c = 0; c < nch; ++c)
-    mm = fmaxf(mm, partial[(((size_t)(slot0 + c) * seg_heads + sh) * kTile + q) * kPartLd + 64]);
-  float num = 0.0f, den = 0.0f;
-  for (int c = 0; c < nch; ++c) {
-    const float* rec = partial + (((size_t)(slot0 + c) * seg_heads + sh) * kTile + q) * kPartLd;
-    const float a = __builtin_amdgcn_exp2f(rec[64] - mm);
-    num += a * rec[d];
-    den += a * rec[65];
+  for (int c = 0; c < nch; ++c) mm = fmaxf(mm, partial[(((size_t)(slot0 + c) * seg_heads + sh) * kTile + q) * LD + D]);
+  for (int d = lane; d < D; d += 64) {
+    float num = 0.0f, den = 0.0f;
+    for (int c = 0; c < nch; ++c) {
+      const float* rec = partial + (((size_t)(slot0 + c) * seg_heads + sh) * kTile + q) * LD;
+      const float a = __builtin_amdgcn_exp2f(rec[D] - mm);
+      num += a * rec[d];
+      den += a * rec[D + 1];
+    }
+    O[((size_t)seg * n + tile_start[qt] + q) * ((size_t)heads * D) + (size_t)h * D + d] = to_bf16(num / den);
   }
-  O[((size_t)seg * n + tile_start[qt] + q) * ((size_t)heads * D) + (size_t)h * D + d] = to_bf16(num / den);
 }
 
 // ---------------------------------------------------------------- short segments (windows)
@@ -606,26 +860,25 @@ __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, 
 
 // ---------------------------------------------------------------- launchers
 
-int attn_mfma64_resident_wgs(int device) {
+// workgroups of the long-segment kernel for head_dim (64 or 80) resident at once
+int attn_long_resident_wgs(int device, int head_dim) {
+  const void* kern = head_dim == 80 ? (const void*)attn_d80_kernel : (const void*)attn_mfma64_kernel;
+  const int lds = head_dim == 80 ? kD80Lds : kAttnLds;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return 0;
-  if (hipFuncSetAttribute((const void*)attn_mfma64_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds) !=
-      hipSuccess)
-    return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_mfma64_kernel, 64 * kAttnWaves,
-                                                   kAttnLds) !=
-      hipSuccess)
-    return 0;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kAttnWaves, lds) != hipSuccess) return 0;
   return cus * per_cu;
 }
 
-bool attn_mfma64_supported(const sparsesam_plan& p) {
-  return p.desc.dtype == SPARSESAM_BF16 && p.desc.head_dim == 64 && p.desc.block == 64 && p.s % 64 == 0;
+bool attn_long_supported(const sparsesam_plan& p) {
+  return p.desc.dtype == SPARSESAM_BF16 && (p.desc.head_dim == 64 || p.desc.head_dim == 80) && p.desc.block == 64 &&
+         p.s % 64 == 0 && p.nt32 == 0;
 }
 
 size_t attn_partial_bytes(const sparsesam_plan& p, int segments) {
-  if (!attn_mfma64_supported(p)) return 0;
-  return (size_t)p.n_slots * segments * p.desc.heads * kTile * kPartLd * sizeof(float);
+  if (!attn_long_supported(p)) return 0;
+  return (size_t)p.n_slots * segments * p.desc.heads * kTile * part_ld(p.desc.head_dim) * sizeof(float);
 }
 
 template <typename T, int D>
@@ -667,22 +920,35 @@ hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, c
       }
       return hipGetLastError();
     }
-    if (attn_mfma64_supported(p)) {
+    if (attn_long_supported(p)) {
+      const bool d80 = p.desc.head_dim == 80;
+      const void* kern = d80 ? (const void*)attn_d80_kernel : (const void*)attn_mfma64_kernel;
+      const int lds = d80 ? kD80Lds : kAttnLds;
       const int seg_heads = segments * p.desc.heads;
-      hipError_t e = hipFuncSetAttribute((const void*)attn_mfma64_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         kAttnLds);
+      hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (e != hipSuccess) return e;
       const int units = p.n_items * seg_heads;
       dim3 grid((unsigned)std::min(units, std::max(1, p.attn_resident_wgs)));
-      hipLaunchKernelGGL(attn_mfma64_kernel, grid, dim3(64 * kAttnWaves), kAttnLds, st, q, k, vt, o,
-                         reinterpret_cast<const int4*>(p.d_items), p.d_col_idx, p.d_tile_start, p.n, p.n_pad,
-                         p.desc.heads, seg_heads, p.n_items, c_log2, static_cast<float*>(partial));
+      const auto* items = reinterpret_cast<const int4*>(p.d_items);
+      if (d80)
+        hipLaunchKernelGGL(attn_d80_kernel, grid, dim3(64 * kAttnWaves), lds, st, q, k, vt, o, items, p.d_col_idx,
+                           p.d_tile_start, p.n, p.n_pad, p.desc.heads, seg_heads, p.n_items, c_log2,
+                           static_cast<float*>(partial));
+      else
+        hipLaunchKernelGGL(attn_mfma64_kernel, grid, dim3(64 * kAttnWaves), lds, st, q, k, vt, o, items,
+                           p.d_col_idx, p.d_tile_start, p.n, p.n_pad, p.desc.heads, seg_heads, p.n_items, c_log2,
+                           static_cast<float*>(partial));
       e = hipGetLastError();
       if (e != hipSuccess || p.n_split_rows == 0) return e;
       const int waves = p.n_split_rows * seg_heads * kTile;
-      hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
-                         static_cast<const float*>(partial), p.d_splits, p.d_tile_start, o, p.n, p.desc.heads,
-                         seg_heads, waves);
+      if (d80)
+        hipLaunchKernelGGL(attn_combine_kernel<80>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
+                           static_cast<const float*>(partial), p.d_splits, p.d_tile_start, o, p.n, p.desc.heads,
+                           seg_heads, waves);
+      else
+        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
+                           static_cast<const float*>(partial), p.d_splits, p.d_tile_start, o, p.n, p.desc.heads,
+                           seg_heads, waves);
       return hipGetLastError();
     }
   }
