@@ -231,6 +231,28 @@ sparsesam_status sparsesam_block(sparsesam_plan_t plan, const sparsesam_block_we
                                  float* x, int32_t batch, const int32_t* perm, const int32_t* routed,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * (6) Encoder: a stack of n_layers blocks (5) in place on x, layer l a global block
+ * (kinds[l] = 1, global_plan, perm_global / routed_global) or a windowed block
+ * (kinds[l] = 0, window_plan, perm_window / routed_window). The permutations depend on
+ * the image only, so one set per block type, computed once by sparsesam_permute, serves
+ * every layer of that type ("Technische Samenvatting: SparseSAM", Methodologie, closing
+ * paragraph of part 2; SAM's encoders place four global blocks among windowed ones).
+ *   layers [n_layers] host array; kinds [n_layers] host uint8 in {0, 1}.
+ *   global_plan and window_plan share grid, channels, heads, head_dim, mlp_hidden,
+ *   dtype and device; either may be null when no layer uses it.
+ *   workspace >= the block_workspace_bytes of every plan used, batch <= their max_batch.
+ * Every layer is validated before the first launch: on INVALID_ARGUMENT, UNSUPPORTED,
+ * NO_DEVICE or WORKSPACE nothing runs and x is untouched. A launch failure in layer l
+ * returns ERR_HIP with layers 0..l-1 applied.
+ */
+sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_t window_plan,
+                                   const sparsesam_block_weights* layers /* host */, const uint8_t* kinds /* host */,
+                                   int32_t n_layers, float* x, int32_t batch, const int32_t* perm_global,
+                                   const int32_t* routed_global, const int32_t* perm_window,
+                                   const int32_t* routed_window, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

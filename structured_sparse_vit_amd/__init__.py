@@ -8,6 +8,7 @@ stream. If the library is not built, every call raises.
     imp = importance(img)                     # [b, H, W] fp32 -> [b, tokens]
     perm, inv, routed = permute(plan, imp)    # stripe-sort + keep-set
     block(plan, weights, x, perm, routed)     # one encoder block, in place on x
+    encoder(plan_g, plan_w, layers, kinds, x, perms)   # a stack of blocks, in place on x
 """
 import ctypes
 
@@ -16,7 +17,8 @@ import torch
 from . import _lib
 from ._lib import SPARSESAM_BF16, SPARSESAM_F32, SparseSAMError, check
 
-__all__ = ["Plan", "importance", "permute", "attn", "mlp", "block", "SparseSAMError", "library_path", "weights_to_device"]
+__all__ = ["Plan", "importance", "permute", "attn", "mlp", "block", "encoder", "SparseSAMError", "library_path",
+           "weights_to_device"]
 
 
 def library_path() -> str:
@@ -225,4 +227,51 @@ def block(plan, weights, x, perm, routed, workspace=None):
     bw = _lib.BlockWeights(*[weights[name].data_ptr() for name in _WEIGHT_NAMES])
     check(lib.sparsesam_block(plan.handle, ctypes.byref(bw), _ptr(x), b, _ptr(perm), _ptr(routed), _ptr(ws),
                               ws.numel(), _stream(x.device)), "sparsesam_block")
+    return x
+
+
+def encoder(global_plan, window_plan, layers, kinds, x, global_perm=None, window_perm=None, workspace=None):
+    """A stack of blocks in place on x [batch, grid_h, grid_w, C] fp32.
+
+    layers: list of weight dicts (weights_to_device); kinds: list of 1 (global block)
+    or 0 (windowed block); global_perm / window_perm: (perm, routed) of permute() for
+    the plan of that block type, computed once and reused by every layer of the type.
+    """
+    lib = _lib.load()
+    n = len(layers)
+    if len(kinds) != n:
+        raise ValueError("layers and kinds must have the same length")
+    plans = [p for p in (global_plan, window_plan) if p is not None]
+    if not plans:
+        raise ValueError("at least one plan is needed")
+    for p in plans:
+        _need(x, "x", torch.float32, device=p.device)
+    b = x.shape[0]
+    ptrs = {}
+    for name, plan, pr in (("global", global_plan, global_perm), ("window", window_plan, window_perm)):
+        if plan is None or pr is None:
+            ptrs[name] = (ctypes.c_void_p(0), ctypes.c_void_p(0))
+            continue
+        perm, routed = pr
+        n_seq, segs, rpi = plan.info["seq_len"], plan.info["segments_per_image"], plan.info["routed_per_image"]
+        _need(perm, name + "_perm", torch.int32, (b * segs, n_seq), plan.device)
+        _need(routed, name + "_routed", torch.int32, (b * rpi,), plan.device)
+        ptrs[name] = (_ptr(perm), _ptr(routed))
+    ref = plans[0]
+    dt, C, Hm = ref.torch_dtype, ref.desc.channels, ref.desc.mlp_hidden
+    shapes = {"ln1_g": (C,), "ln1_b": (C,), "w_qkv": (3 * C, C), "b_qkv": (3 * C,), "w_proj": (C, C),
+              "b_proj": (C,), "ln2_g": (C,), "ln2_b": (C,), "w1": (Hm, C), "b1": (Hm,), "w2": (C, Hm), "b2": (C,)}
+    arr = (_lib.BlockWeights * max(1, n))()
+    for l, w in enumerate(layers):
+        for name in _WEIGHT_NAMES:
+            _need(w[name], "layer %d %s" % (l, name), dt if name in _MATRICES else torch.float32, shapes[name],
+                  ref.device)
+        arr[l] = _lib.BlockWeights(*[w[name].data_ptr() for name in _WEIGHT_NAMES])
+    kind_arr = (ctypes.c_uint8 * max(1, n))(*[int(k) for k in kinds])
+    need = max(p.info["block_workspace_bytes"] for p in plans)
+    ws = _workspace(need, x.device, workspace)
+    check(lib.sparsesam_encoder(global_plan.handle if global_plan is not None else None,
+                                window_plan.handle if window_plan is not None else None, arr, kind_arr, n, _ptr(x),
+                                b, ptrs["global"][0], ptrs["global"][1], ptrs["window"][0], ptrs["window"][1],
+                                _ptr(ws), ws.numel(), _stream(x.device)), "sparsesam_encoder")
     return x

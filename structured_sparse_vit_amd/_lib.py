@@ -31,6 +31,7 @@ EXPORTS = [
     "sparsesam_attn",
     "sparsesam_mlp",
     "sparsesam_block",
+    "sparsesam_encoder",
 ]
 
 
@@ -87,6 +88,7 @@ def load():
         "sparsesam_attn": ([P, I32, P, P, P, P, F32, P, SZ, P], I32),
         "sparsesam_mlp": ([P, P, I64, P, I32, P, P, P, P, P, P, P, SZ, P], I32),
         "sparsesam_block": ([P, ctypes.POINTER(BlockWeights), P, I32, P, P, P, SZ, P], I32),
+        "sparsesam_encoder": ([P, P, ctypes.POINTER(BlockWeights), P, I32, P, I32, P, P, P, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

@@ -537,11 +537,10 @@ static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weigh
   return launch_gemm_residual<T>(hid, (const T*)w.w2, rows, C, p.desc.mlp_hidden, e2, st);
 }
 
-extern "C" {
-
-sparsesam_status sparsesam_block(sparsesam_plan_t p, const sparsesam_block_weights* w, float* x, int32_t batch,
-                                 const int32_t* perm, const int32_t* routed, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+// Validation of one block call (no launch, no side effects).
+static sparsesam_status block_check(sparsesam_plan_t p, const sparsesam_block_weights* w, const float* x,
+                                    int32_t batch, const int32_t* perm, const int32_t* routed, const void* workspace,
+                                    size_t workspace_bytes) {
   sparsesam_status st = check_device(p);
   if (st != SPARSESAM_OK) return st;
   if (!w) return invalid("weights must not be null");
@@ -557,12 +556,70 @@ sparsesam_status sparsesam_block(sparsesam_plan_t p, const sparsesam_block_weigh
     set_error("block workspace needs " + std::to_string(need) + " bytes");
     return SPARSESAM_ERR_WORKSPACE;
   }
+  return SPARSESAM_OK;
+}
+
+static sparsesam_status block_impl(sparsesam_plan_t p, const sparsesam_block_weights* w, float* x, int32_t batch,
+                                   const int32_t* perm, const int32_t* routed, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  sparsesam_status st = block_check(p, w, x, batch, perm, routed, workspace, workspace_bytes);
+  if (st != SPARSESAM_OK || batch == 0) return st;
   hipError_t e;
   if (p->desc.dtype == SPARSESAM_BF16)
     e = run_block<bf16_t>(*p, *w, x, batch, perm, routed, (char*)workspace, (hipStream_t)stream);
   else
     e = run_block<float>(*p, *w, x, batch, perm, routed, (char*)workspace, (hipStream_t)stream);
   return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_block launch");
+}
+
+extern "C" {
+
+sparsesam_status sparsesam_block(sparsesam_plan_t p, const sparsesam_block_weights* w, float* x, int32_t batch,
+                                 const int32_t* perm, const int32_t* routed, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return block_impl(p, w, x, batch, perm, routed, workspace, workspace_bytes, stream);
+}
+
+sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_t window_plan,
+                                   const sparsesam_block_weights* layers, const uint8_t* kinds, int32_t n_layers,
+                                   float* x, int32_t batch, const int32_t* perm_global, const int32_t* routed_global,
+                                   const int32_t* perm_window, const int32_t* routed_window, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (n_layers < 0) return invalid("n_layers must be >= 0");
+  if (n_layers == 0) return SPARSESAM_OK;
+  if (!layers || !kinds) return invalid("layers and kinds must not be null");
+  bool any_global = false, any_window = false;
+  for (int l = 0; l < n_layers; ++l) {
+    if (kinds[l] > 1) return invalid("kinds must hold 1 (global block) or 0 (windowed block)");
+    if (kinds[l])
+      any_global = true;
+    else
+      any_window = true;
+  }
+  if (any_global && !global_plan) return invalid("a global layer needs global_plan");
+  if (any_window && !window_plan) return invalid("a windowed layer needs window_plan");
+  if (any_global && any_window) {
+    const sparsesam_plan_desc &g = global_plan->desc, &w = window_plan->desc;
+    if (g.grid_h != w.grid_h || g.grid_w != w.grid_w || g.channels != w.channels || g.heads != w.heads ||
+        g.head_dim != w.head_dim || g.mlp_hidden != w.mlp_hidden || g.dtype != w.dtype ||
+        global_plan->device != window_plan->device)
+      return invalid("global_plan and window_plan must share grid, channels, heads, head_dim, mlp_hidden, dtype "
+                     "and device");
+  }
+  // every layer is validated before the first launch: no partial run on bad input
+  for (int l = 0; l < n_layers; ++l) {
+    sparsesam_status st = block_check(kinds[l] ? global_plan : window_plan, &layers[l], x, batch,
+                                      kinds[l] ? perm_global : perm_window, kinds[l] ? routed_global : routed_window,
+                                      workspace, workspace_bytes);
+    if (st != SPARSESAM_OK) return st;
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    sparsesam_status st = block_impl(kinds[l] ? global_plan : window_plan, &layers[l], x, batch,
+                                     kinds[l] ? perm_global : perm_window, kinds[l] ? routed_global : routed_window,
+                                     workspace, workspace_bytes, stream);
+    if (st != SPARSESAM_OK) return st;
+  }
+  return SPARSESAM_OK;
 }
 
 }  // extern "C"

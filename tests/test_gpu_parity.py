@@ -281,3 +281,46 @@ def test_block_density_one_matches_dense_oracle():
     xd = torch.from_numpy(x.copy()).to(DEV)
     ss.block(plan, ss.weights_to_device(w, plan), xd, perm, routed)
     check_close(xd.cpu().numpy(), want, max_abs=1e-4, rel_l2=1e-5, what="dense fp32 block")
+
+
+# ------------------------------------------------------------------ encoder
+
+def test_encoder_matches_block_by_block_and_oracle():
+    """An 8-block stack of the c4 (ViT-L) layout at reduced width, batch 2: global blocks
+    at layers 1, 3, 5, 7, windowed elsewhere, one permutation set per block type. The
+    native encoder equals the same blocks called one by one (deterministic kernels:
+    bit-equal) and the fp64 oracle encoder to the per-block bar scaled by sqrt(8) (each
+    block adds its own independent bf16 rounding)."""
+    _say("encoder 8 layers")
+    import math
+
+    from synth import block_weights, encoder_global_layers, token_features
+    from synth.configs import global_variant, window_variant
+    layers, b = 8, 2
+    base = config("c4").with_(batch=b, channels=256, heads=4, mlp_hidden=512, layers=layers)
+    cg, cw = global_variant(base).with_(batch=b), window_variant(base).with_(batch=b)
+    pg, pw = _plan(cg), _plan(cw)
+    imgs = np.stack([images("c4")[0], images("c4")[1]])
+    imp = np.stack([oracle.importance(im, base.patch) for im in imgs])
+    x0 = token_features(base, 0)
+    gl = encoder_global_layers(layers)
+    kinds = [1 if l in gl else 0 for l in range(layers)]
+    ws = [block_weights(base, 0, layer=l) for l in range(layers)]
+    wd = [ss.weights_to_device(w, pg) for w in ws]
+    imp_d = torch.from_numpy(imp).to(DEV)
+    perm_g, _, routed_g = ss.permute(pg, imp_d)
+    perm_w, _, routed_w = ss.permute(pw, imp_d)
+    x_enc = torch.from_numpy(x0.copy()).to(DEV)
+    ss.encoder(pg, pw, wd, kinds, x_enc, (perm_g, routed_g), (perm_w, routed_w))
+    x_seq = torch.from_numpy(x0.copy()).to(DEV)
+    for l in range(layers):
+        if kinds[l]:
+            ss.block(pg, wd[l], x_seq, perm_g, routed_g)
+        else:
+            ss.block(pw, wd[l], x_seq, perm_w, routed_w)
+    got = x_enc.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), x_seq.cpu().numpy().view(np.uint32))
+    want = oracle.encoder_forward(x0, imp, ws, gl, cg, cw)
+    s = math.sqrt(layers)
+    _say("  encoder max-abs %.3e rel-L2 %.3e" % (np.abs(got - want).max(), rel_l2(got, want)))
+    check_close(got, want, max_abs=1e-2 * s, rel_l2=5e-3 * s, what="encoder")

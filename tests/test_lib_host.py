@@ -162,3 +162,30 @@ def test_null_plan_and_info():
     assert lib.sparsesam_plan_create(None, None) == 1
     assert lib.sparsesam_plan_get_info(None, None) == 1
     lib.sparsesam_plan_destroy(None)
+
+
+def test_encoder_validation_before_launch():
+    """sparsesam_encoder rejects bad layer kinds, missing or mismatched plans before any
+    launch (these checks come before the device check, so they run without a GPU)."""
+    lib = _lib.load()
+    g = _create()
+    w_cfg = get_config("c3").with_(channels=g.desc.channels, heads=g.desc.heads, head_dim=g.desc.head_dim,
+                                   mlp_hidden=g.desc.mlp_hidden)
+    w = ss.Plan.from_config(w_cfg)
+    layers = (_lib.BlockWeights * 2)()
+    p = ctypes.c_void_p(16)
+
+    def call(gp, wp, kinds, n=2):
+        karr = (ctypes.c_uint8 * 2)(*kinds)
+        return lib.sparsesam_encoder(gp, wp, layers, karr, n, p, 1, p, p, p, p, p, 1 << 30, None)
+
+    assert call(g.handle, w.handle, [1, 0], n=0) == 0          # no layers: a no-op
+    assert call(g.handle, w.handle, [1, 2]) == 1                # kinds outside {0, 1}
+    assert call(None, w.handle, [1, 0]) == 1                    # a global layer without a global plan
+    assert call(g.handle, None, [1, 0]) == 1                    # a windowed layer without a window plan
+    assert lib.sparsesam_encoder(g.handle, w.handle, None, None, 2, p, 1, p, p, p, p, p, 1, None) == 1
+    assert lib.sparsesam_encoder(g.handle, w.handle, layers, (ctypes.c_uint8 * 2)(1, 0), -1, p, 1, p, p, p, p, p,
+                                 1, None) == 1
+    other = ss.Plan.from_config(w_cfg.with_(channels=2 * g.desc.channels, heads=2 * g.desc.heads))
+    assert call(g.handle, other.handle, [1, 0]) == 1            # plans of different shapes
+    assert b"share grid" in lib.sparsesam_last_error()
