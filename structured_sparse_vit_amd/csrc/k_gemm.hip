@@ -41,6 +41,33 @@ __device__ __forceinline__ void store8<float>(float* dst, const float* v) {
   *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
+// Batched epilogues. Each thread of a tile owns a fixed 8-column chunk c..c+7 of ITER
+// rows (row-major destinations) or a fixed 8-token chunk of ITER channels (V^T). What
+// the epilogue reads from global memory -- the bias chunk, the residual rows' source
+// indices -- is requested before the K loop (row_prefetch / col_prefetch), and the
+// residual stream is read for all ITER rows before any of them is written, so the
+// latency of those loads is paid once per tile instead of once per row in sequence.
+template <int ITER>
+struct RowPre {
+  float b[8];
+  int raw[ITER];
+};
+
+__device__ __forceinline__ void load_bias8(const float* bias, int c, int N, float* b) {
+  if (c + 8 <= N) {
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(bias + c);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(bias + c + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b[i] = b0[i];
+      b[4 + i] = b1[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = c + i < N ? bias[c + i] : 0.0f;
+  }
+}
+
 // q, k [seg, H, N, D] and V^T [seg, H, D, N_pad] from the columns of the QKV product.
 // Token r of the stripe-sorted rows is slot p of segment seg; column c is channel d of
 // head h of part `which` (q, k, v). Divisions by n, C and D use FastDiv.
@@ -103,6 +130,54 @@ struct QKVStore {
     }
     for (int i = 0; i < count; ++i) elem(r + i, c, v[i]);
   }
+
+  template <int ITER>
+  __device__ __forceinline__ void row_prefetch(RowPre<ITER>& pre, const int*, int c, int, int N) const {
+    if (c < N) load_bias8(bias, c, N, pre.b);
+  }
+  template <int ITER>
+  __device__ __forceinline__ void row_store(const RowPre<ITER>& pre, const int* ms, int c, const float (*v)[8], int M,
+                                            int N) const {
+    if (c >= N) return;
+    const int which = f_C.div(c);
+    if (c + 8 > N || which >= 2) {  // not a whole chunk of one q / k head: element by element
+#pragma unroll
+      for (int it = 0; it < ITER; ++it)
+        if (ms[it] < M)
+          for (int i = 0; i < 8 && c + i < N; ++i) elem(ms[it], c + i, v[it][i]);
+      return;
+    }
+    const int cc = c - which * C;
+    const int h = f_D.div(cc), d = cc - h * D;
+    T* base = (which == 0 ? q : k) + (size_t)h * n * D + d;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int m = ms[it];
+      if (m >= M) continue;
+      const int seg = f_n.div(m), p = m - seg * n;
+      float w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = v[it][i] + pre.b[i];
+      store8<T>(base + ((size_t)seg * heads * n + p) * (size_t)D, w);
+    }
+  }
+  __device__ __forceinline__ float col_bias(int c, int N) const { return c < N ? bias[c] : 0.0f; }
+  // Eight tokens r..r+7 of channel c with the channel's bias b already loaded.
+  __device__ __forceinline__ void col8b(int r, int c, const float* v, int count, float b) const {
+    const int seg = f_n.div(r), p = r - seg * n;
+    const int which = f_C.div(c);
+    if (which == 2 && count == 8 && p + 8 <= n && (p & 7) == 0) {
+      const int cc = c - 2 * C;
+      const int h = f_D.div(cc), d = cc - h * D;
+      const size_t sh = (size_t)seg * heads + h;
+      float w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = v[i] + b;
+      store8<T>(vt + (sh * D + d) * (size_t)n_pad + p, w);
+      return;
+    }
+    for (int i = 0; i < count; ++i) elem(r + i, c, v[i]);
+  }
 };
 
 // Hidden activation of the routed MLP: out[r, c] = GELU(acc + bias).
@@ -124,6 +199,30 @@ struct GeluStore {
   __device__ __forceinline__ void col8(int r, int c, const float* v, int count) const {
     for (int i = 0; i < count; ++i) elem(r + i, c, v[i]);
   }
+  template <int ITER>
+  __device__ __forceinline__ void row_prefetch(RowPre<ITER>& pre, const int*, int c, int, int N) const {
+    if (c < N) load_bias8(bias, c, N, pre.b);
+  }
+  template <int ITER>
+  __device__ __forceinline__ void row_store(const RowPre<ITER>& pre, const int* ms, int c, const float (*v)[8], int M,
+                                            int N) const {
+    if (c >= N) return;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int m = ms[it];
+      if (m >= M) continue;
+      if (c + 8 <= N) {
+        float w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = gelu_erf(v[it][i] + pre.b[i]);
+        store8<T>(out + (size_t)m * ld + c, w);
+      } else {
+        for (int i = 0; c + i < N; ++i) elem(m, c + i, v[it][i]);
+      }
+    }
+  }
+  __device__ __forceinline__ float col_bias(int, int) const { return 0.0f; }
+  __device__ __forceinline__ void col8b(int r, int c, const float* v, int count, float) const { col8(r, c, v, count); }
 };
 
 // Residual update of the fp32 stream: x[dst(r), c] += acc + bias, where dst maps a
@@ -164,6 +263,53 @@ struct ResidualAdd {
   __device__ __forceinline__ void col8(int r, int c, const float* v, int count) const {
     for (int i = 0; i < count; ++i) elem(r + i, c, v[i]);
   }
+  template <int ITER>
+  __device__ __forceinline__ void row_prefetch(RowPre<ITER>& pre, const int* ms, int c, int M, int N) const {
+    if (c < N) load_bias8(bias, c, N, pre.b);
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) pre.raw[it] = ms[it] < M ? (list ? list[ms[it]] : perm[ms[it]]) : -1;
+  }
+  template <int ITER>
+  __device__ __forceinline__ void row_store(const RowPre<ITER>& pre, const int* ms, int c, const float (*v)[8], int M,
+                                            int N) const {
+    if (c >= N) return;
+    if (c + 8 > N) {
+#pragma unroll
+      for (int it = 0; it < ITER; ++it)
+        if (ms[it] < M)
+          for (int i = 0; c + i < N; ++i) elem(ms[it], c + i, v[it][i]);
+      return;
+    }
+    // destination rows, then every row's current values, then the updates
+    long long off[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      int row = -1;
+      if (ms[it] < M && pre.raw[it] >= 0) row = list ? pre.raw[it] : map.row_of(map.seg_of(ms[it]), pre.raw[it]);
+      off[it] = (row < 0 || row >= x_rows) ? -1 : (long long)row * ldx + c;
+    }
+    f32x4 cur[ITER][2];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it)
+      if (off[it] >= 0) {
+        cur[it][0] = *reinterpret_cast<const f32x4*>(x + off[it]);
+        cur[it][1] = *reinterpret_cast<const f32x4*>(x + off[it] + 4);
+      }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it)
+      if (off[it] >= 0) {
+        f32x4 a = cur[it][0], b = cur[it][1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[i] = a[i] + (v[it][i] + pre.b[i]);
+          b[i] = b[i] + (v[it][4 + i] + pre.b[4 + i]);
+        }
+        *reinterpret_cast<f32x4*>(x + off[it]) = a;
+        *reinterpret_cast<f32x4*>(x + off[it] + 4) = b;
+      }
+  }
+  __device__ __forceinline__ float col_bias(int, int) const { return 0.0f; }
+  __device__ __forceinline__ void col8b(int r, int c, const float* v, int count, float) const { col8(r, c, v, count); }
 };
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM
@@ -247,6 +393,24 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
     }
   };
 
+  // epilogue inputs requested now, consumed after the K loop (see RowPre)
+  constexpr int CPR = BN / 8, ITER = BM * CPR / 256;  // row path: chunks per row, chunks per thread
+  constexpr int RPC = BM / 8, ITERT = BN * RPC / 256;  // V^T path: chunks per channel, per thread
+  static_assert(256 % CPR == 0 && 256 % RPC == 0, "fixed chunk per thread");
+  const int ec = n0 + (tid % CPR) * 8;
+  int ems[ITER];
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) ems[it] = m0 + tid / CPR + it * (256 / CPR);
+  RowPre<ITER> rpre;
+  const int tm = m0 + (tid % RPC) * 8;
+  float tb[ITERT];
+  if constexpr (!TR) {
+    epi.row_prefetch(rpre, ems, ec, M, N);
+  } else {
+#pragma unroll
+    for (int it = 0; it < ITERT; ++it) tb[it] = epi.col_bias(n0 + tid / RPC + it * (256 / RPC), N);
+  }
+
   const int nk = K / BK;
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
@@ -315,28 +479,29 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
       }
   __syncthreads();
   if constexpr (!TR) {
-    for (int idx = tid; idx < BM * (BN / 8); idx += 256) {
-      const int ml = idx / (BN / 8), nl = (idx - ml * (BN / 8)) * 8;
-      const int m = m0 + ml, n = n0 + nl;
-      if (m >= M || n >= N) continue;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(ct + ml * TL::CT_LD + nl);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(ct + ml * TL::CT_LD + nl + 4);
-      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      if (n + 8 <= N) {
-        epi.row8(m, n, v);
-      } else {
-        for (int i = 0; i < N - n; ++i) epi.elem(m, n + i, v[i]);
+    float v[ITER][8];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const float* src = ct + (ems[it] - m0) * TL::CT_LD + (ec - n0);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[it][i] = a[i];
+        v[it][4 + i] = b[i];
       }
     }
+    epi.row_store(rpre, ems, ec, v, M, N);
   } else {
-    for (int idx = tid; idx < BN * (BM / 8); idx += 256) {
-      const int nl = idx / (BM / 8), ml = (idx - nl * (BM / 8)) * 8;
-      const int m = m0 + ml, n = n0 + nl;
-      if (m >= M || n >= N) continue;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(ct + nl * TL::CTT_LD + ml);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(ct + nl * TL::CTT_LD + ml + 4);
+#pragma unroll
+    for (int it = 0; it < ITERT; ++it) {
+      const int n = n0 + tid / RPC + it * (256 / RPC);
+      if (tm >= M || n >= N) continue;
+      const float* src = ct + (n - n0) * TL::CTT_LD + (tm - m0);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
       const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      epi.col8(m, n, v, min(8, M - m));
+      epi.col8b(tm, n, v, min(8, M - tm), tb[it]);
     }
   }
 }
