@@ -174,6 +174,60 @@ def torch_dense_block_ms(cfg, dev, iters=20):
         return time_region(run, iters, 3)
 
 
+def encoder_run(key, dev, density=None, passes=3):
+    """One pass of a whole encoder config (c4: ViT-L 24 blocks, c5: ViT-H 32 blocks) through
+    sparsesam_encoder: importance and both permutations once per pass, then every block.
+    Timing only: one random-init layer's weights serve every layer (the work per layer
+    is the same). Returns tokens/s and ms per pass."""
+    import torch
+
+    import structured_sparse_vit_amd as ss
+    from synth import block_weights, encoder_global_layers, get_config, synthetic_images, token_features
+    from synth.configs import global_variant, window_variant
+    base = get_config(key)
+    if density is not None:
+        base = base.with_(attn_density=density, mlp_density=density)
+    cg, cw = global_variant(base).with_(batch=base.batch), window_variant(base).with_(batch=base.batch)
+    pg, pw = ss.Plan.from_config(cg), ss.Plan.from_config(cw)
+    wd = ss.weights_to_device(block_weights(cg, 0), pg)
+    layers = [wd] * base.layers
+    gl = set(encoder_global_layers(base.layers))
+    kinds = [1 if l in gl else 0 for l in range(base.layers)]
+    img = torch.from_numpy(synthetic_images(base, 0)).to(dev)
+    x0 = torch.from_numpy(token_features(base, 0)).to(dev)
+    x = x0.clone()
+    ws = torch.empty(max(pg.info["block_workspace_bytes"], pw.info["block_workspace_bytes"]), dtype=torch.uint8,
+                     device=dev)
+
+    def one_pass():
+        x.copy_(x0)  # every pass starts from the same features
+        imp = ss.importance(img, base.patch)
+        perm_g, _, routed_g = ss.permute(pg, imp)
+        perm_w, _, routed_w = ss.permute(pw, imp)
+        ss.encoder(pg, pw, layers, kinds, x, (perm_g, routed_g), (perm_w, routed_w), workspace=ws)
+
+    ms = time_region(one_pass, passes, 1)
+    tokens = base.batch * base.grid * base.grid
+    del x, ws
+    return {"batch": base.batch, "blocks": base.layers, "global_blocks": sorted(gl),
+            "attn_density": base.attn_density, "mlp_density": base.mlp_density,
+            "ms_per_pass": round(ms, 3), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "weights": "one random-init layer reused by every layer (timing only)"}
+
+
+def window_block_run(dev):
+    """The c3 windowed block (ViT-B, 25 windows of 14 x 14 per image, batch 4)."""
+    from synth import get_config
+    cfg = get_config("c3")
+    wl = Workload(cfg, dev)
+    wl.step()
+    blk = time_region(lambda: wl.ss.block(wl.plan, wl.w, wl.x, wl.perm, wl.routed, workspace=wl.ws), 20, 3)
+    step = time_region(wl.step, 20, 3)
+    tokens = cfg.batch * cfg.grid * cfg.grid
+    return {"batch": cfg.batch, "block_ms": round(blk, 5), "step_ms": round(step, 5),
+            "tokens_per_s": round(tokens / (step * 1e-3), 1)}
+
+
 def cpu_baseline(cfg, budget_s=25.0):
     """The oracle, as it stands, on a bounded sample of the same workload on this host."""
     import numpy as np
@@ -262,8 +316,8 @@ def summarize_profiles(src):
     cf, _ = _counter_kib(os.path.join(src, "pmc_fetch_copy"), "FETCH_SIZE", "copyBuffer")
     cw, _ = _counter_kib(os.path.join(src, "pmc_write_copy"), "WRITE_SIZE", "copyBuffer")
     f_scale, w_scale = (COPY_BYTES / 1024) / cf, (COPY_BYTES / 1024) / cw
-    lines = ["# HBM traffic of one sparsesam_attn launch on the c2 workload (attention kernel plus",
-             "# the combine of split rows), from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch,",
+    lines = ["# HBM traffic of one sparsesam_attn launch on the c2 workload (attention kernel, and the",
+             "# combine of split rows when there are any), from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch,",
              "# separate passes), each scaled by the same counter on a plain 256 MiB device copy.",
              "# commands (from the repository root):"]
     lines += ["#   " + PROFILE_COMMANDS[k] for k in ("fetch", "write", "copy_fetch", "copy_write")]
@@ -271,8 +325,12 @@ def summarize_profiles(src):
               "fetch_scale = %.5f" % f_scale, "write_scale = %.5f" % w_scale]
     total = 0.0
     for kname in ATTN_KERNELS:
-        fk, nf = _counter_kib(os.path.join(src, "pmc_fetch_c2"), "FETCH_SIZE", kname)
-        wk, nw = _counter_kib(os.path.join(src, "pmc_write_c2"), "WRITE_SIZE", kname)
+        try:
+            fk, nf = _counter_kib(os.path.join(src, "pmc_fetch_c2"), "FETCH_SIZE", kname)
+            wk, nw = _counter_kib(os.path.join(src, "pmc_write_c2"), "WRITE_SIZE", kname)
+        except SystemExit:  # not launched at this workload (the combine runs only for split rows)
+            lines.append("%s: no dispatches" % kname)
+            continue
         b = (fk * f_scale + wk * w_scale) * 1024
         total += b
         lines += ["%s_fetch_kib = %.1f  # average of %d dispatches" % (kname, fk, nf),
@@ -293,6 +351,7 @@ def main():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-encoders", action="store_true", help="skip the c3 windowed block and c4 / c5 encoder runs")
     ap.add_argument("--profile-only", action="store_true", help="run the steps only (for rocprofv3)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy 5 times (scale factor for HBM byte counters)")
@@ -394,6 +453,18 @@ def main():
                           "torch_eager_block_ms": round(dense_torch, 5),
                           "speedup_vs_faster_dense": round(best / ms, 3)}
 
+    if not args.no_encoders:
+        extra["c3_window_block"] = window_block_run(dev)
+        _log("c3 windowed block", extra["c3_window_block"])
+        enc = {}
+        for key in ("c4", "c5"):
+            enc[key] = {"sparse": encoder_run(key, dev), "density_1.0": encoder_run(key, dev, density=1.0)}
+            enc[key]["speedup_vs_density_1"] = round(enc[key]["density_1.0"]["ms_per_pass"] /
+                                                     enc[key]["sparse"]["ms_per_pass"], 3)
+            _log("encoder", key, enc[key])
+            torch.cuda.empty_cache()
+        extra["encoders"] = enc
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg)
@@ -417,7 +488,7 @@ def main():
                    "attn_density": cfg.attn_density, "mlp_density": cfg.mlp_density,
                    "realised_attn_density": plan.info["realised_density"],
                    "routed_tokens": plan.info["routed_per_image"] * cfg.batch},
-        "roofline": {"bound": "mfma", "kernel": "sparsesam_attn (attn_mfma64_kernel + attn_combine_kernel)", "achieved": round(attn_tf, 2),
+        "roofline": {"bound": "mfma", "kernel": "sparsesam_attn (attn_mfma64_kernel)", "achieved": round(attn_tf, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(), "launch_ms": round(attn_ms, 5),
                      "algorithmic_flop": attention_flops(plan) * segs},
