@@ -20,6 +20,8 @@ constexpr int kWave = 64;
 // counters unconstrained), in the gfx9 encoding: vmcnt[3:0], expcnt[6:4],
 // lgkmcnt[11:8], vmcnt[5:4] in bits [15:14].
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+// AND-ed into a vmcnt_imm value: also wait until no LDS read is outstanding (lgkmcnt 0)
+constexpr int lgkmcnt0_mask() { return ~(15 << 8); }
 
 // fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
 __device__ __forceinline__ bf16_t to_bf16(float f) { return (bf16_t)f; }

@@ -9,22 +9,24 @@
 //
 // Kernels:
 //  * attn_mfma64_kernel (bf16, head_dim 64, B = 64, stripes a multiple of 64 long):
-//    persistent 256-thread workgroups walk units = (work item, segment, head), longest
-//    first; a work item is a query tile against at most 32 of its kept key tiles
-//    (longer rows, the global one, are split and merged by attn_combine_kernel).
-//    Wavefronts 0 and 1 own query halves 0..31 and 32..63 on the even key tiles of the
-//    item, wavefronts 2 and 3 the same queries on the odd ones; the two halves merge
-//    through LDS at the end. S^T = K Q^T and O^T = V^T P^T run on
+//    persistent 512-thread workgroups walk units = (work item, segment, head), longest
+//    first. A work item is a group of up to four query tiles with identical kept-key
+//    lists (one per stripe at the same offset) against that list; every K and V^T
+//    tile is loaded into LDS once for the group. S^T = K Q^T and O^T = V^T P^T run on
 //    v_mfma_f32_32x32x16_bf16, so a lane holds one query's scores (the row max needs
-//    one permlane swap with lane ^ 32) and one query's output column. K and V^T tiles
-//    arrive by direct-to-LDS loads into swizzled two-slot rings, K one tile ahead of
-//    V^T, so each step overlaps the next tile's S MFMAs with the current softmax.
-//    Online softmax in fp32 with exp2, the scale folded into one multiply-add per
-//    score, and the output rescale skipped unless a row max passes its reference
-//    by more than 2^8.
+//    one permlane swap with lane ^ 32) and one query's output column. K tile rows are
+//    stored in a permuted order so that the S^T accumulator already has the layout of
+//    the P^T operand. Online softmax in fp32 with exp2, the scale folded into one
+//    multiply-add per score, and the output rescale skipped unless a row max passes
+//    its reference by more than 2^8.
+//  * attn_d80_kernel: the same work items for head_dim 80.
+//  * attn_short_kernel: short segments (windows, N <= 256), one workgroup per
+//    (segment, head) with the segment's K and V^T in LDS.
+//  * attn_combine_kernel: merges the partial results of rows split over several
+//    work items (none at ViT sizes).
 //  * attn_simt_kernel (fp32 or bf16 storage, any pattern and head_dim <= 128): one
 //    thread per query, keys read through the cache; the exact path for small
-//    configs and for windows.
+//    configs.
 #include <algorithm>
 
 #include "internal.hpp"
@@ -49,6 +51,17 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // probabilities then stay below 2^8, far inside the fp32 and bf16 range.
 constexpr float kRescaleSlack = 8.0f;
 
+// max of three floats; the compiler forms v_max3_f32 (and, unlike inline assembly,
+// inserts the wait states a read of fresh MFMA results needs)
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// key row held by row r of a K tile in LDS: rows 4..7 and 8..11 of each 16-row group
+// are exchanged (an involution)
+__device__ __forceinline__ int kperm16(int r) {
+  const int q = r & 12;
+  return q == 4 ? r + 4 : q == 8 ? r - 4 : r;
+}
+
 // max over lanes l and l ^ 32 (one permlane swap, no LDS round trip)
 __device__ __forceinline__ float max_xor32(float v) {
   const unsigned u = __float_as_uint(v);
@@ -68,13 +81,17 @@ __device__ __forceinline__ float max_xor32(float v) {
 //
 // Item record (two int4): {kb, ke, slot or -1, G | P << 4}, {query tile of each member}.
 //
-// Pipeline of a wavefront (its j-th tile is list entry p + P j): K tiles run one step
-// ahead of V^T tiles. In step j the workgroup issues the direct-to-LDS loads of
-// K_{j+2} and V_{j+1} of every parity (wavefront w loads row group w of each tile), and
-// each wavefront starts S_{j+1} = K_{j+1} Q^T on the matrix cores while it runs the
-// softmax of S_j and O^T += V_j^T P_j^T. Each parity has a two-slot ring for K and for
-// V^T; one barrier per step both publishes the loads of the previous step and retires
-// the slots they overwrite.
+// Pipeline of a wavefront (its j-th tile is list entry p + P j): each parity has a
+// two-slot ring for K and one for V^T. Step j computes S_j = K_j Q^T on the matrix
+// cores from K fragments read into registers in step j - 1 (tile t's in register set
+// t & 1), so the MFMAs start right after the barrier; then the softmax of S_j and
+// O^T += V_j^T P_j^T. Meanwhile the step reads K_{j+1}'s fragments for the next step
+// and V_j's for its own O^T update, and the workgroup issues the direct-to-LDS loads
+// of K_{j+2} and V_{j+1} of every parity (wavefront w loads row group w of each tile)
+// into the slots of K_j and V_{j-1}, whose fragments were read in step j - 1. One
+// barrier per step, after each wavefront's own loads and LDS reads are complete, both
+// publishes K_{j+1} and V_j and retires the slots the step overwrites. (Loading more
+// steps ahead through deeper rings measured slower.)
 static_assert(kAttnItemTiles <= 64, "one key tile per lane");
 __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                                  const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
@@ -97,7 +114,9 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   const bf16_t* q_base = Q + (size_t)sh * n * D;
   const bf16_t* k_base = Kt + (size_t)sh * n * D;
   const bf16_t* v_base = VT + (size_t)sh * D * n_pad;
-  char* ring = smem + (active ? kp : 0) * kParityBytes;
+  constexpr int R = 2;                            // ring slots per parity
+  constexpr int ring_bytes = 2 * R * kTileBytes;  // K ring then V^T ring
+  char* ring = smem + (active ? kp : 0) * ring_bytes;
 
   const int q_local = qh * 32 + (lane & 31);
   const int my_q = tile_start[qt] + q_local;
@@ -118,40 +137,51 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   // Direct-to-LDS tile loads: wavefront w fills row group w (rows 8 w .. 8 w + 7) of
   // every tile; lane L fetches the chunk that the swizzle places at byte 16 L.
   const int krow = 8 * wave + (lane >> 3), kch = (lane & 7) ^ swz_key(8 * wave + (lane >> 3));
-  const int k_src = krow * D + kch * 8, v_src = krow * n_pad + kch * 8;
-  auto issue_k = [&](int j, int s) {  // K tiles of step j (every parity) into K slot s
+  // K tile row r holds key kperm(r): rows 4..7 and 8..11 of every 16-row group are
+  // swapped, so that the S^T accumulator hands lane half h of every 16-key group keys
+  // 8h .. 8h+7 in order -- the layout of the P^T operand -- with no lane exchange
+  const int k_src = kperm16(krow) * D + kch * 8, v_src = krow * n_pad + kch * 8;
+  auto issue_k = [&](int j) {  // K tiles of step j (every parity) into K slot j mod R
+    if (j < 0) return;
+    char* dst = smem + (j & (R - 1)) * kTileBytes + wave * 1024;
     for (int p = 0; p < P; ++p) {
       const int t = p + P * j;
       if (t >= total) break;
       const int k0 = __builtin_amdgcn_readlane(koff, t);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(k_base + (size_t)k0 * D + k_src),
-          (__attribute__((address_space(3))) void*)(smem + p * kParityBytes + s * kTileBytes + wave * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(k_base + (size_t)k0 * D + k_src),
+                                       (__attribute__((address_space(3))) void*)(dst + p * ring_bytes), 16, 0, 0);
     }
   };
-  auto issue_v = [&](int j, int s) {  // V^T tiles of step j (every parity) into V slot s
+  auto issue_v = [&](int j) {  // V^T tiles of step j (every parity) into V slot j mod R
+    if (j < 0) return;
+    char* dst = smem + (R + (j & (R - 1))) * kTileBytes + wave * 1024;
     for (int p = 0; p < P; ++p) {
       const int t = p + P * j;
       if (t >= total) break;
       const int k0 = __builtin_amdgcn_readlane(koff, t);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(v_base + k0 + v_src),
-          (__attribute__((address_space(3))) void*)(smem + p * kParityBytes + (2 + s) * kTileBytes + wave * 1024), 16,
-          0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(v_base + k0 + v_src),
+                                       (__attribute__((address_space(3))) void*)(dst + p * ring_bytes), 16, 0, 0);
     }
+  };
+  // wait until this wavefront's tile loads and LDS reads are complete, then meet the
+  // other wavefronts
+  auto ready = [&]() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkmcnt0_mask());
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
   // fragments of the K tile in slot s (A operand of S^T = K Q^T: two 32-key blocks) and
   // of the V^T tile in slot s (A operand of O^T = V^T P^T: two 32-channel blocks)
-  auto read_k = [&](int s, bf16x8 (&kf)[4][2]) {
-    const char* Ks = ring + s * kTileBytes;
+  auto read_k = [&](int j, bf16x8 (&kf)[4][2]) {
+    const char* Ks = ring + (j & (R - 1)) * kTileBytes;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
         kf[ks][mb] = *reinterpret_cast<const bf16x8*>(Ks + swz(mb * 32 + (lane & 31), ks * 2 + (lane >> 5)));
   };
-  auto read_v = [&](int s, bf16x8 (&vf)[4][2]) {
-    const char* Vs = ring + (2 + s) * kTileBytes;
+  auto read_v = [&](int j, bf16x8 (&vf)[4][2]) {
+    const char* Vs = ring + (R + (j & (R - 1))) * kTileBytes;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -182,11 +212,12 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   // online softmax of S_j (this lane's query: 32 of the tile's 64 scores, the rest in
   // lane ^ 32) into the P^T operand
   auto softmax = [&](const f32x16 (&sc)[2], bf16x8 (&pf)[4]) {
-    float mx = sc[0][0];
+    float t[11];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[mb][e]);
+    for (int i = 0; i < 10; ++i) t[i] = max3f(sc[(3 * i) >> 4][(3 * i) & 15], sc[(3 * i + 1) >> 4][(3 * i + 1) & 15],
+                                             sc[(3 * i + 2) >> 4][(3 * i + 2) & 15]);
+    t[10] = fmaxf(sc[1][14], sc[1][15]);
+    float mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]), max3f(t[6], t[7], max3f(t[8], t[9], t[10])));
     mx = max_xor32(mx);
     const float m_new = fmaxf(m_run, mx * c_log2);
     // rescale only when some row's max passed its reference by more than the slack
@@ -200,30 +231,27 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
         for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
       m_run = m_new;
     }
-    // P^T operand of key group kk (keys 16 kk .. + 15): the accumulator gives lane half
-    // hf keys 4 hf + 0..3 and 8 + 4 hf + 0..3 of the group; the MFMA wants keys
-    // 8 hf + 0..7 (the V^T tile is in natural key order). Swapping the middle pairs of
-    // bf16 pairs between lane halves puts them there.
-    float psum0 = 0.0f, psum1 = 0.0f;
+    // P^T operand of key group kk (keys 16 kk .. + 15): with the permuted K rows,
+    // accumulator elements 8 (kk & 1) .. + 7 of block kk / 2 are keys 8 h .. 8 h + 7 of
+    // the group for lane half h, in order
+    float ps[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 v;
+      float a = 0.0f, b = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + e], c_log2, -m_run));
         if (e & 1)
-          psum1 += p;
+          b += p;
         else
-          psum0 += p;
+          a += p;
         v[e] = to_bf16(p);
       }
-      u32x4 r = __builtin_bit_cast(u32x4, v);
-      const auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
-      const auto s13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
-      r = u32x4{s02[0], s13[0], s02[1], s13[1]};
-      pf[kk] = __builtin_bit_cast(bf16x8, r);
+      ps[kk] = a + b;
+      pf[kk] = v;
     }
-    l_run += psum0 + psum1;
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
   // O^T += V^T P^T over four 16-key steps
   auto pv = [&](const bf16x8 (&vf)[4][2], const bf16x8 (&pf)[4]) {
@@ -236,45 +264,29 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
 
   const int nj = active ? (total - kp + P - 1) / P : 0;  // tiles of this wavefront's parity
   const int niter = (total + P - 1) / P;                  // steps (parity 0 has the most)
-  f32x16 s0[2], s1[2];
-  issue_k(0, 0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  issue_k(1, 1);
-  issue_v(0, 0);
-  if (nj > 0) {
-    bf16x8 kf[4][2];
-    read_k(0, kf);
-    scores(kf, s0);
-  }
-  // step j: S_j is in (j even ? s0 : s1); V_j and K_{j+1} were issued in step j - 1.
-  // All fragment reads of the step are issued first; S_{j+1} and the softmax of S_j
-  // share one block so their MFMA and VALU work can interleave. Every wavefront takes
-  // every step's barrier; it computes while j < nj.
-  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue_k(j + 2, j & 1);
-    issue_v(j + 1, (j + 1) & 1);
-    bf16x8 vf[4][2], pf[4];
-    if (j + 1 < nj) {
-      bf16x8 kf[4][2];
-      read_k((j + 1) & 1, kf);
-      read_v(j & 1, vf);
-      scores(kf, nxt);
-      softmax(cur, pf);
-      pv(vf, pf);
-    } else if (j < nj) {
-      read_v(j & 1, vf);
-      softmax(cur, pf);
+  f32x16 sacc[2];
+  bf16x8 kb2[2][4][2];
+  issue_k(0);
+  issue_k(1);
+  issue_v(0);
+  ready();
+  if (nj > 0) read_k(0, kb2[0]);
+  auto step = [&](int j, bf16x8 (&k_use)[4][2], bf16x8 (&k_next)[4][2]) {
+    ready();
+    issue_k(j + 2);
+    issue_v(j + 1);
+    if (j + 1 < nj) read_k(j + 1, k_next);
+    if (j < nj) {
+      bf16x8 vf[4][2], pf[4];
+      read_v(j, vf);
+      scores(k_use, sacc);
+      softmax(sacc, pf);
       pv(vf, pf);
     }
   };
   for (int j = 0; j < niter; j += 2) {
-    step(j, s0, s1);
-    if (j + 1 < niter) step(j + 1, s1, s0);
+    step(j, kb2[0], kb2[1]);
+    if (j + 1 < niter) step(j + 1, kb2[1], kb2[0]);
   }
   // every wavefront is done with the rings before the exchange area reuses them
   __syncthreads();
