@@ -5,21 +5,29 @@
 // weights). bf16 operands run on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16,
 // fp32 accumulation); the fp32 path is a plain SIMT kernel for small exact checks.
 //
-// bf16 kernel: BM x BN output tile (128 x 64 or 64 x 64) per 256-thread workgroup,
-// K step 64, four wavefronts in a 2 x 2 layout each owning a (BM/2) x (BN/2) block of
-// 32 x 32 MFMA tiles. A and W tiles go straight from global memory into LDS
-// (global_load_lds_dwordx4, no register staging) through an ST-stage ring of swizzled
-// 128-byte rows, with an explicit vmcnt wait and one barrier per K step; ST - 1 steps
-// of loads stay in flight while one step multiplies. The tile grid is cut into one
-// rectangle per XCD (each XCD's L2 then holds only the A and W rows it needs).
+// bf16 kernel: one BM x BN output tile per 256-thread workgroup, K step 64, four
+// wavefronts in a 2 x 2 layout, each owning a (BM/2) x (BN/2) block of 32 x 32 MFMA
+// tiles. Tiles are large (up to 256 x 192) because an MI355X CU gets about 64 bytes
+// per clock from its XCD's L2 on average: a 128 x 64 tile needs 94 bytes per clock
+// at the matrix-core rate, a 192 x 128 tile 53. The host picks, per product, the tile
+// shape whose grid fills the 256 CUs in the fewest rounds (see pick_tile).
 //
-// Epilogue: the fp32 tile is staged in LDS, then written out as 16-byte chunks along
-// the destination's contiguous axis -- 8 channels of one token for q, k, the MLP
-// hidden activation and the residual stream, 8 tokens of one channel for the
-// transposed V the attention kernel reads -- so every store is a full vector store
-// and the index decoding (token -> segment, column -> head) runs once per chunk.
-// (Storing straight from the accumulators, 4-element pieces of 32 rows per
-// instruction, measured slower: four times the memory transactions.)
+// A and W tiles go straight from global memory into LDS (global_load_lds_dwordx4, no
+// register staging) through an ST-slot ring of swizzled 128-byte rows; every slot is
+// filled before the first step, and a slot is refilled with step kt + ST as soon as
+// step kt has been read out of it. The operand fragments of the next 16-wide K slice
+// are read from LDS while the MFMAs of the current one run, across step boundaries
+// too, so one wavefront per SIMD keeps its matrix core fed.
+//
+// Epilogue straight from the accumulators: the MFMA operands are ordered so that a
+// lane's accumulator holds one output row with four consecutive columns per group of
+// four registers; one v_permlane32_swap per register pair then gives every lane eight
+// consecutive columns of one row (eight consecutive tokens of one channel for the
+// transposed V tiles), written as one 16-byte (bf16) or 32-byte (fp32) chunk. No LDS
+// staging, no barrier after the K loop.
+#include <algorithm>
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace sparsesam {
@@ -41,18 +49,6 @@ __device__ __forceinline__ void store8<float>(float* dst, const float* v) {
   *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
-// Batched epilogues. Each thread of a tile owns a fixed 8-column chunk c..c+7 of ITER
-// rows (row-major destinations) or a fixed 8-token chunk of ITER channels (V^T). What
-// the epilogue reads from global memory -- the bias chunk, the residual rows' source
-// indices -- is requested before the K loop (row_prefetch / col_prefetch), and the
-// residual stream is read for all ITER rows before any of them is written, so the
-// latency of those loads is paid once per tile instead of once per row in sequence.
-template <int ITER>
-struct RowPre {
-  float b[8];
-  int raw[ITER];
-};
-
 __device__ __forceinline__ void load_bias8(const float* bias, int c, int N, float* b) {
   if (c + 8 <= N) {
     const f32x4 b0 = *reinterpret_cast<const f32x4*>(bias + c);
@@ -68,8 +64,14 @@ __device__ __forceinline__ void load_bias8(const float* bias, int c, int N, floa
   }
 }
 
+// Epilogue interface. rows(): a lane holds MR rows r[i] and NC column chunks c[j]
+// (eight consecutive columns c[j] .. c[j] + 7, c[j] % 8 == 0), values v[i][j][0..7];
+// rows >= M and columns >= N are not stored. cols(): the transposed form, NCOL columns
+// c[j] and RC row chunks r[i] (eight consecutive rows), values v[j][i][0..7].
+// col_tile(n0): the tile starting at column n0 is written along rows (cols()).
+
 // q, k [seg, H, N, D] and V^T [seg, H, D, N_pad] from the columns of the QKV product.
-// Token r of the stripe-sorted rows is slot p of segment seg; column c is channel d of
+// Row r of the stripe-sorted rows is slot p of segment seg; column c is channel d of
 // head h of part `which` (q, k, v). Divisions by n, C and D use FastDiv.
 template <typename T>
 struct QKVStore {
@@ -95,88 +97,64 @@ struct QKVStore {
   }
   // Tiles whose columns are all V columns are written along tokens.
   __device__ __forceinline__ bool col_tile(int c0) const { return c0 >= 2 * C; }
-  // Eight channels c..c+7 of token r (c % 8 == 0 and D % 8 == 0: one head, one part).
-  __device__ __forceinline__ void row8(int r, int c, const float* v) const {
-    const int which = f_C.div(c);
-    if (which >= 2) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) elem(r, c + i, v[i]);
-      return;
-    }
-    const int cc = c - which * C;
-    const int h = f_D.div(cc), d = cc - h * D;
-    const int seg = f_n.div(r), p = r - seg * n;
-    const size_t sh = (size_t)seg * heads + h;
-    float w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = v[i] + bias[c + i];
-    T* base = which == 0 ? q : k;
-    store8<T>(base + (sh * n + p) * (size_t)D + d, w);
-  }
-  // Eight tokens r..r+7 (r % 8 == 0, count of them below M) of channel c.
-  __device__ __forceinline__ void col8(int r, int c, const float* v, int count) const {
-    const int seg = f_n.div(r), p = r - seg * n;
-    const int which = f_C.div(c);
-    if (which == 2 && count == 8 && p + 8 <= n && (p & 7) == 0) {
-      const int cc = c - 2 * C;
-      const int h = f_D.div(cc), d = cc - h * D;
-      const size_t sh = (size_t)seg * heads + h;
-      const float b = bias[c];
-      float w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = v[i] + b;
-      store8<T>(vt + (sh * D + d) * (size_t)n_pad + p, w);
-      return;
-    }
-    for (int i = 0; i < count; ++i) elem(r + i, c, v[i]);
-  }
 
-  template <int ITER>
-  __device__ __forceinline__ void row_prefetch(RowPre<ITER>& pre, const int*, int c, int, int N) const {
-    if (c < N) load_bias8(bias, c, N, pre.b);
-  }
-  template <int ITER>
-  __device__ __forceinline__ void row_store(const RowPre<ITER>& pre, const int* ms, int c, const float (*v)[8], int M,
-                                            int N) const {
-    if (c >= N) return;
-    const int which = f_C.div(c);
-    if (c + 8 > N || which >= 2) {  // not a whole chunk of one q / k head: element by element
+  template <int MR, int NC>
+  __device__ __forceinline__ void rows(const int (&r)[MR], const int (&c)[NC], float (&v)[MR][NC][8], int M,
+                                       int N) const {
 #pragma unroll
-      for (int it = 0; it < ITER; ++it)
-        if (ms[it] < M)
-          for (int i = 0; i < 8 && c + i < N; ++i) elem(ms[it], c + i, v[it][i]);
-      return;
-    }
-    const int cc = c - which * C;
-    const int h = f_D.div(cc), d = cc - h * D;
-    T* base = (which == 0 ? q : k) + (size_t)h * n * D + d;
+    for (int j = 0; j < NC; ++j) {
+      if (c[j] >= N) continue;
+      const int which = f_C.div(c[j]);
+      if (c[j] + 8 > N || which >= 2) {  // not a whole chunk of one q / k head: element by element
 #pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int m = ms[it];
-      if (m >= M) continue;
-      const int seg = f_n.div(m), p = m - seg * n;
-      float w[8];
+        for (int i = 0; i < MR; ++i)
+          if (r[i] < M)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = v[it][i] + pre.b[i];
-      store8<T>(base + ((size_t)seg * heads * n + p) * (size_t)D, w);
-    }
-  }
-  __device__ __forceinline__ float col_bias(int c, int N) const { return c < N ? bias[c] : 0.0f; }
-  // Eight tokens r..r+7 of channel c with the channel's bias b already loaded.
-  __device__ __forceinline__ void col8b(int r, int c, const float* v, int count, float b) const {
-    const int seg = f_n.div(r), p = r - seg * n;
-    const int which = f_C.div(c);
-    if (which == 2 && count == 8 && p + 8 <= n && (p & 7) == 0) {
-      const int cc = c - 2 * C;
+            for (int e = 0; e < 8; ++e)
+              if (c[j] + e < N) elem(r[i], c[j] + e, v[i][j][e]);
+        continue;
+      }
+      const int cc = c[j] - which * C;
       const int h = f_D.div(cc), d = cc - h * D;
-      const size_t sh = (size_t)seg * heads + h;
-      float w[8];
+      T* base = (which == 0 ? q : k) + (size_t)h * n * D + d;
+      float b[8];
+      load_bias8(bias, c[j], N, b);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = v[i] + b;
-      store8<T>(vt + (sh * D + d) * (size_t)n_pad + p, w);
-      return;
+      for (int i = 0; i < MR; ++i) {
+        if (r[i] >= M) continue;
+        const int seg = f_n.div(r[i]), p = r[i] - seg * n;
+        float w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = v[i][j][e] + b[e];
+        store8<T>(base + ((size_t)seg * heads * n + p) * (size_t)D, w);
+      }
     }
-    for (int i = 0; i < count; ++i) elem(r + i, c, v[i]);
+  }
+  template <int NCOL, int RC>
+  __device__ __forceinline__ void cols(const int (&c)[NCOL], const int (&r)[RC], float (&v)[NCOL][RC][8], int M,
+                                       int N) const {
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j) {
+      if (c[j] >= N) continue;
+      const int cc = c[j] - 2 * C;
+      const int h = f_D.div(cc), d = cc - h * D;
+      const float b = bias[c[j]];
+#pragma unroll
+      for (int i = 0; i < RC; ++i) {
+        if (r[i] >= M) continue;
+        const int seg = f_n.div(r[i]), p = r[i] - seg * n;
+        if (r[i] + 8 <= M && p + 8 <= n && (p & 7) == 0) {
+          float w[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] = v[j][i][e] + b;
+          store8<T>(vt + (((size_t)seg * heads + h) * D + d) * (size_t)n_pad + p, w);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (r[i] + e < M) elem(r[i] + e, c[j], v[j][i][e]);
+        }
+      }
+    }
   }
 };
 
@@ -190,39 +168,41 @@ struct GeluStore {
     out[(size_t)r * ld + c] = from_f32<T>(gelu_erf(v + bias[c]));
   }
   __device__ __forceinline__ bool col_tile(int) const { return false; }
-  __device__ __forceinline__ void row8(int r, int c, const float* v) const {
-    float w[8];
+  template <int MR, int NC>
+  __device__ __forceinline__ void rows(const int (&r)[MR], const int (&c)[NC], float (&v)[MR][NC][8], int M,
+                                       int N) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = gelu_erf(v[i] + bias[c + i]);
-    store8<T>(out + (size_t)r * ld + c, w);
-  }
-  __device__ __forceinline__ void col8(int r, int c, const float* v, int count) const {
-    for (int i = 0; i < count; ++i) elem(r + i, c, v[i]);
-  }
-  template <int ITER>
-  __device__ __forceinline__ void row_prefetch(RowPre<ITER>& pre, const int*, int c, int, int N) const {
-    if (c < N) load_bias8(bias, c, N, pre.b);
-  }
-  template <int ITER>
-  __device__ __forceinline__ void row_store(const RowPre<ITER>& pre, const int* ms, int c, const float (*v)[8], int M,
-                                            int N) const {
-    if (c >= N) return;
+    for (int j = 0; j < NC; ++j) {
+      if (c[j] >= N) continue;
+      float b[8];
+      load_bias8(bias, c[j], N, b);
 #pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int m = ms[it];
-      if (m >= M) continue;
-      if (c + 8 <= N) {
-        float w[8];
+      for (int i = 0; i < MR; ++i) {
+        if (r[i] >= M) continue;
+        if (c[j] + 8 <= N) {
+          float w[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = gelu_erf(v[it][i] + pre.b[i]);
-        store8<T>(out + (size_t)m * ld + c, w);
-      } else {
-        for (int i = 0; c + i < N; ++i) elem(m, c + i, v[it][i]);
+          for (int e = 0; e < 8; ++e) w[e] = gelu_erf(v[i][j][e] + b[e]);
+          store8<T>(out + (size_t)r[i] * ld + c[j], w);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (c[j] + e < N) elem(r[i], c[j] + e, v[i][j][e]);
+        }
       }
     }
   }
-  __device__ __forceinline__ float col_bias(int, int) const { return 0.0f; }
-  __device__ __forceinline__ void col8b(int r, int c, const float* v, int count, float) const { col8(r, c, v, count); }
+  template <int NCOL, int RC>
+  __device__ __forceinline__ void cols(const int (&c)[NCOL], const int (&r)[RC], float (&v)[NCOL][RC][8], int M,
+                                       int N) const {
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j)
+#pragma unroll
+      for (int i = 0; i < RC; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c[j] < N && r[i] + e < M) elem(r[i] + e, c[j], v[j][i][e]);
+  }
 };
 
 // Residual update of the fp32 stream: x[dst(r), c] += acc + bias, where dst maps a
@@ -247,117 +227,140 @@ struct ResidualAdd {
     *px = *px + (v + bias[c]);
   }
   __device__ __forceinline__ bool col_tile(int) const { return false; }
-  __device__ __forceinline__ void row8(int r, int c, const float* v) const {
-    const int row = dst_row(r);
-    if (row < 0 || row >= x_rows) return;
-    f32x4* px = reinterpret_cast<f32x4*>(x + (size_t)row * ldx + c);
-    f32x4 a = px[0], b = px[1];
+  // destination rows, then every chunk's current values, then the updates: the loads
+  // of a lane's whole tile part are in flight together
+  template <int MR, int NC>
+  __device__ __forceinline__ void rows(const int (&r)[MR], const int (&c)[NC], float (&v)[MR][NC][8], int M,
+                                       int N) const {
+    int raw[MR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = a[i] + (v[i] + bias[c + i]);
-      b[i] = b[i] + (v[4 + i] + bias[c + 4 + i]);
-    }
-    px[0] = a;
-    px[1] = b;
-  }
-  __device__ __forceinline__ void col8(int r, int c, const float* v, int count) const {
-    for (int i = 0; i < count; ++i) elem(r + i, c, v[i]);
-  }
-  template <int ITER>
-  __device__ __forceinline__ void row_prefetch(RowPre<ITER>& pre, const int* ms, int c, int M, int N) const {
-    if (c < N) load_bias8(bias, c, N, pre.b);
+    for (int i = 0; i < MR; ++i) raw[i] = r[i] < M ? (list ? list[r[i]] : perm[r[i]]) : -1;
+    long long off[MR];
 #pragma unroll
-    for (int it = 0; it < ITER; ++it) pre.raw[it] = ms[it] < M ? (list ? list[ms[it]] : perm[ms[it]]) : -1;
-  }
-  template <int ITER>
-  __device__ __forceinline__ void row_store(const RowPre<ITER>& pre, const int* ms, int c, const float (*v)[8], int M,
-                                            int N) const {
-    if (c >= N) return;
-    if (c + 8 > N) {
-#pragma unroll
-      for (int it = 0; it < ITER; ++it)
-        if (ms[it] < M)
-          for (int i = 0; c + i < N; ++i) elem(ms[it], c + i, v[it][i]);
-      return;
-    }
-    // destination rows, then every row's current values, then the updates
-    long long off[ITER];
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
+    for (int i = 0; i < MR; ++i) {
       int row = -1;
-      if (ms[it] < M && pre.raw[it] >= 0) row = list ? pre.raw[it] : map.row_of(map.seg_of(ms[it]), pre.raw[it]);
-      off[it] = (row < 0 || row >= x_rows) ? -1 : (long long)row * ldx + c;
+      if (raw[i] >= 0) row = list ? raw[i] : map.row_of(map.seg_of(r[i]), raw[i]);
+      off[i] = (row < 0 || row >= x_rows) ? -1 : (long long)row * ldx;
     }
-    f32x4 cur[ITER][2];
 #pragma unroll
-    for (int it = 0; it < ITER; ++it)
-      if (off[it] >= 0) {
-        cur[it][0] = *reinterpret_cast<const f32x4*>(x + off[it]);
-        cur[it][1] = *reinterpret_cast<const f32x4*>(x + off[it] + 4);
+    for (int j = 0; j < NC; ++j) {
+      if (c[j] >= N) continue;
+      if (c[j] + 8 > N) {
+#pragma unroll
+        for (int i = 0; i < MR; ++i)
+          if (off[i] >= 0)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (c[j] + e < N) x[off[i] + c[j] + e] += v[i][j][e] + bias[c[j] + e];
+        continue;
       }
+      float b[8];
+      load_bias8(bias, c[j], N, b);
+      f32x4 cur[MR][2];
 #pragma unroll
-    for (int it = 0; it < ITER; ++it)
-      if (off[it] >= 0) {
-        f32x4 a = cur[it][0], b = cur[it][1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a[i] = a[i] + (v[it][i] + pre.b[i]);
-          b[i] = b[i] + (v[it][4 + i] + pre.b[4 + i]);
+      for (int i = 0; i < MR; ++i)
+        if (off[i] >= 0) {
+          cur[i][0] = *reinterpret_cast<const f32x4*>(x + off[i] + c[j]);
+          cur[i][1] = *reinterpret_cast<const f32x4*>(x + off[i] + c[j] + 4);
         }
-        *reinterpret_cast<f32x4*>(x + off[it]) = a;
-        *reinterpret_cast<f32x4*>(x + off[it] + 4) = b;
-      }
+#pragma unroll
+      for (int i = 0; i < MR; ++i)
+        if (off[i] >= 0) {
+          f32x4 a = cur[i][0], d = cur[i][1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = a[e] + (v[i][j][e] + b[e]);
+            d[e] = d[e] + (v[i][j][4 + e] + b[4 + e]);
+          }
+          *reinterpret_cast<f32x4*>(x + off[i] + c[j]) = a;
+          *reinterpret_cast<f32x4*>(x + off[i] + c[j] + 4) = d;
+        }
+    }
   }
-  __device__ __forceinline__ float col_bias(int, int) const { return 0.0f; }
-  __device__ __forceinline__ void col8b(int r, int c, const float* v, int count, float) const { col8(r, c, v, count); }
+  template <int NCOL, int RC>
+  __device__ __forceinline__ void cols(const int (&c)[NCOL], const int (&r)[RC], float (&v)[NCOL][RC][8], int M,
+                                       int N) const {
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j)
+#pragma unroll
+      for (int i = 0; i < RC; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c[j] < N && r[i] + e < M) elem(r[i] + e, c[j], v[j][i][e]);
+  }
 };
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM
 
 constexpr int BK = 64;  // K step: one 128-byte row of bf16 per tile row
 
-// ST: LDS pipeline depth (ST - 1 K steps in flight while one is multiplied).
+// ST: LDS ring slots (up to ST - 1 K steps in flight while one is multiplied).
 template <int BM, int BN, int ST>
 struct Tile {
   static constexpr int WM = BM / 2, WN = BN / 2;  // wave block (2 x 2 waves)
   static constexpr int MI = WM / 32, NI = WN / 32;
-  static constexpr int GROUPS = (BM + BN) / 8;     // 1 KiB groups (8 rows x 128 B) per stage
-  static constexpr int LOADS = GROUPS / 4;         // direct-to-LDS loads per wave per stage
+  static constexpr int LOADS = (BM + BN) / 32;     // 1 KiB groups (8 rows x 128 B) per wave per step
   static constexpr int STAGE_BYTES = (BM + BN) * 128;
-  static constexpr int CT_LD = BN + 4;             // fp32 epilogue tile row stride
-  static constexpr int CTT_LD = BM + 4;            // ... of the transposed tile (V^T tiles)
-  static constexpr int CT_BYTES = (BM * CT_LD > BN * CTT_LD ? BM * CT_LD : BN * CTT_LD) * 4;
-  static constexpr int PIPE_BYTES = ST * STAGE_BYTES;
-  static constexpr int LDS_BYTES = PIPE_BYTES > CT_BYTES ? PIPE_BYTES : CT_BYTES;
+  static constexpr int LDS_BYTES = ST * STAGE_BYTES;
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && (BM + BN) % 32 == 0, "tile shape");
+  static_assert(ST >= 2 && ST <= 8, "ring depth");
 };
 
 // Tiles live in LDS in the swizzled 128-byte-row layout of swz() (common.hpp).
 
-// wait until at most n of this wavefront's tile loads are in flight, then meet the
-// other wavefronts; the empty asm keeps the compiler from moving LDS reads above it
+// Wait until at most n of this wavefront's tile loads are in flight and its LDS reads
+// have returned, then meet the other wavefronts; the empty asm keeps the compiler from
+// moving LDS reads above the barrier.
 template <int N>
-__device__ __forceinline__ void stage_ready() {
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+__device__ __forceinline__ void ring_sync() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N) & lgkmcnt0_mask());
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+template <int LOADS, int ST>
+__device__ __forceinline__ void ring_sync_n(int later) {  // later: whole steps allowed in flight
+  static_assert(ST <= 8, "ring depth");
+  switch (later) {
+    case 0: ring_sync<0>(); break;
+    case 1: ring_sync<(ST > 1 ? LOADS : 0)>(); break;
+    case 2: ring_sync<(ST > 2 ? 2 * LOADS : 0)>(); break;
+    case 3: ring_sync<(ST > 3 ? 3 * LOADS : 0)>(); break;
+    case 4: ring_sync<(ST > 4 ? 4 * LOADS : 0)>(); break;
+    case 5: ring_sync<(ST > 5 ? 5 * LOADS : 0)>(); break;
+    default: ring_sync<(ST > 6 ? 6 * LOADS : 0)>(); break;
+  }
+}
 
-// The main loop and epilogue of one tile. TR: the tile's columns are written along
-// tokens (V^T), so the MFMA operands are swapped and the block accumulates C^T.
+// Eight consecutive outputs per lane from a 32 x 32 accumulator. A lane holds outer
+// index l % 32 and inner indices 8 g + 4 (l / 32) + t for register 4 g + t; swapping
+// groups 2p + 1 of the low half with groups 2p of the high half gives the low lanes
+// inner 16p .. 16p + 7 and the high lanes 16p + 8 .. 16p + 15.
+__device__ __forceinline__ void acc_chunk(const f32x16& a, int p, float* out) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[8 * p + t]), __float_as_uint(a[8 * p + 4 + t]),
+                                                    false, false);
+    out[t] = __uint_as_float(s[0]);
+    out[4 + t] = __uint_as_float(s[1]);
+  }
+}
+
+// The K loop and epilogue of one tile. TR: the tile's columns are written along rows
+// (V^T), so the accumulators hold C (lane = column) instead of C^T (lane = row).
 template <int BM, int BN, int ST, bool TR, class Epi>
 __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, int M,
                                                int N, int K, const Epi& epi, char* smem, int m0, int n0) {
   using TL = Tile<BM, BN, ST>;
-  constexpr int kStages = ST;
-  const int tid = threadIdx.x, lane = tid & 63;
+  constexpr int MI = TL::MI, NI = TL::NI;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets stay scalar
   const int wm = wave >> 1, wn = wave & 1;
 
-  f32x16 acc[TL::MI][TL::NI];
+  f32x16 acc[MI][NI];
 #pragma unroll
-  for (int i = 0; i < TL::MI; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < TL::NI; ++j)
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
@@ -382,126 +385,167 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
   }
   const char* a_base = reinterpret_cast<const char*>(A + (size_t)m0 * K);
   const char* w_base = reinterpret_cast<const char*>(W + (size_t)n0 * K);
-  auto issue = [&](int kt) {
-    char* base = smem + (kt % kStages) * TL::STAGE_BYTES;
+  // direct-to-LDS loads [i0, i1) of this wavefront's groups for step kt into `slot`
+  auto issue = [&](int kt, int slot, int i0, int i1) {
+    char* base = smem + slot * TL::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < TL::LOADS; ++i) {
+      if (i < i0 || i >= i1) continue;
       const int g = wave + 4 * i;
       const char* src = (g < BM / 8 ? a_base : w_base) + kt * (BK * 2);
       __builtin_amdgcn_global_load_lds((const void*)(src + voff[i]),
                                        (__attribute__((address_space(3))) void*)(base + g * 1024), 16, 0, 0);
     }
   };
-
-  // epilogue inputs requested now, consumed after the K loop (see RowPre)
-  constexpr int CPR = BN / 8, ITER = BM * CPR / 256;  // row path: chunks per row, chunks per thread
-  constexpr int RPC = BM / 8, ITERT = BN * RPC / 256;  // V^T path: chunks per channel, per thread
-  static_assert(256 % CPR == 0 && 256 % RPC == 0, "fixed chunk per thread");
-  const int ec = n0 + (tid % CPR) * 8;
-  int ems[ITER];
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) ems[it] = m0 + tid / CPR + it * (256 / CPR);
-  RowPre<ITER> rpre;
-  const int tm = m0 + (tid % RPC) * 8;
-  float tb[ITERT];
-  if constexpr (!TR) {
-    epi.row_prefetch(rpre, ems, ec, M, N);
-  } else {
-#pragma unroll
-    for (int it = 0; it < ITERT; ++it) tb[it] = epi.col_bias(n0 + tid / RPC + it * (256 / RPC), N);
-  }
-
   const int nk = K / BK;
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt must be complete; the later stages already issued (at most
-    // kStages - 2 of them) may stay in flight
-    static_assert(kStages >= 2 && kStages <= 5, "pipeline depth");
-    const int later = min(kStages - 2, nk - 1 - kt);
-    if (later <= 0)
-      stage_ready<0>();
-    else if (later == 1)
-      stage_ready<TL::LOADS>();
-    else if (later == 2)
-      stage_ready<2 * TL::LOADS>();
-    else
-      stage_ready<3 * TL::LOADS>();
-    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);  // into the buffer read last step
-    const char* As = smem + (kt % kStages) * TL::STAGE_BYTES;
+  // Fragments of 16-wide K slice ks of the step held in `slot`, one register set per
+  // slice.
+  bf16x8 fa[BK / 16][MI], fb[BK / 16][NI];
+  auto read = [&](int slot, int ks) {
+    const char* As = smem + slot * TL::STAGE_BYTES;
     const char* Bs = As + BM * 128;
-    // every fragment of the K step is requested before the first MFMA
-    bf16x8 af[BK / 16][TL::MI], bfr[BK / 16][TL::NI];
+    const int c = ks * 2 + hi;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = ks * 2 + (lane >> 5);
+    for (int i = 0; i < MI; ++i)
+      fa[ks][i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * TL::WM + i * 32 + l32, c));
 #pragma unroll
-      for (int i = 0; i < TL::MI; ++i)
-        af[ks][i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * TL::WM + i * 32 + (lane & 31), c));
+    for (int j = 0; j < NI; ++j)
+      fb[ks][j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * TL::WN + j * 32 + l32, c));
+  };
+  // MFMA q (in (i, j) order) of slice ks
+  auto mfma = [&](int ks, int q) {
+    const int i = q / NI, j = q % NI;
+    if constexpr (!TR)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+  };
+  constexpr int QN = MI * NI;
+  constexpr int Q1 = QN >= 4 ? 2 : 1;  // MFMAs issued ahead of a group's reads / barrier
+  constexpr int SPOTS = 2 * (QN - Q1);  // places for the step's direct loads (slices 0, 1)
+  // One K step kt. Every MFMA of the step is issued between the other instructions, so
+  // the matrix core stays busy while the wavefront feeds LDS and its registers:
+  //  - slice 0: the reads of slice 1, then the direct loads of step kt + ST - 1 (into
+  //    the slot step kt - 1 used) spread one or two per MFMA;
+  //  - slice 1: the reads of slices 2 and 3 (the whole step is then in registers), the
+  //    rest of the direct loads;
+  //  - slice 2: the ring barrier (step kt + 1 landed; every wavefront done with step
+  //    kt), then the reads of slice 0 of step kt + 1;
+  //  - slice 3: MFMAs only.
+  // sched_barrier keeps the compiler from regrouping the pieces.
+  auto step = [&](auto dma_tag, int kt, int later) {
+    constexpr bool DMA = decltype(dma_tag)::value;
+    const int slot = kt % ST;
+    const int dslot = (kt + ST - 1) % ST;
 #pragma unroll
-      for (int j = 0; j < TL::NI; ++j)
-        bfr[ks][j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * TL::WN + j * 32 + (lane & 31), c));
-    }
+    for (int g = 0; g < 2; ++g) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+      for (int q = 0; q < Q1; ++q) mfma(g, q);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g == 0) {
+        read(slot, 1);
+        if constexpr (DMA && SPOTS == 0) issue(kt + ST - 1, dslot, 0, TL::LOADS);
+      } else {
+        read(slot, 2);
+        read(slot, 3);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < TL::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::NI; ++j) {
-          if constexpr (!TR)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks][j], af[ks][i], acc[i][j], 0, 0, 0);
+      for (int q = Q1; q < QN; ++q) {
+        mfma(g, q);
+        if constexpr (DMA) {
+          const int spot = g * (QN - Q1) + (q - Q1);
+          const int i0 = spot * TL::LOADS / (SPOTS > 0 ? SPOTS : 1), i1 = (spot + 1) * TL::LOADS / (SPOTS > 0 ? SPOTS : 1);
+          if (i1 > i0) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue(kt + ST - 1, dslot, i0, i1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
+      }
     }
-  }
-  // every wavefront is done reading the pipeline buffers before they become the
-  // epilogue tile
-  __syncthreads();
+#pragma unroll
+    for (int q = 0; q < Q1; ++q) mfma(2, q);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      // step kt + 1 must have landed (`later` steps after it may stay in flight) and
+      // every wavefront must be done reading step kt before its slot is refilled
+      if constexpr (DMA)
+        ring_sync<(ST - 2) * TL::LOADS>();
+      else
+        ring_sync_n<TL::LOADS, ST>(later);
+      read((kt + 1) % ST, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = Q1; q < QN; ++q) mfma(2, q);
+#pragma unroll
+    for (int q = 0; q < QN; ++q) mfma(3, q);
+  };
 
-  // Stage the fp32 tile in LDS. A lane holds one column of four row quads per 32 x 32
-  // block; on transposed tiles the block holds C^T, and the tile is staged as C^T
-  // ([BN][BM + 4]) so both the stores here and the chunk reads below run along rows.
-  float* ct = reinterpret_cast<float*>(smem);
+  // slots 0 .. ST - 2 are filled up front; step kt fills slot (kt + ST - 1) % ST
 #pragma unroll
-  for (int i = 0; i < TL::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < TL::NI; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int inner = (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        const int outer = lane & 31;
-        if constexpr (!TR)
-          ct[(wm * TL::WM + i * 32 + inner) * TL::CT_LD + wn * TL::WN + j * 32 + outer] = acc[i][j][e];
-        else
-          ct[(wn * TL::WN + j * 32 + inner) * TL::CTT_LD + wm * TL::WM + i * 32 + outer] = acc[i][j][e];
-      }
-  __syncthreads();
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nk) issue(s, s, 0, TL::LOADS);
+  ring_sync_n<TL::LOADS, ST>(min(ST - 2, nk - 1));
+  read(0, 0);
+  int kt = 0;
+  for (; kt + ST - 1 < nk; ++kt) step(std::true_type{}, kt, ST - 2);
+  for (; kt < nk; ++kt) step(std::false_type{}, kt, min(ST - 2, nk - 2 - kt));
+
   if constexpr (!TR) {
-    float v[ITER][8];
+    // Staged through LDS, one 32-row block per wavefront at a time: the accumulators
+    // (lane = row l32, four consecutive columns per register group) go into a private
+    // [32][WN + 4] fp32 area, then every lane takes an eight-column chunk of R rows in
+    // row-contiguous lane order, so a store instruction covers 64 / CPR whole row
+    // segments (full cache lines) instead of 32 short pieces.
+    constexpr int SLD = TL::WN + 4;
+    constexpr int CPR = TL::WN / 8, RPI = 64 / CPR, R = 32 / RPI;
+    static_assert(64 % CPR == 0 && 32 % RPI == 0, "staging layout");
+    __syncthreads();  // every wavefront is done reading the ring
+    float* stg = reinterpret_cast<float*>(smem) + wave * 32 * SLD;
+    const int ch = lane % CPR, r0 = lane / CPR;
+    int cc[1] = {n0 + wn * TL::WN + ch * 8};
 #pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const float* src = ct + (ems[it] - m0) * TL::CT_LD + (ec - n0);
-      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[it][i] = a[i];
-        v[it][4 + i] = b[i];
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(stg + l32 * SLD + j * 32 + 8 * g + 4 * hi) =
+              f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+      int r[R];
+      float v[R][1][8];
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const int row = r0 + t * RPI;
+        r[t] = m0 + wm * TL::WM + i * 32 + row;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(stg + row * SLD + ch * 8);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(stg + row * SLD + ch * 8 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[t][0][e] = a[e];
+          v[t][0][4 + e] = b[e];
+        }
       }
+      epi.rows(r, cc, v, M, N);
     }
-    epi.row_store(rpre, ems, ec, v, M, N);
   } else {
+    // lane: column wn*WN + 32j + l32; rows wm*WM + 32i + 16p + 8hi .. + 7
+    int r[MI * 2];
 #pragma unroll
-    for (int it = 0; it < ITERT; ++it) {
-      const int n = n0 + tid / RPC + it * (256 / RPC);
-      if (tm >= M || n >= N) continue;
-      const float* src = ct + (n - n0) * TL::CTT_LD + (tm - m0);
-      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
-      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      epi.col8b(tm, n, v, min(8, M - tm), tb[it]);
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) r[i * 2 + p] = m0 + wm * TL::WM + i * 32 + 16 * p + 8 * hi;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int c[1] = {n0 + wn * TL::WN + j * 32 + l32};
+      float v[1][MI * 2][8];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) acc_chunk(acc[i][j], p, v[0][i * 2 + p]);
+      epi.cols(c, r, v, M, N);
     }
   }
 }
@@ -605,20 +649,45 @@ static hipError_t run_bf16(const bf16_t* a, const bf16_t* w, int m, int n, int k
   return hipGetLastError();
 }
 
-// Tile choice (measured on the ViT-B shapes): wide products (QKV, fc1) take 128 x 64
-// tiles at two stages (48 KiB of LDS, three workgroups per CU); narrow ones (N <= 1024:
-// the projection) 64 x 64 tiles, twice the workgroups; long K (fc2) 64 x 64 tiles with
-// three steps in flight (64 KiB, two workgroups per CU). Resident workgroups matter
-// more than pipeline depth at K = 768.
-template <class Epi>
-static hipError_t run(const bf16_t* a, const bf16_t* w, int m, int n, int k, const Epi& e, hipStream_t st) {
-  if (k >= 2048) return run_bf16<64, 64, 4>(a, w, m, n, k, e, st);
-  if (n <= 1024) return run_bf16<64, 64, 2>(a, w, m, n, k, e, st);
-  return run_bf16<128, 64, 2>(a, w, m, n, k, e, st);
+// Tile shapes and ring depths. The two-slot shapes (32-48 KiB of LDS) run three to
+// five workgroups per CU, which hides latency on short products; the others (96-160 KiB)
+// run one workgroup per CU and trade that for fewer bytes per MFMA through L1 and LDS.
+enum class TileShape { t64x64, t128x64s2, t128x64, t192x128, t256x128 };
+
+// Shape choice, from timings on MI355X over the ViT-B/L/H products (M x N x K from
+// 1638 x 768 x 3072 to 65536 x 3840 x 1280):
+//  - large products (M N K >= 1.5e10): 256 x 128 or 192 x 128 tiles, whichever needs
+//    fewer (rounds of 256 tiles) x (tile area);
+//  - long K over few tiles (the second MLP product): 128 x 64 tiles with six slots;
+//  - otherwise 64 x 64 tiles for narrow outputs (N <= 1024) and 128 x 64 for wide ones,
+//    both with two slots and several workgroups per CU.
+// `align`: tiles must not straddle multiples of it (the QKV parts), 0 = no constraint.
+static TileShape pick_tile(int m, int n, int k, int align) {
+  auto tiles = [&](int bm, int bn) { return (long)((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  auto fits = [&](int bn) { return align <= 0 || align % bn == 0; };
+  if ((double)m * n * k >= 1.5e10 && fits(128)) {
+    const long r256 = (tiles(256, 128) + 255) / 256, r192 = (tiles(192, 128) + 255) / 256;
+    return r192 * 192 < r256 * 256 ? TileShape::t192x128 : TileShape::t256x128;
+  }
+  if (k >= 2048 && tiles(128, 64) <= 320) return TileShape::t128x64;
+  return n <= 1024 ? TileShape::t64x64 : TileShape::t128x64s2;
 }
 
 template <class Epi>
-static hipError_t run(const float* a, const float* w, int m, int n, int k, const Epi& e, hipStream_t st) {
+static hipError_t run(const bf16_t* a, const bf16_t* w, int m, int n, int k, const Epi& e, hipStream_t st,
+                      int align = 0) {
+  switch (pick_tile(m, n, k, align)) {
+    case TileShape::t256x128: return run_bf16<256, 128, 3>(a, w, m, n, k, e, st);
+    case TileShape::t192x128: return run_bf16<192, 128, 3>(a, w, m, n, k, e, st);
+    case TileShape::t64x64: return run_bf16<64, 64, 2>(a, w, m, n, k, e, st);
+    case TileShape::t128x64s2: return run_bf16<128, 64, 2>(a, w, m, n, k, e, st);
+    default: return run_bf16<128, 64, 6>(a, w, m, n, k, e, st);
+  }
+}
+
+template <class Epi>
+static hipError_t run(const float* a, const float* w, int m, int n, int k, const Epi& e, hipStream_t st,
+                      int = 0) {
   dim3 grid((n + FT - 1) / FT, (m + FT - 1) / FT);
   hipLaunchKernelGGL(gemm_f32_kernel<Epi>, grid, dim3(256), 0, st, a, w, m, n, k, e);
   return hipGetLastError();
@@ -629,7 +698,7 @@ hipError_t launch_gemm_qkv(const T* a, const T* w, int m, int k, const EpiQKV& e
   if (m <= 0) return hipSuccess;
   QKVStore<T> s{e.bias, (T*)e.q, (T*)e.k, (T*)e.vt, e.n, e.n_pad, e.heads, e.head_dim, e.channels,
                 FastDiv((uint32_t)e.n), FastDiv((uint32_t)e.channels), FastDiv((uint32_t)e.head_dim)};
-  return run(a, w, m, 3 * e.channels, k, s, st);
+  return run(a, w, m, 3 * e.channels, k, s, st, e.channels);
 }
 
 template <typename T>
