@@ -118,21 +118,21 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   constexpr int ring_bytes = 2 * R * kTileBytes;  // K ring then V^T ring
   char* ring = smem + (active ? kp : 0) * ring_bytes;
 
+  // Every tile of these plans is 64 tokens long (stripes are multiples of 64), so tile t
+  // starts at token 64 t and no offset table is read. The key offsets are requested
+  // first and Q after them: the first direct loads below wait only for the offsets, and
+  // the barrier before the loop for Q.
+  const int total = ke - kb;
+  // first token of the item's i-th key tile, held by lane i and read with readlane, so
+  // the loop never waits on a dependent index load
+  const int koff = lane < total ? col_idx[kb + lane] * kTile : 0;
   const int q_local = qh * 32 + (lane & 31);
-  const int my_q = tile_start[qt] + q_local;
+  const int my_q = qt * kTile + q_local;
   // Q^T operand: lane holds Q[my_q][16 ks + 8 (lane / 32) .. + 7]
   bf16x8 qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     qf[ks] = *reinterpret_cast<const bf16x8*>(q_base + (size_t)my_q * D + ks * 16 + (lane >> 5) * 8);
-  // first token of the item's i-th key tile, held by lane i and read with readlane, so
-  // the loop never waits on a dependent index load
-  const int total = ke - kb;
-  const int koff = lane < total ? tile_start[col_idx[kb + lane]] : 0;
-  // Wait for Q and the offsets here, on every path: otherwise the compiler, unable to
-  // prove the loads done at the loop head, may wait for them inside the loop -- and
-  // with them for the tile loads issued after them.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // Direct-to-LDS tile loads: wavefront w fills row group w (rows 8 w .. 8 w + 7) of
   // every tile; lane L fetches the chunk that the swizzle places at byte 16 L.
@@ -414,15 +414,15 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
   char* ring = smem + (active ? kp : 0) * kD80Parity;
   const int hi = lane >> 5, l32 = lane & 31;
 
+  // 64-token tiles: tile t starts at token 64 t (no offset table); offsets first, then Q
+  const int total = ke - kb;
+  const int koff = lane < total ? col_idx[kb + lane] * kTile : 0;
   const int q_local = qh * 32 + l32;
-  const int my_q = tile_start[qt] + q_local;
+  const int my_q = qt * kTile + q_local;
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     qf[ks] = *reinterpret_cast<const bf16x8*>(q_base + (size_t)my_q * D + ks * 16 + hi * 8);
-  const int total = ke - kb;
-  const int koff = lane < total ? tile_start[col_idx[kb + lane]] : 0;
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // loads: 10 groups of 1 KiB per tile (K and V^T alike); wavefront w takes groups w
   // and w + 8 (< 10). K: physical chunk 64 g + L is row (64 g + L) / 10, position
