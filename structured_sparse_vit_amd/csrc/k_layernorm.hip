@@ -81,6 +81,14 @@ __global__ void __launch_bounds__(256) gather_ln_vec_kernel(const float* __restr
     for (int i = 0; i < NV; ++i) *reinterpret_cast<bf16x4*>(o + 4 * (lane + 64 * i)) = bf16x4{};
     return;
   }
+  // gamma and beta are requested with the row, not after the reductions, so their
+  // latency overlaps the row's
+  f32x4 gg[NV], bb[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    gg[i] = *reinterpret_cast<const f32x4*>(g + 4 * (lane + 64 * i));
+    bb[i] = *reinterpret_cast<const f32x4*>(b + 4 * (lane + 64 * i));
+  }
   const f32x4* xr = reinterpret_cast<const f32x4*>(x + (size_t)src * C);
   f32x4 v[NV];
   float s = 0.0f;
@@ -102,11 +110,9 @@ __global__ void __launch_bounds__(256) gather_ln_vec_kernel(const float* __restr
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = 4 * (lane + 64 * i);
-    const f32x4 gg = *reinterpret_cast<const f32x4*>(g + c);
-    const f32x4 bb = *reinterpret_cast<const f32x4*>(b + c);
     bf16x4 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = to_bf16((v[i][e] - mean) * rstd * gg[e] + bb[e]);
+    for (int e = 0; e < 4; ++e) w[e] = to_bf16((v[i][e] - mean) * rstd * gg[i][e] + bb[i][e]);
     *reinterpret_cast<bf16x4*>(o + c) = w;
   }
 }
