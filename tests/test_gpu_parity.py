@@ -250,6 +250,38 @@ def test_block_parity_high_gain(key, gain):
     _check_block(key, _run_block(key, gain=gain), gain)
 
 
+@pytest.mark.parametrize("key,kind", [("c4", "global"), ("c4", "window"), ("c5", "global"), ("c5", "window")])
+def test_block_full_batch_sampled(key, kind):
+    """One block of the ViT-L / ViT-H encoder configs at their full batch (8 and 16
+    images: the launch shapes the encoder benchmark times, with the large-tile GEMM
+    paths) against the oracle on sampled images: the first and the last. Images are
+    independent, so the oracle runs each sampled image alone."""
+    from synth import block_weights, token_features
+    from synth.configs import global_variant, window_variant
+    _say("block full batch", key, kind)
+    base = config(key)
+    cfg = global_variant(base) if kind == "global" else window_variant(base)
+    b = cfg.batch
+    plan = _plan(cfg)
+    img = images(key)
+    assert img.shape[0] == b
+    x = token_features(cfg, 0)
+    w = block_weights(cfg, 0)
+    imp_d = ss.importance(torch.from_numpy(img).to(DEV), cfg.patch)
+    perm, inv, routed = ss.permute(plan, imp_d)
+    xd = torch.from_numpy(x.copy()).to(DEV)
+    ss.block(plan, ss.weights_to_device(w, plan), xd, perm, routed)
+    got = xd.cpu().numpy()
+    imp = imp_d.cpu().numpy()
+    one = cfg.with_(batch=1)
+    for i in (0, b - 1):
+        want_imp = oracle.importance(img[i], cfg.patch)
+        assert np.array_equal(imp[i].view(np.uint32), want_imp.view(np.uint32)), "importance of image %d" % i
+        want = oracle.block_forward(x[i:i + 1], imp[i:i + 1], w, one)
+        mx, rel = check_close(got[i:i + 1], want, what="block %s %s image %d of %d" % (key, kind, i, b))
+        _say("  image %d of %d: max-abs %.3e rel-L2 %.3e" % (i, b, mx, rel))
+
+
 def test_block_is_deterministic():
     _say("block determinism")
     cfg = config("c2")
@@ -324,3 +356,34 @@ def test_encoder_matches_block_by_block_and_oracle():
     s = math.sqrt(layers)
     _say("  encoder max-abs %.3e rel-L2 %.3e" % (np.abs(got - want).max(), rel_l2(got, want)))
     check_close(got, want, max_abs=1e-2 * s, rel_l2=5e-3 * s, what="encoder")
+
+
+def test_encoder_full_size_matches_block_by_block():
+    """The ViT-L encoder config at full size (24 blocks, batch 8, global at layers 5, 11,
+    17, 23), one random layer's weights reused by every block: sparsesam_encoder equals
+    the same blocks called one by one, bit for bit (each block is checked against the
+    oracle by the sampled full-batch tests)."""
+    _say("encoder full size c4")
+    from synth import block_weights, encoder_global_layers, token_features
+    from synth.configs import global_variant, window_variant
+    base = config("c4")
+    cg, cw = global_variant(base), window_variant(base)
+    pg, pw = _plan(cg), _plan(cw)
+    gl = encoder_global_layers(base.layers)
+    kinds = [1 if l in gl else 0 for l in range(base.layers)]
+    wd = ss.weights_to_device(block_weights(base, 0), pg)
+    imp_d = ss.importance(torch.from_numpy(images("c4")).to(DEV), base.patch)
+    perm_g, _, routed_g = ss.permute(pg, imp_d)
+    perm_w, _, routed_w = ss.permute(pw, imp_d)
+    x0 = token_features(base, 0)
+    x_enc = torch.from_numpy(x0.copy()).to(DEV)
+    ss.encoder(pg, pw, [wd] * base.layers, kinds, x_enc, (perm_g, routed_g), (perm_w, routed_w))
+    x_seq = torch.from_numpy(x0.copy()).to(DEV)
+    for l in range(base.layers):
+        if kinds[l]:
+            ss.block(pg, wd, x_seq, perm_g, routed_g)
+        else:
+            ss.block(pw, wd, x_seq, perm_w, routed_w)
+    got, ref = x_enc.cpu().numpy(), x_seq.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
