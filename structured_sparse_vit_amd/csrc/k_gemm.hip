@@ -7,10 +7,10 @@
 //
 // bf16 kernel: one BM x BN output tile per 256-thread workgroup, K step 64, four
 // wavefronts in a 2 x 2 layout, each owning a (BM/2) x (BN/2) block of 32 x 32 MFMA
-// tiles. Tiles are large (up to 256 x 192) because an MI355X CU gets about 64 bytes
-// per clock from its XCD's L2 on average: a 128 x 64 tile needs 94 bytes per clock
-// at the matrix-core rate, a 192 x 128 tile 53. The host picks, per product, the tile
-// shape whose grid fills the 256 CUs in the fewest rounds (see pick_tile).
+// tiles. Large products take large tiles (192 x 128 or 256 x 128) because an MI355X CU
+// gets about 64 bytes per clock through L1 from its XCD's L2: a 128 x 64 tile needs 94
+// bytes per clock at the matrix-core rate, a 192 x 128 tile 53. Short products take
+// small tiles at several workgroups per CU (see pick_tile).
 //
 // A and W tiles go straight from global memory into LDS (global_load_lds_dwordx4, no
 // register staging) through an ST-slot ring of swizzled 128-byte rows; every slot is
@@ -649,28 +649,46 @@ static hipError_t run_bf16(const bf16_t* a, const bf16_t* w, int m, int n, int k
   return hipGetLastError();
 }
 
-// Tile shapes and ring depths. The two-slot shapes (32-48 KiB of LDS) run three to
-// five workgroups per CU, which hides latency on short products; the others (96-160 KiB)
-// run one workgroup per CU and trade that for fewer bytes per MFMA through L1 and LDS.
-enum class TileShape { t64x64, t128x64s2, t128x64, t192x128, t256x128 };
+// Tile shapes and ring depths. 256 x 128 with three slots takes 144 KiB of LDS (one
+// workgroup per CU); 192 x 128 with two slots 80 KiB (two per CU, so one tile's
+// epilogue and the next one's first loads overlap the other's K loop); 128 x 64 and
+// 64 x 64 with two slots 48 and 32 KiB (three to five per CU); 128 x 64 with six slots
+// 144 KiB (one per CU, deep prefetch for long K over few tiles).
+enum class TileShape { t64x64, t128x64s2, t128x64, t192x128s2, t256x128 };
 
-// Shape choice, from timings on MI355X over the ViT-B/L/H products (M x N x K from
-// 1638 x 768 x 3072 to 65536 x 3840 x 1280):
-//  - large products (M N K >= 1.5e10): 256 x 128 or 192 x 128 tiles, whichever needs
-//    fewer (rounds of 256 tiles) x (tile area);
-//  - long K over few tiles (the second MLP product): 128 x 64 tiles with six slots;
-//  - otherwise 64 x 64 tiles for narrow outputs (N <= 1024) and 128 x 64 for wide ones,
-//    both with two slots and several workgroups per CU.
+// Shape choice. Long K over few tiles (the ViT-B second MLP product, 1638 x 768 x 3072)
+// takes 128 x 64 with six slots. Otherwise each shape's time is estimated as
+// (rounds of resident workgroups) x (tile area per CU per round) / (efficiency), the
+// efficiencies -- 1.0, 1.3, 0.8 and 0.3 for 256 x 128, 192 x 128, 128 x 64 and 64 x 64
+// -- fitted to timings of every shape on MI355X over 25 ViT-B/L/H products (M x N x K
+// from 1638 x 768 x 3072 to 78400 x 1280 x 1280); the fitted choice is within 3 % of
+// the fastest shape on 20 of them and within 14 % on all.
 // `align`: tiles must not straddle multiples of it (the QKV parts), 0 = no constraint.
 static TileShape pick_tile(int m, int n, int k, int align) {
   auto tiles = [&](int bm, int bn) { return (long)((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
-  auto fits = [&](int bn) { return align <= 0 || align % bn == 0; };
-  if ((double)m * n * k >= 1.5e10 && fits(128)) {
-    const long r256 = (tiles(256, 128) + 255) / 256, r192 = (tiles(192, 128) + 255) / 256;
-    return r192 * 192 < r256 * 256 ? TileShape::t192x128 : TileShape::t256x128;
-  }
   if (k >= 2048 && tiles(128, 64) <= 320) return TileShape::t128x64;
-  return n <= 1024 ? TileShape::t64x64 : TileShape::t128x64s2;
+  struct Cand {
+    TileShape s;
+    int bm, bn, per_cu;
+    double eff;
+  };
+  const Cand cands[] = {{TileShape::t256x128, 256, 128, 1, 1.0},
+                        {TileShape::t192x128s2, 192, 128, 2, 1.3},
+                        {TileShape::t128x64s2, 128, 64, 3, 0.8},
+                        {TileShape::t64x64, 64, 64, 5, 0.3}};
+  TileShape best = TileShape::t128x64s2;
+  double best_cost = -1.0;
+  for (const Cand& c : cands) {
+    if (align > 0 && align % c.bn != 0) continue;
+    const long slots = 256L * c.per_cu;
+    const long rounds = (tiles(c.bm, c.bn) + slots - 1) / slots;
+    const double cost = (double)rounds * c.per_cu * c.bm * c.bn / c.eff;
+    if (best_cost < 0 || cost < best_cost) {
+      best = c.s;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 template <class Epi>
@@ -678,7 +696,7 @@ static hipError_t run(const bf16_t* a, const bf16_t* w, int m, int n, int k, con
                       int align = 0) {
   switch (pick_tile(m, n, k, align)) {
     case TileShape::t256x128: return run_bf16<256, 128, 3>(a, w, m, n, k, e, st);
-    case TileShape::t192x128: return run_bf16<192, 128, 3>(a, w, m, n, k, e, st);
+    case TileShape::t192x128s2: return run_bf16<192, 128, 2>(a, w, m, n, k, e, st);
     case TileShape::t64x64: return run_bf16<64, 64, 2>(a, w, m, n, k, e, st);
     case TileShape::t128x64s2: return run_bf16<128, 64, 2>(a, w, m, n, k, e, st);
     default: return run_bf16<128, 64, 6>(a, w, m, n, k, e, st);
