@@ -202,12 +202,20 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
         sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][mb], qf[ks], sc[mb], 0, 0, 0);
   };
 
-  f32x16 oacc[2];
+  // O^T accumulators: blocks 0 and 1 hold channels 0..63; block 2 holds the softmax
+  // denominators. Its A operand is a row of ones (row 64 of an extended V^T: lanes 0 and
+  // 32, all keys) and zeros, so the matrix cores sum the bf16 probabilities that the
+  // output is weighted with -- 32 VALU additions per step fewer, in a kernel whose
+  // steps are VALU-bound -- and lane q < 32 holds the sum for query q in element 0.
+  f32x16 oacc[3];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 3; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
+  bf16x8 vones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vones[e] = to_bf16((lane & 31) == 0 ? 1.0f : 0.0f);
 
   // online softmax of S_j (this lane's query: 32 of the tile's 64 scores, the rest in
   // lane ^ 32) into the P^T operand
@@ -224,9 +232,8 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
     // (wave-uniform branch; always taken on the first tile, where m_run = -inf)
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
 #pragma unroll
-      for (int md = 0; md < 2; ++md)
+      for (int md = 0; md < 3; ++md)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
       m_run = m_new;
@@ -234,32 +241,24 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
     // P^T operand of key group kk (keys 16 kk .. + 15): with the permuted K rows,
     // accumulator elements 8 (kk & 1) .. + 7 of block kk / 2 are keys 8 h .. 8 h + 7 of
     // the group for lane half h, in order
-    float ps[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 v;
-      float a = 0.0f, b = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + e], c_log2, -m_run));
-        if (e & 1)
-          b += p;
-        else
-          a += p;
-        v[e] = to_bf16(p);
-      }
-      ps[kk] = a + b;
+      for (int e = 0; e < 8; ++e)
+        v[e] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + e], c_log2, -m_run)));
       pf[kk] = v;
     }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
-  // O^T += V^T P^T over four 16-key steps
+  // O^T += V^T P^T over four 16-key steps, and the denominators with them
   auto pv = [&](const bf16x8 (&vf)[4][2], const bf16x8 (&pf)[4]) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int md = 0; md < 2; ++md)
         oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk][md], pf[kk], oacc[md], 0, 0, 0);
+      oacc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vones, pf[kk], oacc[2], 0, 0, 0);
+    }
   };
 
   const int nj = active ? (total - kp + P - 1) / P : 0;  // tiles of this wavefront's parity
@@ -290,6 +289,7 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   }
   // every wavefront is done with the rings before the exchange area reuses them
   __syncthreads();
+  l_run = oacc[2][0];  // lane q < 32: denominator of query q; lanes 32..63: 0
 
   // merge parities 1 .. P-1 into parity 0 through LDS, in parity order (same lane ->
   // same queries); exchange record: [parity - 1][member][query half][lane][m, l, O[32]]
@@ -488,34 +488,27 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
     const float m_new = fmaxf(m_run, mx * c_log2);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
       m_run = m_new;
     }
-    float ps0 = 0.0f, ps1 = 0.0f;
     bf16x8 pf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 v;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + e], c_log2, -m_run));
-        if (e & 1)
-          ps1 += p;
-        else
-          ps0 += p;
-        v[e] = to_bf16(p);
-      }
+      for (int e = 0; e < 8; ++e)
+        v[e] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + e], c_log2, -m_run)));
       u32x4 r = __builtin_bit_cast(u32x4, v);
       const auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
       const auto s13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
       r = u32x4{s02[0], s13[0], s02[1], s13[1]};
       pf[kk] = __builtin_bit_cast(bf16x8, r);
     }
-    l_run += ps0 + ps1;
+    // rows 80..95 of the third block: row 80 is all ones (it accumulates the softmax
+    // denominators on the matrix cores), the rest zero
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -526,7 +519,7 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
           vf = *reinterpret_cast<const bf16x8*>(Vs + swz(min(d, D - 1), kk * 2 + hi));
         } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) vf[i] = (bf16_t)0.0f;
+          for (int i = 0; i < 8; ++i) vf[i] = to_bf16(d == D ? 1.0f : 0.0f);
         }
         oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[md], 0, 0, 0);
       }
@@ -543,6 +536,7 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
     if (j < nj) tile_step(j & 1);
   }
   __syncthreads();
+  l_run = oacc[2][8];  // row 80: lane q < 32 holds the denominator of query q, lanes 32..63 0
 
   float* xch = reinterpret_cast<float*>(smem);
   constexpr int RL = 2 + 16 * MD;  // exchange record: m, l, O[48]
@@ -715,6 +709,7 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
   __syncthreads();
 
   const int hi = lane >> 5, l32 = lane & 31;
+  constexpr bool kSumRow = L::MD * 32 > D;  // spare accumulator rows: denominators on the matrix cores
   for (int qt = wave; qt < nt32; qt += 4) {
     const int qpos = qt * 32 + l32;
     const int qrow = min(qpos, n - 1);
@@ -754,7 +749,7 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
       if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
         // a lane whose reference does not move keeps alpha = 1 (also when both are -inf)
         const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        l_run *= alpha;
+        if constexpr (!kSumRow) l_run *= alpha;
 #pragma unroll
         for (int md = 0; md < L::MD; ++md)
 #pragma unroll
@@ -770,10 +765,12 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
         for (int e = 0; e < 8; ++e) {
           const float x = sc[kk * 8 + e];
           const float p = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c_log2, -m_run));
-          if (e & 1)
-            ps1 += p;
-          else
-            ps0 += p;
+          if constexpr (!kSumRow) {
+            if (e & 1)
+              ps1 += p;
+            else
+              ps0 += p;
+          }
           v[e] = to_bf16(p);
         }
         u32x4 r = __builtin_bit_cast(u32x4, v);
@@ -782,8 +779,10 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
         r = u32x4{s02[0], s13[0], s02[1], s13[1]};
         pf[kk] = __builtin_bit_cast(bf16x8, r);
       }
-      l_run += ps0 + ps1;
-      // O^T += V^T P^T: rows d = 32 md + l32 (zero past D), keys kt*32 + 16 kk + 8 hi ..
+      if constexpr (!kSumRow) l_run += ps0 + ps1;
+      // O^T += V^T P^T: rows d = 32 md + l32 (zero past D; row D all ones when the last
+      // block has spare rows, so the matrix cores sum the denominators), keys kt*32 +
+      // 16 kk + 8 hi ..
 #pragma unroll
       for (int md = 0; md < L::MD; ++md) {
         const int d = md * 32 + l32;
@@ -794,11 +793,18 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
             vf = *reinterpret_cast<const bf16x8*>(Vs + (size_t)min(d, D - 1) * vld + kt * 32 + kk * 16 + hi * 8);
           if (!(md * 32 + 32 <= D) && d >= D) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) vf[i] = (bf16_t)0.0f;
+            for (int i = 0; i < 8; ++i) vf[i] = to_bf16(d == D ? 1.0f : 0.0f);
           }
           oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[md], 0, 0, 0);
         }
       }
+    }
+    if constexpr (kSumRow) {
+      // row D sits at row r = D % 32 of the last block; block row 8 (e / 4) + 4 hi + e % 4
+      // is element e of lane half hi, so row r is element 4 (r / 8) + r % 4 of the lanes
+      // with hi = (r / 4) % 2
+      constexpr int r = D % 32;
+      l_run = ((r >> 2) & 1) == hi ? oacc[L::MD - 1][4 * (r >> 3) + (r & 3)] : 0.0f;
     }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (qpos < n) {
