@@ -51,6 +51,27 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // probabilities then stay below 2^8, far inside the fp32 and bf16 range.
 constexpr float kRescaleSlack = 8.0f;
 
+// The D = 64 kernel moves its reference even more lazily: only when a lane's sum of 32
+// probabilities passes 2^64 (so every probability stays below 2^64, and a row's O and
+// l below 2^64 * 4096 * max |v|, far inside fp32).
+constexpr float kOverflowGuard = 18446744073709551616.0f;  // 2^64
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// acc + a + b for two bf16 values, in one dot product with (1, 1)
+__device__ __forceinline__ float sum_bf16_pair(bf16_t a, bf16_t b, float acc) {
+  const bf16x2 ab = {a, b}, one = {to_bf16(1.0f), to_bf16(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(ab, one, acc, false);
+}
+
+// eight bf16 values times s, rounded back to bf16
+__device__ __forceinline__ bf16x8 scale_bf16x8(bf16x8 v, float s) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = to_bf16(to_f32(v[e]) * s);
+  return r;
+}
+
 // max of three floats; the compiler forms v_max3_f32 (and, unlike inline assembly,
 // inserts the wait states a read of fresh MFMA results needs)
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
@@ -128,11 +149,13 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   const int koff = lane < total ? col_idx[kb + lane] * kTile : 0;
   const int q_local = qh * 32 + (lane & 31);
   const int my_q = qt * kTile + q_local;
-  // Q^T operand: lane holds Q[my_q][16 ks + 8 (lane / 32) .. + 7]
+  // Q^T operand: lane holds Q[my_q][16 ks + 8 (lane / 32) .. + 7], times the softmax
+  // scale and log2(e), so that the matrix cores deliver scores in exp2 units
   bf16x8 qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8*>(q_base + (size_t)my_q * D + ks * 16 + (lane >> 5) * 8);
+    qf[ks] = scale_bf16x8(*reinterpret_cast<const bf16x8*>(q_base + (size_t)my_q * D + ks * 16 + (lane >> 5) * 8),
+                          c_log2);
 
   // Direct-to-LDS tile loads: wavefront w fills row group w (rows 8 w .. 8 w + 7) of
   // every tile; lane L fetches the chunk that the swizzle places at byte 16 L.
@@ -188,13 +211,28 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
       for (int md = 0; md < 2; ++md)
         vf[kk][md] = *reinterpret_cast<const bf16x8*>(Vs + swz(md * 32 + (lane & 31), kk * 2 + (lane >> 5)));
   };
-  // S^T = K Q^T; the two accumulation chains alternate, so each MFMA depends on the one
-  // two back
+  // Reference of exp2 (the online softmax's running max, in exp2 units): m_run, -inf
+  // before the first tile. It enters the scores through a fifth k-step of S^T = K Q^T
+  // whose K operand is a column of ones (dimension 64 of every key: element 0 of lanes
+  // 0..31) and whose Q^T operand holds -m_run (element 0 of lane q < 32), so the
+  // accumulator already holds c s - m_run and each probability costs one exp2. The
+  // reference is kept bf16-exact for that.
+  float m_run = -INFINITY, l_run = 0.0f;
+  bf16x8 kx, qx;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kx[e] = to_bf16(e == 0 && lane < 32 ? 1.0f : 0.0f);
+    qx[e] = to_bf16(0.0f);
+  }
+  // S^T = K Q^T - m_run; the two accumulation chains alternate, so each MFMA depends on
+  // the one two back
   auto scores = [&](const bf16x8 (&kf)[4][2], f32x16 (&sc)[2]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sc[mb][e] = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kx, qx, sc[mb], 0, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -202,63 +240,72 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
         sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][mb], qf[ks], sc[mb], 0, 0, 0);
   };
 
-  // O^T accumulators: blocks 0 and 1 hold channels 0..63; block 2 holds the softmax
-  // denominators. Its A operand is a row of ones (row 64 of an extended V^T: lanes 0 and
-  // 32, all keys) and zeros, so the matrix cores sum the bf16 probabilities that the
-  // output is weighted with -- 32 VALU additions per step fewer, in a kernel whose
-  // steps are VALU-bound -- and lane q < 32 holds the sum for query q in element 0.
-  f32x16 oacc[3];
+  // O^T accumulators: blocks 0 and 1 hold channels 0..63
+  f32x16 oacc[2];
 #pragma unroll
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
-  bf16x8 vones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) vones[e] = to_bf16((lane & 31) == 0 ? 1.0f : 0.0f);
 
-  // online softmax of S_j (this lane's query: 32 of the tile's 64 scores, the rest in
-  // lane ^ 32) into the P^T operand
-  auto softmax = [&](const f32x16 (&sc)[2], bf16x8 (&pf)[4]) {
-    float t[11];
-#pragma unroll
-    for (int i = 0; i < 10; ++i) t[i] = max3f(sc[(3 * i) >> 4][(3 * i) & 15], sc[(3 * i + 1) >> 4][(3 * i + 1) & 15],
-                                             sc[(3 * i + 2) >> 4][(3 * i + 2) & 15]);
-    t[10] = fmaxf(sc[1][14], sc[1][15]);
-    float mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]), max3f(t[6], t[7], max3f(t[8], t[9], t[10])));
-    mx = max_xor32(mx);
-    const float m_new = fmaxf(m_run, mx * c_log2);
-    // rescale only when some row's max passed its reference by more than the slack
-    // (wave-uniform branch; always taken on the first tile, where m_run = -inf)
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int md = 0; md < 3; ++md)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
-      m_run = m_new;
-    }
-    // P^T operand of key group kk (keys 16 kk .. + 15): with the permuted K rows,
-    // accumulator elements 8 (kk & 1) .. + 7 of block kk / 2 are keys 8 h .. 8 h + 7 of
-    // the group for lane half h, in order
+  // P^T operand of key group kk (keys 16 kk .. + 15) from the scores minus `shift`: with
+  // the permuted K rows, accumulator elements 8 (kk & 1) .. + 7 of block kk / 2 are keys
+  // 8 h .. 8 h + 7 of the group for lane half h, in order. Returns this lane's sum of
+  // the 32 bf16 probabilities (the ones the output is weighted with), by bf16 dot
+  // products with (1, 1).
+  auto probs = [&](const f32x16 (&sc)[2], bf16x8 (&pf)[4], float shift) {
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 v;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[e] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + e], c_log2, -m_run)));
+      for (int e = 0; e < 8; ++e) v[e] = to_bf16(__builtin_amdgcn_exp2f(sc[kk >> 1][(kk & 1) * 8 + e] - shift));
       pf[kk] = v;
+      s0 = sum_bf16_pair(v[0], v[1], s0);
+      s1 = sum_bf16_pair(v[2], v[3], s1);
+      s0 = sum_bf16_pair(v[4], v[5], s0);
+      s1 = sum_bf16_pair(v[6], v[7], s1);
     }
+    return s0 + s1;
   };
-  // O^T += V^T P^T over four 16-key steps, and the denominators with them
+  // Online softmax of S_j (this lane's query: 32 of the tile's 64 scores, the rest in
+  // lane ^ 32) into the P^T operand. The reference moves only on the first tile and
+  // when some probability may pass 2^kOverflowLog2 (the lane sum bounds every one of
+  // its 32): the row max is then taken, O and l rescaled, and P recomputed (a
+  // wave-uniform branch, rare after the first tile).
+  auto softmax = [&](const f32x16 (&sc)[2], bf16x8 (&pf)[4], bool first) {
+    float sum = probs(sc, pf, 0.0f);
+    if (first || __builtin_amdgcn_ballot_w64(sum > kOverflowGuard) != 0) {
+      float t[11];
+#pragma unroll
+      for (int i = 0; i < 10; ++i)
+        t[i] = max3f(sc[(3 * i) >> 4][(3 * i) & 15], sc[(3 * i + 1) >> 4][(3 * i + 1) & 15],
+                     sc[(3 * i + 2) >> 4][(3 * i + 2) & 15]);
+      t[10] = fmaxf(sc[1][14], sc[1][15]);
+      float mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]), max3f(t[6], t[7], max3f(t[8], t[9], t[10])));
+      mx = max_xor32(mx);  // relative to the reference the scores carry
+      const float base = first ? 0.0f : m_run;
+      const float m_new = to_f32(to_bf16(base + (first ? mx : fmaxf(mx, 0.0f))));
+      if (!first) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int md = 0; md < 2; ++md)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
+        l_run *= alpha;
+      }
+      m_run = m_new;
+      qx[0] = to_bf16(lane < 32 ? -m_new : 0.0f);
+      sum = probs(sc, pf, m_new - base);
+    }
+    l_run += sum;
+  };
+  // O^T += V^T P^T over four 16-key steps
   auto pv = [&](const bf16x8 (&vf)[4][2], const bf16x8 (&pf)[4]) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int md = 0; md < 2; ++md)
         oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk][md], pf[kk], oacc[md], 0, 0, 0);
-      oacc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vones, pf[kk], oacc[2], 0, 0, 0);
-    }
   };
 
   const int nj = active ? (total - kp + P - 1) / P : 0;  // tiles of this wavefront's parity
@@ -279,7 +326,7 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
       bf16x8 vf[4][2], pf[4];
       read_v(j, vf);
       scores(k_use, sacc);
-      softmax(sacc, pf);
+      softmax(sacc, pf, j == 0);
       pv(vf, pf);
     }
   };
@@ -289,7 +336,6 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   }
   // every wavefront is done with the rings before the exchange area reuses them
   __syncthreads();
-  l_run = oacc[2][0];  // lane q < 32: denominator of query q; lanes 32..63: 0
 
   // merge parities 1 .. P-1 into parity 0 through LDS, in parity order (same lane ->
   // same queries); exchange record: [parity - 1][member][query half][lane][m, l, O[32]]
