@@ -114,6 +114,7 @@ __device__ __forceinline__ float max_xor32(float v) {
 // publishes K_{j+1} and V_j and retires the slots the step overwrites. (Loading more
 // steps ahead through deeper rings measured slower.)
 static_assert(kAttnItemTiles <= 64, "one key tile per lane");
+template <int P>  // key parities of the item (1, 2 or 4): the load code has no run-time loop
 __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                                  const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
                                                  const int4* __restrict__ items, const int* __restrict__ col_idx,
@@ -126,7 +127,7 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   const int4 it0 = items[2 * item], it1 = items[2 * item + 1];
   const int kb = __builtin_amdgcn_readfirstlane(it0.x), ke = __builtin_amdgcn_readfirstlane(it0.y);
   const int slot = __builtin_amdgcn_readfirstlane(it0.z), gp = __builtin_amdgcn_readfirstlane(it0.w);
-  const int G = gp & 15, P = gp >> 4;
+  const int G = gp & 15;
   const int qh = wave & 1, pr = wave >> 1;  // query half; wavefront pair 0..3
   const int gi = pr % G, kp = pr / G;       // member of the group; key parity
   const bool active = kp < P;               // false only for the spare pair of a G = 3 group
@@ -164,24 +165,22 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   // swapped, so that the S^T accumulator hands lane half h of every 16-key group keys
   // 8h .. 8h+7 in order -- the layout of the P^T operand -- with no lane exchange
   const int k_src = kperm16(krow) * D + kch * 8, v_src = krow * n_pad + kch * 8;
+  // Entries past the list are clamped to its last tile: the loads stay unconditional
+  // (no branch in the step) and land in slots no wavefront reads.
   auto issue_k = [&](int j) {  // K tiles of step j (every parity) into K slot j mod R
-    if (j < 0) return;
     char* dst = smem + (j & (R - 1)) * kTileBytes + wave * 1024;
+#pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int t = p + P * j;
-      if (t >= total) break;
-      const int k0 = __builtin_amdgcn_readlane(koff, t);
+      const int k0 = __builtin_amdgcn_readlane(koff, min(p + P * j, total - 1));
       __builtin_amdgcn_global_load_lds((const void*)(k_base + (size_t)k0 * D + k_src),
                                        (__attribute__((address_space(3))) void*)(dst + p * ring_bytes), 16, 0, 0);
     }
   };
   auto issue_v = [&](int j) {  // V^T tiles of step j (every parity) into V slot j mod R
-    if (j < 0) return;
     char* dst = smem + (R + (j & (R - 1))) * kTileBytes + wave * 1024;
+#pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int t = p + P * j;
-      if (t >= total) break;
-      const int k0 = __builtin_amdgcn_readlane(koff, t);
+      const int k0 = __builtin_amdgcn_readlane(koff, min(p + P * j, total - 1));
       __builtin_amdgcn_global_load_lds((const void*)(v_base + k0 + v_src),
                                        (__attribute__((address_space(3))) void*)(dst + p * ring_bytes), 16, 0, 0);
     }
@@ -415,8 +414,16 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma64_kernel(const bf16
     if (u >= total) break;
     if (r > 0) __syncthreads();  // the previous unit's merge has read its LDS exchange
     const int item = u / seg_heads;
-    attn_mfma64_unit(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
-                     u - item * seg_heads, smem);
+    const int parities = __builtin_amdgcn_readfirstlane(items[2 * item].w) >> 4;
+    if (parities == 1)
+      attn_mfma64_unit<1>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
+                          u - item * seg_heads, smem);
+    else if (parities == 2)
+      attn_mfma64_unit<2>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
+                          u - item * seg_heads, smem);
+    else
+      attn_mfma64_unit<4>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
+                          u - item * seg_heads, smem);
   }
 }
 
