@@ -443,6 +443,7 @@ constexpr int kD80Parity = 4 * kD80Tile;           // K ring + V^T ring, two slo
 constexpr int kD80Lds = 4 * kD80Parity;            // four parities: 160 KiB
 __device__ __forceinline__ int k80_off(int r, int c) { return r * 160 + ((c + (r >> 3)) % 10) * 16; }
 
+template <int P>  // key parities of the item (1, 2 or 4)
 __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                               const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
                                               const int4* __restrict__ items, const int* __restrict__ col_idx,
@@ -455,7 +456,7 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
   const int4 it0 = items[2 * item], it1 = items[2 * item + 1];
   const int kb = __builtin_amdgcn_readfirstlane(it0.x), ke = __builtin_amdgcn_readfirstlane(it0.y);
   const int slot = __builtin_amdgcn_readfirstlane(it0.z), gp = __builtin_amdgcn_readfirstlane(it0.w);
-  const int G = gp & 15, P = gp >> 4;
+  const int G = gp & 15;
   const int qh = wave & 1, pr = wave >> 1;
   const int gi = pr % G, kp = pr / G;
   const bool active = kp < P;
@@ -491,14 +492,17 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
     const int vr = 8 * g + (lane >> 3), vc = (lane & 7) ^ swz_key(8 * g + (lane >> 3));
     v_src[i] = vr * n_pad + vc * 8;
   }
-  const int ngrp = wave + 8 < 10 ? 2 : 1;
-  auto issue = [&](int j, int s) {  // K and V^T tiles of step j (every parity) into slot s
+  const bool two_groups = wave + 8 < 10;
+  // K and V^T tiles of step j (every parity) into slot s; entries past the list are
+  // clamped to its last tile (unconditional loads into slots no wavefront reads)
+  auto issue = [&](int j, int s) {
+#pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int t = p + P * j;
-      if (t >= total) break;
-      const int k0 = __builtin_amdgcn_readlane(koff, t);
+      const int k0 = __builtin_amdgcn_readlane(koff, min(p + P * j, total - 1));
       char* base = smem + p * kD80Parity;
-      for (int i = 0; i < ngrp; ++i) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (i == 1 && !two_groups) break;
         const int g = wave + 8 * i;
         __builtin_amdgcn_global_load_lds((const void*)(k_base + (size_t)k0 * D + k_src[i]),
                                          (__attribute__((address_space(3))) void*)(base + s * kD80Tile + g * 1024),
@@ -667,8 +671,16 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_d80_kernel(const bf16_t*
     if (u >= total) break;
     if (r > 0) __syncthreads();
     const int item = u / seg_heads;
-    attn_d80_unit(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
-                  u - item * seg_heads, smem);
+    const int parities = __builtin_amdgcn_readfirstlane(items[2 * item].w) >> 4;
+    if (parities == 1)
+      attn_d80_unit<1>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
+                          u - item * seg_heads, smem);
+    else if (parities == 2)
+      attn_d80_unit<2>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
+                          u - item * seg_heads, smem);
+    else
+      attn_d80_unit<4>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
+                          u - item * seg_heads, smem);
   }
 }
 

@@ -15,7 +15,7 @@
 //
 // rank_kernel: one workgroup per (segment, chunk of slots). Its lanes count, for the
 // chunk's slots, the preceding slots within shares of the segment's keys (held in LDS
-// as 32-bit order keys); lanes of one slot fold their counts with shuffles, the
+// as 64-bit order words); lanes of one slot fold their counts with shuffles, the
 // wavefronts' shares are summed in LDS, and one lane per slot writes perm, inv and --
 // when the rank is below K -- the keep-set entry. The split is chosen so a single
 // image's 4096 slots still spread over 256 workgroups.
@@ -24,6 +24,8 @@
 #include "internal.hpp"
 
 namespace sparsesam {
+
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
 // 32-bit key that orders descending importance ascending: larger value -> smaller key.
 __device__ __forceinline__ uint32_t desc_key(float f) {
@@ -36,9 +38,11 @@ __device__ __forceinline__ uint32_t desc_key(float f) {
 constexpr uint32_t kPadKey = 0xFFFFFFFFu;  // pad slots: after every real slot
 
 // rank_kernel layout: a workgroup of kw wavefronts ranks tpw slots of one segment
-// (tpw = 16 or 64). Lane l of a wavefront serves slot l % tpw and key residue class
-// l / tpw (mod 64 / tpw); wavefront w takes the w-th share of the keys. For N = 4096
-// that is 256 workgroups of 16 wavefronts, every lane comparing 64 keys.
+// (tpw = 16 or 64). The segment's keys sit in LDS as 64-bit words (order key << 32 |
+// slot), so "slot j precedes slot s" is one unsigned compare of two words and every
+// 16-byte read brings two keys. Lane l of a wavefront serves slot l % tpw and key pair
+// residue class l / tpw (mod 64 / tpw); wavefront w takes the w-th share of the keys.
+// For N = 4096 that is 256 workgroups of 16 wavefronts, every lane comparing 64 keys.
 constexpr int kMaxRankWaves = 16;
 
 __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* __restrict__ imp, SegmentMap map,
@@ -47,10 +51,10 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
                                                                   const int* __restrict__ seg_off,
                                                                   int routed_per_image, int* __restrict__ perm,
                                                                   int* __restrict__ inv, int* __restrict__ routed) {
-  extern __shared__ uint32_t key_lds[];  // keys of the segment, padded to a multiple of 64
+  extern __shared__ __attribute__((aligned(16))) uint64_t key_lds[];  // padded to a multiple of 64
   __shared__ int part[kMaxRankWaves * 64];
   const int seg = blockIdx.x / chunks, chunk = blockIdx.x - (blockIdx.x / chunks) * chunks;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kw = blockDim.x >> 6;
   const int tokens = map.grid_h * map.grid_w;
   const int img = map.f_spi.div(seg);
@@ -60,28 +64,29 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
 #pragma unroll 4
   for (int s = tid; s < n64; s += blockDim.x) {
     const int row = s < n ? map.row_of(seg, s) : -1;
-    key_lds[s] = row >= 0 ? desc_key(im[row - img * tokens]) : kPadKey;
+    const uint32_t k = row >= 0 ? desc_key(im[row - img * tokens]) : kPadKey;
+    key_lds[s] = ((uint64_t)k << 32) | (uint32_t)s;
   }
   __syncthreads();
-  const int subs = 64 / tpw;                 // lanes per slot
+  const int subs = 64 / tpw;  // lanes per slot
   const int slot = chunk * tpw + (lane % tpw);
   const int sub = lane / tpw;
-  const bool valid = slot < n;
-  const uint32_t mine = valid ? key_lds[slot] : 0u;
+  const uint64_t mine = slot < n ? key_lds[slot] : 0ull;
   // this wavefront's share of the keys: [j0, j1), a multiple of 64 long
   const int per = ((n64 / 64 + kw - 1) / kw) * 64;
   const int j0 = wave * per, j1 = min(n64, j0 + per);
   int cnt = 0;
-  for (int jb = j0; jb < j1; jb += 4 * subs) {
-    // four keys per lane per step: jb + sub + subs * u, u = 0..3
-    uint32_t kk[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) kk[u] = key_lds[jb + sub + subs * u];
+  // each lane reads key pairs jb + 2 (sub + subs u) (16 bytes) for u = 0..3
+  for (int jb = j0; jb < j1; jb += 8 * subs) {
+    uint64_t kk[8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int jj = jb + sub + subs * u;
-      cnt += (kk[u] < mine) | ((kk[u] == mine) & (jj < slot));
+      const auto v = *reinterpret_cast<const u64x2*>(key_lds + jb + 2 * (sub + subs * u));
+      kk[2 * u] = v[0];
+      kk[2 * u + 1] = v[1];
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cnt += kk[u] < mine;
   }
   // the 64 / tpw lanes of one slot are tpw apart: fold them
   for (int o = tpw; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
@@ -105,7 +110,7 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
   }
 }
 
-size_t permute_lds_bytes(const sparsesam_plan& p) { return (size_t)((p.n + 63) & ~63) * 4; }
+size_t permute_lds_bytes(const sparsesam_plan& p) { return (size_t)((p.n + 63) & ~63) * 8; }
 
 hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
                           hipStream_t st) {
