@@ -722,6 +722,9 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
 // without any kept pair are skipped. S^T = K Q^T and O^T = V^T P^T on
 // v_mfma_f32_32x32x16_bf16 as in the long-segment kernel; head_dim 80 runs V^T as
 // three 32-row blocks with rows 80..95 zero in registers.
+constexpr int kMaxShortBlocks = 8;  // 32-token blocks of a short segment
+static_assert(kShortMaxN <= 32 * kMaxShortBlocks, "short segments fit the unrolled block loop");
+
 template <int D>
 struct ShortLds {
   static constexpr int KLD = D + 8;        // K row stride (bf16): 16-byte pad, conflict-free reads
@@ -752,24 +755,38 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
   const bf16_t* k_base = Kt + (size_t)sh * n * D;
   const bf16_t* v_base = VT + (size_t)sh * D * n_pad;
 
-  // K rows 0..nk-1 (zero past n), 8 channels per 16-byte chunk
-  for (int c = tid; c < nk * (D / 8); c += 256) {
-    const int r = c / (D / 8), ch = c - (c / (D / 8)) * (D / 8);
-    i32x4 v = {0, 0, 0, 0};
-    if (r < n) v = *reinterpret_cast<const i32x4*>(k_base + (size_t)r * D + ch * 8);
-    *reinterpret_cast<i32x4*>(Ks + r * L::KLD + ch * 8) = v;
-  }
-  // V^T rows 0..D-1, keys 0..nk-1 (zero at keys >= n: V^T holds nothing there)
-  for (int c = tid; c < D * (nk / 8); c += 256) {
-    const int d = c / (nk / 8), kc = (c - (c / (nk / 8)) * (nk / 8)) * 8;
-    bf16x8 v;
-    if (kc + 8 <= n) {
-      v = *reinterpret_cast<const bf16x8*>(v_base + (size_t)d * n_pad + kc);
-    } else {
+  // Every load of the fill is issued before any LDS store (fixed trip counts, nk <=
+  // 256), so the workgroup waits for one memory latency instead of one per chunk.
+  // K rows 0..nk-1 (zero past n), 8 channels per 16-byte chunk: chunk c = tid + 256 i.
+  constexpr int KCH = D / 8, KIT = KCH;  // nk * KCH / 256 <= KCH
+  i32x4 kv[KIT];
+  // (loads are unconditional, from clamped in-bounds addresses; rows and keys past n
+  // are zeroed in registers)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = kc + i < n ? v_base[(size_t)d * n_pad + kc + i] : (bf16_t)0.0f;
-    }
-    *reinterpret_cast<bf16x8*>(Vs + d * vld + kc) = v;
+  for (int i = 0; i < KIT; ++i) {
+    const int c = tid + 256 * i, r = c / KCH, ch = c - (c / KCH) * KCH;
+    kv[i] = *reinterpret_cast<const i32x4*>(k_base + (size_t)min(r, n - 1) * D + ch * 8);
+  }
+  // V^T rows d = tid / 32 + 8 i, 16-byte key chunk tid % 32 (of nk / 8 <= 32): keys
+  // past n read as zero. The chunk read lies inside the n_pad-long row.
+  const int vch = tid & 31, kc = vch * 8, kc_in = min(kc, (n - 1) & ~7);
+  bf16x8 vv[D / 8];
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i)
+    vv[i] = *reinterpret_cast<const bf16x8*>(v_base + (size_t)((tid >> 5) + 8 * i) * n_pad + kc_in);
+#pragma unroll
+  for (int i = 0; i < KIT; ++i) {
+    const int c = tid + 256 * i, r = c / KCH, ch = c - (c / KCH) * KCH;
+    if (r < nk) *reinterpret_cast<i32x4*>(Ks + r * L::KLD + ch * 8) = r < n ? kv[i] : i32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (kc + e >= n) vv[i][e] = (bf16_t)0.0f;
+  if (kc < nk) {
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) *reinterpret_cast<bf16x8*>(Vs + ((tid >> 5) + 8 * i) * vld + kc) = vv[i];
   }
   __syncthreads();
 
@@ -790,9 +807,15 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
       for (int e = 0; e < 16; ++e) oacc[md][e] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
     const int any = any32[qt];
-    for (int kt = 0; kt < nt32; ++kt) {
-      if (!((any >> kt) & 1)) continue;  // no kept pair in this 32 x 32 block
-      const unsigned bits = (unsigned)keep32[tq * nt32 + kt];
+    // this lane's mask words, all requested before the first block (index clamped
+    // into the row; only kt < nt32 is used)
+    unsigned kbits[kMaxShortBlocks];
+#pragma unroll
+    for (int kt = 0; kt < kMaxShortBlocks; ++kt) kbits[kt] = (unsigned)keep32[tq * nt32 + min(kt, nt32 - 1)];
+#pragma unroll
+    for (int kt = 0; kt < kMaxShortBlocks; ++kt) {
+      if (kt >= nt32 || !((any >> kt) & 1)) continue;  // no kept pair in this 32 x 32 block
+      const unsigned bits = kbits[kt];
       // S^T block: keys kt*32 + 8 (e / 4) + 4 hi + (e % 4) of this lane's query
       f32x16 sc;
 #pragma unroll
