@@ -63,6 +63,13 @@ __all__ = [
     "window_token_map",
     "segment_importance",
     "descending_order",
+    "ORDERINGS",
+    "morton_code",
+    "hilbert_index",
+    "splitmix64",
+    "order_key",
+    "ascending_order",
+    "segment_order",
     "stripe_sort",
     "routed_count",
     "routed_tokens",
@@ -247,6 +254,107 @@ def routed_rank_order(s: np.ndarray, token_map_row: np.ndarray, mlp_density: flo
     picked = token_map_row[s[:k]]
     assert (picked >= 0).all()
     return picked
+
+
+# ----------------------------------------------------------------------------
+# Ordering variants (the pages' other names for the token order)
+# ----------------------------------------------------------------------------
+#
+# "Technische Samenvatting: SparseSAM" (abstract) and its method section call the
+# permutation a Z-order (Morton) ordering, and the README's method registry lists
+# random and Hilbert-curve orders next to the importance order. Reading: each
+# variant replaces only the sort key of a segment's slots -- ascending key instead
+# of descending importance, ties to the lower slot, window pads after every real
+# slot -- and everything downstream (stripe-sort, pattern, keep-set = the first K of
+# the same order) is unchanged. Keys come from the slot's position inside its
+# segment: (y, x) on the token grid for a global segment, (ly, lx) inside the window
+# for a windowed one.
+
+ORDERINGS = ("importance", "zorder", "hilbert", "random")
+
+
+def morton_code(y: int, x: int) -> int:
+    """Z-order (Morton) code of cell (y, x): bit b of x goes to bit 2b, bit b of y to
+    bit 2b + 1, so x varies fastest inside every 2 x 2 block."""
+    code = 0
+    for b in range(16):
+        code |= ((x >> b) & 1) << (2 * b)
+        code |= ((y >> b) & 1) << (2 * b + 1)
+    return code
+
+
+def hilbert_index(side: int, y: int, x: int) -> int:
+    """Position of cell (y, x) along the Hilbert curve that fills a side x side square
+    (side a power of two), written from its recursive construction: the square splits
+    into quadrants visited in the order (x, y) = (low, low), (low, high), (high, high),
+    (high, low); the curves inside the first and last quadrants are the half-size curve
+    mirrored in the main diagonal and in the anti-diagonal respectively, so that each
+    sub-curve starts next to where the previous one ended. The curve starts at (0, 0)
+    and ends at (x, y) = (side - 1, 0)."""
+    if side == 1:
+        return 0
+    h = side // 2
+    qx, qy = int(x >= h), int(y >= h)
+    lx, ly = x - h * qx, y - h * qy
+    if qy == 0 and qx == 0:
+        q, cx, cy = 0, ly, lx                    # mirrored in the main diagonal
+    elif qy == 1 and qx == 0:
+        q, cx, cy = 1, lx, ly
+    elif qy == 1 and qx == 1:
+        q, cx, cy = 2, lx, ly
+    else:
+        q, cx, cy = 3, h - 1 - ly, h - 1 - lx    # mirrored in the anti-diagonal
+    return q * h * h + hilbert_index(h, cy, cx)
+
+
+def splitmix64(state: int) -> int:
+    """First output of the SplitMix64 generator started at `state` (Steele, Lea and
+    Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014, with the
+    mixing constants of its widely used 64-bit variant): the state advances by the
+    golden-ratio increment and the result goes through two xor-shift-multiply rounds
+    and a final xor-shift."""
+    m = (1 << 64) - 1
+    z = (state + 0x9E3779B97F4A7C15) & m
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & m
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & m
+    return z ^ (z >> 31)
+
+
+def order_key(ordering: str, slot: int, seg_h: int, seg_w: int, seed: int = 0) -> int:
+    """Ascending sort key of a segment slot (slot = ly * seg_w + lx) for a non-importance
+    ordering. Hilbert keys use the smallest power-of-two square covering the segment;
+    random keys are the top 31 bits of splitmix64(seed * 2^32 + slot), the same order in
+    every segment and image."""
+    y, x = divmod(slot, seg_w)
+    if ordering == "zorder":
+        return morton_code(y, x)
+    if ordering == "hilbert":
+        side = 1
+        while side < max(seg_h, seg_w):
+            side *= 2
+        return hilbert_index(side, y, x)
+    if ordering == "random":
+        return splitmix64(((seed & 0xFFFFFFFF) << 32) | slot) >> 33
+    raise ValueError("unknown ordering %r" % (ordering,))
+
+
+def ascending_order(keys, valid=None) -> np.ndarray:
+    """Slot ids sorted by key ascending, ties to the lower slot, slots with valid ==
+    False after every valid slot in index order."""
+    n = len(keys)
+    ok = np.ones(n, bool) if valid is None else np.asarray(valid, bool)
+    return np.array(sorted(range(n), key=lambda i: (0 if ok[i] else 1, int(keys[i]) if ok[i] else 0, i)),
+                    dtype=np.int64)
+
+
+def segment_order(ordering: str, imp: np.ndarray, token_map_row: np.ndarray, seg_h: int, seg_w: int,
+                  seed: int = 0) -> np.ndarray:
+    """The sorted slot list of one segment under `ordering` (see ORDERINGS)."""
+    valid = token_map_row >= 0
+    if ordering == "importance":
+        return descending_order(segment_importance(imp, token_map_row), valid=valid)
+    keys = [order_key(ordering, s, seg_h, seg_w, seed) for s in range(token_map_row.shape[0])]
+    return ascending_order(keys, valid=valid)
 
 
 # ----------------------------------------------------------------------------
