@@ -440,6 +440,18 @@ def main():
     extra["density_0.3"]["mlp_pct_peak"] = round(100 * extra["density_0.3"]["mlp_tflops"] / PEAK_BF16_TFLOPS, 2)
     del wl3
 
+    # the other token orders of the pages (Z-order, Hilbert curve, seeded random) ahead of the
+    # same stripe-sort: the whole step and the permutation alone
+    extra["orderings"] = {}
+    for ordering in ("zorder", "hilbert", "random"):
+        wlo = Workload(cfg.with_(ordering=ordering, order_seed=12345), dev)
+        wlo.step()
+        so = time_region(wlo.step, 30, 5)
+        po = time_region(lambda: ss.permute(wlo.plan, wlo.imp, out=(wlo.perm, wlo.inv, wlo.routed)), 50, 5)
+        extra["orderings"][ordering] = {"step_ms": round(so, 5), "tokens_per_s": round(tokens / (so * 1e-3), 1),
+                                        "permute_ms": round(po, 5)}
+        del wlo
+
     if not args.no_dense:
         cfgd = cfg.with_(attn_density=1.0, mlp_density=1.0)
         wld = Workload(cfgd, dev)

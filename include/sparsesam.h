@@ -56,6 +56,28 @@ typedef enum sparsesam_dtype {
 typedef struct sparsesam_plan* sparsesam_plan_t;
 
 /*
+ * Token order ahead of the stripe-sort. "Technische Samenvatting: SparseSAM" (gist.science)
+ * orders tokens by Sobel importance (method section, 1. Stripe-Sort Attention) and also
+ * calls the ordering a Z-order (Morton) one (abstract); the SparseSAM README's method
+ * registry lists random and Hilbert-curve orders beside it. The variants replace only the
+ * sort key (ascending key, ties to the lower slot, window pads last); the stripe-sort, the
+ * pattern and the keep-set (the first K of the same order) are unchanged. Keys come from a
+ * slot's position in its segment ((y, x) on the grid, (ly, lx) in a window):
+ *   ZORDER:  bit b of x at bit 2b, bit b of y at bit 2b + 1;
+ *   HILBERT: index along the Hilbert curve of the smallest power-of-two square covering the
+ *            segment, starting at (0, 0), quadrants visited (x, y) = (lo, lo), (lo, hi),
+ *            (hi, hi), (hi, lo);
+ *   RANDOM:  top 31 bits of the first SplitMix64 output from state order_seed * 2^32 + slot
+ *            (the same order in every segment and image).
+ */
+typedef enum sparsesam_ordering {
+  SPARSESAM_ORDER_IMPORTANCE = 0,
+  SPARSESAM_ORDER_ZORDER = 1,
+  SPARSESAM_ORDER_HILBERT = 2,
+  SPARSESAM_ORDER_RANDOM = 3
+} sparsesam_ordering;
+
+/*
  * What one plan describes: the segments of an image (one global segment of
  * grid_h*grid_w tokens, or window x window windows over the grid padded up to
  * multiples of `window`), the stripe-sort and its static attention pattern, the
@@ -89,6 +111,8 @@ typedef struct sparsesam_plan_desc {
   int32_t mlp_hidden;
   int32_t max_batch;       /* largest batch a call will pass; sizes the workspace */
   int32_t dtype;           /* sparsesam_dtype */
+  int32_t ordering;        /* sparsesam_ordering: the token order ahead of the stripe-sort (0 = importance) */
+  uint32_t order_seed;     /* seed of SPARSESAM_ORDER_RANDOM */
 } sparsesam_plan_desc;
 
 typedef struct sparsesam_plan_info {
@@ -153,8 +177,10 @@ sparsesam_status sparsesam_importance(const float* img, int32_t batch, int32_t h
  *          token) of the keep-set. Per image, segment by segment (segment w starts at
  *          the sum of the keep-set sizes of segments 0..w-1), each segment's K tokens in
  *          the order below: most important first.
- * Order: importance descending, ties by lower slot, -0.0 == +0.0, NaN after every
- * number, window pad slots after every real slot (so no pad enters the keep-set). The
+ * Order (plan ordering IMPORTANCE): importance descending, ties by lower slot, -0.0 ==
+ * +0.0, NaN after every number, window pad slots after every real slot (so no pad enters
+ * the keep-set); the other orderings replace the importance key as described at
+ * sparsesam_ordering (imp is then not read). The
  * stripe-sort reads the sorted list as an (N/g) x g matrix, transposes it and
  * flattens it: perm[p] = sorted[g * (p % S) + p / S]. All outputs are integers and
  * exactly determined.

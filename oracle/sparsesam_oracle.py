@@ -472,8 +472,9 @@ def block_forward(x: np.ndarray, imp: np.ndarray, w: dict, cfg, radius: int = No
         for seg in range(tmap.shape[0]):
             row = tmap[seg]
             real = row >= 0
-            simp = segment_importance(imp[i], row)
-            s = descending_order(simp, valid=real)
+            seg_h, seg_w = (gh, gw) if cfg.window == 0 else (cfg.window, cfg.window)
+            s = segment_order(getattr(cfg, "ordering", "importance"), imp[i], row, seg_h, seg_w,
+                              getattr(cfg, "order_seed", 0))
             perm, inv = stripe_sort(s, cfg.stripes)
             parts["perm"].append(perm)
             parts["inv"].append(inv)

@@ -48,17 +48,25 @@ def _need(t, name, dtype=None, shape=None, device=None):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
+# token orders ahead of the stripe-sort, in the C enum's order (sparsesam_ordering)
+ORDERINGS = ("importance", "zorder", "hilbert", "random")
+
+
 class Plan:
     """Static description of one block type: segments, stripe-sort pattern, keep-set size."""
 
     def __init__(self, grid_h, grid_w, window, stripes, block, global_tokens, band_radius, attn_density,
-                 mlp_density, channels, heads, head_dim, mlp_hidden, max_batch, dtype):
+                 mlp_density, channels, heads, head_dim, mlp_hidden, max_batch, dtype, ordering="importance",
+                 order_seed=0):
         lib = _lib.load()
         self._lib = lib
         self.dtype = dtype
+        if ordering not in ORDERINGS:
+            raise ValueError("ordering must be one of %s" % (ORDERINGS,))
         self.desc = _lib.PlanDesc(grid_h, grid_w, window, stripes, block, global_tokens, band_radius,
                                   attn_density, mlp_density, channels, heads, head_dim, mlp_hidden, max_batch,
-                                  SPARSESAM_BF16 if dtype == "bf16" else SPARSESAM_F32)
+                                  SPARSESAM_BF16 if dtype == "bf16" else SPARSESAM_F32, ORDERINGS.index(ordering),
+                                  order_seed & 0xFFFFFFFF)
         h = ctypes.c_void_p()
         check(lib.sparsesam_plan_create(ctypes.byref(self.desc), ctypes.byref(h)), "sparsesam_plan_create")
         self._h = h
@@ -71,7 +79,8 @@ class Plan:
     def from_config(cls, cfg, max_batch=None):
         return cls(cfg.grid, cfg.grid, cfg.window, cfg.stripes, cfg.block, cfg.global_tokens, cfg.band_radius,
                    cfg.attn_density, cfg.mlp_density, cfg.channels, cfg.heads, cfg.head_dim, cfg.mlp_hidden,
-                   max_batch or cfg.batch, cfg.dtype)
+                   max_batch or cfg.batch, cfg.dtype, getattr(cfg, "ordering", "importance"),
+                   getattr(cfg, "order_seed", 0))
 
     @property
     def handle(self):

@@ -42,6 +42,7 @@ class PlanDesc(ctypes.Structure):
         ("band_radius", ctypes.c_int32), ("attn_density", ctypes.c_float), ("mlp_density", ctypes.c_float),
         ("channels", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("mlp_hidden", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("ordering", ctypes.c_int32), ("order_seed", ctypes.c_uint32),
     ]
 
 

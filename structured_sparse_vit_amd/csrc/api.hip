@@ -105,6 +105,8 @@ static sparsesam_status validate_desc(const sparsesam_plan_desc& d) {
   if (d.mlp_hidden < 1) return invalid("mlp_hidden must be positive");
   if (d.max_batch < 1) return invalid("max_batch must be >= 1");
   if (d.dtype != SPARSESAM_F32 && d.dtype != SPARSESAM_BF16) return invalid("dtype must be SPARSESAM_F32 or SPARSESAM_BF16");
+  if (d.ordering < SPARSESAM_ORDER_IMPORTANCE || d.ordering > SPARSESAM_ORDER_RANDOM)
+    return invalid("ordering must be a sparsesam_ordering value");
   if (d.channels > 1536) return unsupported("channels above 1536 are not supported");
   if (d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 80 && d.head_dim != 128)
     return unsupported("head_dim must be 32, 64, 80 or 128");
@@ -423,7 +425,8 @@ sparsesam_status sparsesam_permute(sparsesam_plan_t p, const float* imp, int32_t
   if (st != SPARSESAM_OK) return st;
   if (batch < 0) return invalid("batch must be >= 0");
   if (batch == 0) return SPARSESAM_OK;
-  if (!imp || !perm || !inv || !routed) return invalid("imp, perm, inv and routed must not be null");
+  if (!perm || !inv || !routed) return invalid("perm, inv and routed must not be null");
+  if (!imp && p->desc.ordering == SPARSESAM_ORDER_IMPORTANCE) return invalid("imp must not be null");
   hipError_t e = launch_permute(*p, imp, batch, perm, inv, routed, (hipStream_t)stream);
   return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_permute launch");
 }

@@ -7,7 +7,10 @@
 // keep-set is the top of the same deterministic order.
 //
 // The order is total: importance descending (-0.0 == +0.0, NaN after every number,
-// pad slots after every real slot), then slot ascending. A slot's rank is therefore
+// pad slots after every real slot), then slot ascending -- or, for the plan's other
+// orderings (Z-order, Hilbert, seeded random; the same page's abstract and the method
+// registry of the SparseSAM README name them), an ascending position-derived key with
+// the same tie and pad rules. A slot's rank is therefore
 // the number of slots that precede it, and everything follows from the rank alone:
 // rank rho sits at stripe rho % g, offset rho / g, i.e. position (rho % g) * S + rho / g,
 // and the slot is in the keep-set iff rho < K, at index rho of the segment's part of
@@ -37,6 +40,54 @@ __device__ __forceinline__ uint32_t desc_key(float f) {
 }
 constexpr uint32_t kPadKey = 0xFFFFFFFFu;  // pad slots: after every real slot
 
+// Ascending keys of the other token orders (sparsesam_ordering), from a slot's position
+// (y, x) in its segment. All stay below kPadKey.
+// Z-order: bit b of x at bit 2b, bit b of y at bit 2b + 1.
+__device__ __forceinline__ uint32_t zorder_key(uint32_t y, uint32_t x) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int b = 0; b < 16; ++b) c |= (((x >> b) & 1u) << (2 * b)) | (((y >> b) & 1u) << (2 * b + 1));
+  return c;
+}
+// Hilbert curve over a side x side square (a power of two), from the coarsest level down:
+// the quadrants are visited (x, y) = (lo, lo), (lo, hi), (hi, hi), (hi, lo); inside the
+// first one the half-size curve is mirrored in the main diagonal, inside the last one in
+// the anti-diagonal, so the cell's coordinates are mapped the same way before the next
+// level.
+__device__ __forceinline__ uint32_t hilbert_key(int side, int y, int x) {
+  uint32_t d = 0;
+  for (int h = side >> 1; h >= 1; h >>= 1) {
+    const int qx = x >= h, qy = y >= h;
+    int lx = x - h * qx, ly = y - h * qy, q;
+    if (qy) {
+      q = qx ? 2 : 1;
+    } else if (!qx) {
+      q = 0;
+      const int t = lx;  // main-diagonal mirror
+      lx = ly;
+      ly = t;
+    } else {
+      q = 3;
+      const int t = h - 1 - ly;  // anti-diagonal mirror
+      ly = h - 1 - lx;
+      lx = t;
+    }
+    d += (uint32_t)(q * h * h);
+    x = lx;
+    y = ly;
+  }
+  return d;
+}
+// Seeded random order: top 31 bits of the first SplitMix64 output (Steele, Lea and Flood,
+// OOPSLA 2014) from state seed * 2^32 + slot.
+__device__ __forceinline__ uint32_t random_key(uint32_t seed, uint32_t slot) {
+  uint64_t z = (((uint64_t)seed << 32) | slot) + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return (uint32_t)(z >> 33);
+}
+
 // rank_kernel layout: a workgroup of kw wavefronts ranks tpw slots of one segment
 // (tpw = 16 or 64). The segment's keys sit in LDS as 64-bit words (order key << 32 |
 // slot), so "slot j precedes slot s" is one unsigned compare of two words and every
@@ -50,7 +101,9 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
                                                                   const int* __restrict__ seg_k,
                                                                   const int* __restrict__ seg_off,
                                                                   int routed_per_image, int* __restrict__ perm,
-                                                                  int* __restrict__ inv, int* __restrict__ routed) {
+                                                                  int* __restrict__ inv, int* __restrict__ routed,
+                                                                  int ordering, uint32_t seed, int seg_w,
+                                                                  int hilbert_side) {
   extern __shared__ __attribute__((aligned(16))) uint64_t key_lds[];  // padded to a multiple of 64
   __shared__ int part[kMaxRankWaves * 64];
   const int seg = blockIdx.x / chunks, chunk = blockIdx.x - (blockIdx.x / chunks) * chunks;
@@ -64,7 +117,17 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
 #pragma unroll 4
   for (int s = tid; s < n64; s += blockDim.x) {
     const int row = s < n ? map.row_of(seg, s) : -1;
-    const uint32_t k = row >= 0 ? desc_key(im[row - img * tokens]) : kPadKey;
+    uint32_t k = kPadKey;
+    if (row >= 0) {
+      if (ordering == SPARSESAM_ORDER_IMPORTANCE) {
+        k = desc_key(im[row - img * tokens]);
+      } else {
+        const int y = s / seg_w, x = s - (s / seg_w) * seg_w;
+        k = ordering == SPARSESAM_ORDER_ZORDER    ? zorder_key((uint32_t)y, (uint32_t)x)
+            : ordering == SPARSESAM_ORDER_HILBERT ? hilbert_key(hilbert_side, y, x)
+                                                  : random_key(seed, (uint32_t)s);
+      }
+    }
     key_lds[s] = ((uint64_t)k << 32) | (uint32_t)s;
   }
   __syncthreads();
@@ -124,8 +187,14 @@ hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, 
   hipError_t e = hipFuncSetAttribute((const void*)rank_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)key_bytes);
   if (e != hipSuccess) return e;
+  // segment shape for the position-based orders: the grid, or one window
+  const int seg_h = p.desc.window ? p.desc.window : p.desc.grid_h;
+  const int seg_w = p.desc.window ? p.desc.window : p.desc.grid_w;
+  int side = 1;
+  while (side < std::max(seg_h, seg_w)) side *= 2;
   hipLaunchKernelGGL(rank_kernel, dim3((unsigned)(segs * chunks)), dim3(64 * kw), key_bytes, st, imp, p.segmap(),
-                     p.n, p.desc.stripes, chunks, tpw, p.d_seg_k, p.d_seg_off, p.routed_per_image, perm, inv, routed);
+                     p.n, p.desc.stripes, chunks, tpw, p.d_seg_k, p.d_seg_off, p.routed_per_image, perm, inv, routed,
+                     (int)p.desc.ordering, p.desc.order_seed, seg_w, side);
   return hipGetLastError();
 }
 

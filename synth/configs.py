@@ -34,6 +34,8 @@ class Config:
     mlp_density: float
     dtype: str            # "f32" or "bf16": weights and matrix-engine operands
     layers: int = 1       # encoder depth (1 = a single block)
+    ordering: str = "importance"  # token order ahead of the stripe-sort (see oracle.ORDERINGS)
+    order_seed: int = 0           # seed of the "random" ordering
 
     @property
     def grid(self) -> int:

@@ -13,7 +13,11 @@ REL_L2 = 5e-3
 
 
 def config(key):
-    """Named workloads of the tests: the configs plus reduced encoder blocks."""
+    """Named workloads of the tests: the configs plus reduced encoder blocks; "key:order"
+    is workload `key` with another token ordering (seed 12345 for the random one)."""
+    if ":" in key:
+        base, ordering = key.split(":")
+        return config(base).with_(ordering=ordering, order_seed=12345)
     if key == "c4g":
         return global_variant(get_config("c4")).with_(batch=1)
     if key == "c4w":

@@ -30,12 +30,13 @@ def _plan(cfg, **over):
 def _oracle_perm(cfg, imp):
     """Oracle perm / inv / keep-set (segment by segment, rank order) for a batch of maps."""
     tm = oracle.segments_for_image(cfg.grid, cfg.grid, cfg.window)
+    side = cfg.window or cfg.grid
     perms, invs, routed = [], [], []
     tokens = cfg.grid * cfg.grid
     for b in range(imp.shape[0]):
         rs = []
         for row in tm:
-            s = oracle.descending_order(oracle.segment_importance(imp[b], row), valid=row >= 0)
+            s = oracle.segment_order(cfg.ordering, imp[b], row, side, side, cfg.order_seed)
             p, i = oracle.stripe_sort(s, cfg.stripes)
             perms.append(p)
             invs.append(i)
@@ -79,6 +80,22 @@ def test_importance_edge_images():
 def test_permute_bit_exact(key):
     _say("permute", key)
     cfg = config(key)
+    plan = _plan(cfg)
+    imp = oracle_importance(key)
+    perm, inv, routed = ss.permute(plan, torch.from_numpy(imp).to(DEV))
+    wp, wi, wr = _oracle_perm(cfg, imp)
+    assert np.array_equal(perm.cpu().numpy(), wp)
+    assert np.array_equal(inv.cpu().numpy(), wi)
+    assert np.array_equal(routed.cpu().numpy(), wr)
+
+
+@pytest.mark.parametrize("ordering", ["zorder", "hilbert", "random"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "ragged"])
+def test_permute_orderings_bit_exact(key, ordering):
+    """The other token orders (Z-order, Hilbert, seeded random): perm, inv and keep-set
+    bit-exact against the oracle, windows with pads included."""
+    _say("permute", key, ordering)
+    cfg = config(key).with_(ordering=ordering, order_seed=12345)
     plan = _plan(cfg)
     imp = oracle_importance(key)
     perm, inv, routed = ss.permute(plan, torch.from_numpy(imp).to(DEV))
@@ -236,7 +253,8 @@ def _check_block(key, r, gain):
     assert delta_rel <= bar, "block %s: block delta rel-L2 %.3e > %.1e" % (key, delta_rel, bar)
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3", "ragged", "c4g", "c4w"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "ragged", "c4g", "c4w", "c1:zorder", "c3b1:hilbert",
+                                 "c2:random"])
 def test_block_parity(key):
     _say("block", key)
     _check_block(key, _run_block(key), 1.0)
