@@ -16,10 +16,13 @@
 //    v_mfma_f32_32x32x16_bf16, so a lane holds one query's scores (the row max needs
 //    one permlane swap with lane ^ 32) and one query's output column. K tile rows are
 //    stored in a permuted order so that the S^T accumulator already has the layout of
-//    the P^T operand. Online softmax in fp32 with exp2, the scale folded into one
-//    multiply-add per score, and the output rescale skipped unless a row max passes
-//    its reference by more than 2^8.
-//  * attn_d80_kernel: the same work items for head_dim 80.
+//    the P^T operand. Online softmax in fp32 with exp2: Q carries the scale and
+//    log2(e), a fifth MFMA k-step subtracts the bf16-exact running reference, so a
+//    probability costs one v_exp_f32; the reference moves (and O is rescaled) only on
+//    the first tile and when a lane's probability sum passes 2^64. The unit is a
+//    template on the key-parity count, so the per-step tile loads have no branches.
+//  * attn_d80_kernel: the same work items for head_dim 80 (running max with a 2^8
+//    slack, denominators from a ones row of the third V^T block).
 //  * attn_short_kernel: short segments (windows, N <= 256), one workgroup per
 //    (segment, head) with the segment's K and V^T in LDS.
 //  * attn_combine_kernel: merges the partial results of rows split over several
