@@ -68,10 +68,24 @@ __global__ void __launch_bounds__(1024) sobel_pool_strip_kernel(const float* __r
   const int x0 = blockIdx.x * kStripW, ty = blockIdx.y, b = blockIdx.z;
   const int y0 = ty * 16;
   const float* P = img + (size_t)b * height * width;
-  for (int i = threadIdx.x; i < 18 * kHaloW; i += 1024) {
+  // every load of the strip is issued before the first LDS store (addresses clamped
+  // into the image, values outside it replaced by zero afterwards)
+  constexpr int kFill = 18 * kHaloW, kIters = (kFill + 1023) / 1024;
+  float fv[kIters];
+  bool inside[kIters];
+#pragma unroll
+  for (int k = 0; k < kIters; ++k) {
+    const int i = threadIdx.x + 1024 * k;
     const int rr = i / kHaloW, cc = i - (i / kHaloW) * kHaloW;
     const int yy = y0 - 1 + rr, xx = x0 - 1 + cc;
-    tile[rr][cc] = (yy >= 0 && yy < height && xx >= 0 && xx < width) ? P[(size_t)yy * width + xx] : 0.0f;
+    const int cy = min(max(yy, 0), height - 1), cx = min(max(xx, 0), width - 1);
+    fv[k] = P[(size_t)cy * width + cx];
+    inside[k] = (yy >= 0) & (yy < height) & (xx >= 0) & (xx < width);
+  }
+#pragma unroll
+  for (int k = 0; k < kIters; ++k) {
+    const int i = threadIdx.x + 1024 * k;
+    if (i < kFill) tile[i / kHaloW][i - (i / kHaloW) * kHaloW] = inside[k] ? fv[k] : 0.0f;
   }
   __syncthreads();
   {

@@ -113,22 +113,37 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
   const int img = map.f_spi.div(seg);
   const float* im = imp + (size_t)img * tokens;
   const int n64 = (n + 63) & ~63;
-  // keys past n are pad keys with index >= n: they never precede a real slot
-#pragma unroll 4
-  for (int s = tid; s < n64; s += blockDim.x) {
-    const int row = s < n ? map.row_of(seg, s) : -1;
-    uint32_t k = kPadKey;
-    if (row >= 0) {
-      if (ordering == SPARSESAM_ORDER_IMPORTANCE) {
-        k = desc_key(im[row - img * tokens]);
-      } else {
-        const int y = s / seg_w, x = s - (s / seg_w) * seg_w;
-        k = ordering == SPARSESAM_ORDER_ZORDER    ? zorder_key((uint32_t)y, (uint32_t)x)
-            : ordering == SPARSESAM_ORDER_HILBERT ? hilbert_key(hilbert_side, y, x)
-                                                  : random_key(seed, (uint32_t)s);
-      }
+  // keys past n are pad keys with index >= n: they never precede a real slot. Four
+  // slots per thread at a time, their importance loads all issued before the first
+  // key is formed (the index is clamped to a real token; pads discard the value).
+  constexpr int kFillUnroll = 4;
+  for (int base = 0; base < n64; base += kFillUnroll * (int)blockDim.x) {
+    int rows[kFillUnroll];
+    float vals[kFillUnroll];
+#pragma unroll
+    for (int u = 0; u < kFillUnroll; ++u) {
+      const int s = base + tid + u * (int)blockDim.x;
+      rows[u] = s < n ? map.row_of(seg, s) : -1;
+      vals[u] = 0.0f;
+      if (ordering == SPARSESAM_ORDER_IMPORTANCE) vals[u] = im[max(rows[u] - img * tokens, 0)];
     }
-    key_lds[s] = ((uint64_t)k << 32) | (uint32_t)s;
+#pragma unroll
+    for (int u = 0; u < kFillUnroll; ++u) {
+      const int s = base + tid + u * (int)blockDim.x;
+      if (s >= n64) break;
+      uint32_t k = kPadKey;
+      if (rows[u] >= 0) {
+        if (ordering == SPARSESAM_ORDER_IMPORTANCE) {
+          k = desc_key(vals[u]);
+        } else {
+          const int y = s / seg_w, x = s - (s / seg_w) * seg_w;
+          k = ordering == SPARSESAM_ORDER_ZORDER    ? zorder_key((uint32_t)y, (uint32_t)x)
+              : ordering == SPARSESAM_ORDER_HILBERT ? hilbert_key(hilbert_side, y, x)
+                                                    : random_key(seed, (uint32_t)s);
+        }
+      }
+      key_lds[s] = ((uint64_t)k << 32) | (uint32_t)s;
+    }
   }
   __syncthreads();
   const int subs = 64 / tpw;  // lanes per slot
