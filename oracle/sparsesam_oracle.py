@@ -35,6 +35,14 @@ What it computes, step by step, with the passage each step follows:
   residual set is zero; K = floor(d * n_real + 1/2), at least 1.
 * one permutation per image (global blocks) or per window (windowed blocks),
   reused by every block of that type (the closing paragraph of that section).
+* relative-position bias (optional) -- the pages name fused "FA2 + rel-pos"
+  kernels in the SparseSAM repository's kernel folder (the README's repository
+  layout) but never define the term. Reading: SAM's image encoder's decomposed
+  relative position (Kirillov et al., "Segment Anything", 2023, after Li et al.,
+  MViTv2, CVPR 2022): a query at segment coordinates (y, x) adds
+  <q, Rh[y - y' + Sh - 1]> + <q, Rw[x - x' + Sw - 1]> to its logit for the key at
+  (y', x'), with the unscaled query, tables shared by the heads of a block and
+  Sh x Sw the segment shape (the grid, or the padded window).
 
 Block structure (not on the pages; SAM encoder conventions): pre-LN block,
 LayerNorm eps 1e-6 with biased variance, biases on qkv/proj/fc1/fc2, exact-erf
@@ -78,6 +86,7 @@ __all__ = [
     "band_radius",
     "token_mask",
     "masked_attention",
+    "rel_pos_bias",
     "layer_norm",
     "gelu",
     "routed_mlp",
@@ -403,16 +412,43 @@ def token_mask(inv: np.ndarray, stripes: int, block: int, global_tokens: int, ra
 # ----------------------------------------------------------------------------
 
 def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
-                     scale: float) -> np.ndarray:
-    """softmax(q k^T * scale) v with pairs outside ``mask`` removed (score -inf).
+                     scale: float, bias: np.ndarray = None) -> np.ndarray:
+    """softmax(q k^T * scale + bias) v with pairs outside ``mask`` removed (score -inf).
 
-    q, k, v: [n, D]; mask: [n, n] bool (every row keeps at least one key).
+    q, k, v: [n, D]; mask: [n, n] bool (every row keeps at least one key); bias:
+    [n, n] added to the logits (None: no bias).
     """
     s = (q.astype(np.float64) @ k.astype(np.float64).T) * scale
+    if bias is not None:
+        s = s + bias
     s = np.where(mask, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
     return (e / e.sum(axis=1, keepdims=True)) @ v.astype(np.float64)
+
+
+def rel_pos_bias(q: np.ndarray, seg_h: int, seg_w: int, rel_h: np.ndarray, rel_w: np.ndarray) -> np.ndarray:
+    """Decomposed relative-position bias [n, n] of one segment and head (n = seg_h * seg_w).
+
+    q: [n, D] queries in segment slot order (slot = y * seg_w + x), unscaled; rel_h:
+    [2 seg_h - 1, D], rel_w: [2 seg_w - 1, D]. The steps of SAM's encoder: the table
+    rows for every (query row, key row) offset, Rh[y, y'] = rel_h[y - y' + seg_h - 1];
+    the per-query row terms B_h[i, y'] = <q_i, Rh[y_i, y']> (likewise B_w with columns);
+    the bias of the pair (i, k) is B_h[i, y_k] + B_w[i, x_k].
+    """
+    q = q.astype(np.float64)
+    n, D = q.shape
+    assert n == seg_h * seg_w
+    assert rel_h.shape == (2 * seg_h - 1, D) and rel_w.shape == (2 * seg_w - 1, D)
+    yy = np.arange(seg_h)
+    xx = np.arange(seg_w)
+    Rh = rel_h.astype(np.float64)[yy[:, None] - yy[None, :] + seg_h - 1]  # [seg_h, seg_h, D]
+    Rw = rel_w.astype(np.float64)[xx[:, None] - xx[None, :] + seg_w - 1]  # [seg_w, seg_w, D]
+    slot = np.arange(n)
+    y, x = slot // seg_w, slot % seg_w
+    b_h = np.einsum("id,ikd->ik", q, Rh[y])  # [n, seg_h]: query i against key row k
+    b_w = np.einsum("id,ikd->ik", q, Rw[x])  # [n, seg_w]
+    return b_h[:, y] + b_w[:, x]
 
 
 def layer_norm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float = 1e-6) -> np.ndarray:
@@ -452,7 +488,9 @@ def block_forward(x: np.ndarray, imp: np.ndarray, w: dict, cfg, radius: int = No
     ``cfg`` (window, stripes, block, global_tokens, band_radius, attn_density,
     mlp_density, heads, head_dim). Attention is dense with an explicit mask in the
     original token order, per segment; window pad slots carry h = 0 as keys and
-    queries and their outputs are dropped.
+    queries and their outputs are dropped. With w["rel_h"] and w["rel_w"] set, every
+    head adds the relative-position bias (rel_pos_bias) of its segment to its logits;
+    pads have their padded-window coordinates.
     """
     b, gh, gw, C = x.shape
     H, D = cfg.heads, cfg.head_dim
@@ -484,11 +522,13 @@ def block_forward(x: np.ndarray, imp: np.ndarray, w: dict, cfg, radius: int = No
             qkv = _linear(hs, w["w_qkv"], w["b_qkv"])
             mask = token_mask(inv, cfg.stripes, cfg.block, cfg.global_tokens, radius)
             o = np.empty((n, C))
+            rel = w.get("rel_h") is not None
             for hd in range(H):
                 q = qkv[:, hd * D:(hd + 1) * D]
                 k = qkv[:, C + hd * D:C + (hd + 1) * D]
                 v = qkv[:, 2 * C + hd * D:2 * C + (hd + 1) * D]
-                o[:, hd * D:(hd + 1) * D] = masked_attention(q, k, v, mask, scale)
+                bias = rel_pos_bias(q, seg_h, seg_w, w["rel_h"], w["rel_w"]) if rel else None
+                o[:, hd * D:(hd + 1) * D] = masked_attention(q, k, v, mask, scale, bias)
             attn_out[row[real]] = o[real]
         x1 = xf[i] + _linear(attn_out, w["w_proj"], w["b_proj"])
         routed = np.sort(np.concatenate(routed_img))

@@ -13,7 +13,7 @@ no clipping; stored as fp32.
 """
 import numpy as np
 
-_PURPOSE = {"image": 1, "features": 2, "weights": 3}
+_PURPOSE = {"image": 1, "features": 2, "weights": 3, "rel_pos": 4}
 
 
 def _rng(purpose: str, seed: int, index: int = 0) -> np.random.Generator:
@@ -103,6 +103,21 @@ def block_weights(cfg, seed: int = 0, layer: int = 0, gain: float = 1.0) -> dict
         for k in ("w_qkv", "b_qkv", "w_proj", "b_proj", "w1", "b1", "w2", "b2"):
             w[k] = round_to_bf16(w[k])
     return w
+
+
+def rel_pos_tables(cfg, seed: int = 0, layer: int = 0, std: float = 0.2) -> tuple:
+    """Decomposed relative-position tables of one block: rel_h [2 Sh - 1, D] and rel_w
+    [2 Sw - 1, D] fp32 ~ N(0, std), Sh x Sw the segment shape (the grid for global
+    attention, the window otherwise). SAM starts them at zero; a trained encoder's are
+    not, so the synthetic ones are drawn at a scale where the bias moves the logits by
+    about one unit.
+    """
+    rng = _rng("rel_pos", seed, layer)
+    side = cfg.window if cfg.window else cfg.grid
+    D = cfg.head_dim
+    rh = (rng.standard_normal((2 * side - 1, D), dtype=np.float32) * np.float32(std)).astype(np.float32)
+    rw = (rng.standard_normal((2 * side - 1, D), dtype=np.float32) * np.float32(std)).astype(np.float32)
+    return rh, rw
 
 
 def encoder_global_layers(layers: int) -> list:
