@@ -113,6 +113,8 @@ typedef struct sparsesam_plan_desc {
   int32_t dtype;           /* sparsesam_dtype */
   int32_t ordering;        /* sparsesam_ordering: the token order ahead of the stripe-sort (0 = importance) */
   uint32_t order_seed;     /* seed of SPARSESAM_ORDER_RANDOM */
+  int32_t rel_pos;         /* 1: blocks add the relative-position bias (block weights rel_pos_h,
+                              rel_pos_w; segments of at most 64 x 64); 0: no bias */
 } sparsesam_plan_desc;
 
 typedef struct sparsesam_plan_info {
@@ -132,6 +134,8 @@ typedef struct sparsesam_plan_info {
                                    (0 when the plan's attention needs none) */
   int32_t has_device_copy;      /* 1 when the plan can run on the current device */
   int32_t device;               /* HIP device of the device copy, -1 when none */
+  size_t relpos_workspace_bytes; /* workspace sparsesam_attn_relpos needs for max_batch images'
+                                    segments (0 when the segments exceed 64 x 64) */
 } sparsesam_plan_info;
 
 /* Plan lifecycle. sparsesam_plan_create validates the description, builds the
@@ -210,6 +214,32 @@ sparsesam_status sparsesam_attn(sparsesam_plan_t plan, int32_t segments, const v
                                 void* stream);
 
 /*
+ * (3b) The attention (3) with SAM's decomposed relative-position bias added to every
+ * kept logit. The SparseSAM README's repository layout names fused "FA2 + rel-pos"
+ * kernels; the pages do not define the bias, and the reading taken is SAM's image
+ * encoder's (Kirillov et al. 2023, after MViTv2, Li et al. 2022). For a query at
+ * segment coordinates (y, x) and a key at (y', x'):
+ *   logit = scale * <q, k> + <q, rel_h[y - y' + Sh - 1]> + <q, rel_w[x - x' + Sw - 1]>
+ * with the unscaled q, Sh x Sw the segment shape (grid_h x grid_w, or window x window
+ * with pads at their padded-window coordinates) and a slot's coordinates
+ * (slot / Sw, slot % Sw).
+ *   perm   [segments, N] int32: the slot at each position (sparsesam_permute's perm of
+ *          the same segments); values are clamped into [0, N).
+ *   rel_h  [2 Sh - 1, head_dim] fp32, rel_w [2 Sw - 1, head_dim] fp32 (shared by heads).
+ *   q, k, vt, o, scale as in (3). Sh and Sw must be at most 64 and head_dim at most 80
+ *   (UNSUPPORTED otherwise).
+ * The bias is evaluated once per (segment, head, position) into a table in fp32 from
+ * the stored q; bf16 plans with head_dim 64 and a 64 x 64 grid keep the table in fp16
+ * (clamped to +-65504) and run it on the matrix cores, the others use fp32 tables. workspace must hold
+ * relpos_workspace_bytes scaled to `segments` (bytes per segment =
+ * relpos_workspace_bytes / (max_batch * segments_per_image)).
+ */
+sparsesam_status sparsesam_attn_relpos(sparsesam_plan_t plan, int32_t segments, const void* q, const void* k,
+                                       const void* vt, void* o, float scale, const int32_t* perm,
+                                       const float* rel_h, const float* rel_w, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * (4) Residual-Consistency MLP, in place on the fp32 residual stream (same page,
  * 2. Residual-Consistency MLP: the MLP runs on the keep-set only; every other token
  * passes through the residual unchanged). For each row t in routed:
@@ -239,6 +269,9 @@ typedef struct sparsesam_block_weights {
   const float* b1;     /* [hidden] */
   const void* w2;      /* [C, hidden] */
   const float* b2;     /* [C] */
+  const float* rel_pos_h; /* [2 Sh - 1, head_dim] relative-position table (3b) when the plan has
+                             rel_pos = 1, else NULL */
+  const float* rel_pos_w; /* [2 Sw - 1, head_dim], likewise */
 } sparsesam_block_weights;
 
 /*
@@ -248,7 +281,8 @@ typedef struct sparsesam_block_weights {
  * closing paragraph of part 2):
  *   h  = LayerNorm1(x) gathered into stripe-sorted order (window pads: h = 0)
  *   qkv = h W_qkv^T + b_qkv
- *   o  = sparse attention (3) per segment and head, scale head_dim^-0.5
+ *   o  = sparse attention (3) per segment and head, scale head_dim^-0.5 (with the
+ *        relative-position bias (3b) when the plan has rel_pos = 1)
  *   x  = x + o W_proj^T + b_proj          scattered back to raster order, pads dropped
  *   x  = the routed MLP (4) on the keep-set
  * workspace >= block_workspace_bytes; batch <= max_batch.

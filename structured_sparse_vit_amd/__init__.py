@@ -57,7 +57,7 @@ class Plan:
 
     def __init__(self, grid_h, grid_w, window, stripes, block, global_tokens, band_radius, attn_density,
                  mlp_density, channels, heads, head_dim, mlp_hidden, max_batch, dtype, ordering="importance",
-                 order_seed=0):
+                 order_seed=0, rel_pos=False):
         lib = _lib.load()
         self._lib = lib
         self.dtype = dtype
@@ -66,7 +66,7 @@ class Plan:
         self.desc = _lib.PlanDesc(grid_h, grid_w, window, stripes, block, global_tokens, band_radius,
                                   attn_density, mlp_density, channels, heads, head_dim, mlp_hidden, max_batch,
                                   SPARSESAM_BF16 if dtype == "bf16" else SPARSESAM_F32, ORDERINGS.index(ordering),
-                                  order_seed & 0xFFFFFFFF)
+                                  order_seed & 0xFFFFFFFF, 1 if rel_pos else 0)
         h = ctypes.c_void_p()
         check(lib.sparsesam_plan_create(ctypes.byref(self.desc), ctypes.byref(h)), "sparsesam_plan_create")
         self._h = h
@@ -76,11 +76,11 @@ class Plan:
         self.device = torch.device("cuda", info.device) if info.has_device_copy else None
 
     @classmethod
-    def from_config(cls, cfg, max_batch=None):
+    def from_config(cls, cfg, max_batch=None, rel_pos=False):
         return cls(cfg.grid, cfg.grid, cfg.window, cfg.stripes, cfg.block, cfg.global_tokens, cfg.band_radius,
                    cfg.attn_density, cfg.mlp_density, cfg.channels, cfg.heads, cfg.head_dim, cfg.mlp_hidden,
                    max_batch or cfg.batch, cfg.dtype, getattr(cfg, "ordering", "importance"),
-                   getattr(cfg, "order_seed", 0))
+                   getattr(cfg, "order_seed", 0), rel_pos)
 
     @property
     def handle(self):
@@ -172,6 +172,37 @@ def attn(plan, q, k, vt, scale=None, out=None, workspace=None):
     return out
 
 
+def attn_relpos(plan, q, k, vt, perm, rel_h, rel_w, scale=None, out=None, workspace=None):
+    """Block-sparse attention with the decomposed relative-position bias.
+
+    q, k [segments, heads, N, D]; vt [segments, heads, D, N_pad]; perm [segments, N] int32
+    (slot of each position); rel_h [2 Sh - 1, D], rel_w [2 Sw - 1, D] fp32 -> o [segments,
+    N, heads * D].
+    """
+    lib = _lib.load()
+    dt = plan.torch_dtype
+    H, D, n = plan.desc.heads, plan.desc.head_dim, plan.info["seq_len"]
+    n_pad = (n + 7) // 8 * 8
+    segs = q.shape[0]
+    sh_, sw_ = (plan.desc.window, plan.desc.window) if plan.desc.window else (plan.desc.grid_h, plan.desc.grid_w)
+    _need(q, "q", dt, (segs, H, n, D), plan.device)
+    _need(k, "k", dt, (segs, H, n, D), plan.device)
+    _need(vt, "vt", dt, (segs, H, D, n_pad), plan.device)
+    _need(perm, "perm", torch.int32, (segs, n), plan.device)
+    _need(rel_h, "rel_h", torch.float32, (2 * sh_ - 1, D), plan.device)
+    _need(rel_w, "rel_w", torch.float32, (2 * sw_ - 1, D), plan.device)
+    if out is None:
+        out = torch.empty(segs, n, H * D, dtype=dt, device=q.device)
+    _need(out, "out", dt, (segs, n, H * D), plan.device)
+    scale = D ** -0.5 if scale is None else float(scale)
+    per_seg = plan.info["relpos_workspace_bytes"] // max(1, plan.desc.max_batch * plan.info["segments_per_image"])
+    ws = _workspace(per_seg * segs, q.device, workspace)
+    check(lib.sparsesam_attn_relpos(plan.handle, segs, _ptr(q), _ptr(k), _ptr(vt), _ptr(out), scale, _ptr(perm),
+                                    _ptr(rel_h), _ptr(rel_w), _ptr(ws), ws.numel(), _stream(q.device)),
+          "sparsesam_attn_relpos")
+    return out
+
+
 def _workspace(nbytes, device, workspace):
     if workspace is None:
         return torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
@@ -212,7 +243,28 @@ def weights_to_device(w, plan, device=None):
         t = torch.as_tensor(w[name])
         dt = plan.torch_dtype if name in _MATRICES else torch.float32
         out[name] = t.to(device=device, dtype=dt).contiguous()
+    for name, src in (("rel_pos_h", "rel_h"), ("rel_pos_w", "rel_w")):
+        if w.get(src) is not None:
+            out[name] = torch.as_tensor(w[src]).to(device=device, dtype=torch.float32).contiguous()
     return out
+
+
+def _block_weights(plan, w, what=""):
+    """The C struct of one layer's weights; the relative-position tables are passed
+    when the plan adds the bias (their shapes checked) and must be absent otherwise."""
+    rel = [w.get("rel_pos_h"), w.get("rel_pos_w")]
+    if plan.desc.rel_pos:
+        D = plan.desc.head_dim
+        sh_, sw_ = ((plan.desc.window, plan.desc.window) if plan.desc.window
+                    else (plan.desc.grid_h, plan.desc.grid_w))
+        _need(rel[0], what + "rel_pos_h", torch.float32, (2 * sh_ - 1, D), plan.device)
+        _need(rel[1], what + "rel_pos_w", torch.float32, (2 * sw_ - 1, D), plan.device)
+        ptrs = [t.data_ptr() for t in rel]
+    else:
+        if rel[0] is not None or rel[1] is not None:
+            raise ValueError(what + "rel_pos_h / rel_pos_w given to a plan without rel_pos")
+        ptrs = [None, None]
+    return _lib.BlockWeights(*([w[name].data_ptr() for name in _WEIGHT_NAMES] + ptrs))
 
 
 def block(plan, weights, x, perm, routed, workspace=None):
@@ -233,7 +285,7 @@ def block(plan, weights, x, perm, routed, workspace=None):
     _need(perm, "perm", torch.int32, (b * segs, n), plan.device)
     _need(routed, "routed", torch.int32, (b * rpi,), plan.device)
     ws = _workspace(plan.info["block_workspace_bytes"], x.device, workspace)
-    bw = _lib.BlockWeights(*[weights[name].data_ptr() for name in _WEIGHT_NAMES])
+    bw = _block_weights(plan, weights)
     check(lib.sparsesam_block(plan.handle, ctypes.byref(bw), _ptr(x), b, _ptr(perm), _ptr(routed), _ptr(ws),
                               ws.numel(), _stream(x.device)), "sparsesam_block")
     return x
@@ -275,7 +327,7 @@ def encoder(global_plan, window_plan, layers, kinds, x, global_perm=None, window
         for name in _WEIGHT_NAMES:
             _need(w[name], "layer %d %s" % (l, name), dt if name in _MATRICES else torch.float32, shapes[name],
                   ref.device)
-        arr[l] = _lib.BlockWeights(*[w[name].data_ptr() for name in _WEIGHT_NAMES])
+        arr[l] = _block_weights(global_plan if int(kinds[l]) else window_plan, w, "layer %d " % l)
     kind_arr = (ctypes.c_uint8 * max(1, n))(*[int(k) for k in kinds])
     need = max(p.info["block_workspace_bytes"] for p in plans)
     ws = _workspace(need, x.device, workspace)

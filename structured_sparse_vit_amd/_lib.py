@@ -29,6 +29,7 @@ EXPORTS = [
     "sparsesam_importance",
     "sparsesam_permute",
     "sparsesam_attn",
+    "sparsesam_attn_relpos",
     "sparsesam_mlp",
     "sparsesam_block",
     "sparsesam_encoder",
@@ -42,7 +43,7 @@ class PlanDesc(ctypes.Structure):
         ("band_radius", ctypes.c_int32), ("attn_density", ctypes.c_float), ("mlp_density", ctypes.c_float),
         ("channels", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("mlp_hidden", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("dtype", ctypes.c_int32),
-        ("ordering", ctypes.c_int32), ("order_seed", ctypes.c_uint32),
+        ("ordering", ctypes.c_int32), ("order_seed", ctypes.c_uint32), ("rel_pos", ctypes.c_int32),
     ]
 
 
@@ -55,12 +56,14 @@ class PlanInfo(ctypes.Structure):
         ("block_workspace_bytes", ctypes.c_size_t), ("mlp_workspace_bytes", ctypes.c_size_t),
         ("attn_workspace_bytes", ctypes.c_size_t),
         ("has_device_copy", ctypes.c_int32), ("device", ctypes.c_int32),
+        ("relpos_workspace_bytes", ctypes.c_size_t),
     ]
 
 
 class BlockWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_proj", "b_proj", "ln2_g", "ln2_b", "w1", "b1", "w2", "b2")]
+                ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_proj", "b_proj", "ln2_g", "ln2_b", "w1", "b1", "w2", "b2",
+                 "rel_pos_h", "rel_pos_w")]
 
 
 _lib = None
@@ -87,6 +90,7 @@ def load():
         "sparsesam_importance": ([P, I32, I32, I32, I32, P, P], I32),
         "sparsesam_permute": ([P, P, I32, P, P, P, P], I32),
         "sparsesam_attn": ([P, I32, P, P, P, P, F32, P, SZ, P], I32),
+        "sparsesam_attn_relpos": ([P, I32, P, P, P, P, F32, P, P, P, P, SZ, P], I32),
         "sparsesam_mlp": ([P, P, I64, P, I32, P, P, P, P, P, P, P, SZ, P], I32),
         "sparsesam_block": ([P, ctypes.POINTER(BlockWeights), P, I32, P, P, P, SZ, P], I32),
         "sparsesam_encoder": ([P, P, ctypes.POINTER(BlockWeights), P, I32, P, I32, P, P, P, P, P, SZ, P], I32),

@@ -46,6 +46,18 @@ size_t mlp_workspace(const sparsesam_plan& p, int rows, size_t* a2, size_t* hid)
   return off;
 }
 
+RelLayout relpos_layout(const sparsesam_plan& p, int segments) {
+  RelLayout R;
+  const size_t segs = (size_t)std::max(segments, 0);
+  // every region is a whole number of 256-byte-aligned per-segment parts, so the total is
+  // proportional to the segment count (callers scale it per segment)
+  R.table = 0;
+  R.kc = segs * align256((size_t)p.desc.heads * p.n * (size_t)p.rel_tj * sizeof(float));
+  R.part = R.kc + segs * align256((size_t)p.n * sizeof(int));
+  R.total = R.part + segs * align256(attn_partial_bytes(p, 1));
+  return R;
+}
+
 BlockLayout block_layout(const sparsesam_plan& p, int batch) {
   BlockLayout L;
   const size_t es = elem_size(p);
@@ -65,6 +77,13 @@ BlockLayout block_layout(const sparsesam_plan& p, int batch) {
   off += align256(M * C * es);
   L.part = off;
   off += align256(attn_partial_bytes(p, (int)segs));
+  if (p.desc.rel_pos) {
+    const RelLayout R = relpos_layout(p, (int)segs);
+    L.rel_table = off;
+    off += R.kc;
+    L.rel_kc = off;
+    off += R.part - R.kc;
+  }
   L.total_attn = off;
   L.total_mlp = mlp_workspace(p, batch * p.routed_per_image, &L.a2, &L.hid);
   return L;
@@ -107,6 +126,7 @@ static sparsesam_status validate_desc(const sparsesam_plan_desc& d) {
   if (d.dtype != SPARSESAM_F32 && d.dtype != SPARSESAM_BF16) return invalid("dtype must be SPARSESAM_F32 or SPARSESAM_BF16");
   if (d.ordering < SPARSESAM_ORDER_IMPORTANCE || d.ordering > SPARSESAM_ORDER_RANDOM)
     return invalid("ordering must be a sparsesam_ordering value");
+  if (d.rel_pos != 0 && d.rel_pos != 1) return invalid("rel_pos must be 0 or 1");
   if (d.channels > 1536) return unsupported("channels above 1536 are not supported");
   if (d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 80 && d.head_dim != 128)
     return unsupported("head_dim must be 32, 64, 80 or 128");
@@ -192,6 +212,16 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
   }
   p->n_pad = (p->n + 7) & ~7;
   p->s = p->n / d.stripes;
+  p->rel_seg_h = d.window > 0 ? d.window : d.grid_h;
+  p->rel_seg_w = d.window > 0 ? d.window : d.grid_w;
+  if (p->rel_seg_h <= 64 && p->rel_seg_w <= 64 && d.head_dim <= 80) {  // table kernel's LDS
+    p->rel_xoff = 16 * ((p->rel_seg_h + 15) / 16);
+    p->rel_tj = p->rel_xoff + 16 * ((p->rel_seg_w + 15) / 16);
+  }
+  if (d.rel_pos && p->rel_tj == 0) {
+    delete p;
+    return unsupported("the relative-position bias needs segments of at most 64 x 64 tokens and head_dim <= 80");
+  }
   int radius = d.band_radius;
   const int last = (p->s - 1) / d.block;
   if (radius < 0) {
@@ -382,6 +412,8 @@ sparsesam_status sparsesam_plan_get_info(sparsesam_plan_t p, sparsesam_plan_info
   info->block_workspace_bytes = p->block_ws;
   info->mlp_workspace_bytes = p->mlp_ws;
   info->attn_workspace_bytes = attn_partial_bytes(*p, p->desc.max_batch * p->segs_per_img);
+  info->relpos_workspace_bytes =
+      p->rel_tj > 0 ? relpos_layout(*p, p->desc.max_batch * p->segs_per_img).total : 0;
   info->has_device_copy = p->dev ? 1 : 0;
   info->device = p->dev ? p->device : -1;
   return SPARSESAM_OK;
@@ -455,6 +487,38 @@ sparsesam_status sparsesam_attn(sparsesam_plan_t p, int32_t segments, const void
   return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_attn launch");
 }
 
+sparsesam_status sparsesam_attn_relpos(sparsesam_plan_t p, int32_t segments, const void* q, const void* k,
+                                       const void* vt, void* o, float scale, const int32_t* perm,
+                                       const float* rel_h, const float* rel_w, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  sparsesam_status st = check_device(p);
+  if (st != SPARSESAM_OK) return st;
+  if (segments < 0) return invalid("segments must be >= 0");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return invalid("scale must be positive and finite");
+  if (p->rel_tj <= 0)
+    return unsupported("the relative-position bias needs segments of at most 64 x 64 tokens and head_dim <= 80");
+  if (segments == 0) return SPARSESAM_OK;
+  if (!q || !k || !vt || !o || !perm || !rel_h || !rel_w)
+    return invalid("q, k, vt, o, perm, rel_h and rel_w must not be null");
+  const RelLayout R = relpos_layout(*p, segments);
+  if (!workspace || workspace_bytes < R.total) {
+    set_error("relative-position attention workspace needs " + std::to_string(R.total) + " bytes for " +
+              std::to_string(segments) + " segments");
+    return SPARSESAM_ERR_WORKSPACE;
+  }
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e;
+  if (p->desc.dtype == SPARSESAM_BF16)
+    e = launch_attention_relpos<bf16_t>(*p, segments, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
+                                        (bf16_t*)o, scale, perm, rel_h, rel_w, ws + R.table,
+                                        reinterpret_cast<int*>(ws + R.kc), ws + R.part, (hipStream_t)stream);
+  else
+    e = launch_attention_relpos<float>(*p, segments, (const float*)q, (const float*)k, (const float*)vt, (float*)o,
+                                       scale, perm, rel_h, rel_w, ws + R.table, reinterpret_cast<int*>(ws + R.kc),
+                                       ws + R.part, (hipStream_t)stream);
+  return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_attn_relpos launch");
+}
+
 }  // extern "C"
 
 template <typename T>
@@ -523,7 +587,12 @@ static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weigh
   EpiQKV eq{w.b_qkv, q, k, vt, p.n, p.n_pad, p.desc.heads, p.desc.head_dim, C};
   e = launch_gemm_qkv<T>(h, (const T*)w.w_qkv, M, C, eq, st);
   if (e != hipSuccess) return e;
-  e = launch_attention<T>(p, segs, q, k, vt, o, 1.0f / std::sqrt((float)p.desc.head_dim), ws + L.part, st);
+  const float scale = 1.0f / std::sqrt((float)p.desc.head_dim);
+  if (p.desc.rel_pos)
+    e = launch_attention_relpos<T>(p, segs, q, k, vt, o, scale, perm, w.rel_pos_h, w.rel_pos_w, ws + L.rel_table,
+                                   reinterpret_cast<int*>(ws + L.rel_kc), ws + L.part, st);
+  else
+    e = launch_attention<T>(p, segs, q, k, vt, o, scale, ws + L.part, st);
   if (e != hipSuccess) return e;
   EpiResidualScatter er{w.b_proj, x, perm, nullptr, p.segmap(), C, x_rows};
   e = launch_gemm_residual<T>(o, (const T*)w.w_proj, M, C, C, er, st);
@@ -553,6 +622,10 @@ static sparsesam_status block_check(sparsesam_plan_t p, const sparsesam_block_we
   if (!w->ln1_g || !w->ln1_b || !w->w_qkv || !w->b_qkv || !w->w_proj || !w->b_proj || !w->ln2_g || !w->ln2_b ||
       !w->w1 || !w->b1 || !w->w2 || !w->b2)
     return invalid("a weight pointer is null");
+  if (p->desc.rel_pos && (!w->rel_pos_h || !w->rel_pos_w))
+    return invalid("the plan has rel_pos = 1: rel_pos_h and rel_pos_w must not be null");
+  if (!p->desc.rel_pos && (w->rel_pos_h || w->rel_pos_w))
+    return invalid("rel_pos_h / rel_pos_w given to a plan created with rel_pos = 0");
   BlockLayout L = block_layout(*p, batch);
   size_t need = std::max(L.total_attn, L.total_mlp);
   if (!workspace || workspace_bytes < need) {

@@ -49,6 +49,10 @@ struct sparsesam_plan {
   // 32-query block the 32-key blocks holding any kept pair
   std::vector<int> pos_tile, keep32, any32;
   int nt32 = 0;
+  // relative-position bias: segment shape (grid or window) and the bias table row of a
+  // query: key rows at 0 .. rel_seg_h - 1, key columns at rel_xoff .., rel_tj entries
+  // (0 when the segment is larger than 64 x 64: no bias support)
+  int rel_seg_h = 0, rel_seg_w = 0, rel_xoff = 0, rel_tj = 0;
 
   // device copy (one allocation) on `device`
   int device = -1;
@@ -89,10 +93,16 @@ sparsesam_status hip_fail(hipError_t e, const char* where);
 
 // Workspace carve-up of sparsesam_block / sparsesam_mlp.
 struct BlockLayout {
-  size_t h = 0, q = 0, k = 0, vt = 0, o = 0, part = 0, total_attn = 0;
+  size_t h = 0, q = 0, k = 0, vt = 0, o = 0, part = 0, rel_table = 0, rel_kc = 0, total_attn = 0;
   size_t a2 = 0, hid = 0, total_mlp = 0;
 };
 BlockLayout block_layout(const sparsesam_plan& p, int batch);
+// Workspace carve-up of the relative-position bias: tables (sized for fp32 entries),
+// key coordinates, then the attention partials.
+struct RelLayout {
+  size_t table = 0, kc = 0, part = 0, total = 0;
+};
+RelLayout relpos_layout(const sparsesam_plan& p, int segments);
 size_t mlp_workspace(const sparsesam_plan& p, int routed_rows, size_t* a2, size_t* hid);
 
 // ---- launches (each returns hipSuccess or the launch error) ----
@@ -142,6 +152,20 @@ hipError_t launch_gemm_residual(const T* a, const T* w, int m, int n, int k, con
 template <typename T>
 hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
                             float scale, void* partial, hipStream_t st);
+// The same attention with the relative-position bias of each segment added to the
+// logits: `perm` gives each position's slot, rel_h / rel_w the fp32 tables; `table`,
+// `kc` and `partial` are the RelLayout regions of the workspace.
+template <typename T>
+hipError_t launch_attention_relpos(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
+                                   float scale, const int* perm, const float* rel_h, const float* rel_w, void* table,
+                                   int* kc, void* partial, hipStream_t st);
+// bias tables T[segment, head, position, rel_tj] (exp2 units; TT fp16 or fp32) and key
+// coordinates
+template <typename T, typename TT>
+hipError_t launch_relpos_table(const sparsesam_plan& p, int segments, const T* q, const int* perm,
+                               const float* rel_h, const float* rel_w, TT* table, int* kc, hipStream_t st);
+size_t relpos_lds_bytes(int head_dim);
+bool attn_relpos_fused(const sparsesam_plan& p);
 bool attn_long_supported(const sparsesam_plan& p);
 int attn_long_resident_wgs(int device, int head_dim);
 size_t attn_partial_bytes(const sparsesam_plan& p, int segments);

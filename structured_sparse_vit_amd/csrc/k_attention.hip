@@ -59,6 +59,21 @@ constexpr float kRescaleSlack = 8.0f;
 // l below 2^64 * 4096 * max |v|, far inside fp32).
 constexpr float kOverflowGuard = 18446744073709551616.0f;  // 2^64
 
+// Relative-position bias in the D = 64 kernel (attn_mfma64_rel_kernel). A query's bias
+// table row (k_relpos.hip) has 128 fp16 entries: key rows 0..63, key columns at 64..127.
+// The bias enters S^T through eight more MFMA k-steps (fp16 operands, 2^-11 relative
+// rounding of the bias instead of bf16's 2^-8) whose K operand is one-hot in the key's
+// row (k-steps 0..3) or column (4..7) and whose Q^T operand is the query's table row. LDS past the rings: the query halves' table rows (8 KiB each; with P parities the
+// G = 4 / P members need at most 16 KiB after 128 KiB of rings, 64 KiB after 32), then
+// 17 one-hot fp16 rows of 16 bytes (row 8 + e: 1.0 at element e; the others zero) and the
+// key coordinates of every K slot, [slot][parity][64 keys].
+constexpr int kRelTj = 128;
+constexpr int kRelTqBytes = 32 * kRelTj * 2;
+constexpr int kRelOneHot = 4 * kParityBytes + 2 * kRelTqBytes;
+constexpr int kRelKc = kRelOneHot + 512;
+constexpr int kRelLds = kRelKc + 2 * 4 * 64 * 4;
+static_assert(kRelLds <= 160 * 1024, "bias layout fits the LDS");
+
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 // acc + a + b for two bf16 values, in one dot product with (1, 1)
@@ -117,13 +132,16 @@ __device__ __forceinline__ float max_xor32(float v) {
 // publishes K_{j+1} and V_j and retires the slots the step overwrites. (Loading more
 // steps ahead through deeper rings measured slower.)
 static_assert(kAttnItemTiles <= 64, "one key tile per lane");
-template <int P>  // key parities of the item (1, 2 or 4): the load code has no run-time loop
+// P: key parities of the item (1, 2 or 4): the load code has no run-time loop. REL: add
+// the relative-position bias from rel_t (bias table rows) and rel_kc (key coordinates).
+template <int P, bool REL>
 __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                                  const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
                                                  const int4* __restrict__ items, const int* __restrict__ col_idx,
                                                  const int* __restrict__ tile_start, int n, int n_pad, int heads,
                                                  int seg_heads, float c_log2, float* __restrict__ partial, int item,
-                                                 int sh, char* smem) {
+                                                 int sh, char* smem, const f16_t* __restrict__ rel_t,
+                                                 const int* __restrict__ rel_kc) {
   constexpr int D = 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -142,6 +160,7 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   constexpr int R = 2;                            // ring slots per parity
   constexpr int ring_bytes = 2 * R * kTileBytes;  // K ring then V^T ring
   char* ring = smem + (active ? kp : 0) * ring_bytes;
+  char* tq = smem + P * ring_bytes + (gi * 2 + qh) * kRelTqBytes;  // this query half's bias rows
 
   // Every tile of these plans is 64 tokens long (stripes are multiples of 64), so tile t
   // starts at token 64 t and no offset table is read. The key offsets are requested
@@ -178,6 +197,17 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
       __builtin_amdgcn_global_load_lds((const void*)(k_base + (size_t)k0 * D + k_src),
                                        (__attribute__((address_space(3))) void*)(dst + p * ring_bytes), 16, 0, 0);
     }
+    if constexpr (REL) {
+      if (wave == 0) {  // the tiles' key coordinates, one dword per lane
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const int k0 = __builtin_amdgcn_readlane(koff, min(p + P * j, total - 1));
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(rel_kc + (size_t)seg * n + k0 + lane),
+              (__attribute__((address_space(3))) void*)(smem + kRelKc + ((j & (R - 1)) * 4 + p) * 256), 4, 0, 0);
+        }
+      }
+    }
   };
   auto issue_v = [&](int j) {  // V^T tiles of step j (every parity) into V slot j mod R
     char* dst = smem + (R + (j & (R - 1))) * kTileBytes + wave * 1024;
@@ -205,6 +235,12 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
       for (int mb = 0; mb < 2; ++mb)
         kf[ks][mb] = *reinterpret_cast<const bf16x8*>(Ks + swz(mb * 32 + (lane & 31), ks * 2 + (lane >> 5)));
   };
+  // coordinates (row | column << 16) of the keys this lane's K fragment rows hold
+  auto read_kc = [&](int j, int (&kcv)[2]) {
+    const int* kcs = reinterpret_cast<const int*>(smem + kRelKc) + ((j & (R - 1)) * 4 + kp) * 64;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) kcv[mb] = kcs[kperm16(mb * 32 + (lane & 31))];
+  };
   auto read_v = [&](int j, bf16x8 (&vf)[4][2]) {
     const char* Vs = ring + (R + (j & (R - 1))) * kTileBytes;
 #pragma unroll
@@ -228,7 +264,7 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   }
   // S^T = K Q^T - m_run; the two accumulation chains alternate, so each MFMA depends on
   // the one two back
-  auto scores = [&](const bf16x8 (&kf)[4][2], f32x16 (&sc)[2]) {
+  auto scores = [&](const bf16x8 (&kf)[4][2], const int (&kcv)[2], f32x16 (&sc)[2]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -240,6 +276,23 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
         sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][mb], qf[ks], sc[mb], 0, 0, 0);
+    if constexpr (REL) {
+      // table columns 16 ks + 8 h .. + 7 of this lane's query (chunk c of row q sits at
+      // chunk c ^ (q & 15)) against the one-hot row of its key's row or column
+      const int q = lane & 31, hf = lane >> 5;
+      const char* oh = smem + kRelOneHot;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const f16x8 tf = *reinterpret_cast<const f16x8*>(tq + q * (kRelTj * 2) + (((2 * ks + hf) ^ (q & 15)) * 16));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int jj = ks < 4 ? (kcv[mb] & 0xffff) : (kcv[mb] >> 16);
+          const int row = min(max(jj - 16 * ks - 8 * hf + 8, 0), 16);
+          const f16x8 af = *reinterpret_cast<const f16x8*>(oh + row * 16);
+          sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, tf, sc[mb], 0, 0, 0);
+        }
+      }
+    }
   };
 
   // O^T accumulators: blocks 0 and 1 hold channels 0..63
@@ -314,27 +367,58 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   const int niter = (total + P - 1) / P;                  // steps (parity 0 has the most)
   f32x16 sacc[2];
   bf16x8 kb2[2][4][2];
+  int kc2[2][2] = {{0, 0}, {0, 0}};
+  // With the bias the registers do not hold a second set of K fragments: K is then
+  // loaded one step ahead, like V, and read in the step that uses it.
   issue_k(0);
-  issue_k(1);
+  if constexpr (!REL) issue_k(1);
   issue_v(0);
+  if constexpr (REL) {
+    // this query half's 32 bias rows (256 bytes each), once per member: lane L of load i
+    // brings row 4 i + L / 16, logical chunk (L % 16) ^ (row & 15)
+    if (active && kp == 0) {
+      const f16_t* trow = rel_t + ((size_t)sh * n + qt * kTile + qh * 32) * kRelTj;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4), c = (lane & 15) ^ (r & 15);
+        __builtin_amdgcn_global_load_lds((const void*)(trow + r * kRelTj + c * 8),
+                                         (__attribute__((address_space(3))) void*)(tq + i * 1024), 16, 0, 0);
+      }
+    }
+  }
   ready();
-  if (nj > 0) read_k(0, kb2[0]);
-  auto step = [&](int j, bf16x8 (&k_use)[4][2], bf16x8 (&k_next)[4][2]) {
+  if constexpr (!REL)
+    if (nj > 0) read_k(0, kb2[0]);
+  auto step = [&](int j, bf16x8 (&k_use)[4][2], bf16x8 (&k_next)[4][2], int (&kc_use)[2]) {
     ready();
-    issue_k(j + 2);
-    issue_v(j + 1);
-    if (j + 1 < nj) read_k(j + 1, k_next);
+    if constexpr (REL) {
+      issue_k(j + 1);
+      issue_v(j + 1);
+    } else {
+      issue_k(j + 2);
+      issue_v(j + 1);
+      if (j + 1 < nj) read_k(j + 1, k_next);
+    }
     if (j < nj) {
       bf16x8 vf[4][2], pf[4];
+      if constexpr (REL) {
+        read_k(j, k_use);
+        read_kc(j, kc_use);
+      }
       read_v(j, vf);
-      scores(k_use, sacc);
+      scores(k_use, kc_use, sacc);
       softmax(sacc, pf, j == 0);
       pv(vf, pf);
     }
   };
   for (int j = 0; j < niter; j += 2) {
-    step(j, kb2[0], kb2[1]);
-    if (j + 1 < niter) step(j + 1, kb2[1], kb2[0]);
+    if constexpr (REL) {
+      step(j, kb2[0], kb2[0], kc2[0]);
+      if (j + 1 < niter) step(j + 1, kb2[0], kb2[0], kc2[0]);
+    } else {
+      step(j, kb2[0], kb2[1], kc2[0]);
+      if (j + 1 < niter) step(j + 1, kb2[1], kb2[0], kc2[0]);
+    }
   }
   // every wavefront is done with the rings before the exchange area reuses them
   __syncthreads();
@@ -419,14 +503,48 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma64_kernel(const bf16
     const int item = u / seg_heads;
     const int parities = __builtin_amdgcn_readfirstlane(items[2 * item].w) >> 4;
     if (parities == 1)
-      attn_mfma64_unit<1>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
-                          u - item * seg_heads, smem);
+      attn_mfma64_unit<1, false>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2,
+                                 partial, item, u - item * seg_heads, smem, nullptr, nullptr);
     else if (parities == 2)
-      attn_mfma64_unit<2>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
-                          u - item * seg_heads, smem);
+      attn_mfma64_unit<2, false>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2,
+                                 partial, item, u - item * seg_heads, smem, nullptr, nullptr);
     else
-      attn_mfma64_unit<4>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
-                          u - item * seg_heads, smem);
+      attn_mfma64_unit<4, false>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2,
+                                 partial, item, u - item * seg_heads, smem, nullptr, nullptr);
+  }
+}
+
+// The same kernel with the relative-position bias (bias table rows rel_t [segment,
+// head, position, 128] fp16 in exp2 units, key coordinates rel_kc [segment, position]).
+__global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma64_rel_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt, const bf16_t* __restrict__ VT,
+    bf16_t* __restrict__ O, const int4* __restrict__ items, const int* __restrict__ col_idx,
+    const int* __restrict__ tile_start, int n, int n_pad, int heads, int seg_heads, int n_items, float c_log2,
+    float* __restrict__ partial, const f16_t* __restrict__ rel_t, const int* __restrict__ rel_kc) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // the one-hot rows, written once; the first unit's barrier publishes them
+  if (threadIdx.x < 68) {
+    const int row = threadIdx.x >> 2, i = threadIdx.x & 3, e = row - 8;
+    const uint32_t v = e == 2 * i ? 0x3C00u : e == 2 * i + 1 ? 0x3C000000u : 0u;  // fp16 1.0
+    reinterpret_cast<uint32_t*>(smem + kRelOneHot)[threadIdx.x] = v;
+  }
+  const int nwg = gridDim.x, w = blockIdx.x;
+  const int total = n_items * seg_heads;
+  for (int r = 0;; ++r) {
+    const int u = r * nwg + ((r & 1) ? nwg - 1 - w : w);
+    if (u >= total) break;
+    if (r > 0) __syncthreads();
+    const int item = u / seg_heads;
+    const int parities = __builtin_amdgcn_readfirstlane(items[2 * item].w) >> 4;
+    if (parities == 1)
+      attn_mfma64_unit<1, true>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2,
+                                partial, item, u - item * seg_heads, smem, rel_t, rel_kc);
+    else if (parities == 2)
+      attn_mfma64_unit<2, true>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2,
+                                partial, item, u - item * seg_heads, smem, rel_t, rel_kc);
+    else
+      attn_mfma64_unit<4, true>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2,
+                                partial, item, u - item * seg_heads, smem, rel_t, rel_kc);
   }
 }
 
@@ -919,14 +1037,18 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
 
 // ---------------------------------------------------------------- SIMT kernel (any pattern)
 
-template <typename T, int D>
+// REL: add the relative-position bias, rel_t[sh, query, kc & 0xffff] +
+// rel_t[sh, query, kc >> 16] for the key's coordinates kc = rel_kc[seg, key] (fp32
+// tables of rel_tj entries per query, exp2 units).
+template <typename T, int D, bool REL>
 __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, const T* __restrict__ Kt,
                                                        const T* __restrict__ VT, T* __restrict__ O,
                                                        const int* __restrict__ row_ptr,
                                                        const int* __restrict__ col_idx,
                                                        const int* __restrict__ tile_start,
                                                        const int* __restrict__ tile_len, int n, int n_pad, int heads,
-                                                       int chunks, float c_log2) {
+                                                       int chunks, float c_log2, const float* __restrict__ rel_t,
+                                                       const int* __restrict__ rel_kc, int tj) {
   const int qt = blockIdx.x / chunks, chunk = blockIdx.x - (blockIdx.x / chunks) * chunks;
   const int h = blockIdx.y, seg = blockIdx.z;
   const int len = tile_len[qt];
@@ -941,6 +1063,7 @@ __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, 
     acc[d] = 0.0f;
   }
   float m_run = -INFINITY, l_run = 0.0f;
+  const float* trow = REL ? rel_t + (sh * n + qi) * (size_t)tj : nullptr;
   for (int t = row_ptr[qt]; t < row_ptr[qt + 1]; ++t) {
     const int kt = col_idx[t];
     const int k0 = tile_start[kt], kl = tile_len[kt];
@@ -951,6 +1074,10 @@ __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, 
 #pragma unroll
       for (int d = 0; d < D; ++d) sc = fmaf(qv[d], (float)kr[d], sc);
       sc *= c_log2;
+      if constexpr (REL) {
+        const int kc = rel_kc[(size_t)seg * n + kj];
+        sc += trow[kc & 0xffff] + trow[kc >> 16];
+      }
       const float m_new = fmaxf(m_run, sc);
       const float alpha = exp2f(m_run - m_new);
       const float p = exp2f(sc - m_new);
@@ -990,13 +1117,14 @@ size_t attn_partial_bytes(const sparsesam_plan& p, int segments) {
   return (size_t)p.n_slots * segments * p.desc.heads * kTile * part_ld(p.desc.head_dim) * sizeof(float);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool REL = false>
 static hipError_t run_simt(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
-                           float c_log2, hipStream_t st) {
+                           float c_log2, hipStream_t st, const float* rel_t = nullptr, const int* rel_kc = nullptr) {
   const int chunks = (p.desc.block + 63) / 64;
   dim3 grid(p.tiles * chunks, p.desc.heads, segments);
-  hipLaunchKernelGGL((attn_simt_kernel<T, D>), grid, dim3(64), 0, st, q, k, vt, o, p.d_row_ptr, p.d_col_idx,
-                     p.d_tile_start, p.d_tile_len, p.n, p.n_pad, p.desc.heads, chunks, c_log2);
+  hipLaunchKernelGGL((attn_simt_kernel<T, D, REL>), grid, dim3(64), 0, st, q, k, vt, o, p.d_row_ptr, p.d_col_idx,
+                     p.d_tile_start, p.d_tile_len, p.n, p.n_pad, p.desc.heads, chunks, c_log2, rel_t, rel_kc,
+                     p.rel_tj);
   return hipGetLastError();
 }
 
@@ -1069,6 +1197,65 @@ hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, c
     default: return hipErrorInvalidValue;
   }
 }
+
+bool attn_relpos_fused(const sparsesam_plan& p) {
+  return p.desc.dtype == SPARSESAM_BF16 && p.desc.head_dim == 64 && attn_long_supported(p) && p.rel_tj == kRelTj &&
+         p.rel_xoff == 64;
+}
+
+template <typename T>
+hipError_t launch_attention_relpos(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
+                                   float scale, const int* perm, const float* rel_h, const float* rel_w, void* table,
+                                   int* kc, void* partial, hipStream_t st) {
+  if (segments <= 0) return hipSuccess;
+  if (p.rel_tj <= 0) return hipErrorInvalidValue;
+  const float c_log2 = scale * 1.4426950408889634f;
+  if constexpr (sizeof(T) == 2) {
+    if (attn_relpos_fused(p)) {
+      auto* tb = static_cast<f16_t*>(table);
+      hipError_t e = launch_relpos_table<bf16_t, f16_t>(p, segments, reinterpret_cast<const bf16_t*>(q), perm,
+                                                         rel_h, rel_w, tb, kc, st);
+      if (e != hipSuccess) return e;
+      e = hipFuncSetAttribute((const void*)attn_mfma64_rel_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kRelLds);
+      if (e != hipSuccess) return e;
+      const int seg_heads = segments * p.desc.heads;
+      const int units = p.n_items * seg_heads;
+      dim3 grid((unsigned)std::min(units, std::max(1, p.attn_resident_wgs)));
+      const auto* items = reinterpret_cast<const int4*>(p.d_items);
+      hipLaunchKernelGGL(attn_mfma64_rel_kernel, grid, dim3(64 * kAttnWaves), kRelLds, st,
+                         reinterpret_cast<const bf16_t*>(q), reinterpret_cast<const bf16_t*>(k),
+                         reinterpret_cast<const bf16_t*>(vt), reinterpret_cast<bf16_t*>(o), items, p.d_col_idx,
+                         p.d_tile_start, p.n, p.n_pad, p.desc.heads, seg_heads, p.n_items, c_log2,
+                         static_cast<float*>(partial), tb, kc);
+      e = hipGetLastError();
+      if (e != hipSuccess || p.n_split_rows == 0) return e;
+      const int waves = p.n_split_rows * seg_heads * kTile;
+      hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
+                         static_cast<const float*>(partial), p.d_splits, p.d_tile_start,
+                         reinterpret_cast<bf16_t*>(o), p.n, p.desc.heads, seg_heads, waves);
+      return hipGetLastError();
+    }
+  }
+  // every other plan: fp32 tables and the SIMT kernel
+  auto* tf = static_cast<float*>(table);
+  hipError_t e = launch_relpos_table<T, float>(p, segments, q, perm, rel_h, rel_w, tf, kc, st);
+  if (e != hipSuccess) return e;
+  switch (p.desc.head_dim) {
+    case 64: return run_simt<T, 64, true>(p, segments, q, k, vt, o, c_log2, st, tf, kc);
+    case 80: return run_simt<T, 80, true>(p, segments, q, k, vt, o, c_log2, st, tf, kc);
+    case 32: return run_simt<T, 32, true>(p, segments, q, k, vt, o, c_log2, st, tf, kc);
+    case 128: return run_simt<T, 128, true>(p, segments, q, k, vt, o, c_log2, st, tf, kc);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template hipError_t launch_attention_relpos<float>(const sparsesam_plan&, int, const float*, const float*,
+                                                   const float*, float*, float, const int*, const float*,
+                                                   const float*, void*, int*, void*, hipStream_t);
+template hipError_t launch_attention_relpos<bf16_t>(const sparsesam_plan&, int, const bf16_t*, const bf16_t*,
+                                                    const bf16_t*, bf16_t*, float, const int*, const float*,
+                                                    const float*, void*, int*, void*, hipStream_t);
 
 template hipError_t launch_attention<float>(const sparsesam_plan&, int, const float*, const float*, const float*,
                                             float*, float, void*, hipStream_t);
