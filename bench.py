@@ -86,20 +86,24 @@ def block_flops(plan, batch):
 class Workload:
     """Device-resident inputs, weights, outputs and workspace of one config."""
 
-    def __init__(self, cfg, dev, seed=0):
+    def __init__(self, cfg, dev, seed=0, rel_pos=False):
         import numpy as np
         import torch
 
         import structured_sparse_vit_amd as ss
         from synth import block_weights, synthetic_images, token_features
+        from synth.generate import rel_pos_tables
 
         self.cfg = cfg
         self.ss = ss
-        self.plan = ss.Plan.from_config(cfg)
+        self.plan = ss.Plan.from_config(cfg, rel_pos=rel_pos)
         self.img = torch.from_numpy(synthetic_images(cfg, seed)).to(dev)
         self.x0 = torch.from_numpy(token_features(cfg, seed)).to(dev)
         self.x = self.x0.clone()
-        self.w = ss.weights_to_device(block_weights(cfg, seed), self.plan)
+        w = block_weights(cfg, seed)
+        if rel_pos:
+            w["rel_h"], w["rel_w"] = rel_pos_tables(cfg, seed)
+        self.w = ss.weights_to_device(w, self.plan)
         info = self.plan.info
         b = cfg.batch
         self.imp = torch.empty(b, cfg.grid * cfg.grid, dtype=torch.float32, device=dev)
@@ -109,6 +113,8 @@ class Workload:
         self.ws = torch.empty(info["block_workspace_bytes"], dtype=torch.uint8, device=dev)
         self.mlp_ws = torch.empty(info["mlp_workspace_bytes"], dtype=torch.uint8, device=dev)
         self.attn_ws = torch.empty(max(1, info["attn_workspace_bytes"]), dtype=torch.uint8, device=dev)
+        self.relpos_ws = (torch.empty(max(1, info["relpos_workspace_bytes"]), dtype=torch.uint8, device=dev)
+                          if rel_pos else None)
         self.np = np
 
     def step(self):
@@ -353,6 +359,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-encoders", action="store_true", help="skip the c3 windowed block and c4 / c5 encoder runs")
     ap.add_argument("--profile-only", action="store_true", help="run the steps only (for rocprofv3)")
+    ap.add_argument("--rel-pos", action="store_true",
+                    help="with --profile-only: steps of a plan with the relative-position bias")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy 5 times (scale factor for HBM byte counters)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -382,7 +390,9 @@ def main():
         return
     cfg = get_config(args.config)
     _log("workload", cfg)
-    wl = Workload(cfg, dev)
+    if args.rel_pos and not args.profile_only:
+        sys.exit("--rel-pos applies to --profile-only runs; the full run reports the bias under 'relpos'")
+    wl = Workload(cfg, dev, rel_pos=args.rel_pos)
 
     # timed region: K full steps
     for _ in range(args.warmup):
@@ -451,6 +461,21 @@ def main():
         extra["orderings"][ordering] = {"step_ms": round(so, 5), "tokens_per_s": round(tokens / (so * 1e-3), 1),
                                         "permute_ms": round(po, 5)}
         del wlo
+
+    # SAM's decomposed relative-position bias: the step with a rel_pos plan, and the
+    # attention with the bias (table kernel + attention) on the operands timed above
+    wlr = Workload(cfg, dev, rel_pos=True)
+    wlr.step()
+    sr = time_region(wlr.step, 30, 5)
+    ar = time_region(lambda: ss.attn_relpos(wlr.plan, q, k, vt, wlr.perm, wlr.w["rel_pos_h"], wlr.w["rel_pos_w"],
+                                            out=o, workspace=wlr.relpos_ws), 50, 5)
+    ar_tf = attention_flops(plan) * segs / (ar * 1e-3) / 1e12
+    extra["relpos"] = {"step_ms": round(sr, 5), "tokens_per_s": round(tokens / (sr * 1e-3), 1),
+                       "attn_ms": round(ar, 5), "attn_tflops": round(ar_tf, 2),
+                       "attn_pct_peak": round(100 * ar_tf / PEAK_BF16_TFLOPS, 2),
+                       "note": "attn_ms includes the bias-table kernel; TFLOP/s counts QK^T and PV only"}
+    _log("relative-position bias", extra["relpos"])
+    del wlr
 
     if not args.no_dense:
         cfgd = cfg.with_(attn_density=1.0, mlp_density=1.0)

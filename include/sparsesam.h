@@ -225,7 +225,8 @@ sparsesam_status sparsesam_attn(sparsesam_plan_t plan, int32_t segments, const v
  * (slot / Sw, slot % Sw).
  *   perm   [segments, N] int32: the slot at each position (sparsesam_permute's perm of
  *          the same segments); values are clamped into [0, N).
- *   rel_h  [2 Sh - 1, head_dim] fp32, rel_w [2 Sw - 1, head_dim] fp32 (shared by heads).
+ *   rel_h  [2 Sh - 1, head_dim] fp32, rel_w [2 Sw - 1, head_dim] fp32 (shared by heads),
+ *          16-byte aligned.
  *   q, k, vt, o, scale as in (3). Sh and Sw must be at most 64 and head_dim at most 80
  *   (UNSUPPORTED otherwise).
  * The bias is evaluated once per (segment, head, position) into a table in fp32 from

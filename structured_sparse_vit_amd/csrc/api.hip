@@ -500,6 +500,7 @@ sparsesam_status sparsesam_attn_relpos(sparsesam_plan_t p, int32_t segments, con
   if (segments == 0) return SPARSESAM_OK;
   if (!q || !k || !vt || !o || !perm || !rel_h || !rel_w)
     return invalid("q, k, vt, o, perm, rel_h and rel_w must not be null");
+  if (((uintptr_t)rel_h | (uintptr_t)rel_w) & 15) return invalid("rel_h and rel_w must be 16-byte aligned");
   const RelLayout R = relpos_layout(*p, segments);
   if (!workspace || workspace_bytes < R.total) {
     set_error("relative-position attention workspace needs " + std::to_string(R.total) + " bytes for " +
@@ -624,6 +625,8 @@ static sparsesam_status block_check(sparsesam_plan_t p, const sparsesam_block_we
     return invalid("a weight pointer is null");
   if (p->desc.rel_pos && (!w->rel_pos_h || !w->rel_pos_w))
     return invalid("the plan has rel_pos = 1: rel_pos_h and rel_pos_w must not be null");
+  if (((uintptr_t)w->rel_pos_h | (uintptr_t)w->rel_pos_w) & 15)
+    return invalid("rel_pos_h and rel_pos_w must be 16-byte aligned");
   if (!p->desc.rel_pos && (w->rel_pos_h || w->rel_pos_w))
     return invalid("rel_pos_h / rel_pos_w given to a plan created with rel_pos = 0");
   BlockLayout L = block_layout(*p, batch);

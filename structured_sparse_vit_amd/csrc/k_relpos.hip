@@ -13,7 +13,8 @@
 // attention kernels add T[y'] + T[xoff + x'] to the logit of every kept key. The key
 // side needs only (y', x') per position: kc[seg][p] = y' | (xoff + x') << 16.
 //
-// relpos_table_kernel: one 256-thread workgroup per (segment, head, 64 positions). It
+// relpos_table_kernel (head_dim D = 32, 64 or 80): one 256-thread workgroup per
+// (segment, head, 64 positions). It
 // forms G[p][r] = <q_p, R[r]> for all 2 Sh - 1 rows of Rh and 2 Sw - 1 rows of Rw
 // (a 64 x 256 x D product in fp32 from LDS, 4 positions x 16 rows per thread), stores
 // G in LDS and writes T[p][j] = log2(e) * G[p][y_p - j + Sh - 1] (or the Rw part) along
@@ -30,19 +31,37 @@ constexpr int kRelLd = kRelRows + 4;    // LDS row stride of R^T and G (16-byte 
 constexpr int kRelQLd = 64 + 4;         // LDS row stride of Q^T
 constexpr int kRelPos = 64;             // positions per workgroup
 
+// four consecutive table entries in one store (8 bytes fp16, clamped to its range; 16
+// bytes fp32)
 template <typename TT>
-__device__ __forceinline__ TT to_table(float v) {
-  return v;
+__device__ __forceinline__ void store4(TT* dst, const float (&v)[4]);
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, const float (&v)[4]) {
+  *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
 }
 template <>
-__device__ __forceinline__ f16_t to_table<f16_t>(float v) {
-  return (f16_t)fminf(fmaxf(v, -65504.0f), 65504.0f);
+__device__ __forceinline__ void store4<f16_t>(f16_t* dst, const float (&v)[4]) {
+  typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+  f16x4 h;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = (f16_t)fminf(fmaxf(v[e], -65504.0f), 65504.0f);
+  *reinterpret_cast<f16x4*>(dst) = h;
 }
 
-template <typename T, typename TT>
+template <typename TT>
+__device__ __forceinline__ void write_rows(const float* G, int slot_raw, int n, int seg, int h, int p0, int seg_h,
+                                           int seg_w, int xoff, int tj, TT* __restrict__ table_sh,
+                                           int* __restrict__ kc);
+// slot of the position this thread writes in write_rows (position p0 + threadIdx.x / 4),
+// loaded up front so that its latency overlaps the product
+__device__ __forceinline__ int row_slot(const int* __restrict__ perm, int n, int seg, int p0) {
+  return perm[(size_t)seg * n + min(p0 + (int)(threadIdx.x >> 2), n - 1)];
+}
+
+template <typename T, typename TT, int D>
 __global__ void __launch_bounds__(256) relpos_table_kernel(const T* __restrict__ Q, const int* __restrict__ perm,
                                                            const float* __restrict__ rel_h,
-                                                           const float* __restrict__ rel_w, int n, int heads, int D,
+                                                           const float* __restrict__ rel_w, int n, int heads,
                                                            int seg_h, int seg_w, int xoff, int tj,
                                                            TT* __restrict__ table, int* __restrict__ kc) {
   extern __shared__ __attribute__((aligned(16))) float rl[];
@@ -52,20 +71,32 @@ __global__ void __launch_bounds__(256) relpos_table_kernel(const T* __restrict__
   const int sh = blockIdx.y, seg = sh / heads, h = sh - seg * heads;
   const int p0 = blockIdx.x * kRelPos;
   const int nh = 2 * seg_h - 1, nw = 2 * seg_w - 1;
-  for (int i = tid; i < kRelRows * D; i += 256) {
-    const int r = i / D, d = i - (i / D) * D;
-    float v = 0.0f;
-    if (r < 128) {
-      if (r < nh) v = rel_h[(size_t)r * D + d];
-    } else if (r - 128 < nw) {
-      v = rel_w[(size_t)(r - 128) * D + d];
-    }
-    Rt[d * kRelLd + r] = v;
+  // every load of the R and Q tiles is issued before the first LDS store (addresses
+  // clamped to a real row; rows past the tables and positions past n store zero)
+  constexpr int RI = kRelRows * D / 256, QI = kRelPos * D / 256;
+  float rv[RI], qv0[QI];
+#pragma unroll
+  for (int k = 0; k < RI; ++k) {
+    const int i = tid + 256 * k, r = i / D, d = i - (i / D) * D;
+    rv[k] = r < 128 ? rel_h[(size_t)min(r, nh - 1) * D + d] : rel_w[(size_t)min(r - 128, nw - 1) * D + d];
   }
   const T* qs = Q + ((size_t)sh * n + p0) * D;
-  for (int i = tid; i < kRelPos * D; i += 256) {
-    const int p = i / D, d = i - (i / D) * D;
-    Qt[d * kRelQLd + p] = p0 + p < n ? (float)qs[(size_t)p * D + d] : 0.0f;
+  const int prow = n - 1 - p0;  // last real position of this workgroup, relative to p0
+#pragma unroll
+  for (int k = 0; k < QI; ++k) {
+    const int i = tid + 256 * k, p = i / D, d = i - (i / D) * D;
+    qv0[k] = (float)qs[(size_t)min(p, prow) * D + d];
+  }
+#pragma unroll
+  for (int k = 0; k < RI; ++k) {
+    const int i = tid + 256 * k, r = i / D, d = i - (i / D) * D;
+    const bool real = r < 128 ? r < nh : r - 128 < nw;
+    Rt[d * kRelLd + r] = real ? rv[k] : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < QI; ++k) {
+    const int i = tid + 256 * k, p = i / D, d = i - (i / D) * D;
+    Qt[d * kRelQLd + p] = p <= prow ? qv0[k] : 0.0f;
   }
   __syncthreads();
   const int pg = tid >> 4, rg = tid & 15;  // positions 4 pg .. + 3, rows 16 rg .. + 15
@@ -94,24 +125,124 @@ __global__ void __launch_bounds__(256) relpos_table_kernel(const T* __restrict__
       *reinterpret_cast<f32x4*>(G + (4 * pg + a) * kRelLd + 16 * rg + 4 * i) =
           f32x4{acc[a][4 * i], acc[a][4 * i + 1], acc[a][4 * i + 2], acc[a][4 * i + 3]};
   __syncthreads();
-  // four threads per position, each a quarter of the row
+  write_rows<TT>(G, row_slot(perm, n, seg, p0), n, seg, h, p0, seg_h, seg_w, xoff, tj, table + (size_t)sh * n * tj,
+                 kc);
+}
+
+// Table rows of positions p0 .. p0 + 63 from G[p][r] in LDS (row stride kRelLd): four
+// threads per position; store i of thread `part` covers entries 4 (4 i + part) .. + 3,
+// so the four threads of a position write one contiguous piece per store. Head 0 also
+// writes the key coordinates.
+template <typename TT>
+__device__ __forceinline__ void write_rows(const float* G, int slot_raw, int n, int seg, int h, int p0, int seg_h,
+                                           int seg_w, int xoff, int tj, TT* __restrict__ table_sh,
+                                           int* __restrict__ kc) {
+  const int tid = threadIdx.x;
   const int p = tid >> 2, part = tid & 3;
   if (p0 + p >= n) return;
-  const int slot = min(max(perm[(size_t)seg * n + p0 + p], 0), seg_h * seg_w - 1);
+  const int slot = min(max(slot_raw, 0), seg_h * seg_w - 1);
   const int y = slot / seg_w, x = slot - (slot / seg_w) * seg_w;
   if (h == 0 && part == 0) kc[(size_t)seg * n + p0 + p] = y | ((xoff + x) << 16);
   const float log2e = 1.4426950408889634f;
   const float* g = G + p * kRelLd;
-  TT* trow = table + ((size_t)sh * n + p0 + p) * tj;
-  const int per = tj / 4;
-  for (int j = part * per; j < (part + 1) * per; ++j) {
-    float v = 0.0f;
-    if (j < seg_h)
-      v = g[y - j + seg_h - 1];
-    else if (j >= xoff && j < xoff + seg_w)
-      v = g[128 + x - (j - xoff) + seg_w - 1];
-    trow[j] = to_table<TT>(v * log2e);
+  TT* trow = table_sh + (size_t)(p0 + p) * tj;
+  // tj is a multiple of 16: tj / 16 stores of 4 entries per thread. Both candidate G
+  // entries are read (indices clamped into the row) and the right one selected.
+  for (int j0 = 4 * part; j0 < tj; j0 += 16) {
+    float v4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = j0 + e;
+      const float a = g[min(max(y - j + seg_h - 1, 0), 127)];
+      const float b = g[128 + min(max(x - (j - xoff) + seg_w - 1, 0), 127)];
+      const float v = j < seg_h ? a : (j >= xoff && j < xoff + seg_w) ? b : 0.0f;
+      v4[e] = v * log2e;
+    }
+    store4<TT>(trow + j0, v4);
   }
+}
+
+// bf16 queries: G = Q R^T on the matrix cores (v_mfma_f32_32x32x16_bf16). R is fp32, so
+// each R fragment goes in as bf16 hi + lo parts (R - hi rounded again), two MFMAs per
+// k-step: G carries about 2^-16 relative error, far below the table's own rounding.
+// Wavefront w forms G for all 64 positions and R rows 64 w .. 64 w + 63 straight from
+// global memory (Q rows and R rows are each read by the lanes that need them), stores
+// it to LDS and the workgroup writes the table rows as above.
+template <typename TT, int D>
+__global__ void __launch_bounds__(256) relpos_table_mfma_kernel(const bf16_t* __restrict__ Q,
+                                                                const int* __restrict__ perm,
+                                                                const float* __restrict__ rel_h,
+                                                                const float* __restrict__ rel_w, int n, int heads,
+                                                                int seg_h, int seg_w, int xoff, int tj,
+                                                                TT* __restrict__ table, int* __restrict__ kc) {
+  extern __shared__ __attribute__((aligned(16))) float rl[];
+  constexpr int KS = D / 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int sh = blockIdx.y, seg = sh / heads, h = sh - seg * heads;
+  const int p0 = blockIdx.x * kRelPos;
+  const int nh = 2 * seg_h - 1, nw = 2 * seg_w - 1;
+  const int l32 = lane & 31, k8 = (lane >> 5) * 8;
+  const int slot_raw = row_slot(perm, n, seg, p0);
+  // A operand: Q rows p0 + 32 pb + l32 (clamped to the last position), d = 16 ks + k8 ..
+  const bf16_t* qs = Q + (size_t)sh * n * D;
+  bf16x8 qa[2][KS];
+#pragma unroll
+  for (int pb = 0; pb < 2; ++pb) {
+    const int row = min(p0 + 32 * pb + l32, n - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qa[pb][ks] = *reinterpret_cast<const bf16x8*>(qs + (size_t)row * D + 16 * ks + k8);
+  }
+  // B operand: R rows r = 64 w + 32 rb + l32 (rel_h below 128, rel_w above), as hi / lo
+  f32x4 rf[2][KS][2];
+  bool real[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = 64 * w + 32 * rb + l32;
+    real[rb] = r < 128 ? r < nh : r - 128 < nw;
+    const float* src = r < 128 ? rel_h + (size_t)min(r, nh - 1) * D : rel_w + (size_t)min(r - 128, nw - 1) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      rf[rb][ks][0] = *reinterpret_cast<const f32x4*>(src + 16 * ks + k8);
+      rf[rb][ks][1] = *reinterpret_cast<const f32x4*>(src + 16 * ks + k8 + 4);
+    }
+  }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[pb][rb][e] = 0.0f;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = real[rb] ? rf[rb][ks][e >> 2][e & 3] : 0.0f;
+        hi[e] = to_bf16(v);
+        lo[e] = to_bf16(v - to_f32(hi[e]));
+      }
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+        acc[pb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[pb][ks], hi, acc[pb][rb], 0, 0, 0);
+        acc[pb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[pb][ks], lo, acc[pb][rb], 0, 0, 0);
+      }
+    }
+  // C[row = position][col = R row]: lane l holds column l32, rows 8 (i / 4) + 4 (l / 32) + i % 4
+  float* G = rl;
+#pragma unroll
+  for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int p = 32 * pb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        G[p * kRelLd + 64 * w + 32 * rb + l32] = acc[pb][rb][i];
+      }
+  __syncthreads();
+  write_rows<TT>(G, slot_raw, n, seg, h, p0, seg_h, seg_w, xoff, tj, table + (size_t)sh * n * tj, kc);
 }
 
 // R^T and Q^T, or G over the same memory afterwards, whichever is larger
@@ -123,12 +254,25 @@ template <typename T, typename TT>
 hipError_t launch_relpos_table(const sparsesam_plan& p, int segments, const T* q, const int* perm,
                                const float* rel_h, const float* rel_w, TT* table, int* kc, hipStream_t st) {
   const int D = p.desc.head_dim;
+  dim3 grid((unsigned)((p.n + kRelPos - 1) / kRelPos), (unsigned)(segments * p.desc.heads));
+  if constexpr (sizeof(T) == 2) {
+    const size_t lds = (size_t)kRelPos * kRelLd * sizeof(float);
+    auto kern = D == 32 ? relpos_table_mfma_kernel<TT, 32> : D == 80 ? relpos_table_mfma_kernel<TT, 80>
+                                                                     : relpos_table_mfma_kernel<TT, 64>;
+    if (D != 32 && D != 64 && D != 80) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, q, perm, rel_h, rel_w, p.n, p.desc.heads, p.rel_seg_h,
+                       p.rel_seg_w, p.rel_xoff, p.rel_tj, table, kc);
+    return hipGetLastError();
+  }
   const size_t lds = relpos_lds_bytes(D);
-  auto kern = relpos_table_kernel<T, TT>;
+  auto kern = D == 32 ? relpos_table_kernel<T, TT, 32> : D == 80 ? relpos_table_kernel<T, TT, 80>
+                                                                 : relpos_table_kernel<T, TT, 64>;
+  if (D != 32 && D != 64 && D != 80) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)((p.n + kRelPos - 1) / kRelPos), (unsigned)(segments * p.desc.heads));
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, q, perm, rel_h, rel_w, p.n, p.desc.heads, D, p.rel_seg_h,
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, q, perm, rel_h, rel_w, p.n, p.desc.heads, p.rel_seg_h,
                      p.rel_seg_w, p.rel_xoff, p.rel_tj, table, kc);
   return hipGetLastError();
 }
