@@ -474,8 +474,17 @@ def main():
                        "attn_ms": round(ar, 5), "attn_tflops": round(ar_tf, 2),
                        "attn_pct_peak": round(100 * ar_tf / PEAK_BF16_TFLOPS, 2),
                        "note": "attn_ms includes the bias-table kernel; TFLOP/s counts QK^T and PV only"}
-    _log("relative-position bias", extra["relpos"])
     del wlr
+    if not args.no_encoders:
+        # the windowed block (c3, four images) with the bias
+        cw = get_config("c3")
+        wlw = Workload(cw, dev, rel_pos=True)
+        wlw.step()
+        bw = time_region(lambda: ss.block(wlw.plan, wlw.w, wlw.x, wlw.perm, wlw.routed, workspace=wlw.ws), 30, 5)
+        extra["relpos"]["c3_window_block_ms"] = round(bw, 5)
+        extra["relpos"]["c3_window_tokens_per_s"] = round(cw.batch * cw.grid * cw.grid / (bw * 1e-3), 1)
+        del wlw
+    _log("relative-position bias", extra["relpos"])
 
     if not args.no_dense:
         cfgd = cfg.with_(attn_density=1.0, mlp_density=1.0)

@@ -856,13 +856,19 @@ struct ShortLds {
   }
 };
 
-template <int D>
+// REL: add the relative-position bias. Short segments are at most 16 x 16, so a query's
+// table row (rel_t, fp16, exp2 units) has 32 entries, key rows at 0..15 and key columns
+// at 16..31: two fp16 MFMA k-steps whose K operand is one-hot in the key's row (k-step 0)
+// or column (k-step 1), from 17 one-hot rows after the K and V^T tiles in LDS. The
+// scores are then taken to exp2 units before the bias is added.
+template <int D, bool REL>
 __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                                          const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
                                                          const int* __restrict__ pos_tile,
                                                          const int* __restrict__ keep32,
                                                          const int* __restrict__ any32, int n, int n_pad, int nt32,
-                                                         int heads, float c_log2) {
+                                                         int heads, float c_log2, const f16_t* __restrict__ rel_t,
+                                                         const int* __restrict__ rel_kc) {
   using L = ShortLds<D>;
   constexpr int KS = D / 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -909,9 +915,23 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
 #pragma unroll
     for (int i = 0; i < D / 8; ++i) *reinterpret_cast<bf16x8*>(Vs + ((tid >> 5) + 8 * i) * vld + kc) = vv[i];
   }
+  const char* onehot = reinterpret_cast<const char*>(Vs + (size_t)D * vld);
+  if constexpr (REL) {
+    if (tid < 68) {  // row 8 + e: fp16 1.0 at element e; the other rows zero
+      const int row = tid >> 2, i = tid & 3, e = row - 8;
+      const uint32_t v = e == 2 * i ? 0x3C00u : e == 2 * i + 1 ? 0x3C000000u : 0u;
+      reinterpret_cast<uint32_t*>(const_cast<char*>(onehot))[tid] = v;
+    }
+  }
   __syncthreads();
 
   const int hi = lane >> 5, l32 = lane & 31;
+  // the coordinates (row | (16 + column) << 16) of key kt * 32 + l32, every block
+  int kcs[kMaxShortBlocks];
+  if constexpr (REL) {
+#pragma unroll
+    for (int kt = 0; kt < kMaxShortBlocks; ++kt) kcs[kt] = rel_kc[(size_t)seg * n + min(kt * 32 + l32, n - 1)];
+  }
   constexpr bool kSumRow = L::MD * 32 > D;  // spare accumulator rows: denominators on the matrix cores
   for (int qt = wave; qt < nt32; qt += 4) {
     const int qpos = qt * 32 + l32;
@@ -921,6 +941,12 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8*>(q_base + (size_t)qrow * D + ks * 16 + hi * 8);
+    f16x8 tf[2];  // this query's bias entries 16 ks + 8 hi .. + 7
+    if constexpr (REL) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        tf[ks] = *reinterpret_cast<const f16x8*>(rel_t + ((size_t)sh * n + qrow) * 32 + ks * 16 + hi * 8);
+    }
     f32x16 oacc[L::MD];
 #pragma unroll
     for (int md = 0; md < L::MD; ++md)
@@ -946,6 +972,17 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + l32) * L::KLD + ks * 16 + hi * 8);
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc, 0, 0, 0);
       }
+      if constexpr (REL) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[e] *= c_log2;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int jj = ks == 0 ? (kcs[kt] & 0xffff) : (kcs[kt] >> 16);
+          const int row = min(max(jj - 16 * ks - 8 * hi + 8, 0), 16);
+          const f16x8 af = *reinterpret_cast<const f16x8*>(onehot + row * 16);
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, tf[ks], sc, 0, 0, 0);
+        }
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -954,7 +991,7 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
         mx = fmaxf(mx, sc[e]);
       }
       mx = max_xor32(mx);
-      const float m_new = fmaxf(m_run, mx * c_log2);
+      const float m_new = fmaxf(m_run, REL ? mx : mx * c_log2);
       if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
         // a lane whose reference does not move keeps alpha = 1 (also when both are -inf)
         const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
@@ -973,7 +1010,8 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float x = sc[kk * 8 + e];
-          const float p = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c_log2, -m_run));
+          const float p = x == -INFINITY ? 0.0f
+                          : __builtin_amdgcn_exp2f(REL ? x - m_run : __builtin_fmaf(x, c_log2, -m_run));
           if constexpr (!kSumRow) {
             if (e & 1)
               ps1 += p;
@@ -1142,18 +1180,20 @@ hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, c
       auto* ob = reinterpret_cast<bf16_t*>(o);
       if (p.desc.head_dim == 64) {
         const size_t lds = ShortLds<64>::bytes(p.nt32);
-        hipError_t e = hipFuncSetAttribute((const void*)attn_short_kernel<64>,
+        hipError_t e = hipFuncSetAttribute((const void*)attn_short_kernel<64, false>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_short_kernel<64>, dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
-                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2);
+        hipLaunchKernelGGL((attn_short_kernel<64, false>), dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
+                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2, nullptr,
+                           nullptr);
       } else {
         const size_t lds = ShortLds<80>::bytes(p.nt32);
-        hipError_t e = hipFuncSetAttribute((const void*)attn_short_kernel<80>,
+        hipError_t e = hipFuncSetAttribute((const void*)attn_short_kernel<80, false>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_short_kernel<80>, dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
-                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2);
+        hipLaunchKernelGGL((attn_short_kernel<80, false>), dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
+                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2, nullptr,
+                           nullptr);
       }
       return hipGetLastError();
     }
@@ -1234,6 +1274,31 @@ hipError_t launch_attention_relpos(const sparsesam_plan& p, int segments, const 
       hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
                          static_cast<const float*>(partial), p.d_splits, p.d_tile_start,
                          reinterpret_cast<bf16_t*>(o), p.n, p.desc.heads, seg_heads, waves);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (sizeof(T) == 2) {
+    if (p.nt32 > 0 && p.rel_tj == 32 && (p.desc.head_dim == 64 || p.desc.head_dim == 80)) {
+      auto* tb = static_cast<f16_t*>(table);
+      hipError_t e = launch_relpos_table<bf16_t, f16_t>(p, segments, reinterpret_cast<const bf16_t*>(q), perm,
+                                                         rel_h, rel_w, tb, kc, st);
+      if (e != hipSuccess) return e;
+      const int units = segments * p.desc.heads;
+      const auto* qb = reinterpret_cast<const bf16_t*>(q);
+      const auto* kb = reinterpret_cast<const bf16_t*>(k);
+      const auto* vb = reinterpret_cast<const bf16_t*>(vt);
+      auto* ob = reinterpret_cast<bf16_t*>(o);
+      const bool d80 = p.desc.head_dim == 80;
+      const size_t lds = (d80 ? ShortLds<80>::bytes(p.nt32) : ShortLds<64>::bytes(p.nt32)) + 512;
+      const void* kern = d80 ? (const void*)attn_short_kernel<80, true> : (const void*)attn_short_kernel<64, true>;
+      e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      if (d80)
+        hipLaunchKernelGGL((attn_short_kernel<80, true>), dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
+                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2, tb, kc);
+      else
+        hipLaunchKernelGGL((attn_short_kernel<64, true>), dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
+                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2, tb, kc);
       return hipGetLastError();
     }
   }

@@ -1,9 +1,10 @@
 """GPU parity of the decomposed relative-position bias against the oracle.
 
-sparsesam_attn_relpos on random q, k, v and a random slot permutation, at the full
-ViT-B global grid (bf16, matrix-core kernel), a windowed plan with ragged windows and
-the fp32 tiny config (fp32 tables, SIMT kernel); and blocks of rel_pos plans on the
-image pipeline. Bars as in test_gpu_parity: max-abs 1e-2 and relative L2 5e-3.
+sparsesam_attn_relpos on random q, k, v and a random slot permutation: the full ViT-B
+global grid (bf16, matrix-core kernel), ViT-B and ViT-H windows and ragged windows
+(bf16, windowed matrix-core kernel), the ViT-H global grid (head_dim 80: fp32 tables,
+SIMT kernel) and the fp32 tiny config (SIMT kernel); and blocks of rel_pos plans on
+the image pipeline. Bars as in test_gpu_parity: max-abs 1e-2 and relative L2 5e-3.
 """
 import sys
 
@@ -68,7 +69,7 @@ def _attn_relpos_case(key, seed=0, std=0.1, **over):
     return o, want, plan
 
 
-@pytest.mark.parametrize("key", ["c2", "c1", "ragged", "c3b1"])
+@pytest.mark.parametrize("key", ["c2", "c1", "ragged", "c3b1", "c5w", "c5g"])
 def test_attn_relpos_parity(key):
     _say("attention + relative position", key)
     o, want, plan = _attn_relpos_case(key)
