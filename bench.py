@@ -273,6 +273,8 @@ PROFILE_COMMANDS = {
                   "python3 bench.py --copy-calibration",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_copy -o w -- "
                   "python3 bench.py --copy-calibration",
+    "trace_relpos": "rocprofv3 --kernel-trace --stats -T --output-format csv -d gpurun_out/trace_relpos -o relpos -- "
+                    "python3 bench.py --profile-only --rel-pos --steps 20 --warmup 5",
 }
 ATTN_KERNELS = ("attn_mfma64_kernel", "attn_combine_kernel")
 COPY_BYTES = 256 << 20
@@ -303,21 +305,28 @@ def summarize_profiles(src):
     """Turn the rocprofv3 output of PROFILE_COMMANDS (under src) into the text summaries in profiles/."""
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
-    # kernel trace: per-kernel launch statistics of the timed step
-    stats = _csv_rows(os.path.join(src, "trace_c2"), "kernel_stats.csv")
-    lines = ["# Kernel-trace statistics of the c2 step (SAM ViT-B global block, 64 x 64 tokens, C 768,",
-             "# 12 heads x 64, MLP 3072, density 0.4, batch 1): Sobel importance, permutation,",
-             "# keep-set and one SparseSAM block per step; 20 timed + 5 warmup steps (plus bench setup).",
-             "# command (from the repository root):",
-             "#   " + PROFILE_COMMANDS["trace"],
-             "# Durations in microseconds.",
-             "%-88s %6s %10s %10s %10s %7s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "pct")]
-    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-        lines.append("%-88s %6d %10.2f %10.2f %10.2f %7.2f" % (
-            r["Name"][:88], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-    with open(os.path.join(out_dir, "c2_step_kernel_trace.txt"), "w") as f:
-        f.write("\n".join(lines) + "\n")
+    # kernel trace: per-kernel launch statistics of the timed step (and of the step with
+    # the relative-position bias, when that trace is there)
+    traces = [("trace", "trace_c2", "c2_step_kernel_trace.txt", ""),
+              ("trace_relpos", "trace_relpos", "c2_relpos_step_kernel_trace.txt",
+               " with the decomposed relative-position bias")]
+    for key, sub, name, what in traces:
+        if key == "trace_relpos" and not os.path.isdir(os.path.join(src, sub)):
+            continue
+        stats = _csv_rows(os.path.join(src, sub), "kernel_stats.csv")
+        lines = ["# Kernel-trace statistics of the c2 step%s (SAM ViT-B global block, 64 x 64 tokens," % what,
+                 "# C 768, 12 heads x 64, MLP 3072, density 0.4, batch 1): Sobel importance, permutation,",
+                 "# keep-set and one SparseSAM block per step; 20 timed + 5 warmup steps (plus bench setup).",
+                 "# command (from the repository root):",
+                 "#   " + PROFILE_COMMANDS[key],
+                 "# Durations in microseconds.",
+                 "%-88s %6s %10s %10s %10s %7s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "pct")]
+        for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+            lines.append("%-88s %6d %10.2f %10.2f %10.2f %7.2f" % (
+                r["Name"][:88], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+        with open(os.path.join(out_dir, name), "w") as f:
+            f.write("\n".join(lines) + "\n")
     # HBM traffic of the attention launch, scaled by a plain copy of known size
     cf, _ = _counter_kib(os.path.join(src, "pmc_fetch_copy"), "FETCH_SIZE", "copyBuffer")
     cw, _ = _counter_kib(os.path.join(src, "pmc_write_copy"), "WRITE_SIZE", "copyBuffer")
