@@ -146,9 +146,13 @@ __device__ __forceinline__ void write_rows(const float* G, int slot_raw, int n, 
   const float log2e = 1.4426950408889634f;
   const float* g = G + p * kRelLd;
   TT* trow = table_sh + (size_t)(p0 + p) * tj;
-  // tj is a multiple of 16: tj / 16 stores of 4 entries per thread. Both candidate G
-  // entries are read (indices clamped into the row) and the right one selected.
-  for (int j0 = 4 * part; j0 < tj; j0 += 16) {
+  // tj is a multiple of 16 and at most 128: tj / 16 <= 8 stores of 4 entries per thread.
+  // Both candidate G entries are read (indices clamped into the row) and the right one
+  // selected.
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int j0 = 4 * part + 16 * it;
+    if (j0 >= tj) break;
     float v4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
