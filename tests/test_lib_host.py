@@ -189,3 +189,48 @@ def test_encoder_validation_before_launch():
     other = ss.Plan.from_config(w_cfg.with_(channels=2 * g.desc.channels, heads=2 * g.desc.heads))
     assert call(g.handle, other.handle, [1, 0]) == 1            # plans of different shapes
     assert b"share grid" in lib.sparsesam_last_error()
+
+
+# ------------------------------------------------------------------ relative-position bias
+
+def test_relpos_plan_validation_and_workspace():
+    # rel_pos is a flag
+    lib = _lib.load()
+    d = _create().desc
+    d.rel_pos = 2
+    h = ctypes.c_void_p()
+    assert lib.sparsesam_plan_create(ctypes.byref(d), ctypes.byref(h)) == 1
+    # segments above 64 x 64 and head_dim above 80 have no bias tables
+    for over in (dict(grid_h=128, grid_w=128, block=64, global_tokens=64), dict(head_dim=128, heads=6, dtype="f32")):
+        with pytest.raises(ss.SparseSAMError) as ei:
+            _create(rel_pos=True, **over)
+        assert ei.value.status == 2
+        assert _create(**over).info["relpos_workspace_bytes"] == 0
+    # the workspace is proportional to the segment count (callers scale it per segment)
+    for over in (dict(), dict(window=14, stripes=4, block=16, global_tokens=16, max_batch=3)):
+        plan = _create(rel_pos=True, **over)
+        segs = plan.desc.max_batch * plan.info["segments_per_image"]
+        total = plan.info["relpos_workspace_bytes"]
+        assert total > 0 and total % segs == 0
+        per_seg = total // segs
+        n, tj = plan.info["seq_len"], 128 if not over else 32
+        assert per_seg >= plan.desc.heads * n * tj * 4 + n * 4
+        # a rel_pos plan's block workspace holds the tables on top of the plain block's
+        assert plan.info["block_workspace_bytes"] > _create(**over).info["block_workspace_bytes"]
+
+
+def test_attn_relpos_validation_before_launch():
+    lib = _lib.load()
+    plan = _create()
+    p = ctypes.c_void_p(256)
+    f = ctypes.c_float(0.125)
+    if plan.info["has_device_copy"]:
+        # argument checks that come before any launch
+        assert lib.sparsesam_attn_relpos(plan.handle, 1, p, p, p, p, f, None, p, p, p, 1 << 30, None) == 1
+        assert lib.sparsesam_attn_relpos(plan.handle, 1, p, p, p, p, f, p, ctypes.c_void_p(260), p, p, 1 << 30,
+                                         None) == 1  # rel_h not 16-byte aligned
+        assert lib.sparsesam_attn_relpos(plan.handle, 1, p, p, p, p, ctypes.c_float(0.0), p, p, p, p, 1 << 30,
+                                         None) == 1
+        assert lib.sparsesam_attn_relpos(plan.handle, 1, p, p, p, p, f, p, p, p, p, 16, None) == 3  # workspace
+    else:
+        assert lib.sparsesam_attn_relpos(plan.handle, 1, p, p, p, p, f, p, p, p, p, 1 << 30, None) == 6
