@@ -180,7 +180,7 @@ def torch_dense_block_ms(cfg, dev, iters=20):
         return time_region(run, iters, 3)
 
 
-def encoder_run(key, dev, density=None, passes=3):
+def encoder_run(key, dev, density=None, passes=3, rel_pos=False):
     """One pass of a whole encoder config (c4: ViT-L 24 blocks, c5: ViT-H 32 blocks) through
     sparsesam_encoder: importance and both permutations once per pass, then every block.
     Timing only: one random-init layer's weights serve every layer (the work per layer
@@ -194,11 +194,19 @@ def encoder_run(key, dev, density=None, passes=3):
     if density is not None:
         base = base.with_(attn_density=density, mlp_density=density)
     cg, cw = global_variant(base).with_(batch=base.batch), window_variant(base).with_(batch=base.batch)
-    pg, pw = ss.Plan.from_config(cg), ss.Plan.from_config(cw)
+    pg, pw = ss.Plan.from_config(cg, rel_pos=rel_pos), ss.Plan.from_config(cw, rel_pos=rel_pos)
     wd = ss.weights_to_device(block_weights(cg, 0), pg)
-    layers = [wd] * base.layers
     gl = set(encoder_global_layers(base.layers))
     kinds = [1 if l in gl else 0 for l in range(base.layers)]
+    if rel_pos:  # each block type has tables of its own segment shape
+        from synth.generate import rel_pos_tables
+        wg = dict(wd)
+        wg["rel_pos_h"], wg["rel_pos_w"] = (torch.from_numpy(t).to(dev) for t in rel_pos_tables(cg, 0))
+        ww = dict(wd)
+        ww["rel_pos_h"], ww["rel_pos_w"] = (torch.from_numpy(t).to(dev) for t in rel_pos_tables(cw, 0))
+        layers = [wg if k else ww for k in kinds]
+    else:
+        layers = [wd] * base.layers
     img = torch.from_numpy(synthetic_images(base, 0)).to(dev)
     x0 = torch.from_numpy(token_features(base, 0)).to(dev)
     x = x0.clone()
@@ -217,7 +225,7 @@ def encoder_run(key, dev, density=None, passes=3):
     del x, ws
     return {"batch": base.batch, "blocks": base.layers, "global_blocks": sorted(gl),
             "attn_density": base.attn_density, "mlp_density": base.mlp_density,
-            "ms_per_pass": round(ms, 3), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "ms_per_pass": round(ms, 3), "tokens_per_s": round(tokens / (ms * 1e-3), 1), "rel_pos": rel_pos,
             "weights": "one random-init layer reused by every layer (timing only)"}
 
 
@@ -513,7 +521,8 @@ def main():
         _log("c3 windowed block", extra["c3_window_block"])
         enc = {}
         for key in ("c4", "c5"):
-            enc[key] = {"sparse": encoder_run(key, dev), "density_1.0": encoder_run(key, dev, density=1.0)}
+            enc[key] = {"sparse": encoder_run(key, dev), "density_1.0": encoder_run(key, dev, density=1.0),
+                        "sparse_rel_pos": encoder_run(key, dev, rel_pos=True)}
             enc[key]["speedup_vs_density_1"] = round(enc[key]["density_1.0"]["ms_per_pass"] /
                                                      enc[key]["sparse"]["ms_per_pass"], 3)
             _log("encoder", key, enc[key])

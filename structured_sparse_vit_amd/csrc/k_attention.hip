@@ -564,13 +564,24 @@ constexpr int kD80Parity = 4 * kD80Tile;           // K ring + V^T ring, two slo
 constexpr int kD80Lds = 4 * kD80Parity;            // four parities: 160 KiB
 __device__ __forceinline__ int k80_off(int r, int c) { return r * 160 + ((c + (r >> 3)) % 10) * 16; }
 
-template <int P>  // key parities of the item (1, 2 or 4)
+// With the relative-position bias (REL) the unit walks at most two key parities (the
+// rings of four would fill the LDS): a four-parity item runs with wavefront pairs 2 and 3
+// idle. After the rings: the query halves' bias table rows (8 KiB each), the 17 one-hot
+// rows and the key coordinates, as in the head_dim-64 kernel; the scores are taken to
+// exp2 units before the bias k-steps.
+constexpr int kD80RelOneHot = 2 * kD80Parity + 4 * kRelTqBytes;
+constexpr int kD80RelKc = kD80RelOneHot + 512;
+constexpr int kD80RelLds = kD80RelKc + 2 * 4 * 64 * 4;
+static_assert(kD80RelLds <= 160 * 1024, "head_dim-80 bias layout fits the LDS");
+
+template <int P, bool REL = false>  // key parities of the item (1, 2 or 4)
 __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                               const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
                                               const int4* __restrict__ items, const int* __restrict__ col_idx,
                                               const int* __restrict__ tile_start, int n, int n_pad, int heads,
                                               int seg_heads, float c_log2, float* __restrict__ partial, int item,
-                                              int sh, char* smem) {
+                                              int sh, char* smem, const f16_t* __restrict__ rel_t = nullptr,
+                                              const int* __restrict__ rel_kc = nullptr) {
   constexpr int D = kD80, KS = D / 16, MD = 3;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -579,14 +590,16 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
   const int slot = __builtin_amdgcn_readfirstlane(it0.z), gp = __builtin_amdgcn_readfirstlane(it0.w);
   const int G = gp & 15;
   const int qh = wave & 1, pr = wave >> 1;
+  constexpr int PP = REL && P > 2 ? 2 : P;  // parities walked
   const int gi = pr % G, kp = pr / G;
-  const bool active = kp < P;
+  const bool active = kp < PP;
   const int qt = gi == 0 ? it1.x : gi == 1 ? it1.y : gi == 2 ? it1.z : it1.w;
   const int seg = sh / heads, h = sh - seg * heads;
   const bf16_t* q_base = Q + (size_t)sh * n * D;
   const bf16_t* k_base = Kt + (size_t)sh * n * D;
   const bf16_t* v_base = VT + (size_t)sh * D * n_pad;
   char* ring = smem + (active ? kp : 0) * kD80Parity;
+  char* tq = smem + PP * kD80Parity + (gi * 2 + qh) * kRelTqBytes;  // this query half's bias rows
   const int hi = lane >> 5, l32 = lane & 31;
 
   // 64-token tiles: tile t starts at token 64 t (no offset table); offsets first, then Q
@@ -618,8 +631,14 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
   // clamped to its last tile (unconditional loads into slots no wavefront reads)
   auto issue = [&](int j, int s) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int k0 = __builtin_amdgcn_readlane(koff, min(p + P * j, total - 1));
+    for (int p = 0; p < PP; ++p) {
+      const int k0 = __builtin_amdgcn_readlane(koff, min(p + PP * j, total - 1));
+      if constexpr (REL) {
+        if (wave == 0)  // the tile's key coordinates, one dword per lane
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(rel_kc + (size_t)seg * n + k0 + lane),
+              (__attribute__((address_space(3))) void*)(smem + kD80RelKc + (s * 4 + p) * 256), 4, 0, 0);
+      }
       char* base = smem + p * kD80Parity;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -657,13 +676,34 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + k80_off(mb * 32 + l32, ks * 2 + hi));
         sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[mb], 0, 0, 0);
       }
+    if constexpr (REL) {
+      // K tile rows are in key order here: row mb * 32 + l32 holds that key
+      const int* kcs = reinterpret_cast<const int*>(smem + kD80RelKc) + (s * 4 + kp) * 64;
+      const int kcv[2] = {kcs[l32], kcs[32 + l32]};
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[mb][e] *= c_log2;
+      const char* oh = smem + kD80RelOneHot;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const f16x8 tf = *reinterpret_cast<const f16x8*>(tq + l32 * (kRelTj * 2) + (((2 * ks + hi) ^ (l32 & 15)) * 16));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int jj = ks < 4 ? (kcv[mb] & 0xffff) : (kcv[mb] >> 16);
+          const int row = min(max(jj - 16 * ks - 8 * hi + 8, 0), 16);
+          const f16x8 af = *reinterpret_cast<const f16x8*>(oh + row * 16);
+          sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, tf, sc[mb], 0, 0, 0);
+        }
+      }
+    }
     float mx = sc[0][0];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[mb][e]);
     mx = max_xor32(mx);
-    const float m_new = fmaxf(m_run, mx * c_log2);
+    const float m_new = fmaxf(m_run, REL ? mx : mx * c_log2);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
@@ -678,7 +718,8 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
       bf16x8 v;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        v[e] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + e], c_log2, -m_run)));
+        v[e] = to_bf16(__builtin_amdgcn_exp2f(REL ? sc[kk >> 1][(kk & 1) * 8 + e] - m_run
+                                                  : __builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + e], c_log2, -m_run)));
       u32x4 r = __builtin_bit_cast(u32x4, v);
       const auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
       const auto s13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
@@ -703,9 +744,22 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
       }
   };
 
-  const int nj = active ? (total - kp + P - 1) / P : 0;
-  const int niter = (total + P - 1) / P;
+  const int nj = active ? (total - kp + PP - 1) / PP : 0;
+  const int niter = (total + PP - 1) / PP;
   issue(0, 0);
+  if constexpr (REL) {
+    // 32 bias rows of this query half (256 bytes each), once per member: lane L of load i
+    // brings row 4 i + L / 16, logical chunk (L % 16) ^ (row & 15)
+    if (active && kp == 0) {
+      const f16_t* trow = rel_t + ((size_t)sh * n + qt * kTile + qh * 32) * kRelTj;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4), c = (lane & 15) ^ (r & 15);
+        __builtin_amdgcn_global_load_lds((const void*)(trow + r * kRelTj + c * 8),
+                                         (__attribute__((address_space(3))) void*)(tq + i * 1024), 16, 0, 0);
+      }
+    }
+  }
   for (int j = 0; j < niter; ++j) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
@@ -730,7 +784,7 @@ __device__ __forceinline__ void attn_d80_unit(const bf16_t* __restrict__ Q, cons
   }
   __syncthreads();
   if (!active || kp > 0) return;
-  for (int p = 1; p < P; ++p) {
+  for (int p = 1; p < PP; ++p) {
     const float* r = rec_of(p);
     const float m1 = r[0], l1 = r[1];
     const float mm = fmaxf(m_run, m1);
@@ -802,6 +856,39 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_d80_kernel(const bf16_t*
     else
       attn_d80_unit<4>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial, item,
                           u - item * seg_heads, smem);
+  }
+}
+
+// The head_dim-80 kernel with the relative-position bias (rel_t: bias table rows
+// [segment, head, position, 128] fp16 in exp2 units; rel_kc: key coordinates).
+__global__ void __launch_bounds__(64 * kAttnWaves) attn_d80_rel_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt, const bf16_t* __restrict__ VT,
+    bf16_t* __restrict__ O, const int4* __restrict__ items, const int* __restrict__ col_idx,
+    const int* __restrict__ tile_start, int n, int n_pad, int heads, int seg_heads, int n_items, float c_log2,
+    float* __restrict__ partial, const f16_t* __restrict__ rel_t, const int* __restrict__ rel_kc) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  if (threadIdx.x < 68) {  // one-hot rows, published by the first unit's barrier
+    const int row = threadIdx.x >> 2, i = threadIdx.x & 3, e = row - 8;
+    const uint32_t v = e == 2 * i ? 0x3C00u : e == 2 * i + 1 ? 0x3C000000u : 0u;
+    reinterpret_cast<uint32_t*>(smem + kD80RelOneHot)[threadIdx.x] = v;
+  }
+  const int nwg = gridDim.x, w = blockIdx.x;
+  const int total = n_items * seg_heads;
+  for (int r = 0;; ++r) {
+    const int u = r * nwg + ((r & 1) ? nwg - 1 - w : w);
+    if (u >= total) break;
+    if (r > 0) __syncthreads();
+    const int item = u / seg_heads;
+    const int parities = __builtin_amdgcn_readfirstlane(items[2 * item].w) >> 4;
+    if (parities == 1)
+      attn_d80_unit<1, true>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial,
+                             item, u - item * seg_heads, smem, rel_t, rel_kc);
+    else if (parities == 2)
+      attn_d80_unit<2, true>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial,
+                             item, u - item * seg_heads, smem, rel_t, rel_kc);
+    else
+      attn_d80_unit<4, true>(Q, Kt, VT, O, items, col_idx, tile_start, n, n_pad, heads, seg_heads, c_log2, partial,
+                             item, u - item * seg_heads, smem, rel_t, rel_kc);
   }
 }
 
@@ -1239,8 +1326,8 @@ hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, c
 }
 
 bool attn_relpos_fused(const sparsesam_plan& p) {
-  return p.desc.dtype == SPARSESAM_BF16 && p.desc.head_dim == 64 && attn_long_supported(p) && p.rel_tj == kRelTj &&
-         p.rel_xoff == 64;
+  return p.desc.dtype == SPARSESAM_BF16 && (p.desc.head_dim == 64 || p.desc.head_dim == 80) &&
+         attn_long_supported(p) && p.rel_tj == kRelTj && p.rel_xoff == 64;
 }
 
 template <typename T>
@@ -1256,24 +1343,38 @@ hipError_t launch_attention_relpos(const sparsesam_plan& p, int segments, const 
       hipError_t e = launch_relpos_table<bf16_t, f16_t>(p, segments, reinterpret_cast<const bf16_t*>(q), perm,
                                                          rel_h, rel_w, tb, kc, st);
       if (e != hipSuccess) return e;
-      e = hipFuncSetAttribute((const void*)attn_mfma64_rel_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              kRelLds);
+      const bool d80 = p.desc.head_dim == 80;
+      const void* kern = d80 ? (const void*)attn_d80_rel_kernel : (const void*)attn_mfma64_rel_kernel;
+      const int lds = d80 ? kD80RelLds : kRelLds;
+      e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (e != hipSuccess) return e;
       const int seg_heads = segments * p.desc.heads;
       const int units = p.n_items * seg_heads;
       dim3 grid((unsigned)std::min(units, std::max(1, p.attn_resident_wgs)));
       const auto* items = reinterpret_cast<const int4*>(p.d_items);
-      hipLaunchKernelGGL(attn_mfma64_rel_kernel, grid, dim3(64 * kAttnWaves), kRelLds, st,
-                         reinterpret_cast<const bf16_t*>(q), reinterpret_cast<const bf16_t*>(k),
-                         reinterpret_cast<const bf16_t*>(vt), reinterpret_cast<bf16_t*>(o), items, p.d_col_idx,
-                         p.d_tile_start, p.n, p.n_pad, p.desc.heads, seg_heads, p.n_items, c_log2,
-                         static_cast<float*>(partial), tb, kc);
+      const auto* qb = reinterpret_cast<const bf16_t*>(q);
+      const auto* kb = reinterpret_cast<const bf16_t*>(k);
+      const auto* vb = reinterpret_cast<const bf16_t*>(vt);
+      auto* ob = reinterpret_cast<bf16_t*>(o);
+      if (d80)
+        hipLaunchKernelGGL(attn_d80_rel_kernel, grid, dim3(64 * kAttnWaves), lds, st, qb, kb, vb, ob, items,
+                           p.d_col_idx, p.d_tile_start, p.n, p.n_pad, p.desc.heads, seg_heads, p.n_items, c_log2,
+                           static_cast<float*>(partial), tb, kc);
+      else
+        hipLaunchKernelGGL(attn_mfma64_rel_kernel, grid, dim3(64 * kAttnWaves), lds, st, qb, kb, vb, ob, items,
+                           p.d_col_idx, p.d_tile_start, p.n, p.n_pad, p.desc.heads, seg_heads, p.n_items, c_log2,
+                           static_cast<float*>(partial), tb, kc);
       e = hipGetLastError();
       if (e != hipSuccess || p.n_split_rows == 0) return e;
       const int waves = p.n_split_rows * seg_heads * kTile;
-      hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
-                         static_cast<const float*>(partial), p.d_splits, p.d_tile_start,
-                         reinterpret_cast<bf16_t*>(o), p.n, p.desc.heads, seg_heads, waves);
+      if (d80)
+        hipLaunchKernelGGL(attn_combine_kernel<80>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
+                           static_cast<const float*>(partial), p.d_splits, p.d_tile_start, ob, p.n, p.desc.heads,
+                           seg_heads, waves);
+      else
+        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
+                           static_cast<const float*>(partial), p.d_splits, p.d_tile_start, ob, p.n, p.desc.heads,
+                           seg_heads, waves);
       return hipGetLastError();
     }
   }
