@@ -148,6 +148,13 @@ sparsesam_status sparsesam_plan_get_info(sparsesam_plan_t plan, sparsesam_plan_i
  * stripe t / tiles_per_stripe, stripe-local block t % tiles_per_stripe. */
 sparsesam_status sparsesam_plan_tile_list(sparsesam_plan_t plan, int32_t* row_ptr /* host */, int32_t* col_idx /* host */);
 void sparsesam_plan_destroy(sparsesam_plan_t plan);
+/* The same two queries under the names of the boundary's original listing: identical
+ * arguments, behaviour and errors (sparsesam_plan_info_get = sparsesam_plan_get_info,
+ * sparsesam_plan_block_list = sparsesam_plan_tile_list; a "block" of the pattern is one
+ * B x B tile). */
+sparsesam_status sparsesam_plan_info_get(sparsesam_plan_t plan, sparsesam_plan_info* info /* host */);
+sparsesam_status sparsesam_plan_block_list(sparsesam_plan_t plan, int32_t* row_ptr /* host */,
+                                           int32_t* col_idx /* host */);
 
 const char* sparsesam_status_string(sparsesam_status status);
 const char* sparsesam_last_error(void);

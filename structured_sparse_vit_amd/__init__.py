@@ -305,9 +305,19 @@ def encoder(global_plan, window_plan, layers, kinds, x, global_perm=None, window
     plans = [p for p in (global_plan, window_plan) if p is not None]
     if not plans:
         raise ValueError("at least one plan is needed")
+    ref = plans[0]
     for p in plans:
         _need(x, "x", torch.float32, device=p.device)
-    b = x.shape[0]
+        for f in ("grid_h", "grid_w", "channels", "heads", "head_dim", "mlp_hidden", "dtype"):
+            if getattr(p.desc, f) != getattr(ref.desc, f):
+                raise ValueError("global_plan and window_plan must share %s" % f)
+    gh, gw, C = ref.desc.grid_h, ref.desc.grid_w, ref.desc.channels
+    b = x.shape[0] if x.dim() == 4 else -1
+    if x.dim() != 4 or tuple(x.shape) != (b, gh, gw, C):
+        raise ValueError("x must be [batch, %d, %d, %d], got %s" % (gh, gw, C, tuple(x.shape)))
+    for p in plans:
+        if b > p.desc.max_batch:
+            raise ValueError("batch %d exceeds the plan's max_batch %d" % (b, p.desc.max_batch))
     ptrs = {}
     for name, plan, pr in (("global", global_plan, global_perm), ("window", window_plan, window_perm)):
         if plan is None or pr is None:
@@ -318,7 +328,6 @@ def encoder(global_plan, window_plan, layers, kinds, x, global_perm=None, window
         _need(perm, name + "_perm", torch.int32, (b * segs, n_seq), plan.device)
         _need(routed, name + "_routed", torch.int32, (b * rpi,), plan.device)
         ptrs[name] = (_ptr(perm), _ptr(routed))
-    ref = plans[0]
     dt, C, Hm = ref.torch_dtype, ref.desc.channels, ref.desc.mlp_hidden
     shapes = {"ln1_g": (C,), "ln1_b": (C,), "w_qkv": (3 * C, C), "b_qkv": (3 * C,), "w_proj": (C, C),
               "b_proj": (C,), "ln2_g": (C,), "ln2_b": (C,), "w1": (Hm, C), "b1": (Hm,), "w2": (C, Hm), "b2": (C,)}

@@ -23,6 +23,8 @@ EXPORTS = [
     "sparsesam_plan_create",
     "sparsesam_plan_get_info",
     "sparsesam_plan_tile_list",
+    "sparsesam_plan_info_get",
+    "sparsesam_plan_block_list",
     "sparsesam_plan_destroy",
     "sparsesam_status_string",
     "sparsesam_last_error",
@@ -84,6 +86,8 @@ def load():
         "sparsesam_plan_create": ([ctypes.POINTER(PlanDesc), ctypes.POINTER(P)], I32),
         "sparsesam_plan_get_info": ([P, ctypes.POINTER(PlanInfo)], I32),
         "sparsesam_plan_tile_list": ([P, P, P], I32),
+        "sparsesam_plan_info_get": ([P, ctypes.POINTER(PlanInfo)], I32),
+        "sparsesam_plan_block_list": ([P, P, P], I32),
         "sparsesam_plan_destroy": ([P], None),
         "sparsesam_status_string": ([I32], ctypes.c_char_p),
         "sparsesam_last_error": ([], ctypes.c_char_p),

@@ -426,6 +426,14 @@ sparsesam_status sparsesam_plan_tile_list(sparsesam_plan_t p, int32_t* row_ptr, 
   return SPARSESAM_OK;
 }
 
+sparsesam_status sparsesam_plan_info_get(sparsesam_plan_t p, sparsesam_plan_info* info) {
+  return sparsesam_plan_get_info(p, info);
+}
+
+sparsesam_status sparsesam_plan_block_list(sparsesam_plan_t p, int32_t* row_ptr, int32_t* col_idx) {
+  return sparsesam_plan_tile_list(p, row_ptr, col_idx);
+}
+
 void sparsesam_plan_destroy(sparsesam_plan_t p) {
   if (!p) return;
   if (p->dev) {

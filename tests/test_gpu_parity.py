@@ -129,7 +129,9 @@ def test_permute_ties_zero_nan(key):
 
 # ------------------------------------------------------------------ attention
 
-def _attn_case(key, seed=0, **over):
+def _attn_case(key, seed=0, heads_checked=None, **over):
+    """sparsesam_attn on seeded N(0, 1) q, k, v against the oracle's masked dense
+    attention; heads_checked samples the heads the oracle computes (all by default)."""
     cfg = config(key)
     if over:
         cfg = cfg.with_(**over)
@@ -147,11 +149,14 @@ def _attn_case(key, seed=0, **over):
     dev = [torch.from_numpy(a).to(DEV, dt).contiguous() for a in (q, k, vt)]
     o = ss.attn(plan, *dev).float().cpu().numpy()
     keep = oracle.position_keep(n, cfg.stripes, cfg.block, cfg.global_tokens, plan.info["band_radius"])
-    want = np.empty((segs, n, H * D))
-    for s in range(segs):
-        for h in range(H):
-            want[s, :, h * D:(h + 1) * D] = oracle.masked_attention(q[s, h], k[s, h], v[s, h], keep, D ** -0.5)
-    return o, want
+    hs = list(range(H)) if heads_checked is None else list(heads_checked)
+    want = np.empty((segs, n, len(hs) * D))
+    got = np.empty_like(want)
+    for i, h in enumerate(hs):
+        got[:, :, i * D:(i + 1) * D] = o[:, :, h * D:(h + 1) * D]
+        for s in range(segs):
+            want[s, :, i * D:(i + 1) * D] = oracle.masked_attention(q[s, h], k[s, h], v[s, h], keep, D ** -0.5)
+    return got, want
 
 
 @pytest.mark.parametrize("key", ["c1", "c2", "c3b1", "c5g", "c5w", "ragged"])
@@ -166,6 +171,48 @@ def test_attention_density_one_is_dense(key):
     _say("attention dense", key)
     o, want = _attn_case(key, seed=3, attn_density=1.0)
     check_close(o, want, what="dense attention " + key)
+
+
+@pytest.mark.parametrize("density", [0.4, 1.0])
+def test_attention_head_dim_80_global(density):
+    """The ViT-H global grid (head_dim 80, 16 heads) at density 0.4 (r = 3) and 1.0 (every
+    query tile keeps all 64 key tiles): the head_dim-80 long-segment kernel."""
+    _say("attention c5g density", density)
+    o, want = _attn_case("c5g", seed=5, heads_checked=(0, 7, 15), attn_density=density)
+    check_close(o, want, what="c5g attention d=%g" % density)
+
+
+def _max_row_tiles(cfg):
+    rp, _ = _plan(cfg).tile_list()
+    return int(np.diff(rp).max())
+
+
+@pytest.mark.parametrize("head_dim,density", [(64, 0.4), (64, 1.0), (80, 0.4), (80, 1.0)])
+def test_attention_split_rows_and_combine(head_dim, density):
+    """An 80 x 80 token grid (N = 6400, 25 tiles per stripe, 100 tiles): the global row
+    (and at density 1 every row) keeps more than 64 key tiles, so its work is split into
+    pieces that write partial results, merged by the combine kernel."""
+    heads = 2 if head_dim == 64 else 8  # channels a multiple of 128
+    over = dict(image=1280, heads=heads, head_dim=head_dim, channels=heads * head_dim, attn_density=density)
+    cfg = config("c2").with_(**over)
+    assert _max_row_tiles(cfg) > 64, "the plan must split rows"
+    _say("attention split rows D", head_dim, "density", density)
+    o, want = _attn_case("c2", seed=6, heads_checked=(0, heads - 1), **over)
+    check_close(o, want, what="split-row attention D%d d=%g" % (head_dim, density))
+
+
+@pytest.mark.parametrize("key,over", [
+    ("c2", dict(block=32, global_tokens=32)),      # B = 32 over a 64 x 64 grid
+    ("ragged", dict(window=0, block=16)),          # 18 x 18 global grid: stripes of 81, ragged tiles
+])
+def test_attention_bf16_simt_fallback(key, over):
+    """bf16 plans the matrix-core kernels do not take (long segments with B != 64 or
+    stripes not a multiple of 64) run the SIMT kernel on bf16 storage."""
+    _say("attention bf16 simt", key, over)
+    cfg = config(key).with_(**over)
+    hc = (0, cfg.heads - 1)
+    o, want = _attn_case(key, seed=7, heads_checked=hc, **over)
+    check_close(o, want, what="bf16 SIMT attention %s %s" % (key, over))
 
 
 def test_attention_single_stripe_and_wide_band():
@@ -268,16 +315,21 @@ def test_block_parity_high_gain(key, gain):
     _check_block(key, _run_block(key, gain=gain), gain)
 
 
-@pytest.mark.parametrize("key,kind", [("c4", "global"), ("c4", "window"), ("c5", "global"), ("c5", "window")])
-def test_block_full_batch_sampled(key, kind):
+@pytest.mark.parametrize("key,kind,density", [("c4", "global", None), ("c4", "window", None),
+                                              ("c5", "global", None), ("c5", "window", None),
+                                              ("c5", "global", 0.4), ("c5", "window", 0.4),
+                                              ("c5", "global", 1.0), ("c5", "window", 1.0)])
+def test_block_full_batch_sampled(key, kind, density):
     """One block of the ViT-L / ViT-H encoder configs at their full batch (8 and 16
     images: the launch shapes the encoder benchmark times, with the large-tile GEMM
     paths) against the oracle on sampled images: the first and the last. Images are
     independent, so the oracle runs each sampled image alone."""
     from synth import block_weights, token_features
     from synth.configs import global_variant, window_variant
-    _say("block full batch", key, kind)
+    _say("block full batch", key, kind, density)
     base = config(key)
+    if density is not None:  # the ViT-H sweep's other densities (attention and MLP alike)
+        base = base.with_(attn_density=density, mlp_density=density)
     cfg = global_variant(base) if kind == "global" else window_variant(base)
     b = cfg.batch
     plan = _plan(cfg)
@@ -335,22 +387,23 @@ def test_block_density_one_matches_dense_oracle():
 
 # ------------------------------------------------------------------ encoder
 
-def test_encoder_matches_block_by_block_and_oracle():
-    """An 8-block stack of the c4 (ViT-L) layout at reduced width, batch 2: global blocks
-    at layers 1, 3, 5, 7, windowed elsewhere, one permutation set per block type. The
-    native encoder equals the same blocks called one by one (deterministic kernels:
-    bit-equal) and the fp64 oracle encoder to the per-block bar scaled by sqrt(8) (each
-    block adds its own independent bf16 rounding)."""
-    _say("encoder 8 layers")
-    import math
-
+@pytest.mark.parametrize("key,over", [
+    ("c4", dict(channels=256, heads=4, mlp_hidden=512)),                 # ViT-L layout, head_dim 64
+    ("c5", dict(channels=640, heads=8, mlp_hidden=1280)),                # ViT-H layout, head_dim 80
+])
+def test_encoder_matches_block_by_block_and_oracle(key, over):
+    """An 8-block stack of an encoder config's layout at reduced width: global blocks at
+    layers 1, 3, 5, 7, windowed elsewhere, one permutation set per block type. The native
+    encoder equals the same blocks called one by one (deterministic kernels: bit-equal)
+    and matches the fp64 oracle encoder at the contract bar (max-abs 1e-2, rel-L2 5e-3)."""
+    _say("encoder 8 layers", key, over)
     from synth import block_weights, encoder_global_layers, token_features
     from synth.configs import global_variant, window_variant
-    layers, b = 8, 2
-    base = config("c4").with_(batch=b, channels=256, heads=4, mlp_hidden=512, layers=layers)
+    layers, b = 8, (2 if key == "c4" else 1)
+    base = config(key).with_(batch=b, layers=layers, **over)
     cg, cw = global_variant(base).with_(batch=b), window_variant(base).with_(batch=b)
     pg, pw = _plan(cg), _plan(cw)
-    imgs = np.stack([images("c4")[0], images("c4")[1]])
+    imgs = np.stack([images(key)[i] for i in range(b)])
     imp = np.stack([oracle.importance(im, base.patch) for im in imgs])
     x0 = token_features(base, 0)
     gl = encoder_global_layers(layers)
@@ -371,9 +424,8 @@ def test_encoder_matches_block_by_block_and_oracle():
     got = x_enc.cpu().numpy()
     assert np.array_equal(got.view(np.uint32), x_seq.cpu().numpy().view(np.uint32))
     want = oracle.encoder_forward(x0, imp, ws, gl, cg, cw)
-    s = math.sqrt(layers)
-    _say("  encoder max-abs %.3e rel-L2 %.3e" % (np.abs(got - want).max(), rel_l2(got, want)))
-    check_close(got, want, max_abs=1e-2 * s, rel_l2=5e-3 * s, what="encoder")
+    mx, rel = check_close(got, want, what="encoder " + key)
+    _say("  encoder %s max-abs %.3e rel-L2 %.3e" % (key, mx, rel))
 
 
 def test_encoder_full_size_matches_block_by_block():

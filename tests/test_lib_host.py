@@ -32,6 +32,49 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+# The entry points the boundary table lists by name (plan lifecycle and queries, the
+# five hot-path calls); this library exports each of them.
+BOUNDARY_NAMES = ["sparsesam_plan_create", "sparsesam_plan_info_get", "sparsesam_plan_block_list",
+                  "sparsesam_plan_destroy", "sparsesam_status_string", "sparsesam_last_error",
+                  "sparsesam_importance", "sparsesam_permute", "sparsesam_attn", "sparsesam_mlp", "sparsesam_block"]
+
+
+def test_library_exports_the_boundary_names():
+    lib = _lib.load()
+    declared = set(_declared_symbols())
+    for name in BOUNDARY_NAMES:
+        assert name in declared, name
+        assert hasattr(lib, name), name
+
+
+def test_boundary_aliases_agree():
+    """sparsesam_plan_info_get / sparsesam_plan_block_list return what
+    sparsesam_plan_get_info / sparsesam_plan_tile_list return."""
+    import ctypes
+
+    import numpy as np
+    lib = _lib.load()
+    d = _lib.PlanDesc(64, 64, 0, 4, 64, 64, -1, 0.4, 0.4, 768, 12, 64, 3072, 1, 1, 0, 0, 0)
+    h = ctypes.c_void_p()
+    assert lib.sparsesam_plan_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    try:
+        a, b = _lib.PlanInfo(), _lib.PlanInfo()
+        assert lib.sparsesam_plan_get_info(h, ctypes.byref(a)) == 0
+        assert lib.sparsesam_plan_info_get(h, ctypes.byref(b)) == 0
+        assert bytes(a) == bytes(b)
+        assert a.tiles_kept == 1696
+        rp1, rp2 = np.zeros(a.tiles + 1, np.int32), np.zeros(a.tiles + 1, np.int32)
+        ci1, ci2 = np.zeros(a.tiles_kept, np.int32), np.zeros(a.tiles_kept, np.int32)
+        vp = lambda v: v.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+        assert lib.sparsesam_plan_tile_list(h, vp(rp1), vp(ci1)) == 0
+        assert lib.sparsesam_plan_block_list(h, vp(rp2), vp(ci2)) == 0
+        assert np.array_equal(rp1, rp2) and np.array_equal(ci1, ci2)
+        assert lib.sparsesam_plan_info_get(None, ctypes.byref(b)) == 1
+        assert lib.sparsesam_plan_block_list(None, vp(rp2), vp(ci2)) == 1
+    finally:
+        lib.sparsesam_plan_destroy(h)
+
+
 def test_status_strings():
     lib = _lib.load()
     for code in range(7):
