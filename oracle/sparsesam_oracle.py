@@ -35,6 +35,18 @@ What it computes, step by step, with the passage each step follows:
   residual set is zero; K = floor(d * n_real + 1/2), at least 1.
 * one permutation per image (global blocks) or per window (windowed blocks),
   reused by every block of that type (the closing paragraph of that section).
+* dynamic routing (optional) -- the same bullet on selective computation says
+  the keep-set tokens are those with high feature dissimilarity or update
+  magnitude. Reading: per segment, the K tokens whose update by this block's
+  attention sub-block, x1 - x, has the largest squared L2 norm (ranked in fp32,
+  the kernels' precision; ties to the lower slot, pads never chosen), with the
+  same K as the static keep-set.
+* residual correction (optional) -- the residual-propagation bullet writes the
+  bypassing tokens as y_i = x_i + eps_i while calling them unchanged, and the
+  registry API names an ``mlp_merge`` flag. Reading: eps_i = 0 by default (the
+  tokens stay bitwise unchanged); with merging on, every real token of a segment
+  outside its keep-set receives the mean of the MLP updates of that segment's
+  keep-set, the keep-set's updates merged into one shared update.
 * relative-position bias (optional) -- the pages name fused "FA2 + rel-pos"
   kernels in the SparseSAM repository's kernel folder (the README's repository
   layout) but never define the term. Reading: SAM's image encoder's decomposed
@@ -90,6 +102,10 @@ __all__ = [
     "layer_norm",
     "gelu",
     "routed_mlp",
+    "ROUTINGS",
+    "update_score",
+    "top_k_by_score",
+    "merged_update",
     "segments_for_image",
     "block_forward",
     "encoder_forward",
@@ -480,8 +496,34 @@ def routed_mlp(x: np.ndarray, routed: np.ndarray, w: dict) -> np.ndarray:
     return out
 
 
+# ----------------------------------------------------------------------------
+# Dynamic routing and the residual correction (optional readings)
+# ----------------------------------------------------------------------------
+
+ROUTINGS = ("importance", "update")
+
+
+def update_score(x: np.ndarray, x1: np.ndarray) -> np.ndarray:
+    """Squared L2 norm of each row's update, ||x1[t] - x[t]||^2 (fp64): how far this
+    block's attention sub-block moved token t."""
+    d = np.asarray(x1, np.float64) - np.asarray(x, np.float64)
+    return (d * d).sum(axis=-1)
+
+
+def top_k_by_score(score: np.ndarray, valid: np.ndarray, k: int) -> np.ndarray:
+    """Slot ids of the k largest scores, largest first: the importance order's rank
+    count applied to the scores rounded to fp32 (ties to the lower slot, slots with
+    valid == False after every valid slot)."""
+    return descending_order(np.asarray(score, np.float64).astype(F32), valid=valid)[:k]
+
+
+def merged_update(x1_rows: np.ndarray, x2_rows: np.ndarray) -> np.ndarray:
+    """The keep-set's MLP updates merged into one: their mean, [C] (fp64)."""
+    return (np.asarray(x2_rows, np.float64) - np.asarray(x1_rows, np.float64)).mean(axis=0)
+
+
 def block_forward(x: np.ndarray, imp: np.ndarray, w: dict, cfg, radius: int = None,
-                  return_parts: bool = False):
+                  return_parts: bool = False, routed_override: list = None):
     """One SparseSAM encoder block on x [batch, gh, gw, C] (fp32 in, fp64 out).
 
     imp: [batch, gh*gw] fp32 importance. The pattern and keep-set come from
@@ -491,7 +533,16 @@ def block_forward(x: np.ndarray, imp: np.ndarray, w: dict, cfg, radius: int = No
     queries and their outputs are dropped. With w["rel_h"] and w["rel_w"] set, every
     head adds the relative-position bias (rel_pos_bias) of its segment to its logits;
     pads have their padded-window coordinates.
+
+    cfg.routing "update" chooses each segment's keep-set by update_score instead of the
+    importance order (same K); cfg.mlp_merge adds merged_update of a segment's keep-set
+    to its other real tokens. routed_override (one array of image token ids per image)
+    replaces the chosen keep-sets, e.g. by a set another implementation chose.
     """
+    routing = getattr(cfg, "routing", "importance")
+    merge = bool(getattr(cfg, "mlp_merge", False))
+    if routing not in ROUTINGS:
+        raise ValueError("unknown routing %r" % (routing,))
     b, gh, gw, C = x.shape
     H, D = cfg.heads, cfg.head_dim
     tmap = segments_for_image(gh, gw, cfg.window)
@@ -502,11 +553,12 @@ def block_forward(x: np.ndarray, imp: np.ndarray, w: dict, cfg, radius: int = No
     scale = D ** -0.5
     xf = x.reshape(b, gh * gw, C).astype(np.float64)
     out = np.empty_like(xf)
-    parts = {"perm": [], "inv": [], "routed": [], "radius": radius}
+    parts = {"perm": [], "inv": [], "routed": [], "radius": radius, "score": [], "routed_seg": []}
     for i in range(b):
         h = layer_norm(xf[i], w["ln1_g"], w["ln1_b"])
         attn_out = np.zeros((gh * gw, C))
         routed_img = []
+        orders = []
         for seg in range(tmap.shape[0]):
             row = tmap[seg]
             real = row >= 0
@@ -516,7 +568,7 @@ def block_forward(x: np.ndarray, imp: np.ndarray, w: dict, cfg, radius: int = No
             perm, inv = stripe_sort(s, cfg.stripes)
             parts["perm"].append(perm)
             parts["inv"].append(inv)
-            routed_img.append(routed_tokens(s, row, cfg.mlp_density))
+            orders.append(s)
             hs = np.zeros((n, C))
             hs[real] = h[row[real]]
             qkv = _linear(hs, w["w_qkv"], w["b_qkv"])
@@ -531,9 +583,36 @@ def block_forward(x: np.ndarray, imp: np.ndarray, w: dict, cfg, radius: int = No
                 o[:, hd * D:(hd + 1) * D] = masked_attention(q, k, v, mask, scale, bias)
             attn_out[row[real]] = o[real]
         x1 = xf[i] + _linear(attn_out, w["w_proj"], w["b_proj"])
+        score = update_score(xf[i], x1)
+        parts["score"].append(score)
+        for seg in range(tmap.shape[0]):
+            row = tmap[seg]
+            if routing == "importance":
+                routed_img.append(routed_tokens(orders[seg], row, cfg.mlp_density))
+            else:
+                real = row >= 0
+                k = routed_count(cfg.mlp_density, int(real.sum()))
+                slots = top_k_by_score(np.where(real, score[np.maximum(row, 0)], 0.0), real, k)
+                routed_img.append(np.sort(row[slots]))
+        if routed_override is not None:
+            routed_img = [np.sort(np.asarray(routed_override[i], np.int64))]
+        parts["routed_seg"].append(routed_img)
         routed = np.sort(np.concatenate(routed_img))
         parts["routed"].append(routed + i * gh * gw)
-        out[i] = routed_mlp(x1, routed, w)
+        x2 = routed_mlp(x1, routed, w)
+        if merge:
+            # every real token of a segment outside its keep-set gets the mean MLP update of
+            # that segment's keep-set (the keep-sets of an override are split by segment)
+            in_keep = np.zeros(gh * gw, bool)
+            in_keep[routed] = True
+            for seg in range(tmap.shape[0]):
+                row = tmap[seg]
+                toks = row[row >= 0]
+                kept = toks[in_keep[toks]]
+                rest = toks[~in_keep[toks]]
+                if kept.size and rest.size:
+                    x2[rest] = x1[rest] + merged_update(x1[kept], x2[kept])
+        out[i] = x2
     out = out.reshape(b, gh, gw, C)
     if return_parts:
         return out, parts

@@ -36,6 +36,8 @@ class Config:
     layers: int = 1       # encoder depth (1 = a single block)
     ordering: str = "importance"  # token order ahead of the stripe-sort (see oracle.ORDERINGS)
     order_seed: int = 0           # seed of the "random" ordering
+    routing: str = "importance"   # MLP keep-set: the importance order, or "update" (this block's attention update)
+    mlp_merge: bool = False       # the keep-set's mean MLP update added to the segment's other tokens
 
     @property
     def grid(self) -> int:
