@@ -321,6 +321,25 @@ sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_
                                    const int32_t* routed_window, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/*
+ * (5b) sparsesam_block (5) for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Instead of a
+ * caller workspace it uses a fixed scratch array held by the library, one per GPU, of
+ * sparsesam_noalloc_scratch_bytes() bytes (64 MiB) for the life of the process; the call
+ * itself allocates nothing. The caller still passes x, perm, routed and the weights as in
+ * (5), and the results are those of (5).
+ *   Limit: the plan's block workspace at `batch` (block_workspace_bytes at max_batch is an
+ *   upper bound) must fit the scratch; larger requests return SPARSESAM_ERR_WORKSPACE with
+ *   nothing launched. Every other error is reported as by (5).
+ *   All calls on one GPU share that GPU's scratch, which keeps the last call's contents:
+ *   calls that overlap on one GPU (other streams, other threads) race and give undefined
+ *   results. Serialise them, e.g. on one stream.
+ */
+size_t sparsesam_noalloc_scratch_bytes(void);
+sparsesam_status sparsesam_block_noalloc(sparsesam_plan_t plan, const sparsesam_block_weights* weights /* host */,
+                                         float* x, int32_t batch, const int32_t* perm, const int32_t* routed,
+                                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,8 +17,8 @@ import torch
 from . import _lib
 from ._lib import SPARSESAM_BF16, SPARSESAM_F32, SparseSAMError, check
 
-__all__ = ["Plan", "importance", "permute", "attn", "mlp", "block", "encoder", "SparseSAMError", "library_path",
-           "weights_to_device"]
+__all__ = ["Plan", "importance", "permute", "attn", "mlp", "block", "block_noalloc", "noalloc_scratch_bytes",
+           "encoder", "SparseSAMError", "library_path", "weights_to_device"]
 
 
 def library_path() -> str:
@@ -267,9 +267,8 @@ def _block_weights(plan, w, what=""):
     return _lib.BlockWeights(*([w[name].data_ptr() for name in _WEIGHT_NAMES] + ptrs))
 
 
-def block(plan, weights, x, perm, routed, workspace=None):
-    """One SparseSAM encoder block in place on x [batch, grid_h, grid_w, C] fp32."""
-    lib = _lib.load()
+def _block_args(plan, weights, x, perm, routed):
+    """Checks of block() / block_noalloc(); returns (batch, C weight struct)."""
     dt = plan.torch_dtype
     C, Hm = plan.desc.channels, plan.desc.mlp_hidden
     gh, gw = plan.desc.grid_h, plan.desc.grid_w
@@ -284,11 +283,33 @@ def block(plan, weights, x, perm, routed, workspace=None):
     n, segs, rpi = plan.info["seq_len"], plan.info["segments_per_image"], plan.info["routed_per_image"]
     _need(perm, "perm", torch.int32, (b * segs, n), plan.device)
     _need(routed, "routed", torch.int32, (b * rpi,), plan.device)
+    return b, _block_weights(plan, weights)
+
+
+def block(plan, weights, x, perm, routed, workspace=None):
+    """One SparseSAM encoder block in place on x [batch, grid_h, grid_w, C] fp32."""
+    lib = _lib.load()
+    b, bw = _block_args(plan, weights, x, perm, routed)
     ws = _workspace(plan.info["block_workspace_bytes"], x.device, workspace)
-    bw = _block_weights(plan, weights)
     check(lib.sparsesam_block(plan.handle, ctypes.byref(bw), _ptr(x), b, _ptr(perm), _ptr(routed), _ptr(ws),
                               ws.numel(), _stream(x.device)), "sparsesam_block")
     return x
+
+
+def block_noalloc(plan, weights, x, perm, routed):
+    """block() without a workspace: the library's fixed per-GPU scratch serves instead
+    (sparsesam_block_noalloc; for callers that cannot allocate). Calls on one GPU must
+    not overlap."""
+    lib = _lib.load()
+    b, bw = _block_args(plan, weights, x, perm, routed)
+    check(lib.sparsesam_block_noalloc(plan.handle, ctypes.byref(bw), _ptr(x), b, _ptr(perm), _ptr(routed),
+                                      _stream(x.device)), "sparsesam_block_noalloc")
+    return x
+
+
+def noalloc_scratch_bytes():
+    """Size of the library's per-GPU scratch used by block_noalloc()."""
+    return int(_lib.load().sparsesam_noalloc_scratch_bytes())
 
 
 def encoder(global_plan, window_plan, layers, kinds, x, global_perm=None, window_perm=None, workspace=None):

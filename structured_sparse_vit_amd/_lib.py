@@ -35,6 +35,8 @@ EXPORTS = [
     "sparsesam_mlp",
     "sparsesam_block",
     "sparsesam_encoder",
+    "sparsesam_noalloc_scratch_bytes",
+    "sparsesam_block_noalloc",
 ]
 
 
@@ -98,6 +100,8 @@ def load():
         "sparsesam_mlp": ([P, P, I64, P, I32, P, P, P, P, P, P, P, SZ, P], I32),
         "sparsesam_block": ([P, ctypes.POINTER(BlockWeights), P, I32, P, P, P, SZ, P], I32),
         "sparsesam_encoder": ([P, P, ctypes.POINTER(BlockWeights), P, I32, P, I32, P, P, P, P, P, SZ, P], I32),
+        "sparsesam_noalloc_scratch_bytes": ([], SZ),
+        "sparsesam_block_noalloc": ([P, ctypes.POINTER(BlockWeights), P, I32, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

@@ -1,6 +1,7 @@
 // C ABI of libsparsesam: plans, validation and the five hot-path entry points.
 #include <algorithm>
 #include <map>
+#include <mutex>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -665,6 +666,63 @@ sparsesam_status sparsesam_block(sparsesam_plan_t p, const sparsesam_block_weigh
                                  const int32_t* perm, const int32_t* routed, void* workspace, size_t workspace_bytes,
                                  void* stream) {
   return block_impl(p, w, x, batch, perm, routed, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// Scratch memory of sparsesam_block_noalloc: the block workspace, held by the library for
+// callers that cannot allocate. Each GPU the library runs on holds one copy until the
+// process ends. Host code never passes the array's name to a kernel (on the host it is
+// only a stand-in for the symbol): the device address comes from hipGetSymbolAddress,
+// once per device, with that device current, and is kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static std::vector<void*> g_scratch_ptr;  // per device index; null until looked up
+
+// Device address of `scratch` on device `dev` (the current device).
+static sparsesam_status scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (dev < 0) return invalid("bad device index");
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[(size_t)dev]) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the no-alloc scratch");
+    if (!ptr) {
+      set_error("hipGetSymbolAddress returned a null scratch address");
+      return SPARSESAM_ERR_HIP;
+    }
+    g_scratch_ptr[(size_t)dev] = ptr;
+  }
+  *out = g_scratch_ptr[(size_t)dev];
+  return SPARSESAM_OK;
+}
+
+extern "C" {
+
+size_t sparsesam_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+sparsesam_status sparsesam_block_noalloc(sparsesam_plan_t p, const sparsesam_block_weights* w, float* x,
+                                         int32_t batch, const int32_t* perm, const int32_t* routed, void* stream) {
+  sparsesam_status st = check_device(p);
+  if (st != SPARSESAM_OK) return st;
+  if (batch < 0 || batch > p->desc.max_batch) return invalid("batch must be in [0, max_batch]");
+  if (batch == 0) return block_check(p, w, x, 0, perm, routed, nullptr, 0);
+  const BlockLayout L = block_layout(*p, batch);
+  const size_t need = std::max(L.total_attn, L.total_mlp);
+  if (need > kNoAllocScratchBytes) {
+    set_error("sparsesam_block_noalloc: this block needs " + std::to_string(need) +
+              " bytes of scratch at batch " + std::to_string(batch) + ", above the library's fixed " +
+              std::to_string(kNoAllocScratchBytes) + " bytes; use sparsesam_block with a workspace");
+    return SPARSESAM_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  st = scratch_address(p->device, &ws);
+  if (st != SPARSESAM_OK) return st;
+  // the kernels write every scratch byte they read (no region has to start at zero)
+  return block_impl(p, w, x, batch, perm, routed, ws, kNoAllocScratchBytes, stream);
 }
 
 sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_t window_plan,
