@@ -78,6 +78,22 @@ typedef enum sparsesam_ordering {
 } sparsesam_ordering;
 
 /*
+ * How a block picks the MLP keep-set of each segment ("Technische Samenvatting: SparseSAM",
+ * Methodologie, 2. Residual-Consistency MLP: the token-routing bullet partitions the tokens by
+ * the deterministic permutation order; the selective-computation bullet describes the keep-set
+ * as the tokens of high feature dissimilarity or update magnitude). K is the same in both.
+ *   IMPORTANCE: the first K tokens of the segment's importance order, computed once per image
+ *               by sparsesam_permute and reused by every block of the plan.
+ *   UPDATE:     per block, the K tokens whose update by this block's attention sub-block,
+ *               x1 - x, has the largest squared L2 norm (fp32, ties to the lower slot, pads
+ *               never chosen); blocks of such plans run through sparsesam_block_dynamic.
+ */
+typedef enum sparsesam_routing {
+  SPARSESAM_ROUTE_IMPORTANCE = 0,
+  SPARSESAM_ROUTE_UPDATE = 1
+} sparsesam_routing;
+
+/*
  * What one plan describes: the segments of an image (one global segment of
  * grid_h*grid_w tokens, or window x window windows over the grid padded up to
  * multiples of `window`), the stripe-sort and its static attention pattern, the
@@ -115,6 +131,10 @@ typedef struct sparsesam_plan_desc {
   uint32_t order_seed;     /* seed of SPARSESAM_ORDER_RANDOM */
   int32_t rel_pos;         /* 1: blocks add the relative-position bias (block weights rel_pos_h,
                               rel_pos_w; segments of at most 64 x 64); 0: no bias */
+  int32_t routing;         /* sparsesam_routing: how a block picks its MLP keep-set */
+  int32_t mlp_merge;       /* 1: a segment's tokens outside the keep-set receive the mean MLP update of
+                              its keep-set (block calls only, segments of at most 16384 tokens);
+                              0: they stay bitwise unchanged */
 } sparsesam_plan_desc;
 
 typedef struct sparsesam_plan_info {
@@ -253,6 +273,8 @@ sparsesam_status sparsesam_attn_relpos(sparsesam_plan_t plan, int32_t segments, 
  * passes through the residual unchanged). For each row t in routed:
  *   x[t] += fc2(GELU(fc1(LayerNorm(x[t]))))   (exact-erf GELU, LayerNorm eps 1e-6)
  * Rows not in `routed` are never read or written.
+ * Plans with mlp_merge = 1 are not taken (UNSUPPORTED): the merge needs the segments, which
+ * the block calls have.
  *   x [rows, C] fp32; routed [routed_count] int32 distinct row ids in [0, rows);
  *   ln_g, ln_b [C] fp32; w1 [hidden, C], w2 [C, hidden] (plan dtype); b1 [hidden],
  *   b2 [C] fp32. routed_count must not exceed max_batch * routed_per_image;
@@ -262,6 +284,19 @@ sparsesam_status sparsesam_mlp(sparsesam_plan_t plan, float* x, int64_t rows, co
                                int32_t routed_count, const float* ln_g, const float* ln_b, const void* w1,
                                const float* b1, const void* w2, const float* b2, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * (4b) Keep-set selection by score: for each segment of `batch` images, the K tokens with the
+ * largest score (same page, selective-computation bullet; the selection of
+ * SPARSESAM_ROUTE_UPDATE plans), ranked like importance in sparsesam_permute: descending,
+ * -0.0 == +0.0, NaN after every number, ties to the lower slot, window pads never chosen.
+ *   score  [batch, grid_h * grid_w] fp32, tokens in raster order.
+ *   routed [batch * routed_per_image] int32: global row ids, segment by segment as in
+ *          sparsesam_permute, each segment's K tokens largest score first.
+ * Integer output, exactly determined by the scores. Works for plans of either routing.
+ */
+sparsesam_status sparsesam_route_topk(sparsesam_plan_t plan, const float* score, int32_t batch, int32_t* routed,
+                                      void* stream);
 
 /* Parameters of one pre-LN ViT block. Matrices in the plan dtype, [out, in]. */
 typedef struct sparsesam_block_weights {
@@ -293,11 +328,30 @@ typedef struct sparsesam_block_weights {
  *        relative-position bias (3b) when the plan has rel_pos = 1)
  *   x  = x + o W_proj^T + b_proj          scattered back to raster order, pads dropped
  *   x  = the routed MLP (4) on the keep-set
- * workspace >= block_workspace_bytes; batch <= max_batch.
+ * With mlp_merge = 1, every real token of a segment outside its keep-set then adds the mean
+ * of the keep-set's MLP updates (the reading of the residual-propagation bullet's
+ * y_i = x_i + eps_i taken for merging).
+ * workspace >= block_workspace_bytes; batch <= max_batch. Plans with routing = UPDATE are
+ * rejected (INVALID_ARGUMENT): their keep-set is chosen inside the block, see (5c).
  */
 sparsesam_status sparsesam_block(sparsesam_plan_t plan, const sparsesam_block_weights* weights /* host */,
                                  float* x, int32_t batch, const int32_t* perm, const int32_t* routed,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * (5c) One block of a plan with routing = SPARSESAM_ROUTE_UPDATE: as (5), except that after
+ * the attention sub-block (x1 = x + o W_proj^T + b_proj) each segment's keep-set is the K
+ * tokens with the largest ||x1[t] - x[t]||^2, chosen as by (4b), and the MLP (and the merge,
+ * when mlp_merge = 1) runs on that set.
+ *   routed_out [batch * routed_per_image] int32: receives the keep-set (layout of (4b)).
+ *   score_out  [batch, grid_h * grid_w] fp32 or NULL: receives every token's score.
+ *   perm as in (5); workspace >= block_workspace_bytes.
+ * The squared norms are summed in a fixed order, so the keep-set is reproducible run to run;
+ * it is exactly the (4b) selection of score_out.
+ */
+sparsesam_status sparsesam_block_dynamic(sparsesam_plan_t plan, const sparsesam_block_weights* weights /* host */,
+                                         float* x, int32_t batch, const int32_t* perm, int32_t* routed_out,
+                                         float* score_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * (6) Encoder: a stack of n_layers blocks (5) in place on x, layer l a global block
@@ -310,6 +364,7 @@ sparsesam_status sparsesam_block(sparsesam_plan_t plan, const sparsesam_block_we
  *   global_plan and window_plan share grid, channels, heads, head_dim, mlp_hidden,
  *   dtype and device; either may be null when no layer uses it.
  *   workspace >= the block_workspace_bytes of every plan used, batch <= their max_batch.
+ * Plans with routing = UPDATE are not taken (UNSUPPORTED): their blocks run through (5c).
  * Every layer is validated before the first launch: on INVALID_ARGUMENT, UNSUPPORTED,
  * NO_DEVICE or WORKSPACE nothing runs and x is untouched. A launch failure in layer l
  * returns ERR_HIP with layers 0..l-1 applied.

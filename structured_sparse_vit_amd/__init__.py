@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import SPARSESAM_BF16, SPARSESAM_F32, SparseSAMError, check
 
 __all__ = ["Plan", "importance", "permute", "attn", "mlp", "block", "block_noalloc", "noalloc_scratch_bytes",
-           "encoder", "SparseSAMError", "library_path", "weights_to_device"]
+           "route_topk", "block_dynamic", "encoder", "SparseSAMError", "library_path", "weights_to_device"]
 
 
 def library_path() -> str:
@@ -50,6 +50,8 @@ def _need(t, name, dtype=None, shape=None, device=None):
 
 # token orders ahead of the stripe-sort, in the C enum's order (sparsesam_ordering)
 ORDERINGS = ("importance", "zorder", "hilbert", "random")
+# how a block picks its MLP keep-set, in the C enum's order (sparsesam_routing)
+ROUTINGS = ("importance", "update")
 
 
 class Plan:
@@ -57,16 +59,20 @@ class Plan:
 
     def __init__(self, grid_h, grid_w, window, stripes, block, global_tokens, band_radius, attn_density,
                  mlp_density, channels, heads, head_dim, mlp_hidden, max_batch, dtype, ordering="importance",
-                 order_seed=0, rel_pos=False):
+                 order_seed=0, rel_pos=False, routing="importance", mlp_merge=False):
         lib = _lib.load()
         self._lib = lib
         self.dtype = dtype
         if ordering not in ORDERINGS:
             raise ValueError("ordering must be one of %s" % (ORDERINGS,))
+        if routing not in ROUTINGS:
+            raise ValueError("routing must be one of %s" % (ROUTINGS,))
+        self.routing = routing
         self.desc = _lib.PlanDesc(grid_h, grid_w, window, stripes, block, global_tokens, band_radius,
                                   attn_density, mlp_density, channels, heads, head_dim, mlp_hidden, max_batch,
                                   SPARSESAM_BF16 if dtype == "bf16" else SPARSESAM_F32, ORDERINGS.index(ordering),
-                                  order_seed & 0xFFFFFFFF, 1 if rel_pos else 0)
+                                  order_seed & 0xFFFFFFFF, 1 if rel_pos else 0, ROUTINGS.index(routing),
+                                  1 if mlp_merge else 0)
         h = ctypes.c_void_p()
         check(lib.sparsesam_plan_create(ctypes.byref(self.desc), ctypes.byref(h)), "sparsesam_plan_create")
         self._h = h
@@ -80,7 +86,8 @@ class Plan:
         return cls(cfg.grid, cfg.grid, cfg.window, cfg.stripes, cfg.block, cfg.global_tokens, cfg.band_radius,
                    cfg.attn_density, cfg.mlp_density, cfg.channels, cfg.heads, cfg.head_dim, cfg.mlp_hidden,
                    max_batch or cfg.batch, cfg.dtype, getattr(cfg, "ordering", "importance"),
-                   getattr(cfg, "order_seed", 0), rel_pos)
+                   getattr(cfg, "order_seed", 0), rel_pos, getattr(cfg, "routing", "importance"),
+                   bool(getattr(cfg, "mlp_merge", False)))
 
     @property
     def handle(self):
@@ -294,6 +301,46 @@ def block(plan, weights, x, perm, routed, workspace=None):
     check(lib.sparsesam_block(plan.handle, ctypes.byref(bw), _ptr(x), b, _ptr(perm), _ptr(routed), _ptr(ws),
                               ws.numel(), _stream(x.device)), "sparsesam_block")
     return x
+
+
+def route_topk(plan, score, out=None):
+    """Keep-set by score: per segment the K tokens with the largest score [b, tokens] fp32
+    (ties to the lower slot); returns routed int32 [b * routed_per_image]."""
+    lib = _lib.load()
+    tokens = plan.desc.grid_h * plan.desc.grid_w
+    _need(score, "score", torch.float32, device=plan.device)
+    if score.dim() != 2 or score.shape[1] != tokens:
+        raise ValueError("score must be [batch, %d]" % tokens)
+    b = score.shape[0]
+    if out is None:
+        out = torch.empty(b * plan.info["routed_per_image"], dtype=torch.int32, device=score.device)
+    _need(out, "out", torch.int32, (b * plan.info["routed_per_image"],), plan.device)
+    check(lib.sparsesam_route_topk(plan.handle, _ptr(score), b, _ptr(out), _stream(score.device)),
+          "sparsesam_route_topk")
+    return out
+
+
+def block_dynamic(plan, weights, x, perm, routed_out=None, score_out=None, workspace=None, want_score=True):
+    """One block of a plan with routing "update", in place on x: the keep-set of every
+    segment is chosen from this block's attention update. Returns (x, routed, score);
+    score is None when want_score is False and no score_out is given."""
+    lib = _lib.load()
+    if plan.routing != "update":
+        raise ValueError("block_dynamic needs a plan with routing='update'")
+    b = x.shape[0]
+    rpi, tokens = plan.info["routed_per_image"], plan.desc.grid_h * plan.desc.grid_w
+    if routed_out is None:
+        routed_out = torch.empty(b * rpi, dtype=torch.int32, device=x.device)
+    if score_out is None and want_score:
+        score_out = torch.empty(b, tokens, dtype=torch.float32, device=x.device)
+    b, bw = _block_args(plan, weights, x, perm, routed_out)
+    if score_out is not None:
+        _need(score_out, "score_out", torch.float32, (b, tokens), plan.device)
+    ws = _workspace(plan.info["block_workspace_bytes"], x.device, workspace)
+    check(lib.sparsesam_block_dynamic(plan.handle, ctypes.byref(bw), _ptr(x), b, _ptr(perm), _ptr(routed_out),
+                                      _ptr(score_out), _ptr(ws), ws.numel(), _stream(x.device)),
+          "sparsesam_block_dynamic")
+    return x, routed_out, score_out
 
 
 def block_noalloc(plan, weights, x, perm, routed):

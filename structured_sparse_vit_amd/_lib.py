@@ -37,6 +37,8 @@ EXPORTS = [
     "sparsesam_encoder",
     "sparsesam_noalloc_scratch_bytes",
     "sparsesam_block_noalloc",
+    "sparsesam_route_topk",
+    "sparsesam_block_dynamic",
 ]
 
 
@@ -48,6 +50,7 @@ class PlanDesc(ctypes.Structure):
         ("channels", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("mlp_hidden", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("ordering", ctypes.c_int32), ("order_seed", ctypes.c_uint32), ("rel_pos", ctypes.c_int32),
+        ("routing", ctypes.c_int32), ("mlp_merge", ctypes.c_int32),
     ]
 
 
@@ -102,6 +105,8 @@ def load():
         "sparsesam_encoder": ([P, P, ctypes.POINTER(BlockWeights), P, I32, P, I32, P, P, P, P, P, SZ, P], I32),
         "sparsesam_noalloc_scratch_bytes": ([], SZ),
         "sparsesam_block_noalloc": ([P, ctypes.POINTER(BlockWeights), P, I32, P, P, P], I32),
+        "sparsesam_route_topk": ([P, P, I32, P, P], I32),
+        "sparsesam_block_dynamic": ([P, ctypes.POINTER(BlockWeights), P, I32, P, P, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

@@ -86,7 +86,17 @@ BlockLayout block_layout(const sparsesam_plan& p, int batch) {
     off += R.part - R.kc;
   }
   L.total_attn = off;
+  if (p.desc.routing == SPARSESAM_ROUTE_UPDATE) {
+    L.sq_ld = (int)((C + 31) / 32);
+    L.sq = off;
+    off += align256((size_t)batch * p.desc.grid_h * p.desc.grid_w * L.sq_ld * sizeof(float));
+    L.total_dyn = off;
+  }
   L.total_mlp = mlp_workspace(p, batch * p.routed_per_image, &L.a2, &L.hid);
+  if (p.desc.mlp_merge) {
+    L.upd = L.total_mlp;
+    L.total_merge = L.upd + align256((size_t)batch * p.routed_per_image * C * sizeof(float));
+  }
   return L;
 }
 
@@ -128,6 +138,10 @@ static sparsesam_status validate_desc(const sparsesam_plan_desc& d) {
   if (d.ordering < SPARSESAM_ORDER_IMPORTANCE || d.ordering > SPARSESAM_ORDER_RANDOM)
     return invalid("ordering must be a sparsesam_ordering value");
   if (d.rel_pos != 0 && d.rel_pos != 1) return invalid("rel_pos must be 0 or 1");
+  if (d.routing != SPARSESAM_ROUTE_IMPORTANCE && d.routing != SPARSESAM_ROUTE_UPDATE)
+    return invalid("routing must be a sparsesam_routing value");
+  if (d.mlp_merge != 0 && d.mlp_merge != 1) return invalid("mlp_merge must be 0 or 1");
+  if (d.mlp_merge && n > 16384) return unsupported("mlp_merge needs segments of at most 16384 tokens");
   if (d.channels > 1536) return unsupported("channels above 1536 are not supported");
   if (d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 80 && d.head_dim != 128)
     return unsupported("head_dim must be 32, 64, 80 or 128");
@@ -341,7 +355,7 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     return unsupported("a segment's keys or an image's token flags do not fit the permutation kernels' 160 KiB of LDS");
   }
   BlockLayout L = block_layout(*p, d.max_batch);
-  p->block_ws = std::max(L.total_attn, L.total_mlp);
+  p->block_ws = L.total();
   size_t a2, hid;
   p->mlp_ws = mlp_workspace(*p, d.max_batch * p->routed_per_image, &a2, &hid);
 
@@ -561,6 +575,8 @@ sparsesam_status sparsesam_mlp(sparsesam_plan_t p, float* x, int64_t rows, const
   if ((int64_t)routed_count > rows) return invalid("routed_count exceeds rows");
   if ((int64_t)routed_count > (int64_t)p->desc.max_batch * p->routed_per_image)
     return invalid("routed_count exceeds max_batch * routed_per_image");
+  if (p->desc.mlp_merge)
+    return unsupported("sparsesam_mlp does not take mlp_merge plans: the merge needs the block calls' segments");
   if (routed_count == 0) return SPARSESAM_OK;
   if (!x || !routed || !ln_g || !ln_b || !w1 || !b1 || !w2 || !b2) return invalid("null pointer argument");
   size_t a2, hid;
@@ -579,9 +595,11 @@ sparsesam_status sparsesam_mlp(sparsesam_plan_t p, float* x, int64_t rows, const
 
 }  // extern "C"
 
+// One block. routed: the keep-set (input) or, for dynamic plans, where the block writes
+// the keep-set it selects (score_out optional).
 template <typename T>
 static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weights& w, float* x, int batch,
-                            const int32_t* perm, const int32_t* routed, char* ws, hipStream_t st) {
+                            const int32_t* perm, int32_t* routed, float* score_out, char* ws, hipStream_t st) {
   BlockLayout L = block_layout(p, batch);
   const int segs = batch * p.segs_per_img;
   const int M = segs * p.n;
@@ -604,9 +622,18 @@ static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weigh
   else
     e = launch_attention<T>(p, segs, q, k, vt, o, scale, ws + L.part, st);
   if (e != hipSuccess) return e;
+  const bool dynamic = p.desc.routing == SPARSESAM_ROUTE_UPDATE;
   EpiResidualScatter er{w.b_proj, x, perm, nullptr, p.segmap(), C, x_rows};
+  if (dynamic) {  // the projection epilogue also sums each token's squared update
+    er.sq_part = reinterpret_cast<float*>(ws + L.sq);
+    er.sq_ld = L.sq_ld;
+  }
   e = launch_gemm_residual<T>(o, (const T*)w.w_proj, M, C, C, er, st);
   if (e != hipSuccess) return e;
+  if (dynamic) {
+    e = launch_route_topk(p, reinterpret_cast<const float*>(ws + L.sq), L.sq_ld, batch, routed, score_out, st);
+    if (e != hipSuccess) return e;
+  }
   const int rows = batch * p.routed_per_image;
   T* a2 = reinterpret_cast<T*>(ws + L.a2);
   T* hid = reinterpret_cast<T*>(ws + L.hid);
@@ -616,7 +643,10 @@ static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weigh
   e = launch_gemm_gelu<T>(a2, (const T*)w.w1, rows, p.desc.mlp_hidden, C, eg, st);
   if (e != hipSuccess) return e;
   EpiResidualScatter e2{w.b2, x, nullptr, routed, p.segmap(), C, x_rows};
-  return launch_gemm_residual<T>(hid, (const T*)w.w2, rows, C, p.desc.mlp_hidden, e2, st);
+  if (p.desc.mlp_merge) e2.upd = reinterpret_cast<float*>(ws + L.upd);  // keep the updates for the merge
+  e = launch_gemm_residual<T>(hid, (const T*)w.w2, rows, C, p.desc.mlp_hidden, e2, st);
+  if (e != hipSuccess || !p.desc.mlp_merge) return e;
+  return launch_merge(p, x, batch, routed, reinterpret_cast<const float*>(ws + L.upd), st);
 }
 
 // Validation of one block call (no launch, no side effects).
@@ -639,7 +669,7 @@ static sparsesam_status block_check(sparsesam_plan_t p, const sparsesam_block_we
   if (!p->desc.rel_pos && (w->rel_pos_h || w->rel_pos_w))
     return invalid("rel_pos_h / rel_pos_w given to a plan created with rel_pos = 0");
   BlockLayout L = block_layout(*p, batch);
-  size_t need = std::max(L.total_attn, L.total_mlp);
+  size_t need = L.total();
   if (!workspace || workspace_bytes < need) {
     set_error("block workspace needs " + std::to_string(need) + " bytes");
     return SPARSESAM_ERR_WORKSPACE;
@@ -647,17 +677,27 @@ static sparsesam_status block_check(sparsesam_plan_t p, const sparsesam_block_we
   return SPARSESAM_OK;
 }
 
+// routed: the keep-set for static plans, the keep-set output for dynamic ones
 static sparsesam_status block_impl(sparsesam_plan_t p, const sparsesam_block_weights* w, float* x, int32_t batch,
-                                   const int32_t* perm, const int32_t* routed, void* workspace,
+                                   const int32_t* perm, int32_t* routed, float* score_out, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   sparsesam_status st = block_check(p, w, x, batch, perm, routed, workspace, workspace_bytes);
   if (st != SPARSESAM_OK || batch == 0) return st;
   hipError_t e;
   if (p->desc.dtype == SPARSESAM_BF16)
-    e = run_block<bf16_t>(*p, *w, x, batch, perm, routed, (char*)workspace, (hipStream_t)stream);
+    e = run_block<bf16_t>(*p, *w, x, batch, perm, routed, score_out, (char*)workspace, (hipStream_t)stream);
   else
-    e = run_block<float>(*p, *w, x, batch, perm, routed, (char*)workspace, (hipStream_t)stream);
+    e = run_block<float>(*p, *w, x, batch, perm, routed, score_out, (char*)workspace, (hipStream_t)stream);
   return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_block launch");
+}
+
+static sparsesam_status static_plan(sparsesam_plan_t p, const char* what) {
+  if (p && p->desc.routing == SPARSESAM_ROUTE_UPDATE) {
+    set_error(std::string(what) + ": the plan chooses its keep-set per block (routing = UPDATE); "
+              "run its blocks through sparsesam_block_dynamic");
+    return SPARSESAM_ERR_INVALID_ARGUMENT;
+  }
+  return SPARSESAM_OK;
 }
 
 extern "C" {
@@ -665,7 +705,29 @@ extern "C" {
 sparsesam_status sparsesam_block(sparsesam_plan_t p, const sparsesam_block_weights* w, float* x, int32_t batch,
                                  const int32_t* perm, const int32_t* routed, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  return block_impl(p, w, x, batch, perm, routed, workspace, workspace_bytes, stream);
+  sparsesam_status st = static_plan(p, "sparsesam_block");
+  if (st != SPARSESAM_OK) return st;
+  // a static plan's block only reads the keep-set
+  return block_impl(p, w, x, batch, perm, const_cast<int32_t*>(routed), nullptr, workspace, workspace_bytes, stream);
+}
+
+sparsesam_status sparsesam_block_dynamic(sparsesam_plan_t p, const sparsesam_block_weights* w, float* x,
+                                         int32_t batch, const int32_t* perm, int32_t* routed_out, float* score_out,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (p && p->desc.routing != SPARSESAM_ROUTE_UPDATE)
+    return invalid("sparsesam_block_dynamic needs a plan with routing = SPARSESAM_ROUTE_UPDATE");
+  return block_impl(p, w, x, batch, perm, routed_out, score_out, workspace, workspace_bytes, stream);
+}
+
+sparsesam_status sparsesam_route_topk(sparsesam_plan_t p, const float* score, int32_t batch, int32_t* routed,
+                                      void* stream) {
+  sparsesam_status st = check_device(p);
+  if (st != SPARSESAM_OK) return st;
+  if (batch < 0) return invalid("batch must be >= 0");
+  if (batch == 0) return SPARSESAM_OK;
+  if (!score || !routed) return invalid("score and routed must not be null");
+  hipError_t e = launch_route_topk(*p, score, 1, batch, routed, nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_route_topk launch");
 }
 
 }  // extern "C"
@@ -711,18 +773,20 @@ sparsesam_status sparsesam_block_noalloc(sparsesam_plan_t p, const sparsesam_blo
   if (batch < 0 || batch > p->desc.max_batch) return invalid("batch must be in [0, max_batch]");
   if (batch == 0) return block_check(p, w, x, 0, perm, routed, nullptr, 0);
   const BlockLayout L = block_layout(*p, batch);
-  const size_t need = std::max(L.total_attn, L.total_mlp);
+  const size_t need = L.total();
   if (need > kNoAllocScratchBytes) {
     set_error("sparsesam_block_noalloc: this block needs " + std::to_string(need) +
               " bytes of scratch at batch " + std::to_string(batch) + ", above the library's fixed " +
               std::to_string(kNoAllocScratchBytes) + " bytes; use sparsesam_block with a workspace");
     return SPARSESAM_ERR_WORKSPACE;
   }
+  st = static_plan(p, "sparsesam_block_noalloc");
+  if (st != SPARSESAM_OK) return st;
   void* ws = nullptr;
   st = scratch_address(p->device, &ws);
   if (st != SPARSESAM_OK) return st;
   // the kernels write every scratch byte they read (no region has to start at zero)
-  return block_impl(p, w, x, batch, perm, routed, ws, kNoAllocScratchBytes, stream);
+  return block_impl(p, w, x, batch, perm, const_cast<int32_t*>(routed), nullptr, ws, kNoAllocScratchBytes, stream);
 }
 
 sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_t window_plan,
@@ -743,6 +807,10 @@ sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_
   }
   if (any_global && !global_plan) return invalid("a global layer needs global_plan");
   if (any_window && !window_plan) return invalid("a windowed layer needs window_plan");
+  for (sparsesam_plan_t pl : {global_plan, window_plan})
+    if (pl && pl->desc.routing == SPARSESAM_ROUTE_UPDATE)
+      return unsupported("sparsesam_encoder does not take plans with routing = UPDATE; run their blocks through "
+                         "sparsesam_block_dynamic");
   if (any_global && any_window) {
     const sparsesam_plan_desc &g = global_plan->desc, &w = window_plan->desc;
     if (g.grid_h != w.grid_h || g.grid_w != w.grid_w || g.channels != w.channels || g.heads != w.heads ||
@@ -760,7 +828,8 @@ sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_
   }
   for (int l = 0; l < n_layers; ++l) {
     sparsesam_status st = block_impl(kinds[l] ? global_plan : window_plan, &layers[l], x, batch,
-                                     kinds[l] ? perm_global : perm_window, kinds[l] ? routed_global : routed_window,
+                                     kinds[l] ? perm_global : perm_window,
+                                     const_cast<int32_t*>(kinds[l] ? routed_global : routed_window), nullptr,
                                      workspace, workspace_bytes, stream);
     if (st != SPARSESAM_OK) return st;
   }

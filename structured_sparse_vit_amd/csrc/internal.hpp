@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -94,7 +95,14 @@ sparsesam_status hip_fail(hipError_t e, const char* where);
 // Workspace carve-up of sparsesam_block / sparsesam_mlp.
 struct BlockLayout {
   size_t h = 0, q = 0, k = 0, vt = 0, o = 0, part = 0, rel_table = 0, rel_kc = 0, total_attn = 0;
+  // dynamic routing: squared-update partials [x rows, sq_ld] after the attention region
+  // (read by the keep-set selection before the MLP region is written)
+  size_t sq = 0, total_dyn = 0;
+  int sq_ld = 0;
   size_t a2 = 0, hid = 0, total_mlp = 0;
+  // merging: the keep-set's updates [routed rows, C] fp32 after the MLP region
+  size_t upd = 0, total_merge = 0;
+  size_t total() const { return std::max(std::max(total_attn, total_dyn), std::max(total_mlp, total_merge)); }
 };
 BlockLayout block_layout(const sparsesam_plan& p, int batch);
 // Workspace carve-up of the relative-position bias: tables (sized for fp32 entries),
@@ -110,6 +118,16 @@ hipError_t launch_importance(const float* img, int batch, int height, int width,
                              hipStream_t st);
 hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
                           hipStream_t st);
+// Keep-set of every segment by score (descending, ties to the lower slot, pads last):
+// score [batch, tokens, parts] partial sums added in order; score_out (optional)
+// receives each token's summed score.
+hipError_t launch_route_topk(const sparsesam_plan& p, const float* score, int parts, int batch, int* routed,
+                             float* score_out, hipStream_t st);
+// The merge of mlp_merge plans: every real token of a segment outside its keep-set gets
+// the mean of the keep-set's updates upd [batch * routed_per_image, C] (rows in the
+// keep-set's layout).
+hipError_t launch_merge(const sparsesam_plan& p, float* x, int batch, const int* routed, const float* upd,
+                        hipStream_t st);
 
 // LayerNorm of gathered rows: out[r] = LN(x[src(r)]) for r < rows_out, zero rows for pads.
 // Row source: mode 0 = stripe-sorted segment rows through perm, mode 1 = explicit list.
@@ -125,7 +143,7 @@ struct EpiQKV {  // q, k [seg, H, N, D]; vt [seg, H, D, N_pad]
   void* vt;
   int n, n_pad, heads, head_dim, channels;
 };
-struct EpiResidualScatter {  // x[map(r)] += acc + bias, or partials when split
+struct EpiResidualScatter {  // x[map(r)] += acc + bias
   const float* bias;
   float* x;
   const int* perm;  // stripe-sorted rows -> slot (mode 0), or null
@@ -133,6 +151,13 @@ struct EpiResidualScatter {  // x[map(r)] += acc + bias, or partials when split
   SegmentMap map;
   int ldx;
   long long x_rows;  // rows of x; destination rows outside [0, x_rows) are skipped
+  // optional: squared-update partial sums, sq_part[dst row * sq_ld + column / 32] = the sum of
+  // (acc + bias)^2 over a block of 32 or 64 columns starting at that column (a 64-column
+  // block writes 0 into its second slot); sq_ld = ceil(N / 32)
+  float* sq_part = nullptr;
+  int sq_ld = 0;
+  // optional: upd[r * ldx + c] = acc + bias (the update itself, by GEMM row r)
+  float* upd = nullptr;
 };
 struct EpiGelu {  // out[r, c] = GELU(acc + bias)
   const float* bias;

@@ -19,12 +19,14 @@
 // are read from LDS while the MFMAs of the current one run, across step boundaries
 // too, so one wavefront per SIMD keeps its matrix core fed.
 //
-// Epilogue straight from the accumulators: the MFMA operands are ordered so that a
-// lane's accumulator holds one output row with four consecutive columns per group of
-// four registers; one v_permlane32_swap per register pair then gives every lane eight
-// consecutive columns of one row (eight consecutive tokens of one channel for the
-// transposed V tiles), written as one 16-byte (bf16) or 32-byte (fp32) chunk. No LDS
-// staging, no barrier after the K loop.
+// Epilogue: after a barrier (every wavefront done with the ring), each wavefront stages
+// its accumulators, one 32-row block at a time, in a private LDS area and reads them
+// back so that every lane holds eight consecutive columns of one row and the lanes of
+// a store instruction cover whole row segments; the epilogue then writes them as
+// 16-byte (bf16) or 32-byte (fp32) chunks. Tiles written along tokens (the transposed
+// V tiles of the QKV product) skip the staging: one v_permlane32_swap per register
+// pair gives every lane eight consecutive tokens of one channel straight from the
+// accumulators.
 #include <algorithm>
 #include <type_traits>
 
@@ -95,6 +97,7 @@ struct QKVStore {
     T* base = is_v ? vt : (which == 0 ? q : k);
     base[idx] = from_f32<T>(v);
   }
+  static constexpr bool kRowSq = false;
   // Tiles whose columns are all V columns are written along tokens.
   __device__ __forceinline__ bool col_tile(int c0) const { return c0 >= 2 * C; }
 
@@ -164,6 +167,7 @@ struct GeluStore {
   const float* bias;
   T* out;
   int ld;
+  static constexpr bool kRowSq = false;
   __device__ __forceinline__ void elem(int r, int c, float v) const {
     out[(size_t)r * ld + c] = from_f32<T>(gelu_erf(v + bias[c]));
   }
@@ -207,7 +211,9 @@ struct GeluStore {
 
 // Residual update of the fp32 stream: x[dst(r), c] += acc + bias, where dst maps a
 // stripe-sorted row back to its token (through perm and the segment map; pads have
-// no destination) or takes it from an explicit row list (the keep-set).
+// no destination) or takes it from an explicit row list (the keep-set). Optionally
+// also the squared-update partial sums of each destination row (sq_part, the dynamic
+// keep-set's scores) and the updates themselves by GEMM row (upd, the merge).
 struct ResidualAdd {
   const float* bias;
   float* x;
@@ -216,15 +222,52 @@ struct ResidualAdd {
   SegmentMap map;
   int ldx;
   long long x_rows;
+  float* sq_part;
+  int sq_ld;
+  float* upd;
+  static constexpr bool kRowSq = true;
   __device__ __forceinline__ int dst_row(int r) const {
     if (list) return list[r];
     return map.row_of(map.seg_of(r), perm[r]);
   }
   __device__ __forceinline__ void elem(int r, int c, float v) const {
+    const float u = v + bias[c];
+    if (upd) upd[(size_t)r * ldx + c] = u;
     const int row = dst_row(r);
     if (row < 0 || row >= x_rows) return;
     float* px = x + (size_t)row * ldx + c;
-    *px = *px + (v + bias[c]);
+    *px = *px + u;
+  }
+  // Squared-update partial sums of the staged epilogue: a lane holds eight columns c0..c0+7
+  // of rows r[t]; the CPR consecutive lanes of one row cover the wavefront's column block
+  // [cb0, cb0 + W) (W = 8 CPR, 32 or 64). Each lane squares and adds its eight updates in
+  // order, the lanes of a row fold by xor shuffles (offsets 1, 2, ...), and the block's
+  // first lane writes the sum (and, for W = 64, a zero into the second 32-column slot).
+  template <int CPR, int MR>
+  __device__ __forceinline__ void row_sq(const int (&r)[MR], int c0, float (&v)[MR][1][8], int M, int N,
+                                         int cb0) const {
+    float b[8];
+    load_bias8(bias, c0, N, b);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < MR; ++t) {
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float u = c0 + e < N ? v[t][0][e] + b[e] : 0.0f;
+        s = s + u * u;
+      }
+#pragma unroll
+      for (int o = 1; o < CPR; o <<= 1) s += __shfl_xor(s, o, 64);
+      if (lane % CPR == 0 && r[t] < M) {
+        const int row = dst_row(r[t]);
+        if (row >= 0 && row < x_rows) {
+          float* dst = sq_part + (size_t)row * sq_ld + cb0 / 32;
+          dst[0] = s;
+          if (CPR == 8 && cb0 / 32 + 1 < sq_ld) dst[1] = 0.0f;
+        }
+      }
+    }
   }
   __device__ __forceinline__ bool col_tile(int) const { return false; }
   // destination rows, then every chunk's current values, then the updates: the loads
@@ -248,10 +291,14 @@ struct ResidualAdd {
       if (c[j] + 8 > N) {
 #pragma unroll
         for (int i = 0; i < MR; ++i)
-          if (off[i] >= 0)
+          if (r[i] < M)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              if (c[j] + e < N) x[off[i] + c[j] + e] += v[i][j][e] + bias[c[j] + e];
+              if (c[j] + e < N) {
+                const float u = v[i][j][e] + bias[c[j] + e];
+                if (upd) upd[(size_t)r[i] * ldx + c[j] + e] = u;
+                if (off[i] >= 0) x[off[i] + c[j] + e] += u;
+              }
         continue;
       }
       float b[8];
@@ -275,6 +322,17 @@ struct ResidualAdd {
           *reinterpret_cast<f32x4*>(x + off[i] + c[j]) = a;
           *reinterpret_cast<f32x4*>(x + off[i] + c[j] + 4) = d;
         }
+      if (upd) {
+#pragma unroll
+        for (int i = 0; i < MR; ++i)
+          if (r[i] < M) {
+            float* pu = upd + (size_t)r[i] * ldx + c[j];
+            *reinterpret_cast<f32x4*>(pu) =
+                f32x4{v[i][j][0] + b[0], v[i][j][1] + b[1], v[i][j][2] + b[2], v[i][j][3] + b[3]};
+            *reinterpret_cast<f32x4*>(pu + 4) =
+                f32x4{v[i][j][4] + b[4], v[i][j][5] + b[5], v[i][j][6] + b[6], v[i][j][7] + b[7]};
+          }
+      }
     }
   }
   template <int NCOL, int RC>
@@ -529,6 +587,9 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
         }
       }
       epi.rows(r, cc, v, M, N);
+      if constexpr (Epi::kRowSq) {
+        if (epi.sq_part) epi.template row_sq<CPR>(r, cc[0], v, M, N, n0 + wn * TL::WN);
+      }
     }
   } else {
     // lane: column wn*WN + 32j + l32; rows wm*WM + 32i + 16p + 8hi .. + 7
@@ -618,6 +679,34 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
       int m = m0 + tr + 16 * i, n = n0 + tc + 16 * j;
       if (m < M && n < N) epi.elem(m, n, acc[i][j]);
     }
+  if constexpr (Epi::kRowSq) {
+    // squared-update partial sums over the tile's 64 columns: each thread adds its four
+    // columns in order, the 16 consecutive lanes of a row fold by xor shuffles, and lane
+    // tc = 0 writes the sum into the slot of column n0 and a zero into the next one
+    if (epi.sq_part) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + tr + 16 * i;
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + tc + 16 * j;
+          const float u = n < N ? acc[i][j] + epi.bias[n] : 0.0f;
+          s = s + u * u;
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+        if (tc == 0 && m < M) {
+          const int row = epi.dst_row(m);
+          if (row >= 0 && row < epi.x_rows) {
+            float* dst = epi.sq_part + (size_t)row * epi.sq_ld + n0 / 32;
+            dst[0] = s;
+            if (n0 / 32 + 1 < epi.sq_ld) dst[1] = 0.0f;
+          }
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -733,7 +822,7 @@ template <typename T>
 hipError_t launch_gemm_residual(const T* a, const T* w, int m, int n, int k, const EpiResidualScatter& e,
                                 hipStream_t st) {
   if (m <= 0) return hipSuccess;
-  ResidualAdd s{e.bias, e.x, e.perm, e.list, e.map, e.ldx, e.x_rows};
+  ResidualAdd s{e.bias, e.x, e.perm, e.list, e.map, e.ldx, e.x_rows, e.sq_part, e.sq_ld, e.upd};
   return run(a, w, m, n, k, s, st);
 }
 

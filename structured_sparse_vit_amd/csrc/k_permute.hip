@@ -16,6 +16,11 @@
 // and the slot is in the keep-set iff rho < K, at index rho of the segment's part of
 // the keep-set list. No sorted list is ever materialised.
 //
+// The same kernel selects the keep-set of plans whose routing follows a score (the
+// squared attention update of a block): the score takes the place of importance (with
+// the importance order forced), it may arrive as `parts` partial sums per token that the
+// key fill adds in order, and perm / inv are not written.
+//
 // rank_kernel: one workgroup per (segment, chunk of slots). Its lanes count, for the
 // chunk's slots, the preceding slots within shares of the segment's keys (held in LDS
 // as 64-bit order words); lanes of one slot fold their counts with shuffles, the
@@ -103,7 +108,8 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
                                                                   int routed_per_image, int* __restrict__ perm,
                                                                   int* __restrict__ inv, int* __restrict__ routed,
                                                                   int ordering, uint32_t seed, int seg_w,
-                                                                  int hilbert_side) {
+                                                                  int hilbert_side, int parts,
+                                                                  float* __restrict__ score_out) {
   extern __shared__ __attribute__((aligned(16))) uint64_t key_lds[];  // padded to a multiple of 64
   __shared__ int part[kMaxRankWaves * 64];
   const int seg = blockIdx.x / chunks, chunk = blockIdx.x - (blockIdx.x / chunks) * chunks;
@@ -111,7 +117,15 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
   const int kw = blockDim.x >> 6;
   const int tokens = map.grid_h * map.grid_w;
   const int img = map.f_spi.div(seg);
-  const float* im = imp + (size_t)img * tokens;
+  const float* im = imp + (size_t)img * tokens * parts;
+  // a token's key value: imp[token], or the in-order sum of its `parts` partials
+  auto value = [&](int tok) {
+    if (parts == 1) return im[tok];
+    const float* pp = im + (size_t)tok * parts;
+    float v = pp[0];
+    for (int c = 1; c < parts; ++c) v = v + pp[c];
+    return v;
+  };
   const int n64 = (n + 63) & ~63;
   // keys past n are pad keys with index >= n: they never precede a real slot. Four
   // slots per thread at a time, their importance loads all issued before the first
@@ -125,7 +139,12 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
       const int s = base + tid + u * (int)blockDim.x;
       rows[u] = s < n ? map.row_of(seg, s) : -1;
       vals[u] = 0.0f;
-      if (ordering == SPARSESAM_ORDER_IMPORTANCE) vals[u] = im[max(rows[u] - img * tokens, 0)];
+      if (ordering == SPARSESAM_ORDER_IMPORTANCE && parts == 1) vals[u] = im[max(rows[u] - img * tokens, 0)];
+    }
+    if (parts > 1) {
+#pragma unroll
+      for (int u = 0; u < kFillUnroll; ++u)
+        if (rows[u] >= 0) vals[u] = value(rows[u] - img * tokens);
     }
 #pragma unroll
     for (int u = 0; u < kFillUnroll; ++u) {
@@ -179,9 +198,15 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
       const int S = n / stripes;
       const int p = (rank % stripes) * S + rank / stripes;
       const size_t base = (size_t)seg * n;
-      perm[base + p] = sl;
-      inv[base + sl] = p;
+      if (perm) {
+        perm[base + p] = sl;
+        inv[base + sl] = p;
+      }
       const int w_img = seg - img * map.segs_per_img;
+      if (score_out) {
+        const int row = map.row_of(seg, sl);
+        if (row >= 0) score_out[row] = value(row - img * tokens);
+      }
       if (rank < seg_k[w_img])  // K <= real slots, so never a pad
         routed[(size_t)img * routed_per_image + seg_off[w_img] + rank] = map.row_of(seg, sl);
     }
@@ -190,8 +215,8 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
 
 size_t permute_lds_bytes(const sparsesam_plan& p) { return (size_t)((p.n + 63) & ~63) * 8; }
 
-hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
-                          hipStream_t st) {
+static hipError_t launch_rank(const sparsesam_plan& p, const float* imp, int parts, int batch, int* perm, int* inv,
+                              int* routed, float* score_out, int ordering, hipStream_t st) {
   // long segments: 16 slots per workgroup and up to 16 wavefronts splitting the keys;
   // short ones (windows): 64 slots per workgroup, one wavefront per 256 keys
   const int tpw = p.n >= 1024 ? 16 : 64;
@@ -209,8 +234,18 @@ hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, 
   while (side < std::max(seg_h, seg_w)) side *= 2;
   hipLaunchKernelGGL(rank_kernel, dim3((unsigned)(segs * chunks)), dim3(64 * kw), key_bytes, st, imp, p.segmap(),
                      p.n, p.desc.stripes, chunks, tpw, p.d_seg_k, p.d_seg_off, p.routed_per_image, perm, inv, routed,
-                     (int)p.desc.ordering, p.desc.order_seed, seg_w, side);
+                     ordering, p.desc.order_seed, seg_w, side, parts, score_out);
   return hipGetLastError();
+}
+
+hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
+                          hipStream_t st) {
+  return launch_rank(p, imp, 1, batch, perm, inv, routed, nullptr, (int)p.desc.ordering, st);
+}
+
+hipError_t launch_route_topk(const sparsesam_plan& p, const float* score, int parts, int batch, int* routed,
+                             float* score_out, hipStream_t st) {
+  return launch_rank(p, score, parts, batch, nullptr, nullptr, routed, score_out, SPARSESAM_ORDER_IMPORTANCE, st);
 }
 
 }  // namespace sparsesam

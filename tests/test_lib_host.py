@@ -277,3 +277,49 @@ def test_attn_relpos_validation_before_launch():
         assert lib.sparsesam_attn_relpos(plan.handle, 1, p, p, p, p, f, p, p, p, p, 16, None) == 3  # workspace
     else:
         assert lib.sparsesam_attn_relpos(plan.handle, 1, p, p, p, p, f, p, p, p, p, 1 << 30, None) == 6
+
+
+# ------------------------------------------------------------------ dynamic routing and the merge
+
+def test_routing_and_merge_plan_validation_and_workspace():
+    base = _create()
+    dyn = _create(routing="update")
+    mrg = _create(mlp_merge=True)
+    both = _create(routing="update", mlp_merge=True)
+    # the dynamic plan adds the squared-update partials (one fp32 per 32 channels per token),
+    # the merge the keep-set's fp32 updates; the pattern and keep-set size are unchanged
+    assert dyn.info["block_workspace_bytes"] >= base.info["block_workspace_bytes"] + 4096 * 24 * 4
+    assert mrg.info["block_workspace_bytes"] >= 1638 * (768 * 2 + 3072 * 2) + 1638 * 768 * 4
+    assert both.info["block_workspace_bytes"] >= max(dyn.info["block_workspace_bytes"],
+                                                     mrg.info["block_workspace_bytes"])
+    for p in (dyn, mrg, both):
+        assert p.info["tiles_kept"] == base.info["tiles_kept"]
+        assert p.info["routed_per_image"] == base.info["routed_per_image"]
+    lib = _lib.load()
+    for field, val in (("routing", 2), ("routing", -1), ("mlp_merge", 2)):
+        d = _lib.PlanDesc(64, 64, 0, 4, 64, 64, -1, 0.4, 0.4, 768, 12, 64, 3072, 1, 1, 0, 0, 0, 0, 0)
+        setattr(d, field, val)
+        h = ctypes.c_void_p()
+        assert lib.sparsesam_plan_create(ctypes.byref(d), ctypes.byref(h)) == 1, field
+    # the merge keeps a bit per slot of a segment in LDS: at most 16384 slots
+    with pytest.raises(ss.SparseSAMError) as ei:
+        _create(grid_h=160, grid_w=160, block=40, global_tokens=40, mlp_merge=True, channels=768)
+    assert ei.value.status == 2
+
+
+def test_routing_entry_points_check_the_plan_kind_first():
+    """Block calls check the plan's routing before anything else (so without a GPU too):
+    sparsesam_block rejects dynamic plans, sparsesam_block_dynamic static ones, and the
+    encoder does not take dynamic plans."""
+    lib = _lib.load()
+    dyn, sta = _create(routing="update"), _create()
+    w = _lib.BlockWeights()
+    p = ctypes.c_void_p(16)
+    assert lib.sparsesam_block(dyn.handle, ctypes.byref(w), p, 1, p, p, p, 1 << 30, None) == 1
+    assert b"sparsesam_block_dynamic" in lib.sparsesam_last_error()
+    assert lib.sparsesam_block_dynamic(sta.handle, ctypes.byref(w), p, 1, p, p, None, p, 1 << 30, None) == 1
+    assert lib.sparsesam_block_noalloc(dyn.handle, ctypes.byref(w), p, 1, p, p, None) in (1, 6)
+    layers = (_lib.BlockWeights * 1)()
+    karr = (ctypes.c_uint8 * 1)(1)
+    assert lib.sparsesam_encoder(dyn.handle, None, layers, karr, 1, p, 1, p, p, p, p, p, 1 << 30, None) == 2
+    assert lib.sparsesam_route_topk(None, p, 1, p, None) == 1
