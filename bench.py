@@ -15,6 +15,7 @@ bf16 dense block) and the CPU oracle timed on this host on a bounded sample.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--profile-only]
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -180,11 +181,12 @@ def torch_dense_block_ms(cfg, dev, iters=20):
         return time_region(run, iters, 3)
 
 
-def encoder_run(key, dev, density=None, passes=3, rel_pos=False):
+def encoder_run(key, dev, density=None, passes=3, rel_pos=False, sorted_stream=False):
     """One pass of a whole encoder config (c4: ViT-L 24 blocks, c5: ViT-H 32 blocks) through
-    sparsesam_encoder: importance and both permutations once per pass, then every block.
-    Timing only: one random-init layer's weights serve every layer (the work per layer
-    is the same). Returns tokens/s and ms per pass."""
+    sparsesam_encoder (or, sorted_stream, sparsesam_encoder_permuted: the residual stream
+    kept in stripe-sorted order between blocks): importance and both permutations once
+    per pass, then every block. Timing only: one random-init layer's weights serve every
+    layer (the work per layer is the same). Returns tokens/s and ms per pass."""
     import torch
 
     import structured_sparse_vit_amd as ss
@@ -213,12 +215,23 @@ def encoder_run(key, dev, density=None, passes=3, rel_pos=False):
     ws = torch.empty(max(pg.info["block_workspace_bytes"], pw.info["block_workspace_bytes"]), dtype=torch.uint8,
                      device=dev)
 
+    if sorted_stream:
+        need = ctypes.c_size_t()
+        lib = ss._lib.load()
+        ss.check(lib.sparsesam_encoder_permuted_workspace(pg.handle, pw.handle, base.batch, ctypes.byref(need)),
+                 "sparsesam_encoder_permuted_workspace")
+        del ws
+        ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+
     def one_pass():
         x.copy_(x0)  # every pass starts from the same features
         imp = ss.importance(img, base.patch)
-        perm_g, _, routed_g = ss.permute(pg, imp)
-        perm_w, _, routed_w = ss.permute(pw, imp)
-        ss.encoder(pg, pw, layers, kinds, x, (perm_g, routed_g), (perm_w, routed_w), workspace=ws)
+        perm_g, inv_g, routed_g = ss.permute(pg, imp)
+        perm_w, inv_w, routed_w = ss.permute(pw, imp)
+        if sorted_stream:
+            ss.encoder(pg, pw, layers, kinds, x, (perm_g, inv_g), (perm_w, inv_w), workspace=ws, sorted_stream=True)
+        else:
+            ss.encoder(pg, pw, layers, kinds, x, (perm_g, routed_g), (perm_w, routed_w), workspace=ws)
 
     ms = time_region(one_pass, passes, 1)
     tokens = base.batch * base.grid * base.grid
@@ -226,6 +239,7 @@ def encoder_run(key, dev, density=None, passes=3, rel_pos=False):
     return {"batch": base.batch, "blocks": base.layers, "global_blocks": sorted(gl),
             "attn_density": base.attn_density, "mlp_density": base.mlp_density,
             "ms_per_pass": round(ms, 3), "tokens_per_s": round(tokens / (ms * 1e-3), 1), "rel_pos": rel_pos,
+            "sorted_stream": sorted_stream,
             "weights": "one random-init layer reused by every layer (timing only)"}
 
 
@@ -522,9 +536,16 @@ def main():
         enc = {}
         for key in ("c4", "c5"):
             enc[key] = {"sparse": encoder_run(key, dev), "density_1.0": encoder_run(key, dev, density=1.0),
-                        "sparse_rel_pos": encoder_run(key, dev, rel_pos=True)}
+                        "sparse_rel_pos": encoder_run(key, dev, rel_pos=True),
+                        "sparse_sorted_stream": encoder_run(key, dev, sorted_stream=True)}
+            if key == "c5":  # the ViT-H sweep's middle point
+                enc[key]["density_0.4"] = encoder_run(key, dev, density=0.4)
+                enc[key]["speedup_0.4_vs_density_1"] = round(enc[key]["density_1.0"]["ms_per_pass"] /
+                                                             enc[key]["density_0.4"]["ms_per_pass"], 3)
             enc[key]["speedup_vs_density_1"] = round(enc[key]["density_1.0"]["ms_per_pass"] /
                                                      enc[key]["sparse"]["ms_per_pass"], 3)
+            enc[key]["sorted_stream_vs_raster"] = round(enc[key]["sparse"]["ms_per_pass"] /
+                                                        enc[key]["sparse_sorted_stream"]["ms_per_pass"], 3)
             _log("encoder", key, enc[key])
             torch.cuda.empty_cache()
         extra["encoders"] = enc

@@ -395,6 +395,31 @@ sparsesam_status sparsesam_block_noalloc(sparsesam_plan_t plan, const sparsesam_
                                          float* x, int32_t batch, const int32_t* perm, const int32_t* routed,
                                          void* stream);
 
+/*
+ * (6b) The encoder (6) with the residual stream kept in stripe-sorted order ("Technische
+ * Samenvatting: SparseSAM", Methodologie, closing paragraph of part 2: one precomputed
+ * permutation set reused by every layer; Probleemstelling, token-merging bullet: per-layer
+ * scatter-gather passes are the overhead to avoid). The stream is gathered once into the
+ * order of the first block's type; consecutive blocks of that type read and write their
+ * rows in place (no gather through perm, no scatter back; pads and keep-set positions follow
+ * from the plan alone); a change of block type moves the stream by one composed gather
+ * (window order -> global order or back); after the last block it returns to raster order
+ * in x. The arithmetic of every block is that of (6), so the result equals (6) bit for bit.
+ *   perm_* / inv_*: sparsesam_permute's perm and inv of each block type used (the keep-set
+ *   is not passed: in stripe-sorted order it is the plan's first K ranks of each segment).
+ *   workspace >= sparsesam_encoder_permuted_workspace(global_plan, window_plan, batch): two
+ *   stream buffers plus the largest block workspace.
+ * Plans with routing = UPDATE or mlp_merge = 1 are not taken (UNSUPPORTED). Validation as in (6).
+ */
+sparsesam_status sparsesam_encoder_permuted_workspace(sparsesam_plan_t global_plan, sparsesam_plan_t window_plan,
+                                                      int32_t batch, size_t* bytes /* host */);
+sparsesam_status sparsesam_encoder_permuted(sparsesam_plan_t global_plan, sparsesam_plan_t window_plan,
+                                            const sparsesam_block_weights* layers /* host */,
+                                            const uint8_t* kinds /* host */, int32_t n_layers, float* x,
+                                            int32_t batch, const int32_t* perm_global, const int32_t* inv_global,
+                                            const int32_t* perm_window, const int32_t* inv_window, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

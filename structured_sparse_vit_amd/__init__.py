@@ -359,12 +359,15 @@ def noalloc_scratch_bytes():
     return int(_lib.load().sparsesam_noalloc_scratch_bytes())
 
 
-def encoder(global_plan, window_plan, layers, kinds, x, global_perm=None, window_perm=None, workspace=None):
+def encoder(global_plan, window_plan, layers, kinds, x, global_perm=None, window_perm=None, workspace=None,
+            sorted_stream=False):
     """A stack of blocks in place on x [batch, grid_h, grid_w, C] fp32.
 
     layers: list of weight dicts (weights_to_device); kinds: list of 1 (global block)
     or 0 (windowed block); global_perm / window_perm: (perm, routed) of permute() for
-    the plan of that block type, computed once and reused by every layer of the type.
+    the plan of that block type, computed once and reused by every layer of the type;
+    with sorted_stream=True they are (perm, inv) and the residual stream stays in
+    stripe-sorted order between blocks (sparsesam_encoder_permuted).
     """
     lib = _lib.load()
     n = len(layers)
@@ -391,11 +394,14 @@ def encoder(global_plan, window_plan, layers, kinds, x, global_perm=None, window
         if plan is None or pr is None:
             ptrs[name] = (ctypes.c_void_p(0), ctypes.c_void_p(0))
             continue
-        perm, routed = pr
+        perm, second = pr
         n_seq, segs, rpi = plan.info["seq_len"], plan.info["segments_per_image"], plan.info["routed_per_image"]
         _need(perm, name + "_perm", torch.int32, (b * segs, n_seq), plan.device)
-        _need(routed, name + "_routed", torch.int32, (b * rpi,), plan.device)
-        ptrs[name] = (_ptr(perm), _ptr(routed))
+        if sorted_stream:
+            _need(second, name + "_inv", torch.int32, (b * segs, n_seq), plan.device)
+        else:
+            _need(second, name + "_routed", torch.int32, (b * rpi,), plan.device)
+        ptrs[name] = (_ptr(perm), _ptr(second))
     dt, C, Hm = ref.torch_dtype, ref.desc.channels, ref.desc.mlp_hidden
     shapes = {"ln1_g": (C,), "ln1_b": (C,), "w_qkv": (3 * C, C), "b_qkv": (3 * C,), "w_proj": (C, C),
               "b_proj": (C,), "ln2_g": (C,), "ln2_b": (C,), "w1": (Hm, C), "b1": (Hm,), "w2": (C, Hm), "b2": (C,)}
@@ -406,6 +412,17 @@ def encoder(global_plan, window_plan, layers, kinds, x, global_perm=None, window
                   ref.device)
         arr[l] = _block_weights(global_plan if int(kinds[l]) else window_plan, w, "layer %d " % l)
     kind_arr = (ctypes.c_uint8 * max(1, n))(*[int(k) for k in kinds])
+    gh_ = global_plan.handle if global_plan is not None else None
+    wh_ = window_plan.handle if window_plan is not None else None
+    if sorted_stream:
+        need = ctypes.c_size_t()
+        check(lib.sparsesam_encoder_permuted_workspace(gh_, wh_, b, ctypes.byref(need)),
+              "sparsesam_encoder_permuted_workspace")
+        ws = _workspace(need.value, x.device, workspace)
+        check(lib.sparsesam_encoder_permuted(gh_, wh_, arr, kind_arr, n, _ptr(x), b, ptrs["global"][0],
+                                             ptrs["global"][1], ptrs["window"][0], ptrs["window"][1], _ptr(ws),
+                                             ws.numel(), _stream(x.device)), "sparsesam_encoder_permuted")
+        return x
     need = max(p.info["block_workspace_bytes"] for p in plans)
     ws = _workspace(need, x.device, workspace)
     check(lib.sparsesam_encoder(global_plan.handle if global_plan is not None else None,

@@ -39,6 +39,8 @@ EXPORTS = [
     "sparsesam_block_noalloc",
     "sparsesam_route_topk",
     "sparsesam_block_dynamic",
+    "sparsesam_encoder_permuted_workspace",
+    "sparsesam_encoder_permuted",
 ]
 
 
@@ -107,6 +109,9 @@ def load():
         "sparsesam_block_noalloc": ([P, ctypes.POINTER(BlockWeights), P, I32, P, P, P], I32),
         "sparsesam_route_topk": ([P, P, I32, P, P], I32),
         "sparsesam_block_dynamic": ([P, ctypes.POINTER(BlockWeights), P, I32, P, P, P, P, SZ, P], I32),
+        "sparsesam_encoder_permuted_workspace": ([P, P, I32, ctypes.POINTER(SZ)], I32),
+        "sparsesam_encoder_permuted": ([P, P, ctypes.POINTER(BlockWeights), P, I32, P, I32, P, P, P, P, P, SZ, P],
+                                       I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

@@ -350,6 +350,13 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     p->seg_off[w] = p->routed_per_image;
     p->routed_per_image += k;
   }
+  // keep-set positions of a stream kept in stripe-sorted order (max_batch images)
+  p->keep_pos.clear();
+  p->keep_pos.reserve((size_t)d.max_batch * p->routed_per_image);
+  for (int img = 0; img < d.max_batch; ++img)
+    for (int w = 0; w < p->segs_per_img; ++w)
+      for (int rho = 0; rho < p->seg_k[w]; ++rho)
+        p->keep_pos.push_back((img * p->segs_per_img + w) * p->n + (rho % d.stripes) * p->s + rho / d.stripes);
   if (permute_lds_bytes(*p) > 160 * 1024) {
     delete p;
     return unsupported("a segment's keys or an image's token flags do not fit the permutation kernels' 160 KiB of LDS");
@@ -373,7 +380,8 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     };
     size_t o_rp = put(p->row_ptr), o_ci = put(p->col_idx), o_ts = put(p->tile_start), o_tl = put(p->tile_len),
            o_or = put(p->order), o_sk = put(p->seg_k), o_so = put(p->seg_off), o_it = put(p->items),
-           o_sp = put(p->splits), o_pt = put(p->pos_tile), o_k32 = put(p->keep32), o_a32 = put(p->any32);
+           o_sp = put(p->splits), o_pt = put(p->pos_tile), o_k32 = put(p->keep32), o_a32 = put(p->any32),
+           o_kp = put(p->keep_pos);
     blob.push_back(0);
     void* dptr = nullptr;
     hipError_t e = hipMalloc(&dptr, blob.size() * sizeof(int));
@@ -403,6 +411,7 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     p->d_pos_tile = b + o_pt;
     p->d_keep32 = b + o_k32;
     p->d_any32 = b + o_a32;
+    p->d_keep_pos = b + o_kp;
     p->attn_resident_wgs = attn_long_supported(*p) ? attn_long_resident_wgs(dev, p->desc.head_dim) : 0;
     (void)hipGetLastError();
   } else {
@@ -597,9 +606,13 @@ sparsesam_status sparsesam_mlp(sparsesam_plan_t p, float* x, int64_t rows, const
 
 // One block. routed: the keep-set (input) or, for dynamic plans, where the block writes
 // the keep-set it selects (score_out optional).
+// stream_sorted: x is the residual stream in this plan's stripe-sorted order ([segments *
+// N, C], pads included) instead of raster order; the block then reads and writes its
+// rows in place and its keep-set is the plan's static list of keep-set positions.
 template <typename T>
 static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weights& w, float* x, int batch,
-                            const int32_t* perm, int32_t* routed, float* score_out, char* ws, hipStream_t st) {
+                            const int32_t* perm, int32_t* routed, float* score_out, char* ws, hipStream_t st,
+                            bool stream_sorted = false) {
   BlockLayout L = block_layout(p, batch);
   const int segs = batch * p.segs_per_img;
   const int M = segs * p.n;
@@ -609,8 +622,10 @@ static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weigh
   T* k = reinterpret_cast<T*>(ws + L.k);
   T* vt = reinterpret_cast<T*>(ws + L.vt);
   T* o = reinterpret_cast<T*>(ws + L.o);
-  const long long x_rows = (long long)batch * p.desc.grid_h * p.desc.grid_w;
-  hipError_t e = launch_gather_ln<T>(p, x, (int)x_rows, M, perm, nullptr, w.ln1_g, w.ln1_b, h, st);
+  const long long x_rows = stream_sorted ? (long long)M : (long long)batch * p.desc.grid_h * p.desc.grid_w;
+  const int32_t* row_perm = stream_sorted ? nullptr : perm;  // null: rows in place
+  if (stream_sorted) routed = const_cast<int32_t*>(p.d_keep_pos);
+  hipError_t e = launch_gather_ln<T>(p, x, (int)x_rows, M, row_perm, nullptr, w.ln1_g, w.ln1_b, h, st);
   if (e != hipSuccess) return e;
   EpiQKV eq{w.b_qkv, q, k, vt, p.n, p.n_pad, p.desc.heads, p.desc.head_dim, C};
   e = launch_gemm_qkv<T>(h, (const T*)w.w_qkv, M, C, eq, st);
@@ -623,7 +638,7 @@ static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weigh
     e = launch_attention<T>(p, segs, q, k, vt, o, scale, ws + L.part, st);
   if (e != hipSuccess) return e;
   const bool dynamic = p.desc.routing == SPARSESAM_ROUTE_UPDATE;
-  EpiResidualScatter er{w.b_proj, x, perm, nullptr, p.segmap(), C, x_rows};
+  EpiResidualScatter er{w.b_proj, x, row_perm, nullptr, p.segmap(), C, x_rows};
   if (dynamic) {  // the projection epilogue also sums each token's squared update
     er.sq_part = reinterpret_cast<float*>(ws + L.sq);
     er.sq_ld = L.sq_ld;
@@ -789,13 +804,13 @@ sparsesam_status sparsesam_block_noalloc(sparsesam_plan_t p, const sparsesam_blo
   return block_impl(p, w, x, batch, perm, const_cast<int32_t*>(routed), nullptr, ws, kNoAllocScratchBytes, stream);
 }
 
-sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_t window_plan,
-                                   const sparsesam_block_weights* layers, const uint8_t* kinds, int32_t n_layers,
-                                   float* x, int32_t batch, const int32_t* perm_global, const int32_t* routed_global,
-                                   const int32_t* perm_window, const int32_t* routed_window, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
-  if (n_layers < 0) return invalid("n_layers must be >= 0");
-  if (n_layers == 0) return SPARSESAM_OK;
+}  // extern "C"
+
+// Checks shared by both encoder entry points: layer kinds, plans present and of one
+// shape, no dynamic-routing plan.
+static sparsesam_status encoder_plans_check(sparsesam_plan_t global_plan, sparsesam_plan_t window_plan,
+                                            const sparsesam_block_weights* layers, const uint8_t* kinds,
+                                            int32_t n_layers) {
   if (!layers || !kinds) return invalid("layers and kinds must not be null");
   bool any_global = false, any_window = false;
   for (int l = 0; l < n_layers; ++l) {
@@ -809,7 +824,7 @@ sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_
   if (any_window && !window_plan) return invalid("a windowed layer needs window_plan");
   for (sparsesam_plan_t pl : {global_plan, window_plan})
     if (pl && pl->desc.routing == SPARSESAM_ROUTE_UPDATE)
-      return unsupported("sparsesam_encoder does not take plans with routing = UPDATE; run their blocks through "
+      return unsupported("the encoders do not take plans with routing = UPDATE; run their blocks through "
                          "sparsesam_block_dynamic");
   if (any_global && any_window) {
     const sparsesam_plan_desc &g = global_plan->desc, &w = window_plan->desc;
@@ -819,6 +834,20 @@ sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_
       return invalid("global_plan and window_plan must share grid, channels, heads, head_dim, mlp_hidden, dtype "
                      "and device");
   }
+  return SPARSESAM_OK;
+}
+
+extern "C" {
+
+sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_t window_plan,
+                                   const sparsesam_block_weights* layers, const uint8_t* kinds, int32_t n_layers,
+                                   float* x, int32_t batch, const int32_t* perm_global, const int32_t* routed_global,
+                                   const int32_t* perm_window, const int32_t* routed_window, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (n_layers < 0) return invalid("n_layers must be >= 0");
+  if (n_layers == 0) return SPARSESAM_OK;
+  sparsesam_status pst = encoder_plans_check(global_plan, window_plan, layers, kinds, n_layers);
+  if (pst != SPARSESAM_OK) return pst;
   // every layer is validated before the first launch: no partial run on bad input
   for (int l = 0; l < n_layers; ++l) {
     sparsesam_status st = block_check(kinds[l] ? global_plan : window_plan, &layers[l], x, batch,
@@ -834,6 +863,130 @@ sparsesam_status sparsesam_encoder(sparsesam_plan_t global_plan, sparsesam_plan_
     if (st != SPARSESAM_OK) return st;
   }
   return SPARSESAM_OK;
+}
+
+}  // extern "C"
+
+// Workspace of sparsesam_encoder_permuted: two stream buffers (rows of the larger layout)
+// then the largest block workspace of the plans used.
+struct PermutedEncoderLayout {
+  size_t stream_bytes = 0, a = 0, b = 0, block = 0, total = 0;
+};
+static PermutedEncoderLayout permuted_encoder_layout(sparsesam_plan_t gp, sparsesam_plan_t wp, int batch) {
+  PermutedEncoderLayout E;
+  size_t rows = 0, block = 0;
+  for (sparsesam_plan_t pl : {gp, wp}) {
+    if (!pl) continue;
+    rows = std::max(rows, (size_t)batch * pl->segs_per_img * pl->n);
+    rows = std::max(rows, (size_t)batch * pl->desc.grid_h * pl->desc.grid_w);
+    block = std::max(block, block_layout(*pl, batch).total());
+  }
+  const size_t C = gp ? gp->desc.channels : (wp ? wp->desc.channels : 0);
+  E.stream_bytes = align256(rows * C * sizeof(float));
+  E.a = 0;
+  E.b = E.stream_bytes;
+  E.block = 2 * E.stream_bytes;
+  E.total = E.block + block;
+  return E;
+}
+
+static StreamLayout stream_layout(const sparsesam_plan* pl, const int32_t* perm, const int32_t* inv) {
+  StreamLayout L;
+  L.map = pl->segmap();
+  L.perm = perm;
+  L.inv = inv;
+  return L;
+}
+
+extern "C" {
+
+sparsesam_status sparsesam_encoder_permuted_workspace(sparsesam_plan_t global_plan, sparsesam_plan_t window_plan,
+                                                      int32_t batch, size_t* bytes) {
+  if (!bytes) return invalid("bytes must not be null");
+  if (!global_plan && !window_plan) return invalid("at least one plan is needed");
+  if (batch < 0) return invalid("batch must be >= 0");
+  *bytes = permuted_encoder_layout(global_plan, window_plan, batch).total;
+  return SPARSESAM_OK;
+}
+
+sparsesam_status sparsesam_encoder_permuted(sparsesam_plan_t global_plan, sparsesam_plan_t window_plan,
+                                            const sparsesam_block_weights* layers, const uint8_t* kinds,
+                                            int32_t n_layers, float* x, int32_t batch, const int32_t* perm_global,
+                                            const int32_t* inv_global, const int32_t* perm_window,
+                                            const int32_t* inv_window, void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  if (n_layers < 0) return invalid("n_layers must be >= 0");
+  if (n_layers == 0) return SPARSESAM_OK;
+  sparsesam_status st = encoder_plans_check(global_plan, window_plan, layers, kinds, n_layers);
+  if (st != SPARSESAM_OK) return st;
+  for (sparsesam_plan_t pl : {global_plan, window_plan})
+    if (pl && pl->desc.mlp_merge)
+      return unsupported("sparsesam_encoder_permuted does not take mlp_merge plans");
+  if (batch < 0) return invalid("batch must be >= 0");
+  if (batch == 0) return SPARSESAM_OK;
+  const PermutedEncoderLayout E = permuted_encoder_layout(global_plan, window_plan, batch);
+  if (!workspace || workspace_bytes < E.total) {
+    set_error("sparsesam_encoder_permuted needs " + std::to_string(E.total) + " bytes of workspace");
+    return SPARSESAM_ERR_WORKSPACE;
+  }
+  bool any_global = false, any_window = false;
+  for (int l = 0; l < n_layers; ++l) (kinds[l] ? any_global : any_window) = true;
+  if ((any_global && (!perm_global || !inv_global)) || (any_window && (!perm_window || !inv_window)))
+    return invalid("each block type used needs its perm and inv");
+  const sparsesam_plan* ref0 = global_plan ? global_plan : window_plan;
+  if (ref0->desc.channels % 4) return unsupported("channels must be a multiple of 4");
+  if (!x) return invalid("x must not be null");
+  char* ws = static_cast<char*>(workspace);
+  char* blk = ws + E.block;
+  const size_t blk_bytes = workspace_bytes - E.block;
+  // every layer validated before the first launch (the block workspace and the in-place
+  // stream; the keep-set comes from the plan)
+  for (int l = 0; l < n_layers; ++l) {
+    sparsesam_plan_t pl = kinds[l] ? global_plan : window_plan;
+    st = block_check(pl, &layers[l], x, batch, kinds[l] ? perm_global : perm_window, pl->d_keep_pos, blk,
+                     blk_bytes);
+    if (st != SPARSESAM_OK) return st;
+  }
+  const sparsesam_plan* ref = global_plan ? global_plan : window_plan;
+  const int C = ref->desc.channels;
+  const int raster_rows = batch * ref->desc.grid_h * ref->desc.grid_w;
+  hipStream_t hs = (hipStream_t)stream;
+  StreamLayout raster;
+  raster.map = ref->segmap();
+  float* bufs[2] = {reinterpret_cast<float*>(ws + E.a), reinterpret_cast<float*>(ws + E.b)};
+  int cur = -1;   // block kind the stream is ordered for (-1: not yet gathered)
+  int which = 0;  // buffer holding the stream
+  hipError_t e = hipSuccess;
+  for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
+    const int kind = kinds[l];
+    sparsesam_plan_t pl = kind ? global_plan : window_plan;
+    const int32_t* perm = kind ? perm_global : perm_window;
+    const int32_t* inv = kind ? inv_global : inv_window;
+    if (kind != cur) {  // one composed gather into the new block type's order
+      const StreamLayout to = stream_layout(pl, perm, inv);
+      const int rows = batch * pl->segs_per_img * pl->n;
+      if (cur < 0) {
+        e = launch_reorder(bufs[which], x, rows, C, to, raster, hs);
+      } else {
+        sparsesam_plan_t prev = cur ? global_plan : window_plan;
+        const StreamLayout from = stream_layout(prev, cur ? perm_global : perm_window, cur ? inv_global : inv_window);
+        e = launch_reorder(bufs[1 - which], bufs[which], rows, C, to, from, hs);
+        which = 1 - which;
+      }
+      cur = kind;
+      if (e != hipSuccess) break;
+    }
+    if (pl->desc.dtype == SPARSESAM_BF16)
+      e = run_block<bf16_t>(*pl, layers[l], bufs[which], batch, perm, nullptr, nullptr, blk, hs, true);
+    else
+      e = run_block<float>(*pl, layers[l], bufs[which], batch, perm, nullptr, nullptr, blk, hs, true);
+  }
+  if (e == hipSuccess) {  // back to raster order
+    sparsesam_plan_t prev = cur ? global_plan : window_plan;
+    const StreamLayout from = stream_layout(prev, cur ? perm_global : perm_window, cur ? inv_global : inv_window);
+    e = launch_reorder(x, bufs[which], raster_rows, C, raster, from, hs);
+  }
+  return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_encoder_permuted launch");
 }
 
 }  // extern "C"

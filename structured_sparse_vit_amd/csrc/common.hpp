@@ -112,6 +112,21 @@ struct FastDiv {
 struct SegmentMap {
   int grid_h, grid_w, window, nwx, segs_per_img, n;
   FastDiv f_spi, f_nwx, f_win, f_n;  // by segs_per_img, nwx, window (or 1), n
+  int stripes, s;                    // g and the stripe length S = n / g
+  FastDiv f_s;                       // by S
+
+  // Row r of a stream kept in stripe-sorted order holds a window pad iff the rank it
+  // holds, (p % S) * g + p / S, is at least the window's real-token count: pads sort
+  // after every real slot, so this needs no permutation load. Global segments have no pads.
+  __device__ __forceinline__ bool pad_position(int r) const {
+    if (window == 0) return false;
+    const int seg = seg_of(r), p = r - seg * n;
+    const int w = seg - f_spi.div(seg) * segs_per_img;
+    const int wy = f_nwx.div(w), wx = w - wy * nwx;
+    const int ry = min(window, grid_h - wy * window), rx = min(window, grid_w - wx * window);
+    const int a = f_s.div(p), u = p - a * s;
+    return u * stripes + a >= ry * rx;
+  }
 
   // segment of a stripe-sorted segment row r (rows are segment-major, n per segment)
   __device__ __forceinline__ int seg_of(int r) const { return f_n.div(r); }

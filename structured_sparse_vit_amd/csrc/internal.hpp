@@ -70,6 +70,11 @@ struct sparsesam_plan {
   const int* d_pos_tile = nullptr;
   const int* d_keep32 = nullptr;
   const int* d_any32 = nullptr;
+  // keep-set of a stream kept in stripe-sorted order: the positions of ranks 0 .. K - 1
+  // of every segment, (seg * n) + (rank % g) * S + rank / g, for max_batch images in
+  // the keep-set layout (static: the keep-set is the first K ranks)
+  std::vector<int> keep_pos;
+  const int* d_keep_pos = nullptr;
 
   sparsesam::SegmentMap segmap() const {
     sparsesam::SegmentMap m;
@@ -83,6 +88,9 @@ struct sparsesam_plan {
     m.f_nwx = sparsesam::FastDiv((uint32_t)nwx);
     m.f_win = sparsesam::FastDiv((uint32_t)(desc.window > 0 ? desc.window : 1));
     m.f_n = sparsesam::FastDiv((uint32_t)n);
+    m.stripes = desc.stripes;
+    m.s = s;
+    m.f_s = sparsesam::FastDiv((uint32_t)s);
     return m;
   }
 };
@@ -123,6 +131,17 @@ hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, 
 // receives each token's summed score.
 hipError_t launch_route_topk(const sparsesam_plan& p, const float* score, int parts, int batch, int* routed,
                              float* score_out, hipStream_t st);
+// Row order of a residual stream: raster image rows (perm null), or the stripe-sorted
+// segment rows of a plan (its segment map, perm and inv for the batch).
+struct StreamLayout {
+  SegmentMap map;
+  const int* perm = nullptr;
+  const int* inv = nullptr;
+};
+// dst[r] = src[row of the same token in `from`] for the rows of layout `to` (C % 4 == 0);
+// window pad rows of `to` become zero rows.
+hipError_t launch_reorder(float* dst, const float* src, int rows, int C, const StreamLayout& to,
+                          const StreamLayout& from, hipStream_t st);
 // The merge of mlp_merge plans: every real token of a segment outside its keep-set gets
 // the mean of the keep-set's updates upd [batch * routed_per_image, C] (rows in the
 // keep-set's layout).
@@ -130,7 +149,8 @@ hipError_t launch_merge(const sparsesam_plan& p, float* x, int batch, const int*
                         hipStream_t st);
 
 // LayerNorm of gathered rows: out[r] = LN(x[src(r)]) for r < rows_out, zero rows for pads.
-// Row source: mode 0 = stripe-sorted segment rows through perm, mode 1 = explicit list.
+// Row source: stripe-sorted segment rows through perm; an explicit list; or, with both
+// null, the row itself (x already in stripe-sorted order; pads by map.pad_position).
 template <typename T>
 hipError_t launch_gather_ln(const sparsesam_plan& p, const float* x, int x_rows, int rows_out, const int* perm,
                             const int* list, const float* g, const float* b, T* out, hipStream_t st);
@@ -151,6 +171,8 @@ struct EpiResidualScatter {  // x[map(r)] += acc + bias
   SegmentMap map;
   int ldx;
   long long x_rows;  // rows of x; destination rows outside [0, x_rows) are skipped
+  // with perm and list both null the destination is the row itself (a stream kept in
+  // stripe-sorted order)
   // optional: squared-update partial sums, sq_part[dst row * sq_ld + column / 32] = the sum of
   // (acc + bias)^2 over a block of 32 or 64 columns starting at that column (a 64-column
   // block writes 0 into its second slot); sq_ld = ceil(N / 32)

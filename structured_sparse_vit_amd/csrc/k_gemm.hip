@@ -228,6 +228,7 @@ struct ResidualAdd {
   static constexpr bool kRowSq = true;
   __device__ __forceinline__ int dst_row(int r) const {
     if (list) return list[r];
+    if (!perm) return r;  // stream in stripe-sorted order
     return map.row_of(map.seg_of(r), perm[r]);
   }
   __device__ __forceinline__ void elem(int r, int c, float v) const {
@@ -277,12 +278,12 @@ struct ResidualAdd {
                                        int N) const {
     int raw[MR];
 #pragma unroll
-    for (int i = 0; i < MR; ++i) raw[i] = r[i] < M ? (list ? list[r[i]] : perm[r[i]]) : -1;
+    for (int i = 0; i < MR; ++i) raw[i] = r[i] < M ? (list ? list[r[i]] : perm ? perm[r[i]] : r[i]) : -1;
     long long off[MR];
 #pragma unroll
     for (int i = 0; i < MR; ++i) {
       int row = -1;
-      if (raw[i] >= 0) row = list ? raw[i] : map.row_of(map.seg_of(r[i]), raw[i]);
+      if (raw[i] >= 0) row = (list || !perm) ? raw[i] : map.row_of(map.seg_of(r[i]), raw[i]);
       off[i] = (row < 0 || row >= x_rows) ? -1 : (long long)row * ldx;
     }
 #pragma unroll

@@ -22,9 +22,11 @@ __global__ void __launch_bounds__(256) gather_ln_kernel(const float* __restrict_
   int src;
   if (list) {
     src = list[r];
-  } else {
+  } else if (perm) {
     int seg = map.seg_of(r), slot = perm[r];
     src = map.row_of(seg, slot);
+  } else {
+    src = map.pad_position(r) ? -1 : r;
   }
   T* o = out + (size_t)r * C;
   if (src < 0 || src >= x_rows) {
@@ -71,9 +73,11 @@ __global__ void __launch_bounds__(256) gather_ln_vec_kernel(const float* __restr
   int src;
   if (list) {
     src = list[r];
-  } else {
+  } else if (perm) {
     const int seg = map.seg_of(r), slot = perm[r];
     src = map.row_of(seg, slot);
+  } else {
+    src = map.pad_position(r) ? -1 : r;
   }
   bf16_t* o = out + (size_t)r * C;
   if (src < 0 || src >= x_rows) {

@@ -457,3 +457,59 @@ def test_encoder_full_size_matches_block_by_block():
     got, ref = x_enc.cpu().numpy(), x_seq.cpu().numpy()
     assert np.isfinite(got).all()
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def _encoder_pair(key, over, layers, b, rel_pos=False, full_weights=False):
+    """The same encoder run with the raster-order stream (sparsesam_encoder) and with the
+    stream kept in stripe-sorted order (sparsesam_encoder_permuted)."""
+    from synth import block_weights, encoder_global_layers, token_features
+    from synth.configs import global_variant, window_variant
+    from synth.generate import rel_pos_tables
+    base = config(key).with_(batch=b, layers=layers, **over)
+    cg, cw = global_variant(base).with_(batch=b), window_variant(base).with_(batch=b)
+    pg, pw = ss.Plan.from_config(cg, rel_pos=rel_pos), ss.Plan.from_config(cw, rel_pos=rel_pos)
+    gl = encoder_global_layers(layers)
+    kinds = [1 if l in gl else 0 for l in range(layers)]
+    ws = [block_weights(base, 0, layer=0 if full_weights else l) for l in range(layers)]
+    wd = []
+    for l, w in enumerate(ws):
+        if rel_pos:
+            w = dict(w)
+            w["rel_h"], w["rel_w"] = rel_pos_tables(cg if kinds[l] else cw, 0, layer=l)
+        wd.append(ss.weights_to_device(w, pg))
+    imp_d = ss.importance(torch.from_numpy(images(key)[:b].copy()).to(DEV), base.patch)
+    perm_g, inv_g, routed_g = ss.permute(pg, imp_d)
+    perm_w, inv_w, routed_w = ss.permute(pw, imp_d)
+    x0 = token_features(base, 0)
+    xa = torch.from_numpy(x0.copy()).to(DEV)
+    ss.encoder(pg, pw, wd, kinds, xa, (perm_g, routed_g), (perm_w, routed_w))
+    xb = torch.from_numpy(x0.copy()).to(DEV)
+    ss.encoder(pg, pw, wd, kinds, xb, (perm_g, inv_g), (perm_w, inv_w), sorted_stream=True)
+    torch.cuda.synchronize()
+    return xa.cpu().numpy(), xb.cpu().numpy(), x0, imp_d.cpu().numpy(), ws, gl, cg, cw
+
+
+@pytest.mark.parametrize("key,over,layers,b,rel_pos", [
+    ("c4", dict(channels=256, heads=4, mlp_hidden=512), 8, 2, False),     # ViT-L layout
+    ("c5", dict(channels=640, heads=8, mlp_hidden=1280), 8, 1, False),    # ViT-H layout, head_dim 80
+    ("ragged", dict(), 8, 2, False),                                      # 18 x 18 grid: padded windows
+    ("c4", dict(channels=256, heads=4, mlp_hidden=512), 8, 1, True),      # with the relative-position bias
+])
+def test_encoder_sorted_stream_equals_raster_stream(key, over, layers, b, rel_pos):
+    """The residual stream kept in stripe-sorted order between blocks (one composed gather
+    at each change of block type) gives the raster-order encoder's result bit for bit."""
+    _say("encoder sorted stream", key, over, "rel_pos", rel_pos)
+    a, s, x0, imp, ws, gl, cg, cw = _encoder_pair(key, over, layers, b, rel_pos)
+    assert np.isfinite(s).all()
+    assert np.array_equal(a.view(np.uint32), s.view(np.uint32))
+    if not rel_pos and key == "ragged":
+        mx, rel = check_close(s, oracle.encoder_forward(x0, imp, ws, gl, cg, cw), what="sorted-stream encoder")
+        _say("  against the oracle: max-abs %.3e rel-L2 %.3e" % (mx, rel))
+
+
+def test_encoder_sorted_stream_full_size():
+    """The ViT-L encoder at full size (24 blocks, batch 8), one layer's weights reused."""
+    _say("encoder sorted stream full size c4")
+    a, s = _encoder_pair("c4", {}, 24, 8, full_weights=True)[:2]
+    assert np.isfinite(s).all()
+    assert np.array_equal(a.view(np.uint32), s.view(np.uint32))

@@ -323,3 +323,25 @@ def test_routing_entry_points_check_the_plan_kind_first():
     karr = (ctypes.c_uint8 * 1)(1)
     assert lib.sparsesam_encoder(dyn.handle, None, layers, karr, 1, p, 1, p, p, p, p, p, 1 << 30, None) == 2
     assert lib.sparsesam_route_topk(None, p, 1, p, None) == 1
+
+
+def test_sorted_stream_encoder_workspace_and_checks():
+    lib = _lib.load()
+    g = _create()
+    w_cfg = get_config("c3").with_(channels=g.desc.channels, heads=g.desc.heads, head_dim=g.desc.head_dim,
+                                   mlp_hidden=g.desc.mlp_hidden)
+    w = ss.Plan.from_config(w_cfg)
+    need = ctypes.c_size_t()
+    assert lib.sparsesam_encoder_permuted_workspace(g.handle, w.handle, 4, ctypes.byref(need)) == 0
+    # two stream buffers of the windowed order (100 windows x 196 rows, larger than raster) + a block workspace
+    assert need.value >= 2 * 4 * 25 * 196 * 768 * 4 + w.info["block_workspace_bytes"] * 4 // 4
+    assert lib.sparsesam_encoder_permuted_workspace(None, None, 1, ctypes.byref(need)) == 1
+    layers = (_lib.BlockWeights * 2)()
+    karr = (ctypes.c_uint8 * 2)(1, 0)
+    p = ctypes.c_void_p(16)
+    assert lib.sparsesam_encoder_permuted(g.handle, w.handle, layers, karr, 0, p, 1, p, p, p, p, p, 1, None) == 0
+    assert lib.sparsesam_encoder_permuted(None, w.handle, layers, karr, 2, p, 1, p, p, p, p, p, 1 << 40,
+                                          None) == 1
+    m = _create(mlp_merge=True)
+    assert lib.sparsesam_encoder_permuted(m.handle, None, layers, (ctypes.c_uint8 * 2)(1, 1), 2, p, 1, p, p, p, p, p,
+                                          1 << 40, None) == 2
