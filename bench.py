@@ -256,47 +256,102 @@ def window_block_run(dev):
             "tokens_per_s": round(tokens / (step * 1e-3), 1)}
 
 
-def cpu_baseline(cfg, budget_s=25.0):
-    """The oracle, as it stands, on a bounded sample of the same workload on this host."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_step_s(cfg, threads, budget_s, max_runs=3):
+    """Seconds per oracle step (importance + permutation + one block) with `threads` BLAS
+    threads (None: the library's default, all cores); (seconds, runs)."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
     from synth import block_weights, synthetic_images, token_features
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
     imgs = synthetic_images(cfg)
     x = token_features(cfg)
     w = block_weights(cfg)
     done, t0 = 0, time.perf_counter()
-    while True:
-        imp = np.stack([oracle.importance(im, cfg.patch) for im in imgs])
-        oracle.block_forward(x, imp, w, cfg)
-        done += 1
-        if time.perf_counter() - t0 > budget_s / 2 or done >= 3:
-            break
-    dt = (time.perf_counter() - t0) / done
+    with threadpool_limits(threads):
+        while True:
+            imp = np.stack([oracle.importance(im, cfg.patch) for im in imgs])
+            oracle.block_forward(x, imp, w, cfg)
+            done += 1
+            if time.perf_counter() - t0 > budget_s or done >= max_runs:
+                break
+    return (time.perf_counter() - t0) / done, done
+
+
+def cpu_baseline(cfg, budget_s=8.0):
+    """The oracle, as it stands, on a bounded sample of the same workload on this host:
+    the headline figure (all cores) plus the c1 block, one c2 block and one image's c3
+    windowed block (25 windows), each at 1 thread and at all threads."""
+    from threadpoolctl import threadpool_info
+
+    from synth import get_config
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    dt, done = _oracle_step_s(cfg, None, budget_s)
     tokens = cfg.batch * cfg.grid * cfg.grid
+    by_cfg = {}
+    for key, over in (("c1", {}), ("c2", {}), ("c3", {"batch": 1})):
+        c = get_config(key).with_(**over)
+        tk = c.batch * c.grid * c.grid
+        row = {"batch": c.batch, "tokens": tk}
+        for th, label in ((1, "1_thread"), (None, "all_threads")):
+            if key == cfg_key(cfg) and th is None:
+                s, n = dt, done
+            else:
+                s, n = _oracle_step_s(c, th, budget_s / 2, max_runs=3 if key != "c1" else 20)
+            row[label] = {"s_per_step": round(s, 4), "tokens_per_s": round(tk / s, 1), "runs": n}
+        by_cfg[key] = row
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": "%d full step(s) of the same workload (importance + permutation + one block, dense "
-                      "attention with an explicit mask, fp64 numpy), %.2f s each" % (done, dt)}
+                      "attention with an explicit mask, fp64 numpy), %.2f s each" % (done, dt),
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+            "by_config": by_cfg,
+            "note": "the oracle computes every one of the N^2 attention scores (explicit mask) and the MLP on the "
+                    "keep-set rows only; c3 is one image of 25 windows; c4 / c5 are not timed end to end"}
 
 
+def cfg_key(cfg):
+    """The config table key of a workload (c1 .. c5), or '' for derived ones."""
+    from synth.configs import CONFIGS
+    for k, v in CONFIGS.items():
+        if v == cfg:
+            return k
+    return ""
+
+
+def _prof(out, counters, cfg="c2", extra="", steps=5, warmup=2):
+    mode = "--kernel-trace --stats" if counters is None else "--pmc " + counters
+    return ("rocprofv3 %s --output-format csv -d gpurun_out/%s -o p -- python3 bench.py --profile-only --config %s "
+            "--steps %d --warmup %d%s" % (mode, out, cfg, steps, warmup, extra))
+
+
+# rocprofv3 runs behind the summaries in profiles/ (one counter group per run; run each from
+# the repository root, e.g. under `timeout -s KILL 150`), then
+# `python bench.py --summarize-profiles gpurun_out`.
 PROFILE_COMMANDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -T --output-format csv -d gpurun_out/trace_c2 -o c2 -- "
-             "python3 bench.py --profile-only --steps 20 --warmup 5",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_c2 -o f -- "
-             "python3 bench.py --profile-only --steps 5 --warmup 2",
-    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_c2 -o w -- "
-             "python3 bench.py --profile-only --steps 5 --warmup 2",
-    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_copy -o f -- "
+    "trace": _prof("trace_c2", None, steps=20, warmup=5),
+    "trace_relpos": _prof("trace_relpos", None, extra=" --rel-pos", steps=20, warmup=5),
+    "trace_c3": _prof("trace_c3", None, cfg="c3", steps=20, warmup=5),
+    "mfma": _prof("pmc_mfma_c2", "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16"),
+    "fetch": _prof("pmc_fetch_c2", "FETCH_SIZE"),
+    "write": _prof("pmc_write_c2", "WRITE_SIZE"),
+    "mfma_c3": _prof("pmc_mfma_c3", "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16", cfg="c3"),
+    "fetch_c3": _prof("pmc_fetch_c3", "FETCH_SIZE", cfg="c3"),
+    "write_c3": _prof("pmc_write_c3", "WRITE_SIZE", cfg="c3"),
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_copy -o p -- "
                   "python3 bench.py --copy-calibration",
-    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_copy -o w -- "
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_copy -o p -- "
                   "python3 bench.py --copy-calibration",
-    "trace_relpos": "rocprofv3 --kernel-trace --stats -T --output-format csv -d gpurun_out/trace_relpos -o relpos -- "
-                    "python3 bench.py --profile-only --rel-pos --steps 20 --warmup 5",
 }
 ATTN_KERNELS = ("attn_mfma64_kernel", "attn_combine_kernel")
 COPY_BYTES = 256 << 20
@@ -314,6 +369,41 @@ def _csv_rows(folder, suffix):
     return rows
 
 
+_DEMANGLED = {}
+
+
+def _demangle(name):
+    """Itanium-demangled kernel name (binutils' c++filt, with the bf16 / fp16 builtin types
+    spelled as vendor types it knows); the name itself when that fails."""
+    if not name.startswith("_Z"):
+        return name
+    if name not in _DEMANGLED:
+        import subprocess
+        try:
+            r = subprocess.run(["c++filt"], input=name.replace("DF16b", "u6__bf16").replace("DF16_", "u8_Float16"),
+                               capture_output=True, text=True, timeout=10)
+            _DEMANGLED[name] = r.stdout.strip() or name
+        except (OSError, subprocess.SubprocessError):
+            _DEMANGLED[name] = name
+    return _DEMANGLED[name]
+
+
+def _label(name):
+    """Short kernel label: no return type, namespace or argument list."""
+    import re
+    n = _demangle(name).replace("void ", "").replace("sparsesam::", "")
+    depth, out = 0, []
+    for ch in n:  # cut the argument list (the first '(' at template depth 0)
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            break
+        out.append(ch)
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def _counter_kib(folder, counter, match):
     """Average of `counter` (KiB per dispatch) over the dispatches whose kernel name contains match."""
     vals = [float(r["Counter_Value"]) for r in _csv_rows(folder, "counter_collection.csv")
@@ -323,36 +413,94 @@ def _counter_kib(folder, counter, match):
     return sum(vals) / len(vals), len(vals)
 
 
+def _per_kernel(folder, suffix, value):
+    """{label: [values]} over the dispatches of a CSV (value(row) -> float or None)."""
+    out = {}
+    for r in _csv_rows(folder, suffix):
+        v = value(r)
+        if v is not None:
+            out.setdefault(_label(r["Kernel_Name"]), []).append(v)
+    return out
+
+
+def _avg(v):
+    return sum(v) / len(v)
+
+
+def _write_trace(src, sub, name, what, key):
+    durs = _per_kernel(os.path.join(src, sub), "kernel_trace.csv",
+                       lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in durs.values())
+    lines = ["# Kernel-trace statistics of %s." % what,
+             "# command (from the repository root):",
+             "#   " + PROFILE_COMMANDS[key],
+             "# Durations in microseconds (per dispatch, from the kernel trace).",
+             "%-78s %6s %10s %10s %10s %7s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "pct")]
+    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        lines.append("%-78s %6d %10.2f %10.2f %10.2f %7.2f" % (k[:78], len(v), _avg(v), min(v), max(v),
+                                                                100 * sum(v) / total))
+    with open(os.path.join(ROOT, "profiles", name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return durs
+
+
+def _write_counters(src, cfgname, trace_sub, mfma_sub, fetch_sub, write_sub, keys, name, what, f_scale, w_scale):
+    durs = _per_kernel(os.path.join(src, trace_sub), "kernel_trace.csv",
+                       lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    def counter(sub, cname):
+        return _per_kernel(os.path.join(src, sub), "counter_collection.csv",
+                           lambda r: float(r["Counter_Value"]) if r["Counter_Name"] == cname else None)
+    util = counter(mfma_sub, "MfmaUtil")
+    mops = counter(mfma_sub, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    fetch = counter(fetch_sub, "FETCH_SIZE")
+    write = counter(write_sub, "WRITE_SIZE")
+    lines = ["# Hardware counters per kernel of %s." % what,
+             "# commands (from the repository root):"]
+    lines += ["#   " + PROFILE_COMMANDS[k] for k in keys + ("copy_fetch", "copy_write")]
+    lines += ["# avg_us: kernel trace; mfma_util_pct: rocprofv3's MfmaUtil (MFMA-busy cycles over active",
+              "# cycles of all SIMDs); mfma_tflops: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP / avg_us (executed",
+              "# matrix-core work, bf16); hbm_mb: FETCH_SIZE x %.3f + WRITE_SIZE x %.3f (KiB per dispatch, each" % (
+                  f_scale, w_scale),
+              "# scaled by what it reads for a plain 256 MiB copy); gbs: hbm_mb / avg_us; pct_hbm: of 8 TB/s.",
+              "%-70s %8s %8s %9s %9s %8s %7s" % ("kernel", "avg_us", "mfma%", "mfma_TF/s", "hbm_MB", "GB/s",
+                                                "%hbm")]
+    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        us = _avg(v)
+        u = _avg(util[k]) if k in util else float("nan")
+        tf = _avg(mops[k]) * 512 / (us * 1e-6) / 1e12 if k in mops else float("nan")
+        mb = ((_avg(fetch[k]) * f_scale if k in fetch else 0.0) + (_avg(write[k]) * w_scale if k in write else 0.0)) \
+            * 1024 / 1e6
+        gbs = mb * 1e6 / (us * 1e3)
+        lines.append("%-70s %8.2f %8.1f %9.1f %9.2f %8.0f %7.1f" % (k[:70], us, u, tf, mb, gbs, 100 * gbs / 8000))
+    with open(os.path.join(ROOT, "profiles", name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize_profiles(src):
     """Turn the rocprofv3 output of PROFILE_COMMANDS (under src) into the text summaries in profiles/."""
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
-    # kernel trace: per-kernel launch statistics of the timed step (and of the step with
-    # the relative-position bias, when that trace is there)
-    traces = [("trace", "trace_c2", "c2_step_kernel_trace.txt", ""),
-              ("trace_relpos", "trace_relpos", "c2_relpos_step_kernel_trace.txt",
-               " with the decomposed relative-position bias")]
-    for key, sub, name, what in traces:
-        if key == "trace_relpos" and not os.path.isdir(os.path.join(src, sub)):
-            continue
-        stats = _csv_rows(os.path.join(src, sub), "kernel_stats.csv")
-        lines = ["# Kernel-trace statistics of the c2 step%s (SAM ViT-B global block, 64 x 64 tokens," % what,
-                 "# C 768, 12 heads x 64, MLP 3072, density 0.4, batch 1): Sobel importance, permutation,",
-                 "# keep-set and one SparseSAM block per step; 20 timed + 5 warmup steps (plus bench setup).",
-                 "# command (from the repository root):",
-                 "#   " + PROFILE_COMMANDS[key],
-                 "# Durations in microseconds.",
-                 "%-88s %6s %10s %10s %10s %7s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "pct")]
-        for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-            lines.append("%-88s %6d %10.2f %10.2f %10.2f %7.2f" % (
-                r["Name"][:88], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-                float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-        with open(os.path.join(out_dir, name), "w") as f:
-            f.write("\n".join(lines) + "\n")
-    # HBM traffic of the attention launch, scaled by a plain copy of known size
+    c2 = ("the c2 step (SAM ViT-B global block, 64 x 64 tokens, C 768, 12 heads x 64, MLP 3072, density 0.4, "
+          "batch 1: Sobel importance, permutation and keep-set, one SparseSAM block)")
+    c3 = ("the c3 step (SAM ViT-B windowed block, 25 windows of 14 x 14 per image, batch 4, density 0.4: "
+          "importance, permutation, one SparseSAM block)")
+    _write_trace(src, "trace_c2", "c2_step_kernel_trace.txt", c2 + ", 20 timed + 5 warm-up steps", "trace")
+    if os.path.isdir(os.path.join(src, "trace_relpos")):
+        _write_trace(src, "trace_relpos", "c2_relpos_step_kernel_trace.txt",
+                     c2 + " with the decomposed relative-position bias", "trace_relpos")
+    if os.path.isdir(os.path.join(src, "trace_c3")):
+        _write_trace(src, "trace_c3", "c3_step_kernel_trace.txt", c3, "trace_c3")
+    # HBM byte counters are scaled by what they read for a plain copy of known size
     cf, _ = _counter_kib(os.path.join(src, "pmc_fetch_copy"), "FETCH_SIZE", "copyBuffer")
     cw, _ = _counter_kib(os.path.join(src, "pmc_write_copy"), "WRITE_SIZE", "copyBuffer")
     f_scale, w_scale = (COPY_BYTES / 1024) / cf, (COPY_BYTES / 1024) / cw
+    if os.path.isdir(os.path.join(src, "pmc_mfma_c2")):
+        _write_counters(src, "c2", "trace_c2", "pmc_mfma_c2", "pmc_fetch_c2", "pmc_write_c2",
+                        ("trace", "mfma", "fetch", "write"), "c2_step_counters.txt", c2, f_scale, w_scale)
+    if os.path.isdir(os.path.join(src, "pmc_mfma_c3")):
+        _write_counters(src, "c3", "trace_c3", "pmc_mfma_c3", "pmc_fetch_c3", "pmc_write_c3",
+                        ("trace_c3", "mfma_c3", "fetch_c3", "write_c3"), "c3_step_counters.txt", c3, f_scale,
+                        w_scale)
     lines = ["# HBM traffic of one sparsesam_attn launch on the c2 workload (attention kernel, and the",
              "# combine of split rows when there are any), from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch,",
              "# separate passes), each scaled by the same counter on a plain 256 MiB device copy.",
@@ -377,7 +525,7 @@ def summarize_profiles(src):
               "source_sha256_16 = %s" % _source_hash(ATTN_SOURCE)]
     with open(TRAFFIC_PROFILE, "w") as f:
         f.write("\n".join(lines) + "\n")
-    print("wrote", os.path.join(out_dir, "c2_step_kernel_trace.txt"), "and", TRAFFIC_PROFILE)
+    print("wrote the summaries under", out_dir)
 
 
 def main():
@@ -441,6 +589,22 @@ def main():
     _log("step %.4f ms (events), wall %.4f ms" % (ms, wall * 1e3 / args.steps))
     if args.profile_only:
         return
+
+    # cold caches: 512 MiB written between steps (more than the L2s and the 256 MB
+    # Infinity Cache hold), each step timed alone
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(max(5, args.steps // 2)):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        wl.step()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+    cold_ms = sorted(cold)[len(cold) // 2]
+    _log("cold-cache step %.4f ms (median of %d)" % (cold_ms, len(cold)))
 
     ss = wl.ss
     plan = wl.plan
@@ -578,6 +742,10 @@ def main():
                      "traffic": measured_traffic(), "launch_ms": round(attn_ms, 5),
                      "algorithmic_flop": attention_flops(plan) * segs},
         "cpu_baseline": cpu,
+        "timing": {"warm_ms_per_step": round(ms, 5),
+                   "cold_ms_per_step": round(cold_ms, 5),
+                   "note": "warm: steps back to back (the ~30 MB working set stays in the L2s and the Infinity "
+                           "Cache); cold: 512 MiB written before each step, median step"},
         "attn_tflops": round(attn_tf, 2),
         "attn_pct_peak": round(100 * attn_tf / PEAK_BF16_TFLOPS, 2),
         "mlp_tflops": round(mlp_tf, 2),
