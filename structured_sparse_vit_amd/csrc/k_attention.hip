@@ -1049,7 +1049,8 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
 #pragma unroll
     for (int kt = 0; kt < kMaxShortBlocks; ++kt) {
       if (kt >= nt32 || !((any >> kt) & 1)) continue;  // no kept pair in this 32 x 32 block
-      const unsigned bits = kbits[kt];
+      // this lane's half of the block's mask: bit 8 (e / 4) + (e % 4) is score element e
+      const unsigned bits = kbits[kt] >> (4 * hi);
       // S^T block: keys kt*32 + 8 (e / 4) + 4 hi + (e % 4) of this lane's query
       f32x16 sc;
 #pragma unroll
@@ -1070,11 +1071,13 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
           sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, tf[ks], sc, 0, 0, 0);
         }
       }
+      // masked scores become -inf: the kept bit sign-extended to a word selects between
+      // the score's bits and -inf's (two instructions per element, no branch)
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const bool keep = (bits >> (8 * (e >> 2) + 4 * hi + (e & 3))) & 1u;
-        sc[e] = keep ? sc[e] : -INFINITY;
+        const int keep = __builtin_amdgcn_sbfe((int)bits, 8 * (e >> 2) + (e & 3), 1);
+        sc[e] = __int_as_float((__float_as_int(sc[e]) & keep) | (int)(0xFF800000u & ~(unsigned)keep));
         mx = fmaxf(mx, sc[e]);
       }
       mx = max_xor32(mx);
@@ -1089,7 +1092,11 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
           for (int e = 0; e < 16; ++e) oacc[md][e] *= alpha;
         m_run = m_new;
       }
-      float ps0 = 0.0f, ps1 = 0.0f;
+      // branch-free probabilities: the reference is clamped to -FLT_MAX, so a masked score
+      // (-inf) gives exp2(-inf) = 0 even while no key of the row has been kept (the
+      // reference is then -inf); otherwise the reference is finite and unchanged
+      const float mref = fmaxf(m_run, -3.40282347e38f);
+      float ps = 0.0f;
       bf16x8 pf[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -1097,15 +1104,12 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float x = sc[kk * 8 + e];
-          const float p = x == -INFINITY ? 0.0f
-                          : __builtin_amdgcn_exp2f(REL ? x - m_run : __builtin_fmaf(x, c_log2, -m_run));
-          if constexpr (!kSumRow) {
-            if (e & 1)
-              ps1 += p;
-            else
-              ps0 += p;
-          }
-          v[e] = to_bf16(p);
+          v[e] = to_bf16(__builtin_amdgcn_exp2f(REL ? x - mref : __builtin_fmaf(x, c_log2, -mref)));
+        }
+        // the denominator sums exactly the bf16 probabilities V is multiplied with
+        if constexpr (!kSumRow) {
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) ps = sum_bf16_pair(v[e], v[e + 1], ps);
         }
         u32x4 r = __builtin_bit_cast(u32x4, v);
         const auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
@@ -1113,7 +1117,7 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
         r = u32x4{s02[0], s13[0], s02[1], s13[1]};
         pf[kk] = __builtin_bit_cast(bf16x8, r);
       }
-      if constexpr (!kSumRow) l_run += ps0 + ps1;
+      if constexpr (!kSumRow) l_run += ps;
       // O^T += V^T P^T: rows d = 32 md + l32 (zero past D; row D all ones when the last
       // block has spare rows, so the matrix cores sum the denominators), keys kt*32 +
       // 16 kk + 8 hi ..

@@ -151,6 +151,25 @@ struct QKVStore {
 #pragma unroll
           for (int e = 0; e < 8; ++e) w[e] = v[j][i][e] + b;
           store8<T>(vt + (((size_t)seg * heads + h) * D + d) * (size_t)n_pad + p, w);
+        } else if constexpr (sizeof(T) == 2) {
+          // Segments of a length 4 (mod 8) (the 196-token windows) start at multiples of
+          // four rows, so each half of the chunk (rows r .. r+3, r+4 .. r+7; r a multiple of
+          // 8) lies in one segment at a four-aligned position: one 8-byte store per half.
+          if (r[i] + 8 <= M && (n & 3) == 0) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int rr = r[i] + 4 * hh;
+              const int sg = f_n.div(rr), pp = rr - sg * n;
+              bf16x4 w4;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) w4[e] = to_bf16(v[j][i][4 * hh + e] + b);
+              *reinterpret_cast<bf16x4*>(vt + (((size_t)sg * heads + h) * D + d) * (size_t)n_pad + pp) = w4;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (r[i] + e < M) elem(r[i] + e, c[j], v[j][i][e]);
+          }
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -744,10 +763,12 @@ static hipError_t run_bf16(const bf16_t* a, const bf16_t* w, int m, int n, int k
 // epilogue and the next one's first loads overlap the other's K loop); 128 x 64 and
 // 64 x 64 with two slots 48 and 32 KiB (three to five per CU); 128 x 64 with six slots
 // 144 KiB (one per CU, deep prefetch for long K over few tiles).
-enum class TileShape { t64x64, t128x64s2, t128x64, t192x128s2, t256x128 };
+enum class TileShape { t64x64, t128x64s2, t128x64, t192x128s2, t256x128, t64x128s4 };
 
 // Shape choice. Long K over few tiles (the ViT-B second MLP product, 1638 x 768 x 3072)
-// takes 128 x 64 with six slots, narrow short products 64 x 64. Otherwise each shape's time is estimated as
+// takes 64 x 128 with four slots (two workgroups per CU; 3 % faster for that MLP than
+// 128 x 64 with six slots at one per CU, which in turn beat 64 x 64, 64 x 64 with six
+// slots and 128 x 64 with three), narrow short products 64 x 64. Otherwise each shape's time is estimated as
 // (rounds of resident workgroups) x (tile area per CU per round) / (efficiency), the
 // efficiencies -- 1.0, 1.3, 0.8 and 0.3 for 256 x 128, 192 x 128, 128 x 64 and 64 x 64
 // -- fitted to timings of every shape on MI355X over 25 ViT-B/L/H products (M x N x K
@@ -756,7 +777,7 @@ enum class TileShape { t64x64, t128x64s2, t128x64, t192x128s2, t256x128 };
 // `align`: tiles must not straddle multiples of it (the QKV parts), 0 = no constraint.
 static TileShape pick_tile(int m, int n, int k, int align) {
   auto tiles = [&](int bm, int bn) { return (long)((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
-  if (k >= 2048 && tiles(128, 64) <= 320) return TileShape::t128x64;
+  if (k >= 2048 && tiles(128, 64) <= 320 && align == 0) return TileShape::t64x128s4;
   // narrow short products (the ViT-B projection, 4096 x 768 x 768): 64 x 64 measured
   // fastest, by 7 % to 15 % depending on the epilogue
   if (n <= 768 && (double)m * n * k < 1e10) return TileShape::t64x64;
@@ -792,6 +813,7 @@ static hipError_t run(const bf16_t* a, const bf16_t* w, int m, int n, int k, con
     case TileShape::t192x128s2: return run_bf16<192, 128, 2>(a, w, m, n, k, e, st);
     case TileShape::t64x64: return run_bf16<64, 64, 2>(a, w, m, n, k, e, st);
     case TileShape::t128x64s2: return run_bf16<128, 64, 2>(a, w, m, n, k, e, st);
+    case TileShape::t64x128s4: return run_bf16<64, 128, 4>(a, w, m, n, k, e, st);
     default: return run_bf16<128, 64, 6>(a, w, m, n, k, e, st);
   }
 }
