@@ -309,28 +309,48 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
   }
   // short-segment attention tables (n <= 256)
   p->pos_tile.clear();
-  p->keep32.clear();
   p->any32.clear();
+  p->mask_class.clear();
+  p->mask_row.clear();
   p->nt32 = 0;
+  p->mask_ksteps = 0;
   if (p->n <= kShortMaxN) {
     const int nt32 = (p->n + 31) / 32;
-    p->nt32 = nt32;
     p->pos_tile.assign(p->n, 0);
     for (int t = 0; t < p->tiles; ++t)
       for (int i = 0; i < p->tile_len[t]; ++i) p->pos_tile[p->tile_start[t] + i] = t;
-    p->keep32.assign((size_t)p->tiles * nt32, 0);
+    // kept[t1][t2], then the classes of key tiles with equal columns (first appearance)
+    std::vector<char> kept((size_t)p->tiles * p->tiles, 0);
     for (int t = 0; t < p->tiles; ++t)
-      for (int c = p->row_ptr[t]; c < p->row_ptr[t + 1]; ++c) {
-        const int t2 = p->col_idx[c];
-        for (int i = 0; i < p->tile_len[t2]; ++i) {
-          const int k = p->tile_start[t2] + i;
-          p->keep32[(size_t)t * nt32 + k / 32] |= (int)(1u << (k % 32));
+      for (int c = p->row_ptr[t]; c < p->row_ptr[t + 1]; ++c) kept[(size_t)t * p->tiles + p->col_idx[c]] = 1;
+    std::map<std::vector<char>, int> cls_of;
+    std::vector<int> tile_cls(p->tiles), cls_tile;
+    for (int t2 = 0; t2 < p->tiles; ++t2) {
+      std::vector<char> col(p->tiles);
+      for (int t1 = 0; t1 < p->tiles; ++t1) col[t1] = kept[(size_t)t1 * p->tiles + t2];
+      auto f = cls_of.emplace(col, (int)cls_tile.size());
+      if (f.second) cls_tile.push_back(t2);
+      tile_cls[t2] = f.first->second;
+    }
+    const int pad_cls = (int)cls_tile.size(), ncls = pad_cls + 1;
+    if (ncls <= 32) {
+      const int ks = ncls <= 16 ? 1 : 2;
+      p->nt32 = nt32;
+      p->mask_ksteps = ks;
+      p->mask_class.assign((size_t)nt32 * 32, pad_cls);
+      for (int k = 0; k < p->n; ++k) p->mask_class[k] = tile_cls[p->pos_tile[k]];
+      const uint16_t kMasked = 0xF180;  // bf16 -2^100
+      p->mask_row.assign((size_t)p->tiles * ks * 8, 0);
+      for (int t1 = 0; t1 < p->tiles; ++t1)
+        for (int c = 0; c < 16 * ks; ++c) {
+          const bool masked = c == pad_cls || (c < pad_cls && !kept[(size_t)t1 * p->tiles + cls_tile[c]]);
+          if (masked) p->mask_row[(size_t)t1 * ks * 8 + c / 2] |= (int)((uint32_t)kMasked << (16 * (c & 1)));
         }
-      }
-    p->any32.assign(nt32, 0);
-    for (int q = 0; q < p->n; ++q)
-      for (int kt = 0; kt < nt32; ++kt)
-        if (p->keep32[(size_t)p->pos_tile[q] * nt32 + kt] != 0) p->any32[q / 32] |= 1 << kt;
+      p->any32.assign(nt32, 0);
+      for (int q = 0; q < p->n; ++q)
+        for (int k = 0; k < p->n; ++k)
+          if (kept[(size_t)p->pos_tile[q] * p->tiles + p->pos_tile[k]]) p->any32[q / 32] |= 1 << (k / 32);
+    }
   }
   // keep-set size per segment
   p->seg_k.resize(p->segs_per_img);
@@ -380,8 +400,8 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     };
     size_t o_rp = put(p->row_ptr), o_ci = put(p->col_idx), o_ts = put(p->tile_start), o_tl = put(p->tile_len),
            o_or = put(p->order), o_sk = put(p->seg_k), o_so = put(p->seg_off), o_it = put(p->items),
-           o_sp = put(p->splits), o_pt = put(p->pos_tile), o_k32 = put(p->keep32), o_a32 = put(p->any32),
-           o_kp = put(p->keep_pos);
+           o_sp = put(p->splits), o_pt = put(p->pos_tile), o_a32 = put(p->any32), o_mc = put(p->mask_class),
+           o_mr = put(p->mask_row), o_kp = put(p->keep_pos);
     blob.push_back(0);
     void* dptr = nullptr;
     hipError_t e = hipMalloc(&dptr, blob.size() * sizeof(int));
@@ -409,8 +429,9 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     p->d_items = b + o_it;
     p->d_splits = b + o_sp;
     p->d_pos_tile = b + o_pt;
-    p->d_keep32 = b + o_k32;
     p->d_any32 = b + o_a32;
+    p->d_mask_class = b + o_mc;
+    p->d_mask_row = b + o_mr;
     p->d_keep_pos = b + o_kp;
     p->attn_resident_wgs = attn_long_supported(*p) ? attn_long_resident_wgs(dev, p->desc.head_dim) : 0;
     (void)hipGetLastError();

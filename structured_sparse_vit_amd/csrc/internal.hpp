@@ -45,11 +45,14 @@ struct sparsesam_plan {
   std::vector<int> items, splits;
   int n_items = 0, n_split_rows = 0, n_slots = 0;
   int attn_resident_wgs = 0;          // workgroups of the attention kernel resident at once
-  // short segments (n <= 256, the windows): tile of every position; for each (query
-  // tile, 32-key block) the kept key positions of the block as a bit mask; for each
-  // 32-query block the 32-key blocks holding any kept pair
-  std::vector<int> pos_tile, keep32, any32;
-  int nt32 = 0;
+  // short segments (n <= 256, the windows): tile of every position; for each 32-query
+  // block the 32-key blocks holding any kept pair. The mask goes to the matrix cores:
+  // key tiles with the same kept column form one class (pad keys a class of their own);
+  // mask_class[k] is the class of key position k (nt32 * 32 entries), mask_row[t] the
+  // bias of query tile t against each class (16 * mask_ksteps bf16: 0 kept, -2^100
+  // masked, two per int). nt32 = 0: no short-segment kernel (more than 32 classes).
+  std::vector<int> pos_tile, any32, mask_class, mask_row;
+  int nt32 = 0, mask_ksteps = 0;
   // relative-position bias: segment shape (grid or window) and the bias table row of a
   // query: key rows at 0 .. rel_seg_h - 1, key columns at rel_xoff .., rel_tj entries
   // (0 when the segment is larger than 64 x 64: no bias support)
@@ -68,8 +71,9 @@ struct sparsesam_plan {
   const int* d_items = nullptr;
   const int* d_splits = nullptr;
   const int* d_pos_tile = nullptr;
-  const int* d_keep32 = nullptr;
   const int* d_any32 = nullptr;
+  const int* d_mask_class = nullptr;
+  const int* d_mask_row = nullptr;
   // keep-set of a stream kept in stripe-sorted order: the positions of ranks 0 .. K - 1
   // of every segment, (seg * n) + (rank % g) * S + rank / g, for max_batch images in
   // the keep-set layout (static: the keep-set is the first K ranks)

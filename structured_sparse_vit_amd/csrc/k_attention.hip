@@ -933,13 +933,19 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
 constexpr int kMaxShortBlocks = 8;  // 32-token blocks of a short segment
 static_assert(kShortMaxN <= 32 * kMaxShortBlocks, "short segments fit the unrolled block loop");
 
+constexpr int kShortOneHotBytes = 17 * 16;  // 17 one-hot rows of eight 16-bit entries
+constexpr int kShortWaves = 8;               // one wavefront per 32-query block (nt32 <= 8)
+constexpr int kShortThreads = 64 * kShortWaves;
+
 template <int D>
 struct ShortLds {
   static constexpr int KLD = D + 8;        // K row stride (bf16): 16-byte pad, conflict-free reads
   static constexpr int MD = (D + 31) / 32;  // 32-row blocks of V^T
+  // K rows, V^T rows, the fp16 (bias) and bf16 (mask) one-hot tables, then two ints per
+  // key (mask class; coordinates for the bias)
   static size_t bytes(int nt32) {
     const int nk = nt32 * 32;
-    return (size_t)nk * KLD * 2 + (size_t)D * (nk + 8) * 2;
+    return (size_t)nk * KLD * 2 + (size_t)D * (nk + 8) * 2 + 2 * kShortOneHotBytes + (size_t)nk * 8;
   }
 };
 
@@ -948,11 +954,19 @@ struct ShortLds {
 // at 16..31: two fp16 MFMA k-steps whose K operand is one-hot in the key's row (k-step 0)
 // or column (k-step 1), from 17 one-hot rows after the K and V^T tiles in LDS. The
 // scores are then taken to exp2 units before the bias is added.
-template <int D, bool REL>
-__global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
+//
+// The mask rides on the matrix cores too: MK bf16 k-steps add, to the score of a query
+// in tile tq and a key of class c, mask_row[tq][c] (0 kept, -2^100 masked), with a
+// one-hot K operand from 17 bf16 one-hot rows. A masked score is then -2^100 (times the
+// scale): its probability is exactly 0 against any kept reference. A row whose blocks so
+// far hold no kept key takes such a score as its reference; its first kept block then
+// rescales by exp2(-huge) = 0, which leaves exactly what starting there would have.
+template <int D, bool REL, int MK>
+__global__ void __launch_bounds__(kShortThreads) attn_short_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                                          const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
                                                          const int* __restrict__ pos_tile,
-                                                         const int* __restrict__ keep32,
+                                                         const int* __restrict__ mask_class,
+                                                         const int* __restrict__ mask_row,
                                                          const int* __restrict__ any32, int n, int n_pad, int nt32,
                                                          int heads, float c_log2, const f16_t* __restrict__ rel_t,
                                                          const int* __restrict__ rel_kc) {
@@ -971,56 +985,62 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
 
   // Every load of the fill is issued before any LDS store (fixed trip counts, nk <=
   // 256), so the workgroup waits for one memory latency instead of one per chunk.
-  // K rows 0..nk-1 (zero past n), 8 channels per 16-byte chunk: chunk c = tid + 256 i.
-  constexpr int KCH = D / 8, KIT = KCH;  // nk * KCH / 256 <= KCH
+  // K rows 0..nk-1 (zero past n), 8 channels per 16-byte chunk: chunk c = tid + 512 i.
+  constexpr int KCH = D / 8, KIT = 256 * KCH / kShortThreads;  // nk * KCH / 512 <= KIT
   i32x4 kv[KIT];
   // (loads are unconditional, from clamped in-bounds addresses; rows and keys past n
   // are zeroed in registers)
 #pragma unroll
   for (int i = 0; i < KIT; ++i) {
-    const int c = tid + 256 * i, r = c / KCH, ch = c - (c / KCH) * KCH;
+    const int c = tid + kShortThreads * i, r = c / KCH, ch = c - (c / KCH) * KCH;
     kv[i] = *reinterpret_cast<const i32x4*>(k_base + (size_t)min(r, n - 1) * D + ch * 8);
   }
-  // V^T rows d = tid / 32 + 8 i, 16-byte key chunk tid % 32 (of nk / 8 <= 32): keys
+  // V^T rows d = tid / 32 + 16 i, 16-byte key chunk tid % 32 (of nk / 8 <= 32): keys
   // past n read as zero. The chunk read lies inside the n_pad-long row.
   const int vch = tid & 31, kc = vch * 8, kc_in = min(kc, (n - 1) & ~7);
-  bf16x8 vv[D / 8];
+  constexpr int VIT = D / 16;
+  bf16x8 vv[VIT];
 #pragma unroll
-  for (int i = 0; i < D / 8; ++i)
-    vv[i] = *reinterpret_cast<const bf16x8*>(v_base + (size_t)((tid >> 5) + 8 * i) * n_pad + kc_in);
+  for (int i = 0; i < VIT; ++i)
+    vv[i] = *reinterpret_cast<const bf16x8*>(v_base + (size_t)((tid >> 5) + 16 * i) * n_pad + kc_in);
 #pragma unroll
   for (int i = 0; i < KIT; ++i) {
-    const int c = tid + 256 * i, r = c / KCH, ch = c - (c / KCH) * KCH;
+    const int c = tid + kShortThreads * i, r = c / KCH, ch = c - (c / KCH) * KCH;
     if (r < nk) *reinterpret_cast<i32x4*>(Ks + r * L::KLD + ch * 8) = r < n ? kv[i] : i32x4{0, 0, 0, 0};
   }
 #pragma unroll
-  for (int i = 0; i < D / 8; ++i)
+  for (int i = 0; i < VIT; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (kc + e >= n) vv[i][e] = (bf16_t)0.0f;
   if (kc < nk) {
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) *reinterpret_cast<bf16x8*>(Vs + ((tid >> 5) + 8 * i) * vld + kc) = vv[i];
+    for (int i = 0; i < VIT; ++i) *reinterpret_cast<bf16x8*>(Vs + ((tid >> 5) + 16 * i) * vld + kc) = vv[i];
   }
+  // one-hot rows (row 8 + e: 1.0 at element e, the other rows zero): fp16 for the bias,
+  // bf16 for the mask
   const char* onehot = reinterpret_cast<const char*>(Vs + (size_t)D * vld);
-  if constexpr (REL) {
-    if (tid < 68) {  // row 8 + e: fp16 1.0 at element e; the other rows zero
-      const int row = tid >> 2, i = tid & 3, e = row - 8;
-      const uint32_t v = e == 2 * i ? 0x3C00u : e == 2 * i + 1 ? 0x3C000000u : 0u;
-      reinterpret_cast<uint32_t*>(const_cast<char*>(onehot))[tid] = v;
-    }
+  const char* onehot_m = onehot + kShortOneHotBytes;
+  int* key_cls = reinterpret_cast<int*>(const_cast<char*>(onehot_m + kShortOneHotBytes));  // [nk]
+  int* key_rc = key_cls + nk;                                                              // [nk]
+  // per key: mask class (pads their own) and, for the bias, the coordinates
+  // (row | (16 + column) << 16)
+  if (tid < nk) {
+    key_cls[tid] = mask_class[tid];
+    if constexpr (REL) key_rc[tid] = rel_kc[(size_t)seg * n + min(tid, n - 1)];
+  }
+  if (tid < 136) {
+    const int t = tid < 68 ? tid : tid - 68;
+    const int row = t >> 2, i = t & 3, e = row - 8;
+    const uint32_t one = tid < 68 ? 0x3C00u : 0x3F80u;
+    const uint32_t v = e == 2 * i ? one : e == 2 * i + 1 ? one << 16 : 0u;
+    if (REL || tid >= 68) reinterpret_cast<uint32_t*>(const_cast<char*>(tid < 68 ? onehot : onehot_m))[t] = v;
   }
   __syncthreads();
 
   const int hi = lane >> 5, l32 = lane & 31;
-  // the coordinates (row | (16 + column) << 16) of key kt * 32 + l32, every block
-  int kcs[kMaxShortBlocks];
-  if constexpr (REL) {
-#pragma unroll
-    for (int kt = 0; kt < kMaxShortBlocks; ++kt) kcs[kt] = rel_kc[(size_t)seg * n + min(kt * 32 + l32, n - 1)];
-  }
   constexpr bool kSumRow = L::MD * 32 > D;  // spare accumulator rows: denominators on the matrix cores
-  for (int qt = wave; qt < nt32; qt += 4) {
+  for (int qt = wave; qt < nt32; qt += kShortWaves) {
     const int qpos = qt * 32 + l32;
     const int qrow = min(qpos, n - 1);
     const int tq = pos_tile[qrow];
@@ -1034,6 +1054,11 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
       for (int ks = 0; ks < 2; ++ks)
         tf[ks] = *reinterpret_cast<const f16x8*>(rel_t + ((size_t)sh * n + qrow) * 32 + ks * 16 + hi * 8);
     }
+    // this query's mask entries 16 ks + 8 hi .. + 7 (the B operand of the mask k-steps)
+    bf16x8 mq[MK];
+#pragma unroll
+    for (int ks = 0; ks < MK; ++ks)
+      mq[ks] = *reinterpret_cast<const bf16x8*>(mask_row + ((size_t)tq * MK * 16 + ks * 16 + hi * 8) / 2);
     f32x16 oacc[L::MD];
 #pragma unroll
     for (int md = 0; md < L::MD; ++md)
@@ -1041,16 +1066,11 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
       for (int e = 0; e < 16; ++e) oacc[md][e] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
     const int any = any32[qt];
-    // this lane's mask words, all requested before the first block (index clamped
-    // into the row; only kt < nt32 is used)
-    unsigned kbits[kMaxShortBlocks];
-#pragma unroll
-    for (int kt = 0; kt < kMaxShortBlocks; ++kt) kbits[kt] = (unsigned)keep32[tq * nt32 + min(kt, nt32 - 1)];
 #pragma unroll
     for (int kt = 0; kt < kMaxShortBlocks; ++kt) {
       if (kt >= nt32 || !((any >> kt) & 1)) continue;  // no kept pair in this 32 x 32 block
-      // this lane's half of the block's mask: bit 8 (e / 4) + (e % 4) is score element e
-      const unsigned bits = kbits[kt] >> (4 * hi);
+      const int kcl = key_cls[kt * 32 + l32];
+      const int kcs = REL ? key_rc[kt * 32 + l32] : 0;
       // S^T block: keys kt*32 + 8 (e / 4) + 4 hi + (e % 4) of this lane's query
       f32x16 sc;
 #pragma unroll
@@ -1065,21 +1085,22 @@ __global__ void __launch_bounds__(256) attn_short_kernel(const bf16_t* __restric
         for (int e = 0; e < 16; ++e) sc[e] *= c_log2;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int jj = ks == 0 ? (kcs[kt] & 0xffff) : (kcs[kt] >> 16);
+          const int jj = ks == 0 ? (kcs & 0xffff) : (kcs >> 16);
           const int row = min(max(jj - 16 * ks - 8 * hi + 8, 0), 16);
           const f16x8 af = *reinterpret_cast<const f16x8*>(onehot + row * 16);
           sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, tf[ks], sc, 0, 0, 0);
         }
       }
-      // masked scores become -inf: the kept bit sign-extended to a word selects between
-      // the score's bits and -inf's (two instructions per element, no branch)
+      // the mask: -2^100 on masked scores, 0 on kept ones
+#pragma unroll
+      for (int ks = 0; ks < MK; ++ks) {
+        const int row = min(max(kcl - 16 * ks - 8 * hi + 8, 0), 16);
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(onehot_m + row * 16);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, mq[ks], sc, 0, 0, 0);
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int keep = __builtin_amdgcn_sbfe((int)bits, 8 * (e >> 2) + (e & 3), 1);
-        sc[e] = __int_as_float((__float_as_int(sc[e]) & keep) | (int)(0xFF800000u & ~(unsigned)keep));
-        mx = fmaxf(mx, sc[e]);
-      }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[e]);
       mx = max_xor32(mx);
       const float m_new = fmaxf(m_run, REL ? mx : mx * c_log2);
       if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
@@ -1257,6 +1278,21 @@ static hipError_t run_simt(const sparsesam_plan& p, int segments, const T* q, co
   return hipGetLastError();
 }
 
+// The short-segment kernel for a plan: one workgroup per (segment, head), the mask in
+// one or two k-steps.
+template <int D, bool REL>
+static hipError_t launch_short(const sparsesam_plan& p, int units, const bf16_t* q, const bf16_t* k,
+                               const bf16_t* vt, bf16_t* o, float c_log2, const f16_t* tb, const int* kc,
+                               hipStream_t st) {
+  const size_t lds = ShortLds<D>::bytes(p.nt32);
+  auto kern = p.mask_ksteps == 2 ? attn_short_kernel<D, REL, 2> : attn_short_kernel<D, REL, 1>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)units), dim3(kShortThreads), lds, st, q, k, vt, o, p.d_pos_tile, p.d_mask_class,
+                     p.d_mask_row, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2, tb, kc);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
                             float scale, void* partial, hipStream_t st) {
@@ -1269,24 +1305,8 @@ hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, c
       const auto* kb = reinterpret_cast<const bf16_t*>(k);
       const auto* vb = reinterpret_cast<const bf16_t*>(vt);
       auto* ob = reinterpret_cast<bf16_t*>(o);
-      if (p.desc.head_dim == 64) {
-        const size_t lds = ShortLds<64>::bytes(p.nt32);
-        hipError_t e = hipFuncSetAttribute((const void*)attn_short_kernel<64, false>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((attn_short_kernel<64, false>), dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
-                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2, nullptr,
-                           nullptr);
-      } else {
-        const size_t lds = ShortLds<80>::bytes(p.nt32);
-        hipError_t e = hipFuncSetAttribute((const void*)attn_short_kernel<80, false>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((attn_short_kernel<80, false>), dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
-                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2, nullptr,
-                           nullptr);
-      }
-      return hipGetLastError();
+      return p.desc.head_dim == 64 ? launch_short<64, false>(p, units, qb, kb, vb, ob, c_log2, nullptr, nullptr, st)
+                                   : launch_short<80, false>(p, units, qb, kb, vb, ob, c_log2, nullptr, nullptr, st);
     }
     if (attn_long_supported(p)) {
       const bool d80 = p.desc.head_dim == 80;
@@ -1393,18 +1413,8 @@ hipError_t launch_attention_relpos(const sparsesam_plan& p, int segments, const 
       const auto* kb = reinterpret_cast<const bf16_t*>(k);
       const auto* vb = reinterpret_cast<const bf16_t*>(vt);
       auto* ob = reinterpret_cast<bf16_t*>(o);
-      const bool d80 = p.desc.head_dim == 80;
-      const size_t lds = (d80 ? ShortLds<80>::bytes(p.nt32) : ShortLds<64>::bytes(p.nt32)) + 512;
-      const void* kern = d80 ? (const void*)attn_short_kernel<80, true> : (const void*)attn_short_kernel<64, true>;
-      e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      if (d80)
-        hipLaunchKernelGGL((attn_short_kernel<80, true>), dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
-                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2, tb, kc);
-      else
-        hipLaunchKernelGGL((attn_short_kernel<64, true>), dim3((unsigned)units), dim3(256), lds, st, qb, kb, vb, ob,
-                           p.d_pos_tile, p.d_keep32, p.d_any32, p.n, p.n_pad, p.nt32, p.desc.heads, c_log2, tb, kc);
-      return hipGetLastError();
+      return p.desc.head_dim == 80 ? launch_short<80, true>(p, units, qb, kb, vb, ob, c_log2, tb, kc, st)
+                                   : launch_short<64, true>(p, units, qb, kb, vb, ob, c_log2, tb, kc, st);
     }
   }
   // every other plan: fp32 tables and the SIMT kernel
