@@ -244,16 +244,58 @@ def encoder_run(key, dev, density=None, passes=3, rel_pos=False, sorted_stream=F
 
 
 def window_block_run(dev):
-    """The c3 windowed block (ViT-B, 25 windows of 14 x 14 per image, batch 4)."""
+    """The c3 windowed block (ViT-B, 25 windows of 14 x 14 per image, batch 4): step and
+    block times, attention and routed-MLP rates, and the same step at density 1."""
     from synth import get_config
     cfg = get_config("c3")
     wl = Workload(cfg, dev)
     wl.step()
-    blk = time_region(lambda: wl.ss.block(wl.plan, wl.w, wl.x, wl.perm, wl.routed, workspace=wl.ws), 20, 3)
+    ss, plan = wl.ss, wl.plan
+    blk = time_region(lambda: ss.block(plan, wl.w, wl.x, wl.perm, wl.routed, workspace=wl.ws), 20, 3)
     step = time_region(wl.step, 20, 3)
     tokens = cfg.batch * cfg.grid * cfg.grid
+    segs = cfg.batch * plan.info["segments_per_image"]
+    q, k, vt, o = wl.attn_operands()
+    attn_ms = time_region(lambda: ss.attn(plan, q, k, vt, out=o, workspace=wl.attn_ws), 30, 5)
+    attn_tf = attention_flops(plan) * segs / (attn_ms * 1e-3) / 1e12
+    xr = wl.x.view(-1, cfg.channels)
+    mlp_ms = time_region(lambda: ss.mlp(plan, xr, wl.routed, wl.w["ln2_g"], wl.w["ln2_b"], wl.w["w1"], wl.w["b1"],
+                                        wl.w["w2"], wl.w["b2"], workspace=wl.mlp_ws), 30, 5)
+    mlp_tf = mlp_flops(plan, cfg.batch) / (mlp_ms * 1e-3) / 1e12
+    del wl, q, k, vt, o
+    wld = Workload(cfg.with_(attn_density=1.0, mlp_density=1.0), dev)
+    wld.step()
+    dense = time_region(wld.step, 20, 3)
+    del wld
     return {"batch": cfg.batch, "block_ms": round(blk, 5), "step_ms": round(step, 5),
-            "tokens_per_s": round(tokens / (step * 1e-3), 1)}
+            "tokens_per_s": round(tokens / (step * 1e-3), 1),
+            "realised_attn_density": plan.info["realised_density"],
+            "attn_ms": round(attn_ms, 5), "attn_tflops": round(attn_tf, 2),
+            "attn_pct_peak": round(100 * attn_tf / PEAK_BF16_TFLOPS, 2),
+            "mlp_ms": round(mlp_ms, 5), "mlp_tflops": round(mlp_tf, 2),
+            "mlp_pct_peak": round(100 * mlp_tf / PEAK_BF16_TFLOPS, 2),
+            "density_1_step_ms": round(dense, 5), "speedup_vs_density_1": round(dense / step, 3),
+            "note": "attention TFLOP/s counts kept token pairs only (4 D per pair per head)"}
+
+
+def tiny_block_run(dev):
+    """The c1 fp32 block (16 x 16 tokens, C 64, one head): step time and the same step at
+    density 1. fp32 runs on the SIMT kernels; the rates are against the fp32 vector peak."""
+    from synth import get_config
+    cfg = get_config("c1")
+    wl = Workload(cfg, dev)
+    wl.step()
+    step = time_region(wl.step, 50, 5)
+    flops = block_flops(wl.plan, cfg.batch)
+    wld = Workload(cfg.with_(attn_density=1.0, mlp_density=1.0), dev)
+    wld.step()
+    dense = time_region(wld.step, 50, 5)
+    tokens = cfg.batch * cfg.grid * cfg.grid
+    return {"batch": cfg.batch, "step_ms": round(step, 5), "tokens_per_s": round(tokens / (step * 1e-3), 1),
+            "realised_attn_density": wl.plan.info["realised_density"],
+            "block_tflops": round(flops / (step * 1e-3) / 1e12, 4),
+            "density_1_step_ms": round(dense, 5), "speedup_vs_density_1": round(dense / step, 3),
+            "note": "launch-bound: 256 tokens of 64 channels"}
 
 
 def _cpu_model():
@@ -697,6 +739,8 @@ def main():
     if not args.no_encoders:
         extra["c3_window_block"] = window_block_run(dev)
         _log("c3 windowed block", extra["c3_window_block"])
+        extra["c1_block"] = tiny_block_run(dev)
+        _log("c1 block", extra["c1_block"])
         enc = {}
         for key in ("c4", "c5"):
             enc[key] = {"sparse": encoder_run(key, dev), "density_1.0": encoder_run(key, dev, density=1.0),
