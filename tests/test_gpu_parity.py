@@ -215,6 +215,33 @@ def test_attention_bf16_simt_fallback(key, over):
     check_close(o, want, what="bf16 SIMT attention %s %s" % (key, over))
 
 
+# A short global segment (16 x 16 tokens, one stripe of sixteen 16-token tiles): every
+# key tile has its own kept column, so with the pad keys' class there are 17 mask
+# classes and the short-segment kernel adds its mask in two matrix-core k-steps.
+SHORT_TWO_KSTEPS = dict(dtype="bf16", stripes=1, block=16, global_tokens=16, heads=2, mlp_hidden=256,
+                        attn_density=0.3)
+
+
+def mask_classes(cfg, plan):
+    """Distinct kept columns of the plan's token mask (the key classes the plan's mask
+    k-steps must tell apart, pads not counted)."""
+    n = plan.info["seq_len"]
+    keep = oracle.position_keep(n, cfg.stripes, cfg.block, cfg.global_tokens, plan.info["band_radius"])
+    return len({keep[:, k].tobytes() for k in range(n)})
+
+
+@pytest.mark.parametrize("head_dim", [64, 80])
+def test_attention_short_segment_two_mask_ksteps(head_dim):
+    _say("attention short segment, two mask k-steps, head_dim", head_dim)
+    heads = 2 if head_dim == 64 else 8  # bf16 plans take channels in multiples of 128
+    over = dict(SHORT_TWO_KSTEPS, heads=heads, head_dim=head_dim, channels=heads * head_dim)
+    cfg = config("c1").with_(**over)
+    plan = _plan(cfg)
+    assert plan.info["seq_len"] <= 256 and mask_classes(cfg, plan) + 1 > 16
+    o, want = _attn_case("c1", seed=11, **over)
+    check_close(o, want, what="short segment, two mask k-steps, D %d" % head_dim)
+
+
 def test_attention_single_stripe_and_wide_band():
     _say("attention stripes=1")
     o, want = _attn_case("c2", seed=4, stripes=1, band_radius=2)

@@ -77,6 +77,17 @@ def test_attn_relpos_parity(key):
     check_close(o, want, what="attention relpos " + key)
 
 
+def test_attn_relpos_short_segment_two_mask_ksteps():
+    """The bias on a 16 x 16 bf16 segment whose mask needs two k-steps (one stripe of
+    sixteen 16-token tiles, 17 key classes with the pads')."""
+    _say("attention + relative position, two mask k-steps")
+    over = dict(dtype="bf16", stripes=1, block=16, global_tokens=16, heads=2, head_dim=64, channels=128,
+                mlp_hidden=256, attn_density=0.3)
+    o, want, plan = _attn_relpos_case("c1", seed=9, **over)
+    _say("  max-abs %.3e rel-L2 %.3e" % (np.abs(o - want).max(), rel_l2(o, want)))
+    check_close(o, want, what="attention relpos, two mask k-steps")
+
+
 def test_attn_relpos_bias_matters_and_zero_tables_match_plain():
     """At the synthetic tables' default scale (bias about 1.6 logits) the c2 outputs move
     far past the bar, and zero tables give the unbiased result."""
