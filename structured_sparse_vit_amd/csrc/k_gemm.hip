@@ -762,13 +762,18 @@ static hipError_t run_bf16(const bf16_t* a, const bf16_t* w, int m, int n, int k
 // workgroup per CU); 192 x 128 with two slots 80 KiB (two per CU, so one tile's
 // epilogue and the next one's first loads overlap the other's K loop); 128 x 64 and
 // 64 x 64 with two slots 48 and 32 KiB (three to five per CU); 128 x 64 with six slots
-// 144 KiB (one per CU, deep prefetch for long K over few tiles).
-enum class TileShape { t64x64, t128x64s2, t128x64, t192x128s2, t256x128, t64x128s4 };
+// 144 KiB and 192 x 128 with three slots 120 KiB (one per CU, deeper prefetch for long
+// K).
+enum class TileShape { t64x64, t128x64s2, t128x64, t192x128s2, t256x128, t64x128s4, t192x128s3 };
 
 // Shape choice. Long K over few tiles (the ViT-B second MLP product, 1638 x 768 x 3072)
 // takes 64 x 128 with four slots (two workgroups per CU; 3 % faster for that MLP than
 // 128 x 64 with six slots at one per CU, which in turn beat 64 x 64, 64 x 64 with six
-// slots and 128 x 64 with three), narrow short products 64 x 64. Otherwise each shape's time is estimated as
+// slots and 128 x 64 with three); long K over at most one round of 192 x 128 tiles (the
+// windowed ViT-B second MLP product, 6554 x 768 x 3072) takes 192 x 128 with three slots
+// (3 % faster for the c3 block than the model's 128 x 64, in a sweep of eleven shapes
+// over every product of the ViT-B/L/H blocks, where the model's choice was otherwise
+// within noise of the fastest); narrow short products 64 x 64. Otherwise each shape's time is estimated as
 // (rounds of resident workgroups) x (tile area per CU per round) / (efficiency), the
 // efficiencies -- 1.0, 1.3, 0.8 and 0.3 for 256 x 128, 192 x 128, 128 x 64 and 64 x 64
 // -- fitted to timings of every shape on MI355X over 25 ViT-B/L/H products (M x N x K
@@ -778,6 +783,7 @@ enum class TileShape { t64x64, t128x64s2, t128x64, t192x128s2, t256x128, t64x128
 static TileShape pick_tile(int m, int n, int k, int align) {
   auto tiles = [&](int bm, int bn) { return (long)((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
   if (k >= 2048 && tiles(128, 64) <= 320 && align == 0) return TileShape::t64x128s4;
+  if (k >= 2048 && tiles(192, 128) <= 256 && align == 0) return TileShape::t192x128s3;
   // narrow short products (the ViT-B projection, 4096 x 768 x 768): 64 x 64 measured
   // fastest, by 7 % to 15 % depending on the epilogue
   if (n <= 768 && (double)m * n * k < 1e10) return TileShape::t64x64;
@@ -814,6 +820,7 @@ static hipError_t run(const bf16_t* a, const bf16_t* w, int m, int n, int k, con
     case TileShape::t64x64: return run_bf16<64, 64, 2>(a, w, m, n, k, e, st);
     case TileShape::t128x64s2: return run_bf16<128, 64, 2>(a, w, m, n, k, e, st);
     case TileShape::t64x128s4: return run_bf16<64, 128, 4>(a, w, m, n, k, e, st);
+    case TileShape::t192x128s3: return run_bf16<192, 128, 3>(a, w, m, n, k, e, st);
     default: return run_bf16<128, 64, 6>(a, w, m, n, k, e, st);
   }
 }
