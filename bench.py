@@ -119,10 +119,9 @@ class Workload:
         self.np = np
 
     def step(self):
-        ss = self.ss
-        ss.importance(self.img, self.cfg.patch, out=self.imp)
-        ss.permute(self.plan, self.imp, out=(self.perm, self.inv, self.routed))
-        ss.block(self.plan, self.w, self.x, self.perm, self.routed, workspace=self.ws)
+        """Importance, permutation and block: one sparsesam_forward call."""
+        self.ss.forward(self.plan, self.w, self.img, self.x, self.cfg.patch,
+                        out=(self.imp, self.perm, self.inv, self.routed), workspace=self.ws)
 
     def attn_operands(self, seed=1):
         """Random q, k, vt and an output buffer in the layout sparsesam_attn takes."""

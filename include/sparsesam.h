@@ -339,6 +339,23 @@ sparsesam_status sparsesam_block(sparsesam_plan_t plan, const sparsesam_block_we
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * (5d) The whole hot path of one block step: importance (1) of img [batch, height, width]
+ * fp32 into imp, the permutation (2) into perm / inv / routed, then the block (5) in place
+ * on x -- the three calls in one, with the same results bit for bit. ("Technische
+ * Samenvatting: SparseSAM", Methodologie: importance-guided reordering ahead of the
+ * block's attention and MLP.) height = grid_h * patch, width = grid_w * patch. Where the
+ * ranking runs one wavefront per slot (bf16 plans with more than 3840 tokens per segment
+ * and C = 768, 1024 or 1280: the ViT global grids), the permutation kernel also writes
+ * the block's first LayerNorm rows, so the block skips its gather launch.
+ * All pointers are device pointers; workspace as in (5). Plans with routing = UPDATE are
+ * rejected (INVALID_ARGUMENT); other validation as in (1), (2) and (5).
+ */
+sparsesam_status sparsesam_forward(sparsesam_plan_t plan, const sparsesam_block_weights* weights /* host */,
+                                   const float* img, int32_t batch, int32_t height, int32_t width, int32_t patch,
+                                   float* x, float* imp, int32_t* perm, int32_t* inv, int32_t* routed,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * (5c) One block of a plan with routing = SPARSESAM_ROUTE_UPDATE: as (5), except that after
  * the attention sub-block (x1 = x + o W_proj^T + b_proj) each segment's keep-set is the K
  * tokens with the largest ||x1[t] - x[t]||^2, chosen as by (4b), and the MLP (and the merge,

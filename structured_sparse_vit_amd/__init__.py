@@ -8,6 +8,7 @@ stream. If the library is not built, every call raises.
     imp = importance(img)                     # [b, H, W] fp32 -> [b, tokens]
     perm, inv, routed = permute(plan, imp)    # stripe-sort + keep-set
     block(plan, weights, x, perm, routed)     # one encoder block, in place on x
+    forward(plan, weights, img, x)            # importance + permute + block in one call
     encoder(plan_g, plan_w, layers, kinds, x, perms)   # a stack of blocks, in place on x
 """
 import ctypes
@@ -17,8 +18,9 @@ import torch
 from . import _lib
 from ._lib import SPARSESAM_BF16, SPARSESAM_F32, SparseSAMError, check
 
-__all__ = ["Plan", "importance", "permute", "attn", "mlp", "block", "block_noalloc", "noalloc_scratch_bytes",
-           "route_topk", "block_dynamic", "encoder", "SparseSAMError", "library_path", "weights_to_device"]
+__all__ = ["Plan", "importance", "permute", "attn", "mlp", "block", "forward", "block_noalloc",
+           "noalloc_scratch_bytes", "route_topk", "block_dynamic", "encoder", "SparseSAMError", "library_path",
+           "weights_to_device"]
 
 
 def library_path() -> str:
@@ -301,6 +303,36 @@ def block(plan, weights, x, perm, routed, workspace=None):
     check(lib.sparsesam_block(plan.handle, ctypes.byref(bw), _ptr(x), b, _ptr(perm), _ptr(routed), _ptr(ws),
                               ws.numel(), _stream(x.device)), "sparsesam_block")
     return x
+
+
+def forward(plan, weights, img, x, patch=16, out=None, workspace=None):
+    """The whole step of one block: importance of img [batch, H, W] fp32, the permutation,
+    then the block in place on x [batch, grid_h, grid_w, C] -- importance(), permute() and
+    block() in one call, bit for bit. Returns (imp, perm, inv, routed)."""
+    lib = _lib.load()
+    _need(img, "img", torch.float32, device=plan.device)
+    if img.dim() != 3:
+        raise ValueError("img must be [batch, height, width]")
+    b, H, W = img.shape
+    tokens = plan.desc.grid_h * plan.desc.grid_w
+    n, segs, rpi = plan.info["seq_len"], plan.info["segments_per_image"], plan.info["routed_per_image"]
+    if out is None:
+        imp = torch.empty(b, tokens, dtype=torch.float32, device=img.device)
+        perm = torch.empty(b * segs, n, dtype=torch.int32, device=img.device)
+        inv = torch.empty_like(perm)
+        routed = torch.empty(b * rpi, dtype=torch.int32, device=img.device)
+    else:
+        imp, perm, inv, routed = out
+    _need(imp, "imp", torch.float32, (b, tokens), plan.device)
+    _need(inv, "inv", torch.int32, (b * segs, n), plan.device)
+    bx, bw = _block_args(plan, weights, x, perm, routed)
+    if bx != b:
+        raise ValueError("img and x must hold the same number of images")
+    ws = _workspace(plan.info["block_workspace_bytes"], x.device, workspace)
+    check(lib.sparsesam_forward(plan.handle, ctypes.byref(bw), _ptr(img), b, H, W, patch, _ptr(x), _ptr(imp),
+                                _ptr(perm), _ptr(inv), _ptr(routed), _ptr(ws), ws.numel(), _stream(x.device)),
+          "sparsesam_forward")
+    return imp, perm, inv, routed
 
 
 def route_topk(plan, score, out=None):

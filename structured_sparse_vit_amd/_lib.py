@@ -34,6 +34,7 @@ EXPORTS = [
     "sparsesam_attn_relpos",
     "sparsesam_mlp",
     "sparsesam_block",
+    "sparsesam_forward",
     "sparsesam_encoder",
     "sparsesam_noalloc_scratch_bytes",
     "sparsesam_block_noalloc",
@@ -104,6 +105,7 @@ def load():
         "sparsesam_attn_relpos": ([P, I32, P, P, P, P, F32, P, P, P, P, SZ, P], I32),
         "sparsesam_mlp": ([P, P, I64, P, I32, P, P, P, P, P, P, P, SZ, P], I32),
         "sparsesam_block": ([P, ctypes.POINTER(BlockWeights), P, I32, P, P, P, SZ, P], I32),
+        "sparsesam_forward": ([P, ctypes.POINTER(BlockWeights), P, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P], I32),
         "sparsesam_encoder": ([P, P, ctypes.POINTER(BlockWeights), P, I32, P, I32, P, P, P, P, P, SZ, P], I32),
         "sparsesam_noalloc_scratch_bytes": ([], SZ),
         "sparsesam_block_noalloc": ([P, ctypes.POINTER(BlockWeights), P, I32, P, P, P], I32),

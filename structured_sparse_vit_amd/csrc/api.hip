@@ -631,9 +631,11 @@ sparsesam_status sparsesam_mlp(sparsesam_plan_t p, float* x, int64_t rows, const
 // N, C], pads included) instead of raster order; the block then reads and writes its
 // rows in place and its keep-set is the plan's static list of keep-set positions.
 template <typename T>
+// ln1_ready: the first LayerNorm's rows are already in the workspace (written by the
+// fused permutation of sparsesam_forward).
 static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weights& w, float* x, int batch,
                             const int32_t* perm, int32_t* routed, float* score_out, char* ws, hipStream_t st,
-                            bool stream_sorted = false) {
+                            bool stream_sorted = false, bool ln1_ready = false) {
   BlockLayout L = block_layout(p, batch);
   const int segs = batch * p.segs_per_img;
   const int M = segs * p.n;
@@ -646,7 +648,8 @@ static hipError_t run_block(const sparsesam_plan& p, const sparsesam_block_weigh
   const long long x_rows = stream_sorted ? (long long)M : (long long)batch * p.desc.grid_h * p.desc.grid_w;
   const int32_t* row_perm = stream_sorted ? nullptr : perm;  // null: rows in place
   if (stream_sorted) routed = const_cast<int32_t*>(p.d_keep_pos);
-  hipError_t e = launch_gather_ln<T>(p, x, (int)x_rows, M, row_perm, nullptr, w.ln1_g, w.ln1_b, h, st);
+  hipError_t e = hipSuccess;
+  if (!ln1_ready) e = launch_gather_ln<T>(p, x, (int)x_rows, M, row_perm, nullptr, w.ln1_g, w.ln1_b, h, st);
   if (e != hipSuccess) return e;
   EpiQKV eq{w.b_qkv, q, k, vt, p.n, p.n_pad, p.desc.heads, p.desc.head_dim, C};
   e = launch_gemm_qkv<T>(h, (const T*)w.w_qkv, M, C, eq, st);
@@ -745,6 +748,37 @@ sparsesam_status sparsesam_block(sparsesam_plan_t p, const sparsesam_block_weigh
   if (st != SPARSESAM_OK) return st;
   // a static plan's block only reads the keep-set
   return block_impl(p, w, x, batch, perm, const_cast<int32_t*>(routed), nullptr, workspace, workspace_bytes, stream);
+}
+
+sparsesam_status sparsesam_forward(sparsesam_plan_t p, const sparsesam_block_weights* w, const float* img,
+                                   int32_t batch, int32_t height, int32_t width, int32_t patch, float* x, float* imp,
+                                   int32_t* perm, int32_t* inv, int32_t* routed, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  sparsesam_status st = static_plan(p, "sparsesam_forward");
+  if (st != SPARSESAM_OK) return st;
+  st = block_check(p, w, x, batch, perm, routed, workspace, workspace_bytes);
+  if (st != SPARSESAM_OK || batch == 0) return st;
+  if (!img || !imp || !inv) return invalid("img, imp and inv must not be null");
+  if (patch < 1 || patch > 32) return unsupported("patch must be in [1, 32]");
+  if (height != p->desc.grid_h * patch || width != p->desc.grid_w * patch)
+    return invalid("height and width must be the plan's grid times patch");
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_importance(img, batch, height, width, patch, imp, s);
+  if (e != hipSuccess) return hip_fail(e, "sparsesam_forward importance launch");
+  const bool fused = permute_ln_fusable(*p);
+  if (fused) {
+    const BlockLayout L = block_layout(*p, batch);
+    e = launch_permute_ln(*p, imp, batch, perm, inv, routed, x, (long long)batch * p->desc.grid_h * p->desc.grid_w,
+                          w->ln1_g, w->ln1_b, reinterpret_cast<bf16_t*>((char*)workspace + L.h), s);
+  } else {
+    e = launch_permute(*p, imp, batch, perm, inv, routed, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "sparsesam_forward permutation launch");
+  if (p->desc.dtype == SPARSESAM_BF16)
+    e = run_block<bf16_t>(*p, *w, x, batch, perm, routed, nullptr, (char*)workspace, s, false, fused);
+  else
+    e = run_block<float>(*p, *w, x, batch, perm, routed, nullptr, (char*)workspace, s);
+  return e == hipSuccess ? SPARSESAM_OK : hip_fail(e, "sparsesam_forward block launch");
 }
 
 sparsesam_status sparsesam_block_dynamic(sparsesam_plan_t p, const sparsesam_block_weights* w, float* x,

@@ -148,4 +148,53 @@ struct SegmentMap {
   }
 };
 
+// One LayerNorm row of C = 256 NV fp32 channels held by a wavefront: lane l holds the
+// float4 chunks l + 64 i. load() issues the row's and the affine parameters' loads;
+// store() forms the fp32 statistics (two passes over the registers, biased variance, eps
+// 1e-6) and writes the normalised row as bf16. The gathered LayerNorm and the fused
+// permutation kernel both use it, so their rows are bit-identical.
+template <int NV>
+struct LnRow {
+  f32x4 v[NV], g[NV], b[NV];
+  __device__ __forceinline__ void load(const float* __restrict__ xrow, const float* __restrict__ gamma,
+                                       const float* __restrict__ beta, int lane) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      g[i] = *reinterpret_cast<const f32x4*>(gamma + 4 * (lane + 64 * i));
+      b[i] = *reinterpret_cast<const f32x4*>(beta + 4 * (lane + 64 * i));
+    }
+    const f32x4* xr = reinterpret_cast<const f32x4*>(xrow);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = xr[lane + 64 * i];
+  }
+  __device__ __forceinline__ void store(bf16_t* __restrict__ out, int lane) const {
+    constexpr int C = NV * 256;
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    const float mean = wave_sum(s) * (1.0f / C);
+    float q = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = v[i][e] - mean;
+        q += d * d;
+      }
+    const float rstd = rsqrtf(wave_sum(q) * (1.0f / C) + 1e-6f);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = to_bf16((v[i][e] - mean) * rstd * g[i][e] + b[i][e]);
+      *reinterpret_cast<bf16x4*>(out + 4 * (lane + 64 * i)) = w;
+    }
+  }
+  // a zero row (window pads, rows outside x)
+  static __device__ __forceinline__ void zero(bf16_t* __restrict__ out, int lane) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) *reinterpret_cast<bf16x4*>(out + 4 * (lane + 64 * i)) = bf16x4{};
+  }
+};
+
 }  // namespace sparsesam

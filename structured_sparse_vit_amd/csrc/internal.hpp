@@ -130,6 +130,13 @@ hipError_t launch_importance(const float* img, int batch, int height, int width,
                              hipStream_t st);
 hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
                           hipStream_t st);
+// The permutation plus the block's first LayerNorm (bf16 rows in stripe-sorted order,
+// the rows launch_gather_ln writes through perm), for plans where the ranking runs one
+// wavefront per slot (bf16, N > 3840 tokens per segment, C = 768, 1024 or 1280).
+bool permute_ln_fusable(const sparsesam_plan& p);
+hipError_t launch_permute_ln(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
+                             const float* x, long long x_rows, const float* gamma, const float* beta, bf16_t* out,
+                             hipStream_t st);
 // Keep-set of every segment by score (descending, ties to the lower slot, pads last):
 // score [batch, tokens, parts] partial sums added in order; score_out (optional)
 // receives each token's summed score.

@@ -1220,17 +1220,18 @@ __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, 
     for (int j = 0; j < kl; ++j) {
       const int kj = k0 + j;
       const T* kr = Kt + (sh * n + kj) * D;
-      float sc = 0.0f;
+      // four independent partial sums (channels d mod 4), added in a fixed order
+      float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int d = 0; d < D; ++d) sc = fmaf(qv[d], (float)kr[d], sc);
-      sc *= c_log2;
+      for (int d = 0; d < D; ++d) s4[d & 3] = fmaf(qv[d], (float)kr[d], s4[d & 3]);
+      float sc = ((s4[0] + s4[1]) + (s4[2] + s4[3])) * c_log2;
       if constexpr (REL) {
         const int kc = rel_kc[(size_t)seg * n + kj];
         sc += trow[kc & 0xffff] + trow[kc >> 16];
       }
       const float m_new = fmaxf(m_run, sc);
-      const float alpha = exp2f(m_run - m_new);
-      const float p = exp2f(sc - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float p = __builtin_amdgcn_exp2f(sc - m_new);
       l_run = l_run * alpha + p;
       m_run = m_new;
 #pragma unroll

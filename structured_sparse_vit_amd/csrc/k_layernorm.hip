@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(256) gather_ln_kernel(const float* __restrict_
 }
 
 // Vector form for bf16 output and C a multiple of 256: each lane holds NV float4 chunks
-// (16-byte loads) and writes four bf16 per chunk (8-byte stores).
+// (16-byte loads) and writes four bf16 per chunk (8-byte stores), through LnRow.
 template <int NV>
 __global__ void __launch_bounds__(256) gather_ln_vec_kernel(const float* __restrict__ x, int x_rows, int rows_out,
                                                             const int* __restrict__ perm,
@@ -81,44 +81,12 @@ __global__ void __launch_bounds__(256) gather_ln_vec_kernel(const float* __restr
   }
   bf16_t* o = out + (size_t)r * C;
   if (src < 0 || src >= x_rows) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) *reinterpret_cast<bf16x4*>(o + 4 * (lane + 64 * i)) = bf16x4{};
+    LnRow<NV>::zero(o, lane);
     return;
   }
-  // gamma and beta are requested with the row, not after the reductions, so their
-  // latency overlaps the row's
-  f32x4 gg[NV], bb[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    gg[i] = *reinterpret_cast<const f32x4*>(g + 4 * (lane + 64 * i));
-    bb[i] = *reinterpret_cast<const f32x4*>(b + 4 * (lane + 64 * i));
-  }
-  const f32x4* xr = reinterpret_cast<const f32x4*>(x + (size_t)src * C);
-  f32x4 v[NV];
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    v[i] = xr[lane + 64 * i];
-    s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
-  }
-  const float mean = wave_sum(s) * (1.0f / C);
-  float q = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float d = v[i][e] - mean;
-      q += d * d;
-    }
-  const float rstd = rsqrtf(wave_sum(q) * (1.0f / C) + 1e-6f);
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c = 4 * (lane + 64 * i);
-    bf16x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = to_bf16((v[i][e] - mean) * rstd * gg[i][e] + bb[i][e]);
-    *reinterpret_cast<bf16x4*>(o + c) = w;
-  }
+  LnRow<NV> row;
+  row.load(x + (size_t)src * C, g, b, lane);
+  row.store(o, lane);
 }
 
 template <typename T>

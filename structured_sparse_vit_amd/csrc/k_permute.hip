@@ -99,8 +99,23 @@ __device__ __forceinline__ uint32_t random_key(uint32_t seed, uint32_t slot) {
 // 16-byte read brings two keys. Lane l of a wavefront serves slot l % tpw and key pair
 // residue class l / tpw (mod 64 / tpw); wavefront w takes the w-th share of the keys.
 // For N = 4096 that is 256 workgroups of 16 wavefronts, every lane comparing 64 keys.
+//
+// NV > 0 (one wavefront per slot: tpw == kw == 16) also writes the block's first
+// LayerNorm: wavefront w loads the token row of slot chunk * 16 + w (C = 256 NV
+// channels) before the keys are formed, and once the slot's stripe-sorted position p is
+// known writes LayerNorm(row) as bf16 to ln_out[seg * n + p] -- the rows the gathered
+// LayerNorm would write through perm, bit for bit (the same LnRow code).
 constexpr int kMaxRankWaves = 16;
 
+struct RankLn {
+  const float* x = nullptr;
+  long long x_rows = 0;
+  const float* gamma = nullptr;
+  const float* beta = nullptr;
+  bf16_t* out = nullptr;
+};
+
+template <int NV>
 __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* __restrict__ imp, SegmentMap map,
                                                                   int n, int stripes, int chunks, int tpw,
                                                                   const int* __restrict__ seg_k,
@@ -109,14 +124,24 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
                                                                   int* __restrict__ inv, int* __restrict__ routed,
                                                                   int ordering, uint32_t seed, int seg_w,
                                                                   int hilbert_side, int parts,
-                                                                  float* __restrict__ score_out) {
+                                                                  float* __restrict__ score_out, RankLn ln) {
   extern __shared__ __attribute__((aligned(16))) uint64_t key_lds[];  // padded to a multiple of 64
   __shared__ int part[kMaxRankWaves * 64];
+  __shared__ int pos_lds[kMaxRankWaves];
   const int seg = blockIdx.x / chunks, chunk = blockIdx.x - (blockIdx.x / chunks) * chunks;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kw = blockDim.x >> 6;
   const int tokens = map.grid_h * map.grid_w;
   const int img = map.f_spi.div(seg);
+  // the LayerNorm row of this wavefront's slot, requested first
+  LnRow<(NV > 0 ? NV : 1)> lrow;
+  int ln_src = -1;
+  if constexpr (NV > 0) {
+    const int sl = chunk * tpw + wave;
+    ln_src = sl < n ? map.row_of(seg, sl) : -1;
+    if (ln_src >= ln.x_rows) ln_src = -1;
+    if (ln_src >= 0) lrow.load(ln.x + (size_t)ln_src * (NV * 256), ln.gamma, ln.beta, lane);
+  }
   const float* im = imp + (size_t)img * tokens * parts;
   // a token's key value: imp[token], or the in-order sum of its `parts` partials
   auto value = [&](int tok) {
@@ -209,6 +234,18 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
       }
       if (rank < seg_k[w_img])  // K <= real slots, so never a pad
         routed[(size_t)img * routed_per_image + seg_off[w_img] + rank] = map.row_of(seg, sl);
+      if constexpr (NV > 0) pos_lds[tid] = p;
+    }
+  }
+  if constexpr (NV > 0) {
+    __syncthreads();  // every slot's position is in pos_lds
+    const int sl = chunk * tpw + wave;
+    if (sl < n) {
+      bf16_t* o = ln.out + ((size_t)seg * n + pos_lds[wave]) * (NV * 256);
+      if (ln_src >= 0)
+        lrow.store(o, lane);
+      else
+        LnRow<NV>::zero(o, lane);
     }
   }
 }
@@ -216,7 +253,7 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
 size_t permute_lds_bytes(const sparsesam_plan& p) { return (size_t)((p.n + 63) & ~63) * 8; }
 
 static hipError_t launch_rank(const sparsesam_plan& p, const float* imp, int parts, int batch, int* perm, int* inv,
-                              int* routed, float* score_out, int ordering, hipStream_t st) {
+                              int* routed, float* score_out, int ordering, hipStream_t st, RankLn ln = RankLn{}) {
   // long segments: 16 slots per workgroup and up to 16 wavefronts splitting the keys;
   // short ones (windows): 64 slots per workgroup, one wavefront per 256 keys
   const int tpw = p.n >= 1024 ? 16 : 64;
@@ -224,7 +261,11 @@ static hipError_t launch_rank(const sparsesam_plan& p, const float* imp, int par
   const int chunks = (p.n + tpw - 1) / tpw;
   const int segs = batch * p.segs_per_img;
   const size_t key_bytes = permute_lds_bytes(p);
-  hipError_t e = hipFuncSetAttribute((const void*)rank_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+  const int nv = ln.out ? p.desc.channels / 256 : 0;
+  if (ln.out && (tpw != 16 || kw != 16 || p.desc.channels % 256 != 0 || nv < 3 || nv > 5))
+    return hipErrorInvalidValue;
+  auto kern = nv == 3 ? rank_kernel<3> : nv == 4 ? rank_kernel<4> : nv == 5 ? rank_kernel<5> : rank_kernel<0>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)key_bytes);
   if (e != hipSuccess) return e;
   // segment shape for the position-based orders: the grid, or one window
@@ -232,15 +273,35 @@ static hipError_t launch_rank(const sparsesam_plan& p, const float* imp, int par
   const int seg_w = p.desc.window ? p.desc.window : p.desc.grid_w;
   int side = 1;
   while (side < std::max(seg_h, seg_w)) side *= 2;
-  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)(segs * chunks)), dim3(64 * kw), key_bytes, st, imp, p.segmap(),
-                     p.n, p.desc.stripes, chunks, tpw, p.d_seg_k, p.d_seg_off, p.routed_per_image, perm, inv, routed,
-                     ordering, p.desc.order_seed, seg_w, side, parts, score_out);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(segs * chunks)), dim3(64 * kw), key_bytes, st, imp, p.segmap(), p.n,
+                     p.desc.stripes, chunks, tpw, p.d_seg_k, p.d_seg_off, p.routed_per_image, perm, inv, routed,
+                     ordering, p.desc.order_seed, seg_w, side, parts, score_out, ln);
   return hipGetLastError();
 }
 
 hipError_t launch_permute(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
                           hipStream_t st) {
   return launch_rank(p, imp, 1, batch, perm, inv, routed, nullptr, (int)p.desc.ordering, st);
+}
+
+bool permute_ln_fusable(const sparsesam_plan& p) {
+  const int tpw = p.n >= 1024 ? 16 : 64;
+  const int kw = std::max(1, std::min(kMaxRankWaves, (p.n + 255) / 256));
+  const int nv = p.desc.channels / 256;
+  return p.desc.dtype == SPARSESAM_BF16 && tpw == 16 && kw == 16 && p.desc.channels % 256 == 0 && nv >= 3 &&
+         nv <= 5;
+}
+
+hipError_t launch_permute_ln(const sparsesam_plan& p, const float* imp, int batch, int* perm, int* inv, int* routed,
+                             const float* x, long long x_rows, const float* gamma, const float* beta, bf16_t* out,
+                             hipStream_t st) {
+  RankLn ln;
+  ln.x = x;
+  ln.x_rows = x_rows;
+  ln.gamma = gamma;
+  ln.beta = beta;
+  ln.out = out;
+  return launch_rank(p, imp, 1, batch, perm, inv, routed, nullptr, (int)p.desc.ordering, st, ln);
 }
 
 hipError_t launch_route_topk(const sparsesam_plan& p, const float* score, int parts, int batch, int* routed,

@@ -334,6 +334,30 @@ def test_block_parity(key):
     _check_block(key, _run_block(key), 1.0)
 
 
+@pytest.mark.parametrize("key", ["c2", "c4g", "c5g", "c3", "c1", "c2:zorder"])
+def test_forward_equals_the_three_calls(key):
+    """sparsesam_forward (importance, permutation and block in one call; on the ViT global
+    grids the permutation kernel also writes the block's first LayerNorm rows) against
+    sparsesam_importance + sparsesam_permute + sparsesam_block on the same inputs: every
+    output bit for bit."""
+    from synth import block_weights, token_features
+    _say("forward", key)
+    cfg = config(key)
+    plan = _plan(cfg)
+    img = torch.from_numpy(images(key.split(":")[0])).to(DEV)
+    x0 = torch.from_numpy(token_features(cfg, 0)).to(DEV)
+    w = ss.weights_to_device(block_weights(cfg, 0), plan)
+    imp = ss.importance(img, cfg.patch)
+    perm, inv, routed = ss.permute(plan, imp)
+    x1 = x0.clone()
+    ss.block(plan, w, x1, perm, routed)
+    x2 = x0.clone()
+    imp2, perm2, inv2, routed2 = ss.forward(plan, w, img, x2, patch=cfg.patch)
+    assert torch.equal(imp.view(torch.int32), imp2.view(torch.int32))
+    assert torch.equal(perm, perm2) and torch.equal(inv, inv2) and torch.equal(routed, routed2)
+    assert torch.equal(x1.view(torch.int32), x2.view(torch.int32)), "block output of %s" % key
+
+
 @pytest.mark.parametrize("key,gain", [("c1", 10.0), ("c2", 3.0), ("c3b1", 3.0), ("ragged", 3.0)])
 def test_block_parity_high_gain(key, gain):
     """Projection weights scaled up: the attention and MLP branches dominate the residual.

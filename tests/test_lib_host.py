@@ -309,8 +309,8 @@ def test_routing_and_merge_plan_validation_and_workspace():
 
 def test_routing_entry_points_check_the_plan_kind_first():
     """Block calls check the plan's routing before anything else (so without a GPU too):
-    sparsesam_block rejects dynamic plans, sparsesam_block_dynamic static ones, and the
-    encoder does not take dynamic plans."""
+    sparsesam_block and sparsesam_forward reject dynamic plans, sparsesam_block_dynamic
+    static ones, and the encoder does not take dynamic plans."""
     lib = _lib.load()
     dyn, sta = _create(routing="update"), _create()
     w = _lib.BlockWeights()
@@ -318,6 +318,9 @@ def test_routing_entry_points_check_the_plan_kind_first():
     assert lib.sparsesam_block(dyn.handle, ctypes.byref(w), p, 1, p, p, p, 1 << 30, None) == 1
     assert b"sparsesam_block_dynamic" in lib.sparsesam_last_error()
     assert lib.sparsesam_block_dynamic(sta.handle, ctypes.byref(w), p, 1, p, p, None, p, 1 << 30, None) == 1
+    assert lib.sparsesam_forward(dyn.handle, ctypes.byref(w), p, 1, 1024, 1024, 16, p, p, p, p, p, p, 1 << 30,
+                                 None) == 1
+    assert b"sparsesam_block_dynamic" in lib.sparsesam_last_error()
     assert lib.sparsesam_block_noalloc(dyn.handle, ctypes.byref(w), p, 1, p, p, None) in (1, 6)
     layers = (_lib.BlockWeights * 1)()
     karr = (ctypes.c_uint8 * 1)(1)
