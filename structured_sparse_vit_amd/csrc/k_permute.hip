@@ -102,7 +102,7 @@ __device__ __forceinline__ uint32_t random_key(uint32_t seed, uint32_t slot) {
 //
 // NV > 0 (one wavefront per slot: tpw == kw == 16) also writes the block's first
 // LayerNorm: wavefront w loads the token row of slot chunk * 16 + w (C = 256 NV
-// channels) before the keys are formed, and once the slot's stripe-sorted position p is
+// channels) while the keys are ranked, and once the slot's stripe-sorted position p is
 // known writes LayerNorm(row) as bf16 to ln_out[seg * n + p] -- the rows the gathered
 // LayerNorm would write through perm, bit for bit (the same LnRow code).
 constexpr int kMaxRankWaves = 16;
@@ -133,15 +133,6 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
   const int kw = blockDim.x >> 6;
   const int tokens = map.grid_h * map.grid_w;
   const int img = map.f_spi.div(seg);
-  // the LayerNorm row of this wavefront's slot, requested first
-  LnRow<(NV > 0 ? NV : 1)> lrow;
-  int ln_src = -1;
-  if constexpr (NV > 0) {
-    const int sl = chunk * tpw + wave;
-    ln_src = sl < n ? map.row_of(seg, sl) : -1;
-    if (ln_src >= ln.x_rows) ln_src = -1;
-    if (ln_src >= 0) lrow.load(ln.x + (size_t)ln_src * (NV * 256), ln.gamma, ln.beta, lane);
-  }
   const float* im = imp + (size_t)img * tokens * parts;
   // a token's key value: imp[token], or the in-order sum of its `parts` partials
   auto value = [&](int tok) {
@@ -189,6 +180,16 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
       key_lds[s] = ((uint64_t)k << 32) | (uint32_t)s;
     }
   }
+  // the LayerNorm row of this wavefront's slot, requested after the fill's importance
+  // loads (loads retire in order), so that it arrives during the LDS-only ranking loop
+  LnRow<(NV > 0 ? NV : 1)> lrow;
+  int ln_src = -1;
+  if constexpr (NV > 0) {
+    const int sl = chunk * tpw + wave;
+    ln_src = sl < n ? map.row_of(seg, sl) : -1;
+    if (ln_src >= ln.x_rows) ln_src = -1;
+    if (ln_src >= 0) lrow.load(ln.x + (size_t)ln_src * (NV * 256), ln.gamma, ln.beta, lane);
+  }
   __syncthreads();
   const int subs = 64 / tpw;  // lanes per slot
   const int slot = chunk * tpw + (lane % tpw);
@@ -214,31 +215,35 @@ __global__ void __launch_bounds__(64 * kMaxRankWaves) rank_kernel(const float* _
   for (int o = tpw; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
   if (lane < tpw) part[wave * 64 + lane] = cnt;
   __syncthreads();
-  if (tid < tpw) {
-    const int sl = chunk * tpw + tid;
-    if (sl < n) {
-      int rank = 0;
+  // slot chunk * tpw + tid's rank and stripe-sorted position (threads tid < tpw); with
+  // NV > 0 the positions are published first, so that the LayerNorm rows do not wait
+  // for the index writes
+  const int sl_me = chunk * tpw + tid;
+  const bool slot_thread = tid < tpw && sl_me < n;
+  int rank = 0, p = 0;
+  if (slot_thread) {
 #pragma unroll 4
-      for (int w = 0; w < kw; ++w) rank += part[w * 64 + tid];
-      const int S = n / stripes;
-      const int p = (rank % stripes) * S + rank / stripes;
-      const size_t base = (size_t)seg * n;
-      if (perm) {
-        perm[base + p] = sl;
-        inv[base + sl] = p;
-      }
-      const int w_img = seg - img * map.segs_per_img;
-      if (score_out) {
-        const int row = map.row_of(seg, sl);
-        if (row >= 0) score_out[row] = value(row - img * tokens);
-      }
-      if (rank < seg_k[w_img])  // K <= real slots, so never a pad
-        routed[(size_t)img * routed_per_image + seg_off[w_img] + rank] = map.row_of(seg, sl);
-      if constexpr (NV > 0) pos_lds[tid] = p;
+    for (int w = 0; w < kw; ++w) rank += part[w * 64 + tid];
+    const int S = n / stripes;
+    p = (rank % stripes) * S + rank / stripes;
+    if constexpr (NV > 0) pos_lds[tid] = p;
+  }
+  if constexpr (NV > 0) __syncthreads();  // every slot's position is in pos_lds
+  if (slot_thread) {
+    const size_t base = (size_t)seg * n;
+    if (perm) {
+      perm[base + p] = sl_me;
+      inv[base + sl_me] = p;
     }
+    const int w_img = seg - img * map.segs_per_img;
+    if (score_out) {
+      const int row = map.row_of(seg, sl_me);
+      if (row >= 0) score_out[row] = value(row - img * tokens);
+    }
+    if (rank < seg_k[w_img])  // K <= real slots, so never a pad
+      routed[(size_t)img * routed_per_image + seg_off[w_img] + rank] = map.row_of(seg, sl_me);
   }
   if constexpr (NV > 0) {
-    __syncthreads();  // every slot's position is in pos_lds
     const int sl = chunk * tpw + wave;
     if (sl < n) {
       bf16_t* o = ln.out + ((size_t)seg * n + pos_lds[wave]) * (NV * 256);
