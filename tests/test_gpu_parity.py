@@ -334,19 +334,25 @@ def test_block_parity(key):
     _check_block(key, _run_block(key), 1.0)
 
 
-@pytest.mark.parametrize("key", ["c2", "c4g", "c5g", "c3", "c1", "c2:zorder"])
-def test_forward_equals_the_three_calls(key):
+@pytest.mark.parametrize("key,rel_pos", [("c2", False), ("c4g", False), ("c5g", False), ("c3", False),
+                                         ("c1", False), ("c2:zorder", False), ("c2", True), ("c3b1", True)])
+def test_forward_equals_the_three_calls(key, rel_pos):
     """sparsesam_forward (importance, permutation and block in one call; on the ViT global
     grids the permutation kernel also writes the block's first LayerNorm rows) against
     sparsesam_importance + sparsesam_permute + sparsesam_block on the same inputs: every
-    output bit for bit."""
+    output bit for bit, with and without the relative-position bias (whose tables read
+    the permutation the same call writes)."""
     from synth import block_weights, token_features
-    _say("forward", key)
+    from synth.generate import rel_pos_tables
+    _say("forward", key, "rel_pos" if rel_pos else "")
     cfg = config(key)
-    plan = _plan(cfg)
+    plan = ss.Plan.from_config(cfg, rel_pos=True) if rel_pos else _plan(cfg)
     img = torch.from_numpy(images(key.split(":")[0])).to(DEV)
     x0 = torch.from_numpy(token_features(cfg, 0)).to(DEV)
-    w = ss.weights_to_device(block_weights(cfg, 0), plan)
+    wh = block_weights(cfg, 0)
+    if rel_pos:
+        wh["rel_h"], wh["rel_w"] = rel_pos_tables(cfg, 0)
+    w = ss.weights_to_device(wh, plan)
     imp = ss.importance(img, cfg.patch)
     perm, inv, routed = ss.permute(plan, imp)
     x1 = x0.clone()
