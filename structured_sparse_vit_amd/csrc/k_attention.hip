@@ -1214,28 +1214,46 @@ __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, 
   }
   float m_run = -INFINITY, l_run = 0.0f;
   const float* trow = REL ? rel_t + (sh * n + qi) * (size_t)tj : nullptr;
+  // the V rows of a kept tile's keys (from the V^T columns), in chunks of up to 64 keys,
+  // staged in LDS by coalesced loads and read by every thread as 16-byte broadcasts; the
+  // K rows are read straight from global memory (uniform addresses: scalar loads, which
+  // measured faster here than LDS broadcasts)
+  __shared__ __attribute__((aligned(16))) float vs[64][D];
   for (int t = row_ptr[qt]; t < row_ptr[qt + 1]; ++t) {
     const int kt = col_idx[t];
     const int k0 = tile_start[kt], kl = tile_len[kt];
-    for (int j = 0; j < kl; ++j) {
-      const int kj = k0 + j;
-      const T* kr = Kt + (sh * n + kj) * D;
-      // four independent partial sums (channels d mod 4), added in a fixed order
-      float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int d = 0; d < D; ++d) s4[d & 3] = fmaf(qv[d], (float)kr[d], s4[d & 3]);
-      float sc = ((s4[0] + s4[1]) + (s4[2] + s4[3])) * c_log2;
-      if constexpr (REL) {
-        const int kc = rel_kc[(size_t)seg * n + kj];
-        sc += trow[kc & 0xffff] + trow[kc >> 16];
+    for (int c0 = 0; c0 < kl; c0 += 64) {
+      const int cl = min(64, kl - c0);
+      __syncthreads();  // the previous chunk has been read
+      for (int e = threadIdx.x; e < cl * D; e += 64) {
+        const int dv = e / cl, iv = e - (e / cl) * cl;
+        vs[iv][dv] = (float)VT[(sh * D + dv) * n_pad + k0 + c0 + iv];
       }
-      const float m_new = fmaxf(m_run, sc);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      const float p = __builtin_amdgcn_exp2f(sc - m_new);
-      l_run = l_run * alpha + p;
-      m_run = m_new;
+      __syncthreads();
+      for (int j = 0; j < cl; ++j) {
+        const int kj = k0 + c0 + j;
+        const T* kr = Kt + (sh * n + kj) * D;
+        float sc = 0.0f;
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, (float)VT[(sh * D + d) * n_pad + kj], acc[d] * alpha);
+        for (int d = 0; d < D; ++d) sc = fmaf(qv[d], (float)kr[d], sc);
+        sc *= c_log2;
+        if constexpr (REL) {
+          const int kc = rel_kc[(size_t)seg * n + kj];
+          sc += trow[kc & 0xffff] + trow[kc >> 16];
+        }
+        const float m_new = fmaxf(m_run, sc);
+        const float alpha = exp2f(m_run - m_new);
+        const float p = exp2f(sc - m_new);
+        l_run = l_run * alpha + p;
+        m_run = m_new;
+        const f32x4* vr = reinterpret_cast<const f32x4*>(&vs[j][0]);
+#pragma unroll
+        for (int d4 = 0; d4 < D / 4; ++d4) {
+          const f32x4 v4 = vr[d4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * d4 + e] = fmaf(p, v4[e], acc[4 * d4 + e] * alpha);
+        }
+      }
     }
   }
   if (!active) return;
