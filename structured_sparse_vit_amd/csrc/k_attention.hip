@@ -24,12 +24,13 @@
 //  * attn_d80_kernel: the same work items for head_dim 80 (running max with a 2^8
 //    slack, denominators from a ones row of the third V^T block).
 //  * attn_short_kernel: short segments (windows, N <= 256), one workgroup per
-//    (segment, head) with the segment's K and V^T in LDS.
+//    (segment, head) with the segment's K and V^T in LDS; the static mask is one or
+//    two extra MFMA k-steps over key classes.
 //  * attn_combine_kernel: merges the partial results of rows split over several
 //    work items (none at ViT sizes).
 //  * attn_simt_kernel (fp32 or bf16 storage, any pattern and head_dim <= 128): one
-//    thread per query, keys read through the cache; the exact path for small
-//    configs.
+//    thread per query, K rows read through the scalar cache and V rows staged in LDS;
+//    the exact path for small configs.
 #include <algorithm>
 
 #include "internal.hpp"
@@ -922,11 +923,11 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
 
 // ---------------------------------------------------------------- short segments (windows)
 
-// Segments of at most 256 tokens (the 14 x 14 windows): one 256-thread workgroup per
+// Segments of at most 256 tokens (the 14 x 14 windows): one 512-thread workgroup per
 // (segment, head) holds the segment's whole K and V^T in LDS (keys past n zero) and
-// each wavefront takes 32-query blocks. The pattern's blocks (16 tokens, ragged at
-// stripe ends) do not align with 32-token MFMA blocks, so each (query, 32-key block)
-// applies the plan's kept-key bit mask -- static, from the plan -- and 32 x 32 blocks
+// wavefront w takes the 32-query block w. The pattern's blocks (16 tokens, ragged at
+// stripe ends) do not align with 32-token MFMA blocks, so each 32 x 32 block is computed
+// whole and masked by the plan's static mask (added on the matrix cores, below); blocks
 // without any kept pair are skipped. S^T = K Q^T and O^T = V^T P^T on
 // v_mfma_f32_32x32x16_bf16 as in the long-segment kernel; head_dim 80 runs V^T as
 // three 32-row blocks with rows 80..95 zero in registers.
