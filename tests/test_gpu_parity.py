@@ -364,6 +364,40 @@ def test_forward_equals_the_three_calls(key, rel_pos):
     assert torch.equal(x1.view(torch.int32), x2.view(torch.int32)), "block output of %s" % key
 
 
+def test_forward_argument_checks():
+    """sparsesam_forward rejects an image whose size is not the plan's grid times the
+    patch, a null inv and a dynamic plan, before any launch (x is left untouched)."""
+    import ctypes
+    from synth import block_weights, token_features
+    from structured_sparse_vit_amd import _lib
+    cfg = config("c1")
+    plan = _plan(cfg)
+    w = ss.weights_to_device(block_weights(cfg, 0), plan)
+    img = torch.from_numpy(images("c1")).to(DEV)
+    x = torch.from_numpy(token_features(cfg, 0)).to(DEV)
+    x0 = x.clone()
+    imp = torch.empty(cfg.batch, cfg.grid * cfg.grid, dtype=torch.float32, device=DEV)
+    n, rpi = plan.info["seq_len"], plan.info["routed_per_image"]
+    perm = torch.empty(cfg.batch, n, dtype=torch.int32, device=DEV)
+    inv = torch.empty_like(perm)
+    routed = torch.empty(cfg.batch * rpi, dtype=torch.int32, device=DEV)
+    ws = torch.empty(plan.info["block_workspace_bytes"], dtype=torch.uint8, device=DEV)
+    bw = ss._block_weights(plan, w)
+    lib = _lib.load()
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    H, W = img.shape[1], img.shape[2]
+    call = lambda plan_h, h, inv_t: lib.sparsesam_forward(plan_h, ctypes.byref(bw), P(img), cfg.batch, h, W,
+                                                          cfg.patch, P(x), P(imp), P(perm), P(inv_t), P(routed),
+                                                          P(ws), ws.numel(), None)
+    assert call(plan.handle, H + cfg.patch, inv) == 1  # height is not grid_h * patch
+    assert call(plan.handle, H, None) == 1             # inv missing
+    dyn = ss.Plan.from_config(cfg.with_(routing="update"))
+    assert call(dyn.handle, H, inv) == 1               # the plan chooses its keep-set per block
+    torch.cuda.synchronize()
+    assert torch.equal(x, x0)
+    assert call(plan.handle, H, inv) == 0
+
+
 @pytest.mark.parametrize("key,gain", [("c1", 10.0), ("c2", 3.0), ("c3b1", 3.0), ("ragged", 3.0)])
 def test_block_parity_high_gain(key, gain):
     """Projection weights scaled up: the attention and MLP branches dominate the residual.
