@@ -28,9 +28,10 @@
 //    two extra MFMA k-steps over key classes.
 //  * attn_combine_kernel: merges the partial results of rows split over several
 //    work items (none at ViT sizes).
-//  * attn_simt_kernel (fp32 or bf16 storage, any pattern and head_dim <= 128): one
-//    thread per query, K rows read through the scalar cache and V rows staged in LDS;
-//    the exact path for small configs.
+//  * attn_simt_kernel (fp32 or bf16 storage, any pattern and head_dim <= 128): one to
+//    four threads per query (each a share of the keys, merged at the end), K rows read
+//    through the scalar cache and V rows staged in LDS; the exact path for small
+//    configs.
 #include <algorithm>
 
 #include "internal.hpp"
@@ -1203,14 +1204,17 @@ __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, 
                                                        const int* __restrict__ col_idx,
                                                        const int* __restrict__ tile_start,
                                                        const int* __restrict__ tile_len, int n, int n_pad, int heads,
-                                                       int chunks, float c_log2, const float* __restrict__ rel_t,
+                                                       int chunks, int qpw, float c_log2, const float* __restrict__ rel_t,
                                                        const int* __restrict__ rel_kc, int tj) {
   const int qt = blockIdx.x / chunks, chunk = blockIdx.x - (blockIdx.x / chunks) * chunks;
   const int h = blockIdx.y, seg = blockIdx.z;
   const int len = tile_len[qt];
   const size_t sh = (size_t)seg * heads + h;
   float qv[D], acc[D];
-  const int local = chunk * 64 + threadIdx.x;
+  // qpw queries per workgroup (64, 32 or 16), each served by kpar = 64 / qpw threads that
+  // take every kpar-th key and merge their softmax states at the end
+  const int kpar = 64 / qpw, part = threadIdx.x / qpw;
+  const int local = chunk * qpw + (threadIdx.x - part * qpw);
   const bool active = local < len;
   const int qi = tile_start[qt] + (active ? local : 0);
 #pragma unroll
@@ -1236,7 +1240,7 @@ __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, 
         vs[iv][dv] = (float)VT[(sh * D + dv) * n_pad + k0 + c0 + iv];
       }
       __syncthreads();
-      for (int j = 0; j < cl; ++j) {
+      for (int j = part; j < cl; j += kpar) {
         const int kj = k0 + c0 + j;
         const T* kr = Kt + (sh * n + kj) * D;
         float sc = 0.0f;
@@ -1262,7 +1266,19 @@ __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, 
       }
     }
   }
-  if (!active) return;
+  // merge the kpar partial states of a query (lanes q, q + qpw, ...) in a fixed
+  // butterfly order; a part that saw no key (m = -inf) carries weight 0
+  for (int o = qpw; o < 64; o <<= 1) {
+    const float m_o = __shfl_xor(m_run, o, 64), l_o = __shfl_xor(l_run, o, 64);
+    const float mm = fmaxf(m_run, m_o);
+    const float a0 = m_run == -INFINITY ? 0.0f : exp2f(m_run - mm);
+    const float a1 = m_o == -INFINITY ? 0.0f : exp2f(m_o - mm);
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = acc[d] * a0 + __shfl_xor(acc[d], o, 64) * a1;
+    l_run = l_run * a0 + l_o * a1;
+    m_run = mm;
+  }
+  if (!active || part != 0) return;
   T* orow = O + ((size_t)seg * n + qi) * ((size_t)heads * D) + (size_t)h * D;
   const float inv_l = 1.0f / l_run;
 #pragma unroll
@@ -1295,10 +1311,13 @@ size_t attn_partial_bytes(const sparsesam_plan& p, int segments) {
 template <typename T, int D, bool REL = false>
 static hipError_t run_simt(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
                            float c_log2, hipStream_t st, const float* rel_t = nullptr, const int* rel_kc = nullptr) {
-  const int chunks = (p.desc.block + 63) / 64;
+  // queries per workgroup: 64, or the tile length rounded up to 32 or 16, so that short
+  // tiles keep every thread busy with a share of the keys
+  const int qpw = p.desc.block >= 64 ? 64 : p.desc.block > 16 ? 32 : 16;
+  const int chunks = (p.desc.block + qpw - 1) / qpw;
   dim3 grid(p.tiles * chunks, p.desc.heads, segments);
   hipLaunchKernelGGL((attn_simt_kernel<T, D, REL>), grid, dim3(64), 0, st, q, k, vt, o, p.d_row_ptr, p.d_col_idx,
-                     p.d_tile_start, p.d_tile_len, p.n, p.n_pad, p.desc.heads, chunks, c_log2, rel_t, rel_kc,
+                     p.d_tile_start, p.d_tile_len, p.n, p.n_pad, p.desc.heads, chunks, qpw, c_log2, rel_t, rel_kc,
                      p.rel_tj);
   return hipGetLastError();
 }

@@ -692,13 +692,43 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
     }
     __syncthreads();
   }
+  if constexpr (std::is_same_v<Epi, ResidualAdd>) {
+    // the residual update: every current value requested before the first store (the
+    // stores could alias later loads, so elem() by elem() would serialise them)
+    long long off[4];
+    float cur[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int m = m0 + tr + 16 * i, n = n0 + tc + 16 * j;
-      if (m < M && n < N) epi.elem(m, n, acc[i][j]);
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + tr + 16 * i;
+      const int row = m < M ? epi.dst_row(m) : -1;
+      off[i] = (row < 0 || row >= epi.x_rows) ? -1 : (long long)row * epi.ldx;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + tc + 16 * j;
+        cur[i][j] = (off[i] >= 0 && n < N) ? epi.x[off[i] + n] : 0.0f;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + tr + 16 * i, n = n0 + tc + 16 * j;
+        if (m >= M || n >= N) continue;
+        const float u = acc[i][j] + epi.bias[n];
+        if (epi.upd) epi.upd[(size_t)m * epi.ldx + n] = u;
+        if (off[i] >= 0) epi.x[off[i] + n] = cur[i][j] + u;
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int m = m0 + tr + 16 * i, n = n0 + tc + 16 * j;
+        if (m < M && n < N) epi.elem(m, n, acc[i][j]);
+      }
+  }
   if constexpr (Epi::kRowSq) {
     // squared-update partial sums over the tile's 64 columns: each thread adds its four
     // columns in order, the 16 consecutive lanes of a row fold by xor shuffles, and lane
