@@ -29,9 +29,9 @@
 //  * attn_combine_kernel: merges the partial results of rows split over several
 //    work items (none at ViT sizes).
 //  * attn_simt_kernel (fp32 or bf16 storage, any pattern and head_dim <= 128): one to
-//    four threads per query (each a share of the keys, merged at the end), K rows read
-//    through the scalar cache and V rows staged in LDS; the exact path for small
-//    configs.
+//    sixteen threads per query (each a share of the keys, merged at the end), V rows
+//    staged in LDS, K rows read through the scalar cache when one thread serves a query
+//    and staged with V otherwise; the exact path for small configs.
 #include <algorithm>
 
 #include "internal.hpp"
@@ -1211,7 +1211,7 @@ __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, 
   const int len = tile_len[qt];
   const size_t sh = (size_t)seg * heads + h;
   float qv[D], acc[D];
-  // qpw queries per workgroup (64, 32 or 16), each served by kpar = 64 / qpw threads that
+  // qpw queries per workgroup (64, 32 or 4), each served by kpar = 64 / qpw threads that
   // take every kpar-th key and merge their softmax states at the end
   const int kpar = 64 / qpw, part = threadIdx.x / qpw;
   const int local = chunk * qpw + (threadIdx.x - part * qpw);
@@ -1224,28 +1224,76 @@ __global__ void __launch_bounds__(64) attn_simt_kernel(const T* __restrict__ Q, 
   }
   float m_run = -INFINITY, l_run = 0.0f;
   const float* trow = REL ? rel_t + (sh * n + qi) * (size_t)tj : nullptr;
-  // the V rows of a kept tile's keys (from the V^T columns), in chunks of up to 64 keys,
-  // staged in LDS by coalesced loads and read by every thread as 16-byte broadcasts; the
-  // K rows are read straight from global memory (uniform addresses: scalar loads, which
-  // measured faster here than LDS broadcasts)
-  __shared__ __attribute__((aligned(16))) float vs[64][D];
+  // The V rows of a kept tile's keys (from the V^T columns), in chunks of up to KCH keys,
+  // are staged in LDS and read by every thread as 16-byte broadcasts. With one thread
+  // per query (kpar = 1) every lane reads the same K row, so K comes straight from
+  // global memory (uniform addresses: scalar loads, which measured faster than LDS
+  // broadcasts); with several threads per query the lanes read kpar different rows, so
+  // the chunk's K rows are staged too. A thread issues 16 of its staging loads before it
+  // stores any (one round trip per 16 values; storing each value as it arrived cost a
+  // round trip per value).
+  constexpr int KCH = D <= 80 ? 64 : 32;  // keys per staged chunk (LDS: 2 KCH D floats)
+  __shared__ __attribute__((aligned(16))) float vs[KCH][D];
+  __shared__ __attribute__((aligned(16))) float ks[KCH][D];
+  const bool stage_k = kpar > 1;
   for (int t = row_ptr[qt]; t < row_ptr[qt + 1]; ++t) {
     const int kt = col_idx[t];
     const int k0 = tile_start[kt], kl = tile_len[kt];
-    for (int c0 = 0; c0 < kl; c0 += 64) {
-      const int cl = min(64, kl - c0);
+    for (int c0 = 0; c0 < kl; c0 += KCH) {
+      const int cl = min(KCH, kl - c0);
       __syncthreads();  // the previous chunk has been read
-      for (int e = threadIdx.x; e < cl * D; e += 64) {
-        const int dv = e / cl, iv = e - (e / cl) * cl;
-        vs[iv][dv] = (float)VT[(sh * D + dv) * n_pad + k0 + c0 + iv];
+      {
+        // V^T rows dv, columns k0 + c0 + iv: thread (g, iv) takes iv = t mod cl and
+        // channels g, g + G, ... (G = 64 / cl groups; coalesced along iv)
+        const int G = 64 / cl, iv = threadIdx.x % cl, g = threadIdx.x / cl;
+        if (g < G) {
+          const T* vcol = VT + sh * D * n_pad + k0 + c0 + iv;
+          for (int db = g; db < D; db += 16 * G) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+              const int dv = db + u * G;
+              v[u] = dv < D ? (float)vcol[(size_t)dv * n_pad] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+              if (db + u * G < D) vs[iv][db + u * G] = v[u];
+          }
+        }
+      }
+      if (stage_k) {
+        const T* kc = Kt + (sh * n + k0 + c0) * D;  // the chunk's K rows are contiguous
+        for (int eb = threadIdx.x; eb < cl * D; eb += 16 * 64) {
+          float v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) v[u] = eb + 64 * u < cl * D ? (float)kc[eb + 64 * u] : 0.0f;
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int e = eb + 64 * u;
+            if (e < cl * D) ks[e / D][e % D] = v[u];
+          }
+        }
       }
       __syncthreads();
       for (int j = part; j < cl; j += kpar) {
         const int kj = k0 + c0 + j;
-        const T* kr = Kt + (sh * n + kj) * D;
         float sc = 0.0f;
+        if (stage_k) {
+          // four partial sums (channels d mod 4), added in a fixed order
+          const f32x4* kr4 = reinterpret_cast<const f32x4*>(&ks[j][0]);
+          float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int d = 0; d < D; ++d) sc = fmaf(qv[d], (float)kr[d], sc);
+          for (int d4 = 0; d4 < D / 4; ++d4) {
+            const f32x4 k4 = kr4[d4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s4[e] = fmaf(qv[4 * d4 + e], k4[e], s4[e]);
+          }
+          sc = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        } else {
+          const T* kr = Kt + (sh * n + kj) * D;
+#pragma unroll
+          for (int d = 0; d < D; ++d) sc = fmaf(qv[d], (float)kr[d], sc);
+        }
         sc *= c_log2;
         if constexpr (REL) {
           const int kc = rel_kc[(size_t)seg * n + kj];
@@ -1311,9 +1359,11 @@ size_t attn_partial_bytes(const sparsesam_plan& p, int segments) {
 template <typename T, int D, bool REL = false>
 static hipError_t run_simt(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
                            float c_log2, hipStream_t st, const float* rel_t = nullptr, const int* rel_kc = nullptr) {
-  // queries per workgroup: 64, or the tile length rounded up to 32 or 16, so that short
-  // tiles keep every thread busy with a share of the keys
-  const int qpw = p.desc.block >= 64 ? 64 : p.desc.block > 16 ? 32 : 16;
+  // queries per workgroup: 64 for 64-token tiles, 32 or 16 for tiles up to 32 tokens, and
+  // 4 (16 threads per query, four workgroups per 16-token tile) for tiles of at most 16,
+  // so that short tiles keep every thread busy with a share of the keys and spread over
+  // more CUs
+  const int qpw = p.desc.block >= 64 ? 64 : p.desc.block > 16 ? 32 : 4;
   const int chunks = (p.desc.block + qpw - 1) / qpw;
   dim3 grid(p.tiles * chunks, p.desc.heads, segments);
   hipLaunchKernelGGL((attn_simt_kernel<T, D, REL>), grid, dim3(64), 0, st, q, k, vt, o, p.d_row_ptr, p.d_col_idx,
