@@ -657,7 +657,13 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16_t* __restrict
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
 
-constexpr int FT = 64, FK = 16;
+// 64 x 64 tiles, 256 threads (4 x 4 outputs each), K in slices of FK: a slice's A and W
+// values are loaded into registers while the previous slice is multiplied, then stored to
+// LDS (the loads of a slice are all issued before the first store, so a slice costs one
+// round trip to memory, overlapped with the previous slice's arithmetic). Each output
+// adds its K products in ascending k.
+constexpr int FT = 64, FK = 32;
+constexpr int FV = FT * FK / 256;  // values of A (and of W) per thread per slice
 
 template <class Epi>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
@@ -669,14 +675,27 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
   const int ke = K;
   const int tr = tid / 16, tc = tid % 16;
   float acc[4][4] = {};
+  float ra[FV], rb[FV];
+  // value u of this thread in a slice: tile row (i / FK), slice column (i % FK), i = tid + 256 u
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < FV; ++u) {
+      const int i = tid + 256 * u, row = i / FK, kk = i % FK;
+      const int gm = m0 + row, gn = n0 + row, gk = k0 + kk;
+      ra[u] = (gm < M && gk < ke) ? A[(size_t)gm * K + gk] : 0.0f;
+      rb[u] = (gn < N && gk < ke) ? W[(size_t)gn * K + gk] : 0.0f;
+    }
+  };
+  fetch(0);
   for (int k0 = 0; k0 < ke; k0 += FK) {
-    for (int i = tid; i < FT * FK; i += 256) {
-      int row = i / FK, kk = i % FK;
-      int gm = m0 + row, gn = n0 + row, gk = k0 + kk;
-      As[kk][row] = (gm < M && gk < ke) ? A[(size_t)gm * K + gk] : 0.0f;
-      Bs[kk][row] = (gn < N && gk < ke) ? W[(size_t)gn * K + gk] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < FV; ++u) {
+      const int i = tid + 256 * u, row = i / FK, kk = i % FK;
+      As[kk][row] = ra[u];
+      Bs[kk][row] = rb[u];
     }
     __syncthreads();
+    if (k0 + FK < ke) fetch(k0 + FK);  // the next slice, in flight during this one
 #pragma unroll
     for (int kk = 0; kk < FK; ++kk) {
       float a[4], b[4];
