@@ -30,6 +30,8 @@ def config(key):
         return get_config("c3").with_(batch=1)
     if key == "ragged":  # 18 x 18 grid: four windows, three of them partial; small channels
         return get_config("c3").with_(batch=2, image=288, channels=128, heads=2, mlp_hidden=256)
+    if key == "c1odd":  # fp32, head_dim 32 (16 threads per query), MLP hidden 200: ragged GEMM K and N
+        return get_config("c1").with_(channels=96, heads=3, head_dim=32, mlp_hidden=200)
     return get_config(key)
 
 

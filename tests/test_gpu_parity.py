@@ -250,7 +250,7 @@ def test_attention_single_stripe_and_wide_band():
 
 # ------------------------------------------------------------------ MLP
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3b1"])
+@pytest.mark.parametrize("key", ["c1", "c1odd", "c2", "c3b1"])
 def test_mlp_parity_and_unrouted_rows_untouched(key):
     _say("mlp", key)
     x, w, imp, _, parts = oracle_block(key)
@@ -327,7 +327,7 @@ def _check_block(key, r, gain):
     assert delta_rel <= bar, "block %s: block delta rel-L2 %.3e > %.1e" % (key, delta_rel, bar)
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3", "ragged", "c4g", "c4w", "c1:zorder", "c3b1:hilbert",
+@pytest.mark.parametrize("key", ["c1", "c1odd", "c2", "c3", "ragged", "c4g", "c4w", "c1:zorder", "c3b1:hilbert",
                                  "c2:random"])
 def test_block_parity(key):
     _say("block", key)
