@@ -215,6 +215,17 @@ def test_attention_bf16_simt_fallback(key, over):
     check_close(o, want, what="bf16 SIMT attention %s %s" % (key, over))
 
 
+@pytest.mark.parametrize("head_dim,block", [(32, 16), (80, 16), (128, 16), (80, 32), (128, 64)])
+def test_attention_fp32_simt_head_dims(head_dim, block):
+    """The fp32 SIMT kernel at every head_dim it takes and at the three tile lengths that
+    set its threads per query: 16 threads (16-token tiles), 2 (32) and 1 (64; K rows by
+    scalar loads); head_dim 128 stages 32-key chunks."""
+    over = dict(heads=2, head_dim=head_dim, channels=2 * head_dim, block=block, global_tokens=block)
+    _say("attention fp32 simt", over)
+    o, want = _attn_case("c1", seed=8, **over)
+    check_close(o, want, what="fp32 SIMT attention D%d B%d" % (head_dim, block))
+
+
 # A short global segment (16 x 16 tokens, one stripe of sixteen 16-token tiles): every
 # key tile has its own kept column, so with the pad keys' class there are 17 mask
 # classes and the short-segment kernel adds its mask in two matrix-core k-steps.
