@@ -184,6 +184,117 @@ static void build_tiles(sparsesam_plan& p, int radius) {
   p.radius = radius;
 }
 
+// Tables of the window kernel on 16-key blocks (attn_win_kernel) for segments of at most
+// kShortMaxN tokens: key classes in consecutive slots, query groups with their key-block
+// lists, the groups balanced over the wavefronts (longest first onto the least loaded).
+// Leaves win_nslots = 0 when the segment does not fit kWinMaxSlots slots.
+static void build_window_tables(sparsesam_plan& p) {
+  p.win_nslots = 0;
+  p.win_pos_slot.clear();
+  p.win_slot_pos.clear();
+  p.win_groups.clear();
+  p.win_kb.clear();
+  p.win_wave.clear();
+  if (p.n > kShortMaxN || p.desc.stripes * p.s != p.n) return;
+  const int T = p.tiles;
+  std::vector<char> kept((size_t)T * T, 0);
+  for (int t = 0; t < T; ++t)
+    for (int c = p.row_ptr[t]; c < p.row_ptr[t + 1]; ++c) kept[(size_t)t * T + p.col_idx[c]] = 1;
+  // key classes: tiles with the same kept column, in first-appearance order
+  std::map<std::vector<char>, int> cls_of;
+  std::vector<int> tile_cls(T);
+  std::vector<std::vector<int>> cls_tiles;
+  for (int t2 = 0; t2 < T; ++t2) {
+    std::vector<char> col(T);
+    for (int t1 = 0; t1 < T; ++t1) col[t1] = kept[(size_t)t1 * T + t2];
+    auto f = cls_of.emplace(col, (int)cls_tiles.size());
+    if (f.second) cls_tiles.emplace_back();
+    tile_cls[t2] = f.first->second;
+    cls_tiles[f.first->second].push_back(t2);
+  }
+  const int ncls = (int)cls_tiles.size();
+  std::vector<int> pos_slot(kWinMaxSlots, 0), slot_pos(kWinMaxSlots, 0), blk_mask;
+  std::vector<int> cls_b0(ncls), cls_b1(ncls);
+  int slot = 0;
+  for (int c = 0; c < ncls; ++c) {
+    cls_b0[c] = slot / 16;
+    const int first = p.tile_start[cls_tiles[c][0]];
+    for (int t : cls_tiles[c])
+      for (int i = 0; i < p.tile_len[t]; ++i, ++slot) {
+        if (slot >= kWinMaxSlots) return;
+        slot_pos[slot] = p.tile_start[t] + i;
+        pos_slot[p.tile_start[t] + i] = slot;
+      }
+    const int end = (slot + 15) / 16 * 16;
+    if (end > kWinMaxSlots) return;
+    for (int b = cls_b0[c]; b < end / 16; ++b) {
+      int m = 0;
+      for (int i = 0; i < 16; ++i)
+        if (16 * b + i < slot) m |= 1 << i;
+      blk_mask.push_back(m);
+    }
+    for (; slot < end; ++slot) slot_pos[slot] = first;  // empty: a real key, masked
+    cls_b1[c] = end / 16;
+  }
+  // query groups: tiles whose kept key tiles form the same set of classes
+  std::map<std::vector<int>, int> set_of;
+  std::vector<std::vector<int>> set_tiles, set_cls;
+  for (int t1 = 0; t1 < T; ++t1) {
+    std::vector<int> cs;
+    for (int c = p.row_ptr[t1]; c < p.row_ptr[t1 + 1]; ++c) cs.push_back(tile_cls[p.col_idx[c]]);
+    std::sort(cs.begin(), cs.end());
+    cs.erase(std::unique(cs.begin(), cs.end()), cs.end());
+    if (cs.empty()) continue;  // a query tile with no kept key has no output here
+    auto f = set_of.emplace(cs, (int)set_tiles.size());
+    if (f.second) {
+      set_tiles.emplace_back();
+      set_cls.push_back(cs);
+    }
+    set_tiles[f.first->second].push_back(t1);
+  }
+  struct Group { int kb0, kb1, nq; int q[16]; };
+  std::vector<Group> gs;
+  for (size_t st = 0; st < set_tiles.size(); ++st) {
+    const int kb0 = (int)p.win_kb.size();
+    for (int c : set_cls[st])
+      for (int b = cls_b0[c]; b < cls_b1[c]; ++b) p.win_kb.push_back(b | (blk_mask[b] << 16));
+    const int kb1 = (int)p.win_kb.size();
+    std::vector<int> qs;
+    for (int t : set_tiles[st])
+      for (int i = 0; i < p.tile_len[t]; ++i) qs.push_back(p.tile_start[t] + i);
+    for (size_t q0 = 0; q0 < qs.size(); q0 += 16) {
+      Group g{kb0, kb1, (int)std::min<size_t>(16, qs.size() - q0), {}};
+      for (int i = 0; i < 16; ++i) g.q[i] = q0 + i < qs.size() ? qs[q0 + i] : -1;
+      gs.push_back(g);
+    }
+  }
+  // longest first onto the least loaded wavefront (cost: key blocks + 1 for the query
+  // loads and stores)
+  std::vector<int> idx(gs.size());
+  for (size_t i = 0; i < gs.size(); ++i) idx[i] = (int)i;
+  std::stable_sort(idx.begin(), idx.end(),
+                   [&](int a, int b) { return gs[a].kb1 - gs[a].kb0 > gs[b].kb1 - gs[b].kb0; });
+  std::vector<int> load(kWinWaves, 0);
+  std::vector<std::vector<int>> wl(kWinWaves);
+  for (int i : idx) {
+    const int w = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[w] += gs[i].kb1 - gs[i].kb0 + 1;
+    wl[w].push_back(i);
+  }
+  p.win_wave.push_back(0);
+  for (int w = 0; w < kWinWaves; ++w) {
+    for (int i : wl[w]) {
+      const Group& g = gs[i];
+      p.win_groups.insert(p.win_groups.end(), {g.kb0, g.kb1, g.nq, 0});
+      p.win_groups.insert(p.win_groups.end(), g.q, g.q + 16);
+    }
+    p.win_wave.push_back((int)(p.win_groups.size() / kWinGroupInts));
+  }
+  p.win_pos_slot = pos_slot;
+  p.win_slot_pos = slot_pos;
+  p.win_nslots = slot;
+}
+
 }  // namespace sparsesam
 
 using namespace sparsesam;
@@ -352,6 +463,7 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
           if (kept[(size_t)p->pos_tile[q] * p->tiles + p->pos_tile[k]]) p->any32[q / 32] |= 1 << (k / 32);
     }
   }
+  build_window_tables(*p);
   // keep-set size per segment
   p->seg_k.resize(p->segs_per_img);
   p->seg_off.resize(p->segs_per_img);
@@ -401,7 +513,9 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     size_t o_rp = put(p->row_ptr), o_ci = put(p->col_idx), o_ts = put(p->tile_start), o_tl = put(p->tile_len),
            o_or = put(p->order), o_sk = put(p->seg_k), o_so = put(p->seg_off), o_it = put(p->items),
            o_sp = put(p->splits), o_pt = put(p->pos_tile), o_a32 = put(p->any32), o_mc = put(p->mask_class),
-           o_mr = put(p->mask_row), o_kp = put(p->keep_pos);
+           o_mr = put(p->mask_row), o_kp = put(p->keep_pos), o_wps = put(p->win_pos_slot),
+           o_wsp = put(p->win_slot_pos), o_wg = put(p->win_groups), o_wkb = put(p->win_kb),
+           o_ww = put(p->win_wave);
     blob.push_back(0);
     void* dptr = nullptr;
     hipError_t e = hipMalloc(&dptr, blob.size() * sizeof(int));
@@ -433,6 +547,11 @@ sparsesam_status sparsesam_plan_create(const sparsesam_plan_desc* desc, sparsesa
     p->d_mask_class = b + o_mc;
     p->d_mask_row = b + o_mr;
     p->d_keep_pos = b + o_kp;
+    p->d_win_pos_slot = b + o_wps;
+    p->d_win_slot_pos = b + o_wsp;
+    p->d_win_groups = b + o_wg;
+    p->d_win_kb = b + o_wkb;
+    p->d_win_wave = b + o_ww;
     p->attn_resident_wgs = attn_long_supported(*p) ? attn_long_resident_wgs(dev, p->desc.head_dim) : 0;
     (void)hipGetLastError();
   } else {

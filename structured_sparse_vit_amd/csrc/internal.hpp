@@ -14,6 +14,11 @@
 constexpr int kAttnItemTiles = 64;
 // Segments up to this length (the windows) take the short-segment attention kernel.
 constexpr int kShortMaxN = 256;
+// The window kernel on 16-key blocks: wavefronts per workgroup, LDS slots at most, ints
+// per query-group record.
+constexpr int kWinWaves = 8;
+constexpr int kWinMaxSlots = 256;
+constexpr int kWinGroupInts = 20;
 
 struct sparsesam_plan {
   sparsesam_plan_desc desc;
@@ -53,6 +58,16 @@ struct sparsesam_plan {
   // masked, two per int). nt32 = 0: no short-segment kernel (more than 32 classes).
   std::vector<int> pos_tile, any32, mask_class, mask_row;
   int nt32 = 0, mask_ksteps = 0;
+  // short segments on 16-key blocks (attn_win_kernel): key tiles kept by the same query
+  // tiles form a class stored in consecutive LDS slots, cut into blocks of 16 (empty
+  // slots masked); query positions with the same kept key tiles form groups of up to 16.
+  // win_pos_slot[p] / win_slot_pos[s]: slot of position p and position of slot s (an
+  // empty slot holds a real key of its class), both padded to 256 entries; win_groups:
+  // kWinGroupInts ints per group (first key block, end, queries, 0, 16 positions or -1);
+  // win_kb: key blocks (block | valid-slot mask << 16); win_wave: groups of wavefront w
+  // are [win_wave[w], win_wave[w + 1]). win_nslots = 0: not available.
+  std::vector<int> win_pos_slot, win_slot_pos, win_groups, win_kb, win_wave;
+  int win_nslots = 0;
   // relative-position bias: segment shape (grid or window) and the bias table row of a
   // query: key rows at 0 .. rel_seg_h - 1, key columns at rel_xoff .., rel_tj entries
   // (0 when the segment is larger than 64 x 64: no bias support)
@@ -74,6 +89,11 @@ struct sparsesam_plan {
   const int* d_any32 = nullptr;
   const int* d_mask_class = nullptr;
   const int* d_mask_row = nullptr;
+  const int* d_win_pos_slot = nullptr;
+  const int* d_win_slot_pos = nullptr;
+  const int* d_win_groups = nullptr;
+  const int* d_win_kb = nullptr;
+  const int* d_win_wave = nullptr;
   // keep-set of a stream kept in stripe-sorted order: the positions of ranks 0 .. K - 1
   // of every segment, (seg * n) + (rank % g) * S + rank / g, for max_batch images in
   // the keep-set layout (static: the keep-set is the first K ranks)

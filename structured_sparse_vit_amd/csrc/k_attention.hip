@@ -23,9 +23,14 @@
 //    template on the key-parity count, so the per-step tile loads have no branches.
 //  * attn_d80_kernel: the same work items for head_dim 80 (running max with a 2^8
 //    slack, denominators from a ones row of the third V^T block).
-//  * attn_short_kernel: short segments (windows, N <= 256), one workgroup per
-//    (segment, head) with the segment's K and V^T in LDS; the static mask is one or
-//    two extra MFMA k-steps over key classes.
+//  * attn_win_kernel: short segments (windows, N <= 256), one workgroup per (segment,
+//    head). Key tiles kept by the same query tiles share consecutive LDS slots cut into
+//    16-key blocks; query positions keeping the same key tiles form groups of 16; each
+//    group runs on v_mfma_f32_16x16x32_bf16 over exactly its kept key blocks (1.04x the
+//    kept pairs of a ViT-B window, where whole 32 x 32 blocks are 3.0x).
+//  * attn_short_kernel: short segments whose key classes do not fit the window kernel's
+//    256 slots: K and V^T in LDS by position, whole 32 x 32 blocks, the static mask as
+//    one or two extra MFMA k-steps over key classes.
 //  * attn_combine_kernel: merges the partial results of rows split over several
 //    work items (none at ViT sizes).
 //  * attn_simt_kernel (fp32 or bf16 storage, any pattern and head_dim <= 128): one to
@@ -1192,6 +1197,256 @@ __global__ void __launch_bounds__(kShortThreads) __attribute__((amdgpu_waves_per
   }
 }
 
+// ---------------------------------------------------------------- window kernel on 16-key blocks
+
+// Short segments without the bias (the windows), computed on the kept pairs only. The
+// plan (see the window tables in api.hip) packs the segment for the kernel:
+//  - key blocks: key tiles kept by the same set of query tiles form a class; a class's
+//    positions are stored consecutively in LDS slots and cut into blocks of 16 slots
+//    (the last one of a class partly empty, its empty slots masked);
+//  - query groups: query positions whose tiles keep the same key tiles, up to 16 per
+//    group, each with the list of its key blocks (exactly the kept keys of its queries).
+// One workgroup of eight wavefronts per (segment, head); each wavefront takes a list of
+// groups (balanced over the wavefronts by the plan) and walks a group's key blocks two at
+// a time on v_mfma_f32_16x16x32_bf16: S^T = K Q^T per block (lane = query l % 16, keys
+// 4 (l / 16) .. + 3 of the block), online softmax in exp2 units with a reference that
+// moves only past kRescaleSlack, and O^T += V^T P^T over the 32 keys of the pair, whose
+// k order (four keys of each block per lane group) is the one the S^T lanes already hold,
+// so P needs no lane exchange. K rows are stored by slot (every load issued before any
+// LDS store); V^T columns are gathered by slot (an empty slot reads a real key of its
+// class, whose probability is 0).
+constexpr int kWinThreads = 64 * kWinWaves;
+// group record (kWinGroupInts ints): {first key block, end, queries, 0}, then 16 query
+// positions (-1: none)
+
+template <int D>
+struct WinLds {
+  static constexpr int KLD = D + 8;  // K row stride (bf16): 16-byte pad
+  // K rows, V^T rows; with the bias, 17 fp16 one-hot rows and each slot's key coordinates
+  static size_t bytes(int nslots, bool rel) {
+    return (size_t)nslots * KLD * 2 + (size_t)D * (nslots + 8) * 2 + (rel ? kShortOneHotBytes + (size_t)nslots * 4 : 0);
+  }
+};
+
+// REL: add the relative-position bias. A query's table row (rel_t, fp16, exp2 units)
+// holds 32 entries, key rows at 0..15 and key columns at 16..31; one fp16 k-step of 32
+// per key block adds it, its K operand one-hot in the key's row (lane groups 0, 1) or
+// column (groups 2, 3), from 17 one-hot rows in LDS, the scores taken to exp2 units first.
+template <int D, bool REL>
+__global__ void __launch_bounds__(kWinThreads) __attribute__((amdgpu_waves_per_eu(4)))
+attn_win_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt, const bf16_t* __restrict__ VT,
+                bf16_t* __restrict__ O, const int* __restrict__ pos_slot, const int* __restrict__ slot_pos,
+                const int* __restrict__ groups, const int* __restrict__ kblocks, const int* __restrict__ wave_begin,
+                int n, int n_pad, int nslots, int heads, float c_log2, const f16_t* __restrict__ rel_t,
+                const int* __restrict__ rel_kc) {
+  using L = WinLds<D>;
+  constexpr int KCH = D / 8;                                 // 16-byte chunks of a K row
+  constexpr int KIT = (kShortMaxN * KCH + kWinThreads - 1) / kWinThreads;
+  constexpr int VIT = (D * 32 + kWinThreads - 1) / kWinThreads;  // V^T chunks of 8 slots, 32 per row
+  constexpr int KS = (D + 31) / 32;  // 32-wide k-steps of Q K^T; in the last one of D = 80
+                                     // the lanes past D hold zeros in both operands
+  constexpr int MD = D / 16;                                 // 16-row blocks of O^T
+  static_assert(D % 16 == 0 && kShortMaxN <= kWinMaxSlots, "window kernel shapes");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int vld = nslots + 8;
+  bf16_t* Ks = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* Vs = Ks + (size_t)nslots * L::KLD;
+  const int sh = blockIdx.x;
+  const int seg = sh / heads, h = sh - seg * heads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const bf16_t* q_base = Q + (size_t)sh * n * D;
+  const bf16_t* k_base = Kt + (size_t)sh * n * D;
+  const bf16_t* v_base = VT + (size_t)sh * D * n_pad;
+
+  // This wavefront's groups: the first group's query fragments (and bias row) are
+  // requested before the fill, each next group's while the current one is computed.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int gb = wave_begin[wv], ge = wave_begin[wv + 1];
+  bf16x8 qf[KS];
+  f16x8 tf{};  // the query's bias entries 8 g .. + 7
+  auto load_q = [&](int gi, int& qp, bf16x8* f, f16x8& t) {
+    qp = groups[(size_t)gi * kWinGroupInts + 4 + r16];
+    const int qrow = qp < 0 ? 0 : qp;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = ks * 32 + g * 8;
+      f[ks] = *reinterpret_cast<const bf16x8*>(q_base + (size_t)qrow * D + min(d0, D - 8));
+      if (d0 >= D) f[ks] = bf16x8{};
+    }
+    if constexpr (REL) t = *reinterpret_cast<const f16x8*>(rel_t + ((size_t)sh * n + qrow) * 32 + g * 8);
+  };
+  int qp = -1;
+  if (gb < ge) load_q(gb, qp, qf, tf);
+
+  // Fill, every load issued before any LDS store. K rows by position: chunk c = tid +
+  // 512 i is position c / KCH, channels 8 (c % KCH), stored at the position's slot.
+  i32x4 kv[KIT];
+  int ks_slot[KIT];
+#pragma unroll
+  for (int i = 0; i < KIT; ++i) {
+    const int c = tid + kWinThreads * i, p = min(c / KCH, n - 1), ch = c - (c / KCH) * KCH;
+    kv[i] = *reinterpret_cast<const i32x4*>(k_base + (size_t)p * D + ch * 8);
+    ks_slot[i] = pos_slot[p];
+  }
+  // V^T by position: chunk c = tid + 512 i is row c / 32, positions 8 (c % 32) .. + 7,
+  // each element stored at its position's slot
+  bf16x8 vv[VIT];
+  i32x4 vs[VIT][2];
+#pragma unroll
+  for (int i = 0; i < VIT; ++i) {
+    const int c = tid + kWinThreads * i, d = min(c >> 5, D - 1), j = c & 31;
+    vv[i] = *reinterpret_cast<const bf16x8*>(v_base + (size_t)d * n_pad + min(8 * j, n_pad - 8));
+    vs[i][0] = *reinterpret_cast<const i32x4*>(pos_slot + 8 * j);
+    vs[i][1] = *reinterpret_cast<const i32x4*>(pos_slot + 8 * j + 4);
+  }
+  char* onehot = reinterpret_cast<char*>(Vs + (size_t)D * vld);
+  int* key_rc = reinterpret_cast<int*>(onehot + kShortOneHotBytes);  // [nslots]: row | (16 + column) << 16
+  int kc_own = 0;
+  if constexpr (REL) {
+    if (tid < nslots) kc_own = rel_kc[(size_t)seg * n + slot_pos[tid]];
+  }
+  // V^T rows zeroed first (the empty slots of a class's last block must hold finite
+  // values: their probabilities are 0), while the loads are in flight; only LDS
+  // operations are waited for before this barrier
+  for (int i = tid; i < D * vld / 8; i += kWinThreads) reinterpret_cast<i32x4*>(Vs)[i] = i32x4{0, 0, 0, 0};
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & lgkmcnt0_mask());
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < KIT; ++i) {
+    const int c = tid + kWinThreads * i, ch = c - (c / KCH) * KCH;
+    if (c / KCH < n) *reinterpret_cast<i32x4*>(Ks + ks_slot[i] * L::KLD + ch * 8) = kv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < VIT; ++i) {
+    const int c = tid + kWinThreads * i, d = c >> 5, j = c & 31;
+    if (d < D) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (8 * j + e < n) Vs[d * vld + vs[i][e >> 2][e & 3]] = vv[i][e];
+    }
+  }
+  if constexpr (REL) {
+    if (tid < nslots) key_rc[tid] = kc_own;
+    if (tid < 68) {  // row 8 + e: fp16 1.0 at element e; rows 0..7 and 16 zero
+      const int row = tid >> 2, i = tid & 3, e = row - 8;
+      reinterpret_cast<uint32_t*>(onehot)[tid] = (e == 2 * i ? 0x3C00u : 0u) | (e == 2 * i + 1 ? 0x3C000000u : 0u);
+    }
+  }
+  __syncthreads();
+
+  for (int gi = gb; gi < ge; ++gi) {
+    const int* gr = groups + (size_t)gi * kWinGroupInts;
+    const int kb_first = gr[0], kb_end = gr[1];
+    int qp_next = -1;
+    bf16x8 qf_next[KS] = {};
+    f16x8 tf_next{};
+    if (gi + 1 < ge) load_q(gi + 1, qp_next, qf_next, tf_next);
+    f32x4 oacc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) oacc[md] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;
+    // S^T of key block b for this lane's query: keys 16 b + 4 g .. + 3 (with the bias: in
+    // exp2 units)
+    auto scores = [&](int b) {
+      f32x4 s{0.0f, 0.0f, 0.0f, 0.0f};
+      const bf16_t* krow = Ks + (16 * b + r16) * L::KLD;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = ks * 32 + g * 8;
+        bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + min(d0, D - 8));
+        if (d0 >= D) kf = bf16x8{};
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s, 0, 0, 0);
+      }
+      if constexpr (REL) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] *= c_log2;
+        const int kcs = key_rc[16 * b + r16];
+        const int jj = g < 2 ? (kcs & 0xffff) : (kcs >> 16);
+        const int row = min(max(jj - 8 * g + 8, 0), 16);
+        const f16x8 af = *reinterpret_cast<const f16x8*>(onehot + row * 16);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, tf, s, 0, 0, 0);
+      }
+      return s;
+    };
+    for (int kb = kb_first; kb < kb_end; kb += 2) {
+      const bool two = kb + 1 < kb_end;
+      const int e0 = kblocks[kb], e1 = two ? kblocks[kb + 1] : e0;
+      const int b0 = e0 & 0xffff, b1 = e1 & 0xffff;
+      f32x4 s0 = scores(b0), s1;
+      if (two) {
+        s1 = scores(b1);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s1[i] = -INFINITY;
+      }
+      // empty slots of a block: masked (their K rows are not stored)
+      const unsigned v0 = (unsigned)e0 >> 16, v1 = (unsigned)e1 >> 16;
+      if (v0 != 0xffffu) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((v0 >> (4 * g + i)) & 1u)) s0[i] = -INFINITY;
+      }
+      if (two && v1 != 0xffffu) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((v1 >> (4 * g + i)) & 1u)) s1[i] = -INFINITY;
+      }
+      float mx = fmaxf(max3f(s0[0], s0[1], s0[2]), max3f(s0[3], s1[0], s1[1]));
+      mx = max3f(mx, s1[2], s1[3]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = max_xor32(mx);
+      const float m_new = fmaxf(m_run, REL ? mx : mx * c_log2);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
+        const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        l_run *= alpha;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[md][i] *= alpha;
+        m_run = m_new;
+      }
+      const float mref = fmaxf(m_run, -3.40282347e38f);
+      bf16x8 pf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pf[i] = to_bf16(__builtin_amdgcn_exp2f(REL ? s0[i] - mref : __builtin_fmaf(s0[i], c_log2, -mref)));
+        pf[4 + i] = to_bf16(__builtin_amdgcn_exp2f(REL ? s1[i] - mref : __builtin_fmaf(s1[i], c_log2, -mref)));
+      }
+      // the denominator sums exactly the bf16 probabilities V is multiplied with
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) l_run = sum_bf16_pair(pf[i], pf[i + 1], l_run);
+      // O^T += V^T P^T: rows d = 16 md + l % 16, k order = keys 4 g .. + 3 of b0, then of b1
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const bf16_t* vrow = Vs + (16 * md + r16) * vld + 4 * g;
+        const bf16x4 va = *reinterpret_cast<const bf16x4*>(vrow + 16 * b0);
+        const bf16x4 vb = *reinterpret_cast<const bf16x4*>(vrow + 16 * b1);
+        const bf16x8 vf = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+        oacc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[md], 0, 0, 0);
+      }
+    }
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (qp >= 0) {
+      const float inv_l = 1.0f / l_tot;
+      bf16_t* o_row = O + ((size_t)seg * n + qp) * ((size_t)heads * D) + (size_t)h * D;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        bf16x4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = to_bf16(oacc[md][i] * inv_l);
+        *reinterpret_cast<bf16x4*>(o_row + 16 * md + 4 * g) = v4;
+      }
+    }
+    qp = qp_next;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = qf_next[ks];
+    if constexpr (REL) tf = tf_next;
+  }
+}
+
 // ---------------------------------------------------------------- SIMT kernel (any pattern)
 
 // REL: add the relative-position bias, rel_t[sh, query, kc & 0xffff] +
@@ -1387,18 +1642,35 @@ static hipError_t launch_short(const sparsesam_plan& p, int units, const bf16_t*
   return hipGetLastError();
 }
 
+// The window kernel on 16-key blocks: one workgroup per (segment, head).
+template <int D, bool REL>
+static hipError_t launch_win(const sparsesam_plan& p, int units, const bf16_t* q, const bf16_t* k, const bf16_t* vt,
+                             bf16_t* o, float c_log2, const f16_t* tb, const int* kc, hipStream_t st) {
+  const size_t lds = WinLds<D>::bytes(p.win_nslots, REL);
+  auto kern = attn_win_kernel<D, REL>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)units), dim3(kWinThreads), lds, st, q, k, vt, o, p.d_win_pos_slot,
+                     p.d_win_slot_pos, p.d_win_groups, p.d_win_kb, p.d_win_wave, p.n, p.n_pad, p.win_nslots,
+                     p.desc.heads, c_log2, tb, kc);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, const T* k, const T* vt, T* o,
                             float scale, void* partial, hipStream_t st) {
   if (segments <= 0) return hipSuccess;
   const float c_log2 = scale * 1.4426950408889634f;
   if constexpr (sizeof(T) == 2) {
-    if (p.nt32 > 0 && (p.desc.head_dim == 64 || p.desc.head_dim == 80)) {
+    if ((p.win_nslots > 0 || p.nt32 > 0) && (p.desc.head_dim == 64 || p.desc.head_dim == 80)) {
       const int units = segments * p.desc.heads;
       const auto* qb = reinterpret_cast<const bf16_t*>(q);
       const auto* kb = reinterpret_cast<const bf16_t*>(k);
       const auto* vb = reinterpret_cast<const bf16_t*>(vt);
       auto* ob = reinterpret_cast<bf16_t*>(o);
+      if (p.win_nslots > 0)
+        return p.desc.head_dim == 64 ? launch_win<64, false>(p, units, qb, kb, vb, ob, c_log2, nullptr, nullptr, st)
+                                     : launch_win<80, false>(p, units, qb, kb, vb, ob, c_log2, nullptr, nullptr, st);
       return p.desc.head_dim == 64 ? launch_short<64, false>(p, units, qb, kb, vb, ob, c_log2, nullptr, nullptr, st)
                                    : launch_short<80, false>(p, units, qb, kb, vb, ob, c_log2, nullptr, nullptr, st);
     }
@@ -1497,7 +1769,7 @@ hipError_t launch_attention_relpos(const sparsesam_plan& p, int segments, const 
     }
   }
   if constexpr (sizeof(T) == 2) {
-    if (p.nt32 > 0 && p.rel_tj == 32 && (p.desc.head_dim == 64 || p.desc.head_dim == 80)) {
+    if ((p.nt32 > 0 || p.win_nslots > 0) && p.rel_tj == 32 && (p.desc.head_dim == 64 || p.desc.head_dim == 80)) {
       auto* tb = static_cast<f16_t*>(table);
       hipError_t e = launch_relpos_table<bf16_t, f16_t>(p, segments, reinterpret_cast<const bf16_t*>(q), perm,
                                                          rel_h, rel_w, tb, kc, st);
@@ -1507,6 +1779,9 @@ hipError_t launch_attention_relpos(const sparsesam_plan& p, int segments, const 
       const auto* kb = reinterpret_cast<const bf16_t*>(k);
       const auto* vb = reinterpret_cast<const bf16_t*>(vt);
       auto* ob = reinterpret_cast<bf16_t*>(o);
+      if (p.win_nslots > 0)
+        return p.desc.head_dim == 80 ? launch_win<80, true>(p, units, qb, kb, vb, ob, c_log2, tb, kc, st)
+                                     : launch_win<64, true>(p, units, qb, kb, vb, ob, c_log2, tb, kc, st);
       return p.desc.head_dim == 80 ? launch_short<80, true>(p, units, qb, kb, vb, ob, c_log2, tb, kc, st)
                                    : launch_short<64, true>(p, units, qb, kb, vb, ob, c_log2, tb, kc, st);
     }

@@ -227,8 +227,9 @@ def test_attention_fp32_simt_head_dims(head_dim, block):
 
 
 # A short global segment (16 x 16 tokens, one stripe of sixteen 16-token tiles): every
-# key tile has its own kept column, so with the pad keys' class there are 17 mask
-# classes and the short-segment kernel adds its mask in two matrix-core k-steps.
+# key tile has its own kept column, so the window kernel stores sixteen key classes in
+# its 256 LDS slots (one 16-key block each), and the 32 x 32 window kernel would need two
+# mask k-steps (17 classes with its pad keys).
 SHORT_TWO_KSTEPS = dict(dtype="bf16", stripes=1, block=16, global_tokens=16, heads=2, mlp_hidden=256,
                         attn_density=0.3)
 
@@ -242,15 +243,40 @@ def mask_classes(cfg, plan):
 
 
 @pytest.mark.parametrize("head_dim", [64, 80])
-def test_attention_short_segment_two_mask_ksteps(head_dim):
-    _say("attention short segment, two mask k-steps, head_dim", head_dim)
+def test_attention_short_segment_sixteen_classes(head_dim):
+    _say("attention short segment, sixteen key classes, head_dim", head_dim)
     heads = 2 if head_dim == 64 else 8  # bf16 plans take channels in multiples of 128
     over = dict(SHORT_TWO_KSTEPS, heads=heads, head_dim=head_dim, channels=heads * head_dim)
     cfg = config("c1").with_(**over)
     plan = _plan(cfg)
     assert plan.info["seq_len"] <= 256 and mask_classes(cfg, plan) + 1 > 16
     o, want = _attn_case("c1", seed=11, **over)
-    check_close(o, want, what="short segment, two mask k-steps, D %d" % head_dim)
+    check_close(o, want, what="short segment, sixteen key classes, D %d" % head_dim)
+
+
+@pytest.mark.parametrize("grid_h,grid_w,block,head_dim,ksteps", [
+    (16, 15, 8, 64, 2), (16, 15, 8, 80, 2), (15, 17, 17, 64, 1), (15, 17, 17, 80, 1)])
+def test_attention_window_slots_overflow(grid_h, grid_w, block, head_dim, ksteps):
+    """Short global segments whose key classes do not fit 256 LDS slots in 16-key blocks
+    (30 classes of 8 tokens; 15 classes of 17): these run the 32 x 32-block window kernel
+    with its mask in one or two matrix-core k-steps."""
+    heads = 2 if head_dim == 64 else 8  # bf16 plans take channels in multiples of 128
+    plan = ss.Plan(grid_h, grid_w, 0, 1, block, block, -1, 0.3, 0.4, heads * head_dim, heads, head_dim, 256, 1,
+                   "bf16")
+    n = plan.info["seq_len"]
+    _say("attention window slot overflow", grid_h, grid_w, block, head_dim)
+    rng = np.random.default_rng(12)
+    q, k, v = (round_to_bf16(rng.standard_normal((1, heads, n, head_dim), dtype=np.float32)) for _ in range(3))
+    n_pad = (n + 7) // 8 * 8
+    vt = np.full((1, heads, head_dim, n_pad), np.nan, np.float32)
+    vt[..., :n] = v.transpose(0, 1, 3, 2)
+    dev = [torch.from_numpy(a).to(DEV, torch.bfloat16).contiguous() for a in (q, k, vt)]
+    o = ss.attn(plan, *dev).float().cpu().numpy()
+    keep = oracle.position_keep(n, 1, block, block, plan.info["band_radius"])
+    assert len({keep[:, j].tobytes() for j in range(n)}) + 1 > 16 * (ksteps - 1)
+    want = np.concatenate([oracle.masked_attention(q[0, h], k[0, h], v[0, h], keep, head_dim ** -0.5)
+                           for h in range(heads)], axis=1)
+    check_close(o[0], want, what="window slot overflow %dx%d B%d D%d" % (grid_h, grid_w, block, head_dim))
 
 
 def test_attention_single_stripe_and_wide_band():

@@ -77,15 +77,48 @@ def test_attn_relpos_parity(key):
     check_close(o, want, what="attention relpos " + key)
 
 
-def test_attn_relpos_short_segment_two_mask_ksteps():
-    """The bias on a 16 x 16 bf16 segment whose mask needs two k-steps (one stripe of
-    sixteen 16-token tiles, 17 key classes with the pads')."""
-    _say("attention + relative position, two mask k-steps")
+def test_attn_relpos_short_segment_sixteen_classes():
+    """The bias on a 16 x 16 bf16 segment of sixteen key classes (one stripe of sixteen
+    16-token tiles; the window kernel's 256 slots hold one 16-key block per class)."""
+    _say("attention + relative position, sixteen key classes")
     over = dict(dtype="bf16", stripes=1, block=16, global_tokens=16, heads=2, head_dim=64, channels=128,
                 mlp_hidden=256, attn_density=0.3)
     o, want, plan = _attn_relpos_case("c1", seed=9, **over)
     _say("  max-abs %.3e rel-L2 %.3e" % (np.abs(o - want).max(), rel_l2(o, want)))
-    check_close(o, want, what="attention relpos, two mask k-steps")
+    check_close(o, want, what="attention relpos, sixteen key classes")
+
+
+@pytest.mark.parametrize("grid_h,grid_w,block,head_dim", [(16, 15, 8, 64), (15, 17, 17, 80)])
+def test_attn_relpos_window_slots_overflow(grid_h, grid_w, block, head_dim):
+    """The bias on short global segments whose key classes do not fit the window kernel's
+    256 LDS slots in 16-key blocks: the 32 x 32-block window kernel with two (30 classes)
+    or one (15 classes) mask k-steps."""
+    _say("attention + relative position, slot overflow", grid_h, grid_w, block, head_dim)
+    heads = 2 if head_dim == 64 else 8  # bf16 plans take channels in multiples of 128
+    plan = ss.Plan(grid_h, grid_w, 0, 1, block, block, -1, 0.3, 0.4, heads * head_dim, heads, head_dim, 256, 1,
+                   "bf16", rel_pos=True)
+    n, D = plan.info["seq_len"], head_dim
+    rng = np.random.default_rng(13)
+    q, k, v = (round_to_bf16(rng.standard_normal((1, heads, n, D), dtype=np.float32)) for _ in range(3))
+    v = round_to_bf16((v * np.float32(V_STD)).astype(np.float32))
+    perm = rng.permutation(n).astype(np.int32)[None]
+    rh = (rng.standard_normal((2 * grid_h - 1, D), dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+    rw = (rng.standard_normal((2 * grid_w - 1, D), dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+    n_pad = (n + 7) // 8 * 8
+    vt = np.full((1, heads, D, n_pad), np.nan, np.float32)
+    vt[..., :n] = v.transpose(0, 1, 3, 2)
+    dev = [torch.from_numpy(a).to(DEV, torch.bfloat16).contiguous() for a in (q, k, vt)]
+    o = ss.attn_relpos(plan, *dev, torch.from_numpy(perm).to(DEV), torch.from_numpy(rh).to(DEV),
+                       torch.from_numpy(rw).to(DEV)).float().cpu().numpy()
+    keep = oracle.position_keep(n, 1, block, block, plan.info["band_radius"])
+    want = np.empty((n, heads * D))
+    for h in range(heads):
+        q_slot = np.empty((n, D))
+        q_slot[perm[0]] = q[0, h]
+        bias = oracle.rel_pos_bias(q_slot, grid_h, grid_w, rh, rw)[np.ix_(perm[0], perm[0])]
+        want[:, h * D:(h + 1) * D] = oracle.masked_attention(q[0, h], k[0, h], v[0, h], keep, D ** -0.5, bias)
+    _say("  max-abs %.3e rel-L2 %.3e" % (np.abs(o[0] - want).max(), rel_l2(o[0], want)))
+    check_close(o[0], want, what="attention relpos, slot overflow %dx%d B%d D%d" % (grid_h, grid_w, block, D))
 
 
 def test_attn_relpos_bias_matters_and_zero_tables_match_plain():
