@@ -348,3 +348,25 @@ def test_sorted_stream_encoder_workspace_and_checks():
     m = _create(mlp_merge=True)
     assert lib.sparsesam_encoder_permuted(m.handle, None, layers, (ctypes.c_uint8 * 2)(1, 1), 2, p, 1, p, p, p, p, p,
                                           1 << 40, None) == 2
+
+
+def test_window_kernel_tables(tmp_path):
+    """The window kernel's slot map, key blocks and query groups, checked on the host by
+    tests/window_tables_check.cpp for ViT-B/H windows, partial windows, short global
+    segments and two plans whose classes overflow the 256 slots."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not found")
+    exe = str(tmp_path / "window_tables_check")
+    lib_dir = os.path.dirname(_lib.LIB_PATH)
+    cmd = [hipcc, "-std=c++17", "-O1", "-I" + os.path.join(ROOT, "include"),
+           "-I" + os.path.join(ROOT, "structured_sparse_vit_amd", "csrc"),
+           os.path.join(ROOT, "tests", "window_tables_check.cpp"), "-L" + lib_dir, "-lsparsesam",
+           "-Wl,-rpath," + lib_dir, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip().endswith("all ok"), r.stdout[-2000:]
+
