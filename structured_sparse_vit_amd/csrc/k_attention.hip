@@ -1429,16 +1429,28 @@ attn_win_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt, con
     }
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
-    if (qp >= 0) {
-      const float inv_l = 1.0f / l_tot;
-      bf16_t* o_row = O + ((size_t)seg * n + qp) * ((size_t)heads * D) + (size_t)h * D;
+    // O rows in 16-byte pieces: lanes g and g ^ 1 (same query) trade halves, so that for
+    // the blocks md, md + 1 an even lane holds d = 16 md + 4 g .. + 7 and an odd lane
+    // d = 16 (md + 1) + 4 (g - 1) .. + 7 (with an odd MD the last block is written by
+    // the even lanes alone)
+    const float inv_l = 1.0f / l_tot;
+    const bool odd = g & 1;
+    bf16_t* o_row = O + ((size_t)seg * n + (qp < 0 ? 0 : qp)) * ((size_t)heads * D) + (size_t)h * D;
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        bf16x4 v4;
+    for (int mp = 0; mp < MD; mp += 2) {
+      const int m0 = mp, m1 = mp + 1 < MD ? mp + 1 : mp;
+      bf16x4 a, b;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = to_bf16(oacc[md][i] * inv_l);
-        *reinterpret_cast<bf16x4*>(o_row + 16 * md + 4 * g) = v4;
+      for (int i = 0; i < 4; ++i) {
+        a[i] = to_bf16(oacc[m0][i] * inv_l);
+        b[i] = to_bf16(oacc[m1][i] * inv_l);
       }
+      const i32x2 ai = __builtin_bit_cast(i32x2, a), bi = __builtin_bit_cast(i32x2, b);
+      const int r0 = __shfl_xor(odd ? ai[0] : bi[0], 16, 64);
+      const int r1 = __shfl_xor(odd ? ai[1] : bi[1], 16, 64);
+      const i32x4 w = odd ? i32x4{r0, r1, bi[0], bi[1]} : i32x4{ai[0], ai[1], r0, r1};
+      const int d = odd ? 16 * m1 + 4 * (g - 1) : 16 * m0 + 4 * g;
+      if (qp >= 0 && (mp + 1 < MD || !odd)) *reinterpret_cast<i32x4*>(o_row + d) = w;
     }
     qp = qp_next;
 #pragma unroll
