@@ -353,7 +353,8 @@ def test_sorted_stream_encoder_workspace_and_checks():
 def test_window_kernel_tables(tmp_path):
     """The window kernel's slot map, key blocks and query groups, checked on the host by
     tests/window_tables_check.cpp for ViT-B/H windows, partial windows, short global
-    segments and two plans whose classes overflow the 256 slots."""
+    segments, two plans whose classes overflow the 256 slots, and a sweep of about 3500
+    short-segment plan shapes."""
     import shutil
     import subprocess
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -8,8 +8,9 @@
 //    blocks hold (valid slots only) are exactly the kept keys of each of its queries, so
 //    the kernel computes every kept pair once and no other pair;
 //  - the wavefront lists partition the groups.
-// Plans whose classes overflow the 256 slots must leave the table empty (they run the
-// 32 x 32-block kernel). Prints "all ok" and exits 0 when every check holds.
+// Tables are absent exactly when the classes need more than the 256 slots (those plans
+// run the 32 x 32-block kernel, or the SIMT kernel past 31 classes). A sweep over a grid
+// of plan shapes repeats every check. Prints "all ok" and exits 0 when every check holds.
 #include <cstdio>
 #include <set>
 #include <vector>
@@ -28,13 +29,38 @@ static int fails = 0;
     }                                 \
   } while (0)
 
-static void check_plan(const char* name, const sparsesam_plan& p, bool expect_tables) {
+// Slots the key classes need (each class rounded up to whole 16-slot blocks), counted
+// from the plan's tile list: tiles kept by the same query tiles form one class.
+static int class_slots(const sparsesam_plan& p) {
+  std::vector<std::vector<char>> cols;
+  std::vector<int> size;
+  for (int t2 = 0; t2 < p.tiles; ++t2) {
+    std::vector<char> col(p.tiles, 0);
+    for (int t1 = 0; t1 < p.tiles; ++t1)
+      for (int c = p.row_ptr[t1]; c < p.row_ptr[t1 + 1]; ++c)
+        if (p.col_idx[c] == t2) col[t1] = 1;
+    size_t k = 0;
+    while (k < cols.size() && cols[k] != col) ++k;
+    if (k == cols.size()) {
+      cols.push_back(col);
+      size.push_back(0);
+    }
+    size[k] += p.tile_len[t2];
+  }
+  int slots = 0;
+  for (int s : size) slots += (s + 15) / 16 * 16;
+  return slots;
+}
+
+static void check_plan(const char* name, const sparsesam_plan& p, bool expect_tables, bool named) {
   const int n = p.n, ns = p.win_nslots;
   if (!expect_tables) {
     CHECK(ns == 0 && p.win_groups.empty(), "tables built for a plan whose classes overflow the slots");
-    CHECK(p.nt32 > 0, "no short-segment kernel for an overflowing plan");
+    CHECK(class_slots(p) > kWinMaxSlots, "no tables although the classes need %d slots", class_slots(p));
+    if (named) CHECK(p.nt32 > 0, "no 32 x 32-block kernel for an overflowing plan");
     return;
   }
+  CHECK(ns == class_slots(p), "%d slots against %d the classes need", ns, class_slots(p));
   CHECK(ns > 0 && ns % 16 == 0 && ns <= kWinMaxSlots, "slot count %d", ns);
   CHECK(p.win_pos_slot.size() == (size_t)kWinMaxSlots && p.win_slot_pos.size() == (size_t)kWinMaxSlots,
         "table sizes");
@@ -93,8 +119,10 @@ static void check_plan(const char* name, const sparsesam_plan& p, bool expect_ta
   CHECK(pairs == p.pairs_kept, "pairs %lld against %lld kept", pairs, p.pairs_kept);
 }
 
+// expect_tables: 1 tables required, 0 tables must be absent, -1 either (a sweep case:
+// tables absent only when the classes overflow the slots)
 static void check(const char* name, int gh, int gw, int window, int stripes, int block, int G, float density,
-                  int heads, int head_dim, bool expect_tables) {
+                  int heads, int head_dim, int expect_tables) {
   sparsesam_plan_desc d{};
   d.grid_h = gh;
   d.grid_w = gw;
@@ -113,27 +141,55 @@ static void check(const char* name, int gh, int gw, int window, int stripes, int
   d.dtype = SPARSESAM_BF16;
   sparsesam_plan_t h = nullptr;
   if (sparsesam_plan_create(&d, &h) != SPARSESAM_OK) {
+    if (expect_tables < 0) return;  // a sweep shape the plan rules reject
     ++fails;
     std::printf("FAIL %s: plan_create: %s\n", name, sparsesam_last_error());
     return;
   }
-  check_plan(name, *h, expect_tables);
+  if (expect_tables >= 0 || h->n <= kShortMaxN)
+    check_plan(name, *h, expect_tables < 0 ? h->win_nslots > 0 : expect_tables != 0, expect_tables >= 0);
   sparsesam_plan_destroy(h);
 }
 
+// Every short-segment plan of a grid of shapes: grids and windows, stripe counts, tile
+// lengths, global token counts and densities.
+static int sweep() {
+  int plans = 0;
+  const int grids[][2] = {{8, 8}, {12, 12}, {14, 14}, {16, 16}, {16, 15}, {15, 17}, {18, 18}, {28, 28}};
+  for (const auto& gr : grids)
+    for (int window : {0, 7, 8, 14})
+      for (int stripes : {1, 2, 4, 7})
+        for (int block : {4, 8, 12, 16, 32})
+          for (int gm : {0, 1, 2})
+            for (float dens : {0.2f, 0.4f, 1.0f}) {
+              const int seg = window > 0 ? window * window : gr[0] * gr[1];
+              if (seg > kShortMaxN || seg % stripes != 0 || block > seg / stripes) continue;
+              char name[160];
+              std::snprintf(name, sizeof(name), "sweep grid %dx%d window %d stripes %d block %d G %d d %.1f", gr[0],
+                            gr[1], window, stripes, block, gm * block, dens);
+              const int before = fails;
+              check(name, gr[0], gr[1], window, stripes, block, gm * block, dens, 2, 64, -1);
+              ++plans;
+              if (fails > before + 5) return plans;
+            }
+  return plans;
+}
+
 int main() {
-  check("ViT-B windows d 0.4", 64, 64, 14, 4, 16, 16, 0.4f, 12, 64, true);
-  check("ViT-B windows d 0.3", 64, 64, 14, 4, 16, 16, 0.3f, 12, 64, true);
-  check("ViT-B windows d 1.0", 64, 64, 14, 4, 16, 16, 1.0f, 12, 64, true);
-  check("ViT-H windows d 0.4", 64, 64, 14, 4, 16, 16, 0.4f, 16, 80, true);
-  check("18 x 18 grid, partial windows", 18, 18, 14, 4, 16, 16, 0.4f, 2, 64, true);
-  check("16 x 16 global, one stripe", 16, 16, 0, 1, 16, 16, 0.3f, 2, 64, true);
-  check("16 x 16 global, four stripes", 16, 16, 0, 4, 16, 16, 0.4f, 2, 64, true);
-  check("windows of 14, seven stripes of 4-token tiles", 28, 28, 14, 7, 4, 0, 0.5f, 2, 64, true);
-  check("windows of 8", 16, 16, 8, 4, 16, 16, 0.4f, 2, 64, true);
-  check("one stripe of one tile", 14, 14, 14, 1, 49, 49, 1.0f, 2, 64, true);
-  check("30 classes of 8 tokens (overflow)", 16, 15, 0, 1, 8, 8, 0.3f, 2, 64, false);
-  check("15 classes of 17 tokens (overflow)", 15, 17, 0, 1, 17, 17, 0.3f, 8, 80, false);
+  check("ViT-B windows d 0.4", 64, 64, 14, 4, 16, 16, 0.4f, 12, 64, 1);
+  check("ViT-B windows d 0.3", 64, 64, 14, 4, 16, 16, 0.3f, 12, 64, 1);
+  check("ViT-B windows d 1.0", 64, 64, 14, 4, 16, 16, 1.0f, 12, 64, 1);
+  check("ViT-H windows d 0.4", 64, 64, 14, 4, 16, 16, 0.4f, 16, 80, 1);
+  check("18 x 18 grid, partial windows", 18, 18, 14, 4, 16, 16, 0.4f, 2, 64, 1);
+  check("16 x 16 global, one stripe", 16, 16, 0, 1, 16, 16, 0.3f, 2, 64, 1);
+  check("16 x 16 global, four stripes", 16, 16, 0, 4, 16, 16, 0.4f, 2, 64, 1);
+  check("windows of 14, seven stripes of 4-token tiles", 28, 28, 14, 7, 4, 0, 0.5f, 2, 64, 1);
+  check("windows of 8", 16, 16, 8, 4, 16, 16, 0.4f, 2, 64, 1);
+  check("one stripe of one tile", 14, 14, 14, 1, 49, 49, 1.0f, 2, 64, 1);
+  check("30 classes of 8 tokens (overflow)", 16, 15, 0, 1, 8, 8, 0.3f, 2, 64, 0);
+  check("15 classes of 17 tokens (overflow)", 15, 17, 0, 1, 17, 17, 0.3f, 8, 80, 0);
+  const int swept = sweep();
+  std::printf("%d sweep plans\n", swept);
   std::printf(fails ? "%d failures\n" : "all ok\n", fails);
   return fails != 0;
 }
