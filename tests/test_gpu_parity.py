@@ -279,6 +279,25 @@ def test_attention_window_slots_overflow(grid_h, grid_w, block, head_dim, ksteps
     check_close(o[0], want, what="window slot overflow %dx%d B%d D%d" % (grid_h, grid_w, block, head_dim))
 
 
+@pytest.mark.parametrize("over", [
+    dict(window=8, stripes=4, block=4, global_tokens=4, heads=2, head_dim=64, channels=128),
+    dict(image=448, window=14, stripes=7, block=4, global_tokens=0, attn_density=0.5, heads=2, head_dim=64,
+         channels=128),
+    dict(image=192, window=0, stripes=2, block=12, global_tokens=12, heads=8, head_dim=80, channels=640),
+    dict(window=0, stripes=4, block=8, global_tokens=8, attn_density=0.2, heads=2, head_dim=64, channels=128),
+])
+def test_attention_window_kernel_shapes(over):
+    """Short segments of other shapes: on the window kernel's 16-key blocks, 64-token
+    windows of 4-token tiles, seven stripes of 4-token tiles without global tokens (many
+    classes, partly empty blocks) and a 144-token global segment at head_dim 80; and a
+    256-token segment of 8-token tiles at density 0.2, whose classes need more than 256
+    slots (the 32 x 32-block kernel)."""
+    over = dict(over, dtype="bf16", mlp_hidden=256)
+    _say("attention window kernel shape", over)
+    o, want = _attn_case("c1", seed=14, **over)
+    check_close(o, want, what="window kernel shape %s" % over)
+
+
 def test_attention_single_stripe_and_wide_band():
     _say("attention stripes=1")
     o, want = _attn_case("c2", seed=4, stripes=1, band_radius=2)
