@@ -488,11 +488,29 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
   }
 }
 
-// Persistent launch: `nwg` workgroups (as many as stay resident) walk the units in
-// snake order -- unit u = r * nwg + (r even ? w : nwg - 1 - w) for rounds r = 0, 1, ... --
-// where units are (item, segment-head) pairs, items longest first. Long units land on
-// every workgroup in the first round and the shortest ones fill in after the shortest
-// first-round units, which evens out the work per workgroup without any atomics.
+// Unit of workgroup w in round r of a persistent launch of `nwg` workgroups, units u =
+// item * seg_heads + segment-head, items longest first; returns `total` when w is done.
+//  - More units than workgroups: the workgroups walk the units in snake order, u = r *
+//    nwg + (r even ? w : nwg - 1 - w): long units land on every workgroup in the first
+//    round and the shortest ones fill in after the shortest first-round units, which
+//    evens out the work per workgroup without any atomics.
+//  - One round (a workgroup per unit, the ViT-B global block at batch 1): the workgroups
+//    of one XCD (w % 8) take consecutive units in segment-head-major order, so a head's
+//    items share one or two XCDs' L2 and its K and V^T tiles are fetched once per such
+//    XCD (item-major, workgroup 12 i + h sat on XCD (4 i + h) mod 8: every head on two).
+__device__ __forceinline__ int attn_unit(int r, int w, int nwg, int total, int n_items, int seg_heads) {
+  if (total <= nwg) {
+    if (r > 0) return total;
+    const int x = w % kXcds, j = w / kXcds;
+    const int up = x * (nwg / kXcds) + min(x, nwg % kXcds) + j;  // head-major index
+    const int sh = up / n_items, item = up - sh * n_items;
+    return item * seg_heads + sh;
+  }
+  return r * nwg + ((r & 1) ? nwg - 1 - w : w);
+}
+
+// Persistent launch: `nwg` workgroups (as many as stay resident) walk the units in the
+// order attn_unit gives.
 __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma64_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt,
                                                           const bf16_t* __restrict__ VT, bf16_t* __restrict__ O,
                                                           const int4* __restrict__ items,
@@ -504,7 +522,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma64_kernel(const bf16
   const int nwg = gridDim.x, w = blockIdx.x;
   const int total = n_items * seg_heads;
   for (int r = 0;; ++r) {
-    const int u = r * nwg + ((r & 1) ? nwg - 1 - w : w);
+    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads);
     if (u >= total) break;
     if (r > 0) __syncthreads();  // the previous unit's merge has read its LDS exchange
     const int item = u / seg_heads;
@@ -538,7 +556,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma64_rel_kernel(
   const int nwg = gridDim.x, w = blockIdx.x;
   const int total = n_items * seg_heads;
   for (int r = 0;; ++r) {
-    const int u = r * nwg + ((r & 1) ? nwg - 1 - w : w);
+    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads);
     if (u >= total) break;
     if (r > 0) __syncthreads();
     const int item = u / seg_heads;
@@ -849,7 +867,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_d80_kernel(const bf16_t*
   const int nwg = gridDim.x, w = blockIdx.x;
   const int total = n_items * seg_heads;
   for (int r = 0;; ++r) {
-    const int u = r * nwg + ((r & 1) ? nwg - 1 - w : w);
+    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads);
     if (u >= total) break;
     if (r > 0) __syncthreads();
     const int item = u / seg_heads;
@@ -882,7 +900,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_d80_rel_kernel(
   const int nwg = gridDim.x, w = blockIdx.x;
   const int total = n_items * seg_heads;
   for (int r = 0;; ++r) {
-    const int u = r * nwg + ((r & 1) ? nwg - 1 - w : w);
+    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads);
     if (u >= total) break;
     if (r > 0) __syncthreads();
     const int item = u / seg_heads;
