@@ -28,6 +28,7 @@
 // pair gives every lane eight consecutive tokens of one channel straight from the
 // accumulators.
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -634,9 +635,14 @@ __device__ __forceinline__ void gemm_bf16_tile(const bf16_t* __restrict__ A, con
 // XCD rectangles: the (mt x nt) tile grid is cut into xa bands of tile rows times xb
 // bands of tile columns (xa * xb = 8), one rectangle per XCD, so each XCD's L2 holds
 // the A rows and W rows of its own rectangle. Workgroup hw runs on XCD hw % 8 and takes
-// the (hw / 8)-th tile of that rectangle, tile rows fastest.
+// the (hw / 8)-th tile of that rectangle. The rectangle is walked in groups of gm tile
+// rows, tile rows fastest inside a group, so the workgroups resident on an XCD at one
+// time cover about gm rows by (resident / gm) columns of tiles and share their A and W
+// panels in the L2 (walking a whole band of rows at a time made every column of tiles
+// fetch the band's A rows again).
 struct XcdRect {
   int xa, xb, mb, nb;  // bands, and tiles per band (ceil)
+  int gm;              // tile rows per group, 1 .. mb
 };
 
 template <int BM, int BN, int ST, class Epi>
@@ -645,9 +651,12 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16_t* __restrict
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nt = (N + BN - 1) / BN, mt = (M + BM - 1) / BM;
   const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  if (j >= xr.mb * xr.nb) return;
   const int ra = x / xr.xb, rb = x - (x / xr.xb) * xr.xb;
-  const int mi = ra * xr.mb + j % xr.mb, ni = rb * xr.nb + j / xr.mb;
-  if (j >= xr.mb * xr.nb || mi >= mt || ni >= nt) return;
+  const int grp = xr.gm * xr.nb, gi = j / grp, jj = j - gi * grp;
+  const int rows = min(xr.gm, xr.mb - gi * xr.gm);  // tile rows of this group
+  const int mi = ra * xr.mb + gi * xr.gm + jj % rows, ni = rb * xr.nb + jj / rows;
+  if (mi >= mt || ni >= nt) return;
   const int m0 = mi * BM, n0 = ni * BN;
   if (epi.col_tile(n0))
     gemm_bf16_tile<BM, BN, ST, true>(A, W, M, N, K, epi, smem, m0, n0);
@@ -786,22 +795,38 @@ static hipError_t run_bf16(const bf16_t* a, const bf16_t* w, int m, int n, int k
   auto kern = gemm_bf16_kernel<BM, BN, ST, Epi>;
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::LDS_BYTES);
   if (err != hipSuccess) return err;
-  // pick the XCD split with the fewest tiles on the busiest XCD, then the smallest
-  // per-XCD working set (A rows + W rows of a rectangle)
+  // XCD split: among the splits whose busiest XCD holds at most 5 % more tiles than the
+  // fewest possible, the one that fetches the least (each row band of A is read by the
+  // xb XCDs of its band, each column band of W by xa: m xb + n xa rows of K), then the
+  // smallest per-XCD working set (A rows + W rows of a rectangle)
   const int mt = (m + BM - 1) / BM, nt = (n + BN - 1) / BN;
-  XcdRect best{8, 1, (mt + 7) / 8, nt};
-  long best_load = -1, best_ws = 0;
+  long min_load = -1;
+  for (int xa = 1; xa <= 8; xa *= 2) {
+    const long load = (long)((mt + xa - 1) / xa) * ((nt + 8 / xa - 1) / (8 / xa));
+    if (min_load < 0 || load < min_load) min_load = load;
+  }
+  XcdRect best{8, 1, (mt + 7) / 8, nt, 1};
+  long best_load = -1, best_fetch = 0, best_ws = 0;
   for (int xa = 1; xa <= 8; xa *= 2) {
     const int xb = 8 / xa;
     const int mb = (mt + xa - 1) / xa, nb = (nt + xb - 1) / xb;
     const long load = (long)mb * nb;
+    if (load * 20 > min_load * 21) continue;
+    const long fetch = (long)m * xb + (long)n * xa;
     const long ws = (long)mb * BM + (long)nb * BN;
-    if (best_load < 0 || load < best_load || (load == best_load && ws < best_ws)) {
-      best = XcdRect{xa, xb, mb, nb};
+    if (best_load < 0 || fetch < best_fetch || (fetch == best_fetch && ws < best_ws)) {
+      best = XcdRect{xa, xb, mb, nb, 1};
       best_load = load;
+      best_fetch = fetch;
       best_ws = ws;
     }
   }
+  // group height: the resident workgroups of an XCD (32 CUs times the workgroups the LDS
+  // allows per CU) as a gm x (resident / gm) block that reads the fewest panel bytes,
+  // gm ~ sqrt(resident BN / BM)
+  const int per_cu = std::max(1, std::min(8, (int)((160 * 1024) / TL::LDS_BYTES)));
+  const double g = std::sqrt(32.0 * per_cu * BN / BM);
+  best.gm = std::max(1, std::min(best.mb, (int)(g + 0.5)));
   hipLaunchKernelGGL(kern, dim3((unsigned)(kXcds * best_load)), dim3(256), TL::LDS_BYTES, st, a, w, m, n, k, e,
                      best);
   return hipGetLastError();
