@@ -395,6 +395,8 @@ PROFILE_COMMANDS = {
     "mfma_c3": _prof("pmc_mfma_c3", "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16", cfg="c3"),
     "fetch_c3": _prof("pmc_fetch_c3", "FETCH_SIZE", cfg="c3"),
     "write_c3": _prof("pmc_write_c3", "WRITE_SIZE", cfg="c3"),
+    "trace_c5": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_c5 -o p -- "
+                "python3 bench.py --profile-encoder c5 --passes 2",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_copy -o p -- "
                   "python3 bench.py --copy-calibration",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_copy -o p -- "
@@ -537,6 +539,11 @@ def summarize_profiles(src):
                      c2 + " with the decomposed relative-position bias", "trace_relpos")
     if os.path.isdir(os.path.join(src, "trace_c3")):
         _write_trace(src, "trace_c3", "c3_step_kernel_trace.txt", c3, "trace_c3")
+    if os.path.isdir(os.path.join(src, "trace_c5")):
+        _write_trace(src, "trace_c5", "c5_encoder_kernel_trace.txt",
+                     "the c5 encoder (SAM ViT-H shape, 32 blocks: 4 global on 64 x 64 tokens, 28 on 25 windows of "
+                     "14 x 14 per image; C 1280, 16 heads x 80, MLP 5120, density 0.3, batch 16), 3 passes "
+                     "(one untimed), one random-init layer's weights in every block", "trace_c5")
     # HBM byte counters are scaled by what they read for a plain copy of known size
     cf, _ = _counter_kib(os.path.join(src, "pmc_fetch_copy"), "FETCH_SIZE", "copyBuffer")
     cw, _ = _counter_kib(os.path.join(src, "pmc_write_copy"), "WRITE_SIZE", "copyBuffer")
@@ -585,6 +592,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-encoders", action="store_true", help="skip the c3 windowed block and c4 / c5 encoder runs")
     ap.add_argument("--profile-only", action="store_true", help="run the steps only (for rocprofv3)")
+    ap.add_argument("--profile-encoder", metavar="KEY",
+                    help="run passes of encoder KEY (c4 or c5) only (for rocprofv3)")
+    ap.add_argument("--passes", type=int, default=2, help="timed passes of --profile-encoder")
     ap.add_argument("--rel-pos", action="store_true",
                     help="with --profile-only: steps of a plan with the relative-position bias")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -606,6 +616,10 @@ def main():
     from synth import get_config
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile_encoder:
+        r = encoder_run(args.profile_encoder, dev, passes=args.passes)
+        _log("%s encoder: %.3f ms per pass" % (args.profile_encoder, r["ms_per_pass"]))
+        return
     if args.copy_calibration:
         src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
