@@ -1328,6 +1328,7 @@ attn_win_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt, con
   // values: their probabilities are 0), while the loads are in flight; only LDS
   // operations are waited for before this barrier
   for (int i = tid; i < D * vld / 8; i += kWinThreads) reinterpret_cast<i32x4*>(Vs)[i] = i32x4{0, 0, 0, 0};
+  asm volatile("" ::: "memory");  // the zero stores stay above the wait and the barrier
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & lgkmcnt0_mask());
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");

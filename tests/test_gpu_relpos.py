@@ -2,7 +2,8 @@
 
 sparsesam_attn_relpos on random q, k, v and a random slot permutation: the full ViT-B
 global grid (bf16, matrix-core kernel), ViT-B and ViT-H windows and ragged windows
-(bf16, windowed matrix-core kernel), the ViT-H global grid (head_dim 80: fp16 tables,
+(bf16, the window kernel on 16-key blocks; the 32 x 32-block kernel for segments
+whose key classes overflow its slots), the ViT-H global grid (head_dim 80: fp16 tables,
 matrix-core kernel attn_d80_rel_kernel) and the fp32 tiny config (fp32 tables, SIMT
 kernel); and blocks of rel_pos plans on the image pipeline. Bars as in test_gpu_parity: max-abs 1e-2 and relative L2 5e-3.
 """
