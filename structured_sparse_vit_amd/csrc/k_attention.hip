@@ -498,11 +498,18 @@ __device__ __forceinline__ void attn_mfma64_unit(const bf16_t* __restrict__ Q, c
 //    of one XCD (w % 8) take consecutive units in segment-head-major order, so a head's
 //    items share one or two XCDs' L2 and its K and V^T tiles are fetched once per such
 //    XCD (item-major, workgroup 12 i + h sat on XCD (4 i + h) mod 8: every head on two).
-__device__ __forceinline__ int attn_unit(int r, int w, int nwg, int total, int n_items, int seg_heads) {
-  if (total <= nwg) {
-    if (r > 0) return total;
+//  - head_major (several rounds, chosen by the host when the static schedule is no less
+//    balanced than the snake's): round r takes the head-major units r * nwg .., each
+//    XCD's workgroups a consecutive run of them, so the items of a segment-head run in
+//    one round on one or two XCDs and share its K and V^T tiles in L2 (in the snake
+//    order each item of a head runs in another round and fetches the head's tiles again).
+__device__ __forceinline__ int attn_unit(int r, int w, int nwg, int total, int n_items, int seg_heads,
+                                         int head_major) {
+  if (total <= nwg || head_major) {
+    if (total <= nwg && r > 0) return total;
     const int x = w % kXcds, j = w / kXcds;
-    const int up = x * (nwg / kXcds) + min(x, nwg % kXcds) + j;  // head-major index
+    const int up = r * nwg + x * (nwg / kXcds) + min(x, nwg % kXcds) + j;  // head-major index
+    if (up >= total) return total;
     const int sh = up / n_items, item = up - sh * n_items;
     return item * seg_heads + sh;
   }
@@ -517,12 +524,12 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma64_kernel(const bf16
                                                           const int* __restrict__ col_idx,
                                                           const int* __restrict__ tile_start, int n, int n_pad,
                                                           int heads, int seg_heads, int n_items, float c_log2,
-                                                          float* __restrict__ partial) {
+                                                          float* __restrict__ partial, int head_major) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nwg = gridDim.x, w = blockIdx.x;
   const int total = n_items * seg_heads;
   for (int r = 0;; ++r) {
-    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads);
+    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads, head_major);
     if (u >= total) break;
     if (r > 0) __syncthreads();  // the previous unit's merge has read its LDS exchange
     const int item = u / seg_heads;
@@ -545,7 +552,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma64_rel_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt, const bf16_t* __restrict__ VT,
     bf16_t* __restrict__ O, const int4* __restrict__ items, const int* __restrict__ col_idx,
     const int* __restrict__ tile_start, int n, int n_pad, int heads, int seg_heads, int n_items, float c_log2,
-    float* __restrict__ partial, const f16_t* __restrict__ rel_t, const int* __restrict__ rel_kc) {
+    float* __restrict__ partial, const f16_t* __restrict__ rel_t, const int* __restrict__ rel_kc, int head_major) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // the one-hot rows, written once; the first unit's barrier publishes them
   if (threadIdx.x < 68) {
@@ -556,7 +563,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma64_rel_kernel(
   const int nwg = gridDim.x, w = blockIdx.x;
   const int total = n_items * seg_heads;
   for (int r = 0;; ++r) {
-    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads);
+    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads, head_major);
     if (u >= total) break;
     if (r > 0) __syncthreads();
     const int item = u / seg_heads;
@@ -862,12 +869,12 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_d80_kernel(const bf16_t*
                                                                   const int* __restrict__ col_idx,
                                                                   const int* __restrict__ tile_start, int n, int n_pad,
                                                                   int heads, int seg_heads, int n_items, float c_log2,
-                                                                  float* __restrict__ partial) {
+                                                                  float* __restrict__ partial, int head_major) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nwg = gridDim.x, w = blockIdx.x;
   const int total = n_items * seg_heads;
   for (int r = 0;; ++r) {
-    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads);
+    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads, head_major);
     if (u >= total) break;
     if (r > 0) __syncthreads();
     const int item = u / seg_heads;
@@ -890,7 +897,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_d80_rel_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kt, const bf16_t* __restrict__ VT,
     bf16_t* __restrict__ O, const int4* __restrict__ items, const int* __restrict__ col_idx,
     const int* __restrict__ tile_start, int n, int n_pad, int heads, int seg_heads, int n_items, float c_log2,
-    float* __restrict__ partial, const f16_t* __restrict__ rel_t, const int* __restrict__ rel_kc) {
+    float* __restrict__ partial, const f16_t* __restrict__ rel_t, const int* __restrict__ rel_kc, int head_major) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   if (threadIdx.x < 68) {  // one-hot rows, published by the first unit's barrier
     const int row = threadIdx.x >> 2, i = threadIdx.x & 3, e = row - 8;
@@ -900,7 +907,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_d80_rel_kernel(
   const int nwg = gridDim.x, w = blockIdx.x;
   const int total = n_items * seg_heads;
   for (int r = 0;; ++r) {
-    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads);
+    const int u = attn_unit(r, w, nwg, total, n_items, seg_heads, head_major);
     if (u >= total) break;
     if (r > 0) __syncthreads();
     const int item = u / seg_heads;
@@ -1673,6 +1680,36 @@ static hipError_t launch_short(const sparsesam_plan& p, int units, const bf16_t*
   return hipGetLastError();
 }
 
+// Unit order of a launch of several rounds: the head-major order (attn_unit) when the
+// work it gives the busiest workgroup is no more than the snake order gives, from each
+// item's steps (tiles / key parities; a four-parity step loads four tiles, 1.25 steps'
+// time) plus 2.6 steps of prologue and epilogue per unit. Units are assigned statically,
+// so both schedules are known here.
+static bool attn_head_major(const sparsesam_plan& p, int seg_heads, int nwg) {
+  const int total = p.n_items * seg_heads;
+  if (nwg <= 0 || total <= nwg) return false;
+  std::vector<double> cost(p.n_items);
+  for (int i = 0; i < p.n_items; ++i) {
+    const int* it = &p.items[(size_t)8 * i];
+    const int par = std::max(1, it[3] >> 4);
+    cost[i] = (double)((it[1] - it[0] + par - 1) / par) * (par == 4 ? 1.25 : 1.0) + 2.6;
+  }
+  double snake = 0.0, head = 0.0;
+  for (int w = 0; w < nwg; ++w) {
+    double a = 0.0, b = 0.0;
+    for (int r = 0;; ++r) {
+      const int u = r * nwg + ((r & 1) ? nwg - 1 - w : w);
+      if (u >= total) break;
+      a += cost[u / seg_heads];
+    }
+    const int x = w % kXcds, off = x * (nwg / kXcds) + std::min(x, nwg % kXcds) + w / kXcds;
+    for (int up = off; up < total; up += nwg) b += cost[up % p.n_items];
+    snake = std::max(snake, a);
+    head = std::max(head, b);
+  }
+  return head <= snake * 1.001;
+}
+
 // The window kernel on 16-key blocks: one workgroup per (segment, head).
 template <int D, bool REL>
 static hipError_t launch_win(const sparsesam_plan& p, int units, const bf16_t* q, const bf16_t* k, const bf16_t* vt,
@@ -1714,15 +1751,16 @@ hipError_t launch_attention(const sparsesam_plan& p, int segments, const T* q, c
       if (e != hipSuccess) return e;
       const int units = p.n_items * seg_heads;
       dim3 grid((unsigned)std::min(units, std::max(1, p.attn_resident_wgs)));
+      const int hm = attn_head_major(p, seg_heads, (int)grid.x) ? 1 : 0;
       const auto* items = reinterpret_cast<const int4*>(p.d_items);
       if (d80)
         hipLaunchKernelGGL(attn_d80_kernel, grid, dim3(64 * kAttnWaves), lds, st, q, k, vt, o, items, p.d_col_idx,
                            p.d_tile_start, p.n, p.n_pad, p.desc.heads, seg_heads, p.n_items, c_log2,
-                           static_cast<float*>(partial));
+                           static_cast<float*>(partial), hm);
       else
         hipLaunchKernelGGL(attn_mfma64_kernel, grid, dim3(64 * kAttnWaves), lds, st, q, k, vt, o, items,
                            p.d_col_idx, p.d_tile_start, p.n, p.n_pad, p.desc.heads, seg_heads, p.n_items, c_log2,
-                           static_cast<float*>(partial));
+                           static_cast<float*>(partial), hm);
       e = hipGetLastError();
       if (e != hipSuccess || p.n_split_rows == 0) return e;
       const int waves = p.n_split_rows * seg_heads * kTile;
@@ -1772,6 +1810,7 @@ hipError_t launch_attention_relpos(const sparsesam_plan& p, int segments, const 
       const int seg_heads = segments * p.desc.heads;
       const int units = p.n_items * seg_heads;
       dim3 grid((unsigned)std::min(units, std::max(1, p.attn_resident_wgs)));
+      const int hm = attn_head_major(p, seg_heads, (int)grid.x) ? 1 : 0;
       const auto* items = reinterpret_cast<const int4*>(p.d_items);
       const auto* qb = reinterpret_cast<const bf16_t*>(q);
       const auto* kb = reinterpret_cast<const bf16_t*>(k);
@@ -1780,11 +1819,11 @@ hipError_t launch_attention_relpos(const sparsesam_plan& p, int segments, const 
       if (d80)
         hipLaunchKernelGGL(attn_d80_rel_kernel, grid, dim3(64 * kAttnWaves), lds, st, qb, kb, vb, ob, items,
                            p.d_col_idx, p.d_tile_start, p.n, p.n_pad, p.desc.heads, seg_heads, p.n_items, c_log2,
-                           static_cast<float*>(partial), tb, kc);
+                           static_cast<float*>(partial), tb, kc, hm);
       else
         hipLaunchKernelGGL(attn_mfma64_rel_kernel, grid, dim3(64 * kAttnWaves), lds, st, qb, kb, vb, ob, items,
                            p.d_col_idx, p.d_tile_start, p.n, p.n_pad, p.desc.heads, seg_heads, p.n_items, c_log2,
-                           static_cast<float*>(partial), tb, kc);
+                           static_cast<float*>(partial), tb, kc, hm);
       e = hipGetLastError();
       if (e != hipSuccess || p.n_split_rows == 0) return e;
       const int waves = p.n_split_rows * seg_heads * kTile;
