@@ -395,6 +395,8 @@ PROFILE_COMMANDS = {
     "mfma_c3": _prof("pmc_mfma_c3", "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16", cfg="c3"),
     "fetch_c3": _prof("pmc_fetch_c3", "FETCH_SIZE", cfg="c3"),
     "write_c3": _prof("pmc_write_c3", "WRITE_SIZE", cfg="c3"),
+    "trace_c4": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_c4 -o p -- "
+                "python3 bench.py --profile-encoder c4 --passes 2",
     "trace_c5": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_c5 -o p -- "
                 "python3 bench.py --profile-encoder c5 --passes 2",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_copy -o p -- "
@@ -539,6 +541,11 @@ def summarize_profiles(src):
                      c2 + " with the decomposed relative-position bias", "trace_relpos")
     if os.path.isdir(os.path.join(src, "trace_c3")):
         _write_trace(src, "trace_c3", "c3_step_kernel_trace.txt", c3, "trace_c3")
+    if os.path.isdir(os.path.join(src, "trace_c4")):
+        _write_trace(src, "trace_c4", "c4_encoder_kernel_trace.txt",
+                     "the c4 encoder (SAM ViT-L shape, 24 blocks: 4 global on 64 x 64 tokens, 20 on 25 windows of "
+                     "14 x 14 per image; C 1024, 16 heads x 64, MLP 4096, density 0.3, batch 8), 3 passes "
+                     "(one untimed), one random-init layer's weights in every block", "trace_c4")
     if os.path.isdir(os.path.join(src, "trace_c5")):
         _write_trace(src, "trace_c5", "c5_encoder_kernel_trace.txt",
                      "the c5 encoder (SAM ViT-H shape, 32 blocks: 4 global on 64 x 64 tokens, 28 on 25 windows of "
