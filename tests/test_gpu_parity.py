@@ -298,6 +298,27 @@ def test_attention_window_kernel_shapes(over):
     check_close(o, want, what="window kernel shape %s" % over)
 
 
+@pytest.mark.parametrize("key,batch", [("c2", 4), ("c5g", 16)])
+def test_attention_schedule_independent(key, batch):
+    """Every work unit is computed the same whichever workgroup runs it, so attention over
+    a batch (several rounds of units: the snake order, or at ViT-H global batch 16 the
+    head-major order) equals, bit for bit, attention run one segment at a time (one round,
+    XCD-grouped units)."""
+    _say("attention schedule", key, batch)
+    cfg = config(key).with_(batch=batch)
+    plan = _plan(cfg)
+    n, H, D = plan.info["seq_len"], cfg.heads, cfg.head_dim
+    n_pad = (n + 7) // 8 * 8
+    g = torch.Generator(device=DEV).manual_seed(21)
+    q = torch.randn(batch, H, n, D, device=DEV, generator=g).to(torch.bfloat16)
+    k = torch.randn(batch, H, n, D, device=DEV, generator=g).to(torch.bfloat16)
+    vt = torch.randn(batch, H, D, n_pad, device=DEV, generator=g).to(torch.bfloat16)
+    full = ss.attn(plan, q, k, vt)
+    for s in range(batch):
+        one = ss.attn(plan, q[s:s + 1].contiguous(), k[s:s + 1].contiguous(), vt[s:s + 1].contiguous())
+        assert torch.equal(one[0], full[s]), "segment %d differs" % s
+
+
 def test_attention_single_stripe_and_wide_band():
     _say("attention stripes=1")
     o, want = _attn_case("c2", seed=4, stripes=1, band_radius=2)
